@@ -1,0 +1,142 @@
+"""Gated delta-rule forward pass for AMD MI355X (gfx950).
+
+Thin Python layer over the C ABI in libgdr.so: it checks tensors, allocates
+outputs with torch (device memory and streams only) and passes raw pointers.
+All arithmetic runs in the HIP kernels.
+
+    o, S_T = chunk_fwd(q, k, v, beta, log_alpha, initial_state)
+    o      = recurrent_step(q, k, v, beta, log_alpha, state)   # state in place
+
+Gate kind follows log_alpha: None -> DeltaNet (alpha = 1); [B, T, H] ->
+Gated DeltaNet (one decay per head); [B, T, H, Dk] -> KDA (one per channel).
+"""
+
+import torch
+
+from . import _abi
+from ._abi import GdrError, abi_version, status_str, LIB_PATH
+
+__all__ = ["chunk_fwd", "recurrent_step", "GdrError", "abi_version", "status_str",
+           "LIB_PATH", "library_loaded"]
+
+_DT = {torch.float32: _abi.GDR_F32, torch.bfloat16: _abi.GDR_BF16}
+
+
+def library_loaded():
+    return _abi._lib is not None
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _gate_of(log_alpha, lead_shape, Dk):
+    if log_alpha is None:
+        return _abi.GDR_GATE_NONE
+    if tuple(log_alpha.shape) == tuple(lead_shape):
+        return _abi.GDR_GATE_SCALAR
+    if tuple(log_alpha.shape) == tuple(lead_shape) + (Dk,):
+        return _abi.GDR_GATE_CHANNEL
+    raise ValueError(f"log_alpha shape {tuple(log_alpha.shape)} fits neither "
+                     f"{tuple(lead_shape)} (per head) nor {tuple(lead_shape) + (Dk,)} (per channel)")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
+              out_dtype=torch.float32, output_final_state=True, o=None, final_state=None):
+    """Chunkwise forward over whole sequences.
+
+    q, k [B, T, H, Dk] and v [B, T, H, Dv] (bf16 or fp32, same dtype);
+    beta [B, T, H] fp32; log_alpha None | [B, T, H] | [B, T, H, Dk] fp32;
+    initial_state None | [B, H, Dk, Dv] fp32.  Returns (o [B, T, H, Dv] in
+    out_dtype, final state [B, H, Dk, Dv] fp32 or None).  `o` and
+    `final_state` may be passed preallocated; final_state may be the
+    initial_state tensor itself (in-place carry).
+    """
+    _check_dev("q", q)
+    if q.dtype not in _DT:
+        raise TypeError("q/k/v must be bf16 or fp32")
+    for name, t in (("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("beta", beta, torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B, T, H, Dk] and v [B, T, H, Dv]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    if tuple(beta.shape) != (B, T, H):
+        raise ValueError("beta must be [B, T, H]")
+    gate = _gate_of(log_alpha, (B, T, H), Dk)
+    if log_alpha is not None:
+        _check_dev("log_alpha", log_alpha, torch.float32)
+    if initial_state is not None:
+        _check_dev("initial_state", initial_state, torch.float32)
+        if tuple(initial_state.shape) != (B, H, Dk, Dv):
+            raise ValueError("initial_state must be [B, H, Dk, Dv]")
+    if out_dtype not in _DT:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if o is None:
+        o = torch.empty(B, T, H, Dv, device=q.device, dtype=out_dtype)
+    else:
+        _check_dev("o", o, out_dtype)
+        if tuple(o.shape) != (B, T, H, Dv):
+            raise ValueError("o must be [B, T, H, Dv]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty(B, H, Dk, Dv, device=q.device, dtype=torch.float32)
+    elif final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+        if tuple(final_state.shape) != (B, H, Dk, Dv):
+            raise ValueError("final_state must be [B, H, Dk, Dv]")
+    st = _abi.gdr_chunk_fwd(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], _DT[out_dtype], gate,
+                            q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                            _ptr(log_alpha), _ptr(initial_state), o.data_ptr(),
+                            _ptr(final_state), _stream(q.device))
+    if st != _abi.GDR_OK:
+        raise GdrError(st, "gdr_chunk_fwd")
+    return o, final_state
+
+
+def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None):
+    """One decode token for N sequences; `state` [N, H, Dk, Dv] fp32 is
+    updated in place.  q, k [N, H, Dk]; v [N, H, Dv]; beta [N, H];
+    log_alpha None | [N, H] | [N, H, Dk].  Returns o [N, H, Dv]."""
+    _check_dev("q", q)
+    if q.dtype not in _DT:
+        raise TypeError("q/k/v must be bf16 or fp32")
+    for name, t in (("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("beta", beta, torch.float32)
+    _check_dev("state", state, torch.float32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [N, H, Dk] and v [N, H, Dv]")
+    N, H, Dk = q.shape
+    Dv = v.shape[2]
+    if tuple(beta.shape) != (N, H) or tuple(state.shape) != (N, H, Dk, Dv):
+        raise ValueError("beta must be [N, H] and state [N, H, Dk, Dv]")
+    gate = _gate_of(log_alpha, (N, H), Dk)
+    if log_alpha is not None:
+        _check_dev("log_alpha", log_alpha, torch.float32)
+    if o is None:
+        o = torch.empty(N, H, Dv, device=q.device, dtype=out_dtype)
+    else:
+        _check_dev("o", o, out_dtype)
+    st = _abi.gdr_recurrent_step(N, H, Dk, Dv, _DT[q.dtype], _DT[out_dtype], gate,
+                                 q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                 _ptr(log_alpha), state.data_ptr(), o.data_ptr(),
+                                 _stream(q.device))
+    if st != _abi.GDR_OK:
+        raise GdrError(st, "gdr_recurrent_step")
+    return o

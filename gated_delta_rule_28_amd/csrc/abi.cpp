@@ -1,0 +1,107 @@
+// C ABI entry points: argument validation on the host, then dispatch to the
+// kernel launchers.  No exception crosses this boundary and nothing is
+// launched for an invalid call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdr.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void *p, unsigned bytes) {
+  return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(bytes - 1)) == 0;
+}
+
+bool valid_dtype(int d) { return d == GDR_F32 || d == GDR_BF16; }
+bool valid_gate(int g) { return g == GDR_GATE_NONE || g == GDR_GATE_SCALAR || g == GDR_GATE_CHANNEL; }
+bool supported_head(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// gate/log_alpha consistency and common pointer checks for both entry points
+int check_common(int Dk, int Dv, int in_dtype, int out_dtype, int gate, const void *q,
+                 const void *k, const void *v, const float *beta, const float *log_alpha,
+                 const void *o) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate)) return GDR_EINVAL;
+  if ((gate == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
+  if (!q || !k || !v || !beta || !o) return GDR_EINVAL;
+  // q/k/v are read with 16-byte vector loads; the rest needs natural alignment
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned(beta, 4) ||
+      !aligned(o, out_dtype == GDR_BF16 ? 2 : 4) || (log_alpha && !aligned(log_alpha, 4)))
+    return GDR_EINVAL;
+  if (Dk != Dv || !supported_head(Dk)) return GDR_EUNSUPPORTED;
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_status_str(int status) {
+  switch (status) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_EINVAL: return "GDR_EINVAL: invalid argument";
+    case GDR_EUNSUPPORTED: return "GDR_EUNSUPPORTED: shape/dtype/chunk not implemented";
+    case GDR_EHIP: return "GDR_EHIP: HIP runtime error on launch";
+    default: return "unknown gdr status";
+  }
+}
+
+int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int out_dtype,
+                  int gate, const void *q, const void *k, const void *v, const float *beta,
+                  const float *log_alpha, const float *initial_state, void *o,
+                  float *final_state, hipStream_t stream) {
+  if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
+  if (!(chunk == 0 || chunk == 16 || chunk == 32 || chunk == 64)) return GDR_EUNSUPPORTED;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate)) return GDR_EINVAL;
+  if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+    return GDR_EINVAL;
+  if (Dk != Dv || !supported_head(Dk)) return GDR_EUNSUPPORTED;
+  // empty token tensors may carry null pointers, so these return before the
+  // pointer checks
+  if ((long)B * H == 0) return GDR_OK;                   // nothing to compute
+  if (T == 0) {                                          // no tokens: S_T = S_0
+    if (!final_state || final_state == initial_state) return GDR_OK;
+    hipError_t e = gdr::launch_state_passthrough(initial_state, final_state,
+                                                 (long)B * H * Dk * Dv, stream);
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+  }
+  int st = check_common(Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, log_alpha, o);
+  if (st != GDR_OK) return st;
+
+  gdr::ChunkArgs a;
+  a.B = B; a.T = T; a.H = H; a.D = Dk; a.chunk = chunk;
+  a.in_bf16 = in_dtype == GDR_BF16; a.out_bf16 = out_dtype == GDR_BF16;
+  a.gate = gate;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.initial_state = initial_state; a.o = o; a.final_state = final_state;
+  a.stream = stream;
+
+  hipError_t e;
+  if (gdr::chunk_fwd_bf16_supported(a)) e = gdr::launch_chunk_fwd_bf16(a);
+  else if (gdr::chunk_fwd_small_supported(a)) e = gdr::launch_chunk_fwd_small(a);
+  else return GDR_EUNSUPPORTED;
+  return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+int gdr_recurrent_step(int N, int H, int Dk, int Dv, int in_dtype, int out_dtype, int gate,
+                       const void *q, const void *k, const void *v, const float *beta,
+                       const float *log_alpha, float *state, void *o, hipStream_t stream) {
+  if (N < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
+  if ((long)N * H == 0) return GDR_OK;
+  int st = check_common(Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, log_alpha, o);
+  if (st != GDR_OK) return st;
+  if (!state || !aligned16(state)) return GDR_EINVAL;
+  gdr::RecurrentArgs a;
+  a.N = N; a.H = H; a.D = Dk;
+  a.in_bf16 = in_dtype == GDR_BF16; a.out_bf16 = out_dtype == GDR_BF16;
+  a.gate = gate;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.state = state; a.o = o; a.stream = stream;
+  hipError_t e = gdr::launch_recurrent_step(a);
+  return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+}  // extern "C"

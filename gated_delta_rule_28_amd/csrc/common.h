@@ -1,0 +1,40 @@
+// Device-side helpers shared by the gated delta-rule kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+enum Gate { kGateNone = 0, kGateScalar = 1, kGateChannel = 2 };
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Split an fp32 value into bf16 hi + lo with x ~= hi + lo to ~16 bits.
+// x - float(hi) is exact in fp32, so only the rounding of lo is lost.
+__device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+
+// D += A(16x32) * B(32x16), bf16 operands, fp32 accumulate.  Lane l holds
+// A row (l & 15) and B column (l & 15), eight k values per lane (the same k
+// set for A and B, so any consistent k order gives the same product); the
+// result lane l holds column (l & 15), rows 4*(l >> 4) + 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace gdr

@@ -1,0 +1,142 @@
+// Single-token decode step of the gated delta rule, fp32 state updated in place.
+//
+// Per (sequence, head) the step is (page "NLP——线性注意力相关总结", GDN and KDA
+// sections; order decay -> predict -> write -> read as in the diosapp
+// tutorial, section 四):
+//     S' = a S  (or Diag(a) S)        p = S'^T k        d = beta (v - p)
+//     S  = S' + k d^T                 o = S^T q = S'^T q + (k . q) d
+// The second form of o lets one pass over S produce both reductions before
+// the write, so S is read once and written once: 2 * Dk * Dv * 4 bytes of
+// HBM traffic per state, which is the whole cost of the step (HBM-bound).
+//
+// Work mapping: one workgroup per (sequence, head) state, 2*Dv threads.
+// Thread t owns columns 4*(t % (Dv/4)) .. +3 and rows (t / (Dv/4)) * R .. +R-1
+// with R = Dk / 8, so a wavefront reads whole 512-byte rows (Dv = 128) with
+// 16-byte loads.  The eight row groups combine their partial p and S'^T q
+// through LDS.
+#include "common.h"
+#include "internal.h"
+
+namespace gdr {
+
+template <int DK, int DV, typename InT, typename OutT, int GATE>
+__global__ void __launch_bounds__(2 * DV)
+recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
+                      const InT *__restrict__ v, const float *__restrict__ beta,
+                      const float *__restrict__ log_alpha, float *__restrict__ state,
+                      OutT *__restrict__ o) {
+  constexpr int NT = 2 * DV;          // threads per state
+  constexpr int C4 = DV / 4;          // float4 columns per row
+  constexpr int RG = NT / C4;         // row groups (= 8)
+  constexpr int R = DK / RG;          // rows per thread
+  static_assert(RG == 8 && R * RG == DK, "decode mapping");
+
+  const int t = threadIdx.x;
+  const int c4 = t % C4;
+  const int rg = t / C4;
+  const long sid = blockIdx.x;        // (n * H + h)
+
+  __shared__ float s_k[DK], s_q[DK], s_la[DK];
+  __shared__ float s_part[RG][2][DV];
+  __shared__ float s_kq[RG];
+
+  float *S = state + sid * (long)DK * DV;
+  // issue the state loads first: they are the whole cost of the step
+  f32x4 s[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    s[i] = *reinterpret_cast<const f32x4 *>(S + (long)(rg * R + i) * DV + 4 * c4);
+
+  for (int i = t; i < DK; i += NT) {
+    s_k[i] = to_f32(k[sid * DK + i]);
+    s_q[i] = to_f32(q[sid * DK + i]);
+    if (GATE == kGateChannel) s_la[i] = log_alpha[sid * DK + i];
+  }
+  const float b = beta[sid];
+  float a_head = 1.0f;
+  if (GATE == kGateScalar) a_head = __expf(log_alpha[sid]);
+  __syncthreads();
+
+  f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int row = rg * R + i;
+    float a = a_head;
+    if (GATE == kGateChannel) a = __expf(s_la[row]);
+    s[i] *= a;                                   // S' = decayed state
+    const float kr = s_k[row], qr = s_q[row];
+    p += kr * s[i];
+    sq += qr * s[i];
+    kq += kr * qr;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s_part[rg][0][4 * c4 + j] = p[j];
+    s_part[rg][1][4 * c4 + j] = sq[j];
+  }
+  if (c4 == 0) s_kq[rg] = kq;
+  __syncthreads();
+
+  f32x4 pt = {0.f, 0.f, 0.f, 0.f}, st = {0.f, 0.f, 0.f, 0.f};
+  float kqt = 0.f;
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pt[j] += s_part[g][0][4 * c4 + j];
+      st[j] += s_part[g][1][4 * c4 + j];
+    }
+    kqt += s_kq[g];
+  }
+  f32x4 vv, d;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vv[j] = to_f32(v[sid * DV + 4 * c4 + j]);
+    d[j] = b * (vv[j] - pt[j]);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const float kr = s_k[rg * R + i];
+    *reinterpret_cast<f32x4 *>(S + (long)(rg * R + i) * DV + 4 * c4) = s[i] + kr * d;
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[sid * DV + 4 * c4 + j] = from_f32<OutT>(st[j] + kqt * d[j]);
+  }
+}
+
+template <int D, typename InT, typename OutT, int GATE>
+static hipError_t launch_one(const RecurrentArgs &a) {
+  dim3 grid((unsigned)((long)a.N * a.H)), block(2 * D);
+  hipLaunchKernelGGL((recurrent_step_kernel<D, D, InT, OutT, GATE>), grid, block, 0, a.stream,
+                     (const InT *)a.q, (const InT *)a.k, (const InT *)a.v, a.beta, a.log_alpha,
+                     a.state, (OutT *)a.o);
+  return hipGetLastError();
+}
+
+template <int D, typename InT, typename OutT>
+static hipError_t by_gate(const RecurrentArgs &a) {
+  switch (a.gate) {
+    case kGateNone: return launch_one<D, InT, OutT, kGateNone>(a);
+    case kGateScalar: return launch_one<D, InT, OutT, kGateScalar>(a);
+    default: return launch_one<D, InT, OutT, kGateChannel>(a);
+  }
+}
+
+template <int D>
+static hipError_t by_dtype(const RecurrentArgs &a) {
+  if (a.in_bf16) return a.out_bf16 ? by_gate<D, bf16, bf16>(a) : by_gate<D, bf16, float>(a);
+  return a.out_bf16 ? by_gate<D, float, bf16>(a) : by_gate<D, float, float>(a);
+}
+
+hipError_t launch_recurrent_step(const RecurrentArgs &a) {
+  switch (a.D) {
+    case 16: return by_dtype<16>(a);
+    case 32: return by_dtype<32>(a);
+    case 64: return by_dtype<64>(a);
+    default: return by_dtype<128>(a);
+  }
+}
+
+}  // namespace gdr

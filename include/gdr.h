@@ -1,0 +1,137 @@
+/*
+ * gdr.h -- C ABI of the gated delta-rule forward pass for AMD MI355X (gfx950).
+ *
+ * The method (page "NLP——线性注意力相关总结", sections "Gated DeltaNet (GDN)"
+ * and "Kimi Delta Attention (KDA)"; xhh.club digest "Transformer 入坑笔记（五）",
+ * Q&A on Gated DeltaNet and KDA), per (batch, head) chain, token t:
+ *
+ *   GDN       S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T
+ *   DeltaNet  the same with a_t = 1
+ *   KDA       S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T
+ *   output    o_t = S_t^T q_t      (read after the token's own write)
+ *
+ * with a_t = exp(log_alpha_t) (one scalar per head, or one value per key
+ * channel for KDA), b_t = beta_t, S in R^{Dk x Dv}.  No query scale, no
+ * feature map and no normaliser are applied: q and k are used as given.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *    library allocates no device memory and keeps no global mutable state.
+ *  - All tensors are dense, row-major, with the last dimension contiguous.
+ *  - Every call is asynchronous on `stream` (NULL = the default stream).
+ *  - Return value: GDR_OK (0) on success, a negative gdr_status otherwise.
+ *    Arguments are validated on the host before anything is launched; a
+ *    call that fails validation launches nothing and writes nothing.  A
+ *    failed launch returns GDR_EHIP.  Device faults surface at the caller's
+ *    next synchronisation.  No C++ exception crosses this interface.
+ *  - Values are not checked on the device.  Preconditions: log_alpha is
+ *    finite and <= 0 (-inf is not supported; a large negative value such as
+ *    -50 gives a clean hard reset), beta is finite.  Non-finite inputs
+ *    propagate only into the (batch, head) chain they belong to.
+ *  - q, k, v and every state pointer must be 16-byte aligned; beta and
+ *    log_alpha 4-byte aligned; o aligned to its element size.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_EINVAL = -1,       /* bad argument: null pointer, size <= 0, misaligned, gate mismatch */
+  GDR_EUNSUPPORTED = -2, /* valid but not implemented: head size, chunk size, dtype combination */
+  GDR_EHIP = -3          /* the HIP runtime reported an error on launch */
+} gdr_status;
+
+typedef enum gdr_dtype {
+  GDR_F32 = 0,
+  GDR_BF16 = 1
+} gdr_dtype;
+
+typedef enum gdr_gate {
+  GDR_GATE_NONE = 0,    /* a_t = 1 (DeltaNet); log_alpha must be NULL      */
+  GDR_GATE_SCALAR = 1,  /* GDN: log_alpha [.., H], one value per head      */
+  GDR_GATE_CHANNEL = 2  /* KDA: log_alpha [.., H, Dk], one per key channel */
+} gdr_gate;
+
+/* ABI version of the loaded library (GDR_ABI_VERSION of the build). */
+int gdr_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *gdr_status_str(int status);
+
+/*
+ * gdr_chunk_fwd -- forward pass over whole sequences, chunk by chunk.
+ *
+ * Defined by the recurrence above; computed chunkwise (matrix products
+ * inside a chunk, the state carried from chunk to chunk, the in-chunk
+ * recurrence resolved through a unit-lower-triangular solve -- xhh.club
+ * digest, sections on chunked computation and the Gated DeltaNet / KDA
+ * Q&A).  The result does not depend on `chunk` beyond rounding.
+ *
+ *   B, T, H      batch, tokens per sequence (any T >= 1), heads
+ *   Dk, Dv       key / value head sizes (supported: Dk == Dv in {16, 32, 64, 128})
+ *   chunk        tokens per chunk: 0 = default, else 16, 32 or 64
+ *   in_dtype     dtype of q, k, v (GDR_BF16 or GDR_F32)
+ *   out_dtype    dtype of o (GDR_F32 or GDR_BF16)
+ *   gate         GDR_GATE_NONE / _SCALAR / _CHANNEL
+ *   q, k         [B, T, H, Dk] in_dtype
+ *   v            [B, T, H, Dv] in_dtype
+ *   beta         [B, T, H] fp32
+ *   log_alpha    NULL iff gate == NONE; [B, T, H] fp32 (SCALAR) or
+ *                [B, T, H, Dk] fp32 (CHANNEL)
+ *   initial_state [B, H, Dk, Dv] fp32, or NULL for a zero state
+ *   o            [B, T, H, Dv] out_dtype (written)
+ *   final_state  [B, H, Dk, Dv] fp32, or NULL (not written).  May be the
+ *                same pointer as initial_state (in-place carry); any other
+ *                overlap between outputs and inputs is not allowed.
+ *
+ * Accuracy: fp32 state and fp32 accumulation throughout.  With bf16 q/k/v
+ * every product whose operand is not an exact bf16 value is evaluated as a
+ * sum of bf16 hi/lo parts, keeping errors near fp32 level.
+ */
+int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk,
+                  int in_dtype, int out_dtype, int gate,
+                  const void *q, const void *k, const void *v,
+                  const float *beta, const float *log_alpha,
+                  const float *initial_state,
+                  void *o, float *final_state,
+                  hipStream_t stream);
+
+/*
+ * gdr_recurrent_step -- one decode step: a single new token for each of N
+ * independent sequences, with the fp32 state updated IN PLACE (the
+ * constant-size memory that replaces the KV cache; diosapp tutorial,
+ * section 一, decoding cost independent of length).
+ *
+ *   N, H         sequences, heads
+ *   Dk, Dv       head sizes (supported: Dk == Dv in {16, 32, 64, 128})
+ *   in_dtype     dtype of q, k, v;  out_dtype  dtype of o
+ *   gate         as above
+ *   q, k         [N, H, Dk];  v [N, H, Dv]
+ *   beta         [N, H] fp32
+ *   log_alpha    NULL iff gate == NONE; [N, H] (SCALAR) or [N, H, Dk] (CHANNEL)
+ *   state        [N, H, Dk, Dv] fp32, read and overwritten with S_t
+ *   o            [N, H, Dv] out_dtype (written); must not overlap state
+ */
+int gdr_recurrent_step(int N, int H, int Dk, int Dv,
+                       int in_dtype, int out_dtype, int gate,
+                       const void *q, const void *k, const void *v,
+                       const float *beta, const float *log_alpha,
+                       float *state, void *o,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

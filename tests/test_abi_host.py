@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI library (no GPU needed).
+
+The library must load, export every function include/gdr.h declares, and
+reject invalid calls on the host with the documented status codes before
+anything is launched (these calls never reach the HIP runtime).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_28_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == ["gdr_abi_version", "gdr_chunk_fwd", "gdr_recurrent_step",
+                     "gdr_status_str"], names
+    assert set(names) == set(_abi.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert _abi.abi_version() == 1
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3):
+        assert _abi.status_str(st).startswith("GDR_")
+    assert "unknown" in _abi.status_str(-99)
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced
+
+
+def chunk(**kw):
+    a = dict(B=1, T=8, H=1, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+             out_dtype=_abi.GDR_F32, gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE,
+             beta=FAKE, log_alpha=FAKE, initial_state=None, o=FAKE, final_state=None,
+             stream=None)
+    a.update(kw)
+    return _abi.gdr_chunk_fwd(**a)
+
+
+def step(**kw):
+    a = dict(N=1, H=1, Dk=128, Dv=128, in_dtype=_abi.GDR_BF16, out_dtype=_abi.GDR_F32,
+             gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, log_alpha=FAKE,
+             state=FAKE, o=FAKE, stream=None)
+    a.update(kw)
+    return _abi.gdr_recurrent_step(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), _abi.GDR_EINVAL),
+    (dict(T=-5), _abi.GDR_EINVAL),
+    (dict(Dk=0), _abi.GDR_EINVAL),
+    (dict(q=None), _abi.GDR_EINVAL),
+    (dict(o=None), _abi.GDR_EINVAL),
+    (dict(beta=None), _abi.GDR_EINVAL),
+    (dict(q=FAKE + 4), _abi.GDR_EINVAL),                      # misaligned
+    (dict(beta=FAKE + 2), _abi.GDR_EINVAL),
+    (dict(initial_state=FAKE + 8), _abi.GDR_EINVAL),
+    (dict(gate=_abi.GDR_GATE_NONE), _abi.GDR_EINVAL),         # log_alpha given for no gate
+    (dict(log_alpha=None), _abi.GDR_EINVAL),                  # gate without log_alpha
+    (dict(gate=7), _abi.GDR_EINVAL),
+    (dict(in_dtype=5), _abi.GDR_EINVAL),
+    (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
+    (dict(Dk=96, Dv=96), _abi.GDR_EUNSUPPORTED),
+    (dict(chunk=48), _abi.GDR_EUNSUPPORTED),
+    (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),     # fp32 inputs need Dk <= 64
+])
+def test_chunk_fwd_rejects(kw, want):
+    assert chunk(**kw) == want
+
+
+def test_chunk_fwd_empty_batch_is_a_no_op():
+    assert chunk(B=0, q=None, k=None, v=None, o=None) == _abi.GDR_OK
+    assert chunk(H=0, q=None, k=None, v=None, o=None) == _abi.GDR_OK
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(N=-1), _abi.GDR_EINVAL),
+    (dict(state=None), _abi.GDR_EINVAL),
+    (dict(state=FAKE + 4), _abi.GDR_EINVAL),
+    (dict(v=None), _abi.GDR_EINVAL),
+    (dict(gate=_abi.GDR_GATE_NONE), _abi.GDR_EINVAL),
+    (dict(Dk=128, Dv=32), _abi.GDR_EUNSUPPORTED),
+    (dict(Dk=256, Dv=256), _abi.GDR_EUNSUPPORTED),
+])
+def test_recurrent_step_rejects(kw, want):
+    assert step(**kw) == want
+
+
+def test_recurrent_step_empty_is_a_no_op():
+    assert step(N=0, q=None, k=None, v=None, state=None, o=None) == _abi.GDR_OK
