@@ -114,7 +114,7 @@ def bench_decode(w, passes, warmup_passes):
     return wall, per
 
 
-def cpu_baseline(w, batches=2):
+def cpu_baseline(w, batches=6):
     """The fp64 oracle on a bounded sample of the same workload: `batches`
     sequences x all heads x all tokens, the same seeded inputs."""
     import numpy as np  # noqa: F401

@@ -9,35 +9,47 @@
 // and the Gated DeltaNet Q&A).  For a chunk of C tokens with entering state S,
 // g = in-chunk cumulative log decay, gam = e^g, Gam_rs = e^{g_r - g_s}:
 //
-//   A   = strict_lower(diag(b) (K K^T o Gam))         (a2)
-//   T'  = (I + A)^{-1} diag(b)                         (a3, unit lower solve)
-//   P   = lower_incl(Q K^T o Gam)                      (a5)
-//   U   = T' (V - diag(gam) K S)                       (a4, written residuals)
-//   O   = diag(gam) Q S + P U                          (a6/a7)
-//   S  <- gam_last S + K^T diag(e^{g_last - g}) U      (a6, carried state)
+//   A   = strict_lower(diag(b) (K K^T o Gam))         Gram of the keys
+//   T'  = (I + A)^{-1} diag(b)                         unit-lower solve (WY)
+//   P   = lower_incl(Q K^T o Gam)                      masked scores
+//   U   = T' (V - diag(gam) K S)                       written residuals
+//   O   = diag(gam) Q S + P U                          outputs
+//   S  <- gam_last S + K^T diag(e^{g_last - g}) U      carried state
 //
-// Mapping.  One workgroup per (batch, head, Dv-slice of DVS columns); the
-// Dv columns of S, U and O are independent given K, b and g, so slices of a
-// chain never talk.  The workgroup walks the chunks in order.  Each of its
-// DVS/16 waves owns 16 state columns and keeps them in MFMA accumulators for
-// the whole sequence: every state-dependent product (K S, Q S, T'R, P U,
-// K^T U') takes its right operand straight from those accumulator registers
-// (an accumulator tile holds rows 4g..4g+3 of column l&15, which is exactly
-// what a 16x16x32 B operand needs if the k order inside each 32-block is
-// permuted; the left operands in LDS are stored with the same permutation).
-// So the serial state chain never round-trips through LDS.  The per-chunk
-// key-only work (decay cumsum, K K^T, Q K^T, the solve) is shared by the
-// waves through LDS.
+// Mapping.  One workgroup per (batch, head, Dv-slice of DVS columns): the Dv
+// columns of S, U and O are independent given K, b and g.  The workgroup is
+// a two-stage software pipeline over chunks of C = 32 tokens:
+//
+//   state waves (DVS/16 of them) each own 16 state columns and keep them in
+//     MFMA accumulators for the whole sequence.  Every state-dependent
+//     product (K S, Q S, T'R, P U, K^T U') takes its right operand straight
+//     from accumulator registers: an accumulator tile holds rows 4g..4g+3 of
+//     column l&15, which is what a 16x16x32 B operand needs once the k order
+//     inside each 32-block is permuted (the left operands in LDS are stored
+//     with the same permutation).  The serial chain never touches LDS.
+//   prep waves (4) run ahead on the key-only work: they stage chunk i+1
+//     from HBM in registers while writing chunk i to LDS with its decay
+//     cumsum, form K K^T / Q K^T with the decay (A and P) for chunk i, and
+//     solve (I + A) for chunk i-1.
+//
+// Iteration i has two phases separated by workgroup barriers:
+//   X: prep writes chunk i (+cumsum), solves chunk i-1   | state: K S, Q S, U of chunk i-2
+//   Y: prep forms A, P of chunk i                          | state: O and S update of chunk i-2
+// so chunk buffers live three iterations (triple-buffered), A and T' two.
 //
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
 // operand (S, R, U, T', P) is split into bf16 hi + lo and multiplied as
-// hi*hi + hi*lo + lo*hi (two products when the other side is exact), so the
+// hi*hi + hi*lo + lo*hi (two products when the other side is exact), so
 // products carry ~16 significant bits and accumulate in fp32.
 #include "common.h"
 #include "internal.h"
 
 namespace gdr {
 namespace {
+
+constexpr int C = 32;      // tokens per chunk
+constexpr int NPW = 4;     // prep waves
+constexpr int NBUF = 4;    // chunk buffers: a chunk is staged 3 iterations before its state pass
 
 // k order inside each 32-wide block: natural index 32kk + 16h + 4g + j lives
 // at 32kk + 8g + 4h + j, so one 16-byte LDS read returns the eight k values a
@@ -65,6 +77,21 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i receives
+// element (i & 3) of the 8-byte chunks addressed by lanes (i >> 2) + 4c,
+// c = 0..3.  Pointing lane j of a group at &X[t_(j >> 2)][c0 + 4 (j & 3)]
+// therefore hands lane i the column c0 + i of rows t_0..t_3: a transposed
+// 4x16 fragment, straight from a row-major tile.
+__device__ __forceinline__ bf16x4 ld_tr4(const bf16 *p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s *)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
+__device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6], x[7]}; }
+
 // acc += L (16x16, fp32, row-major at L[m*ldl + k]) * R (16x16, fp32, given
 // transposed: R[k][n] = RT[n*ldr + k]) to ~fp32 accuracy with two MFMAs: the
 // 32-deep k axis carries [L_hi | L_lo] against [R_hi ; R_hi], then
@@ -86,42 +113,48 @@ __device__ __forceinline__ f32x4 mm16_split(const float *L, int ldl, const float
   return mfma_bf16(a, b2, acc);
 }
 
-template <int C, int DK, int DVS>
-struct __align__(16) Smem {
+template <int DK, int DVS>
+struct __align__(16) PipeSmem {
   static constexpr int LDK = DK + 8;   // bf16 stride of [C][DK] rows (pads banks)
+  static constexpr int LDV = DVS + 8;  // bf16 stride of [C][DVS] rows
   static constexpr int LDC = C + 8;    // bf16 stride of [*][C] rows
-  static constexpr int LDA = C + 4;    // fp32 stride of [C][C] rows
-  bf16 Q[C][LDK];                      // q rows, dk permuted
-  bf16 K[C][LDK];                      // k rows, dk permuted
-  bf16 KT[DK][LDC];                    // k^T: row = dk, tokens permuted
-  bf16 VT[DVS][LDC];                   // v^T slice: row = value column, tokens natural
-  bf16 Th[C][LDC], Tl[C][LDC];         // T' = (I+A)^{-1} diag(b), cols permuted
-  bf16 Ph[C][LDC], Pl[C][LDC];         // P, cols permuted
-  float gam[C], ec[C], beta[C], g[C];  // e^g, e^{g_last-g}, b, g
-  float A[C][LDA];                     // A (strict lower), natural
-  float TT[C][LDA];                    // T^T: TT[s][r] = T[r][s]
-  float Td[C / 16][16][20];            // diagonal blocks of T, row-major
-  float X[DVS / 16][16][20];           // per-wave transposed scratch
+  struct __align__(16) Buf {           // one chunk, live for four iterations
+    bf16 Q[C][LDK];                    // q rows, dk permuted
+    bf16 K[C][LDK];                    // k rows, dk permuted
+    bf16 V[C][LDV];                    // v rows of this slice, natural order
+    bf16 Ph[C][LDC], Pl[C][LDC];       // P^T: [s][r] = P[r][s]; rows 16..31 x cols 0..15 stay zero
+    float gam[C], ec[C], beta[C], g[C];
+  };
+  Buf buf[NBUF];
+  float ATd[2][16][20];                // diagonal 16x16 blocks of A, transposed: [b][s][r] = A[16b+r][16b+s]
+  float A10[2][16][20];                // block (1,0) of A, row-major
+  bf16 Th[2][C][LDC], Tl[2][C][LDC];   // T'^T: [s][r] = T'[r][s], T' = (I+A)^{-1} diag(b);
+                                       // rows 16..31 x cols 0..15 stay zero
+  float Ost[DVS / 16][C][20];          // per-state-wave output tile, for wide stores
+  float T0T[16][20];                   // T_00^T (solver scratch, chunk being solved)
+  float T1[16][20];                    // T_11 row-major (solver scratch)
+  float X[16][20];                     // X^T (solver scratch)
 };
 
-template <int C, int DK, int DVS, typename OutT, int GATE>
-__global__ void __launch_bounds__(4 * DVS, 1)
+template <int DK, int DVS, typename OutT, int GATE>
+__global__ void __launch_bounds__(64 * (DVS / 16 + NPW), 1)
 chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ v, const float *__restrict__ beta,
                       const float *__restrict__ log_alpha, const float *initial_state,
                       OutT *__restrict__ o, float *final_state, int B, int T, int H) {
-  constexpr int NW = DVS / 16;         // waves; wave w owns value columns 16w..16w+15
-  constexpr int NT = 64 * NW;
+  constexpr int NSW = DVS / 16;        // state waves; wave w owns value columns 16w..16w+15
+  constexpr int NT = 64 * (NSW + NPW);
   constexpr int DV = DK;               // full value width (Dk == Dv)
   constexpr int NSLICE = DV / DVS;
-  constexpr int NB = C / 16;           // 16-row blocks per chunk
   constexpr int KKD = DK / 32;         // 32-deep k steps over dk
-  constexpr int KKC = C / 32;          // 32-deep k steps over tokens
-  static_assert(C == 64 && (DK == 64 || DK == 128) && (DVS == 32 || DVS == 64), "tile config");
-  using S_t = Smem<C, DK, DVS>;
-  __shared__ S_t sm;
+  constexpr int VCS = DVS / 8;         // 8-column segments of the value slice
+  static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
+  using SM = PipeSmem<DK, DVS>;
+  __shared__ SM sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: the role split below is a uniform branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
 
   // workgroup -> (chain, slice); slices of one chain share an XCD (same L2)
@@ -138,329 +171,414 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   }
   const int bb = chain / H, hh = chain % H;
-  const int col0 = slice * DVS + 16 * wave;   // first value column of this wave
-  const long tok_stride = (long)H;            // rows of one head are H apart
-
-  // zero the triangular operands once: their upper blocks are never written
-  for (int i = tid; i < C * S_t::LDC; i += NT) {
-    (&sm.Th[0][0])[i] = (bf16)0.0f;
-    (&sm.Tl[0][0])[i] = (bf16)0.0f;
-    (&sm.Ph[0][0])[i] = (bf16)0.0f;
-    (&sm.Pl[0][0])[i] = (bf16)0.0f;
-  }
-
-  // state columns col0 + lr, rows 16mb + 4lg + e, in accumulators
-  f32x4 Sacc[DK / 16];
-  {
-    const float *S0 = initial_state ? initial_state + (long)chain * DK * DV : nullptr;
-#pragma unroll
-    for (int mb = 0; mb < DK / 16; ++mb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Sacc[mb][e] = S0 ? S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr] : 0.0f;
-  }
-
   const int nchunks = (T + C - 1) / C;
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const int t0 = ci * C;
-    const int n = min(C, T - t0);
-    __syncthreads();   // previous chunk's readers are done with the shared tiles
+  const long tok0 = (long)bb * T * H + hh;   // row index of token 0 of this chain
 
-    // ---- load q, k (row-major, dk permuted) and k^T; v^T slice; b; log a ----
-    for (int it = tid; it < C / 4 * (DK / 8); it += NT) {
-      const int cs = it % (DK / 8), rgp = it / (DK / 8);
-      const int c0 = 8 * cs, r0 = 4 * rgp;
-      bf16x8 qv[4], kv[4];
+  // the upper-right 16x16 blocks of P and T' are never written: zero once
+  for (int i = tid; i < C * SM::LDC; i += NT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        if (r < n) {
-          const long off = (((long)bb * T + t0 + r) * tok_stride + hh) * DK + c0;
-          qv[i] = ld8(q + off);
-          kv[i] = ld8(k + off);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) { qv[i][j] = (bf16)0.0f; kv[i][j] = (bf16)0.0f; }
-        }
-        const int p0 = perm32(c0), p1 = perm32(c0 + 4);
-        *reinterpret_cast<bf16x4 *>(&sm.Q[r][p0]) = bf16x4{qv[i][0], qv[i][1], qv[i][2], qv[i][3]};
-        *reinterpret_cast<bf16x4 *>(&sm.Q[r][p1]) = bf16x4{qv[i][4], qv[i][5], qv[i][6], qv[i][7]};
-        *reinterpret_cast<bf16x4 *>(&sm.K[r][p0]) = bf16x4{kv[i][0], kv[i][1], kv[i][2], kv[i][3]};
-        *reinterpret_cast<bf16x4 *>(&sm.K[r][p1]) = bf16x4{kv[i][4], kv[i][5], kv[i][6], kv[i][7]};
-      }
-      const int pr = perm32(r0);   // 4 consecutive tokens stay consecutive
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<bf16x4 *>(&sm.KT[c0 + j][pr]) = bf16x4{kv[0][j], kv[1][j], kv[2][j], kv[3][j]};
+    for (int b = 0; b < NBUF; ++b) {
+      (&sm.buf[b].Ph[0][0])[i] = (bf16)0.0f;
+      (&sm.buf[b].Pl[0][0])[i] = (bf16)0.0f;
     }
-    for (int it = tid; it < C / 4 * (DVS / 8); it += NT) {
-      const int cs = it % (DVS / 8), rgp = it / (DVS / 8);
-      const int c0 = 8 * cs, r0 = 4 * rgp;
-      bf16x8 vv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        if (r < n) {
-          vv[i] = ld8(v + (((long)bb * T + t0 + r) * tok_stride + hh) * DV + slice * DVS + c0);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vv[i][j] = (bf16)0.0f;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<bf16x4 *>(&sm.VT[c0 + j][r0]) = bf16x4{vv[0][j], vv[1][j], vv[2][j], vv[3][j]};
+    for (int b = 0; b < 2; ++b) {
+      (&sm.Th[b][0][0])[i] = (bf16)0.0f;
+      (&sm.Tl[b][0][0])[i] = (bf16)0.0f;
     }
-    if (wave == 0) {
-      // in-chunk cumulative log decay (a1): inclusive scan over the wave
-      const int r = lane;   // C == 64 == wavefront
-      const long gi = ((long)bb * T + t0 + r) * tok_stride + hh;
-      float la = 0.0f, bt = 0.0f;
-      if (r < n) {
-        bt = beta[gi];
-        if (GATE == kGateScalar) la = log_alpha[gi];
-      }
+  }
+
+  // Both roles run nchunks + 3 iterations with two barriers each, so every
+  // wave executes the same sequence of workgroup barriers.
+  if (wave < NSW) {
+    // =====================================================================
+    // state waves: the serial chunk-to-chunk pass, 16 state columns each
+    // =====================================================================
+    const int col0 = slice * DVS + 16 * wave;   // first value column of this wave
+    // S columns col0 + lr, rows 16 mb + 4 lg + e
+    f32x4 Sacc[DK / 16];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(la, off, 64);
-        if (lane >= off) la += y;
-      }
-      const float glast = __shfl(la, 63, 64);
-      sm.g[r] = la;
-      sm.gam[r] = __expf(la);
-      sm.ec[r] = __expf(glast - la);
-      sm.beta[r] = bt;
+    for (int mb = 0; mb < DK / 16; ++mb) Sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (initial_state) {
+      const float *S0 = initial_state + (long)chain * DK * DV;
+#pragma unroll
+      for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr];
     }
     __syncthreads();
 
-    // ---- a2 / a5: K K^T and Q K^T, lower tiles only, with the decay ----
-    {
-      constexpr int NTILE = NB * (NB + 1) / 2;
-      for (int tt = wave; tt < 2 * NTILE; tt += NW) {
-        const bool isq = tt >= NTILE;
-        int x = isq ? tt - NTILE : tt, i = 0;
-        while (x > i) { x -= i + 1; ++i; }
-        const int j = x;   // tile (i, j), j <= i
-        const bf16(*Xr)[S_t::LDK] = isq ? sm.Q : sm.K;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < nchunks + 3; ++it) {
+      const int s = it - 3;            // chunk of this iteration
+      f32x4 QS[2];                     // carried from phase X to phase Y
+      bf16x8 Uh, Ul, Wh, Wl;
+      // ---- phase X: K S, Q S, R = V - diag(gam) K S, U = T' R ----
+      if (s >= 0) {
+        const typename SM::Buf &bs = sm.buf[s % NBUF];
+        bf16x8 Sh[KKD], Sl[KKD];
 #pragma unroll
-        for (int kk = 0; kk < KKD; ++kk)
-          acc = mfma_bf16(ld8(&Xr[16 * i + lr][32 * kk + 8 * lg]), ld8(&sm.K[16 * j + lr][32 * kk + 8 * lg]), acc);
-        const int s = 16 * j + lr;
-        const float gs = sm.g[s];
+        for (int kk = 0; kk < KKD; ++kk) {
+          bf16x4 h0, l0, h1, l1;
+          split4(Sacc[2 * kk], h0, l0);
+          split4(Sacc[2 * kk + 1], h1, l1);
+          Sh[kk] = cat(h0, h1);
+          Sl[kk] = cat(l0, l1);
+        }
+        f32x4 KS[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * i + 4 * lg + e;
-          const float dec = (GATE == kGateNone) ? 1.0f : __expf(sm.g[r] - gs);
-          if (!isq) {
-            sm.A[r][s] = (s < r) ? sm.beta[r] * acc[e] * dec : 0.0f;
-          } else {
-            const float pv = (s <= r) ? acc[e] * dec : 0.0f;
-            bf16 h, l;
-            split_bf16(pv, h, l);
-            sm.Ph[r][perm32(s)] = h;
-            sm.Pl[r][perm32(s)] = l;
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KKD; ++kk) {
+            const bf16x8 ak = ld8(&bs.K[16 * rb + lr][32 * kk + 8 * lg]);
+            const bf16x8 aq = ld8(&bs.Q[16 * rb + lr][32 * kk + 8 * lg]);
+            a1 = mfma_bf16(ak, Sh[kk], a1);
+            a2 = mfma_bf16(aq, Sh[kk], a2);
+            a1 = mfma_bf16(ak, Sl[kk], a1);
+            a2 = mfma_bf16(aq, Sl[kk], a2);
+          }
+          KS[rb] = a1;
+          QS[rb] = a2;
+        }
+        bf16x4 rh2[2], rl2[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int r0 = 16 * rb + 4 * lg;
+          // V[r0 + c][16 wave + lr], c = 0..3, by a transposing read
+          const bf16x4 vv = ld_tr4(&bs.V[r0 + (lr >> 2)][16 * wave + 4 * (lr & 3)]);
+          const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                                : *reinterpret_cast<const f32x4 *>(&bs.gam[r0]);
+          f32x4 rr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - gm4[e] * KS[rb][e];
+          split4(rr, rh2[rb], rl2[rb]);
+        }
+        const bf16x8 Rh = cat(rh2[0], rh2[1]), Rl = cat(rl2[0], rl2[1]);
+        const bf16(*Th)[SM::LDC] = sm.Th[s & 1];
+        const bf16(*Tl)[SM::LDC] = sm.Tl[s & 1];
+        bf16x4 uh[2], ul[2], wh[2], wl[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          // row 16 rb + lr of T', slots = tokens 16 h + 4 lg + c (the R rows)
+          const bf16x8 th = cat(ld_tr4(&Th[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+          const bf16x8 tl = cat(ld_tr4(&Tl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                ld_tr4(&Tl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+          f32x4 u = {0.f, 0.f, 0.f, 0.f};
+          u = mfma_bf16(th, Rh, u);
+          u = mfma_bf16(tl, Rh, u);
+          u = mfma_bf16(th, Rl, u);
+          split4(u, uh[rb], ul[rb]);
+          const f32x4 ec4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                                : *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
+          split4(u * ec4, wh[rb], wl[rb]);
+        }
+        Uh = cat(uh[0], uh[1]);
+        Ul = cat(ul[0], ul[1]);
+        Wh = cat(wh[0], wh[1]);
+        Wl = cat(wl[0], wl[1]);
+      }
+      __syncthreads();
+      // ---- phase Y: O = diag(gam) Q S + P U; S <- gam_last S + K^T U' ----
+      if (s >= 0) {
+        const typename SM::Buf &bs = sm.buf[s % NBUF];
+        const int t0 = s * C, n = min(C, T - t0);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                                : *reinterpret_cast<const f32x4 *>(&bs.gam[16 * rb + 4 * lg]);
+          f32x4 acc = gm4 * QS[rb];
+          const bf16x8 ph = cat(ld_tr4(&bs.Ph[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                ld_tr4(&bs.Ph[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+          const bf16x8 pl = cat(ld_tr4(&bs.Pl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                ld_tr4(&bs.Pl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+          acc = mfma_bf16(ph, Uh, acc);
+          acc = mfma_bf16(pl, Uh, acc);
+          acc = mfma_bf16(ph, Ul, acc);
+          // transpose through this wave's LDS tile: lane holds column lr,
+          // rows 4 lg + e; the stores below write 4 columns of one row
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.Ost[wave][16 * rb + 4 * lg + e][lr] = acc[e];
+        }
+        {
+          // rows lane/4 and 16 + lane/4, columns 4 (lane & 3) .. + 3
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int r = 16 * hf + (lane >> 2);
+            const f32x4 ov = *reinterpret_cast<const f32x4 *>(&sm.Ost[wave][r][4 * (lane & 3)]);
+            if (r < n) {
+              OutT *dst = o + (tok0 + (long)(t0 + r) * H) * DV + slice * DVS + 16 * wave + 4 * (lane & 3);
+              if constexpr (sizeof(OutT) == 4) {
+                *reinterpret_cast<f32x4 *>(dst) = ov;
+              } else {
+                *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
+              }
+            }
           }
         }
-      }
-    }
-    __syncthreads();
-
-    // ---- a3: T = (I + A)^{-1}; diagonal 16x16 blocks by forward substitution ----
-    for (int bk = wave; bk < NB; bk += NW) {
-      const int j = lr;                 // column of the block inverse
-      float x[16];
+        const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == j) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int s = 0; s < r; ++s) acc -= sm.A[16 * bk + r][16 * bk + s] * x[s];
-        x[r] = acc;
-      }
-      // lane group lg writes rows 4lg..4lg+3 of column j
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * lg + e;
-        sm.Td[bk][r][j] = x[r];
-        const float tp = x[r] * sm.beta[16 * bk + j];
-        bf16 h, l;
-        split_bf16(tp, h, l);
-        sm.Th[16 * bk + r][perm32(16 * bk + j)] = h;
-        sm.Tl[16 * bk + r][perm32(16 * bk + j)] = l;
-      }
-      *reinterpret_cast<f32x4 *>(&sm.TT[16 * bk + j][16 * bk + 4 * lg]) =
-          f32x4{x[4 * lg], x[4 * lg + 1], x[4 * lg + 2], x[4 * lg + 3]};
-    }
-    __syncthreads();
-    // off-diagonal blocks by distance d = i - j:  T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-#pragma unroll
-    for (int d = 1; d < NB; ++d) {
-      for (int jb = wave; jb < NB - d; jb += NW) {
-        const int ib = jb + d;
-        f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = jb; kb < ib; ++kb)
-          xacc = mm16_split(&sm.A[16 * ib][16 * kb], S_t::LDA, &sm.TT[16 * jb][16 * kb], S_t::LDA, xacc, lane);
-        // X^T into this wave's scratch, then T_ij = -T_ii X
-        *reinterpret_cast<f32x4 *>(&sm.X[wave][lr][4 * lg]) = xacc;
-        __builtin_amdgcn_wave_barrier();
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = mm16_split(&sm.Td[ib][0][0], 20, &sm.X[wave][0][0], 20, z, lane);
-        __builtin_amdgcn_wave_barrier();
-        const int s = 16 * jb + lr;
-        const float bs = sm.beta[s];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * ib + 4 * lg + e;
-          z[e] = -z[e];
-          bf16 h, l;
-          split_bf16(z[e] * bs, h, l);
-          sm.Th[r][perm32(s)] = h;
-          sm.Tl[r][perm32(s)] = l;
+        for (int mb = 0; mb < DK / 16; ++mb) {
+          // k^T operand (row = dk 16 mb + lr; slots = tokens 16 h + 4 lg + c,
+          // the order of the U' rows) by two transposing reads of k
+          const int dcol = perm32(16 * mb + 4 * (lr & 3));
+          const bf16x8 a = cat(ld_tr4(&bs.K[4 * lg + (lr >> 2)][dcol]),
+                               ld_tr4(&bs.K[16 + 4 * lg + (lr >> 2)][dcol]));
+          f32x4 acc = Sacc[mb] * glast;
+          acc = mfma_bf16(a, Wh, acc);
+          acc = mfma_bf16(a, Wl, acc);
+          Sacc[mb] = acc;
         }
-        *reinterpret_cast<f32x4 *>(&sm.TT[s][16 * ib + 4 * lg]) = z;
       }
       __syncthreads();
     }
 
-    // ---- serial state pass (a4, a6, a7): wave-local, state in registers ----
-    {
-      // B operands from the state accumulators (k = dk, permuted order)
-      bf16x8 Sh[KKD], Sl[KKD];
+    if (final_state) {
+      float *SF = final_state + (long)chain * DK * DV;
 #pragma unroll
-      for (int kk = 0; kk < KKD; ++kk) {
-        bf16x4 h0, l0, h1, l1;
-        split4(Sacc[2 * kk], h0, l0);
-        split4(Sacc[2 * kk + 1], h1, l1);
-        Sh[kk] = cat(h0, h1);
-        Sl[kk] = cat(l0, l1);
-      }
-      // K S and Q S  (rows = tokens of the chunk, cols = this wave's 16 columns)
-      f32x4 KS[NB], QS[NB];
+      for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KKD; ++kk) {
-          const bf16x8 ak = ld8(&sm.K[16 * rb + lr][32 * kk + 8 * lg]);
-          const bf16x8 aq = ld8(&sm.Q[16 * rb + lr][32 * kk + 8 * lg]);
-          a1 = mfma_bf16(ak, Sh[kk], a1);
-          a1 = mfma_bf16(ak, Sl[kk], a1);
-          a2 = mfma_bf16(aq, Sh[kk], a2);
-          a2 = mfma_bf16(aq, Sl[kk], a2);
-        }
-        KS[rb] = a1;
-        QS[rb] = a2;
-      }
-      // R = V - diag(gam) K S, as split B operands over tokens
-      bf16x8 Rh[KKC], Rl[KKC];
-#pragma unroll
-      for (int kk = 0; kk < KKC; ++kk) {
-        bf16x4 hh2[2], ll2[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rb = 2 * kk + hf;
-          const int r0 = 16 * rb + 4 * lg;
-          const bf16x4 vv = *reinterpret_cast<const bf16x4 *>(&sm.VT[16 * wave + lr][r0]);
-          f32x4 rr;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float gm = (GATE == kGateNone) ? 1.0f : sm.gam[r0 + e];
-            rr[e] = (float)vv[e] - gm * KS[rb][e];
-          }
-          split4(rr, hh2[hf], ll2[hf]);
-        }
-        Rh[kk] = cat(hh2[0], hh2[1]);
-        Rl[kk] = cat(ll2[0], ll2[1]);
-      }
-      // U = T' R  (T' lower triangular: row block rb needs token blocks <= rb)
-      f32x4 U[NB];
-#pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk <= rb / 2; ++kk) {
-          const bf16x8 th = ld8(&sm.Th[16 * rb + lr][32 * kk + 8 * lg]);
-          const bf16x8 tl = ld8(&sm.Tl[16 * rb + lr][32 * kk + 8 * lg]);
-          acc = mfma_bf16(th, Rh[kk], acc);
-          acc = mfma_bf16(th, Rl[kk], acc);
-          acc = mfma_bf16(tl, Rh[kk], acc);
-        }
-        U[rb] = acc;
-      }
-      // split U (for P U) and U' = diag(e^{g_last - g}) U (for the state update)
-      bf16x8 Uh[KKC], Ul[KKC], Wh[KKC], Wl[KKC];
-#pragma unroll
-      for (int kk = 0; kk < KKC; ++kk) {
-        bf16x4 uh[2], ul[2], wh[2], wl[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rb = 2 * kk + hf;
-          split4(U[rb], uh[hf], ul[hf]);
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = (GATE == kGateNone) ? U[rb][e] : sm.ec[16 * rb + 4 * lg + e] * U[rb][e];
-          split4(w, wh[hf], wl[hf]);
-        }
-        Uh[kk] = cat(uh[0], uh[1]);
-        Ul[kk] = cat(ul[0], ul[1]);
-        Wh[kk] = cat(wh[0], wh[1]);
-        Wl[kk] = cat(wl[0], wl[1]);
-      }
-      // O = diag(gam) Q S + P U, written straight from the accumulators
-#pragma unroll
-      for (int rb = 0; rb < NB; ++rb) {
-        f32x4 acc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gm = (GATE == kGateNone) ? 1.0f : sm.gam[16 * rb + 4 * lg + e];
-          acc[e] = gm * QS[rb][e];
-        }
-#pragma unroll
-        for (int kk = 0; kk <= rb / 2; ++kk) {
-          const bf16x8 ph = ld8(&sm.Ph[16 * rb + lr][32 * kk + 8 * lg]);
-          const bf16x8 pl = ld8(&sm.Pl[16 * rb + lr][32 * kk + 8 * lg]);
-          acc = mfma_bf16(ph, Uh[kk], acc);
-          acc = mfma_bf16(ph, Ul[kk], acc);
-          acc = mfma_bf16(pl, Uh[kk], acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * lg + e;
-          if (r < n) o[(((long)bb * T + t0 + r) * tok_stride + hh) * DV + col0 + lr] = from_f32<OutT>(acc[e]);
-        }
-      }
-      // S <- gam_last S + K^T U'
-      const float glast = (GATE == kGateNone) ? 1.0f : sm.gam[C - 1];
-#pragma unroll
-      for (int mb = 0; mb < DK / 16; ++mb) {
-        f32x4 acc = Sacc[mb] * glast;
-#pragma unroll
-        for (int kk = 0; kk < KKC; ++kk) {
-          const bf16x8 a = ld8(&sm.KT[16 * mb + lr][32 * kk + 8 * lg]);
-          acc = mfma_bf16(a, Wh[kk], acc);
-          acc = mfma_bf16(a, Wl[kk], acc);
-        }
-        Sacc[mb] = acc;
-      }
+        for (int e = 0; e < 4; ++e) SF[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr] = Sacc[mb][e];
     }
+    return;
   }
 
-  if (final_state) {
-    float *SF = final_state + (long)chain * DK * DV;
+  // =======================================================================
+  // prep waves: stage chunks from HBM, decay cumsum, A / P tiles, the solve
+  // =======================================================================
+  const int pw = wave - NSW;           // prep wave index 0..NPW-1
+  const int pt = tid - 64 * NSW;       // prep thread index 0..255
+  // q/k item = a 4-token x 8-column block of k (pt < NI) or q (NI <= pt <
+  // 2 NI), adjacent lanes on adjacent column segments (128-byte row runs);
+  // v item = one 8-column segment of one token of this slice
+  constexpr int DCS = DK / 8;          // 8-column segments of a q/k row
+  constexpr int NI = (C / 4) * DCS;    // items per matrix (<= 128)
+  constexpr int NV = C * VCS;          // v items (<= 256)
+  static_assert(2 * NI <= 64 * NPW && NV <= 64 * NPW, "staging items exceed the prep threads");
+  const bool has_qk = pt < 2 * NI;
+  const bool is_k = pt < NI;
+  const int item = is_k ? pt : pt - NI;
+  const int it_r0 = 4 * (item / DCS), it_c0 = 8 * (item % DCS);
+  const bool has_v = pt < NV;
+  const int v_r = pt / VCS, v_c0 = 8 * (pt % VCS);
+  // token t of this chain is `base + t * stride`
+  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + it_c0;
+  const bf16 *v_base = v + tok0 * DV + slice * DVS + v_c0;
+  const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
+  bf16x8 stg[4], stgv;
+  float stg_b = 0.f, stg_la = 0.f;
+
+  // Loads of rows past the end of the sequence read the last valid row
+  // instead (always in bounds) and are zeroed when written to LDS.
+  auto stage_chunk = [&](int j) {
+    const int t0 = j * C, last = T - 1;
+    if (t0 + C <= T) {               // whole chunk in range (uniform)
+      if (has_qk) {
+        const bf16 *src = qk_base + (long)(t0 + it_r0) * qk_stride;
 #pragma unroll
-    for (int mb = 0; mb < DK / 16; ++mb)
+        for (int i = 0; i < 4; ++i) stg[i] = ld8(src + i * qk_stride);
+      }
+      if (has_v) stgv = ld8(v_base + (long)(t0 + v_r) * v_stride);
+      if (pt < C) {
+        const long ri = tok0 + (long)(t0 + pt) * H;
+        stg_b = beta[ri];
+        stg_la = (GATE == kGateScalar) ? log_alpha[ri] : 0.0f;
+      }
+    } else {
+      if (has_qk) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) SF[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr] = Sacc[mb][e];
+        for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + it_r0 + i, last) * qk_stride);
+      }
+      if (has_v) stgv = ld8(v_base + (long)min(t0 + v_r, last) * v_stride);
+      if (pt < C) {
+        const long ri = tok0 + (long)min(t0 + pt, last) * H;
+        stg_b = beta[ri];
+        stg_la = (GATE == kGateScalar) ? log_alpha[ri] : 0.0f;
+      }
+    }
+  };
+  auto zero_if = [](bf16x8 x, bool z) -> bf16x8 {
+    if (z) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
+    }
+    return x;
+  };
+
+  if (nchunks > 0) stage_chunk(0);
+  __syncthreads();
+
+  for (int it = 0; it < nchunks + 3; ++it) {
+    // ---- phase X: write chunk it (+ decay cumsum), stage chunk it+1,
+    //      A / P tiles of chunk it-1, T10 of chunk it-2 ----
+    if (it < nchunks) {
+      typename SM::Buf &bf = sm.buf[it % NBUF];
+      const int n = min(C, T - it * C);
+      if (n < C) {                     // ragged last chunk: zero the padding rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stg[i] = zero_if(stg[i], it_r0 + i >= n);
+        stgv = zero_if(stgv, v_r >= n);
+      }
+      if (has_qk) {
+        bf16(*dst)[SM::LDK] = is_k ? bf.K : bf.Q;
+        const int p0 = perm32(it_c0), p1 = perm32(it_c0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<bf16x4 *>(&dst[it_r0 + i][p0]) = lo4(stg[i]);
+          *reinterpret_cast<bf16x4 *>(&dst[it_r0 + i][p1]) = hi4(stg[i]);
+        }
+      }
+      if (has_v) *reinterpret_cast<bf16x8 *>(&bf.V[v_r][v_c0]) = stgv;
+      if (pw == 0) {
+        // in-chunk cumulative log decay: inclusive scan over lanes 0..C-1;
+        // padded tokens carry log a = 0 and b = 0
+        float la = (lane < n) ? stg_la : 0.0f;
+#pragma unroll
+        for (int off = 1; off < C; off <<= 1) {
+          const float y = __shfl_up(la, off, 64);
+          if (lane >= off) la += y;
+        }
+        const float glast = __shfl(la, C - 1, 64);
+        if (lane < C) {
+          bf.g[lane] = la;
+          bf.gam[lane] = __expf(la);
+          bf.ec[lane] = __expf(glast - la);
+          bf.beta[lane] = (lane < n) ? stg_b : 0.0f;
+        }
+      }
+      if (it + 1 < nchunks) stage_chunk(it + 1);
+    }
+    if ((pw == 1 || pw == 2) && it >= 1 && it - 1 < nchunks) {
+      // lower 16x16 tiles of K K^T (wave 1) or Q K^T (wave 2) of chunk it-1,
+      // with the decay: A (strict lower, times b) and P (lower incl.)
+      const int j = it - 1;
+      typename SM::Buf &bf = sm.buf[j % NBUF];
+      const bool isq = pw == 2;
+      const bf16(*Xr)[SM::LDK] = isq ? bf.Q : bf.K;
+      constexpr int TI[3] = {0, 1, 1}, TJ[3] = {0, 1, 0};
+      f32x4 acc[3];
+#pragma unroll
+      for (int tt = 0; tt < 3; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KKD; ++kk) {
+        const bf16x8 x0 = ld8(&Xr[lr][32 * kk + 8 * lg]);
+        const bf16x8 x1 = ld8(&Xr[16 + lr][32 * kk + 8 * lg]);
+        const bf16x8 k0 = ld8(&bf.K[lr][32 * kk + 8 * lg]);
+        const bf16x8 k1 = ld8(&bf.K[16 + lr][32 * kk + 8 * lg]);
+        acc[0] = mfma_bf16(x0, k0, acc[0]);
+        acc[1] = mfma_bf16(x1, k1, acc[1]);
+        acc[2] = mfma_bf16(x1, k0, acc[2]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 3; ++tt) {
+        const int sc = 16 * TJ[tt] + lr;
+        const int r0 = 16 * TI[tt] + 4 * lg;
+        const float gs = bf.g[sc];
+        const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&bf.g[r0]);
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dec = (GATE == kGateNone) ? 1.0f : __expf(gr4[e] - gs);
+          val[e] = acc[tt][e] * dec;
+        }
+        if (!isq) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.beta[r0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? b4[e] * val[e] : 0.0f;
+          if (TI[tt] == TJ[tt]) {
+            *reinterpret_cast<f32x4 *>(&sm.ATd[TI[tt]][lr][4 * lg]) = val;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.A10[j & 1][4 * lg + e][lr] = val[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? val[e] : 0.0f;
+          bf16x4 h4, l4;
+          split4(val, h4, l4);
+          *reinterpret_cast<bf16x4 *>(&bf.Ph[sc][r0]) = h4;
+          *reinterpret_cast<bf16x4 *>(&bf.Pl[sc][r0]) = l4;
+        }
+      }
+    }
+    if (pw == 3 && it >= 2 && it - 2 < nchunks) {
+      // T10 = -T11 (A10 T00) for chunk it-2 (its diagonal blocks were solved
+      // in the previous phase Y)
+      const int j = it - 2;
+      f32x4 xa = mm16_split(&sm.A10[j & 1][0][0], 20, &sm.T0T[0][0], 20,
+                            f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+      *reinterpret_cast<f32x4 *>(&sm.X[lr][4 * lg]) = xa;   // X^T
+      f32x4 z = mm16_split(&sm.T1[0][0], 20, &sm.X[0][0], 20, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+      const float bc = sm.buf[j % NBUF].beta[lr];
+      bf16x4 h4, l4;
+      split4(-z * bc, h4, l4);
+      *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;
+      *reinterpret_cast<bf16x4 *>(&sm.Tl[j & 1][lr][16 + 4 * lg]) = l4;
+    }
+    __syncthreads();
+
+    // ---- phase Y: diagonal blocks of T = (I + A)^{-1} for chunk it-1 ----
+    if (pw == 3 && it >= 1 && it - 1 < nchunks) {
+      // lane = (block, column); right-looking forward substitution: once x_s
+      // is final it updates all later rows, so the dependent chain is one
+      // FMA per step
+      const int j = it - 1;
+      const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
+      const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+      f32x4 cur[4], nxt[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) cur[q4] = *reinterpret_cast<const f32x4 *>(&At[0][4 * q4]);
+#pragma unroll
+      for (int s2 = 0; s2 < 15; ++s2) {
+        if (s2 + 1 < 15) {
+#pragma unroll
+          for (int q4 = (s2 + 2) / 4; q4 < 4; ++q4)
+            nxt[q4] = *reinterpret_cast<const f32x4 *>(&At[s2 + 1][4 * q4]);
+        }
+#pragma unroll
+        for (int r = s2 + 1; r < 16; ++r) x[r] -= cur[r / 4][r % 4] * x[s2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+      }
+      if (lane < 32) {   // lanes 32..63 hold duplicates
+        const float bcol = sm.buf[j % NBUF].beta[o0 + col];
+        bf16x8 h8[2], l8[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          bf16 h, l;
+          split_bf16(x[r] * bcol, h, l);
+          h8[r / 8][r % 8] = h;
+          l8[r / 8][r % 8] = l;
+        }
+        // T'[o0 + r][o0 + col] for r = 0..15 is row o0 + col of T'^T
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          *reinterpret_cast<bf16x8 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) = h8[hf];
+          *reinterpret_cast<bf16x8 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) = l8[hf];
+        }
+        if (blk == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sm.T1[r][col] = x[r];
+        } else {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4 *>(&sm.T0T[col][4 * q4]) =
+                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
 template <int DK, int DVS, typename OutT, int GATE>
 hipError_t launch_cfg(const ChunkArgs &a) {
-  constexpr int C = 64;
   const int nslice = DK / DVS;
-  dim3 grid((unsigned)(a.B * a.H * nslice)), block(4 * DVS);
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<C, DK, DVS, OutT, GATE>), grid, block, 0, a.stream,
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE>), grid, block, 0, a.stream,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
                      a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
   return hipGetLastError();
@@ -480,13 +598,14 @@ hipError_t by_out(const ChunkArgs &a) {
 }  // namespace
 
 bool chunk_fwd_bf16_supported(const ChunkArgs &a) {
-  return a.in_bf16 && (a.D == 128 || a.D == 64) && (a.chunk == 0 || a.chunk == 64) &&
-         a.gate != kGateChannel;
+  // the kernel's chunk is 32 tokens; a requested chunk size only changes
+  // rounding, so 0, 16, 32 and 64 all map here
+  return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate != kGateChannel;
 }
 
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {
-  // 64 value columns per workgroup fills the chip once there are >= 256
-  // (chain, slice) pairs; fewer chains use 32-column slices for more workgroups.
+  // 64 value columns per workgroup once there are >= 256 (chain, slice)
+  // pairs to fill the chip; fewer chains use 32-column slices
   const long chains = (long)a.B * a.H;
   if (a.D == 128) {
     if (chains * 2 >= 256) return by_out<128, 64>(a);

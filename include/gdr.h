@@ -29,8 +29,8 @@
  *    finite and <= 0 (-inf is not supported; a large negative value such as
  *    -50 gives a clean hard reset), beta is finite.  Non-finite inputs
  *    propagate only into the (batch, head) chain they belong to.
- *  - q, k, v and every state pointer must be 16-byte aligned; beta and
- *    log_alpha 4-byte aligned; o aligned to its element size.
+ *  - q, k, v, o and every state pointer must be 16-byte aligned; beta and
+ *    log_alpha 4-byte aligned.
  */
 #ifndef GDR_H_
 #define GDR_H_
