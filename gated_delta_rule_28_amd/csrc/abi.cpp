@@ -70,6 +70,8 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   }
   int st = check_common(Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, log_alpha, o);
   if (st != GDR_OK) return st;
+  // per-channel log decays are read as rows of Dk floats with 16-byte vectors
+  if (gate == GDR_GATE_CHANNEL && !aligned16(log_alpha)) return GDR_EINVAL;
 
   gdr::ChunkArgs a;
   a.B = B; a.T = T; a.H = H; a.D = Dk; a.chunk = chunk;
@@ -81,6 +83,7 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
 
   hipError_t e;
   if (gdr::chunk_fwd_bf16_supported(a)) e = gdr::launch_chunk_fwd_bf16(a);
+  else if (gdr::chunk_fwd_kda_supported(a)) e = gdr::launch_chunk_fwd_kda(a);
   else if (gdr::chunk_fwd_small_supported(a)) e = gdr::launch_chunk_fwd_small(a);
   else return GDR_EUNSUPPORTED;
   return e == hipSuccess ? GDR_OK : GDR_EHIP;

@@ -1,0 +1,487 @@
+// Chunkwise KDA forward (per-channel decay), bf16 q/k/v, fp32 state, MFMA (gfx950).
+//
+// Method.  S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
+// o_t = S_t^T q_t, a_t in [0,1]^{d_k} (page "NLP——线性注意力相关总结", section
+// "Kimi Delta Attention (KDA)"), evaluated chunkwise with the WY form and a
+// triangular solve (xhh.club digest "Transformer 入坑笔记（五）", KDA Q&A).
+// Per chunk of C = 16 tokens, entering state S, G = in-chunk cumulative
+// log decay per (token, channel), g_last its last row:
+//
+//   A_rs = b_r sum_c k_rc k_sc e^{G_rc - G_sc}   (s < r)      Gram
+//   P_rs =     sum_c q_rc k_sc e^{G_rc - G_sc}   (s <= r)     masked scores
+//   T'   = (I + A)^{-1} diag(b)
+//   U    = T' (V - (K o e^G) S)
+//   O    = (Q o e^G) S + P U
+//   S   <- Diag(e^{g_last}) S + (K o e^{g_last - G})^T U
+//
+// Every decay factor in the state products is <= 1 (G is relative to the
+// chunk start and decreasing), so K o e^G, Q o e^G and K o e^{g_last - G}
+// never overflow.  They are not exact bf16 values, so the state products
+// use three MFMAs (hi*hi + hi*lo + lo*hi).
+//
+// The in-chunk Gram and scores need e^{G_r - G_s} per channel.  The page
+// digest notes that these decays can be tiny, so direct division is
+// unstable and a log-space, two-level scheme is used.  Here the factors are
+// taken about the chunk's middle token m: e^{G_r - G_m} and e^{G_m - G_s}
+// are each at most e^{8 max|log a|}, so for |log a| <= 10 the factored
+// operands stay inside the fp32/bf16 range and the Gram is two MFMA
+// products.  A chunk holding any |log a| > 10 (a near-hard reset) takes an
+// exact path instead: every (r, s, c) decay is formed directly in fp32.
+//
+// Mapping and pipeline as in the scalar-gate kernel: one workgroup per
+// (batch, head, Dv slice); DVS/16 state waves keep the state in MFMA
+// accumulators; 4 prep waves run two chunks ahead:
+//   X(i): stage chunk i (raw q/k/v/log a), derive the decayed operands of i-1
+//   Y(i): cumsum of chunk i; Gram + solve (wave 2) and scores (wave 3) of i-1
+//   state: chunk i-2.
+#include "common.h"
+#include "internal.h"
+#include "mfma_util.h"
+
+namespace gdr {
+namespace {
+
+constexpr int KC = 16;                    // tokens per chunk
+constexpr int KNPW = 4;                   // prep waves
+constexpr float kMaxFactoredLog = 10.0f;  // |log a| bound of the factored in-chunk Gram
+
+template <int DK, int DVS>
+struct __align__(16) KdaSmem {
+  static constexpr int LDK = DK + 8;      // bf16 stride of [16][DK] tiles
+  static constexpr int LDG = DK + 4;      // fp32 stride of G
+  static constexpr int LDV = DVS + 8;     // bf16 stride of v rows
+  static constexpr int LDT = KC + 8;      // bf16 stride of transposed 16x16 tiles
+  struct __align__(16) Raw {              // staged chunk, natural channel order
+    bf16 Q[KC][LDK], K[KC][LDK];
+    float G[KC][LDG];                     // log a, then its in-chunk cumulative sum
+    float beta[KC];
+    int extreme;                          // some |log a| > kMaxFactoredLog
+  };
+  struct __align__(16) Der {              // state-side operands of one chunk
+    bf16 Kh[KC][LDK], Kl[KC][LDK];        // K o e^G, dk permuted
+    bf16 Qh[KC][LDK], Ql[KC][LDK];        // Q o e^G, dk permuted
+    bf16 Ch[KC][LDK], Cl[KC][LDK];        // K o e^{g_last - G}, natural order
+    bf16 Ph[KC][LDT], Pl[KC][LDT];        // P^T: [s][r] = P[r][s]
+    float egl[DK];                        // e^{g_last}
+  };
+  Raw raw[2];
+  bf16 V[3][KC][LDV];                     // v rows of this slice, natural order
+  Der der[2];
+  // factored operands of the in-chunk Gram, reference token m = 7
+  bf16 Lkh[KC][LDK], Lkl[KC][LDK];        // K o e^{G - G_m}
+  bf16 Lqh[KC][LDK], Lql[KC][LDK];        // Q o e^{G - G_m}
+  bf16 Rkh[KC][LDK], Rkl[KC][LDK];        // K o e^{G_m - G}
+  float AT[16][20];                       // A^T for the solve
+  bf16 Th[KC][LDT], Tl[KC][LDT];          // T'^T
+  float Ost[DVS / 16][KC][20];            // per-state-wave output tile
+};
+
+template <int DK, int DVS, typename OutT>
+__global__ void __launch_bounds__(64 * (DVS / 16 + KNPW), 1)
+chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                     const bf16 *__restrict__ v, const float *__restrict__ beta,
+                     const float *__restrict__ log_alpha, const float *initial_state,
+                     OutT *__restrict__ o, float *final_state, int B, int T, int H) {
+  constexpr int NSW = DVS / 16;
+  constexpr int NT = 64 * (NSW + KNPW);
+  constexpr int DV = DK;
+  constexpr int NSLICE = DV / DVS;
+  constexpr int KKD = DK / 32;
+  static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
+  using SM = KdaSmem<DK, DVS>;
+  __shared__ SM sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+
+  const int nchain = B * H;
+  int chain, slice;
+  {
+    const int w = blockIdx.x;
+    if ((nchain & 7) == 0) {
+      chain = ((w >> 3) / NSLICE) * 8 + (w & 7);
+      slice = (w >> 3) % NSLICE;
+    } else {
+      chain = w / NSLICE;
+      slice = w % NSLICE;
+    }
+  }
+  const int bb = chain / H, hh = chain % H;
+  const int nchunks = (T + KC - 1) / KC;
+  const long tok0 = (long)bb * T * H + hh;
+
+  const bf16x4 zero4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+
+  if (wave < NSW) {
+    // =====================================================================
+    // state waves
+    // =====================================================================
+    const int col0 = slice * DVS + 16 * wave;
+    f32x4 Sacc[DK / 16];
+#pragma unroll
+    for (int mb = 0; mb < DK / 16; ++mb) Sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (initial_state) {
+      const float *S0 = initial_state + (long)chain * DK * DV;
+#pragma unroll
+      for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr];
+    }
+    __syncthreads();
+
+    for (int it = 0; it < nchunks + 2; ++it) {
+      const int s = it - 2;
+      f32x4 QS;
+      bf16x4 uh4, ul4;
+      if (s >= 0) {
+        // ---- X: K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
+        const typename SM::Der &d = sm.der[s & 1];
+        bf16x8 Sh[KKD], Sl[KKD];
+#pragma unroll
+        for (int kk = 0; kk < KKD; ++kk) {
+          bf16x4 h0, l0, h1, l1;
+          split4(Sacc[2 * kk], h0, l0);
+          split4(Sacc[2 * kk + 1], h1, l1);
+          Sh[kk] = cat(h0, h1);
+          Sl[kk] = cat(l0, l1);
+        }
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KKD; ++kk) {
+          const bf16x8 kh = ld8(&d.Kh[lr][32 * kk + 8 * lg]);
+          const bf16x8 kl = ld8(&d.Kl[lr][32 * kk + 8 * lg]);
+          const bf16x8 qh = ld8(&d.Qh[lr][32 * kk + 8 * lg]);
+          const bf16x8 ql = ld8(&d.Ql[lr][32 * kk + 8 * lg]);
+          a1 = mfma_bf16(kh, Sh[kk], a1);
+          a2 = mfma_bf16(qh, Sh[kk], a2);
+          a1 = mfma_bf16(kh, Sl[kk], a1);
+          a2 = mfma_bf16(qh, Sl[kk], a2);
+          a1 = mfma_bf16(kl, Sh[kk], a1);
+          a2 = mfma_bf16(ql, Sh[kk], a2);
+        }
+        QS = a2;
+        // V[4 lg + c][16 wave + lr] by a transposing read
+        const bf16x4 vv = ld_tr4(&sm.V[s % 3][4 * lg + (lr >> 2)][16 * wave + 4 * (lr & 3)]);
+        f32x4 rr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - a1[e];
+        bf16x4 rh4, rl4;
+        split4(rr, rh4, rl4);
+        // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
+        const bf16x8 ta = cat(ld_tr4(&sm.Th[4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                              ld_tr4(&sm.Tl[4 * lg + (lr >> 2)][4 * (lr & 3)]));
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        u = mfma_bf16(ta, cat(rh4, rh4), u);
+        u = mfma_bf16(ta, cat(rl4, zero4), u);
+        split4(u, uh4, ul4);
+      }
+      __syncthreads();
+      if (s >= 0) {
+        // ---- Y: O = Q^ S + P U; S <- Diag(e^{g_last}) S + (K o e^{g_last-G})^T U ----
+        const typename SM::Der &d = sm.der[s & 1];
+        const int t0 = s * KC, n = min(KC, T - t0);
+        const bf16x8 pa = cat(ld_tr4(&d.Ph[4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                              ld_tr4(&d.Pl[4 * lg + (lr >> 2)][4 * (lr & 3)]));
+        f32x4 acc = QS;
+        acc = mfma_bf16(pa, cat(uh4, uh4), acc);
+        acc = mfma_bf16(pa, cat(ul4, zero4), acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Ost[wave][4 * lg + e][lr] = acc[e];
+        {
+          const int r = lane >> 2;
+          const f32x4 ov = *reinterpret_cast<const f32x4 *>(&sm.Ost[wave][r][4 * (lane & 3)]);
+          if (r < n) {
+            OutT *dst = o + (tok0 + (long)(t0 + r) * H) * DV + col0 + 4 * (lane & 3);
+            if constexpr (sizeof(OutT) == 4) {
+              *reinterpret_cast<f32x4 *>(dst) = ov;
+            } else {
+              *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
+            }
+          }
+        }
+        const bf16x8 b1 = cat(uh4, uh4), b2 = cat(ul4, zero4);
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb) {
+          const f32x4 eg4 = *reinterpret_cast<const f32x4 *>(&d.egl[16 * mb + 4 * lg]);
+          const int c0 = 16 * mb + 4 * (lr & 3);
+          const bf16x8 a = cat(ld_tr4(&d.Ch[4 * lg + (lr >> 2)][c0]),
+                               ld_tr4(&d.Cl[4 * lg + (lr >> 2)][c0]));
+          f32x4 sa = Sacc[mb] * eg4;
+          sa = mfma_bf16(a, b1, sa);
+          sa = mfma_bf16(a, b2, sa);
+          Sacc[mb] = sa;
+        }
+      }
+      __syncthreads();
+    }
+
+    if (final_state) {
+      float *SF = final_state + (long)chain * DK * DV;
+#pragma unroll
+      for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) SF[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr] = Sacc[mb][e];
+    }
+    return;
+  }
+
+  // =======================================================================
+  // prep waves
+  // =======================================================================
+  const int pw = wave - NSW;
+  const int pt = tid - 64 * NSW;       // 0..255
+  // staging items: q/k = 4 tokens x 8 channels (pt < 2 NI); log a = 4 channels
+  // of one token (two per thread); v = 8 columns of one token; beta pt < 16
+  constexpr int DCS = DK / 8;
+  constexpr int NI = (KC / 4) * DCS;   // <= 64
+  constexpr int VCS = DVS / 8;
+  constexpr int NV = KC * VCS;         // <= 128
+  constexpr int NLA = KC * DK / 4;     // f32x4 items of log a (<= 512)
+  static_assert(2 * NI <= 256 && NV <= 128 && NLA <= 512, "staging items");
+  const bool has_qk = pt < 2 * NI;
+  const bool is_k = pt < NI;
+  const int item = is_k ? pt : pt - NI;
+  const int it_r0 = 4 * (item / DCS), it_c0 = 8 * (item % DCS);
+  const int vi = pt - 128;
+  const bool has_v = vi >= 0 && vi < NV;
+  const int v_r = vi / VCS, v_c0 = 8 * (vi % VCS);
+  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + it_c0;
+  const bf16 *v_base = v + tok0 * DV + slice * DVS + v_c0;
+  const float *la_base = log_alpha + tok0 * DK;
+  const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
+  bf16x8 stg[4], stgv;
+  f32x4 stgl[2];
+  float stg_b = 0.f;
+
+  auto stage_chunk = [&](int j) {
+    const int t0 = j * KC, last = T - 1;
+    if (has_qk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + it_r0 + i, last) * qk_stride);
+    }
+    if (has_v) stgv = ld8(v_base + (long)min(t0 + v_r, last) * v_stride);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int li = pt + 256 * h2;
+      if (li < NLA) {
+        const int r = li / (DK / 4), c4 = 4 * (li % (DK / 4));
+        stgl[h2] = *reinterpret_cast<const f32x4 *>(la_base + (long)min(t0 + r, last) * qk_stride + c4);
+      }
+    }
+    if (pt < KC) stg_b = beta[tok0 + (long)min(t0 + pt, last) * H];
+  };
+
+  if (nchunks > 0) stage_chunk(0);
+  __syncthreads();
+
+  for (int it = 0; it < nchunks + 2; ++it) {
+    // ================= phase X =================
+    if (it < nchunks) {
+      // write staged chunk it; padding tokens (past T) become zeros with log a = 0
+      typename SM::Raw &rw = sm.raw[it & 1];
+      const int n = min(KC, T - it * KC);
+      if (has_qk) {
+        bf16(*dst)[SM::LDK] = is_k ? rw.K : rw.Q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8 x = stg[i];
+          if (it_r0 + i >= n) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
+          }
+          *reinterpret_cast<bf16x8 *>(&dst[it_r0 + i][it_c0]) = x;
+        }
+      }
+      if (has_v) {
+        bf16x8 x = stgv;
+        if (v_r >= n) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
+        }
+        *reinterpret_cast<bf16x8 *>(&sm.V[it % 3][v_r][v_c0]) = x;
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int li = pt + 256 * h2;
+        if (li < NLA) {
+          const int r = li / (DK / 4), c4 = 4 * (li % (DK / 4));
+          *reinterpret_cast<f32x4 *>(&rw.G[r][c4]) = (r < n) ? stgl[h2] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      if (pt < KC) rw.beta[pt] = (pt < n) ? stg_b : 0.0f;
+      if (pt == 0) rw.extreme = 0;
+      if (it + 1 < nchunks) stage_chunk(it + 1);
+    }
+    if (it >= 1 && it - 1 < nchunks) {
+      // derive the decayed operands of chunk j = it - 1 (its G was summed in
+      // the previous phase Y); thread = (channel pair, group of tokens)
+      const int j = it - 1;
+      const typename SM::Raw &rw = sm.raw[j & 1];
+      typename SM::Der &d = sm.der[j & 1];
+      constexpr int NCP = DK / 2;                 // channel pairs
+      constexpr int TPG = KC * NCP / 256;         // tokens per thread
+      const int cp = pt % NCP, tq = pt / NCP;
+      const int c0 = 2 * cp;
+      const f32x2 gm = *reinterpret_cast<const f32x2 *>(&rw.G[7][c0]);
+      const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
+      if (tq == 0) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
+      const int pc = perm32(c0);
+      auto put2 = [](bf16 (*hi)[SM::LDK], bf16 (*lo)[SM::LDK], int r, int c, float x0, float x1) {
+        bf16 h0, l0, h1, l1;
+        split_bf16(x0, h0, l0);
+        split_bf16(x1, h1, l1);
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<bf16x2 *>(&hi[r][c]) = bf16x2{h0, h1};
+        *reinterpret_cast<bf16x2 *>(&lo[r][c]) = bf16x2{l0, l1};
+      };
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        const int r = TPG * tq + i;
+        const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+        const float k0 = (float)rw.K[r][c0], k1 = (float)rw.K[r][c0 + 1];
+        const float q0 = (float)rw.Q[r][c0], q1 = (float)rw.Q[r][c0 + 1];
+        const float e0 = __expf(g[0]), e1 = __expf(g[1]);
+        const float c0e = __expf(gl[0] - g[0]), c1e = __expf(gl[1] - g[1]);
+        const float m0 = __expf(g[0] - gm[0]), m1 = __expf(g[1] - gm[1]);
+        const float n0 = __expf(gm[0] - g[0]), n1 = __expf(gm[1] - g[1]);
+        put2(d.Kh, d.Kl, r, pc, k0 * e0, k1 * e1);
+        put2(d.Qh, d.Ql, r, pc, q0 * e0, q1 * e1);
+        put2(d.Ch, d.Cl, r, c0, k0 * c0e, k1 * c1e);
+        put2(sm.Lkh, sm.Lkl, r, c0, k0 * m0, k1 * m1);
+        put2(sm.Lqh, sm.Lql, r, c0, q0 * m0, q1 * m1);
+        put2(sm.Rkh, sm.Rkl, r, c0, k0 * n0, k1 * n1);
+      }
+    }
+    __syncthreads();
+
+    // ================= phase Y =================
+    if (it < nchunks && pt < DK) {
+      // in-chunk cumulative log decay, one channel per thread; flag chunks
+      // whose factored Gram could leave the floating-point range
+      typename SM::Raw &rw = sm.raw[it & 1];
+      float acc = 0.0f, amax = 0.0f;
+#pragma unroll
+      for (int r = 0; r < KC; ++r) {
+        const float la = rw.G[r][pt];
+        amax = fmaxf(amax, fabsf(la));
+        acc += la;
+        rw.G[r][pt] = acc;
+      }
+      if (amax > kMaxFactoredLog) atomicOr(&rw.extreme, 1);
+    }
+    if ((pw == 2 || pw == 3) && it >= 1 && it - 1 < nchunks) {
+      // Gram (wave 2: A, then the solve) or scores (wave 3: P) of chunk it-1
+      const int j = it - 1;
+      const typename SM::Raw &rw = sm.raw[j & 1];
+      const bool isq = pw == 3;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (!rw.extreme) {
+        const bf16(*Lh)[SM::LDK] = isq ? sm.Lqh : sm.Lkh;
+        const bf16(*Ll)[SM::LDK] = isq ? sm.Lql : sm.Lkl;
+#pragma unroll
+        for (int kk = 0; kk < KKD; ++kk) {
+          const bf16x8 ah = ld8(&Lh[lr][32 * kk + 8 * lg]);
+          const bf16x8 al = ld8(&Ll[lr][32 * kk + 8 * lg]);
+          const bf16x8 bh = ld8(&sm.Rkh[lr][32 * kk + 8 * lg]);
+          const bf16x8 bl = ld8(&sm.Rkl[lr][32 * kk + 8 * lg]);
+          acc = mfma_bf16(ah, bh, acc);
+          acc = mfma_bf16(ah, bl, acc);
+          acc = mfma_bf16(al, bh, acc);
+        }
+      } else {
+        // exact: every decay e^{G_rc - G_sc} formed directly (s <= r only)
+        const bf16(*X)[SM::LDK] = isq ? rw.Q : rw.K;
+        const int sc = lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * lg + e;
+          float sum = 0.0f;
+          if (sc <= r) {
+            for (int c = 0; c < DK; ++c)
+              sum += (float)X[r][c] * (float)rw.K[sc][c] * __expf(rw.G[r][c] - rw.G[sc][c]);
+          }
+          acc[e] = sum;
+        }
+      }
+      const int sc = lr, r0 = 4 * lg;
+      if (isq) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
+        bf16x4 h4, l4;
+        split4(val, h4, l4);
+        *reinterpret_cast<bf16x4 *>(&sm.der[j & 1].Ph[sc][r0]) = h4;
+        *reinterpret_cast<bf16x4 *>(&sm.der[j & 1].Pl[sc][r0]) = l4;
+      } else {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? rw.beta[r0 + e] * acc[e] : 0.0f;
+        *reinterpret_cast<f32x4 *>(&sm.AT[sc][r0]) = val;   // AT[s][r] = A[r][s]
+        // T = (I + A)^{-1}, lane = column; right-looking forward substitution
+        const int col = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < 15; ++s2) {
+          f32x4 a4[4];
+#pragma unroll
+          for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4) a4[q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
+#pragma unroll
+          for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[r / 4][r % 4] * x[s2];
+        }
+        if (lane < 16) {
+          const float bcol = rw.beta[col];
+          bf16x8 h8[2], l8[2];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            bf16 h, l;
+            split_bf16(x[r] * bcol, h, l);
+            h8[r / 8][r % 8] = h;
+            l8[r / 8][r % 8] = l;
+          }
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            *reinterpret_cast<bf16x8 *>(&sm.Th[col][8 * hf]) = h8[hf];
+            *reinterpret_cast<bf16x8 *>(&sm.Tl[col][8 * hf]) = l8[hf];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int DK, int DVS, typename OutT>
+hipError_t launch_kda(const ChunkArgs &a) {
+  const int nslice = DK / DVS;
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + KNPW));
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT>), grid, block, 0, a.stream,
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
+                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
+  return hipGetLastError();
+}
+
+template <int DK, int DVS>
+hipError_t kda_by_out(const ChunkArgs &a) {
+  return a.out_bf16 ? launch_kda<DK, DVS, bf16>(a) : launch_kda<DK, DVS, float>(a);
+}
+
+}  // namespace
+
+bool chunk_fwd_kda_supported(const ChunkArgs &a) {
+  return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate == kGateChannel;
+}
+
+hipError_t launch_chunk_fwd_kda(const ChunkArgs &a) {
+  const long chains = (long)a.B * a.H;
+  if (a.D == 128) {
+    if (chains * 2 >= 256) return kda_by_out<128, 64>(a);
+    return kda_by_out<128, 32>(a);
+  }
+  if (chains >= 256) return kda_by_out<64, 64>(a);
+  return kda_by_out<64, 32>(a);
+}
+
+}  // namespace gdr

@@ -33,6 +33,9 @@ hipError_t launch_recurrent_step(const RecurrentArgs &a);
 // bf16 q/k/v, MFMA path (D = 128 and 64)
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a);
 bool chunk_fwd_bf16_supported(const ChunkArgs &a);
+// bf16 q/k/v with the per-channel gate, MFMA path (D = 128 and 64)
+hipError_t launch_chunk_fwd_kda(const ChunkArgs &a);
+bool chunk_fwd_kda_supported(const ChunkArgs &a);
 // plain fp32 arithmetic path: fp32 or bf16 q/k/v, D <= 64, every gate
 hipError_t launch_chunk_fwd_small(const ChunkArgs &a);
 bool chunk_fwd_small_supported(const ChunkArgs &a);

@@ -1,0 +1,70 @@
+// MFMA operand helpers shared by the chunkwise kernels (gfx950).
+#pragma once
+
+#include "common.h"
+
+namespace gdr {
+
+// k order inside each 32-wide block: natural index 32kk + 16h + 4g + j lives
+// at 32kk + 8g + 4h + j, so one 16-byte LDS read returns the eight k values a
+// lane needs for an operand that pairs with accumulator rows 4g..4g+3 of two
+// adjacent 16-row tiles.
+__device__ __forceinline__ int perm32(int c) {
+  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ void split4(const f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bf16 h, l;
+    split_bf16(x[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
+  }
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i receives
+// element (i & 3) of the 8-byte chunks addressed by lanes (i >> 2) + 4c,
+// c = 0..3.  Pointing lane j of a group at &X[t_(j >> 2)][c0 + 4 (j & 3)]
+// therefore hands lane i the column c0 + i of rows t_0..t_3: a transposed
+// 4x16 fragment, straight from a row-major tile.
+__device__ __forceinline__ bf16x4 ld_tr4(const bf16 *p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s *)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
+__device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6], x[7]}; }
+
+// acc += L (16x16, fp32, row-major at L[m*ldl + k]) * R (16x16, fp32, given
+// transposed: R[k][n] = RT[n*ldr + k]) to ~fp32 accuracy with two MFMAs: the
+// 32-deep k axis carries [L_hi | L_lo] against [R_hi ; R_hi], then
+// [L_hi | L_lo] against [R_lo ; 0].
+__device__ __forceinline__ f32x4 mm16_split(const float *L, int ldl, const float *RT, int ldr,
+                                            f32x4 acc, int lane) {
+  const int m = lane & 15, g = lane >> 4, k0 = 8 * (g & 1);
+  bf16x8 a, b1, b2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bf16 lh, ll, rh, rl;
+    split_bf16(L[m * ldl + k0 + j], lh, ll);
+    split_bf16(RT[m * ldr + k0 + j], rh, rl);
+    a[j] = g < 2 ? lh : ll;
+    b1[j] = rh;
+    b2[j] = g < 2 ? rl : (bf16)0.0f;
+  }
+  acc = mfma_bf16(a, b1, acc);
+  return mfma_bf16(a, b2, acc);
+}
+
+}  // namespace gdr

@@ -30,7 +30,8 @@
  *    -50 gives a clean hard reset), beta is finite.  Non-finite inputs
  *    propagate only into the (batch, head) chain they belong to.
  *  - q, k, v, o and every state pointer must be 16-byte aligned; beta and
- *    log_alpha 4-byte aligned.
+ *    log_alpha 4-byte aligned, except that gdr_chunk_fwd with
+ *    GDR_GATE_CHANNEL needs log_alpha 16-byte aligned (GDR_EINVAL otherwise).
  */
 #ifndef GDR_H_
 #define GDR_H_
@@ -79,7 +80,9 @@ const char *gdr_status_str(int status);
  * Q&A).  The result does not depend on `chunk` beyond rounding.
  *
  *   B, T, H      batch, tokens per sequence (any T >= 1), heads
- *   Dk, Dv       key / value head sizes (supported: Dk == Dv in {16, 32, 64, 128})
+ *   Dk, Dv       key / value head sizes (supported: Dk == Dv in {16, 32, 64, 128}
+ *                with bf16 q/k/v, Dk == Dv in {16, 32, 64} with fp32 q/k/v;
+ *                other combinations return GDR_EUNSUPPORTED)
  *   chunk        tokens per chunk: 0 = default, else 16, 32 or 64
  *   in_dtype     dtype of q, k, v (GDR_BF16 or GDR_F32)
  *   out_dtype    dtype of o (GDR_F32 or GDR_BF16)

@@ -81,6 +81,9 @@ def step(**kw):
     (dict(Dk=96, Dv=96), _abi.GDR_EUNSUPPORTED),
     (dict(chunk=48), _abi.GDR_EUNSUPPORTED),
     (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),     # fp32 inputs need Dk <= 64
+    (dict(gate=_abi.GDR_GATE_CHANNEL, in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
+    # per-channel log decays are read with 16-byte vectors
+    (dict(gate=_abi.GDR_GATE_CHANNEL, log_alpha=FAKE + 4), _abi.GDR_EINVAL),
 ])
 def test_chunk_fwd_rejects(kw, want):
     assert chunk(**kw) == want

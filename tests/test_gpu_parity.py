@@ -208,15 +208,73 @@ def test_chunk_mfma_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# chunk forward, per-channel decay (KDA), MFMA path (bf16, Dk = Dv in {64, 128})
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100])
+@pytest.mark.parametrize("s0", [False, True])
+def test_chunk_kda_small_batch(D, T, s0):
+    say("chunk kda", D, T, s0)
+    inp = W.make_chunk_inputs(2, T, 3, D, D, "channel", "bf16", seed=3 * T + D, device=DEV)
+    if s0:
+        inp = with_state(inp)
+    o, S = run_chunk(inp)
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = rel_err(np64(o), o_ref), rel_err(np64(S), S_ref)
+    say("max|err|/rms o", eo, "state", es)
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+@pytest.mark.parametrize("alpha_mu,alpha_sigma", [(-3.0, 1.0), (1.0, 1.0), (3.0, 2.5)])
+def test_chunk_kda_decay_range(alpha_mu, alpha_sigma):
+    # from weak decay to per-step log decays beyond -10 on some channels,
+    # which sends those chunks down the exact (unfactored) in-chunk path
+    say("chunk kda decay range", alpha_mu, alpha_sigma)
+    inp = with_state(W.make_chunk_inputs(2, 97, 4, 128, 128, "channel", "bf16", seed=11,
+                                         device=DEV, alpha_mu=alpha_mu, alpha_sigma=alpha_sigma))
+    o, S = run_chunk(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = rel_err(np64(o), o_ref), rel_err(np64(S), S_ref)
+    say("max|err|/rms o", eo, "state", es)
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+def test_chunk_kda_many_chains():
+    # 128 chains: the 64-column slice configuration
+    say("chunk kda many chains")
+    inp = with_state(W.make_chunk_inputs(8, 70, 16, 128, 128, "channel", "bf16", seed=5,
+                                         device=DEV))
+    o, S = run_chunk(inp)
+    o_ref, S_ref = oracle_on(inp)
+    assert rel_err(np64(o), o_ref) <= BF16_TOL
+    assert rel_err(np64(S), S_ref) <= BF16_TOL
+
+
+def test_chunk_kda_bf16_output_and_determinism():
+    say("chunk kda bf16 out")
+    inp = with_state(W.make_chunk_inputs(2, 150, 2, 128, 128, "channel", "bf16", seed=9,
+                                         device=DEV))
+    o, _ = run_chunk(inp, out_dtype=torch.bfloat16)
+    o2, _ = run_chunk(inp, out_dtype=torch.bfloat16)
+    assert torch.equal(o, o2)
+    o_ref, _ = oracle_on(inp)
+    rms = math.sqrt(float(np.mean(o_ref ** 2)))
+    assert np.all(np.abs(np64(o) - o_ref) <= BF16_TOL * rms + bf16_half_ulp(o_ref))
+
+
+# ---------------------------------------------------------------------------
 # state carry and special cases
 
 
-@pytest.mark.parametrize("D,in_dtype", [(128, "bf16"), (32, "f32")])
-def test_state_passing_split_and_decode(D, in_dtype):
-    say("state passing", D, in_dtype)
+@pytest.mark.parametrize("D,in_dtype,gate", [(128, "bf16", "scalar"), (32, "f32", "scalar"),
+                                             (128, "bf16", "channel")])
+def test_state_passing_split_and_decode(D, in_dtype, gate):
+    say("state passing", D, in_dtype, gate)
     T = 150
     tol = BF16_TOL if in_dtype == "bf16" else F32_TOL
-    inp = with_state(W.make_chunk_inputs(2, T, 3, D, D, "scalar", in_dtype, seed=6, device=DEV))
+    inp = with_state(W.make_chunk_inputs(2, T, 3, D, D, gate, in_dtype, seed=6, device=DEV))
     o_all, S_all = run_chunk(inp)
     # split at 70: run [0, 70) then [70, T) from the carried state
     cut = lambda x, a, b: x[:, a:b].contiguous()
@@ -271,10 +329,11 @@ def test_empty_sequence_passes_state_through():
     assert torch.count_nonzero(S) == 0
 
 
-@pytest.mark.parametrize("D,in_dtype", [(128, "bf16"), (16, "f32")])
-def test_hard_reset_gate_has_no_nan(D, in_dtype):
-    say("hard reset", D, in_dtype)
-    inp = with_state(W.make_chunk_inputs(1, 80, 2, D, D, "scalar", in_dtype, seed=1, device=DEV))
+@pytest.mark.parametrize("D,in_dtype,gate", [(128, "bf16", "scalar"), (16, "f32", "scalar"),
+                                             (128, "bf16", "channel")])
+def test_hard_reset_gate_has_no_nan(D, in_dtype, gate):
+    say("hard reset", D, in_dtype, gate)
+    inp = with_state(W.make_chunk_inputs(1, 80, 2, D, D, gate, in_dtype, seed=1, device=DEV))
     inp["log_alpha"] = torch.full_like(inp["log_alpha"], -50.0)
     o, S = run_chunk(inp)
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
@@ -310,3 +369,7 @@ def test_workload_gdn_b4h8_sampled():
 
 def test_workload_gdn_b8h16_sampled():
     _sampled(W.HEADLINE, [(0, 0), (5, 9), (7, 15)])
+
+
+def test_workload_kda_b2h32_sampled():
+    _sampled(W.by_name("kda_bf16_b2h32t8192"), [(0, 0), (1, 17), (1, 31)])
