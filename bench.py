@@ -1,35 +1,89 @@
 """Benchmark of the gated delta-rule forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+    python bench.py --only counters        # the kernels alone, for rocprofv3 --pmc
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   # (CPU) counter CSVs -> profiles/
 
 One "step" is one gdr_chunk_fwd call over the Gated DeltaNet layer workload
-(B=8, H=16, T=4096, d_k = d_v = 128, chunk 64, bf16 q/k/v, fp32 state, fp32
-output): every row of the chunkwise hot path (in-chunk log-decay cumsum,
-K K^T / Q K^T with the decay, the unit-lower triangular solve, the WY
-factors, the serial inter-chunk state pass and the outputs) runs inside
-that one kernel.  Inputs are seeded synthetic tensors already resident in
-HBM when the timed region starts.
+gdn_bf16_b8h16t4096 (B=8, H=16, T=4096, d_k = d_v = 128, bf16 q/k/v, fp32
+beta/log alpha, fp32 state, fp32 output): every row of the chunkwise hot path
+(in-chunk log-decay cumsum, K K^T and Q K^T with the decay, the unit-lower
+triangular solve, the WY factors, the serial inter-chunk state pass and the
+outputs) runs inside that one kernel.  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
 
-Printed: ONE JSON line with tokens/s (B*T per step time), the roofline of
-the chunk kernel (HBM-bound: algorithmic bytes / measured kernel time / 8
-TB/s), the fp64 oracle timed on the host cores on a bounded sample, and a
-secondary measurement of the batched decode step (256 sequences x 32 heads,
-128 consecutive steps, HBM-bound state read-modify-write).
+Printed: ONE JSON line with tokens/s (B*T / wall time per step), the roofline
+of the chunk kernel (HBM-bound: algorithmic bytes / mean kernel time from HIP
+events on the launch stream / 8 TB/s; measured HBM traffic from the committed
+counter summary when it was taken on the current kernel source), the fp64
+oracle timed on the host cores, and secondary lines: bf16 output, the KDA
+workload kda_bf16_b2h32t8192, and the batched decode step (256 sequences x 32
+heads, 128 consecutive steps, eager and as one HIP graph).
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
-import torch
-
-import gated_delta_rule_28_amd as gdr
-import workloads as W
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+# tokens per chunk of the MFMA kernels' state pass (the chunk argument of
+# gdr_chunk_fwd only changes rounding, so the kernels use their own)
+KERNEL_CHUNK = {"none": 32, "scalar": 32, "channel": 16}
+KERNEL_OF_GATE = {"none": "chunk_fwd_bf16_kernel", "scalar": "chunk_fwd_bf16_kernel",
+                  "channel": "chunk_fwd_kda_kernel"}
+KERNEL_SOURCES = {
+    "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "mfma_util.h", "common.h"],
+    "chunk_fwd_kda_kernel": ["chunk_fwd_kda.hip", "mfma_util.h", "common.h"],
+    "recurrent_step_kernel": ["recurrent_step.hip", "common.h"],
+}
+# the plain copy used to calibrate the byte counters: |x| over 1 GiB of fp32
+COPY_BYTES = 1 << 30
+COPY_REGEX = "AbsFunctor"
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel, workload, root=PROFILES):
+    return os.path.join(root, f"traffic_{kernel}_{workload}.txt")
+
+
+def read_traffic(kernel, workload, root=PROFILES):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = traffic_file(kernel, workload, root)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != source_hash(kernel):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+# ---------------------------------------------------------------------------
+# algorithmic counts
 
 
 def chunk_alg_bytes(w, out_bytes=4):
@@ -46,11 +100,11 @@ def chunk_alg_bytes(w, out_bytes=4):
     return th * per_th + w.B * w.H * w.Dk * w.Dv * 4
 
 
-def chunk_alg_flops(w):
-    """Algorithmic flops per call: per token-head 6 dk dv (W S, Q S, K~^T U)
-    + 2 C dk (Q K^T and K K^T halves) + (C-1)(dk+dv) (solve on [bV | bgK])
-    + (C+1) dv (masked P U)."""
-    C, dk, dv = w.chunk, w.Dk, w.Dv
+def chunk_alg_flops(w, C):
+    """Algorithmic flops per call at chunk length C: per token-head 6 dk dv
+    (W S, Q S, K~^T U) + 2 C dk (Q K^T and K K^T halves) + (C-1)(dk+dv)
+    (solve on [bV | bgK]) + (C+1) dv (masked P U)."""
+    dk, dv = w.Dk, w.Dv
     per_th = 6 * dk * dv + 2 * C * dk + (C - 1) * (dk + dv) + (C + 1) * dv
     return w.B * w.T * w.H * per_th
 
@@ -62,10 +116,14 @@ def decode_alg_bytes(w):
     return n * (2 * 4 * w.Dk * w.Dv + in_b * (2 * w.Dk + w.Dv) + 8 + 4 * w.Dv)
 
 
-def time_launches(fn, steps, warmup):
-    """Run fn warmup times, then exactly `steps` times between two full
-    synchronisations; every launch is also bracketed by events on the
-    current stream (the stream the kernels are launched on)."""
+# ---------------------------------------------------------------------------
+# GPU timing
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Run fn `warmup` times, then exactly `steps` times between two full
+    synchronisations; each call is also bracketed by events on the current
+    stream, the stream the kernels are launched on."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -82,7 +140,7 @@ def time_launches(fn, steps, warmup):
     return wall, per
 
 
-def bench_chunk(w, steps, warmup, out_dtype=torch.float32):
+def chunk_setup(torch, gdr, W, w, out_dtype):
     inp = W.make_workload_inputs(w, seed=0, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.Dv, device="cuda", dtype=out_dtype)
     S = torch.empty(w.B, w.H, w.Dk, w.Dv, device="cuda", dtype=torch.float32)
@@ -90,34 +148,88 @@ def bench_chunk(w, steps, warmup, out_dtype=torch.float32):
     def step():
         gdr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None,
                       chunk=w.chunk, out_dtype=out_dtype, o=o, final_state=S)
-
-    wall, per = time_launches(step, steps, warmup)
-    if not bool(torch.isfinite(o).all()):
-        raise RuntimeError("non-finite output in the timed run")
-    return wall, per
+    return step, o, S
 
 
-def bench_decode(w, passes, warmup_passes):
-    inp = W.make_decode_inputs(w.N, w.H, w.Dk, w.Dv, w.steps, w.gate, w.in_dtype, seed=0,
-                               device="cuda", alpha_mu=w.alpha_mu, alpha_sigma=w.alpha_sigma,
-                               state_std=w.state_std)
+def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype):
+    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype)
+    wall, per = time_launches(torch, step, steps, warmup)
+    if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())):
+        raise RuntimeError(f"non-finite output in the timed run of {w.name}")
+    out_b = 2 if out_dtype == torch.bfloat16 else 4
+    kern = KERNEL_OF_GATE[w.gate]
+    C = KERNEL_CHUNK[w.gate]
+    mean_ms = statistics.fmean(per)
+    alg_b = chunk_alg_bytes(w, out_b)
+    alg_f = chunk_alg_flops(w, C)
+    achieved = alg_b / (mean_ms * 1e-3) / 1e9
+    traffic = read_traffic(kern, w.name) if out_b == 4 else None
+    return {
+        "workload": w.name, "tokens": w.B * w.T, "wall_s": wall, "steps": steps,
+        "ms_per_step": 1e3 * wall / steps,
+        "value": w.B * w.T / (wall / steps),
+        "kernel": kern, "kernel_chunk": C,
+        "kernel_ms": {"mean": mean_ms, "median": statistics.median(per), "min": min(per)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": alg_b},
+        "mfma_alg": {"achieved": alg_f / (mean_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": alg_f / (mean_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "alg_flops_per_launch": alg_f},
+    }
+
+
+def decode_setup(torch, gdr, W, d):
+    inp = W.make_decode_inputs(d.N, d.H, d.Dk, d.Dv, d.steps, d.gate, d.in_dtype, seed=0,
+                               device="cuda", alpha_mu=d.alpha_mu, alpha_sigma=d.alpha_sigma,
+                               state_std=d.state_std)
     state = inp["state"]
-    o = torch.empty(w.N, w.H, w.Dv, device="cuda", dtype=torch.float32)
+    o = torch.empty(d.steps, d.N, d.H, d.Dv, device="cuda", dtype=torch.float32)
 
     def one_pass():
-        # the workload: `steps` consecutive tokens, each step consumes the state
-        for t in range(w.steps):
+        # the workload: `steps` consecutive tokens, each consuming the state
+        for t in range(d.steps):
             gdr.recurrent_step(inp["q"][t], inp["k"][t], inp["v"][t], inp["beta"][t],
-                               inp["log_alpha"][t], state, o=o)
-
-    wall, per = time_launches(one_pass, passes, warmup_passes)
-    return wall, per
+                               inp["log_alpha"][t], state, o=o[t])
+    return one_pass, state, o
 
 
-def cpu_baseline(w, batches=6):
+def decode_line(torch, gdr, W, d, passes=3):
+    one_pass, state, o = decode_setup(torch, gdr, W, d)
+    _, per_eager = time_launches(torch, one_pass, passes, 1)
+    # the same 128 launches captured once and replayed as one HIP graph
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    _, per_graph = time_launches(torch, graph.replay, passes, 1)
+    if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(state).all())):
+        raise RuntimeError("non-finite decode output")
+    db = decode_alg_bytes(d)
+    ms_eager = statistics.fmean(per_eager) / d.steps
+    ms_graph = statistics.fmean(per_graph) / d.steps
+    traffic = read_traffic("recurrent_step_kernel", d.name)
+    return {
+        "workload": d.name, "unit": "tokens/s",
+        "value": d.N / (ms_graph * 1e-3),
+        "ms_per_token_step": {"graph": ms_graph, "eager": ms_eager},
+        "roofline": {"bound": "hbm", "achieved": db / (ms_graph * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": db / (ms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": traffic, "alg_bytes_per_launch": db,
+                     "note": "per-step time of the 128-step graph replay (launch gaps included)"},
+    }
+
+
+def cpu_baseline(W, w, batches=8):
     """The fp64 oracle on a bounded sample of the same workload: `batches`
-    sequences x all heads x all tokens, the same seeded inputs."""
-    import numpy as np  # noqa: F401
+    sequences x all heads x all tokens, the same seeded inputs, one thread."""
     from oracle import gated_delta_recurrence
     try:
         from threadpoolctl import threadpool_limits
@@ -126,10 +238,9 @@ def cpu_baseline(w, batches=6):
     inp = W.make_chunk_inputs(batches, w.T, w.H, w.Dk, w.Dv, w.gate, w.in_dtype, seed=0,
                               device="cpu", alpha_mu=w.alpha_mu, alpha_sigma=w.alpha_sigma)
     a = {k: W.to_f64(v) for k, v in inp.items()}
-    ctx = threadpool_limits(1) if threadpool_limits else None
     t0 = time.perf_counter()
-    if ctx:
-        with ctx:
+    if threadpool_limits is not None:
+        with threadpool_limits(1):
             gated_delta_recurrence(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"])
     else:
         gated_delta_recurrence(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"])
@@ -140,77 +251,181 @@ def cpu_baseline(w, batches=6):
                       f"({tokens * w.H} token-heads, {dt:.1f} s wall, fp64 numpy, 1 thread)"}
 
 
+# ---------------------------------------------------------------------------
+# counter runs
+
+
+def run_counter_targets(torch, gdr, W, reps=3):
+    """The three measured kernels on their workloads, `reps` launches each,
+    then the calibration copy; prints a line per part."""
+    for w in (W.HEADLINE, W.by_name("kda_bf16_b2h32t8192")):
+        step, _, _ = chunk_setup(torch, gdr, W, w, torch.float32)
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        print(f"counters: {w.name} x{reps}", flush=True)
+    d = W.DECODE
+    one_pass, _, _ = decode_setup(torch, gdr, W, d)
+    one_pass()
+    torch.cuda.synchronize()
+    print(f"counters: {d.name} x{d.steps}", flush=True)
+    src = torch.empty(COPY_BYTES // 4, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.abs(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"counters: copy {COPY_BYTES} bytes x{reps}", flush=True)
+
+
+def _pmc_means(d, counter):
+    """Mean per dispatch of `counter` (summed over its dimensions), by kernel."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Kernel_Name"], row.get("Dispatch_Id") or row["Correlation_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    return per
+
+
+def summarize_pmc(fetch_dir, write_dir, command, out_dir=PROFILES):
+    """Write profiles/traffic_<kernel>_<workload>.txt from a FETCH_SIZE run and
+    a WRITE_SIZE run of `bench.py --only counters`."""
+    import workloads as W
+    fetch = _pmc_means(fetch_dir, "FETCH_SIZE")
+    write = _pmc_means(write_dir, "WRITE_SIZE")
+
+    def mean_of(per, pat):
+        vals = [v for (k, _), v in per.items() if pat in k]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    cf, ncf = mean_of(fetch, COPY_REGEX)
+    cw, ncw = mean_of(write, COPY_REGEX)
+    if not cf or not cw:
+        raise RuntimeError("calibration copy not found in the counter runs")
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    os.makedirs(out_dir, exist_ok=True)
+    targets = [("chunk_fwd_bf16_kernel", W.HEADLINE.name,
+                chunk_alg_bytes(W.HEADLINE)),
+               ("chunk_fwd_kda_kernel", "kda_bf16_b2h32t8192",
+                chunk_alg_bytes(W.by_name("kda_bf16_b2h32t8192"))),
+               ("recurrent_step_kernel", W.DECODE.name, decode_alg_bytes(W.DECODE))]
+    for kern, wname, alg in targets:
+        kf, nf = mean_of(fetch, kern)
+        kw, nw = mean_of(write, kern)
+        if kf is None or kw is None:
+            print(f"{kern}: no dispatches in the counter runs", file=sys.stderr)
+            continue
+        traffic = kf * 1024.0 * f_scale + kw * 1024.0 * w_scale
+        lines = [
+            f"# HBM traffic of {kern} on {wname}, from rocprofv3 byte counters",
+            "# counter runs (each on its own):",
+            f"#   {command.format(counter='FETCH_SIZE', dir=fetch_dir)}",
+            f"#   {command.format(counter='WRITE_SIZE', dir=write_dir)}",
+            f"# summary: python bench.py --summarize-pmc {fetch_dir} {write_dir}",
+            "# The counters are scaled by what they read for a plain copy of known",
+            f"# size in the same runs ({COPY_BYTES} bytes read + written, torch abs).",
+            f"kernel: {kern}",
+            f"workload: {wname}",
+            f"source_sha256: {source_hash(kern)}",
+            f"dispatches: fetch {nf}, write {nw}",
+            f"fetch_kib_per_dispatch: {kf:.1f}",
+            f"write_kib_per_dispatch: {kw:.1f}",
+            f"copy_dispatches: fetch {ncf}, write {ncw}",
+            f"copy_fetch_kib_per_dispatch: {cf:.1f}",
+            f"copy_write_kib_per_dispatch: {cw:.1f}",
+            f"fetch_scale: {f_scale:.4f}",
+            f"write_scale: {w_scale:.4f}",
+            f"read_bytes_per_launch: {kf * 1024.0 * f_scale:.0f}",
+            f"written_bytes_per_launch: {kw * 1024.0 * w_scale:.0f}",
+            f"traffic_bytes_per_launch: {traffic:.0f}",
+            f"algorithmic_bytes_per_launch: {alg}",
+            f"traffic_over_algorithmic: {traffic / alg:.3f}",
+        ]
+        path = traffic_file(kern, wname, out_dir)
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {path}: traffic/alg = {traffic / alg:.3f}")
+    return 0
+
+
+# ---------------------------------------------------------------------------
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline line only (no bf16-output, KDA and decode lines)")
+    ap.add_argument("--only", choices=["counters"], default=None)
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-command", default="rocprofv3 --pmc {counter} --kernel-include-regex "
+                    "'chunk_fwd|recurrent_step|AbsFunctor' --output-format csv -d {dir} -o pmc "
+                    "-- python3 bench.py --only counters")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        return summarize_pmc(*args.summarize_pmc, args.pmc_command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every (batch, head) chain is independent; see the sharding notes).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path here "
+              "(every (batch, head) chain is independent, so batch or heads shard "
+              "across GPUs with no exchange).", file=sys.stderr)
         return 2
+
+    import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    import gated_delta_rule_28_amd as gdr
+    import workloads as W
+
+    if args.only == "counters":
+        run_counter_targets(torch, gdr, W)
+        return 0
 
     w = W.HEADLINE
-    wall, per = bench_chunk(w, args.steps, args.warmup)
-    ms_per_step = 1e3 * wall / args.steps
-    kern_ms = sum(per) / len(per)
-    tokens = w.B * w.T
-    alg_bytes = chunk_alg_bytes(w)
-    alg_flops = chunk_alg_flops(w)
-    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    head = chunk_line(torch, gdr, W, w, args.steps, args.warmup, torch.float32)
     rec = {
         "metric": "tokens/s gated-delta chunk fwd (H=16,d=128,T=4096) + % MFMA/HBM roofline",
-        "value": tokens / (ms_per_step * 1e-3),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "Dk": w.Dk, "Dv": w.Dv,
-                   "chunk": w.chunk, "gate": "scalar (Gated DeltaNet)",
+                   "gate": "scalar (Gated DeltaNet)", "kernel_chunk": head["kernel_chunk"],
                    "inputs": "bf16 q/k/v, fp32 beta/log_alpha, fp32 state, fp32 output",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_fwd_bf16_kernel", "kernel_ms": kern_ms,
-                     "alg_bytes_per_launch": alg_bytes},
-        "mfma_alg": {"achieved_tflops": alg_flops / (kern_ms * 1e-3) / 1e12,
-                     "peak_tflops": BF16_PEAK_TFLOPS,
-                     "frac": alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                     "alg_flops_per_launch": alg_flops},
+        "roofline": dict(head["roofline"], kernel=head["kernel"], kernel_ms=head["kernel_ms"]),
+        "mfma_alg": head["mfma_alg"],
     }
-    # bf16-output variant of the same step (secondary)
-    wall_b, per_b = bench_chunk(w, max(5, args.steps // 5), 2, out_dtype=torch.bfloat16)
-    kb = sum(per_b) / len(per_b)
-    rec["bf16_output"] = {"value": tokens / (kb * 1e-3), "unit": "tokens/s", "kernel_ms": kb,
-                          "hbm_frac": chunk_alg_bytes(w, 2) / (kb * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if not args.no_decode:
-        d = W.DECODE
-        passes = 3
-        wall_d, per_d = bench_decode(d, passes, 1)
-        ms_pass = sum(per_d) / len(per_d)
-        ms_step = ms_pass / d.steps
-        db = decode_alg_bytes(d)
-        rec["decode"] = {"workload": d.name, "value": d.N * d.steps / (ms_pass * 1e-3),
-                         "unit": "tokens/s", "ms_per_token_step": ms_step,
-                         "roofline": {"bound": "hbm", "achieved": db / (ms_step * 1e-3) / 1e9,
-                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": db / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                      "alg_bytes_per_launch": db}}
+    if not args.no_extra:
+        nb = max(5, args.steps // 2)
+        b = chunk_line(torch, gdr, W, w, nb, 2, torch.bfloat16)
+        rec["bf16_output"] = {"value": w.B * w.T / (b["kernel_ms"]["mean"] * 1e-3),
+                              "unit": "tokens/s", "kernel_ms": b["kernel_ms"],
+                              "roofline": b["roofline"]}
+        kda = chunk_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2, torch.float32)
+        rec["kda"] = {k: kda[k] for k in ("workload", "value", "kernel", "kernel_chunk",
+                                          "kernel_ms", "roofline", "mfma_alg")}
+        rec["kda"]["unit"] = "tokens/s"
+        rec["decode"] = decode_line(torch, gdr, W, W.DECODE)
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"] = cpu_baseline(W, w)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -159,6 +159,43 @@ def test_chunk_small_bf16_inputs(gate):
     assert rel_err(np64(S), S_ref) <= F32_TOL
 
 
+def test_decode_graph_replays_match_eager():
+    # the decode loop captured once as a HIP graph: every replay, with eager
+    # work and synchronisations in between, equals the eager loop bit for bit
+    say("decode graph replay")
+    N, H, D, steps = 8, 4, 128, 6
+    inp = W.make_decode_inputs(N, H, D, D, steps, "scalar", "bf16", seed=21, device=DEV)
+    state = inp["state"].clone()
+    o = torch.empty(steps, N, H, D, device=DEV)
+
+    def one_pass():
+        for t in range(steps):
+            gdr.recurrent_step(inp["q"][t], inp["k"][t], inp["v"][t], inp["beta"][t],
+                               inp["log_alpha"][t], state, o=o[t])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    for rep in range(3):
+        start = 0.02 * (rep + 1) * torch.randn(N, H, D, D, device=DEV, generator=gen)
+        state.copy_(start)
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_s = o.clone(), state.clone()
+        state.copy_(start)
+        one_pass()
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, o) and torch.equal(got_s, state), rep
+
+
 # ---------------------------------------------------------------------------
 # chunk forward, MFMA path (bf16 q/k/v, Dk = Dv in {64, 128})
 
