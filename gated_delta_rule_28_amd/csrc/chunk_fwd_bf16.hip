@@ -29,13 +29,15 @@
 //     with the same permutation).  The serial chain never touches LDS.
 //   prep waves (4) run ahead on the key-only work: they stage chunk i+1
 //     from HBM in registers while writing chunk i to LDS with its decay
-//     cumsum, form K K^T / Q K^T with the decay (A and P) for chunk i, and
-//     solve (I + A) for chunk i-1.
+//     cumsum, form K K^T / Q K^T with the decay (A and P), and solve (I + A).
 //
 // Iteration i has two phases separated by workgroup barriers:
-//   X: prep writes chunk i (+cumsum), solves chunk i-1   | state: K S, Q S, U of chunk i-2
-//   Y: prep forms A, P of chunk i                          | state: O and S update of chunk i-2
-// so chunk buffers live three iterations (triple-buffered), A and T' two.
+//   X: prep writes chunk i (+ cumsum) and loads i+1, forms the A and P tiles
+//      of chunk i-1 and the off-diagonal 16x16 block of T' of chunk i-2
+//                                                   | state: K S, Q S, U of chunk i-3
+//   Y: prep solves the diagonal 16x16 blocks of (I + A) of chunk i-1
+//                                                   | state: O, S update of chunk i-3
+// so a chunk buffer lives four iterations (NBUF = 4), A and T' two.
 //
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
 // operand (S, R, U, T', P) is split into bf16 hi + lo and multiplied as
