@@ -32,17 +32,18 @@
 //     cumsum, form K K^T / Q K^T with the decay (A and P), and solve (I + A).
 //
 // Iteration i has two phases separated by workgroup barriers:
-//   X: prep writes chunk i (+ cumsum) and loads i+1, forms the A and P tiles
-//      of chunk i-1 and the off-diagonal 16x16 block of T' of chunk i-2
-//                                                   | state: K S, Q S, U of chunk i-3
-//   Y: prep solves the diagonal 16x16 blocks of (I + A) of chunk i-1
-//                                                   | state: O, S update of chunk i-3
-// so a chunk buffer lives four iterations (NBUF = 4), A and T' two.
+//   X: prep writes chunk i (+ cumsum) and loads i+1; solves the diagonal
+//      16x16 blocks of (I + A) of chunk i-1     | state: K S, Q S, U of chunk i-2
+//   Y: prep forms the A and P tiles of chunk i and the off-diagonal block
+//      of T' of chunk i-1                        | state: O, S update of chunk i-2
+// so a chunk buffer lives three iterations (NBUF = 3), T' two.
 //
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
 // operand (S, R, U, T', P) is split into bf16 hi + lo and multiplied as
 // hi*hi + hi*lo + lo*hi (two products when the other side is exact), so
 // products carry ~16 significant bits and accumulate in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -52,7 +53,25 @@ namespace {
 
 constexpr int C = 32;      // tokens per chunk
 constexpr int NPW = 4;     // prep waves
-constexpr int NBUF = 4;    // chunk buffers: a chunk is staged 3 iterations before its state pass
+constexpr int NBUF = 3;    // chunk buffers: a chunk is written 2 iterations before its state pass
+
+// Inclusive prefix sum over lanes 0..31 of a wave with DPP row shifts
+// (within 16-lane rows) and a row broadcast of lane 15 into the next row.
+// Lanes 32..63 carry values that are not used.
+__device__ __forceinline__ float scan32_inclusive(float x) {
+  auto shr = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});   // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});   // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});   // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});   // row_shr:8
+  // row_bcast:15 into rows 1 and 3; rows 0 and 2 add 0
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142,
+                                                             0xA, 0xF, false));
+  return x;
+}
 
 template <int DK, int DVS>
 struct __align__(16) PipeSmem {
@@ -129,7 +148,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   }
 
-  // Both roles run nchunks + 3 iterations with two barriers each, so every
+  // Both roles run nchunks + 2 iterations with two barriers each, so every
   // wave executes the same sequence of workgroup barriers.
   if (wave < NSW) {
     // =====================================================================
@@ -149,8 +168,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
     __syncthreads();
 
-    for (int it = 0; it < nchunks + 3; ++it) {
-      const int s = it - 3;            // chunk of this iteration
+    for (int it = 0; it < nchunks + 2; ++it) {
+      const int s = it - 2;            // chunk of this iteration
       f32x4 QS[2];                     // carried from phase X to phase Y
       bf16x8 Uh, Ul, Wh, Wl;
       // ---- phase X: K S, Q S, R = V - diag(gam) K S, U = T' R ----
@@ -302,41 +321,30 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int it_r0 = 4 * (item / DCS), it_c0 = 8 * (item % DCS);
   const bool has_v = pt < NV;
   const int v_r = pt / VCS, v_c0 = 8 * (pt % VCS);
+  // load addresses: threads without an item re-load a valid one, so every
+  // prep thread issues the same unconditional loads (no branch merges the
+  // staging registers, and nothing waits on the loads before they are used)
+  const int ld_item = min(item, NI - 1);
+  const int ld_r0 = 4 * (ld_item / DCS), ld_c0 = 8 * (ld_item % DCS);
+  const int ld_vr = min(v_r, C - 1);
+  const int ld_bt = pt & (C - 1);
   // token t of this chain is `base + t * stride`
-  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + it_c0;
-  const bf16 *v_base = v + tok0 * DV + slice * DVS + v_c0;
+  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + ld_c0;
+  const bf16 *v_base = v + tok0 * DV + slice * DVS + 8 * (pt % VCS);
   const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
   bf16x8 stg[4], stgv;
   float stg_b = 0.f, stg_la = 0.f;
 
-  // Loads of rows past the end of the sequence read the last valid row
-  // instead (always in bounds) and are zeroed when written to LDS.
+  // Rows past the end of the sequence re-load the last valid row (always in
+  // bounds); they are zeroed when written to LDS.
   auto stage_chunk = [&](int j) {
     const int t0 = j * C, last = T - 1;
-    if (t0 + C <= T) {               // whole chunk in range (uniform)
-      if (has_qk) {
-        const bf16 *src = qk_base + (long)(t0 + it_r0) * qk_stride;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) stg[i] = ld8(src + i * qk_stride);
-      }
-      if (has_v) stgv = ld8(v_base + (long)(t0 + v_r) * v_stride);
-      if (pt < C) {
-        const long ri = tok0 + (long)(t0 + pt) * H;
-        stg_b = beta[ri];
-        stg_la = (GATE == kGateScalar) ? log_alpha[ri] : 0.0f;
-      }
-    } else {
-      if (has_qk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + it_r0 + i, last) * qk_stride);
-      }
-      if (has_v) stgv = ld8(v_base + (long)min(t0 + v_r, last) * v_stride);
-      if (pt < C) {
-        const long ri = tok0 + (long)min(t0 + pt, last) * H;
-        stg_b = beta[ri];
-        stg_la = (GATE == kGateScalar) ? log_alpha[ri] : 0.0f;
-      }
-    }
+    for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + ld_r0 + i, last) * qk_stride);
+    stgv = ld8(v_base + (long)min(t0 + ld_vr, last) * v_stride);
+    const long ri = tok0 + (long)min(t0 + ld_bt, last) * H;
+    stg_b = beta[ri];
+    if constexpr (GATE == kGateScalar) stg_la = log_alpha[ri];
   };
   auto zero_if = [](bf16x8 x, bool z) -> bf16x8 {
     if (z) {
@@ -349,9 +357,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   if (nchunks > 0) stage_chunk(0);
   __syncthreads();
 
-  for (int it = 0; it < nchunks + 3; ++it) {
-    // ---- phase X: write chunk it (+ decay cumsum), stage chunk it+1,
-    //      A / P tiles of chunk it-1, T10 of chunk it-2 ----
+  for (int it = 0; it < nchunks + 2; ++it) {
+    // ---- phase X: write chunk it (+ decay cumsum), stage chunk it+1;
+    //      diagonal blocks of T' of chunk it-1 ----
     if (it < nchunks) {
       typename SM::Buf &bf = sm.buf[it % NBUF];
       const int n = min(C, T - it * C);
@@ -373,13 +381,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (pw == 0) {
         // in-chunk cumulative log decay: inclusive scan over lanes 0..C-1;
         // padded tokens carry log a = 0 and b = 0
-        float la = (lane < n) ? stg_la : 0.0f;
-#pragma unroll
-        for (int off = 1; off < C; off <<= 1) {
-          const float y = __shfl_up(la, off, 64);
-          if (lane >= off) la += y;
-        }
-        const float glast = __shfl(la, C - 1, 64);
+        const float la = scan32_inclusive((lane < n) ? stg_la : 0.0f);
+        const float glast = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), C - 1));
         if (lane < C) {
           bf.g[lane] = la;
           bf.gam[lane] = __expf(la);
@@ -389,10 +393,61 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       }
       if (it + 1 < nchunks) stage_chunk(it + 1);
     }
-    if ((pw == 1 || pw == 2) && it >= 1 && it - 1 < nchunks) {
-      // lower 16x16 tiles of K K^T (wave 1) or Q K^T (wave 2) of chunk it-1,
-      // with the decay: A (strict lower, times b) and P (lower incl.)
+    if (pw == 3 && it >= 1 && it - 1 < nchunks) {
+      // diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it-1; lane =
+      // (block, column); right-looking forward substitution: once x_s is
+      // final it updates all later rows, so the dependent chain is one FMA
+      // per step
       const int j = it - 1;
+      const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
+      const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+      // every needed entry of A^T (rows s, columns r > s: 36 float4) is
+      // loaded up front, so the 15 dependent steps wait on no LDS read
+      f32x4 a4[15][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+        for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
+          a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
+#pragma unroll
+      for (int s2 = 0; s2 < 15; ++s2) {
+#pragma unroll
+        for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
+      }
+      if (lane < 32) {   // lanes 32..63 hold duplicates
+        const float bcol = sm.buf[j % NBUF].beta[o0 + col];
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        unsigned h8[2][4], l8[2][4];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+        // T'[o0 + r][o0 + col] for r = 0..15 is row o0 + col of T'^T
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+          *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+        }
+        if (blk == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sm.T1[r][col] = x[r];
+        } else {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4 *>(&sm.T0T[col][4 * q4]) =
+                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- phase Y: A / P tiles of chunk it; off-diagonal block of T' of
+    //      chunk it-1 ----
+    if ((pw == 1 || pw == 2) && it < nchunks) {
+      // lower 16x16 tiles of K K^T (wave 1) or Q K^T (wave 2), with the
+      // decay: A (strict lower, times b) and P (lower incl.)
+      const int j = it;
       typename SM::Buf &bf = sm.buf[j % NBUF];
       const bool isq = pw == 2;
       const bf16(*Xr)[SM::LDK] = isq ? bf.Q : bf.K;
@@ -442,10 +497,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
       }
     }
-    if (pw == 3 && it >= 2 && it - 2 < nchunks) {
-      // T10 = -T11 (A10 T00) for chunk it-2 (its diagonal blocks were solved
-      // in the previous phase Y)
-      const int j = it - 2;
+    if (pw == 0 && it >= 1 && it - 1 < nchunks) {
+      // T10 = -T11 (A10 T00) of chunk it-1 (its diagonal blocks were solved
+      // in this iteration's phase X)
+      const int j = it - 1;
       f32x4 xa = mm16_split(&sm.A10[j & 1][0][0], 20, &sm.T0T[0][0], 20,
                             f32x4{0.f, 0.f, 0.f, 0.f}, lane);
       *reinterpret_cast<f32x4 *>(&sm.X[lr][4 * lg]) = xa;   // X^T
@@ -455,61 +510,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       split4(-z * bc, h4, l4);
       *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;
       *reinterpret_cast<bf16x4 *>(&sm.Tl[j & 1][lr][16 + 4 * lg]) = l4;
-    }
-    __syncthreads();
-
-    // ---- phase Y: diagonal blocks of T = (I + A)^{-1} for chunk it-1 ----
-    if (pw == 3 && it >= 1 && it - 1 < nchunks) {
-      // lane = (block, column); right-looking forward substitution: once x_s
-      // is final it updates all later rows, so the dependent chain is one
-      // FMA per step
-      const int j = it - 1;
-      const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
-      const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
-      f32x4 cur[4], nxt[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) cur[q4] = *reinterpret_cast<const f32x4 *>(&At[0][4 * q4]);
-#pragma unroll
-      for (int s2 = 0; s2 < 15; ++s2) {
-        if (s2 + 1 < 15) {
-#pragma unroll
-          for (int q4 = (s2 + 2) / 4; q4 < 4; ++q4)
-            nxt[q4] = *reinterpret_cast<const f32x4 *>(&At[s2 + 1][4 * q4]);
-        }
-#pragma unroll
-        for (int r = s2 + 1; r < 16; ++r) x[r] -= cur[r / 4][r % 4] * x[s2];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-      }
-      if (lane < 32) {   // lanes 32..63 hold duplicates
-        const float bcol = sm.buf[j % NBUF].beta[o0 + col];
-        bf16x8 h8[2], l8[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          bf16 h, l;
-          split_bf16(x[r] * bcol, h, l);
-          h8[r / 8][r % 8] = h;
-          l8[r / 8][r % 8] = l;
-        }
-        // T'[o0 + r][o0 + col] for r = 0..15 is row o0 + col of T'^T
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          *reinterpret_cast<bf16x8 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) = h8[hf];
-          *reinterpret_cast<bf16x8 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) = l8[hf];
-        }
-        if (blk == 1) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sm.T1[r][col] = x[r];
-        } else {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4 *>(&sm.T0T[col][4 * q4]) =
-                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-        }
-      }
     }
     __syncthreads();
   }

@@ -246,30 +246,35 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int vi = pt - 128;
   const bool has_v = vi >= 0 && vi < NV;
   const int v_r = vi / VCS, v_c0 = 8 * (vi % VCS);
-  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + it_c0;
-  const bf16 *v_base = v + tok0 * DV + slice * DVS + v_c0;
+  // load addresses: threads without an item re-load a valid one, so every
+  // prep thread issues the same unconditional loads (no branch merges the
+  // staging registers, and nothing waits on the loads before they are used)
+  const int ld_item = min(item, NI - 1);
+  const int ld_r0 = 4 * (ld_item / DCS), ld_c0 = 8 * (ld_item % DCS);
+  const int ld_vi = min(max(vi, 0), NV - 1);
+  const int ld_vr = ld_vi / VCS;
+  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + ld_c0;
+  const bf16 *v_base = v + tok0 * DV + slice * DVS + 8 * (ld_vi % VCS);
   const float *la_base = log_alpha + tok0 * DK;
   const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
   bf16x8 stg[4], stgv;
   f32x4 stgl[2];
   float stg_b = 0.f;
 
+  // rows past the end of the sequence re-load the last valid row (always in
+  // bounds); they are zeroed when written to LDS
   auto stage_chunk = [&](int j) {
     const int t0 = j * KC, last = T - 1;
-    if (has_qk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + it_r0 + i, last) * qk_stride);
-    }
-    if (has_v) stgv = ld8(v_base + (long)min(t0 + v_r, last) * v_stride);
+    for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + ld_r0 + i, last) * qk_stride);
+    stgv = ld8(v_base + (long)min(t0 + ld_vr, last) * v_stride);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int li = pt + 256 * h2;
-      if (li < NLA) {
-        const int r = li / (DK / 4), c4 = 4 * (li % (DK / 4));
-        stgl[h2] = *reinterpret_cast<const f32x4 *>(la_base + (long)min(t0 + r, last) * qk_stride + c4);
-      }
+      const int li = min(pt + 256 * h2, NLA - 1);
+      const int r = li / (DK / 4), c4 = 4 * (li % (DK / 4));
+      stgl[h2] = *reinterpret_cast<const f32x4 *>(la_base + (long)min(t0 + r, last) * qk_stride + c4);
     }
-    if (pt < KC) stg_b = beta[tok0 + (long)min(t0 + pt, last) * H];
+    stg_b = beta[tok0 + (long)min(t0 + (pt & (KC - 1)), last) * H];
   };
 
   if (nchunks > 0) stage_chunk(0);
@@ -328,12 +333,10 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (tq == 0) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
       const int pc = perm32(c0);
       auto put2 = [](bf16 (*hi)[SM::LDK], bf16 (*lo)[SM::LDK], int r, int c, float x0, float x1) {
-        bf16 h0, l0, h1, l1;
-        split_bf16(x0, h0, l0);
-        split_bf16(x1, h1, l1);
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<bf16x2 *>(&hi[r][c]) = bf16x2{h0, h1};
-        *reinterpret_cast<bf16x2 *>(&lo[r][c]) = bf16x2{l0, l1};
+        unsigned h, l;
+        split2(x0, x1, h, l);
+        *reinterpret_cast<unsigned *>(&hi[r][c]) = h;
+        *reinterpret_cast<unsigned *>(&lo[r][c]) = l;
       };
 #pragma unroll
       for (int i = 0; i < TPG; ++i) {
@@ -423,28 +426,29 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+        // every needed entry of A^T is loaded before the dependent steps
+        f32x4 a4[15][4];
+#pragma unroll
+        for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+          for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
+            a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
 #pragma unroll
         for (int s2 = 0; s2 < 15; ++s2) {
-          f32x4 a4[4];
 #pragma unroll
-          for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4) a4[q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
-#pragma unroll
-          for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[r / 4][r % 4] * x[s2];
+          for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
         }
         if (lane < 16) {
           const float bcol = rw.beta[col];
-          bf16x8 h8[2], l8[2];
+          typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+          unsigned h8[2][4], l8[2][4];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            bf16 h, l;
-            split_bf16(x[r] * bcol, h, l);
-            h8[r / 8][r % 8] = h;
-            l8[r / 8][r % 8] = l;
-          }
+          for (int r = 0; r < 16; r += 2)
+            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<bf16x8 *>(&sm.Th[col][8 * hf]) = h8[hf];
-            *reinterpret_cast<bf16x8 *>(&sm.Tl[col][8 * hf]) = l8[hf];
+            *reinterpret_cast<u32x4 *>(&sm.Th[col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&sm.Tl[col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
           }
         }
       }

@@ -17,14 +17,26 @@ __device__ __forceinline__ bf16x8 ld8(const bf16 *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Split two fp32 values into packed bf16 hi and lo pairs (x ~= hi + lo to
+// ~16 bits, hi = RNE(x), lo = RNE(x - hi)).  One packed conversion makes
+// both hi values; their fp32 values are the bf16 bits shifted into the top
+// half, so x - hi is exact and a second packed conversion makes the lo pair.
+__device__ __forceinline__ void split2(float x0, float x1, unsigned &hi, unsigned &lo) {
+  hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float h0 = __builtin_bit_cast(float, hi << 16);
+  const float h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+}
+
 __device__ __forceinline__ void split4(const f32x4 x, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16 h, l;
-    split_bf16(x[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
-  }
+  unsigned h01, l01, h23, l23;
+  split2(x[0], x[1], h01, l01);
+  split2(x[2], x[3], h23, l23);
+  hi = __builtin_bit_cast(bf16x4, u32x2{h01, h23});
+  lo = __builtin_bit_cast(bf16x4, u32x2{l01, l23});
 }
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
@@ -52,19 +64,20 @@ __device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6]
 // [L_hi | L_lo] against [R_lo ; 0].
 __device__ __forceinline__ f32x4 mm16_split(const float *L, int ldl, const float *RT, int ldr,
                                             f32x4 acc, int lane) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const int m = lane & 15, g = lane >> 4, k0 = 8 * (g & 1);
-  bf16x8 a, b1, b2;
+  u32x4 a, b1, b2;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bf16 lh, ll, rh, rl;
-    split_bf16(L[m * ldl + k0 + j], lh, ll);
-    split_bf16(RT[m * ldr + k0 + j], rh, rl);
+  for (int j = 0; j < 4; ++j) {
+    unsigned lh, ll, rh, rl;
+    split2(L[m * ldl + k0 + 2 * j], L[m * ldl + k0 + 2 * j + 1], lh, ll);
+    split2(RT[m * ldr + k0 + 2 * j], RT[m * ldr + k0 + 2 * j + 1], rh, rl);
     a[j] = g < 2 ? lh : ll;
     b1[j] = rh;
-    b2[j] = g < 2 ? rl : (bf16)0.0f;
+    b2[j] = g < 2 ? rl : 0u;
   }
-  acc = mfma_bf16(a, b1, acc);
-  return mfma_bf16(a, b2, acc);
+  acc = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b1), acc);
+  return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b2), acc);
 }
 
 }  // namespace gdr
