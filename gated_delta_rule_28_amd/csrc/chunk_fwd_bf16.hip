@@ -308,43 +308,72 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // =======================================================================
   const int pw = wave - NSW;           // prep wave index 0..NPW-1
   const int pt = tid - 64 * NSW;       // prep thread index 0..255
-  // q/k item = a 4-token x 8-column block of k (pt < NI) or q (NI <= pt <
-  // 2 NI), adjacent lanes on adjacent column segments (128-byte row runs);
-  // v item = one 8-column segment of one token of this slice
+  // Staging runs on prep waves 0..2 (192 threads); wave 3 solves instead.
+  // q/k item = a 4-token x 8-column block of k (index < NI) or q (NI <=
+  // index < 2 NI), adjacent lanes on adjacent column segments (128-byte row
+  // runs); v item = one 8-column segment of one token of this slice.  Each
+  // staging thread takes q/k item pt and v item pt; wave 1 also takes q/k
+  // item pt + 128 and wave 2 v item pt + 64 when there are more than 192.
   constexpr int DCS = DK / 8;          // 8-column segments of a q/k row
   constexpr int NI = (C / 4) * DCS;    // items per matrix (<= 128)
   constexpr int NV = C * VCS;          // v items (<= 256)
-  static_assert(2 * NI <= 64 * NPW && NV <= 64 * NPW, "staging items exceed the prep threads");
-  const bool has_qk = pt < 2 * NI;
-  const bool is_k = pt < NI;
-  const int item = is_k ? pt : pt - NI;
-  const int it_r0 = 4 * (item / DCS), it_c0 = 8 * (item % DCS);
-  const bool has_v = pt < NV;
-  const int v_r = pt / VCS, v_c0 = 8 * (pt % VCS);
-  // load addresses: threads without an item re-load a valid one, so every
-  // prep thread issues the same unconditional loads (no branch merges the
-  // staging registers, and nothing waits on the loads before they are used)
-  const int ld_item = min(item, NI - 1);
-  const int ld_r0 = 4 * (ld_item / DCS), ld_c0 = 8 * (ld_item % DCS);
-  const int ld_vr = min(v_r, C - 1);
-  const int ld_bt = pt & (C - 1);
-  // token t of this chain is `base + t * stride`
-  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + ld_c0;
-  const bf16 *v_base = v + tok0 * DV + slice * DVS + 8 * (pt % VCS);
+  constexpr bool QK2 = 2 * NI > 192, V2 = NV > 192;
+  static_assert(2 * NI <= 256 && NV <= 256, "staging items exceed the staging threads");
+  struct QKItem {
+    bool valid, is_k;
+    int r0, c0;
+    const bf16 *base;                  // row 0 of this chain at column c0
+  };
+  struct VItem {
+    bool valid;
+    int r, c0;
+    const bf16 *base;
+  };
+  // items past the end re-load a valid one (loads stay unconditional, so no
+  // branch merges the staging registers); only valid items are written
+  auto qk_item = [&](int idx) {
+    QKItem m;
+    m.valid = idx < 2 * NI;
+    const int i = min(idx, 2 * NI - 1);
+    m.is_k = i < NI;
+    const int it = m.is_k ? i : i - NI;
+    m.r0 = 4 * (it / DCS);
+    m.c0 = 8 * (it % DCS);
+    m.base = (m.is_k ? k : q) + tok0 * DK + m.c0;
+    return m;
+  };
+  auto v_item = [&](int idx) {
+    VItem m;
+    m.valid = idx < NV;
+    const int i = min(idx, NV - 1);
+    m.r = i / VCS;
+    m.c0 = 8 * (i % VCS);
+    m.base = v + tok0 * DV + slice * DVS + m.c0;
+    return m;
+  };
+  const QKItem qa = qk_item(pt), qb = qk_item(pt + 128);
+  const VItem va = v_item(pt), vb = v_item(pt + 64);
   const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
-  bf16x8 stg[4], stgv;
+  bf16x8 stga[4], stgb[4], stgva, stgvb;
   float stg_b = 0.f, stg_la = 0.f;
 
   // Rows past the end of the sequence re-load the last valid row (always in
   // bounds); they are zeroed when written to LDS.
   auto stage_chunk = [&](int j) {
     const int t0 = j * C, last = T - 1;
+    if (pw == 0) {   // b and log a feed wave 0's cumsum; issued first
+      const long ri = tok0 + (long)min(t0 + (lane & (C - 1)), last) * H;
+      stg_b = beta[ri];
+      if constexpr (GATE == kGateScalar) stg_la = log_alpha[ri];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + ld_r0 + i, last) * qk_stride);
-    stgv = ld8(v_base + (long)min(t0 + ld_vr, last) * v_stride);
-    const long ri = tok0 + (long)min(t0 + ld_bt, last) * H;
-    stg_b = beta[ri];
-    if constexpr (GATE == kGateScalar) stg_la = log_alpha[ri];
+    for (int i = 0; i < 4; ++i) stga[i] = ld8(qa.base + (long)min(t0 + qa.r0 + i, last) * qk_stride);
+    stgva = ld8(va.base + (long)min(t0 + va.r, last) * v_stride);
+    if (QK2 && pw == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stgb[i] = ld8(qb.base + (long)min(t0 + qb.r0 + i, last) * qk_stride);
+    }
+    if (V2 && pw == 2) stgvb = ld8(vb.base + (long)min(t0 + vb.r, last) * v_stride);
   };
   auto zero_if = [](bf16x8 x, bool z) -> bf16x8 {
     if (z) {
@@ -353,31 +382,147 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
     return x;
   };
+  auto write_qk = [&](typename SM::Buf &bf, const QKItem &m, const bf16x8 *x, int n) {
+    bf16(*dst)[SM::LDK] = m.is_k ? bf.K : bf.Q;
+    const int p0 = perm32(m.c0), p1 = perm32(m.c0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 y = zero_if(x[i], m.r0 + i >= n);
+      *reinterpret_cast<bf16x4 *>(&dst[m.r0 + i][p0]) = lo4(y);
+      *reinterpret_cast<bf16x4 *>(&dst[m.r0 + i][p1]) = hi4(y);
+    }
+  };
+  auto write_v = [&](typename SM::Buf &bf, const VItem &m, bf16x8 x, int n) {
+    *reinterpret_cast<bf16x8 *>(&bf.V[m.r][m.c0]) = zero_if(x, m.r >= n);
+  };
 
+  // lower 16x16 tiles of X K^T with the decay, two per wave: A (X = K,
+  // strict lower, times b) or P (X = Q, lower incl.) of chunk j
+  auto store_tile = [&](typename SM::Buf &bf, int j, f32x4 acc, int ti, int tj, bool isq) {
+    const int sc = 16 * tj + lr;
+    const int r0 = 16 * ti + 4 * lg;
+    const float gs = bf.g[sc];
+    const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&bf.g[r0]);
+    f32x4 val;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float dec = (GATE == kGateNone) ? 1.0f : __expf(gr4[e] - gs);
+      val[e] = acc[e] * dec;
+    }
+    if (!isq) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.beta[r0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? b4[e] * val[e] : 0.0f;
+      if (ti == tj) {
+        *reinterpret_cast<f32x4 *>(&sm.ATd[ti][lr][4 * lg]) = val;   // A^T of the block
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.A10[j & 1][4 * lg + e][lr] = val[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? val[e] : 0.0f;
+      bf16x4 h4, l4;
+      split4(val, h4, l4);
+      *reinterpret_cast<bf16x4 *>(&bf.Ph[sc][r0]) = h4;
+      *reinterpret_cast<bf16x4 *>(&bf.Pl[sc][r0]) = l4;
+    }
+  };
+  auto two_tiles = [&](typename SM::Buf &bf, int j, bool q1, int ti1, int tj1, bool q2, int ti2,
+                       int tj2) {
+    const bf16(*X1)[SM::LDK] = q1 ? bf.Q : bf.K;
+    const bf16(*X2)[SM::LDK] = q2 ? bf.Q : bf.K;
+    f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KKD; ++kk) {
+      const int c = 32 * kk + 8 * lg;
+      acc1 = mfma_bf16(ld8(&X1[16 * ti1 + lr][c]), ld8(&bf.K[16 * tj1 + lr][c]), acc1);
+      acc2 = mfma_bf16(ld8(&X2[16 * ti2 + lr][c]), ld8(&bf.K[16 * tj2 + lr][c]), acc2);
+    }
+    store_tile(bf, j, acc1, ti1, tj1, q1);
+    store_tile(bf, j, acc2, ti2, tj2, q2);
+  };
+
+  if (pw == 3) {
+    // ---- solver wave: its own loop, so the staging registers of waves
+    //      0..2 are not live across the solve ----
+    __syncthreads();
+    for (int it = 0; it < nchunks + 2; ++it) {
+      // phase X: diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it-1;
+      // lane = (block, column); right-looking forward substitution: once
+      // x_s is final it updates all later rows, so the dependent chain is
+      // one FMA per step
+      if (it >= 1 && it - 1 < nchunks) {
+        const int j = it - 1;
+        const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
+        const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+        // every needed entry of A^T (rows s, columns r > s: 36 float4) is
+        // loaded up front, so the 15 dependent steps wait on no LDS read
+        f32x4 a4[15][4];
+#pragma unroll
+        for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+          for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
+            a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
+#pragma unroll
+        for (int s2 = 0; s2 < 15; ++s2) {
+#pragma unroll
+          for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
+        }
+        if (lane < 32) {   // lanes 32..63 hold duplicates
+          const float bcol = sm.buf[j % NBUF].beta[o0 + col];
+          typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+          unsigned h8[2][4], l8[2][4];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+          // T'[o0 + r][o0 + col] for r = 0..15 is row o0 + col of T'^T
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) =
+                u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) =
+                u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+          }
+          if (blk == 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.T1[r][col] = x[r];
+          } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              *reinterpret_cast<f32x4 *>(&sm.T0T[col][4 * q4]) =
+                  f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+          }
+        }
+      }
+      __syncthreads();
+      // phase Y: the off-diagonal A and P tiles of chunk it
+      if (it < nchunks) two_tiles(sm.buf[it % NBUF], it, false, 1, 0, true, 1, 0);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---- staging waves 0..2 ----
   if (nchunks > 0) stage_chunk(0);
   __syncthreads();
 
   for (int it = 0; it < nchunks + 2; ++it) {
-    // ---- phase X: write chunk it (+ decay cumsum), stage chunk it+1;
-    //      diagonal blocks of T' of chunk it-1 ----
+    // phase X: write chunk it (+ decay cumsum on wave 0), stage chunk it+1.
+    // Every load in flight is one of chunk it's, consumed right here: one
+    // wait for all of them, on every path, so no later register reuse waits
+    // on a load that some skipped branch might have left pending.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     if (it < nchunks) {
       typename SM::Buf &bf = sm.buf[it % NBUF];
       const int n = min(C, T - it * C);
-      if (n < C) {                     // ragged last chunk: zero the padding rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) stg[i] = zero_if(stg[i], it_r0 + i >= n);
-        stgv = zero_if(stgv, v_r >= n);
-      }
-      if (has_qk) {
-        bf16(*dst)[SM::LDK] = is_k ? bf.K : bf.Q;
-        const int p0 = perm32(it_c0), p1 = perm32(it_c0 + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<bf16x4 *>(&dst[it_r0 + i][p0]) = lo4(stg[i]);
-          *reinterpret_cast<bf16x4 *>(&dst[it_r0 + i][p1]) = hi4(stg[i]);
-        }
-      }
-      if (has_v) *reinterpret_cast<bf16x8 *>(&bf.V[v_r][v_c0]) = stgv;
+      if (qa.valid) write_qk(bf, qa, stga, n);
+      if (QK2 && pw == 1 && qb.valid) write_qk(bf, qb, stgb, n);
+      if (va.valid) write_v(bf, va, stgva, n);
+      if (V2 && pw == 2 && vb.valid) write_v(bf, vb, stgvb, n);
       if (pw == 0) {
         // in-chunk cumulative log decay: inclusive scan over lanes 0..C-1;
         // padded tokens carry log a = 0 and b = 0
@@ -393,109 +538,13 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       }
       if (it + 1 < nchunks) stage_chunk(it + 1);
     }
-    if (pw == 3 && it >= 1 && it - 1 < nchunks) {
-      // diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it-1; lane =
-      // (block, column); right-looking forward substitution: once x_s is
-      // final it updates all later rows, so the dependent chain is one FMA
-      // per step
-      const int j = it - 1;
-      const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
-      const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
-      // every needed entry of A^T (rows s, columns r > s: 36 float4) is
-      // loaded up front, so the 15 dependent steps wait on no LDS read
-      f32x4 a4[15][4];
-#pragma unroll
-      for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-        for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
-          a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
-#pragma unroll
-      for (int s2 = 0; s2 < 15; ++s2) {
-#pragma unroll
-        for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
-      }
-      if (lane < 32) {   // lanes 32..63 hold duplicates
-        const float bcol = sm.buf[j % NBUF].beta[o0 + col];
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        unsigned h8[2][4], l8[2][4];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-        // T'[o0 + r][o0 + col] for r = 0..15 is row o0 + col of T'^T
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-          *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
-        }
-        if (blk == 1) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sm.T1[r][col] = x[r];
-        } else {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4 *>(&sm.T0T[col][4 * q4]) =
-                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-        }
-      }
-    }
     __syncthreads();
 
-    // ---- phase Y: A / P tiles of chunk it; off-diagonal block of T' of
-    //      chunk it-1 ----
-    if ((pw == 1 || pw == 2) && it < nchunks) {
-      // lower 16x16 tiles of K K^T (wave 1) or Q K^T (wave 2), with the
-      // decay: A (strict lower, times b) and P (lower incl.)
-      const int j = it;
-      typename SM::Buf &bf = sm.buf[j % NBUF];
-      const bool isq = pw == 2;
-      const bf16(*Xr)[SM::LDK] = isq ? bf.Q : bf.K;
-      constexpr int TI[3] = {0, 1, 1}, TJ[3] = {0, 1, 0};
-      f32x4 acc[3];
-#pragma unroll
-      for (int tt = 0; tt < 3; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KKD; ++kk) {
-        const bf16x8 x0 = ld8(&Xr[lr][32 * kk + 8 * lg]);
-        const bf16x8 x1 = ld8(&Xr[16 + lr][32 * kk + 8 * lg]);
-        const bf16x8 k0 = ld8(&bf.K[lr][32 * kk + 8 * lg]);
-        const bf16x8 k1 = ld8(&bf.K[16 + lr][32 * kk + 8 * lg]);
-        acc[0] = mfma_bf16(x0, k0, acc[0]);
-        acc[1] = mfma_bf16(x1, k1, acc[1]);
-        acc[2] = mfma_bf16(x1, k0, acc[2]);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 3; ++tt) {
-        const int sc = 16 * TJ[tt] + lr;
-        const int r0 = 16 * TI[tt] + 4 * lg;
-        const float gs = bf.g[sc];
-        const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&bf.g[r0]);
-        f32x4 val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dec = (GATE == kGateNone) ? 1.0f : __expf(gr4[e] - gs);
-          val[e] = acc[tt][e] * dec;
-        }
-        if (!isq) {
-          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.beta[r0]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? b4[e] * val[e] : 0.0f;
-          if (TI[tt] == TJ[tt]) {
-            *reinterpret_cast<f32x4 *>(&sm.ATd[TI[tt]][lr][4 * lg]) = val;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.A10[j & 1][4 * lg + e][lr] = val[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? val[e] : 0.0f;
-          bf16x4 h4, l4;
-          split4(val, h4, l4);
-          *reinterpret_cast<bf16x4 *>(&bf.Ph[sc][r0]) = h4;
-          *reinterpret_cast<bf16x4 *>(&bf.Pl[sc][r0]) = l4;
-        }
-      }
+    // phase Y: the diagonal A (wave 1) and P (wave 2) tiles of chunk it;
+    // the off-diagonal block of T' of chunk it-1 (wave 0)
+    if (pw >= 1 && it < nchunks) {
+      if (pw == 1) two_tiles(sm.buf[it % NBUF], it, false, 0, 0, false, 1, 1);
+      else two_tiles(sm.buf[it % NBUF], it, true, 0, 0, true, 1, 1);
     }
     if (pw == 0 && it >= 1 && it - 1 < nchunks) {
       // T10 = -T11 (A10 T00) of chunk it-1 (its diagonal blocks were solved

@@ -282,6 +282,9 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   for (int it = 0; it < nchunks + 2; ++it) {
     // ================= phase X =================
+    // every load in flight is one of chunk it's, consumed right here: one
+    // wait for all of them on every path
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     if (it < nchunks) {
       // write staged chunk it; padding tokens (past T) become zeros with log a = 0
       typename SM::Raw &rw = sm.raw[it & 1];
