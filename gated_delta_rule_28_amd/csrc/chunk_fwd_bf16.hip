@@ -76,8 +76,9 @@ __device__ __forceinline__ float scan32_inclusive(float x) {
 template <int DK, int DVS>
 struct __align__(16) PipeSmem {
   static constexpr int LDK = DK + 8;   // bf16 stride of [C][DK] rows (pads banks)
-  static constexpr int LDV = DVS + 8;  // bf16 stride of [C][DVS] rows
-  static constexpr int LDC = C + 8;    // bf16 stride of [*][C] rows
+  static constexpr int LDV = DVS + 16; // bf16 stride of [C][DVS] rows (transposing reads
+                                       // of 8 rows hit 64 distinct banks)
+  static constexpr int LDC = C + 16;   // bf16 stride of [*][C] rows (likewise)
   struct __align__(16) Buf {           // one chunk, live for four iterations
     bf16 Q[C][LDK];                    // q rows, dk permuted
     bf16 K[C][LDK];                    // k rows, dk permuted
@@ -90,9 +91,8 @@ struct __align__(16) PipeSmem {
   float A10[2][16][20];                // block (1,0) of A, row-major
   bf16 Th[2][C][LDC], Tl[2][C][LDC];   // T'^T: [s][r] = T'[r][s], T' = (I+A)^{-1} diag(b);
                                        // rows 16..31 x cols 0..15 stay zero
-  float Ost[DVS / 16][C][20];          // per-state-wave output tile, for wide stores
-  float T0T[16][20];                   // T_00^T (solver scratch, chunk being solved)
-  float T1[16][20];                    // T_11 row-major (solver scratch)
+  float TdT[2][16][20];                // diagonal blocks of T = (I+A)^{-1}, transposed:
+                                       // [b][c][r] = T[16b+r][16b+c] (solver output)
   float X[16][20];                     // X^T (solver scratch)
 };
 
@@ -167,6 +167,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr];
     }
     __syncthreads();
+
+    // byte offsets of this lane's output values from a chunk's first row
+    int ooff[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ooff[rb][e] = (int)sizeof(OutT) * ((16 * rb + 4 * lg + e) * H * DV + col0 + lr);
 
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;            // chunk of this iteration
@@ -243,6 +251,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (s >= 0) {
         const typename SM::Buf &bs = sm.buf[s % NBUF];
         const int t0 = s * C, n = min(C, T - t0);
+        const long orow = (tok0 + (long)t0 * H) * DV;   // element offset of the chunk's first row
+        const rsrc_t ro = make_rsrc(o + orow, (long)sizeof(OutT) * ((long)B * T * H * DV - orow));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
@@ -255,35 +265,28 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(ph, Uh, acc);
           acc = mfma_bf16(pl, Uh, acc);
           acc = mfma_bf16(ph, Ul, acc);
-          // transpose through this wave's LDS tile: lane holds column lr,
-          // rows 4 lg + e; the stores below write 4 columns of one row
+          // lane holds O rows 16 rb + 4 lg + e of column col0 + lr: stored
+          // straight from the accumulator (16 lanes write 16 adjacent values
+          // of a row); rows past the end of the sequence are not written
+          if (n == C) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sm.Ost[wave][16 * rb + 4 * lg + e][lr] = acc[e];
-        }
-        {
-          // rows lane/4 and 16 + lane/4, columns 4 (lane & 3) .. + 3
+            for (int e = 0; e < 4; ++e) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[rb][e]);
+          } else {
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int r = 16 * hf + (lane >> 2);
-            const f32x4 ov = *reinterpret_cast<const f32x4 *>(&sm.Ost[wave][r][4 * (lane & 3)]);
-            if (r < n) {
-              OutT *dst = o + (tok0 + (long)(t0 + r) * H) * DV + slice * DVS + 16 * wave + 4 * (lane & 3);
-              if constexpr (sizeof(OutT) == 4) {
-                *reinterpret_cast<f32x4 *>(dst) = ov;
-              } else {
-                *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
-              }
-            }
+            for (int e = 0; e < 4; ++e)
+              if (16 * rb + 4 * lg + e < n) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[rb][e]);
           }
         }
         const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
+        // k^T operand (row = dk 16 mb + lr; slots = tokens 16 h + 4 lg + c,
+        // the order of the U' rows) by two transposing reads of k; dk
+        // 16 mb + 4 j is stored at perm32(16 mb + 4 j) = 8 j + 32 (mb >> 1)
+        // + 4 (mb & 1): a lane part plus a constant per mb
+        const bf16 *kt = &bs.K[4 * lg + (lr >> 2)][8 * (lr & 3)];
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb) {
-          // k^T operand (row = dk 16 mb + lr; slots = tokens 16 h + 4 lg + c,
-          // the order of the U' rows) by two transposing reads of k
-          const int dcol = perm32(16 * mb + 4 * (lr & 3));
-          const bf16x8 a = cat(ld_tr4(&bs.K[4 * lg + (lr >> 2)][dcol]),
-                               ld_tr4(&bs.K[16 + 4 * lg + (lr >> 2)][dcol]));
+          const int dc = 32 * (mb >> 1) + 4 * (mb & 1);
+          const bf16x8 a = cat(ld_tr4(kt + dc), ld_tr4(kt + 16 * SM::LDK + dc));
           f32x4 acc = Sacc[mb] * glast;
           acc = mfma_bf16(a, Wh, acc);
           acc = mfma_bf16(a, Wl, acc);
@@ -319,27 +322,32 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int NV = C * VCS;          // v items (<= 256)
   constexpr bool QK2 = 2 * NI > 192, V2 = NV > 192;
   static_assert(2 * NI <= 256 && NV <= 256, "staging items exceed the staging threads");
+  static_assert(NI % 64 == 0, "q/k items of a wave must all come from one matrix");
+  // A wave's q/k items all come from one matrix (NI is a multiple of 64), so
+  // each wave reads through one buffer descriptor.  Loads are unconditional:
+  // items past the end re-load the last one, rows past the end of the
+  // sequence read the next rows (or zeros past the end of the tensor), and
+  // only valid items and rows are written to LDS.
   struct QKItem {
-    bool valid, is_k;
+    bool valid, is_k;                  // wave-uniform
     int r0, c0;
-    const bf16 *base;                  // row 0 of this chain at column c0
+    int voff[4];                       // byte offsets of rows r0..r0+3 from the chunk's row 0
   };
   struct VItem {
     bool valid;
     int r, c0;
-    const bf16 *base;
+    int voff;
   };
-  // items past the end re-load a valid one (loads stay unconditional, so no
-  // branch merges the staging registers); only valid items are written
-  auto qk_item = [&](int idx) {
+  auto qk_item = [&](int wave_first, int idx) {
     QKItem m;
-    m.valid = idx < 2 * NI;
+    m.valid = wave_first < 2 * NI;
+    m.is_k = wave_first < NI;
     const int i = min(idx, 2 * NI - 1);
-    m.is_k = i < NI;
-    const int it = m.is_k ? i : i - NI;
+    const int it = m.is_k ? min(i, NI - 1) : i - NI;
     m.r0 = 4 * (it / DCS);
     m.c0 = 8 * (it % DCS);
-    m.base = (m.is_k ? k : q) + tok0 * DK + m.c0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m.voff[r] = 2 * ((m.r0 + r) * H * DK + m.c0);
     return m;
   };
   auto v_item = [&](int idx) {
@@ -348,32 +356,34 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int i = min(idx, NV - 1);
     m.r = i / VCS;
     m.c0 = 8 * (i % VCS);
-    m.base = v + tok0 * DV + slice * DVS + m.c0;
+    m.voff = 2 * (m.r * H * DV + slice * DVS + m.c0);
     return m;
   };
-  const QKItem qa = qk_item(pt), qb = qk_item(pt + 128);
+  const QKItem qa = qk_item(64 * pw, pt), qb = qk_item(64 * pw + 128, pt + 128);
   const VItem va = v_item(pt), vb = v_item(pt + 64);
-  const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
+  const long qk_total = (long)B * T * H * DK;          // elements of q (and of k, v)
+  const bf16 *qa_src = qa.is_k ? k : q, *qb_src = qb.is_k ? k : q;
   bf16x8 stga[4], stgb[4], stgva, stgvb;
   float stg_b = 0.f, stg_la = 0.f;
 
-  // Rows past the end of the sequence re-load the last valid row (always in
-  // bounds); they are zeroed when written to LDS.
   auto stage_chunk = [&](int j) {
-    const int t0 = j * C, last = T - 1;
+    const long row0 = tok0 + (long)j * C * H;          // token row of the chunk's first token
     if (pw == 0) {   // b and log a feed wave 0's cumsum; issued first
-      const long ri = tok0 + (long)min(t0 + (lane & (C - 1)), last) * H;
-      stg_b = beta[ri];
-      if constexpr (GATE == kGateScalar) stg_la = log_alpha[ri];
+      const int off = 4 * (lane & (C - 1)) * H;
+      stg_b = buf_ld1f(make_rsrc(beta + row0, 4 * ((long)B * T * H - row0)), off);
+      if constexpr (GATE == kGateScalar)
+        stg_la = buf_ld1f(make_rsrc(log_alpha + row0, 4 * ((long)B * T * H - row0)), off);
     }
+    const rsrc_t ra = make_rsrc(qa_src + row0 * DK, 2 * (qk_total - row0 * DK));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) stga[i] = ld8(qa.base + (long)min(t0 + qa.r0 + i, last) * qk_stride);
-    stgva = ld8(va.base + (long)min(t0 + va.r, last) * v_stride);
+    for (int i = 0; i < 4; ++i) stga[i] = buf_ld8(ra, qa.voff[i]);
+    stgva = buf_ld8(make_rsrc(v + row0 * DV, 2 * (qk_total - row0 * DV)), va.voff);
     if (QK2 && pw == 1) {
+      const rsrc_t rb = make_rsrc(qb_src + row0 * DK, 2 * (qk_total - row0 * DK));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) stgb[i] = ld8(qb.base + (long)min(t0 + qb.r0 + i, last) * qk_stride);
+      for (int i = 0; i < 4; ++i) stgb[i] = buf_ld8(rb, qb.voff[i]);
     }
-    if (V2 && pw == 2) stgvb = ld8(vb.base + (long)min(t0 + vb.r, last) * v_stride);
+    if (V2 && pw == 2) stgvb = buf_ld8(make_rsrc(v + row0 * DV, 2 * (qk_total - row0 * DV)), vb.voff);
   };
   auto zero_if = [](bf16x8 x, bool z) -> bf16x8 {
     if (z) {
@@ -447,6 +457,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // ---- solver wave: its own loop, so the staging registers of waves
     //      0..2 are not live across the solve ----
     __syncthreads();
+    float x[16];                       // column lane & 15 of block (lane >> 4) & 1 of T
     for (int it = 0; it < nchunks + 2; ++it) {
       // phase X: diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it-1;
       // lane = (block, column); right-looking forward substitution: once
@@ -456,7 +467,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const int j = it - 1;
         const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
         const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
-        float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
         // every needed entry of A^T (rows s, columns r > s: 36 float4) is
@@ -467,19 +477,39 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
             a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
+        // keep the loads ahead of the dependent steps (the scheduler would
+        // otherwise sink them next to their uses to save registers)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s2 = 0; s2 < 15; ++s2) {
 #pragma unroll
           for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
         }
-        if (lane < 32) {   // lanes 32..63 hold duplicates
-          const float bcol = sm.buf[j % NBUF].beta[o0 + col];
-          typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        if (lane < 32) {   // lanes 32..63 hold duplicates; fp32 T^T rows only
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4 *>(&sm.TdT[blk][col][4 * q4]) =
+                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+        }
+      }
+      __syncthreads();
+      // phase Y: the off-diagonal A and P tiles of chunk it, then the bf16
+      // hi/lo diagonal blocks of T' of chunk it-1 from this phase X's solve
+      if (it < nchunks) two_tiles(sm.buf[it % NBUF], it, false, 1, 0, true, 1, 0);
+      if (it >= 1 && it - 1 < nchunks) {
+        const int j = it - 1;
+        const float *bj = sm.buf[j % NBUF].beta;
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        if (lane < 32) {
+          // T'[o0 + r][o0 + col] = T[o0 + r][o0 + col] b_{o0 + col}, r = 0..15,
+          // is row o0 + col of T'^T
+          // (x still holds this lane's column of T from phase X)
+          const int blk = lane >> 4, col = lane & 15, o0 = 16 * blk;
+          const float bcol = bj[o0 + col];
           unsigned h8[2][4], l8[2][4];
 #pragma unroll
           for (int r = 0; r < 16; r += 2)
             split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-          // T'[o0 + r][o0 + col] for r = 0..15 is row o0 + col of T'^T
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) =
@@ -487,20 +517,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) =
                 u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
           }
-          if (blk == 1) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.T1[r][col] = x[r];
-          } else {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-              *reinterpret_cast<f32x4 *>(&sm.T0T[col][4 * q4]) =
-                  f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-          }
         }
       }
-      __syncthreads();
-      // phase Y: the off-diagonal A and P tiles of chunk it
-      if (it < nchunks) two_tiles(sm.buf[it % NBUF], it, false, 1, 0, true, 1, 0);
       __syncthreads();
     }
     return;
@@ -550,11 +568,12 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       // T10 = -T11 (A10 T00) of chunk it-1 (its diagonal blocks were solved
       // in this iteration's phase X)
       const int j = it - 1;
-      f32x4 xa = mm16_split(&sm.A10[j & 1][0][0], 20, &sm.T0T[0][0], 20,
+      const float *bj = sm.buf[j % NBUF].beta;
+      f32x4 xa = mm16_split(&sm.A10[j & 1][0][0], 20, &sm.TdT[0][0][0], 20,
                             f32x4{0.f, 0.f, 0.f, 0.f}, lane);
       *reinterpret_cast<f32x4 *>(&sm.X[lr][4 * lg]) = xa;   // X^T
-      f32x4 z = mm16_split(&sm.T1[0][0], 20, &sm.X[0][0], 20, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-      const float bc = sm.buf[j % NBUF].beta[lr];
+      f32x4 z = mm16_split_lt(&sm.TdT[1][0][0], 20, &sm.X[0][0], 20, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
+      const float bc = bj[lr];
       bf16x4 h4, l4;
       split4(-z * bc, h4, l4);
       *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;

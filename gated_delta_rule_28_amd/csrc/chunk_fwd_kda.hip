@@ -436,6 +436,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
             a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
+        // keep the loads ahead of the dependent steps
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s2 = 0; s2 < 15; ++s2) {
 #pragma unroll
