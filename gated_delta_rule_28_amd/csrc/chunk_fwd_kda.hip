@@ -21,18 +21,21 @@
 //
 // The in-chunk Gram and scores need e^{G_r - G_s} per channel.  The page
 // digest notes that these decays can be tiny, so direct division is
-// unstable and a log-space, two-level scheme is used.  Here the factors are
-// taken about the chunk's middle token m: e^{G_r - G_m} and e^{G_m - G_s}
-// are each at most e^{8 max|log a|}, so for |log a| <= 10 the factored
-// operands stay inside the fp32/bf16 range and the Gram is two MFMA
-// products.  A chunk holding any |log a| > 10 (a near-hard reset) takes an
-// exact path instead: every (r, s, c) decay is formed directly in fp32.
+// unstable and a log-space, two-level scheme is used.  Here they factor
+// about the chunk start: e^{G_r - G_s} = e^{G_r} e^{-G_s}, so the Gram is
+// (K o e^G)(K o e^{-G})^T and the scores (Q o e^G)(K o e^{-G})^T, reusing
+// the state-side operands on the left.  e^{-G_s} <= e^{-g_last}, so while
+// every channel's in-chunk log decay stays above -64 the factored operands
+// stay inside the fp32/bf16 range.  A chunk with a channel below that (a
+// near-hard reset) takes an exact path instead: every (r, s, c) decay is
+// formed directly in fp32.
 //
 // Mapping and pipeline as in the scalar-gate kernel: one workgroup per
 // (batch, head, Dv slice); DVS/16 state waves keep the state in MFMA
 // accumulators; 4 prep waves run two chunks ahead:
 //   X(i): stage chunk i (raw q/k/v/log a), derive the decayed operands of i-1
-//   Y(i): cumsum of chunk i; Gram + solve (wave 2) and scores (wave 3) of i-1
+//   Y(i): cumsum of chunk i (waves 0, 1); Gram + solve (wave 2, which has a
+//         loop of its own and stages nothing) and scores (wave 3) of i-1
 //   state: chunk i-2.
 #include "common.h"
 #include "internal.h"
@@ -41,39 +44,36 @@
 namespace gdr {
 namespace {
 
-constexpr int KC = 16;                    // tokens per chunk
-constexpr int KNPW = 4;                   // prep waves
-constexpr float kMaxFactoredLog = 10.0f;  // |log a| bound of the factored in-chunk Gram
+constexpr int KC = 16;               // tokens per chunk
+constexpr int KNPW = 4;              // prep waves
+constexpr float kMaxSpan = 64.0f;    // per-channel in-chunk log-decay bound of the factored Gram
 
 template <int DK, int DVS>
 struct __align__(16) KdaSmem {
-  static constexpr int LDK = DK + 8;      // bf16 stride of [16][DK] tiles
+  static constexpr int LDK = DK + 8;      // bf16 stride of [16][DK] tiles read by rows
+  static constexpr int LDC = DK + 16;     // bf16 stride of C, read transposed (8 rows x 8 banks)
   static constexpr int LDG = DK + 4;      // fp32 stride of G
-  static constexpr int LDV = DVS + 8;     // bf16 stride of v rows
-  static constexpr int LDT = KC + 8;      // bf16 stride of transposed 16x16 tiles
+  static constexpr int LDV = DVS + 16;    // bf16 stride of v rows, read transposed
+  static constexpr int LDT = KC;          // bf16 stride of 16x16 tiles, read transposed
   struct __align__(16) Raw {              // staged chunk, natural channel order
     bf16 Q[KC][LDK], K[KC][LDK];
     float G[KC][LDG];                     // log a, then its in-chunk cumulative sum
     float beta[KC];
-    int extreme;                          // some |log a| > kMaxFactoredLog
+    int extreme;                          // some channel's in-chunk log decay < -kMaxSpan
   };
-  struct __align__(16) Der {              // state-side operands of one chunk
+  struct __align__(16) Der {              // operands of one chunk
     bf16 Kh[KC][LDK], Kl[KC][LDK];        // K o e^G, dk permuted
     bf16 Qh[KC][LDK], Ql[KC][LDK];        // Q o e^G, dk permuted
-    bf16 Ch[KC][LDK], Cl[KC][LDK];        // K o e^{g_last - G}, natural order
+    bf16 Ch[KC][LDC], Cl[KC][LDC];        // K o e^{g_last - G}, natural order
     bf16 Ph[KC][LDT], Pl[KC][LDT];        // P^T: [s][r] = P[r][s]
     float egl[DK];                        // e^{g_last}
   };
   Raw raw[2];
   bf16 V[3][KC][LDV];                     // v rows of this slice, natural order
   Der der[2];
-  // factored operands of the in-chunk Gram, reference token m = 7
-  bf16 Lkh[KC][LDK], Lkl[KC][LDK];        // K o e^{G - G_m}
-  bf16 Lqh[KC][LDK], Lql[KC][LDK];        // Q o e^{G - G_m}
-  bf16 Rkh[KC][LDK], Rkl[KC][LDK];        // K o e^{G_m - G}
+  bf16 Rkh[KC][LDK], Rkl[KC][LDK];        // K o e^{-G}, dk permuted (right operand of A and P)
   float AT[16][20];                       // A^T for the solve
   bf16 Th[KC][LDT], Tl[KC][LDT];          // T'^T
-  float Ost[DVS / 16][KC][20];            // per-state-wave output tile
 };
 
 template <int DK, int DVS, typename OutT>
@@ -83,7 +83,6 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const float *__restrict__ log_alpha, const float *initial_state,
                      OutT *__restrict__ o, float *final_state, int B, int T, int H) {
   constexpr int NSW = DVS / 16;
-  constexpr int NT = 64 * (NSW + KNPW);
   constexpr int DV = DK;
   constexpr int NSLICE = DV / DVS;
   constexpr int KKD = DK / 32;
@@ -109,8 +108,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
   const int bb = chain / H, hh = chain % H;
   const int nchunks = (T + KC - 1) / KC;
-  const long tok0 = (long)bb * T * H + hh;
-
+  const long tok0 = (long)bb * T * H + hh;   // token row of token 0 of this chain
+  const long ntok = (long)B * T * H;         // token rows of every input tensor
   const bf16x4 zero4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
 
   if (wave < NSW) {
@@ -128,6 +127,10 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr];
     }
+    // byte offsets of this lane's output values from a chunk's first row
+    int ooff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ooff[e] = (int)sizeof(OutT) * ((4 * lg + e) * H * DV + col0 + lr);
     __syncthreads();
 
     for (int it = 0; it < nchunks + 2; ++it) {
@@ -186,19 +189,17 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         f32x4 acc = QS;
         acc = mfma_bf16(pa, cat(uh4, uh4), acc);
         acc = mfma_bf16(pa, cat(ul4, zero4), acc);
+        // lane holds O rows 4 lg + e of column col0 + lr: stored straight from
+        // the accumulator; rows past the end of the sequence are not written
+        const long orow = (tok0 + (long)t0 * H) * DV;
+        const rsrc_t ro = make_rsrc(o + orow, (long)sizeof(OutT) * (ntok * DV - orow));
+        if (n == KC) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Ost[wave][4 * lg + e][lr] = acc[e];
-        {
-          const int r = lane >> 2;
-          const f32x4 ov = *reinterpret_cast<const f32x4 *>(&sm.Ost[wave][r][4 * (lane & 3)]);
-          if (r < n) {
-            OutT *dst = o + (tok0 + (long)(t0 + r) * H) * DV + col0 + 4 * (lane & 3);
-            if constexpr (sizeof(OutT) == 4) {
-              *reinterpret_cast<f32x4 *>(dst) = ov;
-            } else {
-              *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
-            }
-          }
+          for (int e = 0; e < 4; ++e) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * lg + e < n) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[e]);
         }
         const bf16x8 b1 = cat(uh4, uh4), b2 = cat(ul4, zero4);
 #pragma unroll
@@ -231,50 +232,206 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // =======================================================================
   const int pw = wave - NSW;
   const int pt = tid - 64 * NSW;       // 0..255
-  // staging items: q/k = 4 tokens x 8 channels (pt < 2 NI); log a = 4 channels
-  // of one token (two per thread); v = 8 columns of one token; beta pt < 16
+  // Staging runs on prep waves 0, 1 and 3; wave 2 (Gram and solve) runs a
+  // loop of its own.  Waves 0 and 1 load k and q (item = RPI tokens x 8
+  // columns, 64 items per matrix, so each wave reads one matrix through one
+  // buffer descriptor); wave 3 loads v (item = 8 columns of one token);
+  // all three load log a (float4 items) and wave 0 beta.  Loads are
+  // unconditional inside each wave; rows past the end of the sequence read
+  // the next rows (or zeros past the end of a tensor) and are zeroed when
+  // written to LDS.
   constexpr int DCS = DK / 8;
-  constexpr int NI = (KC / 4) * DCS;   // <= 64
+  constexpr int RPI = KC * DCS / 64;   // tokens per q/k item (4 at d = 128, 2 at d = 64)
   constexpr int VCS = DVS / 8;
-  constexpr int NV = KC * VCS;         // <= 128
-  constexpr int NLA = KC * DK / 4;     // f32x4 items of log a (<= 512)
-  static_assert(2 * NI <= 256 && NV <= 128 && NLA <= 512, "staging items");
-  const bool has_qk = pt < 2 * NI;
-  const bool is_k = pt < NI;
-  const int item = is_k ? pt : pt - NI;
-  const int it_r0 = 4 * (item / DCS), it_c0 = 8 * (item % DCS);
-  const int vi = pt - 128;
-  const bool has_v = vi >= 0 && vi < NV;
-  const int v_r = vi / VCS, v_c0 = 8 * (vi % VCS);
-  // load addresses: threads without an item re-load a valid one, so every
-  // prep thread issues the same unconditional loads (no branch merges the
-  // staging registers, and nothing waits on the loads before they are used)
-  const int ld_item = min(item, NI - 1);
-  const int ld_r0 = 4 * (ld_item / DCS), ld_c0 = 8 * (ld_item % DCS);
-  const int ld_vi = min(max(vi, 0), NV - 1);
-  const int ld_vr = ld_vi / VCS;
-  const bf16 *qk_base = (is_k ? k : q) + tok0 * DK + ld_c0;
-  const bf16 *v_base = v + tok0 * DV + slice * DVS + 8 * (ld_vi % VCS);
-  const float *la_base = log_alpha + tok0 * DK;
-  const long qk_stride = (long)H * DK, v_stride = (long)H * DV;
-  bf16x8 stg[4], stgv;
-  f32x4 stgl[2];
-  float stg_b = 0.f;
+  constexpr int NV = KC * VCS;         // v items (128 or 64)
+  constexpr int NVS = NV / 64;         // v items per wave-3 thread
+  constexpr int NLA = KC * DK / 4;     // float4 items of log a (512 or 256)
+  constexpr int NLS = (NLA + 191) / 192;   // log a items per staging thread
+  static_assert(RPI * 64 == KC * DCS && NV % 64 == 0 && NLA % 64 == 0, "staging items");
+  const int ps = (pw == 3 ? 128 : 64 * pw) + lane;   // staging thread index 0..191
+  const bool is_k = pw == 0;
+  const int q_r0 = RPI * (lane / DCS), q_c0 = 8 * (lane % DCS);
+  int v_r[NVS], v_c0[NVS];
+#pragma unroll
+  for (int h = 0; h < NVS; ++h) {
+    const int vi = lane + 64 * h;
+    v_r[h] = vi / VCS;
+    v_c0[h] = 8 * (vi % VCS);
+  }
+  // one set of 16-byte load slots per staging thread, whatever its tensor:
+  // q/k rows on waves 0 and 1, v items on wave 3 (surplus slots re-load the
+  // first item), so the staging loads are the same straight-line code on
+  // every staging wave
+  constexpr int NL = RPI > NVS ? RPI : NVS;
+  int soff[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    soff[i] = (pw < 2) ? 2 * ((q_r0 + (i < RPI ? i : 0)) * H * DK + q_c0)
+                       : 2 * (v_r[i < NVS ? i : 0] * H * DV + slice * DVS + v_c0[i < NVS ? i : 0]);
+  const bf16 *ssrc = pw == 0 ? k : (pw == 1 ? q : v);   // wave-uniform
+  bool la_ok[NLS];                     // wave-uniform
+  int lavoff[NLS], la_r[NLS], la_c4[NLS];
+#pragma unroll
+  for (int h = 0; h < NLS; ++h) {
+    const int li = ps + 192 * h;
+    la_ok[h] = li < NLA;
+    const int lc = la_ok[h] ? li : 0;
+    la_r[h] = lc / (DK / 4);
+    la_c4[h] = 4 * (lc % (DK / 4));
+    lavoff[h] = 4 * (la_r[h] * H * DK + la_c4[h]);
+  }
 
-  // rows past the end of the sequence re-load the last valid row (always in
-  // bounds); they are zeroed when written to LDS
-  auto stage_chunk = [&](int j) {
-    const int t0 = j * KC, last = T - 1;
+  // operands of chunk j = it - 1 (its G was summed in the previous phase
+  // Y); all four prep waves take a share: thread = (channel pair, tokens)
+  auto derive = [&](int j) {
+    const typename SM::Raw &rw = sm.raw[j & 1];
+    typename SM::Der &d = sm.der[j & 1];
+    constexpr int NCP = DK / 2;                 // channel pairs
+    constexpr int TPG = KC * NCP / 256;         // tokens per thread
+    const int cp = pt % NCP, tq = pt / NCP;
+    const int c0 = 2 * cp;
+    const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
+    if (tq == 0) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
+    // e^{-g_last}: scales K o e^{g_last - G} to K o e^{-G}; it can overflow
+    // only in chunks that take the exact Gram path, which do not read Rk
+    const float eng0 = __expf(-gl[0]), eng1 = __expf(-gl[1]);
+    const int pc = perm32(c0);
+    auto put2 = [](bf16 *hi, bf16 *lo, float x0, float x1) {
+      unsigned h, l;
+      split2(x0, x1, h, l);
+      *reinterpret_cast<unsigned *>(hi) = h;
+      *reinterpret_cast<unsigned *>(lo) = l;
+    };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) stg[i] = ld8(qk_base + (long)min(t0 + ld_r0 + i, last) * qk_stride);
-    stgv = ld8(v_base + (long)min(t0 + ld_vr, last) * v_stride);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int li = min(pt + 256 * h2, NLA - 1);
-      const int r = li / (DK / 4), c4 = 4 * (li % (DK / 4));
-      stgl[h2] = *reinterpret_cast<const f32x4 *>(la_base + (long)min(t0 + r, last) * qk_stride + c4);
+    for (int i = 0; i < TPG; ++i) {
+      const int r = TPG * tq + i;
+      const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      const float k0 = (float)rw.K[r][c0], k1 = (float)rw.K[r][c0 + 1];
+      const float q0 = (float)rw.Q[r][c0], q1 = (float)rw.Q[r][c0 + 1];
+      const float e0 = __expf(g[0]), e1 = __expf(g[1]);
+      const float c0e = k0 * __expf(gl[0] - g[0]), c1e = k1 * __expf(gl[1] - g[1]);
+      put2(&d.Kh[r][pc], &d.Kl[r][pc], k0 * e0, k1 * e1);
+      put2(&d.Qh[r][pc], &d.Ql[r][pc], q0 * e0, q1 * e1);
+      put2(&d.Ch[r][c0], &d.Cl[r][c0], c0e, c1e);
+      put2(&sm.Rkh[r][pc], &sm.Rkl[r][pc], c0e * eng0, c1e * eng1);
     }
-    stg_b = beta[tok0 + (long)min(t0 + (pt & (KC - 1)), last) * H];
+  };
+
+  // Gram (isq = false: A, then the solve) or scores (isq = true: P) of chunk j
+  auto gram_or_scores = [&](int j, bool isq) {
+    const typename SM::Raw &rw = sm.raw[j & 1];
+    typename SM::Der &d = sm.der[j & 1];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!rw.extreme) {
+      // (X o e^G)(K o e^{-G})^T with X = K or Q, in dk-permuted order
+      const bf16(*Lh)[SM::LDK] = isq ? d.Qh : d.Kh;
+      const bf16(*Ll)[SM::LDK] = isq ? d.Ql : d.Kl;
+#pragma unroll
+      for (int kk = 0; kk < KKD; ++kk) {
+        const bf16x8 ah = ld8(&Lh[lr][32 * kk + 8 * lg]);
+        const bf16x8 al = ld8(&Ll[lr][32 * kk + 8 * lg]);
+        const bf16x8 bh = ld8(&sm.Rkh[lr][32 * kk + 8 * lg]);
+        const bf16x8 bl = ld8(&sm.Rkl[lr][32 * kk + 8 * lg]);
+        acc = mfma_bf16(ah, bh, acc);
+        acc = mfma_bf16(ah, bl, acc);
+        acc = mfma_bf16(al, bh, acc);
+      }
+    } else {
+      // exact: every decay e^{G_rc - G_sc} formed directly (s <= r only)
+      const bf16(*X)[SM::LDK] = isq ? rw.Q : rw.K;
+      const int sc = lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * lg + e;
+        float sum = 0.0f;
+        if (sc <= r) {
+          for (int c = 0; c < DK; ++c)
+            sum += (float)X[r][c] * (float)rw.K[sc][c] * __expf(rw.G[r][c] - rw.G[sc][c]);
+        }
+        acc[e] = sum;
+      }
+    }
+    const int sc = lr, r0 = 4 * lg;
+    if (isq) {
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
+      bf16x4 h4, l4;
+      split4(val, h4, l4);
+      *reinterpret_cast<bf16x4 *>(&d.Ph[sc][r0]) = h4;
+      *reinterpret_cast<bf16x4 *>(&d.Pl[sc][r0]) = l4;
+      return;
+    }
+    f32x4 val;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? rw.beta[r0 + e] * acc[e] : 0.0f;
+    *reinterpret_cast<f32x4 *>(&sm.AT[sc][r0]) = val;   // AT[s][r] = A[r][s]
+    // T = (I + A)^{-1}, lane = column; right-looking forward substitution
+    const int col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+    // every needed entry of A^T is loaded before the dependent steps (the
+    // scheduling barrier keeps the loads there)
+    f32x4 a4[15][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+      for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
+        a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s2 = 0; s2 < 15; ++s2) {
+#pragma unroll
+      for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
+    }
+    if (lane < 16) {
+      const float bcol = rw.beta[col];
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      unsigned h8[2][4], l8[2][4];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        *reinterpret_cast<u32x4 *>(&sm.Th[col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+        *reinterpret_cast<u32x4 *>(&sm.Tl[col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+      }
+    }
+  };
+
+  if (pw == 2) {
+    // ---- Gram/solve wave: derivation share in phase X, A and T' in Y ----
+    __syncthreads();
+    for (int it = 0; it < nchunks + 2; ++it) {
+      if (it >= 1 && it - 1 < nchunks) derive(it - 1);
+      __syncthreads();
+      if (it >= 1 && it - 1 < nchunks) gram_or_scores(it - 1, false);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---- staging waves 0, 1, 3 ----
+  bf16x8 stg[NL];
+  f32x4 stgl[NLS];
+  float stg_b = 0.f;
+  auto stage_chunk = [&](int j) {
+    const long row0 = tok0 + (long)j * KC * H;
+    stg_b = buf_ld1f(make_rsrc(beta + row0, 4 * (ntok - row0)), 4 * (lane & (KC - 1)) * H);
+    const rsrc_t r = make_rsrc(ssrc + row0 * DK, 2 * (ntok - row0) * DK);   // DK == DV
+#pragma unroll
+    for (int i = 0; i < NL; ++i) stg[i] = buf_ld8(r, soff[i]);
+    const rsrc_t rl = make_rsrc(log_alpha + row0 * DK, 4 * (ntok - row0) * DK);
+#pragma unroll
+    for (int h = 0; h < NLS; ++h) stgl[h] = buf_ld4f(rl, lavoff[h]);
+  };
+  auto zero_rows = [](bf16x8 x, bool z) -> bf16x8 {
+    if (z) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
+    }
+    return x;
   };
 
   if (nchunks > 0) stage_chunk(0);
@@ -289,175 +446,42 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       // write staged chunk it; padding tokens (past T) become zeros with log a = 0
       typename SM::Raw &rw = sm.raw[it & 1];
       const int n = min(KC, T - it * KC);
-      if (has_qk) {
+      if (pw < 2) {
         bf16(*dst)[SM::LDK] = is_k ? rw.K : rw.Q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x8 x = stg[i];
-          if (it_r0 + i >= n) {
+        for (int i = 0; i < RPI; ++i)
+          *reinterpret_cast<bf16x8 *>(&dst[q_r0 + i][q_c0]) = zero_rows(stg[i], q_r0 + i >= n);
+      } else {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
-          }
-          *reinterpret_cast<bf16x8 *>(&dst[it_r0 + i][it_c0]) = x;
-        }
-      }
-      if (has_v) {
-        bf16x8 x = stgv;
-        if (v_r >= n) {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
-        }
-        *reinterpret_cast<bf16x8 *>(&sm.V[it % 3][v_r][v_c0]) = x;
+        for (int h = 0; h < NVS; ++h)
+          *reinterpret_cast<bf16x8 *>(&sm.V[it % 3][v_r[h]][v_c0[h]]) = zero_rows(stg[h], v_r[h] >= n);
       }
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int li = pt + 256 * h2;
-        if (li < NLA) {
-          const int r = li / (DK / 4), c4 = 4 * (li % (DK / 4));
-          *reinterpret_cast<f32x4 *>(&rw.G[r][c4]) = (r < n) ? stgl[h2] : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-      if (pt < KC) rw.beta[pt] = (pt < n) ? stg_b : 0.0f;
+      for (int h = 0; h < NLS; ++h)
+        if (la_ok[h])
+          *reinterpret_cast<f32x4 *>(&rw.G[la_r[h]][la_c4[h]]) =
+              (la_r[h] < n) ? stgl[h] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (pw == 0 && lane < KC) rw.beta[lane] = (lane < n) ? stg_b : 0.0f;
       if (pt == 0) rw.extreme = 0;
       if (it + 1 < nchunks) stage_chunk(it + 1);
     }
-    if (it >= 1 && it - 1 < nchunks) {
-      // derive the decayed operands of chunk j = it - 1 (its G was summed in
-      // the previous phase Y); thread = (channel pair, group of tokens)
-      const int j = it - 1;
-      const typename SM::Raw &rw = sm.raw[j & 1];
-      typename SM::Der &d = sm.der[j & 1];
-      constexpr int NCP = DK / 2;                 // channel pairs
-      constexpr int TPG = KC * NCP / 256;         // tokens per thread
-      const int cp = pt % NCP, tq = pt / NCP;
-      const int c0 = 2 * cp;
-      const f32x2 gm = *reinterpret_cast<const f32x2 *>(&rw.G[7][c0]);
-      const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
-      if (tq == 0) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
-      const int pc = perm32(c0);
-      auto put2 = [](bf16 (*hi)[SM::LDK], bf16 (*lo)[SM::LDK], int r, int c, float x0, float x1) {
-        unsigned h, l;
-        split2(x0, x1, h, l);
-        *reinterpret_cast<unsigned *>(&hi[r][c]) = h;
-        *reinterpret_cast<unsigned *>(&lo[r][c]) = l;
-      };
-#pragma unroll
-      for (int i = 0; i < TPG; ++i) {
-        const int r = TPG * tq + i;
-        const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
-        const float k0 = (float)rw.K[r][c0], k1 = (float)rw.K[r][c0 + 1];
-        const float q0 = (float)rw.Q[r][c0], q1 = (float)rw.Q[r][c0 + 1];
-        const float e0 = __expf(g[0]), e1 = __expf(g[1]);
-        const float c0e = __expf(gl[0] - g[0]), c1e = __expf(gl[1] - g[1]);
-        const float m0 = __expf(g[0] - gm[0]), m1 = __expf(g[1] - gm[1]);
-        const float n0 = __expf(gm[0] - g[0]), n1 = __expf(gm[1] - g[1]);
-        put2(d.Kh, d.Kl, r, pc, k0 * e0, k1 * e1);
-        put2(d.Qh, d.Ql, r, pc, q0 * e0, q1 * e1);
-        put2(d.Ch, d.Cl, r, c0, k0 * c0e, k1 * c1e);
-        put2(sm.Lkh, sm.Lkl, r, c0, k0 * m0, k1 * m1);
-        put2(sm.Lqh, sm.Lql, r, c0, q0 * m0, q1 * m1);
-        put2(sm.Rkh, sm.Rkl, r, c0, k0 * n0, k1 * n1);
-      }
-    }
+    if (it >= 1 && it - 1 < nchunks) derive(it - 1);
     __syncthreads();
 
     // ================= phase Y =================
-    if (it < nchunks && pt < DK) {
+    if (pw < 2 && it < nchunks && pt < DK) {
       // in-chunk cumulative log decay, one channel per thread; flag chunks
       // whose factored Gram could leave the floating-point range
       typename SM::Raw &rw = sm.raw[it & 1];
-      float acc = 0.0f, amax = 0.0f;
+      float acc = 0.0f;
 #pragma unroll
       for (int r = 0; r < KC; ++r) {
-        const float la = rw.G[r][pt];
-        amax = fmaxf(amax, fabsf(la));
-        acc += la;
+        acc += rw.G[r][pt];
         rw.G[r][pt] = acc;
       }
-      if (amax > kMaxFactoredLog) atomicOr(&rw.extreme, 1);
+      if (acc < -kMaxSpan) atomicOr(&rw.extreme, 1);
     }
-    if ((pw == 2 || pw == 3) && it >= 1 && it - 1 < nchunks) {
-      // Gram (wave 2: A, then the solve) or scores (wave 3: P) of chunk it-1
-      const int j = it - 1;
-      const typename SM::Raw &rw = sm.raw[j & 1];
-      const bool isq = pw == 3;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (!rw.extreme) {
-        const bf16(*Lh)[SM::LDK] = isq ? sm.Lqh : sm.Lkh;
-        const bf16(*Ll)[SM::LDK] = isq ? sm.Lql : sm.Lkl;
-#pragma unroll
-        for (int kk = 0; kk < KKD; ++kk) {
-          const bf16x8 ah = ld8(&Lh[lr][32 * kk + 8 * lg]);
-          const bf16x8 al = ld8(&Ll[lr][32 * kk + 8 * lg]);
-          const bf16x8 bh = ld8(&sm.Rkh[lr][32 * kk + 8 * lg]);
-          const bf16x8 bl = ld8(&sm.Rkl[lr][32 * kk + 8 * lg]);
-          acc = mfma_bf16(ah, bh, acc);
-          acc = mfma_bf16(ah, bl, acc);
-          acc = mfma_bf16(al, bh, acc);
-        }
-      } else {
-        // exact: every decay e^{G_rc - G_sc} formed directly (s <= r only)
-        const bf16(*X)[SM::LDK] = isq ? rw.Q : rw.K;
-        const int sc = lr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * lg + e;
-          float sum = 0.0f;
-          if (sc <= r) {
-            for (int c = 0; c < DK; ++c)
-              sum += (float)X[r][c] * (float)rw.K[sc][c] * __expf(rw.G[r][c] - rw.G[sc][c]);
-          }
-          acc[e] = sum;
-        }
-      }
-      const int sc = lr, r0 = 4 * lg;
-      if (isq) {
-        f32x4 val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
-        bf16x4 h4, l4;
-        split4(val, h4, l4);
-        *reinterpret_cast<bf16x4 *>(&sm.der[j & 1].Ph[sc][r0]) = h4;
-        *reinterpret_cast<bf16x4 *>(&sm.der[j & 1].Pl[sc][r0]) = l4;
-      } else {
-        f32x4 val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? rw.beta[r0 + e] * acc[e] : 0.0f;
-        *reinterpret_cast<f32x4 *>(&sm.AT[sc][r0]) = val;   // AT[s][r] = A[r][s]
-        // T = (I + A)^{-1}, lane = column; right-looking forward substitution
-        const int col = lane & 15;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
-        // every needed entry of A^T is loaded before the dependent steps
-        f32x4 a4[15][4];
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-          for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
-            a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
-        // keep the loads ahead of the dependent steps
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2) {
-#pragma unroll
-          for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
-        }
-        if (lane < 16) {
-          const float bcol = rw.beta[col];
-          typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-          unsigned h8[2][4], l8[2][4];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2)
-            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4 *>(&sm.Th[col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4 *>(&sm.Tl[col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
-          }
-        }
-      }
-    }
+    if (pw == 3 && it >= 1 && it - 1 < nchunks) gram_or_scores(it - 1, true);
     __syncthreads();
   }
 }
