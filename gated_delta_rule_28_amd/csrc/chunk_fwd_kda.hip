@@ -30,13 +30,14 @@
 // near-hard reset) takes an exact path instead: every (r, s, c) decay is
 // formed directly in fp32.
 //
-// Mapping and pipeline as in the scalar-gate kernel: one workgroup per
-// (batch, head, Dv slice); DVS/16 state waves keep the state in MFMA
-// accumulators; 4 prep waves run two chunks ahead:
-//   X(i): stage chunk i (raw q/k/v/log a), derive the decayed operands of i-1
-//   Y(i): cumsum of chunk i (waves 0, 1); Gram + solve (wave 2, which has a
-//         loop of its own and stages nothing) and scores (wave 3) of i-1
-//   state: chunk i-2.
+// Mapping as in the scalar-gate kernel: one workgroup per (batch, head, Dv
+// slice); DVS/16 state waves keep the state in MFMA accumulators; 4 prep
+// waves run two chunks ahead:
+//   X(i): waves 0, 1, 3 write chunk i (the threads that own a channel's log
+//         decays sum them as they write) and load chunk i+1; wave 2 forms A
+//         and solves it, wave 3 forms P, of chunk i-1
+//   Y(i): all prep waves derive the decayed operands of chunk i
+//   state: chunk i-2 (operand buffers three deep, T' two deep).
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -59,7 +60,8 @@ struct __align__(16) KdaSmem {
     bf16 Q[KC][LDK], K[KC][LDK];
     float G[KC][LDG];                     // log a, then its in-chunk cumulative sum
     float beta[KC];
-    int extreme;                          // some channel's in-chunk log decay < -kMaxSpan
+    int extreme[2];                       // per summing wave: some channel's in-chunk
+                                          // log decay < -kMaxSpan
   };
   struct __align__(16) Der {              // operands of one chunk
     bf16 Kh[KC][LDK], Kl[KC][LDK];        // K o e^G, dk permuted
@@ -70,10 +72,10 @@ struct __align__(16) KdaSmem {
   };
   Raw raw[2];
   bf16 V[3][KC][LDV];                     // v rows of this slice, natural order
-  Der der[2];
+  Der der[3];
   bf16 Rkh[KC][LDK], Rkl[KC][LDK];        // K o e^{-G}, dk permuted (right operand of A and P)
   float AT[16][20];                       // A^T for the solve
-  bf16 Th[KC][LDT], Tl[KC][LDT];          // T'^T
+  bf16 Th[2][KC][LDT], Tl[2][KC][LDT];    // T'^T
 };
 
 template <int DK, int DVS, typename OutT>
@@ -139,7 +141,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       bf16x4 uh4, ul4;
       if (s >= 0) {
         // ---- X: K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
-        const typename SM::Der &d = sm.der[s & 1];
+        const typename SM::Der &d = sm.der[s % 3];
         bf16x8 Sh[KKD], Sl[KKD];
 #pragma unroll
         for (int kk = 0; kk < KKD; ++kk) {
@@ -172,8 +174,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         bf16x4 rh4, rl4;
         split4(rr, rh4, rl4);
         // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
-        const bf16x8 ta = cat(ld_tr4(&sm.Th[4 * lg + (lr >> 2)][4 * (lr & 3)]),
-                              ld_tr4(&sm.Tl[4 * lg + (lr >> 2)][4 * (lr & 3)]));
+        const bf16x8 ta = cat(ld_tr4(&sm.Th[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                              ld_tr4(&sm.Tl[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]));
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         u = mfma_bf16(ta, cat(rh4, rh4), u);
         u = mfma_bf16(ta, cat(rl4, zero4), u);
@@ -182,7 +184,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       __syncthreads();
       if (s >= 0) {
         // ---- Y: O = Q^ S + P U; S <- Diag(e^{g_last}) S + (K o e^{g_last-G})^T U ----
-        const typename SM::Der &d = sm.der[s & 1];
+        const typename SM::Der &d = sm.der[s % 3];
         const int t0 = s * KC, n = min(KC, T - t0);
         const bf16x8 pa = cat(ld_tr4(&d.Ph[4 * lg + (lr >> 2)][4 * (lr & 3)]),
                               ld_tr4(&d.Pl[4 * lg + (lr >> 2)][4 * (lr & 3)]));
@@ -235,20 +237,17 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // Staging runs on prep waves 0, 1 and 3; wave 2 (Gram and solve) runs a
   // loop of its own.  Waves 0 and 1 load k and q (item = RPI tokens x 8
   // columns, 64 items per matrix, so each wave reads one matrix through one
-  // buffer descriptor); wave 3 loads v (item = 8 columns of one token);
-  // all three load log a (float4 items) and wave 0 beta.  Loads are
-  // unconditional inside each wave; rows past the end of the sequence read
-  // the next rows (or zeros past the end of a tensor) and are zeroed when
-  // written to LDS.
+  // buffer descriptor); wave 3 loads v (item = 8 columns of one token) and
+  // beta.  Thread c < Dk of waves 0 and 1 also loads the 16 log decays of
+  // channel c and sums them as it writes them.  Loads are unconditional
+  // inside each wave; rows past the end of the sequence read the next rows
+  // (or zeros past the end of a tensor) and are zeroed when written to LDS.
   constexpr int DCS = DK / 8;
   constexpr int RPI = KC * DCS / 64;   // tokens per q/k item (4 at d = 128, 2 at d = 64)
   constexpr int VCS = DVS / 8;
   constexpr int NV = KC * VCS;         // v items (128 or 64)
   constexpr int NVS = NV / 64;         // v items per wave-3 thread
-  constexpr int NLA = KC * DK / 4;     // float4 items of log a (512 or 256)
-  constexpr int NLS = (NLA + 191) / 192;   // log a items per staging thread
-  static_assert(RPI * 64 == KC * DCS && NV % 64 == 0 && NLA % 64 == 0, "staging items");
-  const int ps = (pw == 3 ? 128 : 64 * pw) + lane;   // staging thread index 0..191
+  static_assert(RPI * 64 == KC * DCS && NV % 64 == 0, "staging items");
   const bool is_k = pw == 0;
   const int q_r0 = RPI * (lane / DCS), q_c0 = 8 * (lane % DCS);
   int v_r[NVS], v_c0[NVS];
@@ -269,23 +268,14 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     soff[i] = (pw < 2) ? 2 * ((q_r0 + (i < RPI ? i : 0)) * H * DK + q_c0)
                        : 2 * (v_r[i < NVS ? i : 0] * H * DV + slice * DVS + v_c0[i < NVS ? i : 0]);
   const bf16 *ssrc = pw == 0 ? k : (pw == 1 ? q : v);   // wave-uniform
-  bool la_ok[NLS];                     // wave-uniform
-  int lavoff[NLS], la_r[NLS], la_c4[NLS];
-#pragma unroll
-  for (int h = 0; h < NLS; ++h) {
-    const int li = ps + 192 * h;
-    la_ok[h] = li < NLA;
-    const int lc = la_ok[h] ? li : 0;
-    la_r[h] = lc / (DK / 4);
-    la_c4[h] = 4 * (lc % (DK / 4));
-    lavoff[h] = 4 * (la_r[h] * H * DK + la_c4[h]);
-  }
+  const int la_c = (pw == 1 && DK > 64) ? 64 + lane : lane;   // channel summed by this thread
+  const bool sums = pw < 2 && 64 * pw + lane < DK;           // wave-uniform
 
-  // operands of chunk j = it - 1 (its G was summed in the previous phase
-  // Y); all four prep waves take a share: thread = (channel pair, tokens)
+  // operands of chunk j (its G was summed in phase X); all four prep waves
+  // take a share: thread = (channel pair, tokens)
   auto derive = [&](int j) {
     const typename SM::Raw &rw = sm.raw[j & 1];
-    typename SM::Der &d = sm.der[j & 1];
+    typename SM::Der &d = sm.der[j % 3];
     constexpr int NCP = DK / 2;                 // channel pairs
     constexpr int TPG = KC * NCP / 256;         // tokens per thread
     const int cp = pt % NCP, tq = pt / NCP;
@@ -317,15 +307,19 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   };
 
-  // Gram (isq = false: A, then the solve) or scores (isq = true: P) of chunk j
-  auto gram_or_scores = [&](int j, bool isq) {
+  // lower 16x16 tile (X o e^G)-decayed Gram of chunk j: X = K (isq false)
+  // or X = Q (isq true); lane holds rows 4 lg + e of column lr
+  auto tile = [&](int j, bool isq) -> f32x4 {
     const typename SM::Raw &rw = sm.raw[j & 1];
-    typename SM::Der &d = sm.der[j & 1];
+    const typename SM::Der &d = sm.der[j % 3];
+    const bool extreme = rw.extreme[0] | (DK > 64 ? rw.extreme[1] : 0);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (!rw.extreme) {
-      // (X o e^G)(K o e^{-G})^T with X = K or Q, in dk-permuted order
+    if (!extreme) {
+      // (X o e^G)(K o e^{-G})^T with X = K or Q, in dk-permuted order; the
+      // three products accumulate separately (independent MFMA chains)
       const bf16(*Lh)[SM::LDK] = isq ? d.Qh : d.Kh;
       const bf16(*Ll)[SM::LDK] = isq ? d.Ql : d.Kl;
+      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KKD; ++kk) {
         const bf16x8 ah = ld8(&Lh[lr][32 * kk + 8 * lg]);
@@ -333,9 +327,10 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const bf16x8 bh = ld8(&sm.Rkh[lr][32 * kk + 8 * lg]);
         const bf16x8 bl = ld8(&sm.Rkl[lr][32 * kk + 8 * lg]);
         acc = mfma_bf16(ah, bh, acc);
-        acc = mfma_bf16(ah, bl, acc);
-        acc = mfma_bf16(al, bh, acc);
+        a1 = mfma_bf16(ah, bl, a1);
+        a2 = mfma_bf16(al, bh, a2);
       }
+      acc += a1 + a2;
     } else {
       // exact: every decay e^{G_rc - G_sc} formed directly (s <= r only)
       const bf16(*X)[SM::LDK] = isq ? rw.Q : rw.K;
@@ -351,17 +346,26 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         acc[e] = sum;
       }
     }
+    return acc;
+  };
+  // P of chunk j (lower incl.), split hi/lo, transposed
+  auto scores = [&](int j) {
+    typename SM::Der &d = sm.der[j % 3];
+    const f32x4 acc = tile(j, true);
     const int sc = lr, r0 = 4 * lg;
-    if (isq) {
-      f32x4 val;
+    f32x4 val;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
-      bf16x4 h4, l4;
-      split4(val, h4, l4);
-      *reinterpret_cast<bf16x4 *>(&d.Ph[sc][r0]) = h4;
-      *reinterpret_cast<bf16x4 *>(&d.Pl[sc][r0]) = l4;
-      return;
-    }
+    for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
+    bf16x4 h4, l4;
+    split4(val, h4, l4);
+    *reinterpret_cast<bf16x4 *>(&d.Ph[sc][r0]) = h4;
+    *reinterpret_cast<bf16x4 *>(&d.Pl[sc][r0]) = l4;
+  };
+  // A of chunk j (strict lower, times b), then T' = (I + A)^{-1} diag(b)
+  auto gram_solve = [&](int j) {
+    const typename SM::Raw &rw = sm.raw[j & 1];
+    const f32x4 acc = tile(j, false);
+    const int sc = lr, r0 = 4 * lg;
     f32x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? rw.beta[r0 + e] * acc[e] : 0.0f;
@@ -394,19 +398,20 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        *reinterpret_cast<u32x4 *>(&sm.Th[col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-        *reinterpret_cast<u32x4 *>(&sm.Tl[col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+        *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+        *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
       }
     }
   };
 
   if (pw == 2) {
-    // ---- Gram/solve wave: derivation share in phase X, A and T' in Y ----
+    // ---- Gram/solve wave: A and T' of chunk it-1 in phase X, a share of the
+    //      derivation of chunk it in phase Y ----
     __syncthreads();
     for (int it = 0; it < nchunks + 2; ++it) {
-      if (it >= 1 && it - 1 < nchunks) derive(it - 1);
+      if (it >= 1 && it - 1 < nchunks) gram_solve(it - 1);
       __syncthreads();
-      if (it >= 1 && it - 1 < nchunks) gram_or_scores(it - 1, false);
+      if (it < nchunks) derive(it);
       __syncthreads();
     }
     return;
@@ -414,7 +419,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // ---- staging waves 0, 1, 3 ----
   bf16x8 stg[NL];
-  f32x4 stgl[NLS];
+  float stl[KC];                       // log decays of channel la_c, rows 0..15
   float stg_b = 0.f;
   auto stage_chunk = [&](int j) {
     const long row0 = tok0 + (long)j * KC * H;
@@ -424,7 +429,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int i = 0; i < NL; ++i) stg[i] = buf_ld8(r, soff[i]);
     const rsrc_t rl = make_rsrc(log_alpha + row0 * DK, 4 * (ntok - row0) * DK);
 #pragma unroll
-    for (int h = 0; h < NLS; ++h) stgl[h] = buf_ld4f(rl, lavoff[h]);
+    for (int rr = 0; rr < KC; ++rr) stl[rr] = buf_ld1f(rl, 4 * (rr * H * DK + la_c));
   };
   auto zero_rows = [](bf16x8 x, bool z) -> bf16x8 {
     if (z) {
@@ -451,37 +456,31 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int i = 0; i < RPI; ++i)
           *reinterpret_cast<bf16x8 *>(&dst[q_r0 + i][q_c0]) = zero_rows(stg[i], q_r0 + i >= n);
+        if (sums) {
+          // in-chunk cumulative log decay of channel la_c; flag the chunk
+          // when the factored Gram could leave the floating-point range
+          float acc = 0.0f;
+#pragma unroll
+          for (int rr = 0; rr < KC; ++rr) {
+            acc += (rr < n) ? stl[rr] : 0.0f;
+            rw.G[rr][la_c] = acc;
+          }
+          const unsigned long long bad = __ballot(acc < -kMaxSpan);
+          if (lane == 0) rw.extreme[pw] = bad != 0ull;
+        }
       } else {
 #pragma unroll
         for (int h = 0; h < NVS; ++h)
           *reinterpret_cast<bf16x8 *>(&sm.V[it % 3][v_r[h]][v_c0[h]]) = zero_rows(stg[h], v_r[h] >= n);
+        if (lane < KC) rw.beta[lane] = (lane < n) ? stg_b : 0.0f;
       }
-#pragma unroll
-      for (int h = 0; h < NLS; ++h)
-        if (la_ok[h])
-          *reinterpret_cast<f32x4 *>(&rw.G[la_r[h]][la_c4[h]]) =
-              (la_r[h] < n) ? stgl[h] : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (pw == 0 && lane < KC) rw.beta[lane] = (lane < n) ? stg_b : 0.0f;
-      if (pt == 0) rw.extreme = 0;
       if (it + 1 < nchunks) stage_chunk(it + 1);
     }
-    if (it >= 1 && it - 1 < nchunks) derive(it - 1);
+    if (pw == 3 && it >= 1 && it - 1 < nchunks) scores(it - 1);
     __syncthreads();
 
     // ================= phase Y =================
-    if (pw < 2 && it < nchunks && pt < DK) {
-      // in-chunk cumulative log decay, one channel per thread; flag chunks
-      // whose factored Gram could leave the floating-point range
-      typename SM::Raw &rw = sm.raw[it & 1];
-      float acc = 0.0f;
-#pragma unroll
-      for (int r = 0; r < KC; ++r) {
-        acc += rw.G[r][pt];
-        rw.G[r][pt] = acc;
-      }
-      if (acc < -kMaxSpan) atomicOr(&rw.extreme, 1);
-    }
-    if (pw == 3 && it >= 1 && it - 1 < nchunks) gram_or_scores(it - 1, true);
+    if (it < nchunks) derive(it);
     __syncthreads();
   }
 }
