@@ -176,6 +176,21 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int e = 0; e < 4; ++e)
         ooff[rb][e] = (int)sizeof(OutT) * ((16 * rb + 4 * lg + e) * H * DV + col0 + lr);
 
+    // hi/lo bf16 split of the state, the right operand of K S and Q S; it
+    // is formed at the end of the previous phase Y, as soon as S is final
+    bf16x8 Sh[KKD], Sl[KKD];
+    auto split_state = [&]() {
+#pragma unroll
+      for (int kk = 0; kk < KKD; ++kk) {
+        bf16x4 h0, l0, h1, l1;
+        split4(Sacc[2 * kk], h0, l0);
+        split4(Sacc[2 * kk + 1], h1, l1);
+        Sh[kk] = cat(h0, h1);
+        Sl[kk] = cat(l0, l1);
+      }
+    };
+    split_state();
+
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;            // chunk of this iteration
       f32x4 QS[2];                     // carried from phase X to phase Y
@@ -183,15 +198,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       // ---- phase X: K S, Q S, R = V - diag(gam) K S, U = T' R ----
       if (s >= 0) {
         const typename SM::Buf &bs = sm.buf[s % NBUF];
-        bf16x8 Sh[KKD], Sl[KKD];
-#pragma unroll
-        for (int kk = 0; kk < KKD; ++kk) {
-          bf16x4 h0, l0, h1, l1;
-          split4(Sacc[2 * kk], h0, l0);
-          split4(Sacc[2 * kk + 1], h1, l1);
-          Sh[kk] = cat(h0, h1);
-          Sl[kk] = cat(l0, l1);
-        }
         f32x4 KS[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -292,6 +298,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(a, Wl, acc);
           Sacc[mb] = acc;
         }
+        split_state();   // for the next chunk's phase X
       }
       __syncthreads();
     }
