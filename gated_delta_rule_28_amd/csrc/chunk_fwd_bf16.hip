@@ -17,31 +17,43 @@
 //   S  <- gam_last S + K^T diag(e^{g_last - g}) U      carried state
 //
 // Mapping.  One workgroup per (batch, head, Dv-slice of DVS columns): the Dv
-// columns of S, U and O are independent given K, b and g.  The workgroup is
-// a two-stage software pipeline over chunks of C = 32 tokens:
+// columns of S, U and O are independent given K, b and g.  Chunks are C = 32
+// tokens.  Roles:
 //
 //   state waves (DVS/16 of them) each own 16 state columns and keep them in
 //     MFMA accumulators for the whole sequence.  Every state-dependent
 //     product (K S, Q S, T'R, P U, K^T U') takes its right operand straight
-//     from accumulator registers: an accumulator tile holds rows 4g..4g+3 of
-//     column l&15, which is what a 16x16x32 B operand needs once the k order
-//     inside each 32-block is permuted (the left operands in LDS are stored
-//     with the same permutation).  The serial chain never touches LDS.
-//   prep waves (4) run ahead on the key-only work: they stage chunk i+1
-//     from HBM in registers while writing chunk i to LDS with its decay
-//     cumsum, form K K^T / Q K^T with the decay (A and P), and solve (I + A).
+//     from accumulator registers: an accumulator tile holds rows 4g..4g+3
+//     of a column, which is what a 16x16x32 B operand needs when the k axis
+//     of S is ordered so that tile pair (2kk, 2kk+1) holds dk 32kk + 8g + j
+//     (j < 4) and 32kk + 8g + 4 + j in its rows 4g + j.  q and k then stay
+//     in natural dk order in LDS.
+//   prep waves 0..2 bring chunks into LDS with LDS DMA (no registers, no
+//     LDS write instructions), scan the log decays and form the decayed
+//     K K^T / Q K^T tiles (A and P); prep wave 3 solves the diagonal 16x16
+//     blocks of (I + A) and forms the off-diagonal block of T'.
 //
-// Iteration i has two phases separated by workgroup barriers:
-//   X: prep writes chunk i (+ cumsum) and loads i+1; solves the diagonal
-//      16x16 blocks of (I + A) of chunk i-1     | state: K S, Q S, U of chunk i-2
-//   Y: prep forms the A and P tiles of chunk i and the off-diagonal block
-//      of T' of chunk i-1                        | state: O, S update of chunk i-2
-// so a chunk buffer lives three iterations (NBUF = 3), T' two.
+// Schedule.  Iteration i has two phases separated by workgroup barriers:
+//   X: DMA of chunk i+2 issued; A tiles of chunk i (and P10); T' of chunk
+//      i-1 completed (off-diagonal block, bf16 splits)  | state: K S, Q S, U of i-2
+//   Y: log-decay scan of chunk i+1; P tiles of chunk i; diagonal solve of
+//      chunk i                                          | state: O, S update of i-2
+// A chunk's inputs are in flight for about one and a half iterations before
+// the barrier that publishes them, so HBM latency is hidden; a chunk's input
+// slot lives five iterations (NIN = 5), its P tiles three, T' two.
+//
+// LDS layouts.  q, k rows are 2 DK bytes and v rows 2 DVS bytes with no
+// padding; the 16-byte blocks of each row are XOR-permuted by a function of
+// the row (swz_qk, swz_v) so that the row reads (16 rows, one block) and
+// the transposing reads (8 rows, 4 blocks) of the products hit distinct
+// banks.  The DMA lanes fetch the block that belongs at their fixed LDS
+// position.
 //
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
-// operand (S, R, U, T', P) is split into bf16 hi + lo and multiplied as
-// hi*hi + hi*lo + lo*hi (two products when the other side is exact), so
-// products carry ~16 significant bits and accumulate in fp32.
+// operand (S, R, U, T', P, and the fp32 solve outputs) is split into bf16
+// hi + lo and multiplied as hi*hi + hi*lo + lo*hi (two products when the
+// other side is exact), so products carry ~16 significant bits and
+// accumulate in fp32.
 #include <type_traits>
 
 #include "common.h"
@@ -53,7 +65,8 @@ namespace {
 
 constexpr int C = 32;      // tokens per chunk
 constexpr int NPW = 4;     // prep waves
-constexpr int NBUF = 3;    // chunk buffers: a chunk is written 2 iterations before its state pass
+constexpr int NIN = 5;     // input slots: DMA'd in iteration i-2, last read in iteration i+2
+constexpr int NPR = 3;     // P slots: written in iteration i, last read in iteration i+2
 
 // Inclusive prefix sum over lanes 0..31 of a wave with DPP row shifts
 // (within 16-lane rows) and a row broadcast of lane 15 into the next row.
@@ -73,27 +86,55 @@ __device__ __forceinline__ float scan32_inclusive(float x) {
   return x;
 }
 
+// Block permutation of a q/k row with NB 16-byte blocks (NB = 16: 256-byte
+// rows spanning all 64 banks; NB = 8: 128-byte rows, two rows per bank
+// sweep).  Row reads touch rows r0..r0+15 at one block: the value is a
+// bijection on those rows (on each row parity for NB = 8).  Transposing
+// reads touch rows 0..7 (or 8..15) at four adjacent blocks: the value moves
+// each row to a different group of four blocks, so 32 lanes meet each bank
+// pair at most twice (the minimum: every lane reads the same 8-byte half).
+template <int NB>
+__device__ __forceinline__ int swz_qk(int r) {
+  if constexpr (NB == 16) {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  } else {
+    const int j = (r >> 1) & 7;
+    return 4 * (j & 1) + (j >> 1);
+  }
+}
+
+// Block permutation of a v row (NB = 8: 128-byte rows; NB = 4: 64-byte
+// rows): the transposing reads of 8 rows x 2 blocks x 2 halves then hit 32
+// distinct bank pairs.
+template <int NB>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (NB == 8) return r & 6;
+  else return 2 * ((r >> 2) & 1);
+}
+
 template <int DK, int DVS>
 struct __align__(16) PipeSmem {
-  static constexpr int LDK = DK + 8;   // bf16 stride of [C][DK] rows (pads banks)
-  static constexpr int LDV = DVS + 16; // bf16 stride of [C][DVS] rows (transposing reads
-                                       // of 8 rows hit 64 distinct banks)
-  static constexpr int LDC = C + 16;   // bf16 stride of [*][C] rows (likewise)
-  struct __align__(16) Buf {           // one chunk, live for four iterations
-    bf16 Q[C][LDK];                    // q rows, dk permuted
-    bf16 K[C][LDK];                    // k rows, dk permuted
-    bf16 V[C][LDV];                    // v rows of this slice, natural order
-    bf16 Ph[C][LDC], Pl[C][LDC];       // P^T: [s][r] = P[r][s]; rows 16..31 x cols 0..15 stay zero
-    float gam[C], ec[C], beta[C], g[C];
+  static constexpr int LDC = C + 16;   // bf16 stride of [*][C] rows (transposing reads of
+                                       // 8 rows hit 64 distinct banks)
+  static constexpr int LDT = 24;       // bf16 stride of the 16x16 hi/lo blocks
+  struct __align__(16) In {            // one chunk's inputs (LDS DMA) and decay terms
+    bf16 Q[C][DK];                     // q rows, blocks permuted by swz_qk
+    bf16 K[C][DK];                     // k rows, likewise
+    bf16 V[C][DVS];                    // v rows of this slice, blocks permuted by swz_v
+    float la[64], beta[64];            // log a and b of the 64 tokens from the chunk start
+    float g[C], gam[C], ec[C], bt[C];  // g, e^g, e^{g_last - g}, b (0 past the end)
   };
-  Buf buf[NBUF];
+  struct __align__(16) PT {
+    bf16 Ph[C][LDC], Pl[C][LDC];       // P^T: [s][r] = P[r][s]; rows 16..31 x cols 0..15 stay zero
+  };
+  In in[NIN];
+  PT p[NPR];
   float ATd[2][16][20];                // diagonal 16x16 blocks of A, transposed: [b][s][r] = A[16b+r][16b+s]
-  float A10[2][16][20];                // block (1,0) of A, row-major
+  bf16 A10h[2][16][LDT], A10l[2][16][LDT];   // block (1,0) of A, transposed: [s][r] = A[16+r][s]
+  bf16 TTh[2][16][LDT], TTl[2][16][LDT];     // diagonal blocks of T = (I+A)^{-1}, transposed:
+                                             // [b][c][r] = T[16b+r][16b+c]
   bf16 Th[2][C][LDC], Tl[2][C][LDC];   // T'^T: [s][r] = T'[r][s], T' = (I+A)^{-1} diag(b);
                                        // rows 16..31 x cols 0..15 stay zero
-  float TdT[2][16][20];                // diagonal blocks of T = (I+A)^{-1}, transposed:
-                                       // [b][c][r] = T[16b+r][16b+c] (solver output)
-  float X[16][20];                     // X^T (solver scratch)
 };
 
 template <int DK, int DVS, typename OutT, int GATE>
@@ -107,9 +148,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int DV = DK;               // full value width (Dk == Dv)
   constexpr int NSLICE = DV / DVS;
   constexpr int KKD = DK / 32;         // 32-deep k steps over dk
-  constexpr int VCS = DVS / 8;         // 8-column segments of the value slice
+  constexpr int QB = DK / 8, VB = DVS / 8;      // 16-byte blocks per q/k and v row
+  constexpr int QRB = 2 * DK, VRB = 2 * DVS;    // bytes per q/k and v row
   static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
   using SM = PipeSmem<DK, DVS>;
+  using In = typename SM::In;
+  static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(In) % 16 == 0 && (C * QRB) % 1024 == 0 && (C * VRB) % 1024 == 0,
+                "DMA runs are whole 1 KiB waves");
   __shared__ SM sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -134,12 +180,21 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int nchunks = (T + C - 1) / C;
   const long tok0 = (long)bb * T * H + hh;   // row index of token 0 of this chain
 
+  // byte offset inside a q/k (v) tile of row r, natural 16-byte block b
+  auto qk_at = [](int r, int b) { return r * QRB + 16 * (b ^ swz_qk<QB>(r)); };
+  auto v_at = [](int r, int b) { return r * VRB + 16 * (b ^ swz_v<VB>(r)); };
+  // row reads of q/k: lane (lr, lg) takes row 16 t + lr, dk 32 kk + 8 lg .. +7;
+  // the permutation depends on r & 15 = lr only, so tile t adds 16 t rows
+  int kq_off[KKD];
+#pragma unroll
+  for (int kk = 0; kk < KKD; ++kk) kq_off[kk] = qk_at(lr, 4 * kk + lg);
+
   // the upper-right 16x16 blocks of P and T' are never written: zero once
   for (int i = tid; i < C * SM::LDC; i += NT) {
 #pragma unroll
-    for (int b = 0; b < NBUF; ++b) {
-      (&sm.buf[b].Ph[0][0])[i] = (bf16)0.0f;
-      (&sm.buf[b].Pl[0][0])[i] = (bf16)0.0f;
+    for (int b = 0; b < NPR; ++b) {
+      (&sm.p[b].Ph[0][0])[i] = (bf16)0.0f;
+      (&sm.p[b].Pl[0][0])[i] = (bf16)0.0f;
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -148,14 +203,15 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   }
 
-  // Both roles run nchunks + 2 iterations with two barriers each, so every
-  // wave executes the same sequence of workgroup barriers.
+  // Every role runs two prologue barriers and nchunks + 2 iterations of two
+  // barriers, so all waves execute the same sequence of workgroup barriers.
   if (wave < NSW) {
     // =====================================================================
     // state waves: the serial chunk-to-chunk pass, 16 state columns each
     // =====================================================================
     const int col0 = slice * DVS + 16 * wave;   // first value column of this wave
-    // S columns col0 + lr, rows 16 mb + 4 lg + e
+    // Sacc[mb][e] = S[srow(mb, e)][col0 + lr]
+    auto srow = [&](int mb, int e) { return 32 * (mb >> 1) + 8 * lg + 4 * (mb & 1) + e; };
     f32x4 Sacc[DK / 16];
 #pragma unroll
     for (int mb = 0; mb < DK / 16; ++mb) Sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -164,8 +220,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr];
+        for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)srow(mb, e) * DV + col0 + lr];
     }
+    __syncthreads();
     __syncthreads();
 
     // byte offsets of this lane's output values from a chunk's first row
@@ -175,6 +232,15 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         ooff[rb][e] = (int)sizeof(OutT) * ((16 * rb + 4 * lg + e) * H * DV + col0 + lr);
+    // v, transposing read: rows 16 rb + 4 lg + (lr >> 2), columns
+    // 16 wave + 4 (lr & 3) .. +3 (an 8-byte half of a 16-byte block)
+    const int v_off = v_at(4 * lg + (lr >> 2), 2 * wave + ((lr & 3) >> 1)) + 8 * (lr & 1);
+    // k^T operand of the state update for tile mb: rows (tokens) 4 lg + (lr >> 2)
+    // (+16), dk srow(mb, 0) + 4 (lr & 3) .. +3 = natural block (lr & 3) +
+    // 4 (mb >> 1), half mb & 1
+    int kt_off[KKD];
+#pragma unroll
+    for (int kk = 0; kk < KKD; ++kk) kt_off[kk] = qk_at(4 * lg + (lr >> 2), (lr & 3) + 4 * kk);
 
     // hi/lo bf16 split of the state, the right operand of K S and Q S; it
     // is formed at the end of the previous phase Y, as soon as S is final
@@ -197,15 +263,18 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       bf16x8 Uh, Ul, Wh, Wl;
       // ---- phase X: K S, Q S, R = V - diag(gam) K S, U = T' R ----
       if (s >= 0) {
-        const typename SM::Buf &bs = sm.buf[s % NBUF];
+        const In &bs = sm.in[s % NIN];
+        const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
+        const char *Qb = reinterpret_cast<const char *>(&bs.Q[0][0]);
+        const char *Vb = reinterpret_cast<const char *>(&bs.V[0][0]);
         f32x4 KS[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KKD; ++kk) {
-            const bf16x8 ak = ld8(&bs.K[16 * rb + lr][32 * kk + 8 * lg]);
-            const bf16x8 aq = ld8(&bs.Q[16 * rb + lr][32 * kk + 8 * lg]);
+            const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
+            const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
             a1 = mfma_bf16(ak, Sh[kk], a1);
             a2 = mfma_bf16(aq, Sh[kk], a2);
             a1 = mfma_bf16(ak, Sl[kk], a1);
@@ -219,7 +288,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int rb = 0; rb < 2; ++rb) {
           const int r0 = 16 * rb + 4 * lg;
           // V[r0 + c][16 wave + lr], c = 0..3, by a transposing read
-          const bf16x4 vv = ld_tr4(&bs.V[r0 + (lr >> 2)][16 * wave + 4 * (lr & 3)]);
+          const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(Vb + 16 * rb * VRB + v_off));
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                                 : *reinterpret_cast<const f32x4 *>(&bs.gam[r0]);
           f32x4 rr;
@@ -255,7 +324,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       __syncthreads();
       // ---- phase Y: O = diag(gam) Q S + P U; S <- gam_last S + K^T U' ----
       if (s >= 0) {
-        const typename SM::Buf &bs = sm.buf[s % NBUF];
+        const In &bs = sm.in[s % NIN];
+        const typename SM::PT &ps = sm.p[s % NPR];
         const int t0 = s * C, n = min(C, T - t0);
         const long orow = (tok0 + (long)t0 * H) * DV;   // element offset of the chunk's first row
         const rsrc_t ro = make_rsrc(o + orow, (long)sizeof(OutT) * ((long)B * T * H * DV - orow));
@@ -264,10 +334,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                                 : *reinterpret_cast<const f32x4 *>(&bs.gam[16 * rb + 4 * lg]);
           f32x4 acc = gm4 * QS[rb];
-          const bf16x8 ph = cat(ld_tr4(&bs.Ph[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
-                                ld_tr4(&bs.Ph[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
-          const bf16x8 pl = cat(ld_tr4(&bs.Pl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
-                                ld_tr4(&bs.Pl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+          const bf16x8 ph = cat(ld_tr4(&ps.Ph[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                ld_tr4(&ps.Ph[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+          const bf16x8 pl = cat(ld_tr4(&ps.Pl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                ld_tr4(&ps.Pl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
           acc = mfma_bf16(ph, Uh, acc);
           acc = mfma_bf16(pl, Uh, acc);
           acc = mfma_bf16(ph, Ul, acc);
@@ -284,15 +354,12 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           }
         }
         const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
-        // k^T operand (row = dk 16 mb + lr; slots = tokens 16 h + 4 lg + c,
-        // the order of the U' rows) by two transposing reads of k; dk
-        // 16 mb + 4 j is stored at perm32(16 mb + 4 j) = 8 j + 32 (mb >> 1)
-        // + 4 (mb & 1): a lane part plus a constant per mb
-        const bf16 *kt = &bs.K[4 * lg + (lr >> 2)][8 * (lr & 3)];
+        const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb) {
-          const int dc = 32 * (mb >> 1) + 4 * (mb & 1);
-          const bf16x8 a = cat(ld_tr4(kt + dc), ld_tr4(kt + 16 * SM::LDK + dc));
+          const char *p = Kb + kt_off[mb >> 1] + 8 * (mb & 1);
+          const bf16x8 a = cat(ld_tr4(reinterpret_cast<const bf16 *>(p)),
+                               ld_tr4(reinterpret_cast<const bf16 *>(p + 16 * QRB)));
           f32x4 acc = Sacc[mb] * glast;
           acc = mfma_bf16(a, Wh, acc);
           acc = mfma_bf16(a, Wl, acc);
@@ -308,171 +375,115 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) SF[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr] = Sacc[mb][e];
+        for (int e = 0; e < 4; ++e) SF[(long)srow(mb, e) * DV + col0 + lr] = Sacc[mb][e];
     }
     return;
   }
 
   // =======================================================================
-  // prep waves: stage chunks from HBM, decay cumsum, A / P tiles, the solve
+  // prep waves
   // =======================================================================
   const int pw = wave - NSW;           // prep wave index 0..NPW-1
-  const int pt = tid - 64 * NSW;       // prep thread index 0..255
-  // Staging runs on prep waves 0..2 (192 threads); wave 3 solves instead.
-  // q/k item = a 4-token x 8-column block of k (index < NI) or q (NI <=
-  // index < 2 NI), adjacent lanes on adjacent column segments (128-byte row
-  // runs); v item = one 8-column segment of one token of this slice.  Each
-  // staging thread takes q/k item pt and v item pt; wave 1 also takes q/k
-  // item pt + 128 and wave 2 v item pt + 64 when there are more than 192.
-  constexpr int DCS = DK / 8;          // 8-column segments of a q/k row
-  constexpr int NI = (C / 4) * DCS;    // items per matrix (<= 128)
-  constexpr int NV = C * VCS;          // v items (<= 256)
-  constexpr bool QK2 = 2 * NI > 192, V2 = NV > 192;
-  static_assert(2 * NI <= 256 && NV <= 256, "staging items exceed the staging threads");
-  static_assert(NI % 64 == 0, "q/k items of a wave must all come from one matrix");
-  // A wave's q/k items all come from one matrix (NI is a multiple of 64), so
-  // each wave reads through one buffer descriptor.  Loads are unconditional:
-  // items past the end re-load the last one, rows past the end of the
-  // sequence read the next rows (or zeros past the end of the tensor), and
-  // only valid items and rows are written to LDS.
-  struct QKItem {
-    bool valid, is_k;                  // wave-uniform
-    int r0, c0;
-    int voff[4];                       // byte offsets of rows r0..r0+3 from the chunk's row 0
-  };
-  struct VItem {
-    bool valid;
-    int r, c0;
-    int voff;
-  };
-  auto qk_item = [&](int wave_first, int idx) {
-    QKItem m;
-    m.valid = wave_first < 2 * NI;
-    m.is_k = wave_first < NI;
-    const int i = min(idx, 2 * NI - 1);
-    const int it = m.is_k ? min(i, NI - 1) : i - NI;
-    m.r0 = 4 * (it / DCS);
-    m.c0 = 8 * (it % DCS);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m.voff[r] = 2 * ((m.r0 + r) * H * DK + m.c0);
-    return m;
-  };
-  auto v_item = [&](int idx) {
-    VItem m;
-    m.valid = idx < NV;
-    const int i = min(idx, NV - 1);
-    m.r = i / VCS;
-    m.c0 = 8 * (i % VCS);
-    m.voff = 2 * (m.r * H * DV + slice * DVS + m.c0);
-    return m;
-  };
-  const QKItem qa = qk_item(64 * pw, pt), qb = qk_item(64 * pw + 128, pt + 128);
-  const VItem va = v_item(pt), vb = v_item(pt + 64);
-  const long qk_total = (long)B * T * H * DK;          // elements of q (and of k, v)
-  const bf16 *qa_src = qa.is_k ? k : q, *qb_src = qb.is_k ? k : q;
-  bf16x8 stga[4], stgb[4], stgva, stgvb;
-  float stg_b = 0.f, stg_la = 0.f;
 
-  auto stage_chunk = [&](int j) {
-    const long row0 = tok0 + (long)j * C * H;          // token row of the chunk's first token
-    if (pw == 0) {   // b and log a feed wave 0's cumsum; issued first
-      const int off = 4 * (lane & (C - 1)) * H;
-      stg_b = buf_ld1f(make_rsrc(beta + row0, 4 * ((long)B * T * H - row0)), off);
-      if constexpr (GATE == kGateScalar)
-        stg_la = buf_ld1f(make_rsrc(log_alpha + row0, 4 * ((long)B * T * H - row0)), off);
-    }
-    const rsrc_t ra = make_rsrc(qa_src + row0 * DK, 2 * (qk_total - row0 * DK));
+  // A (X = K, strict lower, times b) or P (X = Q, lower incl.) tile (ti, tj)
+  // of X K^T with the decay, as the MFMA accumulator: lane (lr, lg) holds
+  // rows 16 ti + 4 lg + e of column 16 tj + lr
+  auto tile_acc = [&](const In &bf, bool isq, int ti, int tj) {
+    const char *X = reinterpret_cast<const char *>(isq ? &bf.Q[0][0] : &bf.K[0][0]);
+    const char *Kc = reinterpret_cast<const char *>(&bf.K[0][0]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) stga[i] = buf_ld8(ra, qa.voff[i]);
-    stgva = buf_ld8(make_rsrc(v + row0 * DV, 2 * (qk_total - row0 * DV)), va.voff);
-    if (QK2 && pw == 1) {
-      const rsrc_t rb = make_rsrc(qb_src + row0 * DK, 2 * (qk_total - row0 * DK));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) stgb[i] = buf_ld8(rb, qb.voff[i]);
-    }
-    if (V2 && pw == 2) stgvb = buf_ld8(make_rsrc(v + row0 * DV, 2 * (qk_total - row0 * DV)), vb.voff);
+    for (int kk = 0; kk < KKD; ++kk)
+      acc = mfma_bf16(ld8(reinterpret_cast<const bf16 *>(X + 16 * ti * QRB + kq_off[kk])),
+                      ld8(reinterpret_cast<const bf16 *>(Kc + 16 * tj * QRB + kq_off[kk])), acc);
+    return acc;
   };
-  auto zero_if = [](bf16x8 x, bool z) -> bf16x8 {
-    if (z) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
-    }
-    return x;
-  };
-  auto write_qk = [&](typename SM::Buf &bf, const QKItem &m, const bf16x8 *x, int n) {
-    bf16(*dst)[SM::LDK] = m.is_k ? bf.K : bf.Q;
-    const int p0 = perm32(m.c0), p1 = perm32(m.c0 + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 y = zero_if(x[i], m.r0 + i >= n);
-      *reinterpret_cast<bf16x4 *>(&dst[m.r0 + i][p0]) = lo4(y);
-      *reinterpret_cast<bf16x4 *>(&dst[m.r0 + i][p1]) = hi4(y);
-    }
-  };
-  auto write_v = [&](typename SM::Buf &bf, const VItem &m, bf16x8 x, int n) {
-    *reinterpret_cast<bf16x8 *>(&bf.V[m.r][m.c0]) = zero_if(x, m.r >= n);
-  };
-
-  // lower 16x16 tiles of X K^T with the decay, two per wave: A (X = K,
-  // strict lower, times b) or P (X = Q, lower incl.) of chunk j
-  auto store_tile = [&](typename SM::Buf &bf, int j, f32x4 acc, int ti, int tj, bool isq) {
+  auto decayed = [&](const In &bf, f32x4 acc, int ti, int tj, bool isq) {
     const int sc = 16 * tj + lr;
     const int r0 = 16 * ti + 4 * lg;
     const float gs = bf.g[sc];
     const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&bf.g[r0]);
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.bt[r0]);
     f32x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float dec = (GATE == kGateNone) ? 1.0f : __expf(gr4[e] - gs);
-      val[e] = acc[e] * dec;
+      val[e] = isq ? ((sc <= r0 + e) ? acc[e] * dec : 0.0f)
+                   : ((sc < r0 + e) ? b4[e] * acc[e] * dec : 0.0f);
     }
-    if (!isq) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.beta[r0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? b4[e] * val[e] : 0.0f;
-      if (ti == tj) {
-        *reinterpret_cast<f32x4 *>(&sm.ATd[ti][lr][4 * lg]) = val;   // A^T of the block
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.A10[j & 1][4 * lg + e][lr] = val[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? val[e] : 0.0f;
-      bf16x4 h4, l4;
-      split4(val, h4, l4);
-      *reinterpret_cast<bf16x4 *>(&bf.Ph[sc][r0]) = h4;
-      *reinterpret_cast<bf16x4 *>(&bf.Pl[sc][r0]) = l4;
-    }
+    return val;
   };
-  auto two_tiles = [&](typename SM::Buf &bf, int j, bool q1, int ti1, int tj1, bool q2, int ti2,
-                       int tj2) {
-    const bf16(*X1)[SM::LDK] = q1 ? bf.Q : bf.K;
-    const bf16(*X2)[SM::LDK] = q2 ? bf.Q : bf.K;
-    f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KKD; ++kk) {
-      const int c = 32 * kk + 8 * lg;
-      acc1 = mfma_bf16(ld8(&X1[16 * ti1 + lr][c]), ld8(&bf.K[16 * tj1 + lr][c]), acc1);
-      acc2 = mfma_bf16(ld8(&X2[16 * ti2 + lr][c]), ld8(&bf.K[16 * tj2 + lr][c]), acc2);
-    }
-    store_tile(bf, j, acc1, ti1, tj1, q1);
-    store_tile(bf, j, acc2, ti2, tj2, q2);
+  auto store_p = [&](typename SM::PT &pt, f32x4 val, int ti, int tj) {
+    bf16x4 h4, l4;
+    split4(val, h4, l4);
+    *reinterpret_cast<bf16x4 *>(&pt.Ph[16 * tj + lr][16 * ti + 4 * lg]) = h4;
+    *reinterpret_cast<bf16x4 *>(&pt.Pl[16 * tj + lr][16 * ti + 4 * lg]) = l4;
   };
 
   if (pw == 3) {
-    // ---- solver wave: its own loop, so the staging registers of waves
-    //      0..2 are not live across the solve ----
+    // ---- solver wave ----
     __syncthreads();
-    float x[16];                       // column lane & 15 of block (lane >> 4) & 1 of T
+    __syncthreads();
+    float x[16];                       // column lane & 15 of diagonal block (lane >> 4) & 1 of T
     for (int it = 0; it < nchunks + 2; ++it) {
-      // phase X: diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it-1;
+      // phase X: T' of chunk it-1.  Diagonal blocks: T'[o0 + r][o0 + col] =
+      // T[o0 + r][o0 + col] b_{o0 + col} from the solve's registers.  Block
+      // (1,0): T10 = -T11 A10 T00, so T'10 = -(T11 (A10 T00)) diag(b_0), two
+      // 16x16x16 split products with the first result fed to the second as
+      // its B operand straight from the accumulator.
+      if (it >= 1 && it - 1 < nchunks) {
+        const int j = it - 1;
+        const float *bj = sm.in[j % NIN].bt;
+        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+        if (lane < 32) {
+          const int blk = lane >> 4, col = lane & 15, o0 = 16 * blk;
+          const float bcol = bj[o0 + col];
+          unsigned h8[2][4], l8[2][4];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            *reinterpret_cast<u32x4_t *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) =
+                u32x4_t{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4_t *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) =
+                u32x4_t{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+          }
+        }
+        // Y1 = A10 T00: A operand A10[m][4 lg ..] = column m of A10^T rows 4 lg..;
+        // B operand T00[4 lg ..][n] = row n of T00^T
+        const bf16x4 ah = ld_tr4(&sm.A10h[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 al = ld_tr4(&sm.A10l[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 bh = *reinterpret_cast<const bf16x4 *>(&sm.TTh[0][lr][4 * lg]);
+        const bf16x4 bl = *reinterpret_cast<const bf16x4 *>(&sm.TTl[0][lr][4 * lg]);
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        y = mfma16_bf16(ah, bh, y);
+        y = mfma16_bf16(ah, bl, y);
+        y = mfma16_bf16(al, bh, y);
+        bf16x4 yh, yl;
+        split4(y, yh, yl);
+        // Z = T11 Y1: A operand T11[m][4 lg ..] = column m of T11^T rows 4 lg..
+        const bf16x4 th = ld_tr4(&sm.TTh[1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 tl = ld_tr4(&sm.TTl[1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z = mfma16_bf16(th, yh, z);
+        z = mfma16_bf16(th, yl, z);
+        z = mfma16_bf16(tl, yh, z);
+        // lane holds Z[4 lg + e][lr]: T'^T[lr][16 + 4 lg + e] = -Z b_lr
+        const float bc = bj[lr];
+        bf16x4 h4, l4;
+        split4(-z * bc, h4, l4);
+        *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;
+        *reinterpret_cast<bf16x4 *>(&sm.Tl[j & 1][lr][16 + 4 * lg]) = l4;
+      }
+      __syncthreads();
+      // phase Y: diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it;
       // lane = (block, column); right-looking forward substitution: once
       // x_s is final it updates all later rows, so the dependent chain is
       // one FMA per step
-      if (it >= 1 && it - 1 < nchunks) {
-        const int j = it - 1;
+      if (it < nchunks) {
         const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
+        (void)o0;
         const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
@@ -492,37 +503,16 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
         }
-        if (lane < 32) {   // lanes 32..63 hold duplicates; fp32 T^T rows only
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4 *>(&sm.TdT[blk][col][4 * q4]) =
-                f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-        }
-      }
-      __syncthreads();
-      // phase Y: the off-diagonal A and P tiles of chunk it, then the bf16
-      // hi/lo diagonal blocks of T' of chunk it-1 from this phase X's solve
-      if (it < nchunks) two_tiles(sm.buf[it % NBUF], it, false, 1, 0, true, 1, 0);
-      if (it >= 1 && it - 1 < nchunks) {
-        const int j = it - 1;
-        const float *bj = sm.buf[j % NBUF].beta;
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        // T^T hi/lo rows for the off-diagonal block (lanes 32..63 hold duplicates)
         if (lane < 32) {
-          // T'[o0 + r][o0 + col] = T[o0 + r][o0 + col] b_{o0 + col}, r = 0..15,
-          // is row o0 + col of T'^T
-          // (x still holds this lane's column of T from phase X)
-          const int blk = lane >> 4, col = lane & 15, o0 = 16 * blk;
-          const float bcol = bj[o0 + col];
           unsigned h8[2][4], l8[2][4];
 #pragma unroll
-          for (int r = 0; r < 16; r += 2)
-            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+          for (int r = 0; r < 16; r += 2) split2(x[r], x[r + 1], h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+          typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) =
-                u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) =
-                u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+            *reinterpret_cast<u32x4_t *>(&sm.TTh[blk][col][8 * hf]) = u32x4_t{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4_t *>(&sm.TTl[blk][col][8 * hf]) = u32x4_t{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
           }
         }
       }
@@ -531,60 +521,124 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     return;
   }
 
-  // ---- staging waves 0..2 ----
-  if (nchunks > 0) stage_chunk(0);
+  // ---- prep waves 0..2: LDS DMA, decay scan, A and P tiles ----
+  // DMA shares: wave 0 v (+ log a, b), wave 1 k, wave 2 q.  Instruction i of
+  // a matrix fills LDS bytes 1024 i .. +1023 of its tile: lane l lands at
+  // row i RPI + l / BPR, stored block l % BPR, and fetches the natural block
+  // that the row's permutation puts there.
+  constexpr int NQI = C * QRB / 1024, NVI = C * VRB / 1024;
+  constexpr int NI = (NQI > NVI) ? NQI : NVI;
+  constexpr bool SCALAR = (GATE == kGateScalar);
+  constexpr int N0 = NVI + 1 + (SCALAR ? 1 : 0);   // DMA instructions per chunk, wave 0
+  constexpr int N12 = NQI;                         // waves 1 and 2
+  unsigned voff[NI];
+  if (pw == 0) {
+    constexpr int BPR = VRB / 16, RPI = 1024 / VRB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + lane / BPR, sb = lane % BPR;
+      voff[i] = (unsigned)(row * H * DV * 2 + 2 * slice * DVS + 16 * (sb ^ swz_v<VB>(row)));
+    }
+  } else {
+    constexpr int BPR = QRB / 16, RPI = 1024 / QRB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + lane / BPR, sb = lane % BPR;
+      voff[i] = (unsigned)(row * H * DK * 2 + 16 * (sb ^ swz_qk<QB>(row)));
+    }
+  }
+  const unsigned soff = (unsigned)(lane * H * 4);   // log a / b of token `lane`
+
+  auto issue = [&](int j) {
+    In &dst = sm.in[j % NIN];
+    const int n = min(C, T - j * C);
+    const long row0 = tok0 + (long)j * C * H;         // token row of the chunk's first token
+    if (pw == 0) {
+      // v rows (all slices' columns of rows < n are inside the descriptor)
+      const u32x4 rv = rsrc_words(v + row0 * DV, 2L * ((long)(n - 1) * H * DV + DV));
+      const unsigned lv = lds_addr(&dst.V[0][0]);
+#pragma unroll
+      for (int i = 0; i < NVI; ++i) lds_dma16(rv, voff[i], lv + 1024 * i);
+      lds_dma4(rsrc_words(beta + row0, 4L * ((long)(n - 1) * H + 1)), soff, lds_addr(&dst.beta[0]));
+      if constexpr (SCALAR)
+        lds_dma4(rsrc_words(log_alpha + row0, 4L * ((long)(n - 1) * H + 1)), soff, lds_addr(&dst.la[0]));
+    } else {
+      const bf16 *src = (pw == 1) ? k : q;
+      const u32x4 rq = rsrc_words(src + row0 * DK, 2L * ((long)(n - 1) * H * DK + DK));
+      const unsigned lq = lds_addr(pw == 1 ? &dst.K[0][0] : &dst.Q[0][0]);
+#pragma unroll
+      for (int i = 0; i < NQI; ++i) lds_dma16(rq, voff[i], lq + 1024 * i);
+    }
+  };
+  // wait for every DMA of chunk j+1 when chunk j+2 was issued after it
+  auto wait_prev = [&](bool newer_issued) {
+    if (newer_issued) {
+      if (pw == 0) wait_vmcnt<N0>();
+      else wait_vmcnt<N12>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+  // in-chunk cumulative log decay of chunk j (wave 0): inclusive scan over
+  // lanes 0..C-1; padded tokens carry log a = 0 and b = 0
+  auto scan = [&](int j) {
+    In &bf = sm.in[j % NIN];
+    const int n = min(C, T - j * C);
+    const float la = (SCALAR && lane < n) ? bf.la[lane] : 0.0f;
+    const float sc = scan32_inclusive(la);
+    const float glast = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), C - 1));
+    if (lane < C) {
+      bf.g[lane] = sc;
+      bf.gam[lane] = __expf(sc);
+      bf.ec[lane] = __expf(glast - sc);
+      bf.bt[lane] = (lane < n) ? bf.beta[lane] : 0.0f;
+    }
+  };
+
+  // prologue: chunks 0 and 1 in flight, chunk 0 landed and scanned
+  if (pw < 3) {
+    if (nchunks > 0) issue(0);
+    if (nchunks > 1) issue(1);
+    wait_prev(nchunks > 1);
+  }
+  __syncthreads();
+  if (pw == 0 && nchunks > 0) scan(0);
   __syncthreads();
 
   for (int it = 0; it < nchunks + 2; ++it) {
-    // phase X: write chunk it (+ decay cumsum on wave 0), stage chunk it+1.
-    // Every load in flight is one of chunk it's, consumed right here: one
-    // wait for all of them, on every path, so no later register reuse waits
-    // on a load that some skipped branch might have left pending.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // phase X: DMA of chunk it+2; A tiles and P10 of chunk it; then wait
+    // until this wave's DMA of chunk it+1 has landed
+    const bool more = it + 2 < nchunks;
+    if (more) issue(it + 2);
     if (it < nchunks) {
-      typename SM::Buf &bf = sm.buf[it % NBUF];
-      const int n = min(C, T - it * C);
-      if (qa.valid) write_qk(bf, qa, stga, n);
-      if (QK2 && pw == 1 && qb.valid) write_qk(bf, qb, stgb, n);
-      if (va.valid) write_v(bf, va, stgva, n);
-      if (V2 && pw == 2 && vb.valid) write_v(bf, vb, stgvb, n);
+      In &bf = sm.in[it % NIN];
       if (pw == 0) {
-        // in-chunk cumulative log decay: inclusive scan over lanes 0..C-1;
-        // padded tokens carry log a = 0 and b = 0
-        const float la = scan32_inclusive((lane < n) ? stg_la : 0.0f);
-        const float glast = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la), C - 1));
-        if (lane < C) {
-          bf.g[lane] = la;
-          bf.gam[lane] = __expf(la);
-          bf.ec[lane] = __expf(glast - la);
-          bf.beta[lane] = (lane < n) ? stg_b : 0.0f;
-        }
+        // A10, stored transposed as bf16 hi/lo for the off-diagonal solve
+        const f32x4 val = decayed(bf, tile_acc(bf, false, 1, 0), 1, 0, false);
+        bf16x4 h4, l4;
+        split4(val, h4, l4);
+        *reinterpret_cast<bf16x4 *>(&sm.A10h[it & 1][lr][4 * lg]) = h4;
+        *reinterpret_cast<bf16x4 *>(&sm.A10l[it & 1][lr][4 * lg]) = l4;
+      } else if (pw == 1) {
+        // diagonal A blocks, fp32 transposed, for this iteration's solve
+        const f32x4 a0 = tile_acc(bf, false, 0, 0), a1 = tile_acc(bf, false, 1, 1);
+        *reinterpret_cast<f32x4 *>(&sm.ATd[0][lr][4 * lg]) = decayed(bf, a0, 0, 0, false);
+        *reinterpret_cast<f32x4 *>(&sm.ATd[1][lr][4 * lg]) = decayed(bf, a1, 1, 1, false);
+      } else {
+        store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
       }
-      if (it + 1 < nchunks) stage_chunk(it + 1);
     }
+    wait_prev(more);
     __syncthreads();
 
-    // phase Y: the diagonal A (wave 1) and P (wave 2) tiles of chunk it;
-    // the off-diagonal block of T' of chunk it-1 (wave 0)
-    if (pw >= 1 && it < nchunks) {
-      if (pw == 1) two_tiles(sm.buf[it % NBUF], it, false, 0, 0, false, 1, 1);
-      else two_tiles(sm.buf[it % NBUF], it, true, 0, 0, true, 1, 1);
-    }
-    if (pw == 0 && it >= 1 && it - 1 < nchunks) {
-      // T10 = -T11 (A10 T00) of chunk it-1 (its diagonal blocks were solved
-      // in this iteration's phase X)
-      const int j = it - 1;
-      const float *bj = sm.buf[j % NBUF].beta;
-      f32x4 xa = mm16_split(&sm.A10[j & 1][0][0], 20, &sm.TdT[0][0][0], 20,
-                            f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-      *reinterpret_cast<f32x4 *>(&sm.X[lr][4 * lg]) = xa;   // X^T
-      f32x4 z = mm16_split_lt(&sm.TdT[1][0][0], 20, &sm.X[0][0], 20, f32x4{0.f, 0.f, 0.f, 0.f}, lane);
-      const float bc = bj[lr];
-      bf16x4 h4, l4;
-      split4(-z * bc, h4, l4);
-      *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;
-      *reinterpret_cast<bf16x4 *>(&sm.Tl[j & 1][lr][16 + 4 * lg]) = l4;
+    // phase Y: scan of chunk it+1 (wave 0); diagonal P blocks of chunk it
+    if (pw == 0) {
+      if (it + 1 < nchunks) scan(it + 1);
+    } else if (it < nchunks) {
+      const int t = (pw == 1) ? 1 : 0;
+      In &bf = sm.in[it % NIN];
+      store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, t, t), t, t, true), t, t);
     }
     __syncthreads();
   }

@@ -146,8 +146,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int kk = 0; kk < KKD; ++kk) {
           bf16x4 h0, l0, h1, l1;
-          split4(Sacc[2 * kk], h0, l0);
-          split4(Sacc[2 * kk + 1], h1, l1);
+          split4<false>(Sacc[2 * kk], h0, l0);
+          split4<false>(Sacc[2 * kk + 1], h1, l1);
           Sh[kk] = cat(h0, h1);
           Sl[kk] = cat(l0, l1);
         }
@@ -172,14 +172,14 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - a1[e];
         bf16x4 rh4, rl4;
-        split4(rr, rh4, rl4);
+        split4<false>(rr, rh4, rl4);
         // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
         const bf16x8 ta = cat(ld_tr4(&sm.Th[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]),
                               ld_tr4(&sm.Tl[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]));
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         u = mfma_bf16(ta, cat(rh4, rh4), u);
         u = mfma_bf16(ta, cat(rl4, zero4), u);
-        split4(u, uh4, ul4);
+        split4<false>(u, uh4, ul4);
       }
       __syncthreads();
       if (s >= 0) {
@@ -288,7 +288,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int pc = perm32(c0);
     auto put2 = [](bf16 *hi, bf16 *lo, float x0, float x1) {
       unsigned h, l;
-      split2(x0, x1, h, l);
+      split2<false>(x0, x1, h, l);
       *reinterpret_cast<unsigned *>(hi) = h;
       *reinterpret_cast<unsigned *>(lo) = l;
     };
@@ -357,7 +357,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
     bf16x4 h4, l4;
-    split4(val, h4, l4);
+    split4<false>(val, h4, l4);
     *reinterpret_cast<bf16x4 *>(&d.Ph[sc][r0]) = h4;
     *reinterpret_cast<bf16x4 *>(&d.Pl[sc][r0]) = l4;
   };
@@ -395,7 +395,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       unsigned h8[2][4], l8[2][4];
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+        split2<false>(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};

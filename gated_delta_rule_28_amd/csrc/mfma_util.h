@@ -22,19 +22,44 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Split two fp32 values into packed bf16 hi and lo pairs (x ~= hi + lo to
 // ~16 bits, hi = RNE(x), lo = RNE(x - hi)).  One packed conversion makes
-// both hi values; their fp32 values are the bf16 bits shifted into the top
-// half, so x - hi is exact and a second packed conversion makes the lo pair.
+// both hi values and x - hi is exact in fp32 (hi is x rounded to 8 bits); a
+// second packed conversion makes the lo pair.
+//
+// x - hi takes one of two forms:
+//  - DOT: one instruction per value, the packed bf16 dot product
+//    hi . m + x with m = (-1, 0) or (0, -1) (bf16 -1.0 is 0xBF80; the
+//    products are exact).  It is written as the three-address VOP3P
+//    instruction because the compiler's own form ties the accumulator to the
+//    destination and copies x first whenever x stays live.  A VALU read of
+//    a dot product's result needs three wait states, which the compiler does
+//    not insert after inline assembly, so the block ends with them (s_nop 2).
+//    Every input of the block is first read by the compiler-visible
+//    conversion that makes hi, so hazards on the inputs (an MFMA result read
+//    by VALU) are resolved before it.
+//  - otherwise: the hi values unpacked by a shift and a mask, then
+//    subtracted (two instructions per value, freely scheduled).
+template <bool DOT = true>
 __device__ __forceinline__ void split2(float x0, float x1, unsigned &hi, unsigned &lo) {
   hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-  const float h0 = __builtin_bit_cast(float, hi << 16);
-  const float h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
-  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+  float r0, r1;
+  if constexpr (DOT) {
+    asm("v_dot2_f32_bf16 %0, %2, %3, %4\n\t"
+        "v_dot2_f32_bf16 %1, %2, %5, %6\n\t"
+        "s_nop 2"
+        : "=&v"(r0), "=v"(r1)
+        : "v"(hi), "s"(0x0000BF80u), "v"(x0), "s"(0xBF800000u), "v"(x1));
+  } else {
+    r0 = x0 - __builtin_bit_cast(float, hi << 16);
+    r1 = x1 - __builtin_bit_cast(float, hi & 0xffff0000u);
+  }
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
+template <bool DOT = true>
 __device__ __forceinline__ void split4(const f32x4 x, bf16x4 &hi, bf16x4 &lo) {
   unsigned h01, l01, h23, l23;
-  split2(x[0], x[1], h01, l01);
-  split2(x[2], x[3], h23, l23);
+  split2<DOT>(x[0], x[1], h01, l01);
+  split2<DOT>(x[2], x[3], h23, l23);
   hi = __builtin_bit_cast(bf16x4, u32x2{h01, h23});
   lo = __builtin_bit_cast(bf16x4, u32x2{l01, l23});
 }
@@ -81,6 +106,76 @@ __device__ __forceinline__ void buf_st1(float x, rsrc_t r, int off) {
 }
 __device__ __forceinline__ void buf_st1(bf16 x, rsrc_t r, int off) {
   __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+}
+
+// D += A(16x16) * B(16x16), bf16 operands, fp32 accumulate: lane l holds
+// A[l & 15][4 (l >> 4) .. +3] and B[4 (l >> 4) .. +3][l & 15]; the result
+// lane l holds D[4 (l >> 4) + e][l & 15] -- the B operand layout, so an
+// accumulator split into bf16 feeds the next product's B side directly.
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// ---- LDS DMA: buffer loads that write LDS directly ----
+//
+// buffer_load_dword{,x4} ... lds writes lane l's 4 (16) bytes to LDS at
+// M0 + 4 l (M0 + 16 l): a wave moves one contiguous 256 B (1 KiB) run of
+// LDS, while each lane's global offset is free, so a layout in LDS is chosen
+// through the per-lane offsets.  Offsets past the descriptor's size read as
+// zero.  The loads are issued from inline assembly, so the compiler neither
+// tracks them nor waits on them before later LDS reads of the issuing wave:
+// the issuing wave waits with wait_vmcnt() before a barrier that publishes
+// the data.  M0 is saved and restored around the load (the compiler owns
+// it); an SALU write of M0 takes one wait state before the load reads it.
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// gfx9 raw buffer descriptor as four scalar dwords (stride 0, 32-bit data)
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, long bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  const long b = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFL ? 0xFFFFFFFFL : bytes);
+  return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a),
+               (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu)),
+               (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b), 0x00020000u};
+}
+
+// byte address of an LDS object (wave-uniform)
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return (unsigned)__builtin_amdgcn_readfirstlane(
+      (int)(unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
+__device__ __forceinline__ void lds_dma16(u32x4 r, unsigned voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(u32x4 r, unsigned voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(r)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
