@@ -88,19 +88,18 @@ __device__ __forceinline__ float scan32_inclusive(float x) {
 
 // Block permutation of a q/k row with NB 16-byte blocks (NB = 16: 256-byte
 // rows spanning all 64 banks; NB = 8: 128-byte rows, two rows per bank
-// sweep).  Row reads touch rows r0..r0+15 at one block: the value is a
-// bijection on those rows (on each row parity for NB = 8).  Transposing
-// reads touch rows 0..7 (or 8..15) at four adjacent blocks: the value moves
-// each row to a different group of four blocks, so 32 lanes meet each bank
-// pair at most twice (the minimum: every lane reads the same 8-byte half).
+// sweep).  A ds_read_b128 is serviced in four passes of 16 lanes; lane l
+// joins pass (l >> 5, parity of (l >> 2) & 7) (measured on gfx950 with the
+// bank-conflict counter), so one pass holds rows lr with
+// parity(lr >> 2) = p of lane group 2h and the other rows of group 2h + 1,
+// whose natural blocks differ in bit 0.  The permutation maps each of those
+// two row sets onto the even blocks (with the row parity for NB = 8), so a
+// pass reads 16 distinct blocks.  The transposing reads of k^T (64 lanes,
+// one 8-byte half) meet each bank pair four times, their minimum.
 template <int NB>
 __device__ __forceinline__ int swz_qk(int r) {
-  if constexpr (NB == 16) {
-    return 4 * (r & 3) + ((r >> 2) & 3);
-  } else {
-    const int j = (r >> 1) & 7;
-    return 4 * (j & 1) + (j >> 1);
-  }
+  if constexpr (NB == 16) return 2 * (r & 7);
+  else return 2 * ((r >> 1) & 3);
 }
 
 // Block permutation of a v row (NB = 8: 128-byte rows; NB = 4: 64-byte
