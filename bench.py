@@ -120,10 +120,18 @@ def decode_alg_bytes(w):
 # GPU timing
 
 
-def time_launches(torch, fn, steps, warmup):
-    """Run fn `warmup` times, then exactly `steps` times between two full
-    synchronisations; each call is also bracketed by events on the current
-    stream, the stream the kernels are launched on."""
+def time_launches(torch, fn, steps, warmup, settle_s=0.0):
+    """Run fn for `settle_s` seconds of wall time (untimed: the GPU clock
+    ramps up over the first ~80 launches of a fresh process and the first
+    launches run up to ~20% slower), then `warmup` times, then exactly
+    `steps` times between two full synchronisations; each timed call is also
+    bracketed by events on the current stream, the stream the kernels are
+    launched on."""
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -151,9 +159,9 @@ def chunk_setup(torch, gdr, W, w, out_dtype):
     return step, o, S
 
 
-def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype):
+def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0):
     step, o, S = chunk_setup(torch, gdr, W, w, out_dtype)
-    wall, per = time_launches(torch, step, steps, warmup)
+    wall, per = time_launches(torch, step, steps, warmup, settle_s)
     if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())):
         raise RuntimeError(f"non-finite output in the timed run of {w.name}")
     out_b = 2 if out_dtype == torch.bfloat16 else 4
@@ -195,9 +203,9 @@ def decode_setup(torch, gdr, W, d):
     return one_pass, state, o
 
 
-def decode_line(torch, gdr, W, d, passes=3):
+def decode_line(torch, gdr, W, d, passes=3, settle_s=0.0):
     one_pass, state, o = decode_setup(torch, gdr, W, d)
-    _, per_eager = time_launches(torch, one_pass, passes, 1)
+    _, per_eager = time_launches(torch, one_pass, passes, 1, settle_s)
     # the same 128 launches captured once and replayed as one HIP graph
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -363,6 +371,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-s", type=float, default=0.25,
+                    help="untimed seconds of the same launches before each line's warm-up, "
+                         "so the timed steps run at the settled GPU clock")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline line only (no bf16-output, KDA and decode lines)")
@@ -392,7 +403,7 @@ def main(argv=None):
         return 0
 
     w = W.HEADLINE
-    head = chunk_line(torch, gdr, W, w, args.steps, args.warmup, torch.float32)
+    head = chunk_line(torch, gdr, W, w, args.steps, args.warmup, torch.float32, args.settle_s)
     rec = {
         "metric": "tokens/s gated-delta chunk fwd (H=16,d=128,T=4096) + % MFMA/HBM roofline",
         "value": head["value"],
@@ -400,6 +411,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_s": args.settle_s,
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -415,15 +427,16 @@ def main(argv=None):
     }
     if not args.no_extra:
         nb = max(5, args.steps // 2)
-        b = chunk_line(torch, gdr, W, w, nb, 2, torch.bfloat16)
+        b = chunk_line(torch, gdr, W, w, nb, 2, torch.bfloat16, args.settle_s)
         rec["bf16_output"] = {"value": w.B * w.T / (b["kernel_ms"]["mean"] * 1e-3),
                               "unit": "tokens/s", "kernel_ms": b["kernel_ms"],
                               "roofline": b["roofline"]}
-        kda = chunk_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2, torch.float32)
+        kda = chunk_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2, torch.float32,
+                         args.settle_s)
         rec["kda"] = {k: kda[k] for k in ("workload", "value", "kernel", "kernel_chunk",
                                           "kernel_ms", "roofline", "mfma_alg")}
         rec["kda"]["unit"] = "tokens/s"
-        rec["decode"] = decode_line(torch, gdr, W, W.DECODE)
+        rec["decode"] = decode_line(torch, gdr, W, W.DECODE, settle_s=args.settle_s)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(W, w)
     print(json.dumps(rec), flush=True)
