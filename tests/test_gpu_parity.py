@@ -227,6 +227,17 @@ def test_chunk_mfma_many_chains(gate):
     assert rel_err(np64(S), S_ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("gate", ["none", "scalar"])
+def test_chunk_mfma_d64_many_chains(gate):
+    # 256 chains at d = 64: the 64-column (whole-width) slice configuration
+    say("chunk mfma d64 many chains", gate)
+    inp = with_state(W.make_chunk_inputs(4, 70, 64, 64, 64, gate, "bf16", seed=6, device=DEV))
+    o, S = run_chunk(inp)
+    o_ref, S_ref = oracle_on(inp)
+    assert rel_err(np64(o), o_ref) <= BF16_TOL
+    assert rel_err(np64(S), S_ref) <= BF16_TOL
+
+
 def test_chunk_mfma_bf16_output():
     say("chunk mfma bf16 out")
     inp = W.make_chunk_inputs(2, 150, 2, 128, 128, "scalar", "bf16", seed=8, device=DEV)
@@ -282,6 +293,17 @@ def test_chunk_kda_many_chains():
     # 128 chains: the 64-column slice configuration
     say("chunk kda many chains")
     inp = with_state(W.make_chunk_inputs(8, 70, 16, 128, 128, "channel", "bf16", seed=5,
+                                         device=DEV))
+    o, S = run_chunk(inp)
+    o_ref, S_ref = oracle_on(inp)
+    assert rel_err(np64(o), o_ref) <= BF16_TOL
+    assert rel_err(np64(S), S_ref) <= BF16_TOL
+
+
+def test_chunk_kda_d64_many_chains():
+    # 256 chains at d = 64: the whole-width slice configuration
+    say("chunk kda d64 many chains")
+    inp = with_state(W.make_chunk_inputs(4, 70, 64, 64, 64, "channel", "bf16", seed=7,
                                          device=DEV))
     o, S = run_chunk(inp)
     o_ref, S_ref = oracle_on(inp)
