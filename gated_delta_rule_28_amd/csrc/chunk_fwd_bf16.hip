@@ -327,7 +327,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const typename SM::PT &ps = sm.p[s % NPR];
         const int t0 = s * C, n = min(C, T - t0);
         const long orow = (tok0 + (long)t0 * H) * DV;   // element offset of the chunk's first row
-        const rsrc_t ro = make_rsrc(o + orow, (long)sizeof(OutT) * ((long)B * T * H * DV - orow));
+        // the chunk's rows: smaller than 4 GiB (the host checks the shape)
+        const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
@@ -554,16 +555,16 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const long row0 = tok0 + (long)j * C * H;         // token row of the chunk's first token
     if (pw == 0) {
       // v rows (all slices' columns of rows < n are inside the descriptor)
-      const u32x4 rv = rsrc_words(v + row0 * DV, 2L * ((long)(n - 1) * H * DV + DV));
+      const u32x4 rv = rsrc_words(v + row0 * DV, 2u * ((unsigned)(n - 1) * H * DV + DV));
       const unsigned lv = lds_addr(&dst.V[0][0]);
 #pragma unroll
       for (int i = 0; i < NVI; ++i) lds_dma16(rv, voff[i], lv + 1024 * i);
-      lds_dma4(rsrc_words(beta + row0, 4L * ((long)(n - 1) * H + 1)), soff, lds_addr(&dst.beta[0]));
+      lds_dma4(rsrc_words(beta + row0, 4u * ((unsigned)(n - 1) * H + 1)), soff, lds_addr(&dst.beta[0]));
       if constexpr (SCALAR)
-        lds_dma4(rsrc_words(log_alpha + row0, 4L * ((long)(n - 1) * H + 1)), soff, lds_addr(&dst.la[0]));
+        lds_dma4(rsrc_words(log_alpha + row0, 4u * ((unsigned)(n - 1) * H + 1)), soff, lds_addr(&dst.la[0]));
     } else {
       const bf16 *src = (pw == 1) ? k : q;
-      const u32x4 rq = rsrc_words(src + row0 * DK, 2L * ((long)(n - 1) * H * DK + DK));
+      const u32x4 rq = rsrc_words(src + row0 * DK, 2u * ((unsigned)(n - 1) * H * DK + DK));
       const unsigned lq = lds_addr(pw == 1 ? &dst.K[0][0] : &dst.Q[0][0]);
 #pragma unroll
       for (int i = 0; i < NQI; ++i) lds_dma16(rq, voff[i], lq + 1024 * i);
@@ -668,8 +669,12 @@ hipError_t by_out(const ChunkArgs &a) {
 
 bool chunk_fwd_bf16_supported(const ChunkArgs &a) {
   // the kernel's chunk is 32 tokens; a requested chunk size only changes
-  // rounding, so 0, 16, 32 and 64 all map here
-  return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate != kGateChannel;
+  // rounding, so 0, 16, 32 and 64 all map here.  Its per-chunk buffer
+  // descriptors span one chunk's rows of a [*, H, D] tensor and must stay
+  // below 4 GiB (H * D below ~34 million)
+  const long chunk_bytes = (long)4 * ((long)(C - 1) * a.H * a.D + a.D);
+  return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate != kGateChannel &&
+         chunk_bytes < 0xFFFFFFFFL;
 }
 
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {

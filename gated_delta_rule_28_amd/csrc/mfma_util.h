@@ -92,6 +92,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, long bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(unsigned)b,
                                            0x00020000);
 }
+// Descriptor of a range known to be shorter than 4 GiB (no clamp: a 64-bit
+// clamp compiles to VALU compares that the scalar code then waits for).
+__device__ __forceinline__ rsrc_t make_rsrc32(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 __device__ __forceinline__ bf16x8 buf_ld8(rsrc_t r, int off) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -131,12 +137,12 @@ __device__ __forceinline__ f32x4 mfma16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // gfx9 raw buffer descriptor as four scalar dwords (stride 0, 32-bit data)
-__device__ __forceinline__ u32x4 rsrc_words(const void *base, long bytes) {
+// of a range known to be shorter than 4 GiB
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, unsigned bytes) {
   const unsigned long long a = (unsigned long long)base;
-  const long b = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFL ? 0xFFFFFFFFL : bytes);
   return u32x4{(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a),
                (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xffffu)),
-               (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b), 0x00020000u};
+               (unsigned)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
 }
 
 // byte address of an LDS object (wave-uniform)

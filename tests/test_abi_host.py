@@ -82,6 +82,8 @@ def step(**kw):
     (dict(chunk=48), _abi.GDR_EUNSUPPORTED),
     (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),     # fp32 inputs need Dk <= 64
     (dict(gate=_abi.GDR_GATE_CHANNEL, in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
+    # one chunk's rows of a [*, H, 128] tensor must span less than 4 GiB
+    (dict(H=300000), _abi.GDR_EUNSUPPORTED),
     # per-channel log decays are read with 16-byte vectors
     (dict(gate=_abi.GDR_GATE_CHANNEL, log_alpha=FAKE + 4), _abi.GDR_EINVAL),
 ])
