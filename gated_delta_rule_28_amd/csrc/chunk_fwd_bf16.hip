@@ -31,16 +31,18 @@
 //   prep waves 0..2 bring chunks into LDS with LDS DMA (no registers, no
 //     LDS write instructions), scan the log decays and form the decayed
 //     K K^T / Q K^T tiles (A and P); prep wave 3 solves the diagonal 16x16
-//     blocks of (I + A) and forms the off-diagonal block of T'.
+//     blocks of T = (I + A)^{-1} and forms its off-diagonal block.  T is
+//     kept without the diag(b) factor: the state waves scale R by b instead,
+//     T' R = T (b o R), which takes two passes over T off the solver.
 //
 // Schedule.  Iteration i has two phases separated by workgroup barriers:
-//   X: DMA of chunk i+2 issued; A tiles of chunk i (and P10); T' of chunk
-//      i-1 completed (off-diagonal block, bf16 splits)  | state: K S, Q S, U of i-2
+//   X: DMA of chunk i+2 issued; A tiles of chunk i (and P10); T of chunk
+//      i-1 completed (off-diagonal block)          | state: K S, Q S, U of i-2
 //   Y: log-decay scan of chunk i+1; P tiles of chunk i; diagonal solve of
 //      chunk i                                          | state: O, S update of i-2
 // A chunk's inputs are in flight for about one and a half iterations before
 // the barrier that publishes them, so HBM latency is hidden; a chunk's input
-// slot lives five iterations (NIN = 5), its P tiles three, T' two.
+// slot lives five iterations (NIN = 5), its P tiles three, T two.
 //
 // LDS layouts.  q, k rows are 2 DK bytes and v rows 2 DVS bytes with no
 // padding; the 16-byte blocks of each row are XOR-permuted by a function of
@@ -50,7 +52,7 @@
 // position.
 //
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
-// operand (S, R, U, T', P, and the fp32 solve outputs) is split into bf16
+// operand (S, R, U, T, P) is split into bf16
 // hi + lo and multiplied as hi*hi + hi*lo + lo*hi (two products when the
 // other side is exact), so products carry ~16 significant bits and
 // accumulate in fp32.
@@ -130,9 +132,7 @@ struct __align__(16) PipeSmem {
   PT p[NPR];
   float ATd[2][16][20];                // diagonal 16x16 blocks of A, transposed: [b][s][r] = A[16b+r][16b+s]
   bf16 A10h[2][16][LDT], A10l[2][16][LDT];   // block (1,0) of A, transposed: [s][r] = A[16+r][s]
-  bf16 TTh[2][16][LDT], TTl[2][16][LDT];     // diagonal blocks of T = (I+A)^{-1}, transposed:
-                                             // [b][c][r] = T[16b+r][16b+c]
-  bf16 Th[2][C][LDC], Tl[2][C][LDC];   // T'^T: [s][r] = T'[r][s], T' = (I+A)^{-1} diag(b);
+  bf16 Th[2][C][LDC], Tl[2][C][LDC];   // T^T: [s][r] = T[r][s], T = (I+A)^{-1} (T' = T diag(b));
                                        // rows 16..31 x cols 0..15 stay zero
 };
 
@@ -290,9 +290,11 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(Vb + 16 * rb * VRB + v_off));
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                                 : *reinterpret_cast<const f32x4 *>(&bs.gam[r0]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.bt[r0]);
+          // b o R: T' R = T diag(b) R with T kept unscaled
           f32x4 rr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - gm4[e] * KS[rb][e];
+          for (int e = 0; e < 4; ++e) rr[e] = ((float)vv[e] - gm4[e] * KS[rb][e]) * b4[e];
           split4(rr, rh2[rb], rl2[rb]);
         }
         const bf16x8 Rh = cat(rh2[0], rh2[1]), Rl = cat(rl2[0], rl2[1]);
@@ -301,7 +303,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         bf16x4 uh[2], ul[2], wh[2], wl[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          // row 16 rb + lr of T', slots = tokens 16 h + 4 lg + c (the R rows)
+          // row 16 rb + lr of T, slots = tokens 16 h + 4 lg + c (the R rows)
           const bf16x8 th = cat(ld_tr4(&Th[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
                                 ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
           const bf16x8 tl = cat(ld_tr4(&Tl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
@@ -421,70 +423,52 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
 
   if (pw == 3) {
-    // ---- solver wave ----
+    // ---- solver wave: T = (I + A)^{-1} of each chunk, stored unscaled (the
+    //      state waves scale R by b, as T' R = T (b o R)) ----
     __syncthreads();
     __syncthreads();
-    float x[16];                       // column lane & 15 of diagonal block (lane >> 4) & 1 of T
     for (int it = 0; it < nchunks + 2; ++it) {
-      // phase X: T' of chunk it-1.  Diagonal blocks: T'[o0 + r][o0 + col] =
-      // T[o0 + r][o0 + col] b_{o0 + col} from the solve's registers.  Block
-      // (1,0): T10 = -T11 A10 T00, so T'10 = -(T11 (A10 T00)) diag(b_0), two
-      // 16x16x16 split products with the first result fed to the second as
-      // its B operand straight from the accumulator.
+      // phase X: block (1,0) of T of chunk it-1, T10 = -T11 A10 T00, from
+      // its diagonal blocks (written in the last phase Y): two 16x16x16
+      // split products, the first result fed to the second as its B operand
+      // straight from the accumulator
       if (it >= 1 && it - 1 < nchunks) {
         const int j = it - 1;
-        const float *bj = sm.in[j % NIN].bt;
-        typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-        if (lane < 32) {
-          const int blk = lane >> 4, col = lane & 15, o0 = 16 * blk;
-          const float bcol = bj[o0 + col];
-          unsigned h8[2][4], l8[2][4];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2)
-            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4_t *>(&sm.Th[j & 1][o0 + col][o0 + 8 * hf]) =
-                u32x4_t{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4_t *>(&sm.Tl[j & 1][o0 + col][o0 + 8 * hf]) =
-                u32x4_t{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
-          }
-        }
+        const bf16(*Th)[SM::LDC] = sm.Th[j & 1];
+        const bf16(*Tl)[SM::LDC] = sm.Tl[j & 1];
         // Y1 = A10 T00: A operand A10[m][4 lg ..] = column m of A10^T rows 4 lg..;
-        // B operand T00[4 lg ..][n] = row n of T00^T
+        // B operand T00[4 lg ..][n] = row n of T^T
         const bf16x4 ah = ld_tr4(&sm.A10h[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
         const bf16x4 al = ld_tr4(&sm.A10l[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
-        const bf16x4 bh = *reinterpret_cast<const bf16x4 *>(&sm.TTh[0][lr][4 * lg]);
-        const bf16x4 bl = *reinterpret_cast<const bf16x4 *>(&sm.TTl[0][lr][4 * lg]);
+        const bf16x4 bh = *reinterpret_cast<const bf16x4 *>(&Th[lr][4 * lg]);
+        const bf16x4 bl = *reinterpret_cast<const bf16x4 *>(&Tl[lr][4 * lg]);
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
         y = mfma16_bf16(ah, bh, y);
         y = mfma16_bf16(ah, bl, y);
         y = mfma16_bf16(al, bh, y);
         bf16x4 yh, yl;
         split4(y, yh, yl);
-        // Z = T11 Y1: A operand T11[m][4 lg ..] = column m of T11^T rows 4 lg..
-        const bf16x4 th = ld_tr4(&sm.TTh[1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
-        const bf16x4 tl = ld_tr4(&sm.TTl[1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        // Z = T11 Y1: A operand T11[m][4 lg ..] = column 16 + m of T^T rows 16 + 4 lg..
+        const bf16x4 th = ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 + 4 * (lr & 3)]);
+        const bf16x4 tl = ld_tr4(&Tl[16 + 4 * lg + (lr >> 2)][16 + 4 * (lr & 3)]);
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         z = mfma16_bf16(th, yh, z);
         z = mfma16_bf16(th, yl, z);
         z = mfma16_bf16(tl, yh, z);
-        // lane holds Z[4 lg + e][lr]: T'^T[lr][16 + 4 lg + e] = -Z b_lr
-        const float bc = bj[lr];
+        // lane holds Z[4 lg + e][lr]: T^T[lr][16 + 4 lg + e] = -Z
         bf16x4 h4, l4;
-        split4(-z * bc, h4, l4);
+        split4(-z, h4, l4);
         *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;
         *reinterpret_cast<bf16x4 *>(&sm.Tl[j & 1][lr][16 + 4 * lg]) = l4;
       }
       __syncthreads();
-      // phase Y: diagonal 16x16 blocks of T = (I + A)^{-1} of chunk it;
-      // lane = (block, column); right-looking forward substitution: once
-      // x_s is final it updates all later rows, so the dependent chain is
-      // one FMA per step
+      // phase Y: diagonal 16x16 blocks of T of chunk it; lane = (block,
+      // column); right-looking forward substitution: once x_s is final it
+      // updates all later rows, so the dependent chain is one FMA per step
       if (it < nchunks) {
         const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
-        (void)o0;
         const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
+        float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
         // every needed entry of A^T (rows s, columns r > s: 36 float4) is
@@ -503,16 +487,17 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
         }
-        // T^T hi/lo rows for the off-diagonal block (lanes 32..63 hold duplicates)
+        // T^T[o0 + col][o0 + r] = x[r], hi/lo (lanes 32..63 hold duplicates)
         if (lane < 32) {
           unsigned h8[2][4], l8[2][4];
 #pragma unroll
           for (int r = 0; r < 16; r += 2) split2(x[r], x[r + 1], h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-          typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4_t *>(&sm.TTh[blk][col][8 * hf]) = u32x4_t{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4_t *>(&sm.TTl[blk][col][8 * hf]) = u32x4_t{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&sm.Th[it & 1][o0 + col][o0 + 8 * hf]) =
+                u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&sm.Tl[it & 1][o0 + col][o0 + 8 * hf]) =
+                u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
           }
         }
       }
