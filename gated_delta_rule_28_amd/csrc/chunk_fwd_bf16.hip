@@ -36,13 +36,13 @@
 //     T' R = T (b o R), which takes two passes over T off the solver.
 //
 // Schedule.  Iteration i has two phases separated by workgroup barriers:
-//   X: DMA of chunk i+2 issued; A tiles of chunk i (and P10); T of chunk
-//      i-1 completed (off-diagonal block)          | state: K S, Q S, U of i-2
-//   Y: log-decay scan of chunk i+1; P tiles of chunk i; diagonal solve of
-//      chunk i                                          | state: O, S update of i-2
-// A chunk's inputs are in flight for about one and a half iterations before
-// the barrier that publishes them, so HBM latency is hidden; a chunk's input
-// slot lives five iterations (NIN = 5), its P tiles three, T two.
+//   X: scan of chunk i+1; DMA of chunk i+2 issued; P10, P11 of chunk i;
+//      the diagonal solve of chunk i              | state: K S, Q S, U of i-2
+//   Y: A tiles of chunk i+1; P00 and the off-diagonal block of T of
+//      chunk i                                    | state: O, S update of i-2
+// Each issuing wave waits for its DMA of chunk i+1 in phase X, a full
+// iteration after issuing it, so HBM latency is hidden; a chunk's input
+// slot lives five iterations (NIN = 5), its P tiles and T three.
 //
 // LDS layouts.  q, k rows are 2 DK bytes and v rows 2 DVS bytes with no
 // padding; the 16-byte blocks of each row are XOR-permuted by a function of
@@ -69,6 +69,7 @@ constexpr int C = 32;      // tokens per chunk
 constexpr int NPW = 4;     // prep waves
 constexpr int NIN = 5;     // input slots: DMA'd in iteration i-2, last read in iteration i+2
 constexpr int NPR = 3;     // P slots: written in iteration i, last read in iteration i+2
+constexpr int NTS = 3;     // T slots: written in iteration i, last read in iteration i+2
 
 // Inclusive prefix sum over lanes 0..31 of a wave with DPP row shifts
 // (within 16-lane rows) and a row broadcast of lane 15 into the next row.
@@ -132,7 +133,7 @@ struct __align__(16) PipeSmem {
   PT p[NPR];
   float ATd[2][16][20];                // diagonal 16x16 blocks of A, transposed: [b][s][r] = A[16b+r][16b+s]
   bf16 A10h[2][16][LDT], A10l[2][16][LDT];   // block (1,0) of A, transposed: [s][r] = A[16+r][s]
-  bf16 Th[2][C][LDC], Tl[2][C][LDC];   // T^T: [s][r] = T[r][s], T = (I+A)^{-1} (T' = T diag(b));
+  bf16 Th[NTS][C][LDC], Tl[NTS][C][LDC];   // T^T: [s][r] = T[r][s], T = (I+A)^{-1} (T' = T diag(b));
                                        // rows 16..31 x cols 0..15 stay zero
 };
 
@@ -196,7 +197,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       (&sm.p[b].Pl[0][0])[i] = (bf16)0.0f;
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < NTS; ++b) {
       (&sm.Th[b][0][0])[i] = (bf16)0.0f;
       (&sm.Tl[b][0][0])[i] = (bf16)0.0f;
     }
@@ -221,6 +222,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)srow(mb, e) * DV + col0 + lr];
     }
+    __syncthreads();
     __syncthreads();
     __syncthreads();
 
@@ -298,8 +300,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           split4(rr, rh2[rb], rl2[rb]);
         }
         const bf16x8 Rh = cat(rh2[0], rh2[1]), Rl = cat(rl2[0], rl2[1]);
-        const bf16(*Th)[SM::LDC] = sm.Th[s & 1];
-        const bf16(*Tl)[SM::LDC] = sm.Tl[s & 1];
+        const bf16(*Th)[SM::LDC] = sm.Th[s % NTS];
+        const bf16(*Tl)[SM::LDC] = sm.Tl[s % NTS];
         bf16x4 uh[2], ul[2], wh[2], wl[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -427,44 +429,12 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     //      state waves scale R by b, as T' R = T (b o R)) ----
     __syncthreads();
     __syncthreads();
+    __syncthreads();
     for (int it = 0; it < nchunks + 2; ++it) {
-      // phase X: block (1,0) of T of chunk it-1, T10 = -T11 A10 T00, from
-      // its diagonal blocks (written in the last phase Y): two 16x16x16
-      // split products, the first result fed to the second as its B operand
-      // straight from the accumulator
-      if (it >= 1 && it - 1 < nchunks) {
-        const int j = it - 1;
-        const bf16(*Th)[SM::LDC] = sm.Th[j & 1];
-        const bf16(*Tl)[SM::LDC] = sm.Tl[j & 1];
-        // Y1 = A10 T00: A operand A10[m][4 lg ..] = column m of A10^T rows 4 lg..;
-        // B operand T00[4 lg ..][n] = row n of T^T
-        const bf16x4 ah = ld_tr4(&sm.A10h[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
-        const bf16x4 al = ld_tr4(&sm.A10l[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
-        const bf16x4 bh = *reinterpret_cast<const bf16x4 *>(&Th[lr][4 * lg]);
-        const bf16x4 bl = *reinterpret_cast<const bf16x4 *>(&Tl[lr][4 * lg]);
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        y = mfma16_bf16(ah, bh, y);
-        y = mfma16_bf16(ah, bl, y);
-        y = mfma16_bf16(al, bh, y);
-        bf16x4 yh, yl;
-        split4(y, yh, yl);
-        // Z = T11 Y1: A operand T11[m][4 lg ..] = column 16 + m of T^T rows 16 + 4 lg..
-        const bf16x4 th = ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 + 4 * (lr & 3)]);
-        const bf16x4 tl = ld_tr4(&Tl[16 + 4 * lg + (lr >> 2)][16 + 4 * (lr & 3)]);
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = mfma16_bf16(th, yh, z);
-        z = mfma16_bf16(th, yl, z);
-        z = mfma16_bf16(tl, yh, z);
-        // lane holds Z[4 lg + e][lr]: T^T[lr][16 + 4 lg + e] = -Z
-        bf16x4 h4, l4;
-        split4(-z, h4, l4);
-        *reinterpret_cast<bf16x4 *>(&sm.Th[j & 1][lr][16 + 4 * lg]) = h4;
-        *reinterpret_cast<bf16x4 *>(&sm.Tl[j & 1][lr][16 + 4 * lg]) = l4;
-      }
-      __syncthreads();
-      // phase Y: diagonal 16x16 blocks of T of chunk it; lane = (block,
-      // column); right-looking forward substitution: once x_s is final it
-      // updates all later rows, so the dependent chain is one FMA per step
+      // phase X: diagonal 16x16 blocks of T of chunk it (A tiles from the
+      // last phase Y); lane = (block, column); right-looking forward
+      // substitution: once x_s is final it updates all later rows, so the
+      // dependent chain is one FMA per step
       if (it < nchunks) {
         const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
         const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
@@ -494,12 +464,45 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int r = 0; r < 16; r += 2) split2(x[r], x[r + 1], h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4 *>(&sm.Th[it & 1][o0 + col][o0 + 8 * hf]) =
+            *reinterpret_cast<u32x4 *>(&sm.Th[it % NTS][o0 + col][o0 + 8 * hf]) =
                 u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4 *>(&sm.Tl[it & 1][o0 + col][o0 + 8 * hf]) =
+            *reinterpret_cast<u32x4 *>(&sm.Tl[it % NTS][o0 + col][o0 + 8 * hf]) =
                 u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
           }
         }
+      }
+      __syncthreads();
+      // phase Y: block (1,0) of T of chunk it, T10 = -T11 A10 T00, from its
+      // diagonal blocks: two 16x16x16 split products, the first result fed to
+      // the second as its B operand straight from the accumulator
+      if (it < nchunks) {
+        const int j = it;
+        const bf16(*Th)[SM::LDC] = sm.Th[j % NTS];
+        const bf16(*Tl)[SM::LDC] = sm.Tl[j % NTS];
+        // Y1 = A10 T00: A operand A10[m][4 lg ..] = column m of A10^T rows 4 lg..;
+        // B operand T00[4 lg ..][n] = row n of T^T
+        const bf16x4 ah = ld_tr4(&sm.A10h[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 al = ld_tr4(&sm.A10l[j & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 bh = *reinterpret_cast<const bf16x4 *>(&Th[lr][4 * lg]);
+        const bf16x4 bl = *reinterpret_cast<const bf16x4 *>(&Tl[lr][4 * lg]);
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        y = mfma16_bf16(ah, bh, y);
+        y = mfma16_bf16(ah, bl, y);
+        y = mfma16_bf16(al, bh, y);
+        bf16x4 yh, yl;
+        split4(y, yh, yl);
+        // Z = T11 Y1: A operand T11[m][4 lg ..] = column 16 + m of T^T rows 16 + 4 lg..
+        const bf16x4 th = ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 + 4 * (lr & 3)]);
+        const bf16x4 tl = ld_tr4(&Tl[16 + 4 * lg + (lr >> 2)][16 + 4 * (lr & 3)]);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z = mfma16_bf16(th, yh, z);
+        z = mfma16_bf16(th, yl, z);
+        z = mfma16_bf16(tl, yh, z);
+        // lane holds Z[4 lg + e][lr]: T^T[lr][16 + 4 lg + e] = -Z
+        bf16x4 h4, l4;
+        split4(-z, h4, l4);
+        *reinterpret_cast<bf16x4 *>(&sm.Th[j % NTS][lr][16 + 4 * lg]) = h4;
+        *reinterpret_cast<bf16x4 *>(&sm.Tl[j % NTS][lr][16 + 4 * lg]) = l4;
       }
       __syncthreads();
     }
@@ -581,49 +584,63 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   };
 
-  // prologue: chunks 0 and 1 in flight, chunk 0 landed and scanned
-  if (pw < 3) {
-    if (nchunks > 0) issue(0);
-    if (nchunks > 1) issue(1);
-    wait_prev(nchunks > 1);
-  }
+  // the A tiles of chunk j (diagonal blocks fp32 transposed for the solve on
+  // wave 1, A10 as bf16 hi/lo on wave 0)
+  auto a_tiles = [&](int j) {
+    const In &bf = sm.in[j % NIN];
+    if (pw == 0) {
+      const f32x4 val = decayed(bf, tile_acc(bf, false, 1, 0), 1, 0, false);
+      bf16x4 h4, l4;
+      split4(val, h4, l4);
+      *reinterpret_cast<bf16x4 *>(&sm.A10h[j & 1][lr][4 * lg]) = h4;
+      *reinterpret_cast<bf16x4 *>(&sm.A10l[j & 1][lr][4 * lg]) = l4;
+    } else if (pw == 1) {
+      const f32x4 a0 = tile_acc(bf, false, 0, 0), a1 = tile_acc(bf, false, 1, 1);
+      *reinterpret_cast<f32x4 *>(&sm.ATd[0][lr][4 * lg]) = decayed(bf, a0, 0, 0, false);
+      *reinterpret_cast<f32x4 *>(&sm.ATd[1][lr][4 * lg]) = decayed(bf, a1, 1, 1, false);
+    }
+  };
+
+  // prologue: chunks 0 and 1 in flight; chunk 0 landed, scanned and its A
+  // tiles formed
+  if (nchunks > 0) issue(0);
+  if (nchunks > 1) issue(1);
+  wait_prev(nchunks > 1);
   __syncthreads();
   if (pw == 0 && nchunks > 0) scan(0);
   __syncthreads();
+  if (nchunks > 0) a_tiles(0);
+  __syncthreads();
 
   for (int it = 0; it < nchunks + 2; ++it) {
-    // phase X: DMA of chunk it+2; A tiles and P10 of chunk it; then wait
-    // until this wave's DMA of chunk it+1 has landed
+    // phase X: wave 0 scans chunk it+1 (its log a / b landed: wave 0 waits
+    // for all its loads first) and issues its DMA of chunk it+2; waves 1 and
+    // 2 issue theirs, form P11 / P10 of chunk it, and wait for their DMA of
+    // chunk it+1
     const bool more = it + 2 < nchunks;
-    if (more) issue(it + 2);
-    if (it < nchunks) {
-      In &bf = sm.in[it % NIN];
-      if (pw == 0) {
-        // A10, stored transposed as bf16 hi/lo for the off-diagonal solve
-        const f32x4 val = decayed(bf, tile_acc(bf, false, 1, 0), 1, 0, false);
-        bf16x4 h4, l4;
-        split4(val, h4, l4);
-        *reinterpret_cast<bf16x4 *>(&sm.A10h[it & 1][lr][4 * lg]) = h4;
-        *reinterpret_cast<bf16x4 *>(&sm.A10l[it & 1][lr][4 * lg]) = l4;
-      } else if (pw == 1) {
-        // diagonal A blocks, fp32 transposed, for this iteration's solve
-        const f32x4 a0 = tile_acc(bf, false, 0, 0), a1 = tile_acc(bf, false, 1, 1);
-        *reinterpret_cast<f32x4 *>(&sm.ATd[0][lr][4 * lg]) = decayed(bf, a0, 0, 0, false);
-        *reinterpret_cast<f32x4 *>(&sm.ATd[1][lr][4 * lg]) = decayed(bf, a1, 1, 1, false);
-      } else {
-        store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
+    if (pw == 0) {
+      wait_vmcnt<0>();
+      if (it + 1 < nchunks) scan(it + 1);
+      if (more) issue(it + 2);
+    } else {
+      if (more) issue(it + 2);
+      if (it < nchunks) {
+        // P11 on wave 1, P10 on wave 2
+        const int tj = (pw == 1) ? 1 : 0;
+        const In &bf = sm.in[it % NIN];
+        store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, 1, tj), 1, tj, true), 1, tj);
       }
+      wait_prev(more);
     }
-    wait_prev(more);
     __syncthreads();
 
-    // phase Y: scan of chunk it+1 (wave 0); diagonal P blocks of chunk it
-    if (pw == 0) {
-      if (it + 1 < nchunks) scan(it + 1);
+    // phase Y: the A tiles of chunk it+1 (waves 0 and 1); P00 of chunk it
+    // (wave 2)
+    if (pw < 2) {
+      if (it + 1 < nchunks) a_tiles(it + 1);
     } else if (it < nchunks) {
-      const int t = (pw == 1) ? 1 : 0;
-      In &bf = sm.in[it % NIN];
-      store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, t, t), t, t, true), t, t);
+      const In &bf = sm.in[it % NIN];
+      store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
     }
     __syncthreads();
   }
