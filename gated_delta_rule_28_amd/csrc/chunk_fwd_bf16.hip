@@ -35,14 +35,17 @@
 //     kept without the diag(b) factor: the state waves scale R by b instead,
 //     T' R = T (b o R), which takes two passes over T off the solver.
 //
-// Schedule.  Iteration i has two phases separated by workgroup barriers:
-//   X: scan of chunk i+1; DMA of chunk i+2 issued; P10, P11 of chunk i;
-//      the diagonal solve of chunk i              | state: K S, Q S, U of i-2
-//   Y: A tiles of chunk i+1; P00 and the off-diagonal block of T of
-//      chunk i                                    | state: O, S update of i-2
-// Each issuing wave waits for its DMA of chunk i+1 in phase X, a full
-// iteration after issuing it, so HBM latency is hidden; a chunk's input
-// slot lives five iterations (NIN = 5), its P tiles and T three.
+// Schedule.  One workgroup barrier per iteration; in iteration i
+//   prep waves 0..2: DMA of chunk i+3 issued; decay scan, A tiles and P
+//                    tiles of chunk i+1; wait for their DMA of chunk i+2
+//   prep wave 3:     T of chunk i (diagonal solve, then the off-diagonal
+//                    block)
+//   state waves:     K S, Q S, U, O and the S update of chunk i-1
+// Every product of iteration i reads only what earlier iterations wrote, so
+// the state waves run their whole chunk without a barrier in between.  A
+// DMA is waited for a full iteration after it was issued, which hides HBM
+// latency; a chunk's input slot lives five iterations (NIN = 5), its P tiles
+// three and its T two.
 //
 // LDS layouts.  q, k rows are 2 DK bytes and v rows 2 DVS bytes with no
 // padding; the 16-byte blocks of each row are XOR-permuted by a function of
@@ -67,9 +70,9 @@ namespace {
 
 constexpr int C = 32;      // tokens per chunk
 constexpr int NPW = 4;     // prep waves
-constexpr int NIN = 5;     // input slots: DMA'd in iteration i-2, last read in iteration i+2
-constexpr int NPR = 3;     // P slots: written in iteration i, last read in iteration i+2
-constexpr int NTS = 3;     // T slots: written in iteration i, last read in iteration i+2
+constexpr int NIN = 5;     // input slots: chunk j DMA'd from iteration j-3, last read in j+1
+constexpr int NPR = 3;     // P slots: chunk j written in iteration j-1, read in j+1
+constexpr int NTS = 2;     // T slots: chunk j written in iteration j, read in j+1
 
 // Inclusive prefix sum over lanes 0..31 of a wave with DPP row shifts
 // (within 16-lane rows) and a row broadcast of lane 15 into the next row.
@@ -124,18 +127,31 @@ struct __align__(16) PipeSmem {
     bf16 K[C][DK];                     // k rows, likewise
     bf16 V[C][DVS];                    // v rows of this slice, blocks permuted by swz_v
     float la[64], beta[64];            // log a and b of the 64 tokens from the chunk start
-    float g[C], gam[C], ec[C], bt[C];  // g, e^g, e^{g_last - g}, b (0 past the end)
+                                       // (0 past the end of the sequence: the DMA
+                                       // reads zeros beyond the chunk's last row)
+    float gam[C], ec[C];               // e^g, e^{g_last - g}
   };
   struct __align__(16) PT {
     bf16 Ph[C][LDC], Pl[C][LDC];       // P^T: [s][r] = P[r][s]; rows 16..31 x cols 0..15 stay zero
   };
   In in[NIN];
   PT p[NPR];
-  float ATd[2][16][20];                // diagonal 16x16 blocks of A, transposed: [b][s][r] = A[16b+r][16b+s]
+  float ATd[2][2][16][20];             // per chunk parity, diagonal 16x16 blocks of A,
+                                       // transposed: [.][b][s][r] = A[16b+r][16b+s]
   bf16 A10h[2][16][LDT], A10l[2][16][LDT];   // block (1,0) of A, transposed: [s][r] = A[16+r][s]
   bf16 Th[NTS][C][LDC], Tl[NTS][C][LDC];   // T^T: [s][r] = T[r][s], T = (I+A)^{-1} (T' = T diag(b));
                                        // rows 16..31 x cols 0..15 stay zero
+  float gw[3][C];                      // in-chunk log decay g, one copy per tile wave
 };
+
+// Makes this wave's earlier LDS writes visible to its later LDS reads of
+// other lanes' data (LDS serves one wave's accesses in order; the fences
+// keep the compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int DK, int DVS, typename OutT, int GATE>
 __global__ void __launch_bounds__(64 * (DVS / 16 + NPW), 1)
@@ -203,8 +219,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   }
 
-  // Every role runs two prologue barriers and nchunks + 2 iterations of two
-  // barriers, so all waves execute the same sequence of workgroup barriers.
+  // Every role runs two prologue barriers and nchunks + 1 iterations of one
+  // barrier, so all waves execute the same sequence of workgroup barriers.
   if (wave < NSW) {
     // =====================================================================
     // state waves: the serial chunk-to-chunk pass, 16 state columns each
@@ -222,7 +238,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)srow(mb, e) * DV + col0 + lr];
     }
-    __syncthreads();
     __syncthreads();
     __syncthreads();
 
@@ -244,7 +259,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int kk = 0; kk < KKD; ++kk) kt_off[kk] = qk_at(4 * lg + (lr >> 2), (lr & 3) + 4 * kk);
 
     // hi/lo bf16 split of the state, the right operand of K S and Q S; it
-    // is formed at the end of the previous phase Y, as soon as S is final
+    // is formed right after the previous chunk's update
     bf16x8 Sh[KKD], Sl[KKD];
     auto split_state = [&]() {
 #pragma unroll
@@ -258,11 +273,11 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     };
     split_state();
 
-    for (int it = 0; it < nchunks + 2; ++it) {
-      const int s = it - 2;            // chunk of this iteration
-      f32x4 QS[2];                     // carried from phase X to phase Y
+    for (int it = 0; it < nchunks + 1; ++it) {
+      const int s = it - 1;            // chunk of this iteration
+      f32x4 QS[2];
       bf16x8 Uh, Ul, Wh, Wl;
-      // ---- phase X: K S, Q S, R = V - diag(gam) K S, U = T' R ----
+      // ---- K S, Q S, R = V - diag(gam) K S, U = T' R ----
       if (s >= 0) {
         const In &bs = sm.in[s % NIN];
         const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
@@ -292,7 +307,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(Vb + 16 * rb * VRB + v_off));
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                                 : *reinterpret_cast<const f32x4 *>(&bs.gam[r0]);
-          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.bt[r0]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.beta[r0]);
           // b o R: T' R = T diag(b) R with T kept unscaled
           f32x4 rr;
 #pragma unroll
@@ -324,8 +339,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         Wh = cat(wh[0], wh[1]);
         Wl = cat(wl[0], wl[1]);
       }
-      __syncthreads();
-      // ---- phase Y: O = diag(gam) Q S + P U; S <- gam_last S + K^T U' ----
+      // ---- O = diag(gam) Q S + P U; S <- gam_last S + K^T U' ----
       if (s >= 0) {
         const In &bs = sm.in[s % NIN];
         const typename SM::PT &ps = sm.p[s % NPR];
@@ -369,7 +383,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(a, Wl, acc);
           Sacc[mb] = acc;
         }
-        split_state();   // for the next chunk's phase X
+        split_state();   // for the next chunk
       }
       __syncthreads();
     }
@@ -402,12 +416,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       ld8(reinterpret_cast<const bf16 *>(Kc + 16 * tj * QRB + kq_off[kk])), acc);
     return acc;
   };
-  auto decayed = [&](const In &bf, f32x4 acc, int ti, int tj, bool isq) {
+  // the decay, the mask and (for A) the factor b of tile (ti, tj); g is the
+  // calling wave's copy of the in-chunk log decay
+  auto decayed = [&](const In &bf, const float *g, f32x4 acc, int ti, int tj, bool isq) {
     const int sc = 16 * tj + lr;
     const int r0 = 16 * ti + 4 * lg;
-    const float gs = bf.g[sc];
-    const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&bf.g[r0]);
-    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.bt[r0]);
+    const float gs = g[sc];
+    const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&g[r0]);
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.beta[r0]);
     f32x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -425,58 +441,57 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
 
   if (pw == 3) {
-    // ---- solver wave: T = (I + A)^{-1} of each chunk, stored unscaled (the
+    // ---- solver wave: T = (I + A)^{-1} of chunk it, stored unscaled (the
     //      state waves scale R by b, as T' R = T (b o R)) ----
     __syncthreads();
     __syncthreads();
-    __syncthreads();
-    for (int it = 0; it < nchunks + 2; ++it) {
-      // phase X: diagonal 16x16 blocks of T of chunk it (A tiles from the
-      // last phase Y); lane = (block, column); right-looking forward
-      // substitution: once x_s is final it updates all later rows, so the
-      // dependent chain is one FMA per step
-      if (it < nchunks) {
-        const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
-        const float(*At)[20] = sm.ATd[blk];   // At[s][r] = A[o0 + r][o0 + s]
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
-        // every needed entry of A^T (rows s, columns r > s: 36 float4) is
-        // loaded up front, so the 15 dependent steps wait on no LDS read
-        f32x4 a4[15][4];
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-          for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
-            a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
-        // keep the loads ahead of the dependent steps (the scheduler would
-        // otherwise sink them next to their uses to save registers)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2) {
-#pragma unroll
-          for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
-        }
-        // T^T[o0 + col][o0 + r] = x[r], hi/lo (lanes 32..63 hold duplicates)
-        if (lane < 32) {
-          unsigned h8[2][4], l8[2][4];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) split2(x[r], x[r + 1], h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4 *>(&sm.Th[it % NTS][o0 + col][o0 + 8 * hf]) =
-                u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4 *>(&sm.Tl[it % NTS][o0 + col][o0 + 8 * hf]) =
-                u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
-          }
-        }
-      }
-      __syncthreads();
-      // phase Y: block (1,0) of T of chunk it, T10 = -T11 A10 T00, from its
-      // diagonal blocks: two 16x16x16 split products, the first result fed to
-      // the second as its B operand straight from the accumulator
+    for (int it = 0; it < nchunks + 1; ++it) {
       if (it < nchunks) {
         const int j = it;
+        // diagonal 16x16 blocks (A tiles from the last iteration); lane =
+        // (block, column); right-looking forward substitution: once x_s is
+        // final it updates all later rows, so the dependent chain is one FMA
+        // per step
+        {
+          const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
+          const float(*At)[20] = sm.ATd[j & 1][blk];   // At[s][r] = A[o0 + r][o0 + s]
+          float x[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+          // every needed entry of A^T (rows s, columns r > s: 36 float4) is
+          // loaded up front, so the 15 dependent steps wait on no LDS read
+          f32x4 a4[15][4];
+#pragma unroll
+          for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+            for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
+              a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
+          // keep the loads ahead of the dependent steps (the scheduler would
+          // otherwise sink them next to their uses to save registers)
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s2 = 0; s2 < 15; ++s2) {
+#pragma unroll
+            for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
+          }
+          // T^T[o0 + col][o0 + r] = x[r], hi/lo (lanes 32..63 hold duplicates)
+          if (lane < 32) {
+            unsigned h8[2][4], l8[2][4];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) split2(x[r], x[r + 1], h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              *reinterpret_cast<u32x4 *>(&sm.Th[j % NTS][o0 + col][o0 + 8 * hf]) =
+                  u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+              *reinterpret_cast<u32x4 *>(&sm.Tl[j % NTS][o0 + col][o0 + 8 * hf]) =
+                  u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+            }
+          }
+        }
+        wave_lds_sync();
+        // block (1,0), T10 = -T11 A10 T00, from the diagonal blocks just
+        // written: two 16x16x16 split products, the first result fed to the
+        // second as its B operand straight from the accumulator
         const bf16(*Th)[SM::LDC] = sm.Th[j % NTS];
         const bf16(*Tl)[SM::LDC] = sm.Tl[j % NTS];
         // Y1 = A10 T00: A operand A10[m][4 lg ..] = column m of A10^T rows 4 lg..;
@@ -558,7 +573,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int i = 0; i < NQI; ++i) lds_dma16(rq, voff[i], lq + 1024 * i);
     }
   };
-  // wait for every DMA of chunk j+1 when chunk j+2 was issued after it
+  // wait for every DMA of chunk j when chunk j+1 was issued after it
   auto wait_prev = [&](bool newer_issued) {
     if (newer_issued) {
       if (pw == 0) wait_vmcnt<N0>();
@@ -567,81 +582,65 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       wait_vmcnt<0>();
     }
   };
-  // in-chunk cumulative log decay of chunk j (wave 0): inclusive scan over
-  // lanes 0..C-1; padded tokens carry log a = 0 and b = 0
-  auto scan = [&](int j) {
-    In &bf = sm.in[j % NIN];
-    const int n = min(C, T - j * C);
-    const float la = (SCALAR && lane < n) ? bf.la[lane] : 0.0f;
-    const float sc = scan32_inclusive(la);
-    const float glast = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), C - 1));
-    if (lane < C) {
-      bf.g[lane] = sc;
-      bf.gam[lane] = __expf(sc);
-      bf.ec[lane] = __expf(glast - sc);
-      bf.bt[lane] = (lane < n) ? bf.beta[lane] : 0.0f;
-    }
-  };
 
-  // the A tiles of chunk j (diagonal blocks fp32 transposed for the solve on
-  // wave 1, A10 as bf16 hi/lo on wave 0)
-  auto a_tiles = [&](int j) {
-    const In &bf = sm.in[j % NIN];
+  // The tiles of chunk j on waves 0..2.  Each wave takes the in-chunk
+  // cumulative log decay itself (an inclusive scan over lanes 0..C-1;
+  // tokens past the end carry log a = 0 and b = 0) into its own copy of g,
+  // so no tile waits on another wave; wave 0 also writes e^g and
+  // e^{g_last - g} for the state waves.  Shares: wave 0 A10 and the second
+  // diagonal A block, wave 1 the first diagonal A block and P11, wave 2 P10
+  // and P00.
+  auto tiles = [&](int j) {
+    In &bf = sm.in[j % NIN];
+    float *g = sm.gw[pw];
+    const float la = SCALAR ? bf.la[lane] : 0.0f;
+    const float sc = scan32_inclusive(la);
+    if (lane < C) g[lane] = sc;
+    if (pw == 0 && GATE != kGateNone) {
+      const float glast = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), C - 1));
+      if (lane < C) {
+        bf.gam[lane] = __expf(sc);
+        bf.ec[lane] = __expf(glast - sc);
+      }
+    }
+    wave_lds_sync();
+    typename SM::PT &pt = sm.p[j % NPR];
     if (pw == 0) {
-      const f32x4 val = decayed(bf, tile_acc(bf, false, 1, 0), 1, 0, false);
+      const f32x4 val = decayed(bf, g, tile_acc(bf, false, 1, 0), 1, 0, false);
       bf16x4 h4, l4;
       split4(val, h4, l4);
       *reinterpret_cast<bf16x4 *>(&sm.A10h[j & 1][lr][4 * lg]) = h4;
       *reinterpret_cast<bf16x4 *>(&sm.A10l[j & 1][lr][4 * lg]) = l4;
+      *reinterpret_cast<f32x4 *>(&sm.ATd[j & 1][1][lr][4 * lg]) =
+          decayed(bf, g, tile_acc(bf, false, 1, 1), 1, 1, false);
     } else if (pw == 1) {
-      const f32x4 a0 = tile_acc(bf, false, 0, 0), a1 = tile_acc(bf, false, 1, 1);
-      *reinterpret_cast<f32x4 *>(&sm.ATd[0][lr][4 * lg]) = decayed(bf, a0, 0, 0, false);
-      *reinterpret_cast<f32x4 *>(&sm.ATd[1][lr][4 * lg]) = decayed(bf, a1, 1, 1, false);
+      *reinterpret_cast<f32x4 *>(&sm.ATd[j & 1][0][lr][4 * lg]) =
+          decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
+      store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
+    } else {
+      store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
+      store_p(pt, decayed(bf, g, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
     }
   };
 
-  // prologue: chunks 0 and 1 in flight; chunk 0 landed, scanned and its A
-  // tiles formed
+  // prologue: chunks 0..2 in flight; chunks 0 and 1 landed; the tiles of
+  // chunk 0 formed
   if (nchunks > 0) issue(0);
   if (nchunks > 1) issue(1);
-  wait_prev(nchunks > 1);
+  if (nchunks > 2) issue(2);
+  wait_prev(nchunks > 2);
   __syncthreads();
-  if (pw == 0 && nchunks > 0) scan(0);
-  __syncthreads();
-  if (nchunks > 0) a_tiles(0);
+  if (nchunks > 0) tiles(0);
   __syncthreads();
 
-  for (int it = 0; it < nchunks + 2; ++it) {
-    // phase X: wave 0 scans chunk it+1 (its log a / b landed: wave 0 waits
-    // for all its loads first) and issues its DMA of chunk it+2; waves 1 and
-    // 2 issue theirs, form P11 / P10 of chunk it, and wait for their DMA of
-    // chunk it+1
-    const bool more = it + 2 < nchunks;
-    if (pw == 0) {
-      wait_vmcnt<0>();
-      if (it + 1 < nchunks) scan(it + 1);
-      if (more) issue(it + 2);
-    } else {
-      if (more) issue(it + 2);
-      if (it < nchunks) {
-        // P11 on wave 1, P10 on wave 2
-        const int tj = (pw == 1) ? 1 : 0;
-        const In &bf = sm.in[it % NIN];
-        store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, 1, tj), 1, tj, true), 1, tj);
-      }
-      wait_prev(more);
-    }
-    __syncthreads();
-
-    // phase Y: the A tiles of chunk it+1 (waves 0 and 1); P00 of chunk it
-    // (wave 2)
-    if (pw < 2) {
-      if (it + 1 < nchunks) a_tiles(it + 1);
-    } else if (it < nchunks) {
-      const In &bf = sm.in[it % NIN];
-      store_p(sm.p[it % NPR], decayed(bf, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
-    }
+  for (int it = 0; it < nchunks + 1; ++it) {
+    // DMA of chunk it+3; tiles of chunk it+1 (landed by the last barrier);
+    // then wait for this wave's DMA of chunk it+2
+    const bool more = it + 3 < nchunks;
+    if (more) issue(it + 3);
+    if (it + 1 < nchunks) tiles(it + 1);
+    wait_prev(more);
     __syncthreads();
   }
 }

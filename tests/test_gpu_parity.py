@@ -401,6 +401,43 @@ def test_hard_reset_gate_has_no_nan(D, in_dtype, gate):
     assert rel_err(np64(o), o_ref) <= tol
 
 
+def _chunk_decays(B, T, H, per_token, seed):
+    """log a with a per-chunk decay regime: chunk c of every chain draws its
+    mean per-token log decay from `per_token`, and each token varies by up to
+    50% around it."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    nch = (T + 31) // 32
+    pick = torch.randint(0, len(per_token), (B, nch, H), device=DEV, generator=g)
+    mean = torch.tensor(per_token, device=DEV, dtype=torch.float32)[pick]
+    mean = mean.repeat_interleave(32, dim=1)[:, :T]
+    return mean * (0.5 + torch.rand(B, T, H, device=DEV, generator=g))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("regime", ["steady", "mixed", "hard_then_soft"])
+def test_chunk_scalar_decay_regimes(D, regime):
+    # long runs of decay (the total log decay of a chain reaches several
+    # hundred), chunks whose own decay is beyond e^-40, and mixtures of both
+    say("chunk scalar decay regime", D, regime)
+    B, T, H = 2, 613, 4
+    inp = with_state(W.make_chunk_inputs(B, T, H, D, D, "scalar", "bf16", seed=D + 7, device=DEV))
+    if regime == "steady":
+        la = _chunk_decays(B, T, H, [-0.6], seed=3)
+    elif regime == "mixed":
+        la = _chunk_decays(B, T, H, [-0.01, -0.3, -0.9, -2.5], seed=4)
+    else:
+        la = _chunk_decays(B, T, H, [-0.02], seed=5)
+        la[:, :96] = -3.0
+    inp["log_alpha"] = la.contiguous()
+    o, S = run_chunk(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = rel_err(np64(o), o_ref), rel_err(np64(S), S_ref)
+    say("max|err|/rms o", eo, "state", es)
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size, outputs of sampled chains against the
 # oracle (every token and value column of each sampled chain)
