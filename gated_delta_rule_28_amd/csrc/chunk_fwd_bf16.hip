@@ -136,8 +136,8 @@ struct __align__(16) PipeSmem {
   };
   In in[NIN];
   PT p[NPR];
-  float ATd[2][2][16][20];             // per chunk parity, diagonal 16x16 blocks of A,
-                                       // transposed: [.][b][s][r] = A[16b+r][16b+s]
+  float ATd[2][2][16][20];             // per chunk parity, diagonal 16x16 blocks of -A,
+                                       // transposed: [.][b][s][r] = -A[16b+r][16b+s]
   bf16 A10h[2][16][LDT], A10l[2][16][LDT];   // block (1,0) of A, transposed: [s][r] = A[16+r][s]
   bf16 Th[NTS][C][LDC], Tl[NTS][C][LDC];   // T^T: [s][r] = T[r][s], T = (I+A)^{-1} (T' = T diag(b));
                                        // rows 16..31 x cols 0..15 stay zero
@@ -451,28 +451,28 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         // diagonal 16x16 blocks (A tiles from the last iteration); lane =
         // (block, column); right-looking forward substitution: once x_s is
         // final it updates all later rows, so the dependent chain is one FMA
-        // per step
+        // per step.  Lane col of a 16-lane row holds column col of -A; step s
+        // takes column s from lane s by a row broadcast (DPP row_newbcast)
+        // folded into the FMA, so A is read from LDS once, without
+        // broadcast reads
         {
           const int blk = (lane >> 4) & 1, col = lane & 15, o0 = 16 * blk;
-          const float(*At)[20] = sm.ATd[j & 1][blk];   // At[s][r] = A[o0 + r][o0 + s]
+          float na[16];                          // na[r] = -A[o0 + r][o0 + col]
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(&sm.ATd[j & 1][blk][col][4 * q4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) na[4 * q4 + e] = t[e];
+          }
           float x[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
-          // every needed entry of A^T (rows s, columns r > s: 36 float4) is
-          // loaded up front, so the 15 dependent steps wait on no LDS read
-          f32x4 a4[15][4];
-#pragma unroll
-          for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-            for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
-              a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&At[s2][4 * q4]);
-          // keep the loads ahead of the dependent steps (the scheduler would
-          // otherwise sink them next to their uses to save registers)
-          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int s2 = 0; s2 < 15; ++s2) {
 #pragma unroll
-            for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
+            for (int r = s2 + 1; r < 16; ++r)
+              asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                           : "+v"(x[r]) : "v"(na[r]), "v"(x[s2]), "i"(s2));
           }
           // T^T[o0 + col][o0 + r] = x[r], hi/lo (lanes 32..63 hold duplicates)
           if (lane < 32) {
@@ -613,10 +613,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       *reinterpret_cast<bf16x4 *>(&sm.A10h[j & 1][lr][4 * lg]) = h4;
       *reinterpret_cast<bf16x4 *>(&sm.A10l[j & 1][lr][4 * lg]) = l4;
       *reinterpret_cast<f32x4 *>(&sm.ATd[j & 1][1][lr][4 * lg]) =
-          decayed(bf, g, tile_acc(bf, false, 1, 1), 1, 1, false);
+          -decayed(bf, g, tile_acc(bf, false, 1, 1), 1, 1, false);
     } else if (pw == 1) {
       *reinterpret_cast<f32x4 *>(&sm.ATd[j & 1][0][lr][4 * lg]) =
-          decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
+          -decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
       store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
     } else {
       store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
