@@ -92,31 +92,6 @@ __device__ __forceinline__ float scan32_inclusive(float x) {
   return x;
 }
 
-// Block permutation of a q/k row with NB 16-byte blocks (NB = 16: 256-byte
-// rows spanning all 64 banks; NB = 8: 128-byte rows, two rows per bank
-// sweep).  A ds_read_b128 is serviced in four passes of 16 lanes; lane l
-// joins pass (l >> 5, parity of (l >> 2) & 7) (measured on gfx950 with the
-// bank-conflict counter), so one pass holds rows lr with
-// parity(lr >> 2) = p of lane group 2h and the other rows of group 2h + 1,
-// whose natural blocks differ in bit 0.  The permutation maps each of those
-// two row sets onto the even blocks (with the row parity for NB = 8), so a
-// pass reads 16 distinct blocks.  The transposing reads of k^T (64 lanes,
-// one 8-byte half) meet each bank pair four times, their minimum.
-template <int NB>
-__device__ __forceinline__ int swz_qk(int r) {
-  if constexpr (NB == 16) return 2 * (r & 7);
-  else return 2 * ((r >> 1) & 3);
-}
-
-// Block permutation of a v row (NB = 8: 128-byte rows; NB = 4: 64-byte
-// rows): the transposing reads of 8 rows x 2 blocks x 2 halves then hit 32
-// distinct bank pairs.
-template <int NB>
-__device__ __forceinline__ int swz_v(int r) {
-  if constexpr (NB == 8) return r & 6;
-  else return 2 * ((r >> 2) & 1);
-}
-
 template <int DK, int DVS>
 struct __align__(16) PipeSmem {
   static constexpr int LDC = C + 16;   // bf16 stride of [*][C] rows (transposing reads of
@@ -143,15 +118,6 @@ struct __align__(16) PipeSmem {
                                        // rows 16..31 x cols 0..15 stay zero
   float gw[3][C];                      // in-chunk log decay g, one copy per tile wave
 };
-
-// Makes this wave's earlier LDS writes visible to its later LDS reads of
-// other lanes' data (LDS serves one wave's accesses in order; the fences
-// keep the compiler from moving accesses across).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 template <int DK, int DVS, typename OutT, int GATE>
 __global__ void __launch_bounds__(64 * (DVS / 16 + NPW), 1)

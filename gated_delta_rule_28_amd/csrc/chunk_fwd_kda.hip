@@ -7,37 +7,42 @@
 // Per chunk of C = 16 tokens, entering state S, G = in-chunk cumulative
 // log decay per (token, channel), g_last its last row:
 //
-//   A_rs = b_r sum_c k_rc k_sc e^{G_rc - G_sc}   (s < r)      Gram
-//   P_rs =     sum_c q_rc k_sc e^{G_rc - G_sc}   (s <= r)     masked scores
+//   K^ = K o e^G,  Q^ = Q o e^G,  R^ = K o e^{-G}
+//   A_rs = b_r (K^ R^T)_rs   (s < r)      Gram
+//   P_rs =     (Q^ R^T)_rs   (s <= r)     masked scores
 //   T'   = (I + A)^{-1} diag(b)
-//   U    = T' (V - (K o e^G) S)
-//   O    = (Q o e^G) S + P U
-//   S   <- Diag(e^{g_last}) S + (K o e^{g_last - G})^T U
+//   U    = T' (V - K^ S)
+//   O    = Q^ S + P U
+//   S   <- Diag(e^{g_last}) (S + R^T U)
 //
-// Every decay factor in the state products is <= 1 (G is relative to the
-// chunk start and decreasing), so K o e^G, Q o e^G and K o e^{g_last - G}
-// never overflow.  They are not exact bf16 values, so the state products
-// use three MFMAs (hi*hi + hi*lo + lo*hi).
+// The last line is Diag(e^{g_last}) S + (K o e^{g_last - G})^T U with the
+// per-channel factor taken out of the product, so one derived key operand
+// (R^) serves the Gram, the scores and the state update.  The in-chunk
+// decays e^{G_r - G_s} factor about the chunk start; the page digest notes
+// that they can be tiny, so direct division is avoided and the factors stay
+// in range: K^ and Q^ are at most |k|, |q|, and R^ is at most e^{64} |k|
+// while every channel's in-chunk log decay stays above -64.  A chunk with a
+// channel below that (a near-hard reset) takes an exact path: its Gram and
+// scores are formed with every decay e^{G_rc - G_sc} directly in fp32, and
+// its state update uses K o e^{g_last - G} with the factor applied first.
 //
-// The in-chunk Gram and scores need e^{G_r - G_s} per channel.  The page
-// digest notes that these decays can be tiny, so direct division is
-// unstable and a log-space, two-level scheme is used.  Here they factor
-// about the chunk start: e^{G_r - G_s} = e^{G_r} e^{-G_s}, so the Gram is
-// (K o e^G)(K o e^{-G})^T and the scores (Q o e^G)(K o e^{-G})^T, reusing
-// the state-side operands on the left.  e^{-G_s} <= e^{-g_last}, so while
-// every channel's in-chunk log decay stays above -64 the factored operands
-// stay inside the fp32/bf16 range.  A chunk with a channel below that (a
-// near-hard reset) takes an exact path instead: every (r, s, c) decay is
-// formed directly in fp32.
+// Derived operands are not exact bf16, so every product takes three MFMAs
+// (hi*hi + hi*lo + lo*hi).
 //
-// Mapping as in the scalar-gate kernel: one workgroup per (batch, head, Dv
-// slice); DVS/16 state waves keep the state in MFMA accumulators; 4 prep
-// waves run two chunks ahead:
-//   X(i): waves 0, 1, 3 write chunk i (the threads that own a channel's log
-//         decays sum them as they write) and load chunk i+1; wave 2 forms A
-//         and solves it, wave 3 forms P, of chunk i-1
-//   Y(i): all prep waves derive the decayed operands of chunk i
-//   state: chunk i-2 (operand buffers three deep, T' two deep).
+// Mapping.  One workgroup per (batch, head, Dv slice of DVS columns); DVS/16
+// state waves keep the state in MFMA accumulators with the k axis ordered as
+// in the scalar-gate kernel (tile pair (2kk, 2kk+1) holds dk 32kk + 8g + j and
+// 32kk + 8g + 4 + j in rows 4g + j), so K^ S, Q^ S take the state straight
+// from registers and the update reads R^ transposed from a row-major tile.
+// Four prep waves; one workgroup barrier per iteration; in iteration i
+//   wave 0: LDS DMA of log a and b of chunk i+3; derives chunk i (a share)
+//   wave 1: LDS DMA of q, k of chunk i+3; sums the log decays of chunk i+1;
+//           derives chunk i (a share)
+//   wave 2: LDS DMA of v of chunk i; scores of chunk i-1; derives chunk i
+//   wave 3: Gram and solve of chunk i-1
+//   state:  chunk i-2
+// Raw inputs live four iterations (DMA to derivation), derived operands
+// three, v three, T' and P two.
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -47,35 +52,36 @@ namespace {
 
 constexpr int KC = 16;               // tokens per chunk
 constexpr int KNPW = 4;              // prep waves
-constexpr float kMaxSpan = 64.0f;    // per-channel in-chunk log-decay bound of the factored Gram
+constexpr float kMaxSpan = 64.0f;    // per-channel in-chunk log-decay bound of the factored form
+constexpr int NRAW = 4;              // raw slots: chunk j from iteration j-3 to j
+constexpr int NDER = 3;              // derived slots: chunk j from iteration j to j+2
+constexpr int NVB = 3;               // v slots: chunk j from iteration j to j+2
 
 template <int DK, int DVS>
 struct __align__(16) KdaSmem {
-  static constexpr int LDK = DK + 8;      // bf16 stride of [16][DK] tiles read by rows
-  static constexpr int LDC = DK + 16;     // bf16 stride of C, read transposed (8 rows x 8 banks)
-  static constexpr int LDG = DK + 4;      // fp32 stride of G
-  static constexpr int LDV = DVS + 16;    // bf16 stride of v rows, read transposed
-  static constexpr int LDT = KC;          // bf16 stride of 16x16 tiles, read transposed
-  struct __align__(16) Raw {              // staged chunk, natural channel order
-    bf16 Q[KC][LDK], K[KC][LDK];
-    float G[KC][LDG];                     // log a, then its in-chunk cumulative sum
-    float beta[KC];
-    int extreme[2];                       // per summing wave: some channel's in-chunk
-                                          // log decay < -kMaxSpan
+  static constexpr int LDX = 20;          // fp32 stride of the 16x16 exact-path and solve tiles
+  struct __align__(16) Raw {              // one chunk as the DMA leaves it
+    bf16 Q[KC][DK], K[KC][DK];            // natural channel order
+    float G[KC][DK];                      // log a, summed in place into G
+    float beta[64];                       // b of the 64 tokens from the chunk start (16 used)
+    int flag[4];                          // [0]: some channel's in-chunk log decay < -kMaxSpan
   };
-  struct __align__(16) Der {              // operands of one chunk
-    bf16 Kh[KC][LDK], Kl[KC][LDK];        // K o e^G, dk permuted
-    bf16 Qh[KC][LDK], Ql[KC][LDK];        // Q o e^G, dk permuted
-    bf16 Ch[KC][LDC], Cl[KC][LDC];        // K o e^{g_last - G}, natural order
-    bf16 Ph[KC][LDT], Pl[KC][LDT];        // P^T: [s][r] = P[r][s]
+  struct __align__(16) Der {              // operands of one chunk, rows permuted by swz_qk
+    bf16 Kh[KC][DK], Kl[KC][DK];          // K^ = K o e^G
+    bf16 Qh[KC][DK], Ql[KC][DK];          // Q^ = Q o e^G
+    bf16 Rh[KC][DK], Rl[KC][DK];          // R^ = K o e^{-G} (exact path: K o e^{g_last - G})
     float egl[DK];                        // e^{g_last}
+    float beta[KC];
+    int flag[4];
   };
-  Raw raw[2];
-  bf16 V[3][KC][LDV];                     // v rows of this slice, natural order
-  Der der[3];
-  bf16 Rkh[KC][LDK], Rkl[KC][LDK];        // K o e^{-G}, dk permuted (right operand of A and P)
-  float AT[16][20];                       // A^T for the solve
-  bf16 Th[2][KC][LDT], Tl[2][KC][LDT];    // T'^T
+  Raw raw[NRAW];
+  Der der[NDER];
+  bf16 V[NVB][KC][DVS];                   // v rows of this slice, blocks permuted by swz_v
+  bf16 Th[2][KC][KC], Tl[2][KC][KC];      // T'^T: [s][r] = T'[r][s]
+  bf16 Ph[2][KC][KC], Pl[2][KC][KC];      // P^T
+  float xA[2][KC][LDX];                   // exact path: -A^T ([s][r] = -A[r][s])
+  float xP[2][KC][LDX];                   // exact path: P^T
+  float At[KC][LDX];                      // -A^T of the chunk being solved
 };
 
 template <int DK, int DVS, typename OutT>
@@ -88,14 +94,21 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int DV = DK;
   constexpr int NSLICE = DV / DVS;
   constexpr int KKD = DK / 32;
+  constexpr int QB = DK / 8, VB = DVS / 8;      // 16-byte blocks per q/k and v row
+  constexpr int QRB = 2 * DK, VRB = 2 * DVS;    // bytes per q/k and v row
   static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
   using SM = KdaSmem<DK, DVS>;
+  static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(typename SM::Raw) % 16 == 0 && sizeof(typename SM::Der) % 16 == 0 &&
+                    (KC * QRB) % 1024 == 0 && (KC * VRB) % 1024 == 0,
+                "DMA runs are whole 1 KiB waves");
   __shared__ SM sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
 
+  // workgroup -> (chain, slice); slices of one chain share an XCD (same L2)
   const int nchain = B * H;
   int chain, slice;
   {
@@ -111,14 +124,22 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int bb = chain / H, hh = chain % H;
   const int nchunks = (T + KC - 1) / KC;
   const long tok0 = (long)bb * T * H + hh;   // token row of token 0 of this chain
-  const long ntok = (long)B * T * H;         // token rows of every input tensor
-  const bf16x4 zero4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
 
+  // byte offset inside a derived tile of row r, natural 16-byte block b
+  auto qk_at = [](int r, int b) { return r * QRB + 16 * (b ^ swz_qk<QB>(r)); };
+  // row reads: lane (lr, lg) takes row lr, dk 32 kk + 8 lg .. +7
+  int kq_off[KKD];
+#pragma unroll
+  for (int kk = 0; kk < KKD; ++kk) kq_off[kk] = qk_at(lr, 4 * kk + lg);
+
+  // Every role runs two prologue barriers and nchunks + 2 iterations of one
+  // barrier, so all waves execute the same sequence of workgroup barriers.
   if (wave < NSW) {
     // =====================================================================
-    // state waves
+    // state waves: the serial pass, 16 state columns each
     // =====================================================================
     const int col0 = slice * DVS + 16 * wave;
+    auto srow = [&](int mb, int e) { return 32 * (mb >> 1) + 8 * lg + 4 * (mb & 1) + e; };
     f32x4 Sacc[DK / 16];
 #pragma unroll
     for (int mb = 0; mb < DK / 16; ++mb) Sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -127,37 +148,54 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr];
+        for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)srow(mb, e) * DV + col0 + lr];
     }
-    // byte offsets of this lane's output values from a chunk's first row
+    __syncthreads();
+    __syncthreads();
+
     int ooff[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) ooff[e] = (int)sizeof(OutT) * ((4 * lg + e) * H * DV + col0 + lr);
-    __syncthreads();
+    // v, transposing read: rows 4 lg + (lr >> 2), columns 16 wave + 4 (lr & 3) .. +3
+    const int v_off = (4 * lg + (lr >> 2)) * VRB +
+                      16 * ((2 * wave + ((lr & 3) >> 1)) ^ swz_v<VB>(4 * lg + (lr >> 2))) + 8 * (lr & 1);
+    // R^T operand of the update for tile mb: rows (tokens) 4 lg + (lr >> 2),
+    // dk srow(mb, 0) + 4 (lr & 3) .. +3 = natural block (lr & 3) + 4 (mb >> 1), half mb & 1
+    int kt_off[KKD];
+#pragma unroll
+    for (int kk = 0; kk < KKD; ++kk) kt_off[kk] = qk_at(4 * lg + (lr >> 2), (lr & 3) + 4 * kk);
+    const bf16x4 zero4 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+
+    bf16x8 Sh[KKD], Sl[KKD];
+    auto split_state = [&]() {
+#pragma unroll
+      for (int kk = 0; kk < KKD; ++kk) {
+        bf16x4 h0, l0, h1, l1;
+        split4(Sacc[2 * kk], h0, l0);
+        split4(Sacc[2 * kk + 1], h1, l1);
+        Sh[kk] = cat(h0, h1);
+        Sl[kk] = cat(l0, l1);
+      }
+    };
+    split_state();
 
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;
-      f32x4 QS;
-      bf16x4 uh4, ul4;
       if (s >= 0) {
-        // ---- X: K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
-        const typename SM::Der &d = sm.der[s % 3];
-        bf16x8 Sh[KKD], Sl[KKD];
-#pragma unroll
-        for (int kk = 0; kk < KKD; ++kk) {
-          bf16x4 h0, l0, h1, l1;
-          split4<false>(Sacc[2 * kk], h0, l0);
-          split4<false>(Sacc[2 * kk + 1], h1, l1);
-          Sh[kk] = cat(h0, h1);
-          Sl[kk] = cat(l0, l1);
-        }
+        const typename SM::Der &d = sm.der[s % NDER];
+        const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
+        // ---- K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+        const char *Kh = reinterpret_cast<const char *>(&d.Kh[0][0]);
+        const char *Kl = reinterpret_cast<const char *>(&d.Kl[0][0]);
+        const char *Qh = reinterpret_cast<const char *>(&d.Qh[0][0]);
+        const char *Ql = reinterpret_cast<const char *>(&d.Ql[0][0]);
 #pragma unroll
         for (int kk = 0; kk < KKD; ++kk) {
-          const bf16x8 kh = ld8(&d.Kh[lr][32 * kk + 8 * lg]);
-          const bf16x8 kl = ld8(&d.Kl[lr][32 * kk + 8 * lg]);
-          const bf16x8 qh = ld8(&d.Qh[lr][32 * kk + 8 * lg]);
-          const bf16x8 ql = ld8(&d.Ql[lr][32 * kk + 8 * lg]);
+          const bf16x8 kh = ld8(reinterpret_cast<const bf16 *>(Kh + kq_off[kk]));
+          const bf16x8 qh = ld8(reinterpret_cast<const bf16 *>(Qh + kq_off[kk]));
+          const bf16x8 kl = ld8(reinterpret_cast<const bf16 *>(Kl + kq_off[kk]));
+          const bf16x8 ql = ld8(reinterpret_cast<const bf16 *>(Ql + kq_off[kk]));
           a1 = mfma_bf16(kh, Sh[kk], a1);
           a2 = mfma_bf16(qh, Sh[kk], a2);
           a1 = mfma_bf16(kh, Sl[kk], a1);
@@ -165,36 +203,32 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           a1 = mfma_bf16(kl, Sh[kk], a1);
           a2 = mfma_bf16(ql, Sh[kk], a2);
         }
-        QS = a2;
-        // V[4 lg + c][16 wave + lr] by a transposing read
-        const bf16x4 vv = ld_tr4(&sm.V[s % 3][4 * lg + (lr >> 2)][16 * wave + 4 * (lr & 3)]);
+        const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(
+            reinterpret_cast<const char *>(&sm.V[s % NVB][0][0]) + v_off));
         f32x4 rr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - a1[e];
         bf16x4 rh4, rl4;
-        split4<false>(rr, rh4, rl4);
+        split4(rr, rh4, rl4);
         // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
         const bf16x8 ta = cat(ld_tr4(&sm.Th[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]),
                               ld_tr4(&sm.Tl[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]));
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         u = mfma_bf16(ta, cat(rh4, rh4), u);
         u = mfma_bf16(ta, cat(rl4, zero4), u);
-        split4<false>(u, uh4, ul4);
-      }
-      __syncthreads();
-      if (s >= 0) {
-        // ---- Y: O = Q^ S + P U; S <- Diag(e^{g_last}) S + (K o e^{g_last-G})^T U ----
-        const typename SM::Der &d = sm.der[s % 3];
+        bf16x4 uh4, ul4;
+        split4(u, uh4, ul4);
+
+        // ---- O = Q^ S + P U ----
         const int t0 = s * KC, n = min(KC, T - t0);
-        const bf16x8 pa = cat(ld_tr4(&d.Ph[4 * lg + (lr >> 2)][4 * (lr & 3)]),
-                              ld_tr4(&d.Pl[4 * lg + (lr >> 2)][4 * (lr & 3)]));
-        f32x4 acc = QS;
+        const bf16x8 pa = cat(ld_tr4(&sm.Ph[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                              ld_tr4(&sm.Pl[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]));
+        f32x4 acc = a2;
         acc = mfma_bf16(pa, cat(uh4, uh4), acc);
         acc = mfma_bf16(pa, cat(ul4, zero4), acc);
-        // lane holds O rows 4 lg + e of column col0 + lr: stored straight from
-        // the accumulator; rows past the end of the sequence are not written
         const long orow = (tok0 + (long)t0 * H) * DV;
-        const rsrc_t ro = make_rsrc(o + orow, (long)sizeof(OutT) * (ntok * DV - orow));
+        // the chunk's rows: smaller than 4 GiB (the host checks the shape)
+        const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
         if (n == KC) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[e]);
@@ -203,18 +237,23 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int e = 0; e < 4; ++e)
             if (4 * lg + e < n) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[e]);
         }
+
+        // ---- S <- Diag(e^{g_last}) (S + R^T U) (exact path: factor first) ----
         const bf16x8 b1 = cat(uh4, uh4), b2 = cat(ul4, zero4);
+        const char *Rh = reinterpret_cast<const char *>(&d.Rh[0][0]);
+        const char *Rl = reinterpret_cast<const char *>(&d.Rl[0][0]);
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb) {
-          const f32x4 eg4 = *reinterpret_cast<const f32x4 *>(&d.egl[16 * mb + 4 * lg]);
-          const int c0 = 16 * mb + 4 * (lr & 3);
-          const bf16x8 a = cat(ld_tr4(&d.Ch[4 * lg + (lr >> 2)][c0]),
-                               ld_tr4(&d.Cl[4 * lg + (lr >> 2)][c0]));
-          f32x4 sa = Sacc[mb] * eg4;
+          const f32x4 eg4 = *reinterpret_cast<const f32x4 *>(&d.egl[srow(mb, 0)]);
+          const int off = kt_off[mb >> 1] + 8 * (mb & 1);
+          const bf16x8 a = cat(ld_tr4(reinterpret_cast<const bf16 *>(Rh + off)),
+                               ld_tr4(reinterpret_cast<const bf16 *>(Rl + off)));
+          f32x4 sa = exact ? Sacc[mb] * eg4 : Sacc[mb];
           sa = mfma_bf16(a, b1, sa);
           sa = mfma_bf16(a, b2, sa);
-          Sacc[mb] = sa;
+          Sacc[mb] = exact ? sa : sa * eg4;
         }
+        split_state();
       }
       __syncthreads();
     }
@@ -224,7 +263,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) SF[(long)(16 * mb + 4 * lg + e) * DV + col0 + lr] = Sacc[mb][e];
+        for (int e = 0; e < 4; ++e) SF[(long)srow(mb, e) * DV + col0 + lr] = Sacc[mb][e];
     }
     return;
   }
@@ -233,254 +272,275 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // prep waves
   // =======================================================================
   const int pw = wave - NSW;
-  const int pt = tid - 64 * NSW;       // 0..255
-  // Staging runs on prep waves 0, 1 and 3; wave 2 (Gram and solve) runs a
-  // loop of its own.  Waves 0 and 1 load k and q (item = RPI tokens x 8
-  // columns, 64 items per matrix, so each wave reads one matrix through one
-  // buffer descriptor); wave 3 loads v (item = 8 columns of one token) and
-  // beta.  Thread c < Dk of waves 0 and 1 also loads the 16 log decays of
-  // channel c and sums them as it writes them.  Loads are unconditional
-  // inside each wave; rows past the end of the sequence read the next rows
-  // (or zeros past the end of a tensor) and are zeroed when written to LDS.
-  constexpr int DCS = DK / 8;
-  constexpr int RPI = KC * DCS / 64;   // tokens per q/k item (4 at d = 128, 2 at d = 64)
-  constexpr int VCS = DVS / 8;
-  constexpr int NV = KC * VCS;         // v items (128 or 64)
-  constexpr int NVS = NV / 64;         // v items per wave-3 thread
-  static_assert(RPI * 64 == KC * DCS && NV % 64 == 0, "staging items");
-  const bool is_k = pw == 0;
-  const int q_r0 = RPI * (lane / DCS), q_c0 = 8 * (lane % DCS);
-  int v_r[NVS], v_c0[NVS];
-#pragma unroll
-  for (int h = 0; h < NVS; ++h) {
-    const int vi = lane + 64 * h;
-    v_r[h] = vi / VCS;
-    v_c0[h] = 8 * (vi % VCS);
-  }
-  // one set of 16-byte load slots per staging thread, whatever its tensor:
-  // q/k rows on waves 0 and 1, v items on wave 3 (surplus slots re-load the
-  // first item), so the staging loads are the same straight-line code on
-  // every staging wave
-  constexpr int NL = RPI > NVS ? RPI : NVS;
-  int soff[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i)
-    soff[i] = (pw < 2) ? 2 * ((q_r0 + (i < RPI ? i : 0)) * H * DK + q_c0)
-                       : 2 * (v_r[i < NVS ? i : 0] * H * DV + slice * DVS + v_c0[i < NVS ? i : 0]);
-  const bf16 *ssrc = pw == 0 ? k : (pw == 1 ? q : v);   // wave-uniform
-  const int la_c = (pw == 1 && DK > 64) ? 64 + lane : lane;   // channel summed by this thread
-  const bool sums = pw < 2 && 64 * pw + lane < DK;           // wave-uniform
 
-  // operands of chunk j (its G was summed in phase X); all four prep waves
-  // take a share: thread = (channel pair, tokens)
-  auto derive = [&](int j) {
-    const typename SM::Raw &rw = sm.raw[j & 1];
-    typename SM::Der &d = sm.der[j % 3];
-    constexpr int NCP = DK / 2;                 // channel pairs
-    constexpr int TPG = KC * NCP / 256;         // tokens per thread
-    const int cp = pt % NCP, tq = pt / NCP;
-    const int c0 = 2 * cp;
-    const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
-    if (tq == 0) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
-    // e^{-g_last}: scales K o e^{g_last - G} to K o e^{-G}; it can overflow
-    // only in chunks that take the exact Gram path, which do not read Rk
-    const float eng0 = __expf(-gl[0]), eng1 = __expf(-gl[1]);
-    const int pc = perm32(c0);
-    auto put2 = [](bf16 *hi, bf16 *lo, float x0, float x1) {
-      unsigned h, l;
-      split2<false>(x0, x1, h, l);
-      *reinterpret_cast<unsigned *>(hi) = h;
-      *reinterpret_cast<unsigned *>(lo) = l;
-    };
+  // 16x16 tile L R^T of derived operands (hi/lo both sides, three
+  // independent MFMA chains); lane holds rows 4 lg + e of column lr
+  auto tile = [&](const bf16 *Lh, const bf16 *Ll, const bf16 *Rh, const bf16 *Rl) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, a1 = acc, a2 = acc;
 #pragma unroll
-    for (int i = 0; i < TPG; ++i) {
-      const int r = TPG * tq + i;
-      const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
-      const float k0 = (float)rw.K[r][c0], k1 = (float)rw.K[r][c0 + 1];
-      const float q0 = (float)rw.Q[r][c0], q1 = (float)rw.Q[r][c0 + 1];
-      const float e0 = __expf(g[0]), e1 = __expf(g[1]);
-      const float c0e = k0 * __expf(gl[0] - g[0]), c1e = k1 * __expf(gl[1] - g[1]);
-      put2(&d.Kh[r][pc], &d.Kl[r][pc], k0 * e0, k1 * e1);
-      put2(&d.Qh[r][pc], &d.Ql[r][pc], q0 * e0, q1 * e1);
-      put2(&d.Ch[r][c0], &d.Cl[r][c0], c0e, c1e);
-      put2(&sm.Rkh[r][pc], &sm.Rkl[r][pc], c0e * eng0, c1e * eng1);
+    for (int kk = 0; kk < KKD; ++kk) {
+      const int off = kq_off[kk] / 2;
+      const bf16x8 ah = ld8(Lh + off), al = ld8(Ll + off);
+      const bf16x8 bh = ld8(Rh + off), bl = ld8(Rl + off);
+      acc = mfma_bf16(ah, bh, acc);
+      a1 = mfma_bf16(ah, bl, a1);
+      a2 = mfma_bf16(al, bh, a2);
     }
+    return acc + a1 + a2;
   };
 
-  // lower 16x16 tile (X o e^G)-decayed Gram of chunk j: X = K (isq false)
-  // or X = Q (isq true); lane holds rows 4 lg + e of column lr
-  auto tile = [&](int j, bool isq) -> f32x4 {
-    const typename SM::Raw &rw = sm.raw[j & 1];
-    const typename SM::Der &d = sm.der[j % 3];
-    const bool extreme = rw.extreme[0] | (DK > 64 ? rw.extreme[1] : 0);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (!extreme) {
-      // (X o e^G)(K o e^{-G})^T with X = K or Q, in dk-permuted order; the
-      // three products accumulate separately (independent MFMA chains)
-      const bf16(*Lh)[SM::LDK] = isq ? d.Qh : d.Kh;
-      const bf16(*Ll)[SM::LDK] = isq ? d.Ql : d.Kl;
-      f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KKD; ++kk) {
-        const bf16x8 ah = ld8(&Lh[lr][32 * kk + 8 * lg]);
-        const bf16x8 al = ld8(&Ll[lr][32 * kk + 8 * lg]);
-        const bf16x8 bh = ld8(&sm.Rkh[lr][32 * kk + 8 * lg]);
-        const bf16x8 bl = ld8(&sm.Rkl[lr][32 * kk + 8 * lg]);
-        acc = mfma_bf16(ah, bh, acc);
-        a1 = mfma_bf16(ah, bl, a1);
-        a2 = mfma_bf16(al, bh, a2);
-      }
-      acc += a1 + a2;
-    } else {
-      // exact: every decay e^{G_rc - G_sc} formed directly (s <= r only)
-      const bf16(*X)[SM::LDK] = isq ? rw.Q : rw.K;
-      const int sc = lr;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * lg + e;
-        float sum = 0.0f;
-        if (sc <= r) {
-          for (int c = 0; c < DK; ++c)
-            sum += (float)X[r][c] * (float)rw.K[sc][c] * __expf(rw.G[r][c] - rw.G[sc][c]);
-        }
-        acc[e] = sum;
-      }
-    }
-    return acc;
-  };
-  // P of chunk j (lower incl.), split hi/lo, transposed
-  auto scores = [&](int j) {
-    typename SM::Der &d = sm.der[j % 3];
-    const f32x4 acc = tile(j, true);
-    const int sc = lr, r0 = 4 * lg;
-    f32x4 val;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) val[e] = (sc <= r0 + e) ? acc[e] : 0.0f;
-    bf16x4 h4, l4;
-    split4<false>(val, h4, l4);
-    *reinterpret_cast<bf16x4 *>(&d.Ph[sc][r0]) = h4;
-    *reinterpret_cast<bf16x4 *>(&d.Pl[sc][r0]) = l4;
-  };
-  // A of chunk j (strict lower, times b), then T' = (I + A)^{-1} diag(b)
-  auto gram_solve = [&](int j) {
-    const typename SM::Raw &rw = sm.raw[j & 1];
-    const f32x4 acc = tile(j, false);
-    const int sc = lr, r0 = 4 * lg;
-    f32x4 val;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) val[e] = (sc < r0 + e) ? rw.beta[r0 + e] * acc[e] : 0.0f;
-    *reinterpret_cast<f32x4 *>(&sm.AT[sc][r0]) = val;   // AT[s][r] = A[r][s]
-    // T = (I + A)^{-1}, lane = column; right-looking forward substitution
-    const int col = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
-    // every needed entry of A^T is loaded before the dependent steps (the
-    // scheduling barrier keeps the loads there)
-    f32x4 a4[15][4];
-#pragma unroll
-    for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-      for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4)
-        a4[s2][q4] = *reinterpret_cast<const f32x4 *>(&sm.AT[s2][4 * q4]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s2 = 0; s2 < 15; ++s2) {
-#pragma unroll
-      for (int r = s2 + 1; r < 16; ++r) x[r] -= a4[s2][r / 4][r % 4] * x[s2];
-    }
-    if (lane < 16) {
-      const float bcol = rw.beta[col];
-      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-      unsigned h8[2][4], l8[2][4];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        split2<false>(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-        *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
-      }
-    }
-  };
-
-  if (pw == 2) {
-    // ---- Gram/solve wave: A and T' of chunk it-1 in phase X, a share of the
-    //      derivation of chunk it in phase Y ----
+  if (pw == 3) {
+    // ---- Gram and solve of chunk it-1: T' = (I + A)^{-1} diag(b) ----
+    __syncthreads();
     __syncthreads();
     for (int it = 0; it < nchunks + 2; ++it) {
-      if (it >= 1 && it - 1 < nchunks) gram_solve(it - 1);
-      __syncthreads();
-      if (it < nchunks) derive(it);
+      const int j = it - 1;
+      if (j >= 0 && j < nchunks) {
+        const typename SM::Der &d = sm.der[j % NDER];
+        const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
+        const float(*src)[SM::LDX] = sm.At;
+        if (!exact) {
+          const f32x4 acc = tile(&d.Kh[0][0], &d.Kl[0][0], &d.Rh[0][0], &d.Rl[0][0]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&d.beta[4 * lg]);
+          f32x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = (lr < 4 * lg + e) ? -b4[e] * acc[e] : 0.0f;
+          *reinterpret_cast<f32x4 *>(&sm.At[lr][4 * lg]) = val;   // [s][r] = -A[r][s]
+          wave_lds_sync();
+        } else {
+          src = sm.xA[j & 1];
+        }
+        // right-looking forward substitution, lane = column col (each
+        // 16-lane row holds all columns); lane col keeps column col of -A
+        // and step s takes column s from lane s by a row broadcast folded
+        // into the FMA
+        const int col = lr;
+        float na[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 t = *reinterpret_cast<const f32x4 *>(&src[col][4 * q4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) na[4 * q4 + e] = t[e];
+        }
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < 15; ++s2) {
+#pragma unroll
+          for (int r = s2 + 1; r < 16; ++r)
+            asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                         : "+v"(x[r]) : "v"(na[r]), "v"(x[s2]), "i"(s2));
+        }
+        // T'^T[col][r] = T[r][col] b_col, hi/lo (lanes 16..63 hold duplicates)
+        if (lane < 16) {
+          const float bcol = d.beta[col];
+          unsigned h8[2][4], l8[2][4];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+          }
+        }
+      }
       __syncthreads();
     }
     return;
   }
 
-  // ---- staging waves 0, 1, 3 ----
-  bf16x8 stg[NL];
-  float stl[KC];                       // log decays of channel la_c, rows 0..15
-  float stg_b = 0.f;
-  auto stage_chunk = [&](int j) {
-    const long row0 = tok0 + (long)j * KC * H;
-    stg_b = buf_ld1f(make_rsrc(beta + row0, 4 * (ntok - row0)), 4 * (lane & (KC - 1)) * H);
-    const rsrc_t r = make_rsrc(ssrc + row0 * DK, 2 * (ntok - row0) * DK);   // DK == DV
+  // ---- prep waves 0..2: LDS DMA, log-decay sums, derivation, scores ----
+  // DMA shares: wave 0 log a (+ b), wave 1 q and k, wave 2 v.  Instruction i
+  // of a tile fills LDS bytes 1024 i .. +1023 of it.
+  constexpr int NQI = KC * QRB / 1024;         // per q or k tile
+  constexpr int NLI = KC * 4 * DK / 1024;      // log a tile
+  constexpr int NVI = KC * VRB / 1024;         // v tile
+  constexpr int N0 = NLI + 1, N1 = 2 * NQI, N2 = NVI;
+  constexpr int NI = (NLI > NQI) ? NLI : NQI;
+  unsigned voff[NI];
+  if (pw == 0) {
+    constexpr int BPR = 4 * DK / 16, RPI = 1024 / (4 * DK);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) stg[i] = buf_ld8(r, soff[i]);
-    const rsrc_t rl = make_rsrc(log_alpha + row0 * DK, 4 * (ntok - row0) * DK);
-#pragma unroll
-    for (int rr = 0; rr < KC; ++rr) stl[rr] = buf_ld1f(rl, 4 * (rr * H * DK + la_c));
-  };
-  auto zero_rows = [](bf16x8 x, bool z) -> bf16x8 {
-    if (z) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) x[jj] = (bf16)0.0f;
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + lane / BPR;
+      voff[i] = (unsigned)(row * H * DK * 4 + 16 * (lane % BPR));
     }
-    return x;
+  } else if (pw == 1) {
+    constexpr int BPR = QRB / 16, RPI = 1024 / QRB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + lane / BPR;
+      voff[i] = (unsigned)(row * H * DK * 2 + 16 * (lane % BPR));
+    }
+  } else {
+    constexpr int BPR = VRB / 16, RPI = 1024 / VRB;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + lane / BPR, sb = lane % BPR;
+      voff[i] = (unsigned)(row * H * DV * 2 + 2 * slice * DVS + 16 * (sb ^ swz_v<VB>(row)));
+    }
+  }
+  const unsigned soff = (unsigned)(lane * H * 4);   // b of token `lane`
+
+  // q, k, log a and b of chunk j (waves 0 and 1)
+  auto issue_raw = [&](int j) {
+    typename SM::Raw &dst = sm.raw[j % NRAW];
+    const int n = min(KC, T - j * KC);
+    const long row0 = tok0 + (long)j * KC * H;
+    if (pw == 0) {
+      const u32x4 rl = rsrc_words(log_alpha + row0 * DK, 4u * ((unsigned)(n - 1) * H * DK + DK));
+      const unsigned ll = lds_addr(&dst.G[0][0]);
+#pragma unroll
+      for (int i = 0; i < NLI; ++i) lds_dma16(rl, voff[i], ll + 1024 * i);
+      lds_dma4(rsrc_words(beta + row0, 4u * ((unsigned)(n - 1) * H + 1)), soff, lds_addr(&dst.beta[0]));
+    } else {
+      const u32x4 rq = rsrc_words(q + row0 * DK, 2u * ((unsigned)(n - 1) * H * DK + DK));
+      const u32x4 rk = rsrc_words(k + row0 * DK, 2u * ((unsigned)(n - 1) * H * DK + DK));
+      const unsigned lq = lds_addr(&dst.Q[0][0]), lk = lds_addr(&dst.K[0][0]);
+#pragma unroll
+      for (int i = 0; i < NQI; ++i) lds_dma16(rq, voff[i], lq + 1024 * i);
+#pragma unroll
+      for (int i = 0; i < NQI; ++i) lds_dma16(rk, voff[i], lk + 1024 * i);
+    }
+  };
+  // v of chunk j, this slice's columns (wave 2)
+  auto issue_v = [&](int j) {
+    const int n = min(KC, T - j * KC);
+    const long row0 = tok0 + (long)j * KC * H;
+    const u32x4 rv = rsrc_words(v + row0 * DV, 2u * ((unsigned)(n - 1) * H * DV + DV));
+    const unsigned lv = lds_addr(&sm.V[j % NVB][0][0]);
+#pragma unroll
+    for (int i = 0; i < NVI; ++i) lds_dma16(rv, voff[i], lv + 1024 * i);
   };
 
-  if (nchunks > 0) stage_chunk(0);
+  // in-chunk cumulative log decay of chunk j, in place (wave 1): lane = a
+  // channel pair; padded tokens read log a = 0; flags a chunk whose
+  // factored operands could leave the floating-point range
+  auto gsum = [&](int j) {
+    typename SM::Raw &rw = sm.raw[j % NRAW];
+    constexpr int NCP = DK / 2;
+    const int c0 = 2 * (lane % NCP);
+    f32x2 acc = {0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < KC; ++r) {
+      acc += *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      if (lane < NCP) *reinterpret_cast<f32x2 *>(&rw.G[r][c0]) = acc;
+    }
+    const unsigned long long bad = __ballot(acc[0] < -kMaxSpan || acc[1] < -kMaxSpan);
+    if (lane == 0) rw.flag[0] = bad != 0ull;
+  };
+
+  // derived operands of chunk j: wave w of 0..2 takes work rows
+  // [b(w), b(w+1)) of NRW, a work row = 64 lanes = (channel pair, token)
+  constexpr int NCP = DK / 2, TPR = 64 / NCP, NRW = KC / TPR;
+  auto derive = [&](int j) {
+    const typename SM::Raw &rw = sm.raw[j % NRAW];
+    typename SM::Der &d = sm.der[j % NDER];
+    const int exact = __builtin_amdgcn_readfirstlane(rw.flag[0]);
+    const int cp = lane % NCP, c0 = 2 * cp;
+    const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
+    if (pw == 0) {
+      if (lane < NCP) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
+      if (lane < KC) d.beta[lane] = rw.beta[lane];
+      if (lane == 0) d.flag[0] = exact;
+    }
+    const int rb0 = (pw * NRW + 2) / 3, rb1 = ((pw + 1) * NRW + 2) / 3;
+    const int coff = 2 * (c0 & 7);                 // byte offset inside the 16-byte block
+    const f32x2 sh = exact ? gl : f32x2{0.f, 0.f};   // R^ = K o e^{sh - G}
+    auto put = [&](bf16 (*hi)[DK], bf16 (*lo)[DK], int r, float x0, float x1) {
+      unsigned h, l;
+      split2<false>(x0, x1, h, l);
+      const int off = qk_at(r, c0 >> 3) + coff;
+      *reinterpret_cast<unsigned *>(reinterpret_cast<char *>(&hi[0][0]) + off) = h;
+      *reinterpret_cast<unsigned *>(reinterpret_cast<char *>(&lo[0][0]) + off) = l;
+    };
+    for (int w = rb0; w < rb1; ++w) {
+      const int r = w * TPR + lane / NCP;
+      const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      const unsigned kb = *reinterpret_cast<const unsigned *>(&rw.K[r][c0]);
+      const unsigned qb = *reinterpret_cast<const unsigned *>(&rw.Q[r][c0]);
+      const float k0 = __builtin_bit_cast(float, kb << 16), k1 = __builtin_bit_cast(float, kb & 0xffff0000u);
+      const float q0 = __builtin_bit_cast(float, qb << 16), q1 = __builtin_bit_cast(float, qb & 0xffff0000u);
+      const float e0 = __expf(g[0]), e1 = __expf(g[1]);
+      const float f0 = __expf(sh[0] - g[0]), f1 = __expf(sh[1] - g[1]);
+      put(d.Kh, d.Kl, r, k0 * e0, k1 * e1);
+      put(d.Qh, d.Ql, r, q0 * e0, q1 * e1);
+      put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);
+    }
+    if (exact) {
+      // exact Gram and scores: every decay formed directly; entry (r, s)
+      // of both tiles per item, 256 items over the three waves
+      for (int idx = 64 * pw + lane; idx < KC * KC; idx += 192) {
+        const int r = idx / KC, s = idx % KC;
+        float sa = 0.0f, sp = 0.0f;
+        if (s <= r) {
+          for (int c = 0; c < DK; ++c) {
+            const float ks = (float)rw.K[s][c] * __expf(rw.G[r][c] - rw.G[s][c]);
+            sa += (float)rw.K[r][c] * ks;
+            sp += (float)rw.Q[r][c] * ks;
+          }
+        }
+        sm.xA[j & 1][s][r] = (s < r) ? -rw.beta[r] * sa : 0.0f;
+        sm.xP[j & 1][s][r] = sp;
+      }
+    }
+  };
+
+  // P of chunk j (lower incl.), split hi/lo, transposed (wave 2)
+  auto scores = [&](int j) {
+    const typename SM::Der &d = sm.der[j % NDER];
+    const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
+    f32x4 val;
+    if (!exact) {
+      const f32x4 acc = tile(&d.Qh[0][0], &d.Ql[0][0], &d.Rh[0][0], &d.Rl[0][0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (lr <= 4 * lg + e) ? acc[e] : 0.0f;
+    } else {
+      val = *reinterpret_cast<const f32x4 *>(&sm.xP[j & 1][lr][4 * lg]);
+    }
+    bf16x4 h4, l4;
+    split4(val, h4, l4);
+    *reinterpret_cast<bf16x4 *>(&sm.Ph[j & 1][lr][4 * lg]) = h4;
+    *reinterpret_cast<bf16x4 *>(&sm.Pl[j & 1][lr][4 * lg]) = l4;
+  };
+
+  auto wait_own = [&](bool newer_issued) {
+    if (newer_issued) {
+      if (pw == 0) wait_vmcnt<N0>();
+      else if (pw == 1) wait_vmcnt<N1>();
+      else wait_vmcnt<N2>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  };
+
+  // prologue: raw chunks 0..2 in flight, 0 and 1 landed, chunk 0 summed
+  if (pw < 2) {
+    if (nchunks > 0) issue_raw(0);
+    if (nchunks > 1) issue_raw(1);
+    if (nchunks > 2) issue_raw(2);
+    wait_own(nchunks > 2);
+  }
+  __syncthreads();
+  if (pw == 1 && nchunks > 0) gsum(0);
   __syncthreads();
 
   for (int it = 0; it < nchunks + 2; ++it) {
-    // ================= phase X =================
-    // every load in flight is one of chunk it's, consumed right here: one
-    // wait for all of them on every path
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if (it < nchunks) {
-      // write staged chunk it; padding tokens (past T) become zeros with log a = 0
-      typename SM::Raw &rw = sm.raw[it & 1];
-      const int n = min(KC, T - it * KC);
-      if (pw < 2) {
-        bf16(*dst)[SM::LDK] = is_k ? rw.K : rw.Q;
-#pragma unroll
-        for (int i = 0; i < RPI; ++i)
-          *reinterpret_cast<bf16x8 *>(&dst[q_r0 + i][q_c0]) = zero_rows(stg[i], q_r0 + i >= n);
-        if (sums) {
-          // in-chunk cumulative log decay of channel la_c; flag the chunk
-          // when the factored Gram could leave the floating-point range
-          float acc = 0.0f;
-#pragma unroll
-          for (int rr = 0; rr < KC; ++rr) {
-            acc += (rr < n) ? stl[rr] : 0.0f;
-            rw.G[rr][la_c] = acc;
-          }
-          const unsigned long long bad = __ballot(acc < -kMaxSpan);
-          if (lane == 0) rw.extreme[pw] = bad != 0ull;
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < NVS; ++h)
-          *reinterpret_cast<bf16x8 *>(&sm.V[it % 3][v_r[h]][v_c0[h]]) = zero_rows(stg[h], v_r[h] >= n);
-        if (lane < KC) rw.beta[lane] = (lane < n) ? stg_b : 0.0f;
-      }
-      if (it + 1 < nchunks) stage_chunk(it + 1);
+    if (pw < 2) {
+      const bool more = it + 3 < nchunks;
+      if (more) issue_raw(it + 3);
+      if (pw == 1 && it + 1 < nchunks) gsum(it + 1);
+      if (it < nchunks) derive(it);
+      wait_own(more);
+    } else {
+      const bool more = it < nchunks;
+      if (more) issue_v(it);
+      if (it >= 1 && it - 1 < nchunks) scores(it - 1);
+      if (it < nchunks) derive(it);
+      wait_own(more);
     }
-    if (pw == 3 && it >= 1 && it - 1 < nchunks) scores(it - 1);
-    __syncthreads();
-
-    // ================= phase Y =================
-    if (it < nchunks) derive(it);
     __syncthreads();
   }
 }
@@ -503,7 +563,10 @@ hipError_t kda_by_out(const ChunkArgs &a) {
 }  // namespace
 
 bool chunk_fwd_kda_supported(const ChunkArgs &a) {
-  return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate == kGateChannel;
+  // the chunk-sized buffer descriptors of the log decays (the widest rows)
+  // are 32-bit
+  return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate == kGateChannel &&
+         4.0 * ((double)(KC - 1) * a.H * a.D + a.D) < 4294967295.0;
 }
 
 hipError_t launch_chunk_fwd_kda(const ChunkArgs &a) {

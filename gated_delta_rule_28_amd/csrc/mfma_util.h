@@ -17,6 +17,41 @@ __device__ __forceinline__ bf16x8 ld8(const bf16 *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
+// Block permutation of a q/k row with NB 16-byte blocks (NB = 16: 256-byte
+// rows spanning all 64 banks; NB = 8: 128-byte rows, two rows per bank
+// sweep).  A ds_read_b128 is serviced in four passes of 16 lanes; lane l
+// joins pass (l >> 5, parity of (l >> 2) & 7) (measured on gfx950 with the
+// bank-conflict counter), so one pass holds rows lr with
+// parity(lr >> 2) = p of lane group 2h and the other rows of group 2h + 1,
+// whose natural blocks differ in bit 0.  The permutation maps each of those
+// two row sets onto the even blocks (with the row parity for NB = 8), so a
+// pass reads 16 distinct blocks.  The transposing reads of k^T (64 lanes,
+// one 8-byte half) meet each bank pair four times, their minimum.
+template <int NB>
+__device__ __forceinline__ int swz_qk(int r) {
+  if constexpr (NB == 16) return 2 * (r & 7);
+  else return 2 * ((r >> 1) & 3);
+}
+
+// Block permutation of a v row (NB = 8: 128-byte rows; NB = 4: 64-byte
+// rows): the transposing reads of 8 rows x 2 blocks x 2 halves then hit 32
+// distinct bank pairs.
+template <int NB>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (NB == 8) return r & 6;
+  else return 2 * ((r >> 2) & 1);
+}
+
+// Makes this wave's earlier LDS writes visible to its later LDS reads of
+// other lanes' data (LDS serves one wave's accesses in order; the fences
+// keep the compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
