@@ -34,12 +34,13 @@
 // in the scalar-gate kernel (tile pair (2kk, 2kk+1) holds dk 32kk + 8g + j and
 // 32kk + 8g + 4 + j in rows 4g + j), so K^ S, Q^ S take the state straight
 // from registers and the update reads R^ transposed from a row-major tile.
-// Four prep waves; one workgroup barrier per iteration; in iteration i
+// Four or six prep waves; one workgroup barrier per iteration; in iteration i
 //   wave 0: LDS DMA of log a and b of chunk i+3; derives chunk i (a share)
 //   wave 1: LDS DMA of q, k of chunk i+3; sums the log decays of chunk i+1;
 //           derives chunk i (a share)
 //   wave 2: LDS DMA of v of chunk i; scores of chunk i-1; derives chunk i
 //   wave 3: Gram and solve of chunk i-1
+//   waves 4, 5 (32-column slices): derive chunk i (shares)
 //   state:  chunk i-2
 // Raw inputs live four iterations (DMA to derivation), derived operands
 // three, v three, T' and P two.
@@ -51,7 +52,9 @@ namespace gdr {
 namespace {
 
 constexpr int KC = 16;               // tokens per chunk
-constexpr int KNPW = 4;              // prep waves
+// prep waves: 4, or 6 with 32-column slices (8 waves, two per SIMD)
+template <int DVS>
+constexpr int kda_npw() { return DVS == 32 ? 6 : 4; }
 constexpr float kMaxSpan = 64.0f;    // per-channel in-chunk log-decay bound of the factored form
 constexpr int NRAW = 4;              // raw slots: chunk j from iteration j-3 to j
 constexpr int NDER = 3;              // derived slots: chunk j from iteration j to j+2
@@ -85,7 +88,7 @@ struct __align__(16) KdaSmem {
 };
 
 template <int DK, int DVS, typename OutT>
-__global__ void __launch_bounds__(64 * (DVS / 16 + KNPW), 1)
+__global__ void __launch_bounds__(64 * (DVS / 16 + kda_npw<DVS>()), 1)
 chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ beta,
                      const float *__restrict__ log_alpha, const float *initial_state,
@@ -432,9 +435,24 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (lane == 0) rw.flag[0] = bad != 0ull;
   };
 
-  // derived operands of chunk j: wave w of 0..2 takes work rows
-  // [b(w), b(w+1)) of NRW, a work row = 64 lanes = (channel pair, token)
+  // derived operands of chunk j: a work row is 64 lanes = (channel pair,
+  // token), shared by every prep wave but the solver's; wave 0 takes the
+  // most (it only issues DMA besides), wave 2 the fewest (it forms the
+  // scores).  Boundaries in 16ths of the NRW rows: 4 waves 0|7|12|16, 6
+  // waves 0|4|7|9|13|16 (waves 0, 1, 2, 4, 5).
+  constexpr int NPW = kda_npw<DVS>();
+  constexpr int NDW = NPW - 1;                 // deriving waves
   constexpr int NCP = DK / 2, TPR = 64 / NCP, NRW = KC / TPR;
+  const int dw = pw < 3 ? pw : pw - 1;         // index among the deriving waves
+  auto row_bound = [&](int w) {
+    if constexpr (NPW == 6) {
+      constexpr int b[6] = {0, 4, 7, 9, 13, 16};
+      return b[w] * NRW / 16;
+    } else {
+      constexpr int b[4] = {0, 7, 12, 16};
+      return b[w] * NRW / 16;
+    }
+  };
   auto derive = [&](int j) {
     const typename SM::Raw &rw = sm.raw[j % NRAW];
     typename SM::Der &d = sm.der[j % NDER];
@@ -446,7 +464,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (lane < KC) d.beta[lane] = rw.beta[lane];
       if (lane == 0) d.flag[0] = exact;
     }
-    const int rb0 = (pw * NRW + 2) / 3, rb1 = ((pw + 1) * NRW + 2) / 3;
+    const int rb0 = row_bound(dw), rb1 = row_bound(dw + 1);
     const int coff = 2 * (c0 & 7);                 // byte offset inside the 16-byte block
     const f32x2 sh = exact ? gl : f32x2{0.f, 0.f};   // R^ = K o e^{sh - G}
     auto put = [&](bf16 (*hi)[DK], bf16 (*lo)[DK], int r, float x0, float x1) {
@@ -471,8 +489,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
     if (exact) {
       // exact Gram and scores: every decay formed directly; entry (r, s)
-      // of both tiles per item, 256 items over the three waves
-      for (int idx = 64 * pw + lane; idx < KC * KC; idx += 192) {
+      // of both tiles per item, 256 items over the deriving waves
+      for (int idx = 64 * dw + lane; idx < KC * KC; idx += 64 * NDW) {
         const int r = idx / KC, s = idx % KC;
         float sa = 0.0f, sp = 0.0f;
         if (s <= r) {
@@ -534,12 +552,14 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (pw == 1 && it + 1 < nchunks) gsum(it + 1);
       if (it < nchunks) derive(it);
       wait_own(more);
-    } else {
+    } else if (pw == 2) {
       const bool more = it < nchunks;
       if (more) issue_v(it);
       if (it >= 1 && it - 1 < nchunks) scores(it - 1);
       if (it < nchunks) derive(it);
       wait_own(more);
+    } else if (it < nchunks) {
+      derive(it);
     }
     __syncthreads();
   }
@@ -548,7 +568,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 template <int DK, int DVS, typename OutT>
 hipError_t launch_kda(const ChunkArgs &a) {
   const int nslice = DK / DVS;
-  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + KNPW));
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
   hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT>), grid, block, 0, a.stream,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
                      a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
