@@ -171,14 +171,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int kk = 0; kk < KKD; ++kk) kq_off[kk] = qk_at(lr, 4 * kk + lg);
 
-  // byte offset of slot i of a rotating LDS buffer, as a wave-uniform value
-  // the compiler cannot strength-reduce: an LDS address in a loop is then
-  // one add of a scalar to a per-lane offset (the induction form took two)
-  auto slot = [](int i, int bytes) { return __builtin_amdgcn_readfirstlane(i * bytes); };
-  auto at = [](auto *base, int off) {
-    return reinterpret_cast<decltype(base)>(reinterpret_cast<char *>(base) + off);
-  };
-
   // the upper-right 16x16 blocks of P and T' are never written: zero once
   for (int i = tid; i < C * SM::LDC; i += NT) {
 #pragma unroll
@@ -253,7 +245,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       bf16x8 Uh, Ul, Wh, Wl;
       // ---- K S, Q S, R = V - diag(gam) K S, U = T' R ----
       if (s >= 0) {
-        const In &bs = *at(&sm.in[0], slot(s % NIN, (int)sizeof(In)));
+        const In &bs = *at_off(&sm.in[0], slot_off(s % NIN, (int)sizeof(In)));
         const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
         const char *Qb = reinterpret_cast<const char *>(&bs.Q[0][0]);
         const char *Vb = reinterpret_cast<const char *>(&bs.V[0][0]);
@@ -289,9 +281,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           split4(rr, rh2[rb], rl2[rb]);
         }
         const bf16x8 Rh = cat(rh2[0], rh2[1]), Rl = cat(rl2[0], rl2[1]);
-        const int tso = slot(s % NTS, (int)sizeof(sm.Th[0]));
-        const bf16(*Th)[SM::LDC] = at(&sm.Th[0][0], tso);
-        const bf16(*Tl)[SM::LDC] = at(&sm.Tl[0][0], tso);
+        const int tso = slot_off(s % NTS, (int)sizeof(sm.Th[0]));
+        const bf16(*Th)[SM::LDC] = at_off(&sm.Th[0][0], tso);
+        const bf16(*Tl)[SM::LDC] = at_off(&sm.Tl[0][0], tso);
         bf16x4 uh[2], ul[2], wh[2], wl[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -316,8 +308,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       }
       // ---- O = diag(gam) Q S + P U; S <- gam_last S + K^T U' ----
       if (s >= 0) {
-        const In &bs = *at(&sm.in[0], slot(s % NIN, (int)sizeof(In)));
-        const typename SM::PT &ps = *at(&sm.p[0], slot(s % NPR, (int)sizeof(typename SM::PT)));
+        const In &bs = *at_off(&sm.in[0], slot_off(s % NIN, (int)sizeof(In)));
+        const typename SM::PT &ps = *at_off(&sm.p[0], slot_off(s % NPR, (int)sizeof(typename SM::PT)));
         const int t0 = s * C, n = min(C, T - t0);
         const long orow = (tok0 + (long)t0 * H) * DV;   // element offset of the chunk's first row
         // the chunk's rows: smaller than 4 GiB (the host checks the shape)
@@ -423,9 +415,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int it = 0; it < nchunks + 1; ++it) {
       if (it < nchunks) {
         const int j = it;
-        const int tso = slot(j % NTS, (int)sizeof(sm.Th[0]));
-        const int ao = slot(j & 1, (int)sizeof(sm.ATd[0]));
-        const int a10o = slot(j & 1, (int)sizeof(sm.A10h[0]));
+        const int tso = slot_off(j % NTS, (int)sizeof(sm.Th[0]));
+        const int ao = slot_off(j & 1, (int)sizeof(sm.ATd[0]));
+        const int a10o = slot_off(j & 1, (int)sizeof(sm.A10h[0]));
         // diagonal 16x16 blocks (A tiles from the last iteration); lane =
         // (block, column); right-looking forward substitution: once x_s is
         // final it updates all later rows, so the dependent chain is one FMA
@@ -438,7 +430,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           float na[16];                          // na[r] = -A[o0 + r][o0 + col]
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(&(*at(&sm.ATd[0], ao))[blk][col][4 * q4]);
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(&(*at_off(&sm.ATd[0], ao))[blk][col][4 * q4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) na[4 * q4 + e] = t[e];
           }
@@ -459,9 +451,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             for (int r = 0; r < 16; r += 2) split2(x[r], x[r + 1], h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-              *reinterpret_cast<u32x4 *>(&at(&sm.Th[0][0], tso)[o0 + col][o0 + 8 * hf]) =
+              *reinterpret_cast<u32x4 *>(&at_off(&sm.Th[0][0], tso)[o0 + col][o0 + 8 * hf]) =
                   u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-              *reinterpret_cast<u32x4 *>(&at(&sm.Tl[0][0], tso)[o0 + col][o0 + 8 * hf]) =
+              *reinterpret_cast<u32x4 *>(&at_off(&sm.Tl[0][0], tso)[o0 + col][o0 + 8 * hf]) =
                   u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
             }
           }
@@ -470,12 +462,12 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         // block (1,0), T10 = -T11 A10 T00, from the diagonal blocks just
         // written: two 16x16x16 split products, the first result fed to the
         // second as its B operand straight from the accumulator
-        bf16(*Th)[SM::LDC] = at(&sm.Th[0][0], tso);
-        bf16(*Tl)[SM::LDC] = at(&sm.Tl[0][0], tso);
+        bf16(*Th)[SM::LDC] = at_off(&sm.Th[0][0], tso);
+        bf16(*Tl)[SM::LDC] = at_off(&sm.Tl[0][0], tso);
         // Y1 = A10 T00: A operand A10[m][4 lg ..] = column m of A10^T rows 4 lg..;
         // B operand T00[4 lg ..][n] = row n of T^T
-        const bf16x4 ah = ld_tr4(&at(&sm.A10h[0][0], a10o)[4 * lg + (lr >> 2)][4 * (lr & 3)]);
-        const bf16x4 al = ld_tr4(&at(&sm.A10l[0][0], a10o)[4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 ah = ld_tr4(&at_off(&sm.A10h[0][0], a10o)[4 * lg + (lr >> 2)][4 * (lr & 3)]);
+        const bf16x4 al = ld_tr4(&at_off(&sm.A10l[0][0], a10o)[4 * lg + (lr >> 2)][4 * (lr & 3)]);
         const bf16x4 bh = *reinterpret_cast<const bf16x4 *>(&Th[lr][4 * lg]);
         const bf16x4 bl = *reinterpret_cast<const bf16x4 *>(&Tl[lr][4 * lg]);
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
@@ -569,7 +561,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // diagonal A block, wave 1 the first diagonal A block and P11, wave 2 P10
   // and P00.
   auto tiles = [&](int j) {
-    In &bf = *at(&sm.in[0], slot(j % NIN, (int)sizeof(In)));
+    In &bf = *at_off(&sm.in[0], slot_off(j % NIN, (int)sizeof(In)));
     float *g = sm.gw[pw];
     const float la = SCALAR ? bf.la[lane] : 0.0f;
     const float sc = scan32_inclusive(la);
@@ -583,19 +575,19 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       }
     }
     wave_lds_sync();
-    typename SM::PT &pt = *at(&sm.p[0], slot(j % NPR, (int)sizeof(typename SM::PT)));
-    const int a10o = slot(j & 1, (int)sizeof(sm.A10h[0]));
-    const int ao = slot(j & 1, (int)sizeof(sm.ATd[0]));
+    typename SM::PT &pt = *at_off(&sm.p[0], slot_off(j % NPR, (int)sizeof(typename SM::PT)));
+    const int a10o = slot_off(j & 1, (int)sizeof(sm.A10h[0]));
+    const int ao = slot_off(j & 1, (int)sizeof(sm.ATd[0]));
     if (pw == 0) {
       const f32x4 val = decayed(bf, g, tile_acc(bf, false, 1, 0), 1, 0, false);
       bf16x4 h4, l4;
       split4(val, h4, l4);
-      *reinterpret_cast<bf16x4 *>(&at(&sm.A10h[0][0], a10o)[lr][4 * lg]) = h4;
-      *reinterpret_cast<bf16x4 *>(&at(&sm.A10l[0][0], a10o)[lr][4 * lg]) = l4;
-      *reinterpret_cast<f32x4 *>(&(*at(&sm.ATd[0], ao))[1][lr][4 * lg]) =
+      *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10h[0][0], a10o)[lr][4 * lg]) = h4;
+      *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10l[0][0], a10o)[lr][4 * lg]) = l4;
+      *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[1][lr][4 * lg]) =
           -decayed(bf, g, tile_acc(bf, false, 1, 1), 1, 1, false);
     } else if (pw == 1) {
-      *reinterpret_cast<f32x4 *>(&(*at(&sm.ATd[0], ao))[0][lr][4 * lg]) =
+      *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[0][lr][4 * lg]) =
           -decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
       store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
     } else {

@@ -106,6 +106,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                     (KC * QRB) % 1024 == 0 && (KC * VRB) % 1024 == 0,
                 "DMA runs are whole 1 KiB waves");
   __shared__ SM sm;
+  static_assert(sizeof(sm.Th[0]) == sizeof(sm.Ph[0]), "T' and P slots share one offset");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -185,7 +186,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;
       if (s >= 0) {
-        const typename SM::Der &d = sm.der[s % NDER];
+        const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));
+        const int t1 = slot_off(s & 1, (int)sizeof(sm.Th[0]));   // T' and P slots (same size)
         const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
         // ---- K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -207,15 +209,15 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           a2 = mfma_bf16(ql, Sh[kk], a2);
         }
         const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(
-            reinterpret_cast<const char *>(&sm.V[s % NVB][0][0]) + v_off));
+            reinterpret_cast<const char *>(&sm.V[0][0][0]) + slot_off(s % NVB, (int)sizeof(sm.V[0])) + v_off));
         f32x4 rr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - a1[e];
         bf16x4 rh4, rl4;
         split4(rr, rh4, rl4);
         // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
-        const bf16x8 ta = cat(ld_tr4(&sm.Th[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]),
-                              ld_tr4(&sm.Tl[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]));
+        const bf16x8 ta = cat(ld_tr4(&at_off(&sm.Th[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                              ld_tr4(&at_off(&sm.Tl[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]));
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         u = mfma_bf16(ta, cat(rh4, rh4), u);
         u = mfma_bf16(ta, cat(rl4, zero4), u);
@@ -224,8 +226,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
         // ---- O = Q^ S + P U ----
         const int t0 = s * KC, n = min(KC, T - t0);
-        const bf16x8 pa = cat(ld_tr4(&sm.Ph[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]),
-                              ld_tr4(&sm.Pl[s & 1][4 * lg + (lr >> 2)][4 * (lr & 3)]));
+        const bf16x8 pa = cat(ld_tr4(&at_off(&sm.Ph[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                              ld_tr4(&at_off(&sm.Pl[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]));
         f32x4 acc = a2;
         acc = mfma_bf16(pa, cat(uh4, uh4), acc);
         acc = mfma_bf16(pa, cat(ul4, zero4), acc);
@@ -299,7 +301,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int it = 0; it < nchunks + 2; ++it) {
       const int j = it - 1;
       if (j >= 0 && j < nchunks) {
-        const typename SM::Der &d = sm.der[j % NDER];
+        const typename SM::Der &d = *at_off(&sm.der[0], slot_off(j % NDER, (int)sizeof(typename SM::Der)));
+        const int t1 = slot_off(j & 1, (int)sizeof(sm.Th[0]));
         const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
         const float(*src)[SM::LDX] = sm.At;
         if (!exact) {
@@ -311,7 +314,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           *reinterpret_cast<f32x4 *>(&sm.At[lr][4 * lg]) = val;   // [s][r] = -A[r][s]
           wave_lds_sync();
         } else {
-          src = sm.xA[j & 1];
+          src = at_off(&sm.xA[0][0], slot_off(j & 1, (int)sizeof(sm.xA[0])));
         }
         // right-looking forward substitution, lane = column col (each
         // 16-lane row holds all columns); lane col keeps column col of -A
@@ -344,8 +347,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             split2(x[r] * bcol, x[r + 1] * bcol, h8[r / 8][(r % 8) / 2], l8[r / 8][(r % 8) / 2]);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            *reinterpret_cast<u32x4 *>(&sm.Th[j & 1][col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
-            *reinterpret_cast<u32x4 *>(&sm.Tl[j & 1][col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&at_off(&sm.Th[0][0], t1)[col][8 * hf]) = u32x4{h8[hf][0], h8[hf][1], h8[hf][2], h8[hf][3]};
+            *reinterpret_cast<u32x4 *>(&at_off(&sm.Tl[0][0], t1)[col][8 * hf]) = u32x4{l8[hf][0], l8[hf][1], l8[hf][2], l8[hf][3]};
           }
         }
       }
@@ -422,7 +425,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // channel pair; padded tokens read log a = 0; flags a chunk whose
   // factored operands could leave the floating-point range
   auto gsum = [&](int j) {
-    typename SM::Raw &rw = sm.raw[j % NRAW];
+    typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
     constexpr int NCP = DK / 2;
     const int c0 = 2 * (lane % NCP);
     f32x2 acc = {0.f, 0.f};
@@ -454,8 +457,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   };
   auto derive = [&](int j) {
-    const typename SM::Raw &rw = sm.raw[j % NRAW];
-    typename SM::Der &d = sm.der[j % NDER];
+    const typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
+    typename SM::Der &d = *at_off(&sm.der[0], slot_off(j % NDER, (int)sizeof(typename SM::Der)));
     const int exact = __builtin_amdgcn_readfirstlane(rw.flag[0]);
     const int cp = lane % NCP, c0 = 2 * cp;
     const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
@@ -500,7 +503,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             sp += (float)rw.Q[r][c] * ks;
           }
         }
-        sm.xA[j & 1][s][r] = (s < r) ? -rw.beta[r] * sa : 0.0f;
+        sm.xA[j & 1][s][r] = (s < r) ? -rw.beta[r] * sa : 0.0f;   // exact path only: rare
         sm.xP[j & 1][s][r] = sp;
       }
     }
@@ -508,7 +511,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // P of chunk j (lower incl.), split hi/lo, transposed (wave 2)
   auto scores = [&](int j) {
-    const typename SM::Der &d = sm.der[j % NDER];
+    const typename SM::Der &d = *at_off(&sm.der[0], slot_off(j % NDER, (int)sizeof(typename SM::Der)));
+    const int t1 = slot_off(j & 1, (int)sizeof(sm.Ph[0]));
     const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
     f32x4 val;
     if (!exact) {
@@ -520,8 +524,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
     bf16x4 h4, l4;
     split4(val, h4, l4);
-    *reinterpret_cast<bf16x4 *>(&sm.Ph[j & 1][lr][4 * lg]) = h4;
-    *reinterpret_cast<bf16x4 *>(&sm.Pl[j & 1][lr][4 * lg]) = l4;
+    *reinterpret_cast<bf16x4 *>(&at_off(&sm.Ph[0][0], t1)[lr][4 * lg]) = h4;
+    *reinterpret_cast<bf16x4 *>(&at_off(&sm.Pl[0][0], t1)[lr][4 * lg]) = l4;
   };
 
   auto wait_own = [&](bool newer_issued) {

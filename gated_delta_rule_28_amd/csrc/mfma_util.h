@@ -42,6 +42,21 @@ __device__ __forceinline__ int swz_v(int r) {
   else return 2 * ((r >> 2) & 1);
 }
 
+// Byte offset of slot i of a rotating LDS buffer, as a wave-uniform value
+// the compiler cannot strength-reduce: an LDS address in a loop is then one
+// add of a scalar to a per-lane offset (the induction form takes two).
+__device__ __forceinline__ int slot_off(int i, int bytes) {
+  return __builtin_amdgcn_readfirstlane(i * bytes);
+}
+template <typename T>
+__device__ __forceinline__ T *at_off(T *p, int bytes) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(p) + bytes);
+}
+template <typename T>
+__device__ __forceinline__ const T *at_off(const T *p, int bytes) {
+  return reinterpret_cast<const T *>(reinterpret_cast<const char *>(p) + bytes);
+}
+
 // Makes this wave's earlier LDS writes visible to its later LDS reads of
 // other lanes' data (LDS serves one wave's accesses in order; the fences
 // keep the compiler from moving accesses across).
