@@ -22,13 +22,6 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
-// Split an fp32 value into bf16 hi + lo with x ~= hi + lo to ~16 bits.
-// x - float(hi) is exact in fp32, so only the rounding of lo is lost.
-__device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {
-  hi = (bf16)x;
-  lo = (bf16)(x - (float)hi);
-}
-
 // D += A(16x32) * B(32x16), bf16 operands, fp32 accumulate.  Lane l holds
 // A row (l & 15) and B column (l & 15), eight k values per lane (the same k
 // set for A and B, so any consistent k order gives the same product); the

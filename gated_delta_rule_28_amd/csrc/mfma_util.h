@@ -5,14 +5,6 @@
 
 namespace gdr {
 
-// k order inside each 32-wide block: natural index 32kk + 16h + 4g + j lives
-// at 32kk + 8g + 4h + j, so one 16-byte LDS read returns the eight k values a
-// lane needs for an operand that pairs with accumulator rows 4g..4g+3 of two
-// adjacent 16-row tiles.
-__device__ __forceinline__ int perm32(int c) {
-  return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
-}
-
 __device__ __forceinline__ bf16x8 ld8(const bf16 *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
@@ -137,25 +129,11 @@ __device__ __forceinline__ bf16x4 ld_tr4(const bf16 *p) {
 // scalar offset stays 0 so the bounds check sees the whole offset.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, long bytes) {
-  const long b = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFL ? 0xFFFFFFFFL : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(unsigned)b,
-                                           0x00020000);
-}
 // Descriptor of a range known to be shorter than 4 GiB (no clamp: a 64-bit
 // clamp compiles to VALU compares that the scalar code then waits for).
 __device__ __forceinline__ rsrc_t make_rsrc32(const void *base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
-}
-__device__ __forceinline__ bf16x8 buf_ld8(rsrc_t r, int off) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ f32x4 buf_ld4f(rsrc_t r, int off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ float buf_ld1f(rsrc_t r, int off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 __device__ __forceinline__ void buf_st1(float x, rsrc_t r, int off) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);
@@ -232,50 +210,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
-__device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6], x[7]}; }
-
-// acc += L (16x16, fp32, row-major at L[m*ldl + k]) * R (16x16, fp32, given
-// transposed: R[k][n] = RT[n*ldr + k]) to ~fp32 accuracy with two MFMAs: the
-// 32-deep k axis carries [L_hi | L_lo] against [R_hi ; R_hi], then
-// [L_hi | L_lo] against [R_lo ; 0].
-__device__ __forceinline__ f32x4 mm16_split(const float *L, int ldl, const float *RT, int ldr,
-                                            f32x4 acc, int lane) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const int m = lane & 15, g = lane >> 4, k0 = 8 * (g & 1);
-  u32x4 a, b1, b2;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    unsigned lh, ll, rh, rl;
-    split2(L[m * ldl + k0 + 2 * j], L[m * ldl + k0 + 2 * j + 1], lh, ll);
-    split2(RT[m * ldr + k0 + 2 * j], RT[m * ldr + k0 + 2 * j + 1], rh, rl);
-    a[j] = g < 2 ? lh : ll;
-    b1[j] = rh;
-    b2[j] = g < 2 ? rl : 0u;
-  }
-  acc = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b1), acc);
-  return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b2), acc);
-}
-
-// The same product with L given transposed: L[m][k] = LT[k*ldl + m].
-__device__ __forceinline__ f32x4 mm16_split_lt(const float *LT, int ldl, const float *RT, int ldr,
-                                               f32x4 acc, int lane) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const int m = lane & 15, g = lane >> 4, k0 = 8 * (g & 1);
-  u32x4 a, b1, b2;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    unsigned lh, ll, rh, rl;
-    split2(LT[(k0 + 2 * j) * ldl + m], LT[(k0 + 2 * j + 1) * ldl + m], lh, ll);
-    split2(RT[m * ldr + k0 + 2 * j], RT[m * ldr + k0 + 2 * j + 1], rh, rl);
-    a[j] = g < 2 ? lh : ll;
-    b1[j] = rh;
-    b2[j] = g < 2 ? rl : 0u;
-  }
-  acc = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b1), acc);
-  return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b2), acc);
 }
 
 }  // namespace gdr
