@@ -38,9 +38,10 @@
 //   wave 0: LDS DMA of log a and b of chunk i+3; derives chunk i (a share)
 //   wave 1: LDS DMA of q, k of chunk i+3; sums the log decays of chunk i+1;
 //           derives chunk i (a share)
-//   wave 2: LDS DMA of v of chunk i; scores of chunk i-1; derives chunk i
+//   wave 2: scores of chunk i-1; derives chunk i (a share)
 //   wave 3: Gram and solve of chunk i-1
 //   waves 4, 5 (32-column slices): derive chunk i (shares)
+//   LDS DMA of v of chunk i: wave 5, or wave 2 with four prep waves
 //   state:  chunk i-2
 // Raw inputs live four iterations (DMA to derivation), derived operands
 // three, v three, T' and P two.
@@ -277,6 +278,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // prep waves
   // =======================================================================
   const int pw = wave - NSW;
+  // v is loaded by a wave that only derives when there is one
+  constexpr int PW_V = (kda_npw<DVS>() == 6) ? 5 : 2;
 
   // 16x16 tile L R^T of derived operands (hi/lo both sides, three
   // independent MFMA chains); lane holds rows 4 lg + e of column lr
@@ -556,14 +559,12 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (pw == 1 && it + 1 < nchunks) gsum(it + 1);
       if (it < nchunks) derive(it);
       wait_own(more);
-    } else if (pw == 2) {
+    } else {
       const bool more = it < nchunks;
-      if (more) issue_v(it);
-      if (it >= 1 && it - 1 < nchunks) scores(it - 1);
+      if (pw == PW_V && more) issue_v(it);
+      if (pw == 2 && it >= 1 && it - 1 < nchunks) scores(it - 1);
       if (it < nchunks) derive(it);
-      wait_own(more);
-    } else if (it < nchunks) {
-      derive(it);
+      if (pw == PW_V) wait_own(more);
     }
     __syncthreads();
   }
