@@ -289,6 +289,22 @@ def test_chunk_kda_decay_range(alpha_mu, alpha_sigma):
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
+@pytest.mark.parametrize("D,B,H", [(128, 8, 16), (64, 2, 3), (64, 4, 64)])
+def test_chunk_kda_exact_path_configs(D, B, H):
+    # strong per-channel decay (some chunks take the exact in-chunk path) in
+    # the other launch configurations: 64-column slices with four prep waves
+    # (128 chains at d = 128, 256 at d = 64) and d = 64 with 32-column slices
+    say("chunk kda exact path", D, B, H)
+    inp = with_state(W.make_chunk_inputs(B, 70, H, D, D, "channel", "bf16", seed=13 + D,
+                                         device=DEV, alpha_mu=3.0, alpha_sigma=2.5))
+    o, S = run_chunk(inp)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    o_ref, S_ref = oracle_on(inp)
+    eo, es = rel_err(np64(o), o_ref), rel_err(np64(S), S_ref)
+    say("max|err|/rms o", eo, "state", es)
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
 def test_chunk_kda_many_chains():
     # 128 chains: the 64-column slice configuration
     say("chunk kda many chains")
