@@ -85,8 +85,10 @@ const char *gdr_status_str(int status);
  *                other combinations return GDR_EUNSUPPORTED).  With bf16
  *                q/k/v, no gate or the scalar gate and Dk = 128, H * Dk must
  *                stay below 34,000,000 (the kernel addresses one chunk's rows
- *                of a tensor with 32-bit offsets); larger shapes return
- *                GDR_EUNSUPPORTED (at Dk = 64 they take the fp32 kernel)
+ *                of a tensor with 32-bit offsets); with the per-channel
+ *                gate the bound is 71,000,000 (the fp32 log decays of one
+ *                16-token chunk).  Larger shapes return GDR_EUNSUPPORTED (at
+ *                Dk = 64 they take the fp32 kernel)
  *   chunk        tokens per chunk: 0 = default, else 16, 32 or 64
  *   in_dtype     dtype of q, k, v (GDR_BF16 or GDR_F32)
  *   out_dtype    dtype of o (GDR_F32 or GDR_BF16)

@@ -84,6 +84,8 @@ def step(**kw):
     (dict(gate=_abi.GDR_GATE_CHANNEL, in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
     # one chunk's rows of a [*, H, 128] tensor must span less than 4 GiB
     (dict(H=300000), _abi.GDR_EUNSUPPORTED),
+    # per-channel gate: one chunk's rows of the [*, H, 128] fp32 log decays
+    (dict(H=600000, gate=_abi.GDR_GATE_CHANNEL), _abi.GDR_EUNSUPPORTED),
     # per-channel log decays are read with 16-byte vectors
     (dict(gate=_abi.GDR_GATE_CHANNEL, log_alpha=FAKE + 4), _abi.GDR_EINVAL),
 ])
