@@ -9,6 +9,8 @@ All arithmetic runs in the HIP kernels.
 
 Gate kind follows log_alpha: None -> DeltaNet (alpha = 1); [B, T, H] ->
 Gated DeltaNet (one decay per head); [B, T, H, Dk] -> KDA (one per channel).
+erase=False drops the erase term (S = alpha S + beta k v^T): linear
+attention, the Mamba-2 / SSD decay and GLA's, through the same kernels.
 """
 
 import torch
@@ -57,7 +59,8 @@ def _stream(device):
 
 
 def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
-              out_dtype=torch.float32, output_final_state=True, o=None, final_state=None):
+              out_dtype=torch.float32, output_final_state=True, o=None, final_state=None,
+              erase=True):
     """Chunkwise forward over whole sequences.
 
     q, k [B, T, H, Dk] and v [B, T, H, Dv] (bf16 or fp32, same dtype);
@@ -79,7 +82,7 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
     Dv = v.shape[3]
     if tuple(beta.shape) != (B, T, H):
         raise ValueError("beta must be [B, T, H]")
-    gate = _gate_of(log_alpha, (B, T, H), Dk)
+    gate = _gate_of(log_alpha, (B, T, H), Dk) | (0 if erase else _abi.GDR_NO_ERASE)
     if log_alpha is not None:
         _check_dev("log_alpha", log_alpha, torch.float32)
     if initial_state is not None:
@@ -109,7 +112,8 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
     return o, final_state
 
 
-def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None):
+def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None,
+                   erase=True):
     """One decode token for N sequences; `state` [N, H, Dk, Dv] fp32 is
     updated in place.  q, k [N, H, Dk]; v [N, H, Dv]; beta [N, H];
     log_alpha None | [N, H] | [N, H, Dk].  Returns o [N, H, Dv]."""
@@ -126,7 +130,7 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
     Dv = v.shape[2]
     if tuple(beta.shape) != (N, H) or tuple(state.shape) != (N, H, Dk, Dv):
         raise ValueError("beta must be [N, H] and state [N, H, Dk, Dv]")
-    gate = _gate_of(log_alpha, (N, H), Dk)
+    gate = _gate_of(log_alpha, (N, H), Dk) | (0 if erase else _abi.GDR_NO_ERASE)
     if log_alpha is not None:
         _check_dev("log_alpha", log_alpha, torch.float32)
     if o is None:

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EHIP = 0, -1, -2, -3
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_NONE, GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1, 2
+GDR_NO_ERASE = 0x100   # OR'd into a gate: additive write, no erase term
 
 # every function the header declares, with its ctypes signature
 _c_int, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t

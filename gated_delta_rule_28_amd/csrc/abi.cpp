@@ -15,7 +15,12 @@ bool aligned(const void *p, unsigned bytes) {
 }
 
 bool valid_dtype(int d) { return d == GDR_F32 || d == GDR_BF16; }
-bool valid_gate(int g) { return g == GDR_GATE_NONE || g == GDR_GATE_SCALAR || g == GDR_GATE_CHANNEL; }
+bool valid_gate(int g) {
+  const int base = g & ~GDR_NO_ERASE;
+  return base == GDR_GATE_NONE || base == GDR_GATE_SCALAR || base == GDR_GATE_CHANNEL;
+}
+int gate_kind(int g) { return g & ~GDR_NO_ERASE; }
+bool erases(int g) { return (g & GDR_NO_ERASE) == 0; }
 bool supported_head(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // gate/log_alpha consistency and common pointer checks for both entry points
@@ -23,7 +28,7 @@ int check_common(int Dk, int Dv, int in_dtype, int out_dtype, int gate, const vo
                  const void *k, const void *v, const float *beta, const float *log_alpha,
                  const void *o) {
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate)) return GDR_EINVAL;
-  if ((gate == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
+  if ((gate_kind(gate) == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
   if (!q || !k || !v || !beta || !o) return GDR_EINVAL;
   // q/k/v/o are accessed with 16-byte vectors; beta/log_alpha are scalars
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned(beta, 4) ||
@@ -71,12 +76,13 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   int st = check_common(Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, log_alpha, o);
   if (st != GDR_OK) return st;
   // per-channel log decays are read as rows of Dk floats with 16-byte vectors
-  if (gate == GDR_GATE_CHANNEL && !aligned16(log_alpha)) return GDR_EINVAL;
+  if (gate_kind(gate) == GDR_GATE_CHANNEL && !aligned16(log_alpha)) return GDR_EINVAL;
 
   gdr::ChunkArgs a;
   a.B = B; a.T = T; a.H = H; a.D = Dk; a.chunk = chunk;
   a.in_bf16 = in_dtype == GDR_BF16; a.out_bf16 = out_dtype == GDR_BF16;
-  a.gate = gate;
+  a.gate = gate_kind(gate);
+  a.erase = erases(gate);
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
   a.initial_state = initial_state; a.o = o; a.final_state = final_state;
   a.stream = stream;
@@ -100,7 +106,8 @@ int gdr_recurrent_step(int N, int H, int Dk, int Dv, int in_dtype, int out_dtype
   gdr::RecurrentArgs a;
   a.N = N; a.H = H; a.D = Dk;
   a.in_bf16 = in_dtype == GDR_BF16; a.out_bf16 = out_dtype == GDR_BF16;
-  a.gate = gate;
+  a.gate = gate_kind(gate);
+  a.erase = erases(gate);
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
   a.state = state; a.o = o; a.stream = stream;
   hipError_t e = gdr::launch_recurrent_step(a);

@@ -16,6 +16,11 @@
 //   O   = diag(gam) Q S + P U                          outputs
 //   S  <- gam_last S + K^T diag(e^{g_last - g}) U      carried state
 //
+// Without the erase term (S_t = a_t S_{t-1} + b_t k_t v_t^T: linear attention
+// and the Mamba-2 / SSD decay, page "NLP——线性注意力相关总结", section "Linear
+// Attention"; xhh.club digest, abstract) A = 0, so U = diag(b) V: the same
+// kernel skips K S, the A tiles and the solve (template flag ERASE).
+//
 // Mapping.  One workgroup per (batch, head, Dv-slice of DVS columns): the Dv
 // columns of S, U and O are independent given K, b and g.  Chunks are C = 32
 // tokens.  Roles:
@@ -119,7 +124,7 @@ struct __align__(16) PipeSmem {
   float gw[3][C];                      // in-chunk log decay g, one copy per tile wave
 };
 
-template <int DK, int DVS, typename OutT, int GATE>
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
 __global__ void __launch_bounds__(64 * (DVS / 16 + NPW), 1)
 chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ v, const float *__restrict__ beta,
@@ -255,17 +260,23 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KKD; ++kk) {
-            const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
             const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
-            a1 = mfma_bf16(ak, Sh[kk], a1);
-            a2 = mfma_bf16(aq, Sh[kk], a2);
-            a1 = mfma_bf16(ak, Sl[kk], a1);
-            a2 = mfma_bf16(aq, Sl[kk], a2);
+            if constexpr (ERASE) {
+              const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
+              a1 = mfma_bf16(ak, Sh[kk], a1);
+              a2 = mfma_bf16(aq, Sh[kk], a2);
+              a1 = mfma_bf16(ak, Sl[kk], a1);
+              a2 = mfma_bf16(aq, Sl[kk], a2);
+            } else {
+              a2 = mfma_bf16(aq, Sh[kk], a2);
+              a2 = mfma_bf16(aq, Sl[kk], a2);
+            }
           }
           KS[rb] = a1;
           QS[rb] = a2;
         }
         bf16x4 rh2[2], rl2[2];
+        f32x4 rv[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const int r0 = 16 * rb + 4 * lg;
@@ -274,32 +285,46 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                                 : *reinterpret_cast<const f32x4 *>(&bs.gam[r0]);
           const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.beta[r0]);
-          // b o R: T' R = T diag(b) R with T kept unscaled
+          // b o R: T' R = T diag(b) R with T kept unscaled; without the
+          // erase term R = V and U = b o V
           f32x4 rr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rr[e] = ((float)vv[e] - gm4[e] * KS[rb][e]) * b4[e];
+          for (int e = 0; e < 4; ++e)
+            rr[e] = (ERASE ? (float)vv[e] - gm4[e] * KS[rb][e] : (float)vv[e]) * b4[e];
+          rv[rb] = rr;
           split4(rr, rh2[rb], rl2[rb]);
         }
         const bf16x8 Rh = cat(rh2[0], rh2[1]), Rl = cat(rl2[0], rl2[1]);
-        const int tso = slot_off(s % NTS, (int)sizeof(sm.Th[0]));
-        const bf16(*Th)[SM::LDC] = at_off(&sm.Th[0][0], tso);
-        const bf16(*Tl)[SM::LDC] = at_off(&sm.Tl[0][0], tso);
         bf16x4 uh[2], ul[2], wh[2], wl[2];
+        if constexpr (!ERASE) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          // row 16 rb + lr of T, slots = tokens 16 h + 4 lg + c (the R rows)
-          const bf16x8 th = cat(ld_tr4(&Th[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
-                                ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
-          const bf16x8 tl = cat(ld_tr4(&Tl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
-                                ld_tr4(&Tl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
-          f32x4 u = {0.f, 0.f, 0.f, 0.f};
-          u = mfma_bf16(th, Rh, u);
-          u = mfma_bf16(tl, Rh, u);
-          u = mfma_bf16(th, Rl, u);
-          split4(u, uh[rb], ul[rb]);
-          const f32x4 ec4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
-                                                : *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
-          split4(u * ec4, wh[rb], wl[rb]);
+          for (int rb = 0; rb < 2; ++rb) {
+            uh[rb] = rh2[rb];
+            ul[rb] = rl2[rb];
+            const f32x4 ec4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                                  : *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
+            split4(rv[rb] * ec4, wh[rb], wl[rb]);
+          }
+        } else {
+          const int tso = slot_off(s % NTS, (int)sizeof(sm.Th[0]));
+          const bf16(*Th)[SM::LDC] = at_off(&sm.Th[0][0], tso);
+          const bf16(*Tl)[SM::LDC] = at_off(&sm.Tl[0][0], tso);
+  #pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            // row 16 rb + lr of T, slots = tokens 16 h + 4 lg + c (the R rows)
+            const bf16x8 th = cat(ld_tr4(&Th[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                  ld_tr4(&Th[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+            const bf16x8 tl = cat(ld_tr4(&Tl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
+                                  ld_tr4(&Tl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            u = mfma_bf16(th, Rh, u);
+            u = mfma_bf16(tl, Rh, u);
+            u = mfma_bf16(th, Rl, u);
+            split4(u, uh[rb], ul[rb]);
+            const f32x4 ec4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                                  : *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
+            split4(u * ec4, wh[rb], wl[rb]);
+          }
         }
         Uh = cat(uh[0], uh[1]);
         Ul = cat(ul[0], ul[1]);
@@ -413,7 +438,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     __syncthreads();
     __syncthreads();
     for (int it = 0; it < nchunks + 1; ++it) {
-      if (it < nchunks) {
+      if (ERASE && it < nchunks) {   // no solve without the erase term
         const int j = it;
         const int tso = slot_off(j % NTS, (int)sizeof(sm.Th[0]));
         const int ao = slot_off(j & 1, (int)sizeof(sm.ATd[0]));
@@ -579,6 +604,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int a10o = slot_off(j & 1, (int)sizeof(sm.A10h[0]));
     const int ao = slot_off(j & 1, (int)sizeof(sm.ATd[0]));
     if (pw == 0) {
+      if constexpr (!ERASE) return;                  // no A without the erase term
       const f32x4 val = decayed(bf, g, tile_acc(bf, false, 1, 0), 1, 0, false);
       bf16x4 h4, l4;
       split4(val, h4, l4);
@@ -587,8 +613,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[1][lr][4 * lg]) =
           -decayed(bf, g, tile_acc(bf, false, 1, 1), 1, 1, false);
     } else if (pw == 1) {
-      *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[0][lr][4 * lg]) =
-          -decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
+      if constexpr (ERASE)
+        *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[0][lr][4 * lg]) =
+            -decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
       store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
     } else {
       store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
@@ -617,11 +644,11 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 }
 
-template <int DK, int DVS, typename OutT, int GATE>
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
 hipError_t launch_cfg(const ChunkArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE, ERASE>), grid, block, 0, a.stream,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
                      a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
   return hipGetLastError();
@@ -629,8 +656,12 @@ hipError_t launch_cfg(const ChunkArgs &a) {
 
 template <int DK, int DVS, typename OutT>
 hipError_t by_gate(const ChunkArgs &a) {
-  if (a.gate == kGateNone) return launch_cfg<DK, DVS, OutT, kGateNone>(a);
-  return launch_cfg<DK, DVS, OutT, kGateScalar>(a);
+  if (a.erase) {
+    if (a.gate == kGateNone) return launch_cfg<DK, DVS, OutT, kGateNone, true>(a);
+    return launch_cfg<DK, DVS, OutT, kGateScalar, true>(a);
+  }
+  if (a.gate == kGateNone) return launch_cfg<DK, DVS, OutT, kGateNone, false>(a);
+  return launch_cfg<DK, DVS, OutT, kGateScalar, false>(a);
 }
 
 template <int DK, int DVS>

@@ -29,6 +29,11 @@
 // Derived operands are not exact bf16, so every product takes three MFMAs
 // (hi*hi + hi*lo + lo*hi).
 //
+// Without the erase term (S_t = Diag(a_t) S_{t-1} + b_t k_t v_t^T, GLA's
+// per-channel decay; xhh.club digest, abstract and Q&A) A = 0 and
+// U = diag(b) V: the same kernel skips K^, K^ S, the Gram and the solve
+// (template flag ERASE).
+//
 // Mapping.  One workgroup per (batch, head, Dv slice of DVS columns); DVS/16
 // state waves keep the state in MFMA accumulators with the k axis ordered as
 // in the scalar-gate kernel (tile pair (2kk, 2kk+1) holds dk 32kk + 8g + j and
@@ -88,7 +93,7 @@ struct __align__(16) KdaSmem {
   float At[KC][LDX];                      // -A^T of the chunk being solved
 };
 
-template <int DK, int DVS, typename OutT>
+template <int DK, int DVS, typename OutT, bool ERASE>
 __global__ void __launch_bounds__(64 * (DVS / 16 + kda_npw<DVS>()), 1)
 chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ beta,
@@ -198,32 +203,46 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const char *Ql = reinterpret_cast<const char *>(&d.Ql[0][0]);
 #pragma unroll
         for (int kk = 0; kk < KKD; ++kk) {
-          const bf16x8 kh = ld8(reinterpret_cast<const bf16 *>(Kh + kq_off[kk]));
           const bf16x8 qh = ld8(reinterpret_cast<const bf16 *>(Qh + kq_off[kk]));
-          const bf16x8 kl = ld8(reinterpret_cast<const bf16 *>(Kl + kq_off[kk]));
           const bf16x8 ql = ld8(reinterpret_cast<const bf16 *>(Ql + kq_off[kk]));
-          a1 = mfma_bf16(kh, Sh[kk], a1);
-          a2 = mfma_bf16(qh, Sh[kk], a2);
-          a1 = mfma_bf16(kh, Sl[kk], a1);
-          a2 = mfma_bf16(qh, Sl[kk], a2);
-          a1 = mfma_bf16(kl, Sh[kk], a1);
-          a2 = mfma_bf16(ql, Sh[kk], a2);
+          if constexpr (ERASE) {
+            const bf16x8 kh = ld8(reinterpret_cast<const bf16 *>(Kh + kq_off[kk]));
+            const bf16x8 kl = ld8(reinterpret_cast<const bf16 *>(Kl + kq_off[kk]));
+            a1 = mfma_bf16(kh, Sh[kk], a1);
+            a2 = mfma_bf16(qh, Sh[kk], a2);
+            a1 = mfma_bf16(kh, Sl[kk], a1);
+            a2 = mfma_bf16(qh, Sl[kk], a2);
+            a1 = mfma_bf16(kl, Sh[kk], a1);
+            a2 = mfma_bf16(ql, Sh[kk], a2);
+          } else {
+            a2 = mfma_bf16(qh, Sh[kk], a2);
+            a2 = mfma_bf16(qh, Sl[kk], a2);
+            a2 = mfma_bf16(ql, Sh[kk], a2);
+          }
         }
         const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(
             reinterpret_cast<const char *>(&sm.V[0][0][0]) + slot_off(s % NVB, (int)sizeof(sm.V[0])) + v_off));
         f32x4 rr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - a1[e];
-        bf16x4 rh4, rl4;
-        split4(rr, rh4, rl4);
-        // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
-        const bf16x8 ta = cat(ld_tr4(&at_off(&sm.Th[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]),
-                              ld_tr4(&at_off(&sm.Tl[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]));
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        u = mfma_bf16(ta, cat(rh4, rh4), u);
-        u = mfma_bf16(ta, cat(rl4, zero4), u);
         bf16x4 uh4, ul4;
-        split4(u, uh4, ul4);
+        if constexpr (ERASE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[e] = (float)vv[e] - a1[e];
+          bf16x4 rh4, rl4;
+          split4(rr, rh4, rl4);
+          // [T'h | T'l] against [Rh ; Rh] and [Rl ; 0]: slots (half, c) <-> token 4 lg + c
+          const bf16x8 ta = cat(ld_tr4(&at_off(&sm.Th[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]),
+                                ld_tr4(&at_off(&sm.Tl[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]));
+          f32x4 u = {0.f, 0.f, 0.f, 0.f};
+          u = mfma_bf16(ta, cat(rh4, rh4), u);
+          u = mfma_bf16(ta, cat(rl4, zero4), u);
+          split4(u, uh4, ul4);
+        } else {
+          // no erase term: U = diag(b) V
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&d.beta[4 * lg]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[e] = b4[e] * (float)vv[e];
+          split4(rr, uh4, ul4);
+        }
 
         // ---- O = Q^ S + P U ----
         const int t0 = s * KC, n = min(KC, T - t0);
@@ -303,7 +322,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     __syncthreads();
     for (int it = 0; it < nchunks + 2; ++it) {
       const int j = it - 1;
-      if (j >= 0 && j < nchunks) {
+      if (ERASE && j >= 0 && j < nchunks) {   // no solve without the erase term
         const typename SM::Der &d = *at_off(&sm.der[0], slot_off(j % NDER, (int)sizeof(typename SM::Der)));
         const int t1 = slot_off(j & 1, (int)sizeof(sm.Th[0]));
         const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
@@ -489,7 +508,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const float q0 = __builtin_bit_cast(float, qb << 16), q1 = __builtin_bit_cast(float, qb & 0xffff0000u);
       const float e0 = __expf(g[0]), e1 = __expf(g[1]);
       const float f0 = __expf(sh[0] - g[0]), f1 = __expf(sh[1] - g[1]);
-      put(d.Kh, d.Kl, r, k0 * e0, k1 * e1);
+      if constexpr (ERASE) put(d.Kh, d.Kl, r, k0 * e0, k1 * e1);   // K^ feeds only K^ S and A
       put(d.Qh, d.Ql, r, q0 * e0, q1 * e1);
       put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);
     }
@@ -506,7 +525,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             sp += (float)rw.Q[r][c] * ks;
           }
         }
-        sm.xA[j & 1][s][r] = (s < r) ? -rw.beta[r] * sa : 0.0f;   // exact path only: rare
+        if constexpr (ERASE) sm.xA[j & 1][s][r] = (s < r) ? -rw.beta[r] * sa : 0.0f;
         sm.xP[j & 1][s][r] = sp;
       }
     }
@@ -570,11 +589,11 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 }
 
-template <int DK, int DVS, typename OutT>
+template <int DK, int DVS, typename OutT, bool ERASE>
 hipError_t launch_kda(const ChunkArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
-  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT, ERASE>), grid, block, 0, a.stream,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
                      a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
   return hipGetLastError();
@@ -582,7 +601,8 @@ hipError_t launch_kda(const ChunkArgs &a) {
 
 template <int DK, int DVS>
 hipError_t kda_by_out(const ChunkArgs &a) {
-  return a.out_bf16 ? launch_kda<DK, DVS, bf16>(a) : launch_kda<DK, DVS, float>(a);
+  if (a.erase) return a.out_bf16 ? launch_kda<DK, DVS, bf16, true>(a) : launch_kda<DK, DVS, float, true>(a);
+  return a.out_bf16 ? launch_kda<DK, DVS, bf16, false>(a) : launch_kda<DK, DVS, float, false>(a);
 }
 
 }  // namespace

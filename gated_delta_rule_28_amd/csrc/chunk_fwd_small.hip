@@ -47,7 +47,7 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
                        const void *__restrict__ v, const float *__restrict__ beta,
                        const float *__restrict__ log_alpha, const float *initial_state,
                        void *__restrict__ o, float *final_state, int B, int T, int H,
-                       bool in_bf16, bool out_bf16) {
+                       bool in_bf16, bool out_bf16, bool erase) {
   constexpr int NT = 256;
   __shared__ SmemSmall<D, C> sm;
   const int tid = threadIdx.x;
@@ -102,14 +102,15 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
           p += sm.Q[r][c] * ks;
         }
       }
-      sm.A[r][s] = (s < r) ? sm.beta[r] * a : 0.0f;
+      // without the erase term A = 0: the solve below leaves U = diag(b) V
+      sm.A[r][s] = (erase && s < r) ? sm.beta[r] * a : 0.0f;
       sm.P[r][s] = p;
     }
-    // R = V - (K o e^G) S
+    // R = V - (K o e^G) S (R = V without the erase term)
     for (int i = tid; i < C * D; i += NT) {
       const int r = i / D, c = i % D;
       float acc = 0.f;
-      for (int m = 0; m < D; ++m) {
+      for (int m = 0; erase && m < D; ++m) {
         const float x = (GATE == kGateNone) ? sm.K[r][m] : sm.K[r][m] * __expf(sm.G[r][m]);
         acc += x * sm.S[m][c];
       }
@@ -165,7 +166,7 @@ hipError_t by_gate(const ChunkArgs &a) {
 #define GDR_LAUNCH(G)                                                                          \
   hipLaunchKernelGGL((chunk_fwd_small_kernel<D, C, G>), grid, block, 0, a.stream, a.q, a.k,  \
                      a.v, a.beta, a.log_alpha, a.initial_state, a.o, a.final_state, a.B, a.T, \
-                     a.H, a.in_bf16, a.out_bf16)
+                     a.H, a.in_bf16, a.out_bf16, a.erase)
   if (a.gate == kGateNone) GDR_LAUNCH(kGateNone);
   else if (a.gate == kGateScalar) GDR_LAUNCH(kGateScalar);
   else GDR_LAUNCH(kGateChannel);

@@ -10,6 +10,7 @@ struct RecurrentArgs {
   int N, H, D;            // D = Dk = Dv
   bool in_bf16, out_bf16;
   int gate;               // 0 none, 1 scalar, 2 channel
+  bool erase;             // false: additive write, no erase term
   const void *q, *k, *v;
   const float *beta, *log_alpha;
   float *state;
@@ -21,6 +22,7 @@ struct ChunkArgs {
   int B, T, H, D, chunk;  // D = Dk = Dv
   bool in_bf16, out_bf16;
   int gate;
+  bool erase;             // false: additive write, no erase term
   const void *q, *k, *v;
   const float *beta, *log_alpha;
   const float *initial_state;

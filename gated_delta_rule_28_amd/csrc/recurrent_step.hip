@@ -5,6 +5,7 @@
 // tutorial, section 四):
 //     S' = a S  (or Diag(a) S)        p = S'^T k        d = beta (v - p)
 //     S  = S' + k d^T                 o = S^T q = S'^T q + (k . q) d
+// and without the erase term d = beta v (the additive write).
 // The second form of o lets one pass over S produce both reductions before
 // the write, so S is read once and written once: 2 * Dk * Dv * 4 bytes of
 // HBM traffic per state, which is the whole cost of the step (HBM-bound).
@@ -24,7 +25,7 @@ __global__ void __launch_bounds__(2 * DV)
 recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
                       const InT *__restrict__ v, const float *__restrict__ beta,
                       const float *__restrict__ log_alpha, float *__restrict__ state,
-                      OutT *__restrict__ o) {
+                      OutT *__restrict__ o, bool erase) {
   constexpr int NT = 2 * DV;          // threads per state
   constexpr int C4 = DV / 4;          // float4 columns per row
   constexpr int RG = NT / C4;         // row groups (= 8)
@@ -96,7 +97,7 @@ recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     vv[j] = to_f32(v[sid * DV + 4 * c4 + j]);
-    d[j] = b * (vv[j] - pt[j]);
+    d[j] = b * (erase ? vv[j] - pt[j] : vv[j]);
   }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
@@ -114,7 +115,7 @@ static hipError_t launch_one(const RecurrentArgs &a) {
   dim3 grid((unsigned)((long)a.N * a.H)), block(2 * D);
   hipLaunchKernelGGL((recurrent_step_kernel<D, D, InT, OutT, GATE>), grid, block, 0, a.stream,
                      (const InT *)a.q, (const InT *)a.k, (const InT *)a.v, a.beta, a.log_alpha,
-                     a.state, (OutT *)a.o);
+                     a.state, (OutT *)a.o, a.erase);
   return hipGetLastError();
 }
 

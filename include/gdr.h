@@ -61,7 +61,15 @@ typedef enum gdr_dtype {
 typedef enum gdr_gate {
   GDR_GATE_NONE = 0,    /* a_t = 1 (DeltaNet); log_alpha must be NULL      */
   GDR_GATE_SCALAR = 1,  /* GDN: log_alpha [.., H], one value per head      */
-  GDR_GATE_CHANNEL = 2  /* KDA: log_alpha [.., H, Dk], one per key channel */
+  GDR_GATE_CHANNEL = 2, /* KDA: log_alpha [.., H, Dk], one per key channel */
+  /* Flag OR'd into any gate: no erase term.  The write is additive,
+   *   S_t = a_t S_{t-1} + b_t k_t v_t^T    (Diag(a_t) with the channel gate),
+   * which is plain linear attention with no gate and b = 1, the Mamba-2 /
+   * SSD decay with the scalar gate and GLA's with the channel gate (page
+   * "NLP——线性注意力相关总结", section "Linear Attention"; xhh.club digest,
+   * abstract and Q&A).  The same kernels run it without the triangular
+   * solve. */
+  GDR_NO_ERASE = 0x100
 } gdr_gate;
 
 /* ABI version of the loaded library (GDR_ABI_VERSION of the build). */
@@ -92,7 +100,7 @@ const char *gdr_status_str(int status);
  *   chunk        tokens per chunk: 0 = default, else 16, 32 or 64
  *   in_dtype     dtype of q, k, v (GDR_BF16 or GDR_F32)
  *   out_dtype    dtype of o (GDR_F32 or GDR_BF16)
- *   gate         GDR_GATE_NONE / _SCALAR / _CHANNEL
+ *   gate         GDR_GATE_NONE / _SCALAR / _CHANNEL, optionally | GDR_NO_ERASE
  *   q, k         [B, T, H, Dk] in_dtype
  *   v            [B, T, H, Dv] in_dtype
  *   beta         [B, T, H] fp32
@@ -125,7 +133,7 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk,
  *   N, H         sequences, heads
  *   Dk, Dv       head sizes (supported: Dk == Dv in {16, 32, 64, 128})
  *   in_dtype     dtype of q, k, v;  out_dtype  dtype of o
- *   gate         as above
+ *   gate         as above (GDR_NO_ERASE allowed)
  *   q, k         [N, H, Dk];  v [N, H, Dv]
  *   beta         [N, H] fp32
  *   log_alpha    NULL iff gate == NONE; [N, H] (SCALAR) or [N, H, Dk] (CHANNEL)

@@ -103,17 +103,17 @@ def gated_delta_recurrence(q, k, v, beta, log_alpha=None, initial_state=None,
     return o, S
 
 
-def recurrent_step(q, k, v, beta, log_alpha, state):
+def recurrent_step(q, k, v, beta, log_alpha, state, erase=True):
     """One decode step for N independent sequences (a single token each).
 
     q, k [N, H, Dk]; v [N, H, Dv]; beta [N, H]; log_alpha None | [N, H] |
     [N, H, Dk]; state [N, H, Dk, Dv].  Returns (o [N, H, Dv], new_state).
-    This is the recurrence above with T = 1; the state is carried from call
-    to call (the constant-size memory that replaces a KV cache, diosapp
-    tutorial, section 一).
+    This is the recurrence above with T = 1 (``erase`` as there); the state
+    is carried from call to call (the constant-size memory that replaces a
+    KV cache, diosapp tutorial, section 一).
     """
     la = None if log_alpha is None else _f64(log_alpha)[:, None]
     o, S = gated_delta_recurrence(
         _f64(q)[:, None], _f64(k)[:, None], _f64(v)[:, None],
-        _f64(beta)[:, None], la, state)
+        _f64(beta)[:, None], la, state, erase=erase)
     return o[:, 0], S

@@ -76,6 +76,8 @@ def step(**kw):
     (dict(gate=_abi.GDR_GATE_NONE), _abi.GDR_EINVAL),         # log_alpha given for no gate
     (dict(log_alpha=None), _abi.GDR_EINVAL),                  # gate without log_alpha
     (dict(gate=7), _abi.GDR_EINVAL),
+    (dict(gate=_abi.GDR_GATE_SCALAR | 0x200), _abi.GDR_EINVAL),   # unknown flag bit
+    (dict(gate=_abi.GDR_GATE_NONE | _abi.GDR_NO_ERASE), _abi.GDR_EINVAL),   # log_alpha given
     (dict(in_dtype=5), _abi.GDR_EINVAL),
     (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
     (dict(Dk=96, Dv=96), _abi.GDR_EUNSUPPORTED),
