@@ -100,12 +100,16 @@ def chunk_alg_bytes(w, out_bytes=4):
     return th * per_th + w.B * w.H * w.Dk * w.Dv * 4
 
 
-def chunk_alg_flops(w, C):
+def chunk_alg_flops(w, C, erase=True):
     """Algorithmic flops per call at chunk length C: per token-head 6 dk dv
     (W S, Q S, K~^T U) + 2 C dk (Q K^T and K K^T halves) + (C-1)(dk+dv)
-    (solve on [bV | bgK]) + (C+1) dv (masked P U)."""
+    (solve on [bV | bgK]) + (C+1) dv (masked P U).  Without the erase term
+    there is no W S, K K^T or solve: 4 dk dv + C dk + (C+1) dv."""
     dk, dv = w.Dk, w.Dv
-    per_th = 6 * dk * dv + 2 * C * dk + (C - 1) * (dk + dv) + (C + 1) * dv
+    if erase:
+        per_th = 6 * dk * dv + 2 * C * dk + (C - 1) * (dk + dv) + (C + 1) * dv
+    else:
+        per_th = 4 * dk * dv + C * dk + (C + 1) * dv
     return w.B * w.T * w.H * per_th
 
 
@@ -148,19 +152,19 @@ def time_launches(torch, fn, steps, warmup, settle_s=0.0):
     return wall, per
 
 
-def chunk_setup(torch, gdr, W, w, out_dtype):
+def chunk_setup(torch, gdr, W, w, out_dtype, erase=True):
     inp = W.make_workload_inputs(w, seed=0, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.Dv, device="cuda", dtype=out_dtype)
     S = torch.empty(w.B, w.H, w.Dk, w.Dv, device="cuda", dtype=torch.float32)
 
     def step():
         gdr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None,
-                      chunk=w.chunk, out_dtype=out_dtype, o=o, final_state=S)
+                      chunk=w.chunk, out_dtype=out_dtype, o=o, final_state=S, erase=erase)
     return step, o, S
 
 
-def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0):
-    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype)
+def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=True):
+    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype, erase)
     wall, per = time_launches(torch, step, steps, warmup, settle_s)
     if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())):
         raise RuntimeError(f"non-finite output in the timed run of {w.name}")
@@ -169,9 +173,10 @@ def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0):
     C = KERNEL_CHUNK[w.gate]
     mean_ms = statistics.fmean(per)
     alg_b = chunk_alg_bytes(w, out_b)
-    alg_f = chunk_alg_flops(w, C)
+    alg_f = chunk_alg_flops(w, C, erase)
     achieved = alg_b / (mean_ms * 1e-3) / 1e9
-    traffic = read_traffic(kern, w.name) if out_b == 4 else None
+    # counter traffic is taken for the erasing fp32-output launches only
+    traffic = read_traffic(kern, w.name) if out_b == 4 and erase else None
     return {
         "workload": w.name, "tokens": w.B * w.T, "wall_s": wall, "steps": steps,
         "ms_per_step": 1e3 * wall / steps,
@@ -436,6 +441,14 @@ def main(argv=None):
         rec["kda"] = {k: kda[k] for k in ("workload", "value", "kernel", "kernel_chunk",
                                           "kernel_ms", "roofline", "mfma_alg")}
         rec["kda"]["unit"] = "tokens/s"
+        # the erase-free variant (additive write) through the same kernels:
+        # the Mamba-2 / SSD decay on the headline shape, GLA's on the KDA shape
+        for key, wl in (("additive_scalar", w), ("additive_channel", W.by_name("kda_bf16_b2h32t8192"))):
+            ln = chunk_line(torch, gdr, W, wl, nb, 2, torch.float32, args.settle_s, erase=False)
+            rec[key] = {k: ln[k] for k in ("workload", "value", "kernel", "kernel_chunk",
+                                           "kernel_ms", "roofline", "mfma_alg")}
+            rec[key]["unit"] = "tokens/s"
+            rec[key]["variant"] = "no erase term (S = a S + b k v^T)"
         rec["decode"] = decode_line(torch, gdr, W, W.DECODE, settle_s=args.settle_s)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(W, w)

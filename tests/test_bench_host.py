@@ -18,6 +18,8 @@ def test_headline_algorithmic_counts():
     assert bench.chunk_alg_bytes(w) == 683_671_552
     # 139,136 flop per token-head at 64-token chunks
     assert bench.chunk_alg_flops(w, 64) == th * 139_136
+    # without the erase term: 4 dk dv + C dk + (C + 1) dv = 82,048 at C = 64
+    assert bench.chunk_alg_flops(w, 64, erase=False) == th * 82_048
     d = W.DECODE
     assert bench.decode_alg_bytes(d) == 256 * 32 * (2 * 4 * 128 * 128 + 2 * 384 + 8 + 4 * 128)
 
