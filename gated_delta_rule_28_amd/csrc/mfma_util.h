@@ -70,26 +70,27 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // x - hi takes one of two forms:
 //  - DOT: one instruction per value, the packed bf16 dot product
 //    hi . m + x with m = (-1, 0) or (0, -1) (bf16 -1.0 is 0xBF80; the
-//    products are exact).  It is written as the three-address VOP3P
-//    instruction because the compiler's own form ties the accumulator to the
-//    destination and copies x first whenever x stays live.  A VALU read of
-//    a dot product's result needs three wait states, which the compiler does
-//    not insert after inline assembly, so the block ends with them (s_nop 2).
-//    Every input of the block is first read by the compiler-visible
-//    conversion that makes hi, so hazards on the inputs (an MFMA result read
-//    by VALU) are resolved before it.
+//    products are exact).  It goes through the compiler builtin, whose form
+//    ties the accumulator to the destination (a copy of x first when x
+//    stays live).  It must stay visible to the compiler: a VALU write of a
+//    register that an MFMA issued just before still reads as its
+//    accumulator input needs wait states, which the compiler inserts for
+//    its own instructions but not for inline assembly.
 //  - otherwise: the hi values unpacked by a shift and a mask, then
 //    subtracted (two instructions per value, freely scheduled).
 template <bool DOT = true>
 __device__ __forceinline__ void split2(float x0, float x1, unsigned &hi, unsigned &lo) {
-  hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const bf16x2 h = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+  hi = __builtin_bit_cast(unsigned, h);
   float r0, r1;
   if constexpr (DOT) {
-    asm("v_dot2_f32_bf16 %0, %2, %3, %4\n\t"
-        "v_dot2_f32_bf16 %1, %2, %5, %6\n\t"
-        "s_nop 2"
-        : "=&v"(r0), "=v"(r1)
-        : "v"(hi), "s"(0x0000BF80u), "v"(x0), "s"(0xBF800000u), "v"(x1));
+    // the masks reach the instruction from SGPRs: the compiler would fold
+    // (-1, 0) into the inline constant -1.0, which the hardware does not
+    // read as that bf16 pair
+    unsigned m0 = 0x0000BF80u, m1 = 0xBF800000u;
+    asm("" : "+s"(m0), "+s"(m1));
+    r0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m0), x0, false);
+    r1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m1), x1, false);
   } else {
     r0 = x0 - __builtin_bit_cast(float, hi << 16);
     r1 = x1 - __builtin_bit_cast(float, hi & 0xffff0000u);
@@ -134,6 +135,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc32(const void *base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
+}
+__device__ __forceinline__ float buf_ld_bf16(rsrc_t r, int off) {
+  const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return __builtin_bit_cast(float, (unsigned)u << 16);
 }
 __device__ __forceinline__ void buf_st1(float x, rsrc_t r, int off) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);

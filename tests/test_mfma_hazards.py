@@ -1,0 +1,144 @@
+"""Static check of the MFMA kernels' gfx950 assembly (no GPU needed).
+
+A VALU instruction (or a store) that reads an MFMA result must issue enough
+wait states after the MFMA; the compiler inserts s_nop for this, and in
+straight-line code it keeps at least 8 between a 16x16x32 (or 16x16x16)
+bf16 MFMA and the first read of its result.  Its hazard pass has been seen
+to under-count when an if-block without an else sits between the MFMA and
+the read: it counted only the path through the block, so the path that
+jumps over it read a stale accumulator register (wrong results that depend
+on timing).  The kernels avoid runtime branches at such points; this test
+compiles them to assembly and checks, along the shortest path in layout
+order, that every read of an MFMA result reached across a branch is at
+least 8 wait states after the MFMA.
+"""
+
+import concurrent.futures as cf
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc")
+SOURCES = ["chunk_fwd_bf16.hip", "chunk_fwd_kda.hip"]
+MIN_WAIT_STATES = 8
+WINDOW = 64          # instructions scanned after each MFMA
+
+_REG = re.compile(r"v\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _vregs(text):
+    out = set()
+    for m in _REG.finditer(text):
+        if m.group(3):
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def _assembly(src, out_dir):
+    out = os.path.join(out_dir, src + ".s")
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return open(out).read().splitlines()
+
+
+def short_reads(lines, min_ws=MIN_WAIT_STATES):
+    """(mfma line, reader line, wait states) for reads of an MFMA result
+    reached across a branch with fewer than min_ws wait states on the
+    shortest layout-order path."""
+    found = []
+    inf = 10 ** 6
+    for i, line in enumerate(lines):
+        s = line.strip()
+        if not s.startswith("v_mfma"):
+            continue
+        dst = _vregs(s.split()[1])
+        ws, crossed, pending = 0, False, {}
+        for j in range(i + 1, min(i + 1 + WINDOW, len(lines))):
+            t = lines[j].strip()
+            if t.startswith(".LBB") and t.endswith(":"):
+                ws = min(ws, pending.pop(t[:-1], inf))
+                continue
+            if not t or t.startswith((";", ".")):
+                continue
+            if t.startswith("s_endpgm"):
+                break
+            if t.startswith(("s_cbranch", "s_branch")):
+                crossed = True
+                label = t.split()[1]
+                pending[label] = min(pending.get(label, inf), ws + 1)
+                ws = inf if t.startswith("s_branch") else ws + 1
+                continue
+            if t.startswith("s_nop"):
+                ws += int(t.split()[1]) + 1
+                continue
+            parts = t.split(None, 1)
+            if len(parts) == 2:
+                ops = parts[1]
+                if t.startswith("v_mfma"):
+                    if _vregs(ops.split(",", 1)[1]) & dst:
+                        break       # an accumulator chain: not a VALU read
+                elif t.startswith(("ds_write", "buffer_store", "global_store")):
+                    if _vregs(ops) & dst:
+                        if crossed and ws < min_ws:
+                            found.append((i + 1, j + 1, ws))
+                        break
+                elif t.startswith("v_") and "," in ops:
+                    if _vregs(ops.split(",", 1)[1]) & dst:
+                        if crossed and ws < min_ws:
+                            found.append((i + 1, j + 1, ws))
+                        break
+            ws += 1
+    return found
+
+
+def test_scanner_flags_a_read_that_skips_an_if_block():
+    # the shape the check exists for: the MFMA result v6 is read two
+    # instructions after the MFMA on the path that jumps over the block
+    lines = """
+    v_mfma_f32_16x16x32_bf16 v[6:9], v[14:17], v[14:17], v[6:9]
+    s_cbranch_vccnz .LBB0_2
+    ds_read_b128 v[14:17], v14 offset:19712
+    v_mul_f32_e32 v2, v2, v14
+    v_mul_f32_e32 v3, v3, v15
+    v_mul_f32_e32 v4, v4, v16
+    v_mul_f32_e32 v5, v5, v17
+    v_mul_f32_e32 v2, v2, v18
+    v_mul_f32_e32 v3, v3, v18
+    v_mul_f32_e32 v4, v4, v18
+.LBB0_2:
+    ds_read_b128 v[14:17], v12 offset:4096
+    v_mul_f32_e32 v2, v6, v2
+""".splitlines()
+    assert [f[2] for f in short_reads(lines)] == [2]
+    # enough wait states before the branch cover both paths
+    mfma = next(i for i, l in enumerate(lines) if "v_mfma" in l)
+    padded = lines[:mfma + 1] + ["    s_nop 7"] + lines[mfma + 1:]
+    assert short_reads(padded) == []
+    # so does a read inside the block, whose only way in is from the MFMA
+    inside = lines[:mfma + 2] + ["    s_nop 6", "    v_mul_f32_e32 v2, v6, v2"] + lines[mfma + 2:]
+    assert short_reads(inside) == []
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_mfma_results_are_not_read_early_across_branches():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            asm = dict(zip(SOURCES, ex.map(lambda s: _assembly(s, tmp), SOURCES)))
+    problems = {src: short_reads(lines)[:5] for src, lines in asm.items()}
+    assert all(not p for p in problems.values()), problems
