@@ -11,6 +11,12 @@ Gate kind follows log_alpha: None -> DeltaNet (alpha = 1); [B, T, H] ->
 Gated DeltaNet (one decay per head); [B, T, H, Dk] -> KDA (one per channel).
 erase=False drops the erase term (S = alpha S + beta k v^T): linear
 attention, the Mamba-2 / SSD decay and GLA's, through the same kernels.
+
+Fused prologue / epilogue (keyword options of both calls): qk_l2norm=True
+normalises q and k per (token, head); beta_sigmoid=True takes beta as a
+logit; decay="softplus" takes log_alpha as x with log a = -softplus(x),
+decay="gla" as x with a = sigmoid(x)^(1/16); out_gate=g multiplies the
+output by g * sigmoid(g) (SiLU gate, same shape as o, dtype of q).
 """
 
 import torch
@@ -58,9 +64,27 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+_DECAY = {None: 0, "log": 0, "softplus": _abi.GDR_FUSE_DECAY_SOFTPLUS, "gla": _abi.GDR_FUSE_DECAY_GLA}
+
+
+def _fuse_flags(qk_l2norm, beta_sigmoid, decay):
+    if decay not in _DECAY:
+        raise ValueError(f"decay must be one of {sorted(k for k in _DECAY if k)} or None")
+    return ((_abi.GDR_FUSE_QK_L2NORM if qk_l2norm else 0) |
+            (_abi.GDR_FUSE_BETA_SIGMOID if beta_sigmoid else 0) | _DECAY[decay])
+
+
+def _check_gate_tensor(out_gate, shape, dtype):
+    if out_gate is None:
+        return
+    _check_dev("out_gate", out_gate, dtype)
+    if tuple(out_gate.shape) != tuple(shape):
+        raise ValueError(f"out_gate must be {tuple(shape)}")
+
+
 def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
               out_dtype=torch.float32, output_final_state=True, o=None, final_state=None,
-              erase=True):
+              erase=True, qk_l2norm=False, beta_sigmoid=False, decay=None, out_gate=None):
     """Chunkwise forward over whole sequences.
 
     q, k [B, T, H, Dk] and v [B, T, H, Dv] (bf16 or fp32, same dtype);
@@ -103,17 +127,19 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
         _check_dev("final_state", final_state, torch.float32)
         if tuple(final_state.shape) != (B, H, Dk, Dv):
             raise ValueError("final_state must be [B, H, Dk, Dv]")
-    st = _abi.gdr_chunk_fwd(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], _DT[out_dtype], gate,
-                            q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
-                            _ptr(log_alpha), _ptr(initial_state), o.data_ptr(),
-                            _ptr(final_state), _stream(q.device))
+    fuse = _fuse_flags(qk_l2norm, beta_sigmoid, decay)
+    _check_gate_tensor(out_gate, (B, T, H, Dv), q.dtype)
+    st = _abi.gdr_chunk_fwd_ex(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], _DT[out_dtype], gate,
+                               fuse, q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                               _ptr(log_alpha), _ptr(out_gate), _ptr(initial_state),
+                               o.data_ptr(), _ptr(final_state), _stream(q.device))
     if st != _abi.GDR_OK:
-        raise GdrError(st, "gdr_chunk_fwd")
+        raise GdrError(st, "gdr_chunk_fwd_ex")
     return o, final_state
 
 
 def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, o=None,
-                   erase=True):
+                   erase=True, qk_l2norm=False, beta_sigmoid=False, decay=None, out_gate=None):
     """One decode token for N sequences; `state` [N, H, Dk, Dv] fp32 is
     updated in place.  q, k [N, H, Dk]; v [N, H, Dv]; beta [N, H];
     log_alpha None | [N, H] | [N, H, Dk].  Returns o [N, H, Dv]."""
@@ -137,10 +163,12 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
         o = torch.empty(N, H, Dv, device=q.device, dtype=out_dtype)
     else:
         _check_dev("o", o, out_dtype)
-    st = _abi.gdr_recurrent_step(N, H, Dk, Dv, _DT[q.dtype], _DT[out_dtype], gate,
-                                 q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
-                                 _ptr(log_alpha), state.data_ptr(), o.data_ptr(),
-                                 _stream(q.device))
+    fuse = _fuse_flags(qk_l2norm, beta_sigmoid, decay)
+    _check_gate_tensor(out_gate, (N, H, Dv), q.dtype)
+    st = _abi.gdr_recurrent_step_ex(N, H, Dk, Dv, _DT[q.dtype], _DT[out_dtype], gate, fuse,
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                    _ptr(log_alpha), _ptr(out_gate), state.data_ptr(),
+                                    o.data_ptr(), _stream(q.device))
     if st != _abi.GDR_OK:
-        raise GdrError(st, "gdr_recurrent_step")
+        raise GdrError(st, "gdr_recurrent_step_ex")
     return o

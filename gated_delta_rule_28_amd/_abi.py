@@ -16,6 +16,8 @@ GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EHIP = 0, -1, -2, -3
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_NONE, GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1, 2
 GDR_NO_ERASE = 0x100   # OR'd into a gate: additive write, no erase term
+# fused prologue flags (gdr_fuse)
+GDR_FUSE_QK_L2NORM, GDR_FUSE_BETA_SIGMOID, GDR_FUSE_DECAY_SOFTPLUS, GDR_FUSE_DECAY_GLA = 1, 2, 4, 8
 
 # every function the header declares, with its ctypes signature
 _c_int, _vp, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -24,6 +26,8 @@ SIGNATURES = {
     "gdr_status_str": (ctypes.c_char_p, [_c_int]),
     "gdr_chunk_fwd": (_c_int, [_c_int] * 9 + [_vp] * 9),
     "gdr_recurrent_step": (_c_int, [_c_int] * 7 + [_vp] * 8),
+    "gdr_chunk_fwd_ex": (_c_int, [_c_int] * 10 + [_vp] * 10),
+    "gdr_recurrent_step_ex": (_c_int, [_c_int] * 8 + [_vp] * 9),
 }
 
 _lib = None
@@ -79,3 +83,18 @@ def gdr_recurrent_step(N, H, Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, l
     """Raw call of the C entry point with integer sizes and raw pointers."""
     return load().gdr_recurrent_step(N, H, Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta,
                                      log_alpha, state, o, stream)
+
+
+def gdr_chunk_fwd_ex(B, T, H, Dk, Dv, chunk, in_dtype, out_dtype, gate, fuse, q, k, v, beta,
+                     log_alpha, out_gate, initial_state, o, final_state, stream):
+    """Raw call of the C entry point with integer sizes and raw pointers."""
+    return load().gdr_chunk_fwd_ex(B, T, H, Dk, Dv, chunk, in_dtype, out_dtype, gate, fuse, q, k,
+                                   v, beta, log_alpha, out_gate, initial_state, o, final_state,
+                                   stream)
+
+
+def gdr_recurrent_step_ex(N, H, Dk, Dv, in_dtype, out_dtype, gate, fuse, q, k, v, beta,
+                          log_alpha, out_gate, state, o, stream):
+    """Raw call of the C entry point with integer sizes and raw pointers."""
+    return load().gdr_recurrent_step_ex(N, H, Dk, Dv, in_dtype, out_dtype, gate, fuse, q, k, v,
+                                        beta, log_alpha, out_gate, state, o, stream)

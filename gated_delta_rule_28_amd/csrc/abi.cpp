@@ -38,6 +38,19 @@ int check_common(int Dk, int Dv, int in_dtype, int out_dtype, int gate, const vo
   return GDR_OK;
 }
 
+// fused-prologue flags: known bits, at most one decay transform, and a
+// decay transform only with a gate; the output gate is read with vectors
+int check_fuse(int fuse, int gate, const void *out_gate) {
+  const int known = GDR_FUSE_QK_L2NORM | GDR_FUSE_BETA_SIGMOID | GDR_FUSE_DECAY_SOFTPLUS |
+                    GDR_FUSE_DECAY_GLA;
+  if (fuse & ~known) return GDR_EINVAL;
+  const int decay = fuse & (GDR_FUSE_DECAY_SOFTPLUS | GDR_FUSE_DECAY_GLA);
+  if (decay == (GDR_FUSE_DECAY_SOFTPLUS | GDR_FUSE_DECAY_GLA)) return GDR_EINVAL;
+  if (decay && gate_kind(gate) == GDR_GATE_NONE) return GDR_EINVAL;
+  if (out_gate && !aligned16(out_gate)) return GDR_EINVAL;
+  return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,11 +71,21 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
                   int gate, const void *q, const void *k, const void *v, const float *beta,
                   const float *log_alpha, const float *initial_state, void *o,
                   float *final_state, hipStream_t stream) {
+  return gdr_chunk_fwd_ex(B, T, H, Dk, Dv, chunk, in_dtype, out_dtype, gate, 0, q, k, v, beta,
+                          log_alpha, nullptr, initial_state, o, final_state, stream);
+}
+
+int gdr_chunk_fwd_ex(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int out_dtype,
+                     int gate, int fuse, const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_alpha, const void *out_gate,
+                     const float *initial_state, void *o, float *final_state,
+                     hipStream_t stream) {
   if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
   if (!(chunk == 0 || chunk == 16 || chunk == 32 || chunk == 64)) return GDR_EUNSUPPORTED;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate)) return GDR_EINVAL;
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return GDR_EINVAL;
+  if (check_fuse(fuse, gate, out_gate) != GDR_OK) return GDR_EINVAL;
   if (Dk != Dv || !supported_head(Dk)) return GDR_EUNSUPPORTED;
   // empty token tensors may carry null pointers, so these return before the
   // pointer checks
@@ -83,7 +106,9 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   a.in_bf16 = in_dtype == GDR_BF16; a.out_bf16 = out_dtype == GDR_BF16;
   a.gate = gate_kind(gate);
   a.erase = erases(gate);
+  a.fuse = fuse;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.out_gate = out_gate;
   a.initial_state = initial_state; a.o = o; a.final_state = final_state;
   a.stream = stream;
 
@@ -98,17 +123,28 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
 int gdr_recurrent_step(int N, int H, int Dk, int Dv, int in_dtype, int out_dtype, int gate,
                        const void *q, const void *k, const void *v, const float *beta,
                        const float *log_alpha, float *state, void *o, hipStream_t stream) {
+  return gdr_recurrent_step_ex(N, H, Dk, Dv, in_dtype, out_dtype, gate, 0, q, k, v, beta,
+                               log_alpha, nullptr, state, o, stream);
+}
+
+int gdr_recurrent_step_ex(int N, int H, int Dk, int Dv, int in_dtype, int out_dtype, int gate,
+                          int fuse, const void *q, const void *k, const void *v,
+                          const float *beta, const float *log_alpha, const void *out_gate,
+                          float *state, void *o, hipStream_t stream) {
   if (N < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
   if ((long)N * H == 0) return GDR_OK;
   int st = check_common(Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, log_alpha, o);
   if (st != GDR_OK) return st;
   if (!state || !aligned16(state)) return GDR_EINVAL;
+  if (check_fuse(fuse, gate, out_gate) != GDR_OK) return GDR_EINVAL;
   gdr::RecurrentArgs a;
   a.N = N; a.H = H; a.D = Dk;
   a.in_bf16 = in_dtype == GDR_BF16; a.out_bf16 = out_dtype == GDR_BF16;
   a.gate = gate_kind(gate);
   a.erase = erases(gate);
+  a.fuse = fuse;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.out_gate = out_gate;
   a.state = state; a.o = o; a.stream = stream;
   hipError_t e = gdr::launch_recurrent_step(a);
   return e == hipSuccess ? GDR_OK : GDR_EHIP;

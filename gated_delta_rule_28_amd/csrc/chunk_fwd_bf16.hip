@@ -109,7 +109,10 @@ struct __align__(16) PipeSmem {
     float la[64], beta[64];            // log a and b of the 64 tokens from the chunk start
                                        // (0 past the end of the sequence: the DMA
                                        // reads zeros beyond the chunk's last row)
-    float gam[C], ec[C];               // e^g, e^{g_last - g}
+    float gam[C], ec[C];               // e^g, e^{g_last - g} (times 1/|k| when fused)
+    float fq[C], fk[C], bt[C];         // factors of Q S and K S (e^g, times 1/|q|, 1/|k|
+                                       // when fused), b (after the fused sigmoid)
+    float nrm[2][C];                   // fused L2 normalisation: 1/|q|, 1/|k| per token
   };
   struct __align__(16) PT {
     bf16 Ph[C][LDC], Pl[C][LDC];       // P^T: [s][r] = P[r][s]; rows 16..31 x cols 0..15 stay zero
@@ -121,15 +124,16 @@ struct __align__(16) PipeSmem {
   bf16 A10h[2][16][LDT], A10l[2][16][LDT];   // block (1,0) of A, transposed: [s][r] = A[16+r][s]
   bf16 Th[NTS][C][LDC], Tl[NTS][C][LDC];   // T^T: [s][r] = T[r][s], T = (I+A)^{-1} (T' = T diag(b));
                                        // rows 16..31 x cols 0..15 stay zero
-  float gw[3][C];                      // in-chunk log decay g, one copy per tile wave
+  float gw[3][C], bw[3][C];            // in-chunk log decay g and b, one copy per tile wave
 };
 
-template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE, bool FUSED>
 __global__ void __launch_bounds__(64 * (DVS / 16 + NPW), 1)
 chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ v, const float *__restrict__ beta,
                       const float *__restrict__ log_alpha, const float *initial_state,
-                      OutT *__restrict__ o, float *final_state, int B, int T, int H) {
+                      OutT *__restrict__ o, float *final_state, int B, int T, int H, int fuse,
+                      const bf16 *__restrict__ out_gate) {
   constexpr int NSW = DVS / 16;        // state waves; wave w owns value columns 16w..16w+15
   constexpr int NT = 64 * (NSW + NPW);
   constexpr int DV = DK;               // full value width (Dk == Dv)
@@ -144,6 +148,11 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(sizeof(In) % 16 == 0 && (C * QRB) % 1024 == 0 && (C * VRB) % 1024 == 0,
                 "DMA runs are whole 1 KiB waves");
   __shared__ SM sm;
+  // calls without a fused prologue or epilogue compile without their code
+  if constexpr (!FUSED) {
+    fuse = 0;
+    out_gate = nullptr;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar: the role split below is a uniform branch
@@ -197,6 +206,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // state waves: the serial chunk-to-chunk pass, 16 state columns each
     // =====================================================================
     const int col0 = slice * DVS + 16 * wave;   // first value column of this wave
+    const bool gated = out_gate != nullptr;
     // Sacc[mb][e] = S[srow(mb, e)][col0 + lr]
     auto srow = [&](int mb, int e) { return 32 * (mb >> 1) + 8 * lg + 4 * (mb & 1) + e; };
     f32x4 Sacc[DK / 16];
@@ -248,6 +258,21 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const int s = it - 1;            // chunk of this iteration
       f32x4 QS[2];
       bf16x8 Uh, Ul, Wh, Wl;
+      // the fused output gate of this lane's O values, loaded before the
+      // chunk's products (the gate is applied by a select after them: a
+      // branch between an MFMA and the read of its result can hide the
+      // wait states that read needs)
+      f32x4 og[2] = {};
+      if (gated && s >= 0) {
+        const int n = min(C, T - s * C);
+        const long orow = (tok0 + (long)s * C * H) * DV;
+        const rsrc_t rg = make_rsrc32(out_gate + orow, 2u * ((unsigned)(n - 1) * H * DV + DV));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            og[rb][e] = buf_ld_bf16(rg, 2 * (ooff[rb][e] / (int)sizeof(OutT)));
+      }
       // ---- K S, Q S, R = V - diag(gam) K S, U = T' R ----
       if (s >= 0) {
         const In &bs = *at_off(&sm.in[0], slot_off(s % NIN, (int)sizeof(In)));
@@ -282,9 +307,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const int r0 = 16 * rb + 4 * lg;
           // V[r0 + c][16 wave + lr], c = 0..3, by a transposing read
           const bf16x4 vv = ld_tr4(reinterpret_cast<const bf16 *>(Vb + 16 * rb * VRB + v_off));
-          const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
-                                                : *reinterpret_cast<const f32x4 *>(&bs.gam[r0]);
-          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.beta[r0]);
+          const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&bs.fk[r0]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.bt[r0]);
           // b o R: T' R = T diag(b) R with T kept unscaled; without the
           // erase term R = V and U = b o V
           f32x4 rr;
@@ -301,8 +325,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int rb = 0; rb < 2; ++rb) {
             uh[rb] = rh2[rb];
             ul[rb] = rl2[rb];
-            const f32x4 ec4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
-                                                  : *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
+            const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
             split4(rv[rb] * ec4, wh[rb], wl[rb]);
           }
         } else {
@@ -321,8 +344,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             u = mfma_bf16(tl, Rh, u);
             u = mfma_bf16(th, Rl, u);
             split4(u, uh[rb], ul[rb]);
-            const f32x4 ec4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
-                                                  : *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
+            const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
             split4(u * ec4, wh[rb], wl[rb]);
           }
         }
@@ -341,8 +363,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const f32x4 gm4 = (GATE == kGateNone) ? f32x4{1.f, 1.f, 1.f, 1.f}
-                                                : *reinterpret_cast<const f32x4 *>(&bs.gam[16 * rb + 4 * lg]);
+          const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&bs.fq[16 * rb + 4 * lg]);
           f32x4 acc = gm4 * QS[rb];
           const bf16x8 ph = cat(ld_tr4(&ps.Ph[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
                                 ld_tr4(&ps.Ph[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
@@ -351,6 +372,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(ph, Uh, acc);
           acc = mfma_bf16(pl, Uh, acc);
           acc = mfma_bf16(ph, Ul, acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = gated ? silu_gate(acc[e], og[rb][e]) : acc[e];
           // lane holds O rows 16 rb + 4 lg + e of column col0 + lr: stored
           // straight from the accumulator (16 lanes write 16 adjacent values
           // of a row); rows past the end of the sequence are not written
@@ -408,19 +431,29 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       ld8(reinterpret_cast<const bf16 *>(Kc + 16 * tj * QRB + kq_off[kk])), acc);
     return acc;
   };
-  // the decay, the mask and (for A) the factor b of tile (ti, tj); g is the
-  // calling wave's copy of the in-chunk log decay
-  auto decayed = [&](const In &bf, const float *g, f32x4 acc, int ti, int tj, bool isq) {
+  // the decay, the mask and (for A) the factor b of tile (ti, tj); g and b
+  // are the calling wave's copies; with the fused normalisation the row
+  // factor 1/|q_r| (P) or 1/|k_r| (A) and the column factor 1/|k_s|
+  auto decayed = [&](const In &bf, const float *g, const float *bw, f32x4 acc, int ti, int tj,
+                     bool isq) {
     const int sc = 16 * tj + lr;
     const int r0 = 16 * ti + 4 * lg;
     const float gs = g[sc];
     const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&g[r0]);
-    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bf.beta[r0]);
+    // the norms are read whether or not they were formed and picked by a
+    // select: a branch here would sit between the tile's MFMA and the read
+    // of its result, which can hide the wait states that read needs
+    const f32x4 b0 = isq ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4 *>(&bw[r0]);
+    const f32x4 bn = b0 * *reinterpret_cast<const f32x4 *>(&bf.nrm[isq ? 0 : 1][r0]) * bf.nrm[1][sc];
+    const bool l2 = (fuse & kFuseL2) != 0;
+    f32x4 b4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b4[e] = l2 ? bn[e] : b0[e];
     f32x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float dec = (GATE == kGateNone) ? 1.0f : __expf(gr4[e] - gs);
-      val[e] = isq ? ((sc <= r0 + e) ? acc[e] * dec : 0.0f)
+      val[e] = isq ? ((sc <= r0 + e) ? b4[e] * acc[e] * dec : 0.0f)
                    : ((sc < r0 + e) ? b4[e] * acc[e] * dec : 0.0f);
     }
     return val;
@@ -587,16 +620,32 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // and P00.
   auto tiles = [&](int j) {
     In &bf = *at_off(&sm.in[0], slot_off(j % NIN, (int)sizeof(In)));
-    float *g = sm.gw[pw];
-    const float la = SCALAR ? bf.la[lane] : 0.0f;
+    float *g = sm.gw[pw], *bw = sm.bw[pw];
+    // padded tokens carry log a = 0 and b = 0 after the fused transforms too
+    const int n = min(C, T - j * C);
+    const float la = (SCALAR && lane < n) ? fused_log_alpha(bf.la[lane], fuse) : 0.0f;
     const float sc = scan32_inclusive(la);
-    if (lane < C) g[lane] = sc;
-    if (pw == 0 && GATE != kGateNone) {
+    const float bl = (lane < n) ? fused_beta(bf.beta[lane], fuse) : 0.0f;
+    if (lane < C) {
+      g[lane] = sc;
+      bw[lane] = bl;
+    }
+    if (pw == 0) {
+      // the state waves' factors: e^g for Q S and K S (times 1/|q|, 1/|k|),
+      // e^{g_last - g} (times 1/|k|) for the update, b
       const float glast = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), C - 1));
       if (lane < C) {
-        bf.gam[lane] = __expf(sc);
-        bf.ec[lane] = __expf(glast - sc);
+        const float gm = (GATE == kGateNone) ? 1.0f : __expf(sc);
+        const float e = (GATE == kGateNone) ? 1.0f : __expf(glast - sc);
+        const bool l2 = (fuse & kFuseL2) != 0;
+        const float nq = bf.nrm[0][lane], nk = bf.nrm[1][lane];
+        const float rq = l2 ? nq : 1.0f, rk = l2 ? nk : 1.0f;
+        bf.gam[lane] = gm;
+        bf.fq[lane] = gm * rq;
+        bf.fk[lane] = gm * rk;
+        bf.ec[lane] = e * rk;
+        bf.bt[lane] = bl;
       }
     }
     wave_lds_sync();
@@ -605,30 +654,55 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int ao = slot_off(j & 1, (int)sizeof(sm.ATd[0]));
     if (pw == 0) {
       if constexpr (!ERASE) return;                  // no A without the erase term
-      const f32x4 val = decayed(bf, g, tile_acc(bf, false, 1, 0), 1, 0, false);
+      const f32x4 val = decayed(bf, g, bw, tile_acc(bf, false, 1, 0), 1, 0, false);
       bf16x4 h4, l4;
       split4(val, h4, l4);
       *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10h[0][0], a10o)[lr][4 * lg]) = h4;
       *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10l[0][0], a10o)[lr][4 * lg]) = l4;
       *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[1][lr][4 * lg]) =
-          -decayed(bf, g, tile_acc(bf, false, 1, 1), 1, 1, false);
+          -decayed(bf, g, bw, tile_acc(bf, false, 1, 1), 1, 1, false);
     } else if (pw == 1) {
       if constexpr (ERASE)
         *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[0][lr][4 * lg]) =
-            -decayed(bf, g, tile_acc(bf, false, 0, 0), 0, 0, false);
-      store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
+            -decayed(bf, g, bw, tile_acc(bf, false, 0, 0), 0, 0, false);
+      store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
     } else {
-      store_p(pt, decayed(bf, g, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
-      store_p(pt, decayed(bf, g, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
+      store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
+      store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
     }
   };
 
-  // prologue: chunks 0..2 in flight; chunks 0 and 1 landed; the tiles of
-  // chunk 0 formed
+  // fused L2 normalisation: 1/|row| of chunk j's k (wave 1) or q (wave 2),
+  // formed by the wave whose DMA brought the rows, right after its wait;
+  // lane = (row, half row)
+  auto norms = [&](int j) {
+    In &bf = *at_off(&sm.in[0], slot_off(j % NIN, (int)sizeof(In)));
+    const char *X = reinterpret_cast<const char *>(pw == 1 ? &bf.K[0][0] : &bf.Q[0][0]);
+    const int r = lane & (C - 1), h = lane / C;
+    float ss = 0.0f;
+#pragma unroll
+    for (int b = 0; b < QB / 2; ++b) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4 *>(X + r * QRB + 16 * (h * (QB / 2) + b));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_bit_cast(float, w4[i] << 16);
+        const float hi = __builtin_bit_cast(float, w4[i] & 0xffff0000u);
+        ss += lo * lo + hi * hi;
+      }
+    }
+    ss += __shfl_xor(ss, C);
+    if (lane < C) bf.nrm[pw == 1 ? 1 : 0][lane] = rsqrtf(ss + kL2Eps);
+  };
+  const bool l2 = (fuse & kFuseL2) && (pw == 1 || pw == 2);
+
+  // prologue: chunks 0..2 in flight; chunks 0 and 1 landed (and normalised);
+  // the tiles of chunk 0 formed
   if (nchunks > 0) issue(0);
   if (nchunks > 1) issue(1);
   if (nchunks > 2) issue(2);
   wait_prev(nchunks > 2);
+  if (l2 && nchunks > 0) norms(0);
+  if (l2 && nchunks > 1) norms(1);
   __syncthreads();
   if (nchunks > 0) tiles(0);
   __syncthreads();
@@ -640,18 +714,26 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (more) issue(it + 3);
     if (it + 1 < nchunks) tiles(it + 1);
     wait_prev(more);
+    if (l2 && it + 2 < nchunks) norms(it + 2);
     __syncthreads();
   }
 }
 
-template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
-hipError_t launch_cfg(const ChunkArgs &a) {
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE, bool FUSED>
+hipError_t launch_fused(const ChunkArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE, ERASE>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE, ERASE, FUSED>), grid, block, 0, a.stream,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
-                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
+                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H, a.fuse,
+                     (const bf16 *)a.out_gate);
   return hipGetLastError();
+}
+
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
+hipError_t launch_cfg(const ChunkArgs &a) {
+  if (a.fuse != 0 || a.out_gate != nullptr) return launch_fused<DK, DVS, OutT, GATE, ERASE, true>(a);
+  return launch_fused<DK, DVS, OutT, GATE, ERASE, false>(a);
 }
 
 template <int DK, int DVS, typename OutT>

@@ -73,6 +73,7 @@ struct __align__(16) KdaSmem {
     bf16 Q[KC][DK], K[KC][DK];            // natural channel order
     float G[KC][DK];                      // log a, summed in place into G
     float beta[64];                       // b of the 64 tokens from the chunk start (16 used)
+    float nrm[2][KC];                     // fused L2 normalisation: 1/|q|, 1/|k| per token
     int flag[4];                          // [0]: some channel's in-chunk log decay < -kMaxSpan
   };
   struct __align__(16) Der {              // operands of one chunk, rows permuted by swz_qk
@@ -93,12 +94,13 @@ struct __align__(16) KdaSmem {
   float At[KC][LDX];                      // -A^T of the chunk being solved
 };
 
-template <int DK, int DVS, typename OutT, bool ERASE>
+template <int DK, int DVS, typename OutT, bool ERASE, bool FUSED>
 __global__ void __launch_bounds__(64 * (DVS / 16 + kda_npw<DVS>()), 1)
 chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ beta,
                      const float *__restrict__ log_alpha, const float *initial_state,
-                     OutT *__restrict__ o, float *final_state, int B, int T, int H) {
+                     OutT *__restrict__ o, float *final_state, int B, int T, int H, int fuse,
+                     const bf16 *__restrict__ out_gate) {
   constexpr int NSW = DVS / 16;
   constexpr int DV = DK;
   constexpr int NSLICE = DV / DVS;
@@ -106,6 +108,11 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int QB = DK / 8, VB = DVS / 8;      // 16-byte blocks per q/k and v row
   constexpr int QRB = 2 * DK, VRB = 2 * DVS;    // bytes per q/k and v row
   static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
+  // calls without a fused prologue or epilogue compile without their code
+  if constexpr (!FUSED) {
+    fuse = 0;
+    out_gate = nullptr;
+  }
   using SM = KdaSmem<DK, DVS>;
   static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
   static_assert(sizeof(typename SM::Raw) % 16 == 0 && sizeof(typename SM::Der) % 16 == 0 &&
@@ -189,8 +196,21 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     };
     split_state();
 
+    const bool gated = out_gate != nullptr;
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;
+      // the fused output gate of this lane's O values, loaded before the
+      // chunk's products (the gate is applied by a select after them: a
+      // branch between an MFMA and the read of its result can hide the
+      // wait states that read needs)
+      f32x4 og = {};
+      if (gated && s >= 0) {
+        const int n = min(KC, T - s * KC);
+        const rsrc_t rg = make_rsrc32(out_gate + (tok0 + (long)s * KC * H) * DV,
+                                      2u * ((unsigned)(n - 1) * H * DV + DV));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) og[e] = buf_ld_bf16(rg, 2 * (ooff[e] / (int)sizeof(OutT)));
+      }
       if (s >= 0) {
         const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));
         const int t1 = slot_off(s & 1, (int)sizeof(sm.Th[0]));   // T' and P slots (same size)
@@ -252,6 +272,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         acc = mfma_bf16(pa, cat(uh4, uh4), acc);
         acc = mfma_bf16(pa, cat(ul4, zero4), acc);
         const long orow = (tok0 + (long)t0 * H) * DV;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = gated ? silu_gate(acc[e], og[e]) : acc[e];
         // the chunk's rows: smaller than 4 GiB (the host checks the shape)
         const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
         if (n == KC) {
@@ -450,14 +472,42 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
     constexpr int NCP = DK / 2;
     const int c0 = 2 * (lane % NCP);
+    const int n = min(KC, T - j * KC);
+    const bool tf = (fuse & (kFuseSoftplus | kFuseGla)) != 0;
     f32x2 acc = {0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < KC; ++r) {
-      acc += *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      f32x2 la = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      if (tf) {
+        // the fused decay transform; padded tokens keep log a = 0
+        la = (r < n) ? f32x2{fused_log_alpha(la[0], fuse), fused_log_alpha(la[1], fuse)}
+                     : f32x2{0.f, 0.f};
+      }
+      acc += la;
       if (lane < NCP) *reinterpret_cast<f32x2 *>(&rw.G[r][c0]) = acc;
     }
     const unsigned long long bad = __ballot(acc[0] < -kMaxSpan || acc[1] < -kMaxSpan);
     if (lane == 0) rw.flag[0] = bad != 0ull;
+  };
+  // fused L2 normalisation of chunk j: 1/|q_r| and 1/|k_r|; lane = (row,
+  // matrix, half row)
+  auto norms = [&](int j) {
+    typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
+    const int r = lane & (KC - 1), m = (lane >> 4) & 1, h = lane >> 5;
+    const char *X = reinterpret_cast<const char *>(m ? &rw.K[r][0] : &rw.Q[r][0]) + h * DK;
+    float ss = 0.0f;
+#pragma unroll
+    for (int b = 0; b < DK / 16; ++b) {
+      const u32x4 w4 = *reinterpret_cast<const u32x4 *>(X + 16 * b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_bit_cast(float, w4[i] << 16);
+        const float hi = __builtin_bit_cast(float, w4[i] & 0xffff0000u);
+        ss += lo * lo + hi * hi;
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    if (lane < 32) rw.nrm[m][r] = rsqrtf(ss + kL2Eps);
   };
 
   // derived operands of chunk j: a work row is 64 lanes = (channel pair,
@@ -486,7 +536,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
     if (pw == 0) {
       if (lane < NCP) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
-      if (lane < KC) d.beta[lane] = rw.beta[lane];
+      if (lane < KC) d.beta[lane] = (lane < min(KC, T - j * KC)) ? fused_beta(rw.beta[lane], fuse) : 0.0f;
       if (lane == 0) d.flag[0] = exact;
     }
     const int rb0 = row_bound(dw), rb1 = row_bound(dw + 1);
@@ -506,10 +556,16 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const unsigned qb = *reinterpret_cast<const unsigned *>(&rw.Q[r][c0]);
       const float k0 = __builtin_bit_cast(float, kb << 16), k1 = __builtin_bit_cast(float, kb & 0xffff0000u);
       const float q0 = __builtin_bit_cast(float, qb << 16), q1 = __builtin_bit_cast(float, qb & 0xffff0000u);
-      const float e0 = __expf(g[0]), e1 = __expf(g[1]);
-      const float f0 = __expf(sh[0] - g[0]), f1 = __expf(sh[1] - g[1]);
+      float e0 = __expf(g[0]), e1 = __expf(g[1]);
+      float f0 = __expf(sh[0] - g[0]), f1 = __expf(sh[1] - g[1]);
+      float eq0 = e0, eq1 = e1;
+      if (fuse & kFuseL2) {
+        const float rq = rw.nrm[0][r], rk = rw.nrm[1][r];
+        eq0 *= rq; eq1 *= rq;
+        e0 *= rk; e1 *= rk; f0 *= rk; f1 *= rk;
+      }
       if constexpr (ERASE) put(d.Kh, d.Kl, r, k0 * e0, k1 * e1);   // K^ feeds only K^ S and A
-      put(d.Qh, d.Ql, r, q0 * e0, q1 * e1);
+      put(d.Qh, d.Ql, r, q0 * eq0, q1 * eq1);
       put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);
     }
     if (exact) {
@@ -525,7 +581,12 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             sp += (float)rw.Q[r][c] * ks;
           }
         }
-        if constexpr (ERASE) sm.xA[j & 1][s][r] = (s < r) ? -rw.beta[r] * sa : 0.0f;
+        if (fuse & kFuseL2) {
+          sa *= rw.nrm[1][r] * rw.nrm[1][s];
+          sp *= rw.nrm[0][r] * rw.nrm[1][s];
+        }
+        const float br = (r < min(KC, T - j * KC)) ? fused_beta(rw.beta[r], fuse) : 0.0f;
+        if constexpr (ERASE) sm.xA[j & 1][s][r] = (s < r) ? -br * sa : 0.0f;
         sm.xP[j & 1][s][r] = sp;
       }
     }
@@ -567,8 +628,13 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (nchunks > 2) issue_raw(2);
     wait_own(nchunks > 2);
   }
+  // the fused L2 norms run on a wave that only derives (or on the scores
+  // wave with four prep waves)
+  constexpr int PW_NORM = (NPW == 6) ? 4 : 2;
+  const bool l2 = (fuse & kFuseL2) && pw == PW_NORM;
   __syncthreads();
   if (pw == 1 && nchunks > 0) gsum(0);
+  if (l2 && nchunks > 0) norms(0);
   __syncthreads();
 
   for (int it = 0; it < nchunks + 2; ++it) {
@@ -581,6 +647,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     } else {
       const bool more = it < nchunks;
       if (pw == PW_V && more) issue_v(it);
+      if (l2 && it + 1 < nchunks) norms(it + 1);
       if (pw == 2 && it >= 1 && it - 1 < nchunks) scores(it - 1);
       if (it < nchunks) derive(it);
       if (pw == PW_V) wait_own(more);
@@ -589,14 +656,21 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 }
 
-template <int DK, int DVS, typename OutT, bool ERASE>
-hipError_t launch_kda(const ChunkArgs &a) {
+template <int DK, int DVS, typename OutT, bool ERASE, bool FUSED>
+hipError_t launch_kda_fused(const ChunkArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
-  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT, ERASE>), grid, block, 0, a.stream,
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT, ERASE, FUSED>), grid, block, 0, a.stream,
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
-                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H);
+                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H, a.fuse,
+                     (const bf16 *)a.out_gate);
   return hipGetLastError();
+}
+
+template <int DK, int DVS, typename OutT, bool ERASE>
+hipError_t launch_kda(const ChunkArgs &a) {
+  if (a.fuse != 0 || a.out_gate != nullptr) return launch_kda_fused<DK, DVS, OutT, ERASE, true>(a);
+  return launch_kda_fused<DK, DVS, OutT, ERASE, false>(a);
 }
 
 template <int DK, int DVS>

@@ -33,6 +33,7 @@ struct SmemSmall {
   float A[C][LC], P[C][LC];
   float U[C][LD];      // R, then U (in place)
   float beta[C];
+  float nrm[2][C];     // fused L2 normalisation: 1 / |q_r|, 1 / |k_r|
 };
 
 // q/k/v dtype and o dtype are runtime flags here: this path is about
@@ -47,7 +48,8 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
                        const void *__restrict__ v, const float *__restrict__ beta,
                        const float *__restrict__ log_alpha, const float *initial_state,
                        void *__restrict__ o, float *final_state, int B, int T, int H,
-                       bool in_bf16, bool out_bf16, bool erase) {
+                       bool in_bf16, bool out_bf16, bool erase, int fuse,
+                       const void *__restrict__ out_gate) {
   constexpr int NT = 256;
   __shared__ SmemSmall<D, C> sm;
   const int tid = threadIdx.x;
@@ -70,8 +72,8 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
         qv = load_in(q, row * D + c, in_bf16);
         kv = load_in(k, row * D + c, in_bf16);
         vv = load_in(v, row * D + c, in_bf16);
-        if (GATE == kGateScalar) la = log_alpha[row];
-        if (GATE == kGateChannel) la = log_alpha[row * D + c];
+        if (GATE == kGateScalar) la = fused_log_alpha(log_alpha[row], fuse);
+        if (GATE == kGateChannel) la = fused_log_alpha(log_alpha[row * D + c], fuse);
       }
       sm.Q[r][c] = qv;
       sm.K[r][c] = kv;
@@ -79,8 +81,25 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
       sm.G[r][c] = la;
     }
     for (int r = tid; r < C; r += NT)
-      sm.beta[r] = r < n ? beta[((long)bb * T + t0 + r) * H + hh] : 0.0f;
+      sm.beta[r] = r < n ? fused_beta(beta[((long)bb * T + t0 + r) * H + hh], fuse) : 0.0f;
     __syncthreads();
+    if (fuse & kFuseL2) {
+      // q, k rows scaled to unit norm (padded rows stay zero)
+      for (int i = tid; i < 2 * C; i += NT) {
+        const int r = i % C;
+        const float(*X)[SmemSmall<D, C>::LD] = i < C ? sm.Q : sm.K;
+        float ss = 0.f;
+        for (int c = 0; c < D; ++c) ss += X[r][c] * X[r][c];
+        sm.nrm[i / C][r] = rsqrtf(ss + kL2Eps);
+      }
+      __syncthreads();
+      for (int i = tid; i < C * D; i += NT) {
+        const int r = i / D, c = i % D;
+        sm.Q[r][c] *= sm.nrm[0][r];
+        sm.K[r][c] *= sm.nrm[1][r];
+      }
+      __syncthreads();
+    }
     // cumulative log decay down each channel (padded tokens carry 0)
     for (int c = tid; c < D; c += NT) {
       float acc = 0.f;
@@ -139,6 +158,7 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
       }
       for (int s = 0; s <= r; ++s) acc += sm.P[r][s] * sm.U[s][c];
       const long oi = (((long)bb * T + t0 + r) * H + hh) * D + c;
+      if (out_gate) acc = silu_gate(acc, load_in(out_gate, oi, in_bf16));
       if (out_bf16) ((bf16 *)o)[oi] = (bf16)acc;
       else ((float *)o)[oi] = acc;
     }
@@ -166,7 +186,7 @@ hipError_t by_gate(const ChunkArgs &a) {
 #define GDR_LAUNCH(G)                                                                          \
   hipLaunchKernelGGL((chunk_fwd_small_kernel<D, C, G>), grid, block, 0, a.stream, a.q, a.k,  \
                      a.v, a.beta, a.log_alpha, a.initial_state, a.o, a.final_state, a.B, a.T, \
-                     a.H, a.in_bf16, a.out_bf16, a.erase)
+                     a.H, a.in_bf16, a.out_bf16, a.erase, a.fuse, a.out_gate)
   if (a.gate == kGateNone) GDR_LAUNCH(kGateNone);
   else if (a.gate == kGateScalar) GDR_LAUNCH(kGateScalar);
   else GDR_LAUNCH(kGateChannel);

@@ -22,6 +22,28 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// Fused prologue / epilogue (gdr_fuse flags of the C ABI).
+enum Fuse { kFuseL2 = 1, kFuseBetaSigmoid = 2, kFuseSoftplus = 4, kFuseGla = 8 };
+constexpr float kL2Eps = 1e-6f;   // q, k <- x / sqrt(sum x^2 + eps)
+
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// softplus(x) = log(1 + e^x), without overflow for large x
+__device__ __forceinline__ float softplus_f(float x) {
+  return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x)));
+}
+// b from the beta input
+__device__ __forceinline__ float fused_beta(float b, int fuse) {
+  return (fuse & kFuseBetaSigmoid) ? sigmoid_f(b) : b;
+}
+// log a from the log_alpha input: -softplus(x), or GLA's sigmoid(x)^{1/16}
+__device__ __forceinline__ float fused_log_alpha(float x, int fuse) {
+  if (fuse & kFuseSoftplus) return -softplus_f(x);
+  if (fuse & kFuseGla) return -softplus_f(-x) * (1.0f / 16.0f);
+  return x;
+}
+// the SiLU output gate applied to an output value
+__device__ __forceinline__ float silu_gate(float o, float g) { return o * g * sigmoid_f(g); }
+
 // D += A(16x32) * B(32x16), bf16 operands, fp32 accumulate.  Lane l holds
 // A row (l & 15) and B column (l & 15), eight k values per lane (the same k
 // set for A and B, so any consistent k order gives the same product); the

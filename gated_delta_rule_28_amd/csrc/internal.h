@@ -11,8 +11,10 @@ struct RecurrentArgs {
   bool in_bf16, out_bf16;
   int gate;               // 0 none, 1 scalar, 2 channel
   bool erase;             // false: additive write, no erase term
+  int fuse;               // gdr_fuse flags
   const void *q, *k, *v;
   const float *beta, *log_alpha;
+  const void *out_gate;   // SiLU output gate (in_dtype) or nullptr
   float *state;
   void *o;
   hipStream_t stream;
@@ -23,8 +25,10 @@ struct ChunkArgs {
   bool in_bf16, out_bf16;
   int gate;
   bool erase;             // false: additive write, no erase term
+  int fuse;               // gdr_fuse flags
   const void *q, *k, *v;
   const float *beta, *log_alpha;
+  const void *out_gate;   // SiLU output gate (in_dtype) or nullptr
   const float *initial_state;
   void *o;
   float *final_state;

@@ -25,7 +25,8 @@ __global__ void __launch_bounds__(2 * DV)
 recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
                       const InT *__restrict__ v, const float *__restrict__ beta,
                       const float *__restrict__ log_alpha, float *__restrict__ state,
-                      OutT *__restrict__ o, bool erase) {
+                      OutT *__restrict__ o, bool erase, int fuse,
+                      const InT *__restrict__ out_gate) {
   constexpr int NT = 2 * DV;          // threads per state
   constexpr int C4 = DV / 4;          // float4 columns per row
   constexpr int RG = NT / C4;         // row groups (= 8)
@@ -40,6 +41,7 @@ recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
   __shared__ float s_k[DK], s_q[DK], s_la[DK];
   __shared__ float s_part[RG][2][DV];
   __shared__ float s_kq[RG];
+  __shared__ float s_nrm[2];          // fused L2 normalisation: 1 / |k|, 1 / |q|
 
   float *S = state + sid * (long)DK * DV;
   // issue the state loads first: they are the whole cost of the step.  The
@@ -54,12 +56,35 @@ recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
   for (int i = t; i < DK; i += NT) {
     s_k[i] = to_f32(k[sid * DK + i]);
     s_q[i] = to_f32(q[sid * DK + i]);
-    if (GATE == kGateChannel) s_la[i] = log_alpha[sid * DK + i];
+    if (GATE == kGateChannel) s_la[i] = fused_log_alpha(log_alpha[sid * DK + i], fuse);
   }
-  const float b = beta[sid];
+  const float b = fused_beta(beta[sid], fuse);
   float a_head = 1.0f;
-  if (GATE == kGateScalar) a_head = __expf(log_alpha[sid]);
+  if (GATE == kGateScalar) a_head = __expf(fused_log_alpha(log_alpha[sid], fuse));
   __syncthreads();
+  float rk = 1.0f, rq = 1.0f;
+  if (fuse & kFuseL2) {
+    // |k|^2 and |q|^2 by wave 0 (lane-strided sums, then a butterfly)
+    if (t < 64) {
+      float sk = 0.f, sq2 = 0.f;
+      for (int i = t; i < DK; i += 64) {
+        sk += s_k[i] * s_k[i];
+        sq2 += s_q[i] * s_q[i];
+      }
+#pragma unroll
+      for (int m = 32; m > 0; m >>= 1) {
+        sk += __shfl_xor(sk, m);
+        sq2 += __shfl_xor(sq2, m);
+      }
+      if (t == 0) {
+        s_nrm[0] = rsqrtf(sk + kL2Eps);
+        s_nrm[1] = rsqrtf(sq2 + kL2Eps);
+      }
+    }
+    __syncthreads();
+    rk = s_nrm[0];
+    rq = s_nrm[1];
+  }
 
   f32x4 p = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
   float kq = 0.f;
@@ -69,7 +94,7 @@ recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
     float a = a_head;
     if (GATE == kGateChannel) a = __expf(s_la[row]);
     s[i] *= a;                                   // S' = decayed state
-    const float kr = s_k[row], qr = s_q[row];
+    const float kr = s_k[row] * rk, qr = s_q[row] * rq;
     p += kr * s[i];
     sq += qr * s[i];
     kq += kr * qr;
@@ -101,12 +126,16 @@ recurrent_step_kernel(const InT *__restrict__ q, const InT *__restrict__ k,
   }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    const float kr = s_k[rg * R + i];
+    const float kr = s_k[rg * R + i] * rk;
     __builtin_nontemporal_store(s[i] + kr * d, reinterpret_cast<f32x4 *>(S + (long)(rg * R + i) * DV + 4 * c4));
   }
   if (rg == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[sid * DV + 4 * c4 + j] = from_f32<OutT>(st[j] + kqt * d[j]);
+    for (int j = 0; j < 4; ++j) {
+      float x = st[j] + kqt * d[j];
+      if (out_gate) x = silu_gate(x, to_f32(out_gate[sid * DV + 4 * c4 + j]));
+      o[sid * DV + 4 * c4 + j] = from_f32<OutT>(x);
+    }
   }
 }
 
@@ -115,7 +144,7 @@ static hipError_t launch_one(const RecurrentArgs &a) {
   dim3 grid((unsigned)((long)a.N * a.H)), block(2 * D);
   hipLaunchKernelGGL((recurrent_step_kernel<D, D, InT, OutT, GATE>), grid, block, 0, a.stream,
                      (const InT *)a.q, (const InT *)a.k, (const InT *)a.v, a.beta, a.log_alpha,
-                     a.state, (OutT *)a.o, a.erase);
+                     a.state, (OutT *)a.o, a.erase, a.fuse, (const InT *)a.out_gate);
   return hipGetLastError();
 }
 

@@ -72,6 +72,33 @@ typedef enum gdr_gate {
   GDR_NO_ERASE = 0x100
 } gdr_gate;
 
+/*
+ * Prologue and epilogue fused into gdr_chunk_fwd_ex and gdr_recurrent_step_ex
+ * (bit flags in `fuse`): the per-token transforms a layer applies around the
+ * recurrence, so the inputs can be passed as the projections produce them.
+ *   GDR_FUSE_QK_L2NORM    q, k <- x / sqrt(sum_i x_i^2 + 1e-6) per (token,
+ *                         head): the feature map on q and k of
+ *                         "线性注意力架构：机制、权衡与跨层路由", section 3,
+ *                         eqs. (7)-(8), taken as L2 normalisation
+ *   GDR_FUSE_BETA_SIGMOID beta holds a logit: b = 1 / (1 + e^{-beta}), b in
+ *                         (0, 1) (xhh.club digest, Q&A on Gated DeltaNet)
+ *   GDR_FUSE_DECAY_SOFTPLUS  log_alpha holds x: log a = -softplus(x), a in
+ *                         (0, 1)
+ *   GDR_FUSE_DECAY_GLA    log_alpha holds x: a = sigmoid(x)^{1/16},
+ *                         log a = -softplus(-x) / 16 (GLA's gate, xhh.club
+ *                         digest, Q&A on GLA's gate)
+ * (the two decay flags exclude each other and need a gate).  The fused
+ * epilogue is the SiLU output gate (diosapp tutorial, section 四): with
+ * `out_gate` non-NULL ([.., Dv], in_dtype, 16-byte aligned)
+ * o <- o * g * sigmoid(g), g = out_gate.
+ */
+typedef enum gdr_fuse {
+  GDR_FUSE_QK_L2NORM = 1,
+  GDR_FUSE_BETA_SIGMOID = 2,
+  GDR_FUSE_DECAY_SOFTPLUS = 4,
+  GDR_FUSE_DECAY_GLA = 8
+} gdr_fuse;
+
 /* ABI version of the loaded library (GDR_ABI_VERSION of the build). */
 int gdr_abi_version(void);
 
@@ -125,6 +152,22 @@ int gdr_chunk_fwd(int B, int T, int H, int Dk, int Dv, int chunk,
                   hipStream_t stream);
 
 /*
+ * gdr_chunk_fwd_ex -- gdr_chunk_fwd with the fused prologue and epilogue
+ * (`fuse` flags and `out_gate` [B, T, H, Dv] or NULL, as described above).
+ * With fuse = 0 and out_gate = NULL it is gdr_chunk_fwd.  Unknown flag bits,
+ * both decay flags, a decay flag without a gate or a misaligned out_gate
+ * return GDR_EINVAL.
+ */
+int gdr_chunk_fwd_ex(int B, int T, int H, int Dk, int Dv, int chunk,
+                     int in_dtype, int out_dtype, int gate, int fuse,
+                     const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_alpha,
+                     const void *out_gate,
+                     const float *initial_state,
+                     void *o, float *final_state,
+                     hipStream_t stream);
+
+/*
  * gdr_recurrent_step -- one decode step: a single new token for each of N
  * independent sequences, with the fp32 state updated IN PLACE (the
  * constant-size memory that replaces the KV cache; diosapp tutorial,
@@ -146,6 +189,18 @@ int gdr_recurrent_step(int N, int H, int Dk, int Dv,
                        const float *beta, const float *log_alpha,
                        float *state, void *o,
                        hipStream_t stream);
+
+/*
+ * gdr_recurrent_step_ex -- gdr_recurrent_step with the fused prologue and
+ * epilogue (`fuse` flags and `out_gate` [N, H, Dv] or NULL).
+ */
+int gdr_recurrent_step_ex(int N, int H, int Dk, int Dv,
+                          int in_dtype, int out_dtype, int gate, int fuse,
+                          const void *q, const void *k, const void *v,
+                          const float *beta, const float *log_alpha,
+                          const void *out_gate,
+                          float *state, void *o,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

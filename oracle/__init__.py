@@ -16,6 +16,8 @@ closed_forms.py  independent formulations used only to pin the recurrence:
 chunked.py       a plain fp64 chunkwise (WY / triangular-solve) evaluation,
                  pinned against the recurrence; it checks the block algebra
                  the GPU kernels are built on, never the kernels themselves.
+fused.py         the prologue / epilogue activations (q, k normalisation,
+                 sigmoid, softplus, GLA's gate, SiLU output gate).
 
 Every function works in float64 on numpy arrays.  Inputs that arrive in a
 lower precision (bf16, fp32) are upcast exactly before any arithmetic.
@@ -32,6 +34,7 @@ from .closed_forms import (
     scalar_recurrence_d1,
 )
 from .chunked import chunked_gated_delta
+from . import fused
 
 __all__ = [
     "GATES",

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["gdr_abi_version", "gdr_chunk_fwd", "gdr_recurrent_step",
-                     "gdr_status_str"], names
+    assert names == ["gdr_abi_version", "gdr_chunk_fwd", "gdr_chunk_fwd_ex",
+                     "gdr_recurrent_step", "gdr_recurrent_step_ex", "gdr_status_str"], names
     assert set(names) == set(_abi.SIGNATURES)
 
 
@@ -115,3 +115,31 @@ def test_recurrent_step_rejects(kw, want):
 
 def test_recurrent_step_empty_is_a_no_op():
     assert step(N=0, q=None, k=None, v=None, state=None, o=None) == _abi.GDR_OK
+
+
+def chunk_ex(**kw):
+    a = dict(B=1, T=8, H=1, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+             out_dtype=_abi.GDR_F32, gate=_abi.GDR_GATE_SCALAR, fuse=0, q=FAKE, k=FAKE, v=FAKE,
+             beta=FAKE, log_alpha=FAKE, out_gate=None, initial_state=None, o=FAKE,
+             final_state=None, stream=None)
+    a.update(kw)
+    return _abi.gdr_chunk_fwd_ex(**a)
+
+
+def step_ex(**kw):
+    a = dict(N=1, H=1, Dk=128, Dv=128, in_dtype=_abi.GDR_BF16, out_dtype=_abi.GDR_F32,
+             gate=_abi.GDR_GATE_SCALAR, fuse=0, q=FAKE, k=FAKE, v=FAKE, beta=FAKE,
+             log_alpha=FAKE, out_gate=None, state=FAKE, o=FAKE, stream=None)
+    a.update(kw)
+    return _abi.gdr_recurrent_step_ex(**a)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fuse=16),                                                     # unknown flag bit
+    dict(fuse=_abi.GDR_FUSE_DECAY_SOFTPLUS | _abi.GDR_FUSE_DECAY_GLA), # two decay transforms
+    dict(fuse=_abi.GDR_FUSE_DECAY_GLA, gate=_abi.GDR_GATE_NONE, log_alpha=None),  # no gate
+    dict(out_gate=FAKE + 2),                                           # misaligned out_gate
+])
+def test_fused_prologue_validation(kw):
+    assert chunk_ex(**kw) == _abi.GDR_EINVAL
+    assert step_ex(**kw) == _abi.GDR_EINVAL
