@@ -17,7 +17,8 @@ of the chunk kernel (HBM-bound: algorithmic bytes / mean kernel time from HIP
 events on the launch stream / 8 TB/s; measured HBM traffic from the committed
 counter summary when it was taken on the current kernel source), the fp64
 oracle timed on the host cores, and secondary lines: bf16 output, the KDA
-workload kda_bf16_b2h32t8192, and the batched decode step (256 sequences x 32
+workload kda_bf16_b2h32t8192, both shapes without the erase term and with the
+fused prologue / output gate, and the batched decode step (256 sequences x 32
 heads, 128 consecutive steps, eager and as one HIP graph).
 """
 
@@ -86,12 +87,15 @@ def read_traffic(kernel, workload, root=PROFILES):
 # algorithmic counts
 
 
-def chunk_alg_bytes(w, out_bytes=4):
+def chunk_alg_bytes(w, out_bytes=4, out_gate=False):
     """Single-pass minimum HBM bytes of one chunk_fwd call (zero initial
-    state, final state written): q, k, v in, beta and log alpha in, o out."""
+    state, final state written): q, k, v in, beta and log alpha in, o out
+    (and the output gate in, when it is fused)."""
     th = w.B * w.T * w.H
     in_b = 2 if w.in_dtype == "bf16" else 4
     per_th = in_b * (2 * w.Dk + w.Dv) + 4
+    if out_gate:
+        per_th += in_b * w.Dv
     if w.gate == "scalar":
         per_th += 4
     elif w.gate == "channel":
@@ -152,19 +156,45 @@ def time_launches(torch, fn, steps, warmup, settle_s=0.0):
     return wall, per
 
 
-def chunk_setup(torch, gdr, W, w, out_dtype, erase=True):
+def fused_inputs(torch, inp, w):
+    """Pre-activations whose fused transforms give back the workload's own
+    b and decay: beta as the logit of b, log_alpha as x with
+    -softplus(x) = log a, q and k rows rescaled (the L2 normalisation undoes
+    it), and a seeded bf16 output gate."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    out = dict(inp)
+    for name in ("q", "k"):
+        x = inp[name].float()
+        scale = 0.5 + 1.5 * torch.rand(*x.shape[:-1], 1, device="cuda", generator=g)
+        out[name] = (x * scale).to(inp[name].dtype)
+    b = inp["beta"].clamp(1e-4, 1.0 - 1e-4)
+    out["beta"] = torch.log(b / (1.0 - b))
+    if inp["log_alpha"] is not None:
+        out["log_alpha"] = torch.log(torch.expm1(-inp["log_alpha"].clamp(max=-1e-6)))
+    out["out_gate"] = torch.randn(w.B, w.T, w.H, w.Dv, device="cuda", generator=g).to(inp["q"].dtype)
+    return out
+
+
+def chunk_setup(torch, gdr, W, w, out_dtype, erase=True, fused=False):
     inp = W.make_workload_inputs(w, seed=0, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.Dv, device="cuda", dtype=out_dtype)
     S = torch.empty(w.B, w.H, w.Dk, w.Dv, device="cuda", dtype=torch.float32)
+    kw = {}
+    if fused:
+        inp = fused_inputs(torch, inp, w)
+        kw = dict(qk_l2norm=True, beta_sigmoid=True, out_gate=inp["out_gate"],
+                  decay="softplus" if inp["log_alpha"] is not None else None)
 
     def step():
         gdr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None,
-                      chunk=w.chunk, out_dtype=out_dtype, o=o, final_state=S, erase=erase)
+                      chunk=w.chunk, out_dtype=out_dtype, o=o, final_state=S, erase=erase, **kw)
     return step, o, S
 
 
-def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=True):
-    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype, erase)
+def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=True,
+               fused=False):
+    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype, erase, fused)
     wall, per = time_launches(torch, step, steps, warmup, settle_s)
     if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())):
         raise RuntimeError(f"non-finite output in the timed run of {w.name}")
@@ -172,11 +202,11 @@ def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=T
     kern = KERNEL_OF_GATE[w.gate]
     C = KERNEL_CHUNK[w.gate]
     mean_ms = statistics.fmean(per)
-    alg_b = chunk_alg_bytes(w, out_b)
+    alg_b = chunk_alg_bytes(w, out_b, out_gate=fused)
     alg_f = chunk_alg_flops(w, C, erase)
     achieved = alg_b / (mean_ms * 1e-3) / 1e9
-    # counter traffic is taken for the erasing fp32-output launches only
-    traffic = read_traffic(kern, w.name) if out_b == 4 and erase else None
+    # counter traffic is taken for the erasing, unfused fp32-output launches only
+    traffic = read_traffic(kern, w.name) if out_b == 4 and erase and not fused else None
     return {
         "workload": w.name, "tokens": w.B * w.T, "wall_s": wall, "steps": steps,
         "ms_per_step": 1e3 * wall / steps,
@@ -449,6 +479,15 @@ def main(argv=None):
                                            "kernel_ms", "roofline", "mfma_alg")}
             rec[key]["unit"] = "tokens/s"
             rec[key]["variant"] = "no erase term (S = a S + b k v^T)"
+        # the fused prologue (q, k L2 normalisation, sigmoid b, softplus
+        # decay) and SiLU output gate through the same kernels
+        for key, wl in (("fused", w), ("kda_fused", W.by_name("kda_bf16_b2h32t8192"))):
+            ln = chunk_line(torch, gdr, W, wl, nb, 2, torch.float32, args.settle_s, fused=True)
+            rec[key] = {k: ln[k] for k in ("workload", "value", "kernel", "kernel_chunk",
+                                           "kernel_ms", "roofline", "mfma_alg")}
+            rec[key]["unit"] = "tokens/s"
+            rec[key]["variant"] = ("fused prologue (q, k L2 norm, sigmoid b, softplus decay) "
+                                   "and SiLU output gate")
         rec["decode"] = decode_line(torch, gdr, W, W.DECODE, settle_s=args.settle_s)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(W, w)

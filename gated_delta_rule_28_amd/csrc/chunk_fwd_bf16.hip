@@ -254,24 +254,40 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     };
     split_state();
 
+    // the fused output gate of this lane's O values, loaded one chunk ahead
+    // (the state waves are the serial path: a load used in the same chunk
+    // would expose its latency every chunk) and turned into the factor
+    // g sigmoid(g) (1 without a gate) before the O products, which are then
+    // only multiplied: a branch between an MFMA and the read of its result
+    // can hide the wait states that read needs
+    // The loads are unconditional: without a gate, or past the last chunk,
+    // the descriptor is empty and they read zeros without touching memory.
+    f32x4 og[2] = {};
+    unsigned og_next[2][4] = {};
+    auto load_gate = [&](int c) {
+      const bool valid = gated && c < nchunks;
+      const int n = valid ? min(C, T - c * C) : 1;
+      const long orow = valid ? (tok0 + (long)c * C * H) * DV : 0;
+      const rsrc_t rg = make_rsrc32(out_gate + orow,
+                                    valid ? 2u * ((unsigned)(n - 1) * H * DV + DV) : 0u);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          og_next[rb][e] = buf_ld_u16(rg, 2 * (ooff[rb][e] / (int)sizeof(OutT)));
+    };
+
     for (int it = 0; it < nchunks + 1; ++it) {
       const int s = it - 1;            // chunk of this iteration
       f32x4 QS[2];
       bf16x8 Uh, Ul, Wh, Wl;
-      // the fused output gate of this lane's O values, loaded before the
-      // chunk's products (the gate is applied by a select after them: a
-      // branch between an MFMA and the read of its result can hide the
-      // wait states that read needs)
-      f32x4 og[2] = {};
-      if (gated && s >= 0) {
-        const int n = min(C, T - s * C);
-        const long orow = (tok0 + (long)s * C * H) * DV;
-        const rsrc_t rg = make_rsrc32(out_gate + orow, 2u * ((unsigned)(n - 1) * H * DV + DV));
+      if constexpr (FUSED) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            og[rb][e] = buf_ld_bf16(rg, 2 * (ooff[rb][e] / (int)sizeof(OutT)));
+            og[rb][e] = gated ? silu_gate(1.0f, bf16_bits_to_f32(og_next[rb][e])) : 1.0f;
+        load_gate(it);
       }
       // ---- K S, Q S, R = V - diag(gam) K S, U = T' R ----
       if (s >= 0) {
@@ -372,8 +388,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(ph, Uh, acc);
           acc = mfma_bf16(pl, Uh, acc);
           acc = mfma_bf16(ph, Ul, acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = gated ? silu_gate(acc[e], og[rb][e]) : acc[e];
+          if constexpr (FUSED) acc = acc * og[rb];
           // lane holds O rows 16 rb + 4 lg + e of column col0 + lr: stored
           // straight from the accumulator (16 lanes write 16 adjacent values
           // of a row); rows past the end of the sequence are not written

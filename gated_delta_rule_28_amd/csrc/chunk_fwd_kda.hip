@@ -50,6 +50,8 @@
 //   state:  chunk i-2
 // Raw inputs live four iterations (DMA to derivation), derived operands
 // three, v three, T' and P two.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -196,20 +198,31 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     };
     split_state();
 
+    // the fused output gate of this lane's O values, loaded one chunk ahead
+    // (the state waves are the serial path: a load used in the same chunk
+    // would expose its latency every chunk) and turned into the factor
+    // g sigmoid(g) (1 without a gate) before the O products, which are then
+    // only multiplied: a branch between an MFMA and the read of its result
+    // can hide the wait states that read needs
+    // The loads are unconditional: without a gate, or outside the chunks,
+    // the descriptor is empty and they read zeros without touching memory.
     const bool gated = out_gate != nullptr;
+    f32x4 og = {};
+    unsigned og_next[4] = {};
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;
-      // the fused output gate of this lane's O values, loaded before the
-      // chunk's products (the gate is applied by a select after them: a
-      // branch between an MFMA and the read of its result can hide the
-      // wait states that read needs)
-      f32x4 og = {};
-      if (gated && s >= 0) {
-        const int n = min(KC, T - s * KC);
-        const rsrc_t rg = make_rsrc32(out_gate + (tok0 + (long)s * KC * H) * DV,
-                                      2u * ((unsigned)(n - 1) * H * DV + DV));
+      if constexpr (FUSED) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) og[e] = buf_ld_bf16(rg, 2 * (ooff[e] / (int)sizeof(OutT)));
+        for (int e = 0; e < 4; ++e)
+          og[e] = gated ? silu_gate(1.0f, bf16_bits_to_f32(og_next[e])) : 1.0f;
+        const int c = s + 1;
+        const bool valid = gated && c >= 0 && c < nchunks;
+        const int n = valid ? min(KC, T - c * KC) : 1;
+        const long orow = valid ? (tok0 + (long)c * KC * H) * DV : 0;
+        const rsrc_t rg = make_rsrc32(out_gate + orow,
+                                      valid ? 2u * ((unsigned)(n - 1) * H * DV + DV) : 0u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) og_next[e] = buf_ld_u16(rg, 2 * (ooff[e] / (int)sizeof(OutT)));
       }
       if (s >= 0) {
         const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));
@@ -272,8 +285,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         acc = mfma_bf16(pa, cat(uh4, uh4), acc);
         acc = mfma_bf16(pa, cat(ul4, zero4), acc);
         const long orow = (tok0 + (long)t0 * H) * DV;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = gated ? silu_gate(acc[e], og[e]) : acc[e];
+        if constexpr (FUSED) acc = acc * og;
         // the chunk's rows: smaller than 4 GiB (the host checks the shape)
         const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
         if (n == KC) {
@@ -472,32 +484,96 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
     constexpr int NCP = DK / 2;
     const int c0 = 2 * (lane % NCP);
-    const int n = min(KC, T - j * KC);
-    const bool tf = (fuse & (kFuseSoftplus | kFuseGla)) != 0;
     f32x2 acc = {0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < KC; ++r) {
-      f32x2 la = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
-      if (tf) {
-        // the fused decay transform; padded tokens keep log a = 0
-        la = (r < n) ? f32x2{fused_log_alpha(la[0], fuse), fused_log_alpha(la[1], fuse)}
-                     : f32x2{0.f, 0.f};
-      }
-      acc += la;
+      acc += *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
       if (lane < NCP) *reinterpret_cast<f32x2 *>(&rw.G[r][c0]) = acc;
     }
     const unsigned long long bad = __ballot(acc[0] < -kMaxSpan || acc[1] < -kMaxSpan);
     if (lane == 0) rw.flag[0] = bad != 0ull;
   };
-  // fused L2 normalisation of chunk j: 1/|q_r| and 1/|k_r|; lane = (row,
-  // matrix, half row)
-  auto norms = [&](int j) {
+  // with a fused decay transform (two transcendentals per element) the
+  // transform and the sums are shared by NGW waves: wave gi takes channel
+  // pairs PPW gi .. +PPW-1, a lane one pair and RPG consecutive rows, the
+  // RGN row groups of a pair in adjacent lanes, so that the scan of the
+  // group totals is a few DPP row shifts; each wave flags its own channels
+  // in flag[gi]
+  constexpr int NGW = (kda_npw<DVS>() == 6) ? 4 : 2;
+  constexpr int PPW = (DK / 2) / NGW, RGN = 64 / PPW, RPG = KC / RGN;
+  static_assert(PPW * RGN == 64 && RGN * RPG == KC && RGN <= 16, "shared decay sums");
+  auto row_shr = [](float x, auto n) {   // x of the lane n below in the 16-lane row
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), 0x110 + decltype(n)::value, 0xF, 0xF, true));
+  };
+  auto gsum_fused = [&](int j, int gi) {
     typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
-    const int r = lane & (KC - 1), m = (lane >> 4) & 1, h = lane >> 5;
-    const char *X = reinterpret_cast<const char *>(m ? &rw.K[r][0] : &rw.Q[r][0]) + h * DK;
+    const int p = lane / RGN, rg = lane % RGN;
+    const int c0 = 2 * (gi * PPW + p);
+    const int n = min(KC, T - j * KC);
+    f32x2 part[RPG];
+    f32x2 run = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = rg * RPG + i;
+      const f32x2 x = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      // padded tokens keep log a = 0
+      run += (r < n) ? f32x2{fused_log_alpha(x[0], fuse), fused_log_alpha(x[1], fuse)}
+                     : f32x2{0.f, 0.f};
+      part[i] = run;
+    }
+    f32x2 incl = run;
+    if constexpr (RGN > 1) {
+      const f32x2 y = {row_shr(incl[0], std::integral_constant<int, 1>{}),
+                       row_shr(incl[1], std::integral_constant<int, 1>{})};
+      if (rg >= 1) incl += y;
+    }
+    if constexpr (RGN > 2) {
+      const f32x2 y = {row_shr(incl[0], std::integral_constant<int, 2>{}),
+                       row_shr(incl[1], std::integral_constant<int, 2>{})};
+      if (rg >= 2) incl += y;
+    }
+    if constexpr (RGN > 4) {
+      const f32x2 y = {row_shr(incl[0], std::integral_constant<int, 4>{}),
+                       row_shr(incl[1], std::integral_constant<int, 4>{})};
+      if (rg >= 4) incl += y;
+    }
+    static_assert(RGN <= 8, "three scan steps");
+    f32x2 excl = {row_shr(incl[0], std::integral_constant<int, 1>{}),
+                  row_shr(incl[1], std::integral_constant<int, 1>{})};
+    if (rg == 0) excl = f32x2{0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPG; ++i)
+      *reinterpret_cast<f32x2 *>(&rw.G[rg * RPG + i][c0]) = part[i] + excl;
+    const unsigned long long bad =
+        __ballot(rg == RGN - 1 && (incl[0] < -kMaxSpan || incl[1] < -kMaxSpan));
+    if (lane == 0) rw.flag[gi] = bad != 0ull;
+  };
+  const bool shared_gsum = FUSED && (fuse & (kFuseSoftplus | kFuseGla)) != 0;
+  // index of this wave among the NGW summing waves, or -1
+  const int gsum_idx = (kda_npw<DVS>() == 6) ? (pw < 2 ? pw : (pw >= 4 ? pw - 2 : -1))
+                                             : (pw < 2 ? pw : -1);
+  auto sums = [&](int j) {
+    if (shared_gsum) {
+      if (gsum_idx >= 0) gsum_fused(j, gsum_idx);
+    } else if (pw == 1) {
+      gsum(j);
+    }
+  };
+
+  // fused L2 normalisation of chunk j: 1/|q_r| and 1/|k_r|, shared by the
+  // NGW summing waves: wave gi takes 32 / NGW of the (matrix, row) pairs,
+  // LPR lanes to a row, and sums across those lanes
+  constexpr int NRM_R = 2 * KC / NGW, LPR = 64 / NRM_R, CPL = DK / LPR;
+  static_assert(NRM_R * LPR == 64 && CPL % 8 == 0, "shared norms");
+  auto norms = [&](int j, int gi) {
+    typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
+    const int mr = gi * NRM_R + lane / LPR;          // (matrix, row) pair
+    const int m = mr / KC, r = mr % KC, part = lane % LPR;
+    const char *X = reinterpret_cast<const char *>(m ? &rw.K[r][0] : &rw.Q[r][0]) + 2 * CPL * part;
     float ss = 0.0f;
 #pragma unroll
-    for (int b = 0; b < DK / 16; ++b) {
+    for (int b = 0; b < CPL / 8; ++b) {
       const u32x4 w4 = *reinterpret_cast<const u32x4 *>(X + 16 * b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -506,8 +582,9 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         ss += lo * lo + hi * hi;
       }
     }
-    ss += __shfl_xor(ss, 32);
-    if (lane < 32) rw.nrm[m][r] = rsqrtf(ss + kL2Eps);
+#pragma unroll
+    for (int d = 1; d < LPR; d <<= 1) ss += __shfl_xor(ss, d);
+    if (part == 0) rw.nrm[m][r] = rsqrtf(ss + kL2Eps);
   };
 
   // derived operands of chunk j: a work row is 64 lanes = (channel pair,
@@ -531,7 +608,12 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   auto derive = [&](int j) {
     const typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
     typename SM::Der &d = *at_off(&sm.der[0], slot_off(j % NDER, (int)sizeof(typename SM::Der)));
-    const int exact = __builtin_amdgcn_readfirstlane(rw.flag[0]);
+    int fl = rw.flag[0];
+    if (shared_gsum) {
+#pragma unroll
+      for (int i = 1; i < NGW; ++i) fl |= rw.flag[i];
+    }
+    const int exact = __builtin_amdgcn_readfirstlane(fl);
     const int cp = lane % NCP, c0 = 2 * cp;
     const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
     if (pw == 0) {
@@ -628,26 +710,25 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     if (nchunks > 2) issue_raw(2);
     wait_own(nchunks > 2);
   }
-  // the fused L2 norms run on a wave that only derives (or on the scores
-  // wave with four prep waves)
-  constexpr int PW_NORM = (NPW == 6) ? 4 : 2;
-  const bool l2 = (fuse & kFuseL2) && pw == PW_NORM;
+  const bool l2 = (fuse & kFuseL2) && gsum_idx >= 0;
   __syncthreads();
-  if (pw == 1 && nchunks > 0) gsum(0);
-  if (l2 && nchunks > 0) norms(0);
+  if (nchunks > 0) sums(0);
+  if (l2 && nchunks > 0) norms(0, gsum_idx);
   __syncthreads();
 
   for (int it = 0; it < nchunks + 2; ++it) {
     if (pw < 2) {
       const bool more = it + 3 < nchunks;
       if (more) issue_raw(it + 3);
-      if (pw == 1 && it + 1 < nchunks) gsum(it + 1);
+      if (it + 1 < nchunks) sums(it + 1);
+      if (l2 && it + 1 < nchunks) norms(it + 1, gsum_idx);
       if (it < nchunks) derive(it);
       wait_own(more);
     } else {
       const bool more = it < nchunks;
       if (pw == PW_V && more) issue_v(it);
-      if (l2 && it + 1 < nchunks) norms(it + 1);
+      if (l2 && it + 1 < nchunks) norms(it + 1, gsum_idx);
+      if (shared_gsum && it + 1 < nchunks) sums(it + 1);
       if (pw == 2 && it >= 1 && it - 1 < nchunks) scores(it - 1);
       if (it < nchunks) derive(it);
       if (pw == PW_V) wait_own(more);

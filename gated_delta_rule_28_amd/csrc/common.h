@@ -26,10 +26,16 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 enum Fuse { kFuseL2 = 1, kFuseBetaSigmoid = 2, kFuseSoftplus = 4, kFuseGla = 8 };
 constexpr float kL2Eps = 1e-6f;   // q, k <- x / sqrt(sum x^2 + eps)
 
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
-// softplus(x) = log(1 + e^x), without overflow for large x
+// The activations use the hardware exp2 / log2 / reciprocal (about one ulp
+// each): they run per element inside the chunk pipelines, where the
+// library's log1p and the IEEE divide cost more than the rest of a stage.
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}), without
+// overflow for large |x| (the log's argument lies in (1, 2])
 __device__ __forceinline__ float softplus_f(float x) {
-  return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x)));
+  return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x)));
 }
 // b from the beta input
 __device__ __forceinline__ float fused_beta(float b, int fuse) {
@@ -37,9 +43,11 @@ __device__ __forceinline__ float fused_beta(float b, int fuse) {
 }
 // log a from the log_alpha input: -softplus(x), or GLA's sigmoid(x)^{1/16}
 __device__ __forceinline__ float fused_log_alpha(float x, int fuse) {
-  if (fuse & kFuseSoftplus) return -softplus_f(x);
-  if (fuse & kFuseGla) return -softplus_f(-x) * (1.0f / 16.0f);
-  return x;
+  if (!(fuse & (kFuseSoftplus | kFuseGla))) return x;
+  // one softplus either way: log sigmoid(x)^{1/16} = -softplus(-x) / 16
+  const bool gla = (fuse & kFuseGla) != 0;
+  const float sp = softplus_f(gla ? -x : x);
+  return gla ? sp * (-1.0f / 16.0f) : -sp;
 }
 // the SiLU output gate applied to an output value
 __device__ __forceinline__ float silu_gate(float o, float g) { return o * g * sigmoid_f(g); }

@@ -136,9 +136,13 @@ __device__ __forceinline__ rsrc_t make_rsrc32(const void *base, unsigned bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-__device__ __forceinline__ float buf_ld_bf16(rsrc_t r, int off) {
-  const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  return __builtin_bit_cast(float, (unsigned)u << 16);
+// a bf16 value, left as its 16 bits (converted where it is used, so that a
+// load issued ahead is not waited for at once)
+__device__ __forceinline__ unsigned buf_ld_u16(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned u) {
+  return __builtin_bit_cast(float, u << 16);
 }
 __device__ __forceinline__ void buf_st1(float x, rsrc_t r, int off) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);
