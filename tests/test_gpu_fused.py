@@ -188,3 +188,40 @@ def test_recurrent_step_fused(gate, decay, in_dtype, D):
         o_ref = F.silu_gate(o_ref, np64(og[t]))
         assert rel_err(np64(o), o_ref) <= F32_TOL, t
     assert rel_err(np64(state), S_ref) <= F32_TOL
+
+
+@pytest.mark.parametrize("T", [1, 17, 33])
+@pytest.mark.parametrize("D,gate,decay", [(128, "none", None), (128, "scalar", "softplus"),
+                                          (64, "scalar", "gla"), (128, "channel", "softplus"),
+                                          (64, "channel", "gla")])
+def test_chunk_fused_ragged_tails(T, D, gate, decay):
+    # a single partial chunk, and a last chunk of one token: the padded
+    # tokens' transformed beta and decay (nonzero for a zero input) must not
+    # leak into the state; no initial state
+    say("chunk fused ragged", T, D, gate, decay)
+    inp = raw_inputs(2, T, 3, D, gate, "bf16", seed=T + D, decay=decay)
+    inp["initial_state"] = None
+    o, S = gdr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None,
+                         qk_l2norm=True, beta_sigmoid=True, decay=decay, out_gate=inp["out_gate"])
+    torch.cuda.synchronize()
+    q, k, b, la = F.prologue(np64(inp["q"]), np64(inp["k"]), np64(inp["beta"]),
+                             np64(inp["log_alpha"]), qk_l2norm=True, beta_sigmoid=True,
+                             decay=decay)
+    o_ref, S_ref = gated_delta_recurrence(q, k, np64(inp["v"]), b, la, None)
+    o_ref = F.silu_gate(o_ref, np64(inp["out_gate"]))
+    eo, es = rel_err(np64(o), o_ref), rel_err(np64(S), S_ref)
+    say("max|err|/rms o", eo, "state", es)
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+def test_chunk_fused_empty_sequence_keeps_the_state():
+    # T = 0 with every option: the final state is the initial state
+    inp = raw_inputs(1, 1, 2, 128, "scalar", "bf16", seed=5, decay="softplus")
+    empty = {k2: (v2[:, :0] if k2 in ("q", "k", "v", "beta", "log_alpha", "out_gate") else v2)
+             for k2, v2 in inp.items()}
+    o, S = gdr.chunk_fwd(empty["q"], empty["k"], empty["v"], empty["beta"], empty["log_alpha"],
+                         inp["initial_state"], qk_l2norm=True, beta_sigmoid=True,
+                         decay="softplus", out_gate=empty["out_gate"])
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0
+    assert torch.equal(S, inp["initial_state"])
