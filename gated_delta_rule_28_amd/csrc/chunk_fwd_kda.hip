@@ -596,13 +596,17 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int NDW = NPW - 1;                 // deriving waves
   constexpr int NCP = DK / 2, TPR = 64 / NCP, NRW = KC / TPR;
   const int dw = pw < 3 ? pw : pw - 1;         // index among the deriving waves
+  // With the decay sums shared (fused decay transform) the summing waves
+  // take fewer rows and the scores wave more (measured on the KDA shape).
   auto row_bound = [&](int w) {
     if constexpr (NPW == 6) {
       constexpr int b[6] = {0, 4, 7, 9, 13, 16};
-      return b[w] * NRW / 16;
+      constexpr int bs[6] = {0, 3, 5, 10, 13, 16};
+      return (shared_gsum ? bs[w] : b[w]) * NRW / 16;
     } else {
       constexpr int b[4] = {0, 7, 12, 16};
-      return b[w] * NRW / 16;
+      constexpr int bs[4] = {0, 3, 7, 16};
+      return (shared_gsum ? bs[w] : b[w]) * NRW / 16;
     }
   };
   auto derive = [&](int j) {
