@@ -225,3 +225,24 @@ def test_chunk_fused_empty_sequence_keeps_the_state():
     torch.cuda.synchronize()
     assert o.shape[1] == 0
     assert torch.equal(S, inp["initial_state"])
+
+
+@pytest.mark.parametrize("B,H", [(2, 3), (8, 16)])
+@pytest.mark.parametrize("decay", ["softplus", "gla"])
+def test_chunk_fused_kda_strong_decay(B, H, decay):
+    # per-token log decays down to about -15 after the fused transform, so
+    # that some chunks take the exact in-chunk path; the decay sums are
+    # shared by several waves (six prep waves at B=2 H=3, four at B=8 H=16),
+    # each flagging its own channels
+    say("chunk fused kda strong decay", B, H, decay)
+    inp = raw_inputs(B, 70, H, 128, "channel", "bf16", seed=B + H, decay=decay)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(B * H)
+    x = torch.randn(B, 70, H, 128, device=DEV, generator=g)
+    # softplus: log a = -softplus(x), x ~ N(3, 5); GLA: log a = -softplus(-x)/16
+    inp["log_alpha"] = 3.0 + 5.0 * x if decay == "softplus" else -40.0 + 60.0 * x
+    check(inp, BF16_TOL, decay=decay)
+    la = F.log_decay(np64(inp["log_alpha"]), decay)
+    # the case is only meaningful if some chunk crosses the exact-path bound
+    sums = np.add.reduceat(la, np.arange(0, 70, 16), axis=1)
+    assert sums.min() < -64.0
