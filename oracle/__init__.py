@@ -18,6 +18,8 @@ chunked.py       a plain fp64 chunkwise (WY / triangular-solve) evaluation,
                  the GPU kernels are built on, never the kernels themselves.
 fused.py         the prologue / epilogue activations (q, k normalisation,
                  sigmoid, softplus, GLA's gate, SiLU output gate).
+backward.py      reverse-mode gradients of the token recurrence (dq, dk,
+                 dv, dbeta, dlog_alpha, dS0), pinned by finite differences.
 
 Every function works in float64 on numpy arrays.  Inputs that arrive in a
 lower precision (bf16, fp32) are upcast exactly before any arithmetic.
@@ -35,6 +37,7 @@ from .closed_forms import (
 )
 from .chunked import chunked_gated_delta
 from . import fused
+from .backward import gated_delta_backward
 
 __all__ = [
     "GATES",
@@ -44,4 +47,5 @@ __all__ = [
     "unrolled_transition_sum",
     "scalar_recurrence_d1",
     "chunked_gated_delta",
+    "gated_delta_backward",
 ]
