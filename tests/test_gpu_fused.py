@@ -156,7 +156,7 @@ def test_chunk_fused_fp32(gate, decay, D):
 
 @pytest.mark.parametrize("gate,decay", [("none", None), ("scalar", "softplus"),
                                         ("channel", "gla")])
-@pytest.mark.parametrize("in_dtype,D", [("bf16", 128), ("f32", 32)])
+@pytest.mark.parametrize("in_dtype,D", [("bf16", 128), ("f32", 32), ("f32", 16)])
 def test_recurrent_step_fused(gate, decay, in_dtype, D):
     say("recurrent_step fused", gate, decay, in_dtype, D)
     N, H, steps = 4, 3, 4
