@@ -694,17 +694,26 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     In &bf = *at_off(&sm.in[0], slot_off(j % NIN, (int)sizeof(In)));
     const char *X = reinterpret_cast<const char *>(pw == 1 ? &bf.K[0][0] : &bf.Q[0][0]);
     const int r = lane & (C - 1), h = lane / C;
-    float ss = 0.0f;
+    // the two lanes of a row take complementary halves of its blocks, in an
+    // order rotated by a function of the row that is distinct over the 16
+    // lanes of one ds_read_b128 pass (rows 256 bytes apart would otherwise
+    // all hit the same banks)
+    const int rot = (r & 3) + 4 * ((r >> 3) & 3);
+    float ss4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent sums: short chains
 #pragma unroll
     for (int b = 0; b < QB / 2; ++b) {
-      const u32x4 w4 = *reinterpret_cast<const u32x4 *>(X + r * QRB + 16 * (h * (QB / 2) + b));
+      const int blk = (b + h * (QB / 2) + rot) & (QB - 1);
+      const u32x4 w4 = *reinterpret_cast<const u32x4 *>(X + r * QRB + 16 * blk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __builtin_bit_cast(float, w4[i] << 16);
-        const float hi = __builtin_bit_cast(float, w4[i] & 0xffff0000u);
-        ss += lo * lo + hi * hi;
+      for (int i = 0; i < 4; ++i) {   // x0^2 + x1^2 of a bf16 pair, one packed dot product
+        // (through a scalar: a bit_cast of the vector element itself reads
+        // element 0 with this compiler)
+        const unsigned u = w4[i];
+        const bf16x2 x2 = __builtin_bit_cast(bf16x2, u);
+        ss4[i] = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, ss4[i], false);
       }
     }
+    float ss = (ss4[0] + ss4[1]) + (ss4[2] + ss4[3]);
     ss += __shfl_xor(ss, C);
     if (lane < C) bf.nrm[pw == 1 ? 1 : 0][lane] = rsqrtf(ss + kL2Eps);
   };

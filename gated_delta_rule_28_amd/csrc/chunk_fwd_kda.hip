@@ -571,17 +571,20 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int mr = gi * NRM_R + lane / LPR;          // (matrix, row) pair
     const int m = mr / KC, r = mr % KC, part = lane % LPR;
     const char *X = reinterpret_cast<const char *>(m ? &rw.K[r][0] : &rw.Q[r][0]) + 2 * CPL * part;
-    float ss = 0.0f;
+    float ss4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent sums: short chains
 #pragma unroll
     for (int b = 0; b < CPL / 8; ++b) {
       const u32x4 w4 = *reinterpret_cast<const u32x4 *>(X + 16 * b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __builtin_bit_cast(float, w4[i] << 16);
-        const float hi = __builtin_bit_cast(float, w4[i] & 0xffff0000u);
-        ss += lo * lo + hi * hi;
+      for (int i = 0; i < 4; ++i) {   // x0^2 + x1^2 of a bf16 pair, one packed dot product
+        // (through a scalar: a bit_cast of the vector element itself reads
+        // element 0 with this compiler)
+        const unsigned u = w4[i];
+        const bf16x2 x2 = __builtin_bit_cast(bf16x2, u);
+        ss4[i] = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, ss4[i], false);
       }
     }
+    float ss = (ss4[0] + ss4[1]) + (ss4[2] + ss4[3]);
 #pragma unroll
     for (int d = 1; d < LPR; d <<= 1) ss += __shfl_xor(ss, d);
     if (part == 0) rw.nrm[m][r] = rsqrtf(ss + kL2Eps);
