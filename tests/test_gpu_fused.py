@@ -227,18 +227,19 @@ def test_chunk_fused_empty_sequence_keeps_the_state():
     assert torch.equal(S, inp["initial_state"])
 
 
-@pytest.mark.parametrize("B,H", [(2, 3), (8, 16)])
+@pytest.mark.parametrize("D,B,H", [(128, 2, 3), (128, 8, 16), (64, 4, 64)])
 @pytest.mark.parametrize("decay", ["softplus", "gla"])
-def test_chunk_fused_kda_strong_decay(B, H, decay):
+def test_chunk_fused_kda_strong_decay(D, B, H, decay):
     # per-token log decays down to about -15 after the fused transform, so
     # that some chunks take the exact in-chunk path; the decay sums are
-    # shared by several waves (six prep waves at B=2 H=3, four at B=8 H=16),
-    # each flagging its own channels
+    # shared by several waves (six prep waves at d=128 B=2 H=3, four at
+    # d=128 B=8 H=16 and at d=64 with 256 chains), each flagging its own
+    # channels
     say("chunk fused kda strong decay", B, H, decay)
-    inp = raw_inputs(B, 70, H, 128, "channel", "bf16", seed=B + H, decay=decay)
+    inp = raw_inputs(B, 70, H, D, "channel", "bf16", seed=B + H, decay=decay)
     g = torch.Generator(device=DEV)
     g.manual_seed(B * H)
-    x = torch.randn(B, 70, H, 128, device=DEV, generator=g)
+    x = torch.randn(B, 70, H, D, device=DEV, generator=g)
     # softplus: log a = -softplus(x), x ~ N(3, 5); GLA: log a = -softplus(-x)/16
     inp["log_alpha"] = 3.0 + 5.0 * x if decay == "softplus" else -40.0 + 60.0 * x
     check(inp, BF16_TOL, decay=decay)
@@ -246,3 +247,14 @@ def test_chunk_fused_kda_strong_decay(B, H, decay):
     # the case is only meaningful if some chunk crosses the exact-path bound
     sums = np.add.reduceat(la, np.arange(0, 70, 16), axis=1)
     assert sums.min() < -64.0
+
+
+@pytest.mark.parametrize("gate,decay", [("scalar", "softplus"), ("channel", "softplus"),
+                                        ("channel", "gla")])
+def test_chunk_fused_d64_many_chains(gate, decay):
+    # 256 chains at d = 64: the 64-column slice configurations (four prep
+    # waves in the KDA kernel: two waves share the decay sums and the norms,
+    # 16 channel pairs each)
+    say("chunk fused d64 many chains", gate, decay)
+    inp = raw_inputs(4, 45, 64, 64, gate, "bf16", seed=53, decay=decay)
+    check(inp, BF16_TOL, decay=decay)
