@@ -511,6 +511,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int p = lane / RGN, rg = lane % RGN;
     const int c0 = 2 * (gi * PPW + p);
     const int n = min(KC, T - j * KC);
+    const bool gla = (fuse & kFuseGla) != 0;   // a transform is on whenever the sums are shared
     f32x2 part[RPG];
     f32x2 run = {0.f, 0.f};
 #pragma unroll
@@ -518,7 +519,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const int r = rg * RPG + i;
       const f32x2 x = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
       // padded tokens keep log a = 0
-      run += (r < n) ? f32x2{fused_log_alpha(x[0], fuse), fused_log_alpha(x[1], fuse)}
+      run += (r < n) ? f32x2{decay_transform(x[0], gla), decay_transform(x[1], gla)}
                      : f32x2{0.f, 0.f};
       part[i] = run;
     }
@@ -585,8 +586,17 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       }
     }
     float ss = (ss4[0] + ss4[1]) + (ss4[2] + ss4[3]);
-#pragma unroll
-    for (int d = 1; d < LPR; d <<= 1) ss += __shfl_xor(ss, d);
+    // sum over the LPR lanes of the row with DPP moves (no LDS round trip):
+    // within quads, then the upper quad into the lower one, which holds the
+    // writing lane (part 0)
+    static_assert(LPR == 4 || LPR == 8, "norm lanes");
+    auto dpp = [](float x, auto ctrl) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+          0, __builtin_bit_cast(int, x), decltype(ctrl)::value, 0xF, 0xF, true));
+    };
+    ss += dpp(ss, std::integral_constant<int, 0xB1>{});    // quad_perm [1,0,3,2]
+    ss += dpp(ss, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+    if constexpr (LPR == 8) ss += dpp(ss, std::integral_constant<int, 0x104>{});   // row_shl:4
     if (part == 0) rw.nrm[m][r] = rsqrtf(ss + kL2Eps);
   };
 
@@ -629,6 +639,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (lane == 0) d.flag[0] = exact;
     }
     const int rb0 = row_bound(dw), rb1 = row_bound(dw + 1);
+    const bool l2f = (fuse & kFuseL2) != 0;
     const int coff = 2 * (c0 & 7);                 // byte offset inside the 16-byte block
     const f32x2 sh = exact ? gl : f32x2{0.f, 0.f};   // R^ = K o e^{sh - G}
     auto put = [&](bf16 (*hi)[DK], bf16 (*lo)[DK], int r, float x0, float x1) {
@@ -645,14 +656,13 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const unsigned qb = *reinterpret_cast<const unsigned *>(&rw.Q[r][c0]);
       const float k0 = __builtin_bit_cast(float, kb << 16), k1 = __builtin_bit_cast(float, kb & 0xffff0000u);
       const float q0 = __builtin_bit_cast(float, qb << 16), q1 = __builtin_bit_cast(float, qb & 0xffff0000u);
-      float e0 = __expf(g[0]), e1 = __expf(g[1]);
-      float f0 = __expf(sh[0] - g[0]), f1 = __expf(sh[1] - g[1]);
-      float eq0 = e0, eq1 = e1;
-      if (fuse & kFuseL2) {
-        const float rq = rw.nrm[0][r], rk = rw.nrm[1][r];
-        eq0 *= rq; eq1 *= rq;
-        e0 *= rk; e1 *= rk; f0 *= rk; f1 *= rk;
-      }
+      // the fused norms are read whether or not they were formed and picked
+      // by a select (no branch in the row loop)
+      const float nq = rw.nrm[0][r], nk = rw.nrm[1][r];
+      const float rq = l2f ? nq : 1.0f, rk = l2f ? nk : 1.0f;
+      const float eq0 = __expf(g[0]) * rq, eq1 = __expf(g[1]) * rq;
+      const float e0 = __expf(g[0]) * rk, e1 = __expf(g[1]) * rk;
+      const float f0 = __expf(sh[0] - g[0]) * rk, f1 = __expf(sh[1] - g[1]) * rk;
       if constexpr (ERASE) put(d.Kh, d.Kl, r, k0 * e0, k1 * e1);   // K^ feeds only K^ S and A
       put(d.Qh, d.Ql, r, q0 * eq0, q1 * eq1);
       put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);

@@ -42,12 +42,16 @@ __device__ __forceinline__ float fused_beta(float b, int fuse) {
   return (fuse & kFuseBetaSigmoid) ? sigmoid_f(b) : b;
 }
 // log a from the log_alpha input: -softplus(x), or GLA's sigmoid(x)^{1/16}
-__device__ __forceinline__ float fused_log_alpha(float x, int fuse) {
-  if (!(fuse & (kFuseSoftplus | kFuseGla))) return x;
-  // one softplus either way: log sigmoid(x)^{1/16} = -softplus(-x) / 16
-  const bool gla = (fuse & kFuseGla) != 0;
+// log a from x when a decay transform is on (gla: GLA's gate, else the
+// softplus decay); one softplus either way: log sigmoid(x)^{1/16} =
+// -softplus(-x) / 16
+__device__ __forceinline__ float decay_transform(float x, bool gla) {
   const float sp = softplus_f(gla ? -x : x);
   return gla ? sp * (-1.0f / 16.0f) : -sp;
+}
+__device__ __forceinline__ float fused_log_alpha(float x, int fuse) {
+  if (!(fuse & (kFuseSoftplus | kFuseGla))) return x;
+  return decay_transform(x, (fuse & kFuseGla) != 0);
 }
 // the SiLU output gate applied to an output value
 __device__ __forceinline__ float silu_gate(float o, float g) { return o * g * sigmoid_f(g); }
