@@ -14,7 +14,7 @@ before the recurrence and to the read-out after it.  What the pages fix:
 Each function is the plain definition; the GPU path fuses them into its
 kernels (gdr_fuse flags).
 
-Readings adopted (listed in the design doc): the feature map is the L2
+Readings adopted: the feature map is the L2
 normalisation x / sqrt(sum x^2 + 1e-6) per (token, head) over d_k (unit keys
 make the erase an orthogonal projection, diosapp tutorial, section 三); b
 from a logit is the logistic sigmoid; a from an unconstrained x is

@@ -25,7 +25,7 @@ closed-form updates above exactly:
       S  = S' + beta k (v - p)^T
       o  = S^T q              (the read sees this token's own write)
 
-Readings adopted where the pages leave a step open (all listed in the design doc):
+Readings adopted where the pages leave a step open:
 * The gate enters as log alpha (alpha = exp(log alpha)); the DeltaNet case
   is "no gate" (alpha = 1).
 * No 1/sqrt(d_k) query scale, no normaliser Z and no feature map: the delta
