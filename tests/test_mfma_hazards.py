@@ -10,7 +10,10 @@ jumps over it read a stale accumulator register (wrong results that depend
 on timing).  The kernels avoid runtime branches at such points; this test
 compiles them to assembly and checks, along the shortest path in layout
 order, that every read of an MFMA result reached across a branch is at
-least 8 wait states after the MFMA.
+least 8 wait states after the MFMA.  It also checks that no inline-assembly
+instruction writes a register that an MFMA issued just before still reads as
+its accumulator input: the compiler inserts the wait states for that only
+before its own instructions.
 """
 
 import concurrent.futures as cf
@@ -107,6 +110,59 @@ def short_reads(lines, min_ws=MIN_WAIT_STATES):
     return found
 
 
+def asm_writes_after_mfma(lines, min_ws=MIN_WAIT_STATES):
+    """(mfma line, asm line) where an inline-assembly instruction writes a VGPR
+    that an MFMA issued fewer than min_ws wait states before reads as its
+    accumulator input (the compiler protects that read only from its own
+    instructions).  The first operand of each instruction in an inline
+    block is taken as its destination."""
+    found = []
+    inside = False
+    for j, line in enumerate(lines):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not inside or not s.startswith("v_"):
+            continue
+        parts = s.split(None, 1)
+        if len(parts) < 2:
+            continue
+        dst = _vregs(parts[1].split(",")[0])
+        ws = 0
+        for i in range(j - 1, max(j - 1 - WINDOW, -1), -1):
+            t_ = lines[i].strip()
+            if not t_ or t_.startswith((";", ".")):
+                continue
+            if t_.startswith(("s_cbranch", "s_branch", "s_endpgm")) or t_.endswith(":"):
+                break
+            if t_.startswith("v_mfma"):
+                ops = t_.split(None, 1)[1].split(",")
+                if len(ops) >= 4 and _vregs(ops[3]) & dst and ws < min_ws:
+                    found.append((i + 1, j + 1))
+                break
+            ws += int(t_.split()[1]) + 1 if t_.startswith("s_nop") else 1
+    return found
+
+
+def test_scanner_flags_an_asm_write_of_an_mfma_accumulator_input():
+    lines = """
+    v_mfma_f32_16x16x32_bf16 v[12:15], v[162:165], v[56:59], v[142:145]
+    ;;#ASMSTART
+    v_dot2_f32_bf16 v142, v154, s23, v170
+    ;;#ASMEND
+""".splitlines()
+    assert len(asm_writes_after_mfma(lines)) == 1
+    # far enough after the MFMA, or writing another register, it is fine
+    late = lines[:2] + ["    s_nop 7"] + lines[2:]
+    assert asm_writes_after_mfma(late) == []
+    other = [l.replace("v142,", "v150,") for l in lines]
+    assert asm_writes_after_mfma(other) == []
+
+
 def test_scanner_flags_a_read_that_skips_an_if_block():
     # the shape the check exists for: the MFMA result v6 is read two
     # instructions after the MFMA on the path that jumps over the block
@@ -142,3 +198,5 @@ def test_mfma_results_are_not_read_early_across_branches():
             asm = dict(zip(SOURCES, ex.map(lambda s: _assembly(s, tmp), SOURCES)))
     problems = {src: short_reads(lines)[:5] for src, lines in asm.items()}
     assert all(not p for p in problems.values()), problems
+    asm_problems = {src: asm_writes_after_mfma(lines)[:5] for src, lines in asm.items()}
+    assert all(not p for p in asm_problems.values()), asm_problems
