@@ -24,6 +24,17 @@ def test_headline_algorithmic_counts():
     assert bench.decode_alg_bytes(d) == 256 * 32 * (2 * 4 * 128 * 128 + 2 * 384 + 8 + 4 * 128)
 
 
+def test_fused_line_counts_the_output_gate():
+    # the fused lines read the output gate (dtype of q) once per output value
+    for w in (W.HEADLINE, W.by_name("kda_bf16_b2h32t8192")):
+        th = w.B * w.T * w.H
+        assert bench.chunk_alg_bytes(w, out_gate=True) - bench.chunk_alg_bytes(w) == th * 2 * w.Dv
+    # the KDA shape: per-channel log decays (4 Dk bytes per token-head)
+    k = W.by_name("kda_bf16_b2h32t8192")
+    th = k.B * k.T * k.H
+    assert bench.chunk_alg_bytes(k) == th * (2 * 384 + 4 + 4 * 128 + 4 * 128) + k.B * k.H * 128 * 128 * 4
+
+
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
