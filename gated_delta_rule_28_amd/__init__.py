@@ -93,6 +93,12 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
     out_dtype, final state [B, H, Dk, Dv] fp32 or None).  `o` and
     `final_state` may be passed preallocated; final_state may be the
     initial_state tensor itself (in-place carry).
+
+    erase=False drops the erase term (additive write).  Fused options
+    (applied inside the kernels, see the module docstring): qk_l2norm,
+    beta_sigmoid (beta holds logits), decay="softplus" | "gla" (log_alpha
+    holds the pre-activation; needs a gate), out_gate [B, T, H, Dv] in the
+    dtype of q (o <- o * g * sigmoid(g)).
     """
     _check_dev("q", q)
     if q.dtype not in _DT:
@@ -142,7 +148,8 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
                    erase=True, qk_l2norm=False, beta_sigmoid=False, decay=None, out_gate=None):
     """One decode token for N sequences; `state` [N, H, Dk, Dv] fp32 is
     updated in place.  q, k [N, H, Dk]; v [N, H, Dv]; beta [N, H];
-    log_alpha None | [N, H] | [N, H, Dk].  Returns o [N, H, Dv]."""
+    log_alpha None | [N, H] | [N, H, Dk].  Returns o [N, H, Dv].  erase and
+    the fused options are those of chunk_fwd (out_gate [N, H, Dv])."""
     _check_dev("q", q)
     if q.dtype not in _DT:
         raise TypeError("q/k/v must be bf16 or fp32")
