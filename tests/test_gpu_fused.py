@@ -258,3 +258,42 @@ def test_chunk_fused_d64_many_chains(gate, decay):
     say("chunk fused d64 many chains", gate, decay)
     inp = raw_inputs(4, 45, 64, 64, gate, "bf16", seed=53, decay=decay)
     check(inp, BF16_TOL, decay=decay)
+
+
+@pytest.mark.parametrize("gate,decay", [("scalar", "softplus"), ("channel", "gla")])
+def test_chunk_fused_graph_replays_match_eager(gate, decay):
+    # a fused chunk forward captured once as a HIP graph: every replay, with
+    # eager work and synchronisations in between, equals the eager call bit
+    # for bit
+    say("chunk fused graph replay", gate, decay)
+    inp = raw_inputs(2, 70, 3, 128, gate, "bf16", seed=61, decay=decay)
+    o = torch.empty(2, 70, 3, 128, device=DEV)
+    S = torch.empty(2, 3, 128, 128, device=DEV)
+    s0 = inp["initial_state"].clone()
+
+    def call():
+        gdr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], s0,
+                      qk_l2norm=True, beta_sigmoid=True, decay=decay,
+                      out_gate=inp["out_gate"], o=o, final_state=S)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9)
+    for rep in range(3):
+        s0.copy_(0.1 * (rep + 1) * torch.randn(2, 3, 128, 128, device=DEV, generator=gen))
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_s = o.clone(), S.clone()
+        o.zero_()
+        S.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, o) and torch.equal(got_s, S), rep
