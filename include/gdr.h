@@ -192,7 +192,11 @@ int gdr_recurrent_step(int N, int H, int Dk, int Dv,
 
 /*
  * gdr_recurrent_step_ex -- gdr_recurrent_step with the fused prologue and
- * epilogue (`fuse` flags and `out_gate` [N, H, Dv] or NULL).
+ * epilogue (`fuse` flags and `out_gate` [N, H, Dv] or NULL, in_dtype,
+ * 16-byte aligned, owned by the caller and only read).  With fuse = 0 and
+ * out_gate = NULL it is gdr_recurrent_step.  Unknown flag bits, both decay
+ * flags, a decay flag without a gate or a misaligned out_gate return
+ * GDR_EINVAL before anything is launched.
  */
 int gdr_recurrent_step_ex(int N, int H, int Dk, int Dv,
                           int in_dtype, int out_dtype, int gate, int fuse,
