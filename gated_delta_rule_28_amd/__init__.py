@@ -166,10 +166,14 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
     gate = _gate_of(log_alpha, (N, H), Dk) | (0 if erase else _abi.GDR_NO_ERASE)
     if log_alpha is not None:
         _check_dev("log_alpha", log_alpha, torch.float32)
+    if out_dtype not in _DT:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
     if o is None:
         o = torch.empty(N, H, Dv, device=q.device, dtype=out_dtype)
     else:
         _check_dev("o", o, out_dtype)
+        if tuple(o.shape) != (N, H, Dv):
+            raise ValueError("o must be [N, H, Dv]")
     fuse = _fuse_flags(qk_l2norm, beta_sigmoid, decay)
     _check_gate_tensor(out_gate, (N, H, Dv), q.dtype)
     st = _abi.gdr_recurrent_step_ex(N, H, Dk, Dv, _DT[q.dtype], _DT[out_dtype], gate, fuse,

@@ -222,13 +222,18 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     __syncthreads();
     __syncthreads();
 
-    // byte offsets of this lane's output values from a chunk's first row
-    int ooff[2][4];
+    // element offsets of this lane's output values from a chunk's first row,
+    // and their byte offsets in o; unsigned 32-bit, like the buffer offset
+    // they feed (the host bounds one chunk's rows of a 4-byte tensor below
+    // 4 GiB, so neither wraps)
+    unsigned oel[2][4], ooff[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        ooff[rb][e] = (int)sizeof(OutT) * ((16 * rb + 4 * lg + e) * H * DV + col0 + lr);
+      for (int e = 0; e < 4; ++e) {
+        oel[rb][e] = (unsigned)(16 * rb + 4 * lg + e) * (unsigned)(H * DV) + (unsigned)(col0 + lr);
+        ooff[rb][e] = (unsigned)sizeof(OutT) * oel[rb][e];
+      }
     // v, transposing read: rows 16 rb + 4 lg + (lr >> 2), columns
     // 16 wave + 4 (lr & 3) .. +3 (an 8-byte half of a 16-byte block)
     const int v_off = v_at(4 * lg + (lr >> 2), 2 * wave + ((lr & 3) >> 1)) + 8 * (lr & 1);
@@ -274,7 +279,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          og_next[rb][e] = buf_ld_u16(rg, 2 * (ooff[rb][e] / (int)sizeof(OutT)));
+          og_next[rb][e] = buf_ld_u16(rg, 2u * oel[rb][e]);
     };
 
     for (int it = 0; it < nchunks + 1; ++it) {

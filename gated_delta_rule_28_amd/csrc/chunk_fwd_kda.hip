@@ -172,9 +172,15 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     __syncthreads();
     __syncthreads();
 
-    int ooff[4];
+    // element and byte offsets of this lane's output values from a chunk's
+    // first row, unsigned 32-bit like the buffer offset they feed (the host
+    // bounds one chunk's rows of a 4-byte tensor below 4 GiB)
+    unsigned oel[4], ooff[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ooff[e] = (int)sizeof(OutT) * ((4 * lg + e) * H * DV + col0 + lr);
+    for (int e = 0; e < 4; ++e) {
+      oel[e] = (unsigned)(4 * lg + e) * (unsigned)(H * DV) + (unsigned)(col0 + lr);
+      ooff[e] = (unsigned)sizeof(OutT) * oel[e];
+    }
     // v, transposing read: rows 4 lg + (lr >> 2), columns 16 wave + 4 (lr & 3) .. +3
     const int v_off = (4 * lg + (lr >> 2)) * VRB +
                       16 * ((2 * wave + ((lr & 3) >> 1)) ^ swz_v<VB>(4 * lg + (lr >> 2))) + 8 * (lr & 1);
@@ -222,7 +228,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const rsrc_t rg = make_rsrc32(out_gate + orow,
                                       valid ? 2u * ((unsigned)(n - 1) * H * DV + DV) : 0u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) og_next[e] = buf_ld_u16(rg, 2 * (ooff[e] / (int)sizeof(OutT)));
+        for (int e = 0; e < 4; ++e) og_next[e] = buf_ld_u16(rg, 2u * oel[e]);
       }
       if (s >= 0) {
         const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));

@@ -138,17 +138,20 @@ __device__ __forceinline__ rsrc_t make_rsrc32(const void *base, unsigned bytes) 
 }
 // a bf16 value, left as its 16 bits (converted where it is used, so that a
 // load issued ahead is not waited for at once)
-__device__ __forceinline__ unsigned buf_ld_u16(rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+__device__ __forceinline__ unsigned buf_ld_u16(rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, __builtin_bit_cast(int, off), 0, 0);
 }
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned u) {
   return __builtin_bit_cast(float, u << 16);
 }
-__device__ __forceinline__ void buf_st1(float x, rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r, off, 0, 0);
+// (offsets are the unsigned 32-bit buffer offset, passed through bit for bit)
+__device__ __forceinline__ void buf_st1(float x, rsrc_t r, unsigned off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), r,
+                                        __builtin_bit_cast(int, off), 0, 0);
 }
-__device__ __forceinline__ void buf_st1(bf16 x, rsrc_t r, int off) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, off, 0, 0);
+__device__ __forceinline__ void buf_st1(bf16 x, rsrc_t r, unsigned off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r,
+                                        __builtin_bit_cast(int, off), 0, 0);
 }
 
 // D += A(16x16) * B(16x16), bf16 operands, fp32 accumulate: lane l holds

@@ -14,16 +14,17 @@ Definitions followed
       S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
   with alpha_t in [0, 1]^{d_k}, one decay per key channel.
 
-The per-step order is decay -> predict -> write residual -> read.  The
-xhh.club digest "Transformer 入坑笔记（五）" (Q&A on Gated DeltaNet) states
-that the old state is decayed first and the decayed state predicts the
-current value; the diosapp tutorial (section 四, the annotated four-step
-update) gives the same order.  Expanding the four steps reproduces the two
-closed-form updates above exactly:
-      S' = alpha S            (or Diag(alpha) S)
-      p  = S'^T k             (prediction of v from the decayed memory)
-      S  = S' + beta k (v - p)^T
-      o  = S^T q              (the read sees this token's own write)
+Each token applies the equation of its gate as written there, a transition
+of the old state plus a rank-one write:
+      S_t = M_t S_{t-1} + beta_t k_t v_t^T,
+      M_t = alpha_t (I - beta_t k_t k_t^T)          (GDN; alpha_t = 1: DeltaNet)
+      M_t = (I - beta_t k_t k_t^T) Diag(alpha_t)    (KDA: the channel decay is
+                                                     the right-hand factor)
+M_t is applied to S without forming it, as (I - beta k k^T) X = X - beta
+k (k^T X), which is the same product regrouped.  For KDA, X = Diag(alpha) S:
+the decay acts on the old state before the erase, which is also the order
+the xhh.club digest "Transformer 入坑笔记（五）" gives in its Q&A on Gated
+DeltaNet (decay the old state first, then predict from it).
 
 Readings adopted where the pages leave a step open:
 * The gate enters as log alpha (alpha = exp(log alpha)); the DeltaNet case
@@ -83,22 +84,20 @@ def gated_delta_recurrence(q, k, v, beta, log_alpha=None, initial_state=None,
 
     o = np.empty((B, T, H, Dv))
     for t in range(T):
-        # 1) decay the old memory (scalar per head, or one factor per key row)
-        if gate == "scalar":
-            S = S * np.exp(log_alpha[:, t])[:, :, None, None]
-        elif gate == "channel":
-            S = S * np.exp(log_alpha[:, t])[:, :, :, None]
         kt = k[:, t]                                     # [B, H, Dk]
-        bt = beta[:, t][:, :, None]                      # [B, H, 1]
+        bt = beta[:, t][:, :, None, None]                # [B, H, 1, 1]
+        # the channel decay Diag(alpha_t) is the right-hand factor of M_t
+        if gate == "channel":
+            S = np.exp(log_alpha[:, t])[:, :, :, None] * S
         if erase:
-            # 2) what the decayed memory predicts for this key
-            pred = np.einsum("bhkv,bhk->bhv", S, kt)
-            # 3) write only the residual, with strength beta
-            delta = bt * (v[:, t] - pred)
-        else:
-            delta = bt * v[:, t]
-        S = S + np.einsum("bhk,bhv->bhkv", kt, delta)
-        # 4) read the updated memory with the query
+            # (I - beta k k^T) S = S - beta k (k^T S)
+            ktS = np.einsum("bhk,bhkv->bhv", kt, S)
+            S = S - bt * np.einsum("bhk,bhv->bhkv", kt, ktS)
+        # the scalar decay alpha_t multiplies the whole transition
+        if gate == "scalar":
+            S = np.exp(log_alpha[:, t])[:, :, None, None] * S
+        S = S + bt * np.einsum("bhk,bhv->bhkv", kt, v[:, t])
+        # o_t = S_t^T q_t: the read sees this token's own write
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
     return o, S
 

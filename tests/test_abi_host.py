@@ -143,3 +143,35 @@ def step_ex(**kw):
 def test_fused_prologue_validation(kw):
     assert chunk_ex(**kw) == _abi.GDR_EINVAL
     assert step_ex(**kw) == _abi.GDR_EINVAL
+
+
+# one chunk's rows of the fp32 output, with the fused output gate read at the
+# same element offsets: the size bounds hold for that form too
+@pytest.mark.parametrize("gate,H", [(_abi.GDR_GATE_SCALAR, 271000),
+                                    (_abi.GDR_GATE_CHANNEL, 560000)])
+def test_chunk_fwd_size_bound_with_fused_gate(gate, H):
+    assert chunk_ex(H=H, gate=gate, out_gate=FAKE, out_dtype=_abi.GDR_F32) == \
+        _abi.GDR_EUNSUPPORTED
+
+
+def test_recurrent_step_checks_output_shape_before_launch(monkeypatch):
+    """A preallocated o of the wrong shape raises in Python and the C entry
+    point is never called (a smaller o would be written past its end)."""
+    import torch
+    import gated_delta_rule_28_amd as gdr
+
+    def host_check(name, t, dtype=None):   # the device check, minus the device
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(name)
+
+    called = []
+    monkeypatch.setattr(gdr, "_check_dev", host_check)
+    monkeypatch.setattr(_abi, "gdr_recurrent_step_ex", lambda *a: called.append(a) or 0)
+    N, H, D = 2, 3, 16
+    q = torch.zeros(N, H, D)
+    beta = torch.zeros(N, H)
+    state = torch.zeros(N, H, D, D)
+    for bad in (torch.zeros(N, H, D - 1), torch.zeros(1, H, D), torch.zeros(N * H * D)):
+        with pytest.raises(ValueError, match="o must be"):
+            gdr.recurrent_step(q, q, q, beta, None, state, o=bad)
+    assert not called

@@ -14,6 +14,16 @@ least 8 wait states after the MFMA.  It also checks that no inline-assembly
 instruction writes a register that an MFMA issued just before still reads as
 its accumulator input: the compiler inserts the wait states for that only
 before its own instructions.
+
+A third check covers the DPP forms written as inline assembly (the
+v_fmac_f32_dpp row broadcasts of the diagonal triangular solve).  A DPP
+instruction reads its first source through the lane permutation, and on
+gfx9 a VALU write of that VGPR must come at least 2 wait states before the
+DPP read.  The compiler inserts them before its own DPP instructions, not
+before inline assembly, so the check finds, for every inline DPP
+instruction, the last VALU write of its permuted source and requires 2 wait
+states in between (a label or branch inside that window is flagged too,
+since another path could end in a write there).
 """
 
 import concurrent.futures as cf
@@ -148,6 +158,71 @@ def asm_writes_after_mfma(lines, min_ws=MIN_WAIT_STATES):
     return found
 
 
+DPP_MIN_WAIT_STATES = 2
+
+
+def dpp_reads_after_valu_write(lines, min_ws=DPP_MIN_WAIT_STATES):
+    """(writer line, dpp line, wait states) where an inline-assembly DPP
+    instruction reads its permuted source fewer than min_ws wait states
+    after a VALU write of that register (writer line None: a label or branch
+    came first, so the window is not known to be clear)."""
+    found = []
+    inside = False
+    for j, line in enumerate(lines):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not inside or not s.startswith("v_") or "_dpp" not in s.split()[0]:
+            continue
+        ops = s.split(None, 1)[1].split(",")
+        if len(ops) < 2:
+            continue
+        src = _vregs(ops[1])          # src0: the operand the DPP control permutes
+        ws = 0
+        for i in range(j - 1, max(j - 1 - WINDOW, -1), -1):
+            if ws >= min_ws:
+                break
+            t_ = lines[i].strip()
+            if not t_ or t_.startswith((";", ".")):
+                continue
+            if t_.startswith(("s_cbranch", "s_branch")) or t_.endswith(":"):
+                found.append((None, j + 1, ws))
+                break
+            if t_.startswith("s_nop"):
+                ws += int(t_.split()[1]) + 1
+                continue
+            if t_.startswith("v_"):
+                parts = t_.split(None, 1)
+                if len(parts) == 2 and _vregs(parts[1].split(",")[0]) & src:
+                    found.append((i + 1, j + 1, ws))
+                    break
+            ws += 1
+    return found
+
+
+def test_scanner_flags_a_dpp_read_right_after_a_valu_write():
+    lines = """
+    v_mul_f32_e32 v40, v41, v42
+    ;;#ASMSTART
+    v_fmac_f32_dpp v10, v40, v11 row_newbcast:3 row_mask:0xf bank_mask:0xf
+    ;;#ASMEND
+""".splitlines()
+    assert [f[2] for f in dpp_reads_after_valu_write(lines)] == [0]
+    # two wait states in between, a write of the other (unpermuted) source,
+    # or a load (not a VALU write) are fine
+    assert dpp_reads_after_valu_write(lines[:2] + ["    s_nop 1"] + lines[2:]) == []
+    assert dpp_reads_after_valu_write([l.replace("v40, v41", "v11, v41") for l in lines]) == []
+    assert dpp_reads_after_valu_write(
+        [l.replace("v_mul_f32_e32 v40, v41, v42", "ds_read_b32 v40, v41") for l in lines]) == []
+    # one unrelated instruction is one wait state: still short
+    one = lines[:2] + ["    v_add_f32_e32 v50, v51, v52"] + lines[2:]
+    assert [f[2] for f in dpp_reads_after_valu_write(one)] == [1]
+
+
 def test_scanner_flags_an_asm_write_of_an_mfma_accumulator_input():
     lines = """
     v_mfma_f32_16x16x32_bf16 v[12:15], v[162:165], v[56:59], v[142:145]
@@ -200,3 +275,8 @@ def test_mfma_results_are_not_read_early_across_branches():
     assert all(not p for p in problems.values()), problems
     asm_problems = {src: asm_writes_after_mfma(lines)[:5] for src, lines in asm.items()}
     assert all(not p for p in asm_problems.values()), asm_problems
+    dpp_problems = {src: dpp_reads_after_valu_write(lines)[:5] for src, lines in asm.items()}
+    assert all(not p for p in dpp_problems.values()), dpp_problems
+    # the scan saw the solve's inline DPP instructions (it is not vacuous)
+    for src, lines in asm.items():
+        assert sum("v_fmac_f32_dpp" in l for l in lines) >= 120, src
