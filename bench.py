@@ -19,7 +19,16 @@ counter summary when it was taken on the current kernel source), the fp64
 oracle timed on the host cores, and secondary lines: bf16 output, the KDA
 workload kda_bf16_b2h32t8192, both shapes without the erase term and with the
 fused prologue / output gate, and the batched decode step (256 sequences x 32
-heads, 128 consecutive steps, eager and as one HIP graph).
+heads, 128 consecutive steps, eager and as one HIP graph), the tiny fp32
+workload (microseconds per call: launch-latency bound), the B=4, H=8,
+T=2048 DeltaNet and Gated DeltaNet workloads (timed cold, after an untimed
+512 MiB write between calls, and warm), and a 1 GiB device copy whose rate
+is the measured HBM ceiling each roofline is also quoted against.
+
+The oracle baseline runs the fp64 recurrence over every chain of the
+headline run, on the timed run's own inputs copied from the device, split
+across the host cores (one process per core, one BLAS thread each); its
+output is what the `parity` field of the line compares the GPU output with.
 """
 
 import argparse
@@ -52,6 +61,12 @@ KERNEL_SOURCES = {
 # the plain copy used to calibrate the byte counters: |x| over 1 GiB of fp32
 COPY_BYTES = 1 << 30
 COPY_REGEX = "AbsFunctor"
+# the bf16 GEMM of known size that checks the MFMA operation counter's scale
+GEMM_N = 4096
+GEMM_REGEX = "Cijk"
+SIMD_PER_GPU = 256 * 4            # MI355X: 256 compute units x 4 SIMDs
+PARITY_TOL = 2e-3                 # max|d| / RMS(ref), bf16 inputs with fp32 state
+MAX_ORACLE_PROCS = 16             # the host-core share of one GPU
 
 
 def source_hash(kernel):
@@ -81,6 +96,29 @@ def read_traffic(kernel, workload, root=PROFILES):
     if kv.get("source_sha256") != source_hash(kernel):
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+def mfma_file(kernel, workload, root=PROFILES):
+    return os.path.join(root, f"mfma_{kernel}_{workload}.txt")
+
+
+def read_mfma(kernel, workload, root=PROFILES):
+    """MFMA counters per launch from the committed summary (busy fraction,
+    issued bf16 flops), or None when there is none or the kernel source
+    changed since it was taken."""
+    path = mfma_file(kernel, workload, root)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != source_hash(kernel):
+        return None
+    return {"busy_frac": float(kv["mfma_busy_frac"]),
+            "issued_flops_per_launch": float(kv["issued_bf16_flops_per_launch"])}
 
 
 # ---------------------------------------------------------------------------
@@ -128,13 +166,14 @@ def decode_alg_bytes(w):
 # GPU timing
 
 
-def time_launches(torch, fn, steps, warmup, settle_s=0.0):
+def time_launches(torch, fn, steps, warmup, settle_s=0.0, pre=None):
     """Run fn for `settle_s` seconds of wall time (untimed: the GPU clock
     ramps up over the first ~80 launches of a fresh process and the first
     launches run up to ~20% slower), then `warmup` times, then exactly
     `steps` times between two full synchronisations; each timed call is also
     bracketed by events on the current stream, the stream the kernels are
-    launched on."""
+    launched on.  `pre`, when given, runs before every timed call, outside
+    its events (the cache flush of the cold timings)."""
     t_end = time.perf_counter() + settle_s
     while time.perf_counter() < t_end:
         for _ in range(4):
@@ -147,6 +186,8 @@ def time_launches(torch, fn, steps, warmup, settle_s=0.0):
           for _ in range(steps)]
     t0 = time.perf_counter()
     for a, b in ev:
+        if pre is not None:
+            pre()
         a.record()
         fn()
         b.record()
@@ -154,6 +195,26 @@ def time_launches(torch, fn, steps, warmup, settle_s=0.0):
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in ev]
     return wall, per
+
+
+def copy_ceiling(torch, nbytes=COPY_BYTES, steps=10):
+    """Measured HBM ceiling: a plain device-to-device copy of `nbytes` (read
+    once, written once), GB/s of read + written bytes at the median copy."""
+    src = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    _, per = time_launches(torch, lambda: dst.copy_(src), steps, 2, settle_s=0.1)
+    med = statistics.median(per)
+    del src, dst
+    return {"bytes_moved_per_copy": 2 * nbytes, "median_ms": med,
+            "GB/s": 2 * nbytes / (med * 1e-3) / 1e9, "kind": "torch copy_ of a 1 GiB fp32 tensor"}
+
+
+def with_copy_frac(roof, copy):
+    """The roofline dict with its achieved rate also quoted against the
+    measured copy ceiling."""
+    if copy is not None:
+        roof = dict(roof, copy_GBs=copy["GB/s"], frac_of_copy=roof["achieved"] / copy["GB/s"])
+    return roof
 
 
 def fused_inputs(torch, inp, w):
@@ -176,7 +237,7 @@ def fused_inputs(torch, inp, w):
     return out
 
 
-def chunk_setup(torch, gdr, W, w, out_dtype, erase=True, fused=False):
+def chunk_setup(torch, gdr, W, w, out_dtype, erase=True, fused=False, keep=None):
     inp = W.make_workload_inputs(w, seed=0, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.Dv, device="cuda", dtype=out_dtype)
     S = torch.empty(w.B, w.H, w.Dk, w.Dv, device="cuda", dtype=torch.float32)
@@ -189,13 +250,23 @@ def chunk_setup(torch, gdr, W, w, out_dtype, erase=True, fused=False):
     def step():
         gdr.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None,
                       chunk=w.chunk, out_dtype=out_dtype, o=o, final_state=S, erase=erase, **kw)
+    if keep is not None:
+        keep.update(inp=inp, o=o, S=S)
     return step, o, S
 
 
 def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=True,
-               fused=False):
-    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype, erase, fused)
-    wall, per = time_launches(torch, step, steps, warmup, settle_s)
+               fused=False, cold=False, keep=None):
+    """Timed launches of one chunk workload.  cold=True writes a 512 MiB
+    scratch buffer (untimed, on the launch stream) before every timed call,
+    so no input is left in the caches; `keep`, a dict, receives the run's
+    inputs and outputs."""
+    step, o, S = chunk_setup(torch, gdr, W, w, out_dtype, erase, fused, keep=keep)
+    pre = None
+    if cold:
+        scratch = torch.empty(512 << 20, device="cuda", dtype=torch.uint8)
+        pre = scratch.zero_
+    wall, per = time_launches(torch, step, steps, warmup, settle_s, pre=pre)
     if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())):
         raise RuntimeError(f"non-finite output in the timed run of {w.name}")
     out_b = 2 if out_dtype == torch.bfloat16 else 4
@@ -205,8 +276,22 @@ def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=T
     alg_b = chunk_alg_bytes(w, out_b, out_gate=fused)
     alg_f = chunk_alg_flops(w, C, erase)
     achieved = alg_b / (mean_ms * 1e-3) / 1e9
-    # counter traffic is taken for the erasing, unfused fp32-output launches only
-    traffic = read_traffic(kern, w.name) if out_b == 4 and erase and not fused else None
+    # counters are taken for the erasing, unfused fp32-output launches only
+    plain = out_b == 4 and erase and not fused
+    traffic = read_traffic(kern, w.name) if plain else None
+    mc = read_mfma(kern, w.name) if plain else None
+    mfma_counter = None
+    if mc is not None:
+        issued = mc["issued_flops_per_launch"] / (mean_ms * 1e-3) / 1e12
+        mfma_counter = {"busy_frac": mc["busy_frac"], "issued_tflops": issued,
+                        "issued_frac_of_peak": issued / BF16_PEAK_TFLOPS,
+                        "issued_over_alg": mc["issued_flops_per_launch"] / alg_f,
+                        "source": os.path.basename(mfma_file(kern, w.name)),
+                        "note": "rocprofv3 counters: busy = MFMA-busy SIMD cycles / (GPU-active "
+                                "cycles x 1024 SIMDs); issued = bf16 MFMA operations x 512 "
+                                "(hi/lo split products included) / mean event time"}
+    if cold:
+        del scratch
     return {
         "workload": w.name, "tokens": w.B * w.T, "wall_s": wall, "steps": steps,
         "ms_per_step": 1e3 * wall / steps,
@@ -220,6 +305,7 @@ def chunk_line(torch, gdr, W, w, steps, warmup, out_dtype, settle_s=0.0, erase=T
                      "unit": "TFLOP/s",
                      "frac": alg_f / (mean_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                      "alg_flops_per_launch": alg_f},
+        "mfma_counter": mfma_counter,
     }
 
 
@@ -270,28 +356,176 @@ def decode_line(torch, gdr, W, d, passes=3, settle_s=0.0):
     }
 
 
-def cpu_baseline(W, w, batches=8):
-    """The fp64 oracle on a bounded sample of the same workload: `batches`
-    sequences x all heads x all tokens, the same seeded inputs, one thread."""
+def _oracle_worker(args):
+    """One host process's share of the oracle baseline: the fp64 recurrence
+    over a group of chains (laid out as the heads of one sequence), with one
+    BLAS thread.  Returns (o, S_T, seconds)."""
+    q, k, v, beta, log_alpha = args
+    from threadpoolctl import threadpool_limits
     from oracle import gated_delta_recurrence
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        o, S = gated_delta_recurrence(q, k, v, beta, log_alpha)
+        dt = time.perf_counter() - t0
+    return o, S, dt
+
+
+def _warm_worker(_):
+    import numpy  # noqa: F401  (imports paid before the timed map)
+    import oracle  # noqa: F401
+    import threadpoolctl  # noqa: F401
+    return os.getpid()
+
+
+def chain_groups(q, k, v, beta, log_alpha, nproc):
+    """Split [B, T, H, D] inputs into `nproc` groups of whole (batch, head)
+    chains, each laid out as the heads of one sequence ([1, T, n, D]).
+    Returns the groups and, per group, the flat chain indices (b * H + h)."""
+    import numpy as np
+    B, T, H, _ = q.shape
+    chains = np.arange(B * H)
+    parts = [p for p in np.array_split(chains, nproc) if len(p)]
+
+    def take(x, idx):
+        if x is None:
+            return None
+        xt = np.moveaxis(x, 1, 2).reshape((B * H, T) + x.shape[3:])   # [chain, T, ...]
+        return np.moveaxis(xt[idx], 0, 1)[None]                        # [1, T, n, ...]
+    groups = [(take(q, p), take(k, p), take(v, p), take(beta, p), take(log_alpha, p))
+              for p in parts]
+    return groups, parts
+
+
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    inp = W.make_chunk_inputs(batches, w.T, w.H, w.Dk, w.Dv, w.gate, w.in_dtype, seed=0,
-                              device="cpu", alpha_mu=w.alpha_mu, alpha_sigma=w.alpha_sigma)
-    a = {k: W.to_f64(v) for k, v in inp.items()}
-    t0 = time.perf_counter()
-    if threadpool_limits is not None:
-        with threadpool_limits(1):
-            gated_delta_recurrence(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"])
-    else:
-        gated_delta_recurrence(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"])
-    dt = time.perf_counter() - t0
-    tokens = batches * w.T
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{batches} of {w.B} sequences x {w.H} heads x {w.T} tokens "
-                      f"({tokens * w.H} token-heads, {dt:.1f} s wall, fp64 numpy, 1 thread)"}
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def rel_err(got, ref):
+    """max |got - ref| / RMS(ref), in float64."""
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref * ref)))
+
+
+def cpu_baseline(torch, w, kept, nproc=None):
+    """The fp64 oracle over every chain of the timed headline run, on that
+    run's inputs copied from the device, split over the host cores (one
+    process per core, one BLAS thread each).  Returns the baseline record
+    and the parity of the run's o and final state against the oracle."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import numpy as np
+    inp = kept["inp"]
+
+    def host(t):   # the rounded values, upcast exactly (fp32 holds every bf16)
+        return None if t is None else t.detach().to("cpu", torch.float32).numpy()
+    q, k, v, beta, la = (host(inp[n]) for n in ("q", "k", "v", "beta", "log_alpha"))
+    o_gpu = kept["o"].detach().float().cpu().numpy()
+    S_gpu = kept["S"].detach().float().cpu().numpy()
+    avail = len(os.sched_getaffinity(0))
+    P = nproc or min(avail, MAX_ORACLE_PROCS)
+    groups, parts = chain_groups(q, k, v, beta, la, P)
+    B, T, H, Dv = o_gpu.shape
+    o_ref = np.empty((B * H, T, Dv))
+    S_ref = np.empty((B * H,) + S_gpu.shape[2:])
+    # spawned workers (the parent holds a GPU context, so no fork); their
+    # start-up and imports are paid before the timed region
+    with cf.ProcessPoolExecutor(max_workers=len(groups),
+                                mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_warm_worker, range(len(groups))))
+        t0 = time.perf_counter()
+        results = list(ex.map(_oracle_worker, groups))
+        wall = time.perf_counter() - t0
+    for idx, (o, S, _) in zip(parts, results):
+        o_ref[idx] = np.moveaxis(o[0], 1, 0)
+        S_ref[idx] = S[0]
+    o_gpu_c = np.moveaxis(o_gpu, 1, 2).reshape(B * H, T, Dv)
+    S_gpu_c = S_gpu.reshape((B * H,) + S_gpu.shape[2:])
+    e_o, e_S = rel_err(o_gpu_c, o_ref), rel_err(S_gpu_c, S_ref)
+    tokens = B * T
+    base = {"value": tokens / wall, "unit": "tokens/s", "cores": len(groups), "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus_visible": avail,
+            "sample": f"the whole headline run: {B} sequences x {H} heads x {T} tokens "
+                      f"({B * H} chains in {len(groups)} processes of one BLAS thread, "
+                      f"{wall:.1f} s wall, per-process compute "
+                      f"{min(r[2] for r in results):.1f}-{max(r[2] for r in results):.1f} s, "
+                      f"fp64 numpy on the timed run's inputs)"}
+    parity = {"o_max_abs_over_rms": e_o, "S_T_max_abs_over_rms": e_S, "tol": PARITY_TOL,
+              "chains_checked": B * H, "chains_total": B * H,
+              "pass": bool(e_o <= PARITY_TOL and e_S <= PARITY_TOL),
+              "against": "fp64 oracle of this run (cpu_baseline)"}
+    return base, parity
+
+
+def decode_parity(torch, W, d, seqs=(0, 97, 255)):
+    """One fresh 128-step decode pass at the full shape (N=256 x H=32),
+    checked on sampled sequences (all heads, every step's output and the
+    final state) against the fp64 oracle recurrence run over the same steps."""
+    import numpy as np
+    import gated_delta_rule_28_amd as gdr
+    from oracle import gated_delta_recurrence
+    inp = W.make_decode_inputs(d.N, d.H, d.Dk, d.Dv, d.steps, d.gate, d.in_dtype, seed=0,
+                               device="cuda", alpha_mu=d.alpha_mu, alpha_sigma=d.alpha_sigma,
+                               state_std=d.state_std)
+    S0 = inp["state"].clone()
+    state = inp["state"]
+    o = torch.empty(d.steps, d.N, d.H, d.Dv, device="cuda", dtype=torch.float32)
+    for t in range(d.steps):
+        gdr.recurrent_step(inp["q"][t], inp["k"][t], inp["v"][t], inp["beta"][t],
+                           inp["log_alpha"][t], state, o=o[t])
+    torch.cuda.synchronize()
+    idx = list(seqs)
+
+    def pick(x):   # [steps, N, ...] -> [n, steps, ...] for the sampled sequences
+        return None if x is None else np.moveaxis(W.to_f64(x)[:, idx], 0, 1)
+    o_ref, S_ref = gated_delta_recurrence(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]),
+                                          pick(inp["beta"]), pick(inp["log_alpha"]),
+                                          W.to_f64(S0)[idx])
+    e_o = rel_err(np.moveaxis(W.to_f64(o)[:, idx], 0, 1), o_ref)
+    e_S = rel_err(W.to_f64(state)[idx], S_ref)
+    return {"o_max_abs_over_rms": e_o, "S_max_abs_over_rms": e_S, "tol": 1e-5,
+            "sequences_checked": idx, "heads": d.H, "steps": d.steps,
+            "pass": bool(e_o <= 1e-5 and e_S <= 1e-5)}
+
+
+def small_lines(torch, gdr, W, settle_s):
+    """The tiny fp32 workload (launch-latency bound: microseconds per call,
+    warm) and the B=4, H=8, T=2048 DeltaNet / Gated DeltaNet workloads,
+    timed cold (a 512 MiB write between calls: their inputs fit the 256 MB
+    last-level cache) and warm."""
+    out = {}
+    tiny = W.by_name("gdn_f32_tiny")
+    step, _, _ = chunk_setup(torch, gdr, W, tiny, torch.float32)
+    _, per = time_launches(torch, step, 200, 10, settle_s)
+    wall, _ = time_launches(torch, step, 200, 0)
+    out["tiny_fp32"] = {"workload": tiny.name, "unit": "us per call",
+                        "event_us": {"mean": 1e3 * statistics.fmean(per),
+                                     "median": 1e3 * statistics.median(per),
+                                     "min": 1e3 * min(per)},
+                        "wall_us_per_call": 1e6 * wall / 200,
+                        "note": "launch-latency bound (64 tokens, d = 16): no roofline"}
+    for key, name in (("deltanet_b4h8", "deltanet_bf16_b4h8t2048"),
+                      ("gdn_b4h8", "gdn_bf16_b4h8t2048")):
+        wl = W.by_name(name)
+        cold = chunk_line(torch, gdr, W, wl, 20, 3, torch.float32, settle_s, cold=True)
+        warm = chunk_line(torch, gdr, W, wl, 20, 3, torch.float32, 0.0)
+        out[key] = {"workload": name, "unit": "tokens/s",
+                    "cold": {"value": wl.B * wl.T / (cold["kernel_ms"]["median"] * 1e-3),
+                             "kernel_ms": cold["kernel_ms"], "roofline": cold["roofline"]},
+                    "warm": {"value": wl.B * wl.T / (warm["kernel_ms"]["median"] * 1e-3),
+                             "kernel_ms": warm["kernel_ms"], "roofline": warm["roofline"]},
+                    "kernel": cold["kernel"], "kernel_chunk": cold["kernel_chunk"],
+                    "note": "cold: 512 MiB written between timed calls (untimed); "
+                            "warm: back-to-back calls"}
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -318,6 +552,13 @@ def run_counter_targets(torch, gdr, W, reps=3):
         torch.abs(src, out=dst)
     torch.cuda.synchronize()
     print(f"counters: copy {COPY_BYTES} bytes x{reps}", flush=True)
+    # a bf16 GEMM of known size: 2 N^3 flops, the check of the MFMA counter scale
+    a = torch.randn(GEMM_N, GEMM_N, device="cuda").to(torch.bfloat16)
+    b = torch.randn(GEMM_N, GEMM_N, device="cuda").to(torch.bfloat16)
+    for _ in range(reps):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    print(f"counters: bf16 GEMM {GEMM_N}^3 x{reps}", flush=True)
 
 
 def _pmc_means(d, counter):
@@ -398,6 +639,69 @@ def summarize_pmc(fetch_dir, write_dir, command, out_dir=PROFILES):
     return 0
 
 
+def summarize_mfma(ops_dir, util_dir, command, out_dir=PROFILES):
+    """Write profiles/mfma_<kernel>_<workload>.txt from a run of the MFMA
+    operation and busy-cycle counters and a run of the derived MfmaUtil of
+    `bench.py --only counters`."""
+    import workloads as W
+    mops = _pmc_means(ops_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    insts = _pmc_means(ops_dir, "SQ_INSTS_MFMA")
+    busy = _pmc_means(ops_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    util = _pmc_means(util_dir, "MfmaUtil")
+
+    def mean_of(per, pat):
+        vals = [v for (k, _), v in per.items() if pat in k]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    gm, ngm = mean_of(mops, GEMM_REGEX)
+    gemm_flops = 2.0 * GEMM_N ** 3
+    gemm_ratio = (gm * 512.0 / gemm_flops) if gm else None
+    os.makedirs(out_dir, exist_ok=True)
+    kda = W.by_name("kda_bf16_b2h32t8192")
+    targets = [("chunk_fwd_bf16_kernel", W.HEADLINE.name,
+                chunk_alg_flops(W.HEADLINE, KERNEL_CHUNK["scalar"])),
+               ("chunk_fwd_kda_kernel", kda.name, chunk_alg_flops(kda, KERNEL_CHUNK["channel"]))]
+    for kern, wname, alg in targets:
+        m, nm = mean_of(mops, kern)
+        u, nu = mean_of(util, kern)
+        ni, _ = mean_of(insts, kern)
+        nb, _ = mean_of(busy, kern)
+        if m is None or u is None:
+            print(f"{kern}: no dispatches in the counter runs", file=sys.stderr)
+            continue
+        issued = m * 512.0
+        lines = [
+            f"# MFMA counters of {kern} on {wname}, from rocprofv3",
+            "# counter runs (each on its own):",
+            f"#   {command.format(counter='SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES', dir=ops_dir)}",
+            f"#   {command.format(counter='MfmaUtil', dir=util_dir)}",
+            f"# summary: python bench.py --summarize-mfma {ops_dir} {util_dir}",
+            "# mfma_busy_frac = MfmaUtil / 100, the tool's derived metric: MFMA-busy",
+            "#   SIMD cycles summed over the GPU / (GPU-active cycles x 1024 SIMDs).",
+            "# issued_bf16_flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the tool's",
+            "#   MfmaFlopsBF16); it counts every hi/lo split product the kernel issues.",
+            f"# scale check: a bf16 GEMM of {GEMM_N}^3 (2 N^3 = {gemm_flops:.4e} flops) in the same",
+            "#   run reads MOPS x 512 / (2 N^3) = gemm_issued_over_exact below.",
+            f"kernel: {kern}",
+            f"workload: {wname}",
+            f"source_sha256: {source_hash(kern)}",
+            f"dispatches: ops {nm}, util {nu}",
+            f"mfma_instructions_per_launch: {ni:.0f}" if ni is not None else "mfma_instructions_per_launch: none",
+            f"mfma_busy_simd_cycles_per_launch: {nb:.0f}" if nb is not None else "mfma_busy_simd_cycles_per_launch: none",
+            f"mfma_busy_frac: {u / 100.0:.4f}",
+            f"issued_bf16_flops_per_launch: {issued:.6e}",
+            f"algorithmic_flops_per_launch: {alg:.6e}",
+            f"issued_over_algorithmic: {issued / alg:.3f}",
+            f"gemm_dispatches: {ngm}",
+            f"gemm_issued_over_exact: {gemm_ratio:.4f}" if gemm_ratio else "gemm_issued_over_exact: none",
+        ]
+        path = mfma_file(kern, wname, out_dir)
+        with open(path, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {path}: busy {u:.1f}%, issued/alg {issued / alg:.2f}")
+    return 0
+
+
 # ---------------------------------------------------------------------------
 
 
@@ -414,12 +718,15 @@ def main(argv=None):
                     help="headline line only (no bf16-output, KDA and decode lines)")
     ap.add_argument("--only", choices=["counters"], default=None)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("OPS_DIR", "UTIL_DIR"))
     ap.add_argument("--pmc-command", default="rocprofv3 --pmc {counter} --kernel-include-regex "
-                    "'chunk_fwd|recurrent_step|AbsFunctor' --output-format csv -d {dir} -o pmc "
-                    "-- python3 bench.py --only counters")
+                    "'chunk_fwd|recurrent_step|AbsFunctor|Cijk' --output-format csv -d {dir} "
+                    "-o pmc -- python3 bench.py --only counters")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc, args.pmc_command)
+    if args.summarize_mfma:
+        return summarize_mfma(*args.summarize_mfma, args.pmc_command)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path here "
               "(every (batch, head) chain is independent, so batch or heads shard "
@@ -438,7 +745,10 @@ def main(argv=None):
         return 0
 
     w = W.HEADLINE
-    head = chunk_line(torch, gdr, W, w, args.steps, args.warmup, torch.float32, args.settle_s)
+    kept = {}
+    head = chunk_line(torch, gdr, W, w, args.steps, args.warmup, torch.float32, args.settle_s,
+                      keep=kept)
+    copy = None if args.no_extra else copy_ceiling(torch)
     rec = {
         "metric": "tokens/s gated-delta chunk fwd (H=16,d=128,T=4096) + % MFMA/HBM roofline",
         "value": head["value"],
@@ -457,9 +767,17 @@ def main(argv=None):
                    "gate": "scalar (Gated DeltaNet)", "kernel_chunk": head["kernel_chunk"],
                    "inputs": "bf16 q/k/v, fp32 beta/log_alpha, fp32 state, fp32 output",
                    "parallelism": "single GPU"},
-        "roofline": dict(head["roofline"], kernel=head["kernel"], kernel_ms=head["kernel_ms"]),
+        "roofline": dict(with_copy_frac(head["roofline"], copy), kernel=head["kernel"],
+                         kernel_ms=head["kernel_ms"]),
         "mfma_alg": head["mfma_alg"],
+        "mfma_counter": head["mfma_counter"],
+        "copy_ceiling": copy,
     }
+    if not args.no_cpu:
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(torch, w, kept)
+    kept.clear()
+    keys = ("workload", "value", "kernel", "kernel_chunk", "kernel_ms", "roofline", "mfma_alg",
+            "mfma_counter")
     if not args.no_extra:
         nb = max(5, args.steps // 2)
         b = chunk_line(torch, gdr, W, w, nb, 2, torch.bfloat16, args.settle_s)
@@ -468,29 +786,28 @@ def main(argv=None):
                               "roofline": b["roofline"]}
         kda = chunk_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2, torch.float32,
                          args.settle_s)
-        rec["kda"] = {k: kda[k] for k in ("workload", "value", "kernel", "kernel_chunk",
-                                          "kernel_ms", "roofline", "mfma_alg")}
+        rec["kda"] = {k: kda[k] for k in keys}
+        rec["kda"]["roofline"] = with_copy_frac(kda["roofline"], copy)
         rec["kda"]["unit"] = "tokens/s"
         # the erase-free variant (additive write) through the same kernels:
         # the Mamba-2 / SSD decay on the headline shape, GLA's on the KDA shape
         for key, wl in (("additive_scalar", w), ("additive_channel", W.by_name("kda_bf16_b2h32t8192"))):
             ln = chunk_line(torch, gdr, W, wl, nb, 2, torch.float32, args.settle_s, erase=False)
-            rec[key] = {k: ln[k] for k in ("workload", "value", "kernel", "kernel_chunk",
-                                           "kernel_ms", "roofline", "mfma_alg")}
+            rec[key] = {k: ln[k] for k in keys if k != "mfma_counter"}
             rec[key]["unit"] = "tokens/s"
             rec[key]["variant"] = "no erase term (S = a S + b k v^T)"
         # the fused prologue (q, k L2 normalisation, sigmoid b, softplus
         # decay) and SiLU output gate through the same kernels
         for key, wl in (("fused", w), ("kda_fused", W.by_name("kda_bf16_b2h32t8192"))):
             ln = chunk_line(torch, gdr, W, wl, nb, 2, torch.float32, args.settle_s, fused=True)
-            rec[key] = {k: ln[k] for k in ("workload", "value", "kernel", "kernel_chunk",
-                                           "kernel_ms", "roofline", "mfma_alg")}
+            rec[key] = {k: ln[k] for k in keys if k != "mfma_counter"}
             rec[key]["unit"] = "tokens/s"
             rec[key]["variant"] = ("fused prologue (q, k L2 norm, sigmoid b, softplus decay) "
                                    "and SiLU output gate")
         rec["decode"] = decode_line(torch, gdr, W, W.DECODE, settle_s=args.settle_s)
-    if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(W, w)
+        rec["decode"]["roofline"] = with_copy_frac(rec["decode"]["roofline"], copy)
+        rec["decode"]["parity"] = decode_parity(torch, W, W.DECODE)
+        rec.update(small_lines(torch, gdr, W, args.settle_s))
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -1,5 +1,6 @@
 // Chunkwise gated delta-rule forward in plain fp32 arithmetic (VALU), for
-// small heads (Dk = Dv <= 64) and for fp32 inputs, all three gates.
+// small heads (Dk = Dv <= 64) and for fp32 inputs (Dk = Dv <= 128), all
+// three gates.
 //
 // Same chunk algebra as the MFMA kernel (xhh.club digest "Transformer 入坑笔记
 // （五）": products inside a chunk, state carried between chunks, WY form via a
@@ -196,16 +197,22 @@ hipError_t by_gate(const ChunkArgs &a) {
 
 template <int D>
 hipError_t by_chunk(const ChunkArgs &a) {
-  const int c = a.chunk ? a.chunk : (D <= 16 ? 16 : 64);
-  if (c == 16) return by_gate<D, 16>(a);
-  if (c == 32) return by_gate<D, 32>(a);
-  return by_gate<D, 64>(a);
+  // the chunk only changes rounding; at D = 128 the kernel's LDS holds
+  // 16-token chunks (about 109 KB: the state and five 16 x 129 fp32 tiles)
+  if constexpr (D == 128) {
+    return by_gate<D, 16>(a);
+  } else {
+    const int c = a.chunk ? a.chunk : (D <= 16 ? 16 : 64);
+    if (c == 16) return by_gate<D, 16>(a);
+    if (c == 32) return by_gate<D, 32>(a);
+    return by_gate<D, 64>(a);
+  }
 }
 
 }  // namespace
 
 bool chunk_fwd_small_supported(const ChunkArgs &a) {
-  return (a.D == 16 || a.D == 32 || a.D == 64) &&
+  return (a.D == 16 || a.D == 32 || a.D == 64 || (a.D == 128 && !a.in_bf16)) &&
          (a.chunk == 0 || a.chunk == 16 || a.chunk == 32 || a.chunk == 64);
 }
 
@@ -213,7 +220,8 @@ hipError_t launch_chunk_fwd_small(const ChunkArgs &a) {
   switch (a.D) {
     case 16: return by_chunk<16>(a);
     case 32: return by_chunk<32>(a);
-    default: return by_chunk<64>(a);
+    case 64: return by_chunk<64>(a);
+    default: return by_chunk<128>(a);
   }
 }
 

@@ -115,9 +115,10 @@ const char *gdr_status_str(int status);
  * Q&A).  The result does not depend on `chunk` beyond rounding.
  *
  *   B, T, H      batch, tokens per sequence (any T >= 1), heads
- *   Dk, Dv       key / value head sizes (supported: Dk == Dv in {16, 32, 64, 128}
- *                with bf16 q/k/v, Dk == Dv in {16, 32, 64} with fp32 q/k/v;
- *                other combinations return GDR_EUNSUPPORTED).  With bf16
+ *   Dk, Dv       key / value head sizes (supported: Dk == Dv in {16, 32, 64, 128},
+ *                bf16 or fp32 q/k/v; other combinations return
+ *                GDR_EUNSUPPORTED; fp32 q/k/v and heads below 64 run a plain
+ *                fp32 kernel, accurate to fp32 rounding).  With bf16
  *                q/k/v, no gate or the scalar gate and Dk = 128, H * Dk must
  *                stay below 34,000,000 (the kernel addresses one chunk's rows
  *                of a tensor with 32-bit offsets); with the per-channel

@@ -82,8 +82,9 @@ def step(**kw):
     (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
     (dict(Dk=96, Dv=96), _abi.GDR_EUNSUPPORTED),
     (dict(chunk=48), _abi.GDR_EUNSUPPORTED),
-    (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),     # fp32 inputs need Dk <= 64
-    (dict(gate=_abi.GDR_GATE_CHANNEL, in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
+    (dict(in_dtype=_abi.GDR_F32, Dk=96, Dv=96), _abi.GDR_EUNSUPPORTED),
+    (dict(in_dtype=_abi.GDR_F32, Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
+    (dict(in_dtype=_abi.GDR_F32, chunk=48), _abi.GDR_EUNSUPPORTED),
     # one chunk's rows of a [*, H, 128] tensor must span less than 4 GiB
     (dict(H=300000), _abi.GDR_EUNSUPPORTED),
     # per-channel gate: one chunk's rows of the [*, H, 128] fp32 log decays

@@ -71,3 +71,56 @@ def test_counter_summary_scales_by_the_copy(tmp_path):
     text = open(path).read().replace(bench.source_hash("chunk_fwd_bf16_kernel"), "0" * 16)
     open(path, "w").write(text)
     assert bench.read_traffic("chunk_fwd_bf16_kernel", W.HEADLINE.name, root=str(out)) is None
+
+
+def test_chain_groups_cover_every_chain_once():
+    import numpy as np
+    B, T, H, D = 2, 5, 3, 4
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((B, T, H, D))
+    beta = rng.standard_normal((B, T, H))
+    groups, parts = bench.chain_groups(q, q, q, beta, None, 4)
+    assert sorted(np.concatenate(parts).tolist()) == list(range(B * H))
+    for (gq, _, _, gb, gla), idx in zip(groups, parts):
+        assert gla is None and gq.shape == (1, T, len(idx), D) and gb.shape == (1, T, len(idx))
+        for j, c in enumerate(idx):
+            assert np.array_equal(gq[0, :, j], q[c // H, :, c % H])
+            assert np.array_equal(gb[0, :, j], beta[c // H, :, c % H])
+
+
+def test_cpu_baseline_splits_chains_and_checks_parity():
+    """The oracle baseline over two processes reproduces the oracle run on
+    the whole input, and its parity field catches a wrong output value."""
+    import torch
+    from oracle import gated_delta_recurrence
+    w = W.HEADLINE
+    inp = W.make_chunk_inputs(2, 9, 3, 16, 16, "scalar", "bf16", seed=3)
+    a = {k: W.to_f64(v) for k, v in inp.items()}
+    o, S = gated_delta_recurrence(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"])
+    kept = {"inp": inp, "o": torch.from_numpy(o).float(), "S": torch.from_numpy(S).float()}
+    base, parity = bench.cpu_baseline(torch, w, kept, nproc=2)
+    assert base["cores"] == 2 and base["kind"] == "oracle"
+    assert parity["pass"] and parity["o_max_abs_over_rms"] < 1e-6
+    assert parity["chains_checked"] == 6
+    o_bad = o.copy()
+    o_bad[1, 4, 2, 7] += 0.01 * float((o * o).mean() ** 0.5)
+    kept["o"] = torch.from_numpy(o_bad).float()
+    _, parity = bench.cpu_baseline(torch, w, kept, nproc=2)
+    assert not parity["pass"] and parity["o_max_abs_over_rms"] > 5e-3
+
+
+def test_mfma_summary(tmp_path):
+    kern = "void gdr::(anonymous namespace)::chunk_fwd_bf16_kernel<128, 64, float, 1>(...)"
+    gemm = "Cijk_Alik_Bljk_BBS_BH_MT256x256x64"
+    gemm_mops = 2.0 * bench.GEMM_N ** 3 / 512.0
+    _write_csv(tmp_path / "o", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               [(gemm, gemm_mops)] * 2 + [(kern, 1.0e8), (kern, 1.0e8)])
+    _write_csv(tmp_path / "u", "MfmaUtil", [(gemm, 80.0), (kern, 25.0), (kern, 27.0)])
+    out = tmp_path / "prof"
+    assert bench.summarize_mfma(str(tmp_path / "o"), str(tmp_path / "u"),
+                                "cmd {counter} {dir}", out_dir=str(out)) == 0
+    got = bench.read_mfma("chunk_fwd_bf16_kernel", W.HEADLINE.name, root=str(out))
+    assert got["busy_frac"] == pytest.approx(0.26)
+    assert got["issued_flops_per_launch"] == pytest.approx(1.0e8 * 512)
+    text = open(bench.mfma_file("chunk_fwd_bf16_kernel", W.HEADLINE.name, str(out))).read()
+    assert "gemm_issued_over_exact: 1.0000" in text

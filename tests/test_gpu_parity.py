@@ -149,6 +149,47 @@ def test_chunk_small_fp32(D, chunk, gate, T):
     assert rel_err(np64(S), S_ref) <= F32_TOL
 
 
+@pytest.mark.parametrize("chunk", [0, 64])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("T", [1, 37, 100])
+def test_chunk_fp32_d128(chunk, gate, T):
+    """fp32 q/k/v at d = 128 (16-token chunks whatever `chunk` asks), with an
+    initial state and ragged tails, to the fp32 bar."""
+    say("chunk f32 d128", chunk, gate, T)
+    inp = with_state(W.make_chunk_inputs(2, T, 3, 128, 128, gate, "f32", seed=T + 1,
+                                         device=DEV))
+    o, S = run_chunk(inp, chunk=chunk)
+    o_ref, S_ref = oracle_on(inp)
+    assert rel_err(np64(o), o_ref) <= F32_TOL
+    assert rel_err(np64(S), S_ref) <= F32_TOL
+
+
+def test_chunk_fp32_d128_erase_free_and_fused():
+    say("chunk f32 d128 erase-free / fused")
+    from oracle import fused as F
+    inp = with_state(W.make_chunk_inputs(2, 45, 2, 128, 128, "channel", "f32", seed=8,
+                                         device=DEV))
+    o, S = run_chunk(inp, erase=False)
+    a = {k: np64(v) for k, v in inp.items()}
+    o_ref, S_ref = gated_delta_recurrence(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"],
+                                          a["initial_state"], erase=False)
+    assert rel_err(np64(o), o_ref) <= F32_TOL and rel_err(np64(S), S_ref) <= F32_TOL
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4)
+    xb = torch.randn(2, 45, 2, device=DEV, generator=g)
+    xd = -3.0 + torch.randn(2, 45, 2, 128, device=DEV, generator=g)
+    gate = torch.randn(2, 45, 2, 128, device=DEV, generator=g)
+    q2 = inp["q"] * 3.0
+    o, S = gdr.chunk_fwd(q2, inp["k"], inp["v"], xb, xd, inp["initial_state"], qk_l2norm=True,
+                         beta_sigmoid=True, decay="softplus", out_gate=gate)
+    torch.cuda.synchronize()
+    qf, kf, bf, lf = F.prologue(np64(q2), a["k"], np64(xb), np64(xd), qk_l2norm=True,
+                                beta_sigmoid=True, decay="softplus")
+    o_ref, S_ref = gated_delta_recurrence(qf, kf, a["v"], bf, lf, a["initial_state"])
+    o_ref = F.silu_gate(o_ref, np64(gate))
+    assert rel_err(np64(o), o_ref) <= F32_TOL and rel_err(np64(S), S_ref) <= F32_TOL
+
+
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 def test_chunk_small_bf16_inputs(gate):
     say("chunk small bf16", gate)
