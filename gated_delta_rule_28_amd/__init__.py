@@ -6,6 +6,7 @@ All arithmetic runs in the HIP kernels.
 
     o, S_T = chunk_fwd(q, k, v, beta, log_alpha, initial_state)
     o      = recurrent_step(q, k, v, beta, log_alpha, state)   # state in place
+    grads  = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final_state)
 
 Gate kind follows log_alpha: None -> DeltaNet (alpha = 1); [B, T, H] ->
 Gated DeltaNet (one decay per head); [B, T, H, Dk] -> KDA (one per channel).
@@ -24,8 +25,8 @@ import torch
 from . import _abi
 from ._abi import GdrError, abi_version, status_str, LIB_PATH
 
-__all__ = ["chunk_fwd", "recurrent_step", "GdrError", "abi_version", "status_str",
-           "LIB_PATH", "library_loaded"]
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_bwd", "chunk_bwd_workspace_bytes", "GdrError",
+           "abi_version", "status_str", "LIB_PATH", "library_loaded"]
 
 _DT = {torch.float32: _abi.GDR_F32, torch.bfloat16: _abi.GDR_BF16}
 
@@ -183,3 +184,71 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
     if st != _abi.GDR_OK:
         raise GdrError(st, "gdr_recurrent_step_ex")
     return o
+
+
+def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0):
+    """Bytes of device workspace chunk_bwd needs for inputs shaped like q
+    ([B, T, H, Dk]) and this gate (0 when the call is not supported)."""
+    B, T, H, Dk = q.shape
+    gate = _gate_of(log_alpha, (B, T, H), Dk)
+    return int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dk, int(chunk), _DT[q.dtype], gate))
+
+
+def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_final_state=None,
+              *, chunk=0, workspace=None, want_d_initial_state=True):
+    """Gradients of chunk_fwd's o and final state.
+
+    Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, no gate or the
+    per-head gate); d_o [B, T, H, Dv] in the dtype of q (None for zero) and
+    d_final_state [B, H, Dk, Dv] fp32 (None for zero).  Returns a dict with
+    dq, dk, dv (fp32, shaped like q, k, v), dbeta [B, T, H], dlog_alpha
+    (None without a gate, else [B, T, H]) and d_initial_state
+    [B, H, Dk, Dv] (None when want_d_initial_state is False).  `workspace`,
+    a uint8 GPU tensor of at least chunk_bwd_workspace_bytes, is allocated
+    with torch when not given.
+    """
+    _check_dev("q", q)
+    if q.dtype not in _DT:
+        raise TypeError("q/k/v must be bf16 or fp32")
+    for name, t in (("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("beta", beta, torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("expected q, k, v [B, T, H, D] (Dk = Dv)")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    if tuple(beta.shape) != (B, T, H):
+        raise ValueError("beta must be [B, T, H]")
+    gate = _gate_of(log_alpha, (B, T, H), Dk)
+    if log_alpha is not None:
+        _check_dev("log_alpha", log_alpha, torch.float32)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check_dev(name, t, torch.float32)
+            if tuple(t.shape) != (B, H, Dk, Dv):
+                raise ValueError(f"{name} must be [B, H, Dk, Dv]")
+    if d_o is None:
+        d_o = torch.zeros_like(v)
+    _check_dev("d_o", d_o, q.dtype)
+    if tuple(d_o.shape) != (B, T, H, Dv):
+        raise ValueError("d_o must be [B, T, H, Dv]")
+    f32 = dict(device=q.device, dtype=torch.float32)
+    out = {"dq": torch.empty(B, T, H, Dk, **f32), "dk": torch.empty(B, T, H, Dk, **f32),
+           "dv": torch.empty(B, T, H, Dv, **f32), "dbeta": torch.empty(B, T, H, **f32),
+           "dlog_alpha": None if log_alpha is None else torch.empty(B, T, H, **f32),
+           "d_initial_state": torch.empty(B, H, Dk, Dv, **f32) if want_d_initial_state else None}
+    need = int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    else:
+        _check_dev("workspace", workspace, torch.uint8)
+    st = _abi.gdr_chunk_bwd(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate, q.data_ptr(),
+                            k.data_ptr(), v.data_ptr(), beta.data_ptr(), _ptr(log_alpha),
+                            _ptr(initial_state), d_o.data_ptr(), _ptr(d_final_state),
+                            out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(),
+                            out["dbeta"].data_ptr(), _ptr(out["dlog_alpha"]),
+                            _ptr(out["d_initial_state"]), workspace.data_ptr(),
+                            workspace.numel(), _stream(q.device))
+    if st != _abi.GDR_OK:
+        raise GdrError(st, "gdr_chunk_bwd")
+    return out

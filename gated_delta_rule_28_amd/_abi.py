@@ -12,7 +12,8 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EHIP = 0, -1, -2, -3
+GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EHIP, GDR_EWORKSPACE = 0, -1, -2, -3, -4
+ABI_VERSION = 2
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_NONE, GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1, 2
 GDR_NO_ERASE = 0x100   # OR'd into a gate: additive write, no erase term
@@ -28,6 +29,9 @@ SIGNATURES = {
     "gdr_recurrent_step": (_c_int, [_c_int] * 7 + [_vp] * 8),
     "gdr_chunk_fwd_ex": (_c_int, [_c_int] * 10 + [_vp] * 10),
     "gdr_recurrent_step_ex": (_c_int, [_c_int] * 8 + [_vp] * 9),
+    "gdr_chunk_fwd_workspace_bytes": (_sz, [_c_int] * 9),
+    "gdr_chunk_bwd_workspace_bytes": (_sz, [_c_int] * 8),
+    "gdr_chunk_bwd": (_c_int, [_c_int] * 8 + [_vp] * 15 + [_sz, _vp]),
 }
 
 _lib = None
@@ -57,7 +61,7 @@ def load():
                 fn = getattr(lib, name)
                 fn.restype = res
                 fn.argtypes = args
-            if lib.gdr_abi_version() != 1:
+            if lib.gdr_abi_version() != ABI_VERSION:
                 raise RuntimeError("libgdr.so ABI version mismatch")
             _lib = lib
     return _lib
@@ -98,3 +102,20 @@ def gdr_recurrent_step_ex(N, H, Dk, Dv, in_dtype, out_dtype, gate, fuse, q, k, v
     """Raw call of the C entry point with integer sizes and raw pointers."""
     return load().gdr_recurrent_step_ex(N, H, Dk, Dv, in_dtype, out_dtype, gate, fuse, q, k, v,
                                         beta, log_alpha, out_gate, state, o, stream)
+
+
+def gdr_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, out_dtype, gate):
+    return load().gdr_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, out_dtype, gate)
+
+
+def gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, gate):
+    return load().gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, chunk, in_dtype, gate)
+
+
+def gdr_chunk_bwd(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
+                  initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                  d_initial_state, workspace, workspace_bytes, stream):
+    """Raw call of the C entry point with integer sizes and raw pointers."""
+    return load().gdr_chunk_bwd(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
+                                initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                                d_initial_state, workspace, workspace_bytes, stream)

@@ -63,6 +63,7 @@ const char *gdr_status_str(int status) {
     case GDR_EINVAL: return "GDR_EINVAL: invalid argument";
     case GDR_EUNSUPPORTED: return "GDR_EUNSUPPORTED: shape/dtype/chunk not implemented";
     case GDR_EHIP: return "GDR_EHIP: HIP runtime error on launch";
+    case GDR_EWORKSPACE: return "GDR_EWORKSPACE: workspace missing, misaligned or too small";
     default: return "unknown gdr status";
   }
 }
@@ -117,6 +118,91 @@ int gdr_chunk_fwd_ex(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtyp
   else if (gdr::chunk_fwd_kda_supported(a)) e = gdr::launch_chunk_fwd_kda(a);
   else if (gdr::chunk_fwd_small_supported(a)) e = gdr::launch_chunk_fwd_small(a);
   else return GDR_EUNSUPPORTED;
+  return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+size_t gdr_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     int in_dtype, int out_dtype, int gate) {
+  // every forward kernel keeps its intermediates in registers and LDS
+  (void)B; (void)T; (void)H; (void)Dk; (void)Dv; (void)chunk;
+  (void)in_dtype; (void)out_dtype; (void)gate;
+  return 0;
+}
+
+namespace {
+
+// workspace bytes of a supported backward call with at least one token
+size_t bwd_workspace(long B, long T, long H, int D) {
+  const long nchunks = (T + gdr::kBwdChunk - 1) / gdr::kBwdChunk;
+  return (size_t)(B * H * nchunks) * (size_t)gdr::bwd_ws_floats_per_chunk(D) * sizeof(float);
+}
+
+bool bwd_shape_ok(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate) {
+  if (Dk != Dv || !(chunk == 0 || chunk == 16 || chunk == 32 || chunk == 64)) return false;
+  if (!gdr::chunk_bwd_supported(Dk, in_dtype == GDR_BF16, gate_kind(gate), erases(gate), H))
+    return false;
+  // one workgroup per (chain, chunk) in the gradient kernel
+  const long nchunks = ((long)T + gdr::kBwdChunk - 1) / gdr::kBwdChunk;
+  return (long)B * H * nchunks < 0x7FFFFFFFL;
+}
+
+}  // namespace
+
+size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     int in_dtype, int gate) {
+  if (B <= 0 || T <= 0 || H <= 0 || !valid_dtype(in_dtype) || !valid_gate(gate)) return 0;
+  if (!bwd_shape_ok(B, T, H, Dk, Dv, chunk, in_dtype, gate)) return 0;
+  return bwd_workspace(B, T, H, Dk);
+}
+
+int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
+                  const void *q, const void *k, const void *v, const float *beta,
+                  const float *log_alpha, const float *initial_state, const void *d_o,
+                  const float *d_final_state, float *dq, float *dk, float *dv, float *dbeta,
+                  float *dlog_alpha, float *d_initial_state, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
+  if (!valid_dtype(in_dtype) || !valid_gate(gate)) return GDR_EINVAL;
+  if ((gate_kind(gate) == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
+  if ((gate_kind(gate) == GDR_GATE_NONE) != (dlog_alpha == nullptr)) return GDR_EINVAL;
+  if ((initial_state && !aligned16(initial_state)) || (d_final_state && !aligned16(d_final_state)) ||
+      (d_initial_state && !aligned16(d_initial_state)))
+    return GDR_EINVAL;
+  if (!bwd_shape_ok(B, T, H, Dk, Dv, chunk, in_dtype, gate)) return GDR_EUNSUPPORTED;
+  if ((long)B * H == 0) return GDR_OK;                   // nothing to compute
+  if (T == 0) {                                          // no tokens: dS_0 = dS_T
+    if (!d_initial_state) return GDR_OK;
+    hipError_t e = gdr::launch_state_passthrough(d_final_state, d_initial_state,
+                                                 (long)B * H * Dk * Dv, stream);
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+  }
+  if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta) return GDR_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned(beta, 4) || !aligned(dbeta, 4) ||
+      (log_alpha && !aligned(log_alpha, 4)) || (dlog_alpha && !aligned(dlog_alpha, 4)))
+    return GDR_EINVAL;
+  const size_t need = bwd_workspace(B, T, H, Dk);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
+    return GDR_EWORKSPACE;
+
+  gdr::BwdArgs a;
+  a.B = B; a.T = T; a.H = H; a.D = Dk;
+  a.gate = gate_kind(gate);
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;
+  a.d_initial_state = d_initial_state;
+  // workspace partitions: h, dh [chain][chunk][D][D]; R, U, dY [chain][chunk][C][D]
+  const long nblk = (long)B * H * ((T + gdr::kBwdChunk - 1) / gdr::kBwdChunk);
+  float *w = static_cast<float *>(workspace);
+  a.ws_h = w;
+  a.ws_dh = a.ws_h + nblk * Dk * Dk;
+  a.ws_r = a.ws_dh + nblk * Dk * Dk;
+  a.ws_u = a.ws_r + nblk * gdr::kBwdChunk * Dk;
+  a.ws_dy = a.ws_u + nblk * gdr::kBwdChunk * Dk;
+  a.stream = stream;
+  hipError_t e = gdr::launch_chunk_bwd_passes(a);
+  if (e == hipSuccess) e = gdr::launch_chunk_bwd_grads(a);
   return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 

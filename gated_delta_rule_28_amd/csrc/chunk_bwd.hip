@@ -1,0 +1,420 @@
+// Chunk-parallel gradients of the chunkwise gated delta-rule forward
+// (bf16 q/k/v/dO, fp32 state, MFMA, gfx950).
+//
+// The forward evaluated per chunk (xhh.club digest "Transformer 入坑笔记（五）",
+// chunked computation; page "NLP——线性注意力相关总结", sections "Gated DeltaNet
+// (GDN)" and "DeltaNet") with entering state h, g the in-chunk cumulative log
+// decay, gam = e^g, ec = e^{g_last - g}, Gam_rs = e^{g_r - g_s}:
+//
+//   M = strict_lower(K K^T o Gam),  A = diag(b) M,  T = (I + A)^{-1}
+//   P = lower_incl(Q K^T o Gam)
+//   R = V - diag(gam) K h,          U = T diag(b) R
+//   O = diag(gam) Q h + P U,        h' = gam_last h + K^T diag(ec) U
+//
+// is differentiated in reverse.  Two sequential passes (the forward kernel in
+// its recompute and reverse modes) leave in the workspace, per chunk, h, R and
+// U and, from the reverse pass, dh (the gradient of the state leaving the
+// chunk) and dY = T^T dU with dU = diag(ec) K dh + P^T dO.  Given those, every
+// chunk's gradients are independent:
+//
+//   dR = diag(b) dY = dV          dA = -strict_lower(dY U^T)
+//   dP = lower_incl(dO U^T)       dM = diag(b) dA
+//   db_r  = sum_v dY_rv R_rv + sum_s dA_rs M_rs
+//   dQ = diag(gam) dO h^T + (dP o Gam) K
+//   dK = -diag(gam) dR h^T + diag(ec) U dh^T + (dM o Gam) K + (dM o Gam)^T K
+//        + (dP o Gam)^T Q
+//   dg_r  = gam_r q_r.(dO h^T)_r - gam_r k_r.(dR h^T)_r - ec_r k_r.(U dh^T)_r
+//           + rowsum_r(E) - colsum_r(E),   E = dM o M + dP o P
+//   dg_last += sum_r ec_r k_r.(U dh^T)_r + gam_last <h, dh>
+//   dlog a_t = sum_{r >= t} dg_r           (g is a within-chunk cumsum)
+//
+// One workgroup of four waves per (chain, chunk).  q, k and dO are exact
+// bf16 and enter MFMAs unsplit; every derived operand (h, dh, U, dR, dY,
+// the n x n gradient matrices) is split into bf16 hi + lo, as in the forward
+// kernels, so products carry ~16 significant bits with fp32 accumulation.
+#include "common.h"
+#include "internal.h"
+#include "mfma_util.h"
+
+namespace gdr {
+namespace {
+
+constexpr int C = kBwdChunk;   // tokens per chunk (the forward kernel's)
+constexpr int NW = 4;          // waves per workgroup
+
+template <int DK>
+struct __align__(16) BwdSmem {
+  static constexpr int LDB = DK + 8;   // bf16 row stride of q, k, dO: 16-byte row reads of
+                                       // 16 rows hit distinct banks
+  static constexpr int LDF = DK + 4;   // fp32 row stride of U, dY
+  static constexpr int LDN = C + 1;    // fp32 [C][C]
+  static constexpr int LDX = C + 8;    // bf16 [C][C] hi / lo
+  bf16 Q[C][LDB], K[C][LDB], D[C][LDB];
+  float U[C][LDF], Y[C][LDF];
+  float G[C][LDN];                     // dM o M + dP o P
+  float Hm[C][LDN];                    // dA o M
+  bf16 XPh[C][LDX], XPl[C][LDX];       // dP o Gam, lower inclusive
+  bf16 XMh[C][LDX], XMl[C][LDX];       // dM o Gam, strictly lower
+  float g[C], gam[C], ec[C], beta[C];
+  float dba[C];                        // sum_v dY_rv R_rv
+  float dg[C];
+  float dgp[NW][C];                    // per-wave row terms of dg
+  float tlast[NW], hdh[NW];            // per-wave sums for dg_last
+};
+
+// two fp32 float4 (8 consecutive values) -> bf16 hi / lo, times a factor
+__device__ __forceinline__ void split8(const float *p, float f, bf16x8 &hi, bf16x8 &lo) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p) * f;
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4) * f;
+  bf16x4 ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  hi = cat(ah, bh);
+  lo = cat(al, bl);
+}
+__device__ __forceinline__ void split8g(const float *p, bf16x8 &hi, bf16x8 &lo, float &dot,
+                                        const float *q) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  const f32x4 c = *reinterpret_cast<const f32x4 *>(q);
+  const f32x4 d = *reinterpret_cast<const f32x4 *>(q + 4);
+  dot += (a[0] * c[0] + a[1] * c[1]) + (a[2] * c[2] + a[3] * c[3]) +
+         (b[0] * d[0] + b[1] * d[1]) + (b[2] * d[2] + b[3] * d[3]);
+  bf16x4 ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  hi = cat(ah, bh);
+  lo = cat(al, bl);
+}
+
+// sum over the 16 lanes of each row of a wave (lanes 16 j .. 16 j + 15)
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+__device__ __forceinline__ float sum64(float x) {
+  x = sum16(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int DK, int GATE>
+__global__ void __launch_bounds__(64 * NW, 2)
+chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+                      const float *__restrict__ beta, const float *__restrict__ log_alpha,
+                      const bf16 *__restrict__ d_o, const float *__restrict__ ws_h,
+                      const float *__restrict__ ws_r, const float *__restrict__ ws_u,
+                      const float *__restrict__ ws_dh, const float *__restrict__ ws_dy,
+                      float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+                      float *__restrict__ dbeta, float *__restrict__ dlog_alpha, int B, int T,
+                      int H) {
+  constexpr int DV = DK;
+  constexpr int NTW = DK / 64;         // 16-column dk tiles per wave
+  constexpr int KKV = DV / 32;         // 32-deep k steps over dv
+  using SM = BwdSmem<DK>;
+  static_assert(sizeof(SM) <= 80 * 1024, "two workgroups per CU");
+  __shared__ SM sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nchunks = (T + C - 1) / C;
+  const int chain = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+  const int bb = chain / H, hh = chain % H;
+  const int n = min(C, T - c * C);                       // valid rows of this chunk
+  const long row0 = ((long)bb * T + (long)c * C) * H + hh;   // token row of the chunk's row 0
+  auto trow = [&](int r) { return row0 + (long)r * H; };
+  const long wsS = ((long)chain * nchunks + c) * (DK * DV);   // h, dh of this chunk
+  const long wsR = ((long)chain * nchunks + c) * (C * DV);    // R, U, dY of this chunk
+
+  // ---- P0: inputs into LDS; dV = b dY; sum_v dY R; decays ----
+  for (int i = tid; i < C * SM::LDX; i += 64 * NW) {     // upper-right blocks stay zero
+    (&sm.XPh[0][0])[i] = (bf16)0.0f;
+    (&sm.XPl[0][0])[i] = (bf16)0.0f;
+    (&sm.XMh[0][0])[i] = (bf16)0.0f;
+    (&sm.XMl[0][0])[i] = (bf16)0.0f;
+  }
+  for (int i = tid; i < C * SM::LDN; i += 64 * NW) {
+    (&sm.G[0][0])[i] = 0.0f;
+    (&sm.Hm[0][0])[i] = 0.0f;
+  }
+  {
+    constexpr int BPR = DK / 8;                          // 16-byte blocks per bf16 row
+#pragma unroll
+    for (int i = tid; i < C * BPR; i += 64 * NW) {
+      const int r = i / BPR, blk = i % BPR;
+      u32x4 xq = {0u, 0u, 0u, 0u}, xk = xq, xd = xq;
+      if (r < n) {
+        const long off = trow(r) * DK + 8 * blk;
+        xq = *reinterpret_cast<const u32x4 *>(q + off);
+        xk = *reinterpret_cast<const u32x4 *>(k + off);
+        xd = *reinterpret_cast<const u32x4 *>(d_o + off);
+      }
+      *reinterpret_cast<u32x4 *>(&sm.Q[r][8 * blk]) = xq;
+      *reinterpret_cast<u32x4 *>(&sm.K[r][8 * blk]) = xk;
+      *reinterpret_cast<u32x4 *>(&sm.D[r][8 * blk]) = xd;
+    }
+  }
+  {
+    // 8 threads per row, DV / 32 float4 each
+    constexpr int F4 = DV / 32;
+    const int r = tid >> 3, f0 = (tid & 7) * F4;
+    const float b = r < n ? beta[trow(r)] : 0.0f;
+    float dot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < F4; ++j) {
+      const int col = 4 * (f0 + j);
+      const f32x4 u = *reinterpret_cast<const f32x4 *>(ws_u + wsR + r * DV + col);
+      const f32x4 y = *reinterpret_cast<const f32x4 *>(ws_dy + wsR + r * DV + col);
+      const f32x4 rr = *reinterpret_cast<const f32x4 *>(ws_r + wsR + r * DV + col);
+      *reinterpret_cast<f32x4 *>(&sm.U[r][col]) = u;
+      *reinterpret_cast<f32x4 *>(&sm.Y[r][col]) = y;
+      dot += (y[0] * rr[0] + y[1] * rr[1]) + (y[2] * rr[2] + y[3] * rr[3]);
+      if (r < n) *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + col) = y * b;
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    if ((tid & 7) == 0) sm.dba[r] = dot;
+  }
+  if (wave == 0) {
+    // in-chunk cumulative log decay (rows past the end carry log a = 0)
+    const float la = (GATE == kGateScalar && lane < n) ? log_alpha[trow(lane)] : 0.0f;
+    float gs = la;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const float y = __shfl_up(gs, d);
+      if ((lane & 31) >= d) gs += y;
+    }
+    const float glast = __shfl(gs, C - 1);
+    if (lane < C) {
+      sm.g[lane] = gs;
+      sm.gam[lane] = (GATE == kGateNone) ? 1.0f : __expf(gs);
+      sm.ec[lane] = (GATE == kGateNone) ? 1.0f : __expf(glast - gs);
+      sm.beta[lane] = lane < n ? beta[trow(lane)] : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // ---- P1: per 16x16 tile position (waves 0..2): P, M, dA, dP; the
+  //      elementwise terms and the decayed gradient matrices ----
+  if (wave < 3) {
+    const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+    f32x4 pt = {0.f, 0.f, 0.f, 0.f}, mt = pt, at = pt, dt = pt;
+#pragma unroll
+    for (int kk = 0; kk < DK / 32; ++kk) {
+      const int kc = 32 * kk + 8 * lg;
+      const bf16x8 qa = ld8(&sm.Q[16 * ti + lr][kc]);
+      const bf16x8 ka = ld8(&sm.K[16 * ti + lr][kc]);
+      const bf16x8 kb = ld8(&sm.K[16 * tj + lr][kc]);
+      const bf16x8 da = ld8(&sm.D[16 * ti + lr][kc]);
+      bf16x8 yh, yl, uh, ul;
+      split8(&sm.Y[16 * ti + lr][kc], 1.0f, yh, yl);
+      split8(&sm.U[16 * tj + lr][kc], 1.0f, uh, ul);
+      pt = mfma_bf16(qa, kb, pt);
+      mt = mfma_bf16(ka, kb, mt);
+      at = mfma_bf16(yh, uh, at);
+      at = mfma_bf16(yl, uh, at);
+      at = mfma_bf16(yh, ul, at);
+      dt = mfma_bf16(da, uh, dt);
+      dt = mfma_bf16(da, ul, dt);
+    }
+    // lane holds rows 16 ti + 4 lg + e of column s = 16 tj + lr
+    const int s = 16 * tj + lr;
+    const float gs = sm.g[s];
+    f32x4 xp, xm;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ti + 4 * lg + e;
+      const float gm = (GATE == kGateNone) ? 1.0f : __expf(sm.g[r] - gs);
+      const float P = (s <= r) ? pt[e] * gm : 0.0f;
+      const float M = (s < r) ? mt[e] * gm : 0.0f;
+      const float dA = (s < r) ? -at[e] : 0.0f;
+      const float dP = (s <= r) ? dt[e] : 0.0f;
+      const float dM = sm.beta[r] * dA;
+      sm.Hm[r][s] = dA * M;
+      sm.G[r][s] = dM * M + dP * P;
+      xp[e] = dP * gm;
+      xm[e] = dM * gm;
+    }
+    bf16x4 h4, l4;
+    split4(xp, h4, l4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.XPh[16 * ti + 4 * lg + e][s] = h4[e];
+      sm.XPl[16 * ti + 4 * lg + e][s] = l4[e];
+    }
+    split4(xm, h4, l4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.XMh[16 * ti + 4 * lg + e][s] = h4[e];
+      sm.XMl[16 * ti + 4 * lg + e][s] = l4[e];
+    }
+  }
+  __syncthreads();
+
+  // ---- P2: dQ and dK, this wave's dk columns, one 16-column tile at a time ----
+  {
+    const float brow[2] = {sm.beta[lr], sm.beta[16 + lr]};
+    float hdh = 0.0f, tl = 0.0f;
+    float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 1
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int dkt = 16 * (NTW * wave + nt);   // first dk column of this tile
+      f32x4 aq[2], ar[2], au[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        aq[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ar[rb] = aq[rb];
+        au[rb] = aq[rb];
+      }
+#pragma unroll
+      for (int kk = 0; kk < KKV; ++kk) {
+        const int kc = 32 * kk + 8 * lg;
+        // h^T and dh^T as B operands: column dk = dkt + lr, rows dv kc .. kc + 7
+        const long o = wsS + (long)(dkt + lr) * DV + kc;
+        bf16x8 hh, hl, gh, gl;
+        split8g(ws_h + o, hh, hl, hdh, ws_dh + o);
+        split8(ws_dh + o, 1.0f, gh, gl);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const bf16x8 da = ld8(&sm.D[16 * rb + lr][kc]);
+          bf16x8 rh, rl, uh, ul;
+          split8(&sm.Y[16 * rb + lr][kc], brow[rb], rh, rl);   // dR = b dY
+          split8(&sm.U[16 * rb + lr][kc], 1.0f, uh, ul);
+          aq[rb] = mfma_bf16(da, hh, aq[rb]);
+          aq[rb] = mfma_bf16(da, hl, aq[rb]);
+          ar[rb] = mfma_bf16(rh, hh, ar[rb]);
+          ar[rb] = mfma_bf16(rl, hh, ar[rb]);
+          ar[rb] = mfma_bf16(rh, hl, ar[rb]);
+          au[rb] = mfma_bf16(uh, gh, au[rb]);
+          au[rb] = mfma_bf16(ul, gh, au[rb]);
+          au[rb] = mfma_bf16(uh, gl, au[rb]);
+        }
+      }
+      // the n x n x dk products: k = tokens {4 lg + j} u {16 + 4 lg + j};
+      // K and Q columns dkt + lr as B operands (transposing reads)
+      const int c0 = dkt + 4 * (lr & 3);
+      const bf16x8 kb = cat(ld_tr4(&sm.K[4 * lg + (lr >> 2)][c0]),
+                            ld_tr4(&sm.K[16 + 4 * lg + (lr >> 2)][c0]));
+      const bf16x8 qb = cat(ld_tr4(&sm.Q[4 * lg + (lr >> 2)][c0]),
+                            ld_tr4(&sm.Q[16 + 4 * lg + (lr >> 2)][c0]));
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int ra = 16 * rb + lr;
+        auto row8 = [&](const bf16(*X)[SM::LDX]) {
+          return cat(*reinterpret_cast<const bf16x4 *>(&X[ra][4 * lg]),
+                     *reinterpret_cast<const bf16x4 *>(&X[ra][16 + 4 * lg]));
+        };
+        // transposed: row ra of X^T = column ra of X, k rows 4 lg + j (+16)
+        auto col8 = [&](const bf16(*X)[SM::LDX]) {
+          const int cc = 16 * rb + 4 * (lr & 3);
+          return cat(ld_tr4(&X[4 * lg + (lr >> 2)][cc]), ld_tr4(&X[16 + 4 * lg + (lr >> 2)][cc]));
+        };
+        f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xk = xq;
+        xq = mfma_bf16(row8(sm.XPh), kb, xq);
+        xq = mfma_bf16(row8(sm.XPl), kb, xq);
+        xk = mfma_bf16(row8(sm.XMh), kb, xk);
+        xk = mfma_bf16(row8(sm.XMl), kb, xk);
+        xk = mfma_bf16(col8(sm.XMh), kb, xk);
+        xk = mfma_bf16(col8(sm.XMl), kb, xk);
+        xk = mfma_bf16(col8(sm.XPh), qb, xk);
+        xk = mfma_bf16(col8(sm.XPl), qb, xk);
+        // lane holds rows r0 + e of column dkt + lr
+        const int r0 = 16 * rb + 4 * lg, col = dkt + lr;
+        const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&sm.gam[r0]);
+        const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&sm.ec[r0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r0 + e;
+          const float gq = gm4[e] * aq[rb][e];
+          const float gr = gm4[e] * ar[rb][e];
+          const float gu = ec4[e] * au[rb][e];
+          if (r < n) {
+            dq[trow(r) * DK + col] = gq + xq[e];
+            dk[trow(r) * DK + col] = gu - gr + xk[e];
+          }
+          if constexpr (GATE == kGateScalar) {
+            const float qv = (float)sm.Q[r][col], kv = (float)sm.K[r][col];
+            part[rb][e] += qv * gq - kv * gr - kv * gu;
+            tl += kv * gu;
+          }
+        }
+      }
+    }
+    if constexpr (GATE == kGateScalar) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = sum16(part[rb][e]);
+          if (lr == 0) sm.dgp[wave][16 * rb + 4 * lg + e] = p;
+        }
+      tl = sum64(tl);
+      hdh = sum64(hdh);
+      if (lane == 0) {
+        sm.tlast[wave] = tl;
+        sm.hdh[wave] = hdh;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- P3: db, dg and its suffix sums (one lane per row) ----
+  if (wave == 0) {
+    const int r = lane & 31;
+    float db = sm.dba[r], gsum = 0.0f;
+#pragma unroll 8
+    for (int s2 = 0; s2 < C; ++s2) {
+      db += sm.Hm[r][s2];
+      gsum += sm.G[r][s2] - sm.G[s2][r];
+    }
+    if (lane < C && r < n) dbeta[trow(r)] = db;
+    if constexpr (GATE == kGateScalar) {
+      float dg = gsum;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) dg += sm.dgp[w][r];
+      if (r == C - 1) {
+        float tsum = 0.0f, hsum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          tsum += sm.tlast[w];
+          hsum += sm.hdh[w];
+        }
+        dg += tsum + sm.gam[C - 1] * hsum;
+      }
+      if (lane < C) sm.dg[r] = dg;
+      wave_lds_sync();
+      float acc = 0.0f;
+      for (int s2 = r; s2 < C; ++s2) acc += sm.dg[s2];
+      if (lane < C && r < n) dlog_alpha[trow(r)] = acc;
+    }
+  }
+}
+
+template <int DK>
+hipError_t launch_dk(const BwdArgs &a) {
+  const int nchunks = (a.T + C - 1) / C;
+  dim3 grid((unsigned)((long)a.B * a.H * nchunks)), block(64 * NW);
+#define GDR_LAUNCH(G)                                                                           \
+  hipLaunchKernelGGL((chunk_bwd_grad_kernel<DK, G>), grid, block, 0, a.stream,                  \
+                     (const bf16 *)a.q, (const bf16 *)a.k, a.beta, a.log_alpha,                \
+                     (const bf16 *)a.d_o, a.ws_h, a.ws_r, a.ws_u, a.ws_dh, a.ws_dy, a.dq, a.dk, \
+                     a.dv, a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
+  if (a.gate == kGateNone) GDR_LAUNCH(kGateNone);
+  else GDR_LAUNCH(kGateScalar);
+#undef GDR_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bwd_grads(const BwdArgs &a) {
+  return a.D == 128 ? launch_dk<128>(a) : launch_dk<64>(a);
+}
+
+}  // namespace gdr

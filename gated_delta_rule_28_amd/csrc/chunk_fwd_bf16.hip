@@ -59,6 +59,20 @@
 // banks.  The DMA lanes fetch the block that belongs at their fixed LDS
 // position.
 //
+// Backward passes (template MODE).  The same pipeline runs the two sequential
+// passes of the backward: kModeRec recomputes the forward and stores, per
+// chunk, the entering state h, R = V - diag(gam) K h and U (no outputs);
+// kModeRev walks the chunks in reverse with v = dO, carrying dS, the
+// gradient of the state (dS_T in, dS_0 out):
+//
+//   dU  = diag(e^{g_last - g}) K dS + P^T dO        dY = T^T dU
+//   dS <- gam_last dS + Q^T diag(gam) dO - K^T diag(gam b) dY
+//
+// storing dS (the gradient of the state leaving the chunk) and dY per chunk.
+// Both take the prep waves' A, P and T tiles unchanged (T^T and P^T are the
+// tiles as stored); the chunk-parallel kernel (chunk_bwd.hip) forms the
+// token gradients from what they store.
+//
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
 // operand (S, R, U, T, P) is split into bf16
 // hi + lo and multiplied as hi*hi + hi*lo + lo*hi (two products when the
@@ -78,6 +92,8 @@ constexpr int NPW = 4;     // prep waves
 constexpr int NIN = 5;     // input slots: chunk j DMA'd from iteration j-3, last read in j+1
 constexpr int NPR = 3;     // P slots: chunk j written in iteration j-1, read in j+1
 constexpr int NTS = 2;     // T slots: chunk j written in iteration j, read in j+1
+
+enum Mode { kModeFwd = 0, kModeRec = 1, kModeRev = 2 };
 
 // Inclusive prefix sum over lanes 0..31 of a wave with DPP row shifts
 // (within 16-lane rows) and a row broadcast of lane 15 into the next row.
@@ -127,13 +143,14 @@ struct __align__(16) PipeSmem {
   float gw[3][C], bw[3][C];            // in-chunk log decay g and b, one copy per tile wave
 };
 
-template <int DK, int DVS, typename OutT, int GATE, bool ERASE, bool FUSED>
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE, bool FUSED, int MODE>
 __global__ void __launch_bounds__(64 * (DVS / 16 + NPW), 1)
 chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ v, const float *__restrict__ beta,
                       const float *__restrict__ log_alpha, const float *initial_state,
                       OutT *__restrict__ o, float *final_state, int B, int T, int H, int fuse,
-                      const bf16 *__restrict__ out_gate) {
+                      const bf16 *__restrict__ out_gate, float *__restrict__ ws_a,
+                      float *__restrict__ ws_b, float *__restrict__ ws_c) {
   constexpr int NSW = DVS / 16;        // state waves; wave w owns value columns 16w..16w+15
   constexpr int NT = 64 * (NSW + NPW);
   constexpr int DV = DK;               // full value width (Dk == Dv)
@@ -147,6 +164,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
   static_assert(sizeof(In) % 16 == 0 && (C * QRB) % 1024 == 0 && (C * VRB) % 1024 == 0,
                 "DMA runs are whole 1 KiB waves");
+  static_assert(MODE == kModeFwd || (ERASE && !FUSED && GATE != kGateChannel),
+                "the backward passes run the erasing, unfused scalar-gate form");
+  constexpr bool WANT_O = MODE == kModeFwd;      // outputs (Q S, P U, o)
+  constexpr bool WANT_P = MODE != kModeRec;      // the P tiles and q
   __shared__ SM sm;
   // calls without a fused prologue or epilogue compile without their code
   if constexpr (!FUSED) {
@@ -175,6 +196,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int bb = chain / H, hh = chain % H;
   const int nchunks = (T + C - 1) / C;
   const long tok0 = (long)bb * T * H + hh;   // row index of token 0 of this chain
+  // the chunk of pipeline step j (the reverse pass walks the chunks backwards)
+  auto chunk_of = [&](int j) { return MODE == kModeRev ? nchunks - 1 - j : j; };
 
   // byte offset inside a q/k (v) tile of row r, natural 16-byte block b
   auto qk_at = [](int r, int b) { return r * QRB + 16 * (b ^ swz_qk<QB>(r)); };
@@ -284,6 +307,105 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
     for (int it = 0; it < nchunks + 1; ++it) {
       const int s = it - 1;            // chunk of this iteration
+     if constexpr (MODE == kModeRev) {
+      if (s >= 0) {
+        const int c = nchunks - 1 - s;   // chunks run last to first
+        const In &bs = *at_off(&sm.in[0], slot_off(s % NIN, (int)sizeof(In)));
+        const typename SM::PT &ps = *at_off(&sm.p[0], slot_off(s % NPR, (int)sizeof(typename SM::PT)));
+        const int tso = slot_off(s % NTS, (int)sizeof(sm.Th[0]));
+        const bf16(*Th)[SM::LDC] = at_off(&sm.Th[0][0], tso);
+        const bf16(*Tl)[SM::LDC] = at_off(&sm.Tl[0][0], tso);
+        const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
+        const char *Qb = reinterpret_cast<const char *>(&bs.Q[0][0]);
+        const char *Vb = reinterpret_cast<const char *>(&bs.V[0][0]);
+        // dS, the gradient of the state leaving chunk c
+        float *dh = ws_a + ((long)chain * nchunks + c) * (DK * DV);
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_nontemporal_store(Sacc[mb][e], dh + srow(mb, e) * DV + col0 + lr);
+        // K dS
+        f32x4 KS[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x4 a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KKD; ++kk) {
+            const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
+            a1 = mfma_bf16(ak, Sh[kk], a1);
+            a1 = mfma_bf16(ak, Sl[kk], a1);
+          }
+          KS[rb] = a1;
+        }
+        // dO of this lane's column, rows 16 rb + 4 lg + c (transposing reads
+        // of the v slot, which holds dO in this mode): the B operand of P^T dO
+        bf16x4 dov[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          dov[rb] = ld_tr4(reinterpret_cast<const bf16 *>(Vb + 16 * rb * VRB + v_off));
+        const bf16x8 Dd = cat(dov[0], dov[1]);
+        // dU = diag(e^{g_last - g}) K dS + P^T dO; row r of P^T is row r of
+        // the stored P^T tile, k = tokens {4 lg + j} u {16 + 4 lg + j}
+        bf16x4 duh[2], dul[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
+          f32x4 acc = ec4 * KS[rb];
+          const bf16x8 ph = cat(*reinterpret_cast<const bf16x4 *>(&ps.Ph[16 * rb + lr][4 * lg]),
+                                *reinterpret_cast<const bf16x4 *>(&ps.Ph[16 * rb + lr][16 + 4 * lg]));
+          const bf16x8 pl = cat(*reinterpret_cast<const bf16x4 *>(&ps.Pl[16 * rb + lr][4 * lg]),
+                                *reinterpret_cast<const bf16x4 *>(&ps.Pl[16 * rb + lr][16 + 4 * lg]));
+          acc = mfma_bf16(ph, Dd, acc);
+          acc = mfma_bf16(pl, Dd, acc);
+          split4(acc, duh[rb], dul[rb]);
+        }
+        const bf16x8 DUh = cat(duh[0], duh[1]), DUl = cat(dul[0], dul[1]);
+        // dY = T^T dU (stored), and the update's right operands gam dO and
+        // -gam b dY
+        float *dyb = ws_b + ((long)chain * nchunks + c) * (C * DV);
+        bf16x4 bqh[2], bql[2], bkh[2], bkl[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const bf16x8 th = cat(*reinterpret_cast<const bf16x4 *>(&Th[16 * rb + lr][4 * lg]),
+                                *reinterpret_cast<const bf16x4 *>(&Th[16 * rb + lr][16 + 4 * lg]));
+          const bf16x8 tl = cat(*reinterpret_cast<const bf16x4 *>(&Tl[16 * rb + lr][4 * lg]),
+                                *reinterpret_cast<const bf16x4 *>(&Tl[16 * rb + lr][16 + 4 * lg]));
+          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          y = mfma_bf16(th, DUh, y);
+          y = mfma_bf16(tl, DUh, y);
+          y = mfma_bf16(th, DUl, y);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_nontemporal_store(y[e], dyb + (16 * rb + 4 * lg + e) * DV + col0 + lr);
+          const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&bs.gam[16 * rb + 4 * lg]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.bt[16 * rb + 4 * lg]);
+          f32x4 gd;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gd[e] = gm4[e] * (float)dov[rb][e];
+          split4(gd, bqh[rb], bql[rb]);
+          split4(-(gm4 * b4) * y, bkh[rb], bkl[rb]);
+        }
+        const bf16x8 Bqh = cat(bqh[0], bqh[1]), Bql = cat(bql[0], bql[1]);
+        const bf16x8 Bkh = cat(bkh[0], bkh[1]), Bkl = cat(bkl[0], bkl[1]);
+        const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb) {
+          const int off = kt_off[mb >> 1] + 8 * (mb & 1);
+          const bf16x8 ak = cat(ld_tr4(reinterpret_cast<const bf16 *>(Kb + off)),
+                                ld_tr4(reinterpret_cast<const bf16 *>(Kb + off + 16 * QRB)));
+          const bf16x8 aq = cat(ld_tr4(reinterpret_cast<const bf16 *>(Qb + off)),
+                                ld_tr4(reinterpret_cast<const bf16 *>(Qb + off + 16 * QRB)));
+          f32x4 acc = Sacc[mb] * glast;
+          acc = mfma_bf16(ak, Bkh, acc);
+          acc = mfma_bf16(ak, Bkl, acc);
+          acc = mfma_bf16(aq, Bqh, acc);
+          acc = mfma_bf16(aq, Bql, acc);
+          Sacc[mb] = acc;
+        }
+        split_state();
+      }
+     } else {
       f32x4 QS[2];
       bf16x8 Uh, Ul, Wh, Wl;
       if constexpr (FUSED) {
@@ -300,20 +422,34 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
         const char *Qb = reinterpret_cast<const char *>(&bs.Q[0][0]);
         const char *Vb = reinterpret_cast<const char *>(&bs.V[0][0]);
+        if constexpr (MODE == kModeRec) {
+          // the state entering chunk s
+          float *hb = ws_a + ((long)chain * nchunks + s) * (DK * DV);
+#pragma unroll
+          for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              __builtin_nontemporal_store(Sacc[mb][e], hb + srow(mb, e) * DV + col0 + lr);
+        }
         f32x4 KS[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KKD; ++kk) {
-            const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
-            if constexpr (ERASE) {
+            if constexpr (ERASE && !WANT_O) {
+              const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
+              a1 = mfma_bf16(ak, Sh[kk], a1);
+              a1 = mfma_bf16(ak, Sl[kk], a1);
+            } else if constexpr (ERASE) {
+              const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
               const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
               a1 = mfma_bf16(ak, Sh[kk], a1);
               a2 = mfma_bf16(aq, Sh[kk], a2);
               a1 = mfma_bf16(ak, Sl[kk], a1);
               a2 = mfma_bf16(aq, Sl[kk], a2);
             } else {
+              const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
               a2 = mfma_bf16(aq, Sh[kk], a2);
               a2 = mfma_bf16(aq, Sl[kk], a2);
             }
@@ -336,6 +472,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             rr[e] = (ERASE ? (float)vv[e] - gm4[e] * KS[rb][e] : (float)vv[e]) * b4[e];
+          if constexpr (MODE == kModeRec) {
+            // R = V - diag(gam) K S of chunk s (before the factor b)
+            float *rbp = ws_b + ((long)chain * nchunks + s) * (C * DV);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              __builtin_nontemporal_store((float)vv[e] - gm4[e] * KS[rb][e],
+                                          rbp + (r0 + e) * DV + col0 + lr);
+          }
           rv[rb] = rr;
           split4(rr, rh2[rb], rl2[rb]);
         }
@@ -364,6 +508,12 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             u = mfma_bf16(th, Rh, u);
             u = mfma_bf16(tl, Rh, u);
             u = mfma_bf16(th, Rl, u);
+            if constexpr (MODE == kModeRec) {
+              float *ubp = ws_c + ((long)chain * nchunks + s) * (C * DV);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                __builtin_nontemporal_store(u[e], ubp + (16 * rb + 4 * lg + e) * DV + col0 + lr);
+            }
             split4(u, uh[rb], ul[rb]);
             const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
             split4(u * ec4, wh[rb], wl[rb]);
@@ -383,7 +533,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         // the chunk's rows: smaller than 4 GiB (the host checks the shape)
         const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2 && WANT_O; ++rb) {
           const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&bs.fq[16 * rb + 4 * lg]);
           f32x4 acc = gm4 * QS[rb];
           const bf16x8 ph = cat(ld_tr4(&ps.Ph[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
@@ -420,6 +570,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
         split_state();   // for the next chunk
       }
+     }
       __syncthreads();
     }
 
@@ -602,8 +753,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   auto issue = [&](int j) {
     In &dst = sm.in[j % NIN];
-    const int n = min(C, T - j * C);
-    const long row0 = tok0 + (long)j * C * H;         // token row of the chunk's first token
+    const int cj = chunk_of(j);
+    const int n = min(C, T - cj * C);
+    const long row0 = tok0 + (long)cj * C * H;        // token row of the chunk's first token
     if (pw == 0) {
       // v rows (all slices' columns of rows < n are inside the descriptor)
       const u32x4 rv = rsrc_words(v + row0 * DV, 2u * ((unsigned)(n - 1) * H * DV + DV));
@@ -614,6 +766,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if constexpr (SCALAR)
         lds_dma4(rsrc_words(log_alpha + row0, 4u * ((unsigned)(n - 1) * H + 1)), soff, lds_addr(&dst.la[0]));
     } else {
+      if (!WANT_P && pw == 2) return;                  // q feeds only P and Q S
       const bf16 *src = (pw == 1) ? k : q;
       const u32x4 rq = rsrc_words(src + row0 * DK, 2u * ((unsigned)(n - 1) * H * DK + DK));
       const unsigned lq = lds_addr(pw == 1 ? &dst.K[0][0] : &dst.Q[0][0]);
@@ -642,7 +795,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     In &bf = *at_off(&sm.in[0], slot_off(j % NIN, (int)sizeof(In)));
     float *g = sm.gw[pw], *bw = sm.bw[pw];
     // padded tokens carry log a = 0 and b = 0 after the fused transforms too
-    const int n = min(C, T - j * C);
+    const int n = min(C, T - chunk_of(j) * C);
     const float la = (SCALAR && lane < n) ? fused_log_alpha(bf.la[lane], fuse) : 0.0f;
     const float sc = scan32_inclusive(la);
     const float bl = (lane < n) ? fused_beta(bf.beta[lane], fuse) : 0.0f;
@@ -685,8 +838,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if constexpr (ERASE)
         *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[0][lr][4 * lg]) =
             -decayed(bf, g, bw, tile_acc(bf, false, 0, 0), 0, 0, false);
-      store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
-    } else {
+      if constexpr (WANT_P)
+        store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
+    } else if constexpr (WANT_P) {
       store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
       store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
     }
@@ -752,11 +906,35 @@ template <int DK, int DVS, typename OutT, int GATE, bool ERASE, bool FUSED>
 hipError_t launch_fused(const ChunkArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE, ERASE, FUSED>), grid, block, 0, a.stream,
-                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
-                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H, a.fuse,
-                     (const bf16 *)a.out_gate);
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE, ERASE, FUSED, kModeFwd>), grid,
+                     block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                     a.beta, a.log_alpha, a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T,
+                     a.H, a.fuse, (const bf16 *)a.out_gate, nullptr, nullptr, nullptr);
   return hipGetLastError();
+}
+
+// the backward's two sequential passes at one tile configuration
+template <int DK, int DVS, int GATE>
+hipError_t launch_passes(const BwdArgs &a) {
+  const int nslice = DK / DVS;
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, true, false, kModeRec>), grid,
+                     block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                     a.beta, a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0,
+                     nullptr, a.ws_h, a.ws_r, a.ws_u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, true, false, kModeRev>), grid,
+                     block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.d_o,
+                     a.beta, a.log_alpha, a.d_final_state, nullptr, a.d_initial_state, a.B, a.T,
+                     a.H, 0, nullptr, a.ws_dh, a.ws_dy, nullptr);
+  return hipGetLastError();
+}
+
+template <int DK, int DVS>
+hipError_t passes_by_gate(const BwdArgs &a) {
+  if (a.gate == kGateNone) return launch_passes<DK, DVS, kGateNone>(a);
+  return launch_passes<DK, DVS, kGateScalar>(a);
 }
 
 template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
@@ -790,6 +968,25 @@ bool chunk_fwd_bf16_supported(const ChunkArgs &a) {
   const long chunk_bytes = (long)4 * ((long)(C - 1) * a.H * a.D + a.D);
   return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate != kGateChannel &&
          chunk_bytes < 0xFFFFFFFFL;
+}
+
+bool chunk_bwd_supported(int D, bool in_bf16, int gate, bool erase, long H) {
+  const long chunk_bytes = (long)4 * ((long)(C - 1) * H * D + D);
+  return in_bf16 && (D == 128 || D == 64) && (gate == kGateNone || gate == kGateScalar) &&
+         erase && chunk_bytes < 0xFFFFFFFFL;
+}
+
+hipError_t launch_chunk_bwd_passes(const BwdArgs &a) {
+  static_assert(C == kBwdChunk, "the workspace holds this kernel's chunks");
+  // the forward's launch shapes: 64-column slices once there are >= 256
+  // (chain, slice) pairs, 32-column slices below
+  const long chains = (long)a.B * a.H;
+  if (a.D == 128) {
+    if (chains * 2 >= 256) return passes_by_gate<128, 64>(a);
+    return passes_by_gate<128, 32>(a);
+  }
+  if (chains >= 256) return passes_by_gate<64, 64>(a);
+  return passes_by_gate<64, 32>(a);
 }
 
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {

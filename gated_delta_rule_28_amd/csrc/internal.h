@@ -48,4 +48,32 @@ bool chunk_fwd_small_supported(const ChunkArgs &a);
 // zero or copy the state for T == 0
 hipError_t launch_state_passthrough(const float *src, float *dst, long count, hipStream_t stream);
 
+// ---- backward of the chunk forward (bf16 q/k/v/dO, D = 64 or 128, no gate
+//      or the scalar gate, with the erase term) ----
+constexpr int kBwdChunk = 32;   // tokens per chunk of the passes and of the workspace
+
+struct BwdArgs {
+  int B, T, H, D;
+  int gate;                     // kGateNone or kGateScalar
+  const void *q, *k, *v;
+  const float *beta, *log_alpha;
+  const float *initial_state;   // S_0 or nullptr
+  const void *d_o;              // dL/do [B, T, H, D], dtype of q
+  const float *d_final_state;   // dL/dS_T or nullptr
+  float *dq, *dk, *dv, *dbeta, *dlog_alpha, *d_initial_state;
+  // workspace partitions, per (chain, chunk): the entering state h, R, U
+  // (recompute pass); dh, dY (reverse pass)
+  float *ws_h, *ws_r, *ws_u, *ws_dh, *ws_dy;
+  hipStream_t stream;
+};
+
+// workspace floats per (chain, chunk): h and dh [D][D], R, U, dY [C][D]
+inline long bwd_ws_floats_per_chunk(int D) { return 2L * D * D + 3L * kBwdChunk * D; }
+bool chunk_bwd_supported(int D, bool in_bf16, int gate, bool erase, long H);
+// the two sequential passes: the forward recomputed (h, R, U per chunk), then
+// the reverse pass (dh, dY per chunk, and dS_0)
+hipError_t launch_chunk_bwd_passes(const BwdArgs &a);
+// the chunk-parallel gradients dq, dk, dv, dbeta, dlog_alpha
+hipError_t launch_chunk_bwd_grads(const BwdArgs &a);
+
 }  // namespace gdr

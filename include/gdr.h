@@ -44,13 +44,15 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 typedef enum gdr_status {
   GDR_OK = 0,
   GDR_EINVAL = -1,       /* bad argument: null pointer, size <= 0, misaligned, gate mismatch */
   GDR_EUNSUPPORTED = -2, /* valid but not implemented: head size, chunk size, dtype combination */
-  GDR_EHIP = -3          /* the HIP runtime reported an error on launch */
+  GDR_EHIP = -3,         /* the HIP runtime reported an error on launch */
+  GDR_EWORKSPACE = -4    /* workspace missing, not 256-byte aligned, or smaller than
+                            the matching *_workspace_bytes query */
 } gdr_status;
 
 typedef enum gdr_dtype {
@@ -167,6 +169,67 @@ int gdr_chunk_fwd_ex(int B, int T, int H, int Dk, int Dv, int chunk,
                      const float *initial_state,
                      void *o, float *final_state,
                      hipStream_t stream);
+
+/*
+ * gdr_chunk_fwd_workspace_bytes -- device workspace gdr_chunk_fwd needs for
+ * these arguments.  Always 0: every forward kernel keeps its intermediates
+ * (chunk tiles, the triangular solve, the state) in registers and LDS, so
+ * the forward entry points take no workspace argument.  Provided so that a
+ * caller can size workspaces the same way for the forward and the backward.
+ */
+size_t gdr_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     int in_dtype, int out_dtype, int gate);
+
+/*
+ * gdr_chunk_bwd_workspace_bytes -- device workspace gdr_chunk_bwd needs for
+ * these arguments: per (batch, head) chain and 32-token chunk, two Dk x Dv
+ * fp32 states and three 32 x Dv fp32 tiles, 4 (2 Dk Dv + 96 Dv) bytes (about
+ * 2.8 GiB for B = 8, H = 16, T = 4096, Dk = Dv = 128).  0 when the call is
+ * not supported or has no tokens.
+ */
+size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
+                                     int in_dtype, int gate);
+
+/*
+ * gdr_chunk_bwd -- gradients of gdr_chunk_fwd (the backward pass of the
+ * chunkwise forward, which training runs: diosapp tutorial, section 五;
+ * "线性注意力架构：机制、权衡与跨层路由", abstract, on training throughput).
+ *
+ * Given L with dL/do = d_o and dL/dS_T = d_final_state, it returns the
+ * gradients of L with respect to every input of the same forward call:
+ *
+ *   B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
+ *   initial_state  exactly as passed to gdr_chunk_fwd.  Supported: bf16
+ *                 q/k/v, Dk == Dv in {64, 128}, GDR_GATE_NONE or
+ *                 GDR_GATE_SCALAR without GDR_NO_ERASE (others return
+ *                 GDR_EUNSUPPORTED)
+ *   d_o           [B, T, H, Dv] in_dtype, dL/do
+ *   d_final_state [B, H, Dk, Dv] fp32, or NULL for zero
+ *   dq, dk        [B, T, H, Dk] fp32 (written)
+ *   dv            [B, T, H, Dv] fp32 (written)
+ *   dbeta         [B, T, H] fp32 (written)
+ *   dlog_alpha    [B, T, H] fp32 (written); NULL iff gate == GDR_GATE_NONE
+ *   d_initial_state [B, H, Dk, Dv] fp32 (written), or NULL (not written)
+ *   workspace     device memory of at least gdr_chunk_bwd_workspace_bytes,
+ *                 256-byte aligned, owned by the caller; its contents on entry
+ *                 are ignored and on return are unspecified.  GDR_EWORKSPACE
+ *                 if it is NULL, misaligned or smaller.
+ *
+ * The outputs must not overlap each other, the inputs or the workspace.  The
+ * call recomputes the forward's chunk-boundary states into the workspace,
+ * walks the chunks in reverse for the state gradient, then forms every
+ * chunk's token gradients in parallel (three kernel launches on `stream`).
+ * Accuracy as for gdr_chunk_fwd: fp32 state, hi/lo bf16 products.
+ */
+int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
+                  const void *q, const void *k, const void *v,
+                  const float *beta, const float *log_alpha,
+                  const float *initial_state,
+                  const void *d_o, const float *d_final_state,
+                  float *dq, float *dk, float *dv, float *dbeta, float *dlog_alpha,
+                  float *d_initial_state,
+                  void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /*
  * gdr_recurrent_step -- one decode step: a single new token for each of N

@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["gdr_abi_version", "gdr_chunk_fwd", "gdr_chunk_fwd_ex",
+    assert names == ["gdr_abi_version", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_bytes",
+                     "gdr_chunk_fwd", "gdr_chunk_fwd_ex", "gdr_chunk_fwd_workspace_bytes",
                      "gdr_recurrent_step", "gdr_recurrent_step_ex", "gdr_status_str"], names
     assert set(names) == set(_abi.SIGNATURES)
 
@@ -34,11 +35,11 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert _abi.abi_version() == 1
+    assert _abi.abi_version() == _abi.ABI_VERSION == 2
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3):
+    for st in (0, -1, -2, -3, -4):
         assert _abi.status_str(st).startswith("GDR_")
     assert "unknown" in _abi.status_str(-99)
 
@@ -176,3 +177,73 @@ def test_recurrent_step_checks_output_shape_before_launch(monkeypatch):
         with pytest.raises(ValueError, match="o must be"):
             gdr.recurrent_step(q, q, q, beta, None, state, o=bad)
     assert not called
+
+
+
+# ---------------------------------------------------------------------------
+# workspace queries and the backward entry point
+
+
+def test_forward_needs_no_workspace():
+    for args in ((8, 4096, 16, 128, 128, 0, _abi.GDR_BF16, _abi.GDR_F32, _abi.GDR_GATE_SCALAR),
+                 (2, 8192, 32, 128, 128, 64, _abi.GDR_BF16, _abi.GDR_F32, _abi.GDR_GATE_CHANNEL),
+                 (1, 64, 1, 16, 16, 16, _abi.GDR_F32, _abi.GDR_F32, _abi.GDR_GATE_SCALAR)):
+        assert _abi.gdr_chunk_fwd_workspace_bytes(*args) == 0
+
+
+def bwd_ws(B=8, T=4096, H=16, D=128, chunk=0, in_dtype=_abi.GDR_BF16, gate=_abi.GDR_GATE_SCALAR):
+    return _abi.gdr_chunk_bwd_workspace_bytes(B, T, H, D, D, chunk, in_dtype, gate)
+
+
+def test_backward_workspace_size():
+    # per chain and 32-token chunk: two D x D states and three 32 x D tiles, fp32
+    per = 4 * (2 * 128 * 128 + 3 * 32 * 128)
+    assert bwd_ws() == 8 * 16 * 128 * per
+    assert bwd_ws(T=33) == 8 * 16 * 2 * per                 # a ragged tail is one more chunk
+    assert bwd_ws(gate=_abi.GDR_GATE_NONE) == bwd_ws()
+    assert bwd_ws(D=64, T=64, B=1, H=1) == 2 * 4 * (2 * 64 * 64 + 3 * 32 * 64)
+    # unsupported calls and empty inputs need none
+    for kw in (dict(in_dtype=_abi.GDR_F32), dict(gate=_abi.GDR_GATE_CHANNEL), dict(D=32),
+               dict(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE), dict(T=0), dict(B=0),
+               dict(chunk=48), dict(gate=9)):
+        assert bwd_ws(**kw) == 0, kw
+
+
+def bwd(**kw):
+    a = dict(B=1, T=8, H=1, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+             gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, log_alpha=FAKE,
+             initial_state=None, d_o=FAKE, d_final_state=None, dq=FAKE, dk=FAKE, dv=FAKE,
+             dbeta=FAKE, dlog_alpha=FAKE, d_initial_state=None, workspace=FAKE,
+             workspace_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return _abi.gdr_chunk_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), _abi.GDR_EINVAL),
+    (dict(q=None), _abi.GDR_EINVAL),
+    (dict(d_o=None), _abi.GDR_EINVAL),
+    (dict(dq=None), _abi.GDR_EINVAL),
+    (dict(dbeta=None), _abi.GDR_EINVAL),
+    (dict(dlog_alpha=None), _abi.GDR_EINVAL),                  # a gate needs its gradient
+    (dict(gate=_abi.GDR_GATE_NONE, log_alpha=None), _abi.GDR_EINVAL),   # and none without
+    (dict(log_alpha=None), _abi.GDR_EINVAL),
+    (dict(dk=FAKE + 4), _abi.GDR_EINVAL),
+    (dict(d_initial_state=FAKE + 8), _abi.GDR_EINVAL),
+    (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
+    (dict(Dk=32, Dv=32), _abi.GDR_EUNSUPPORTED),
+    (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
+    (dict(gate=_abi.GDR_GATE_CHANNEL), _abi.GDR_EUNSUPPORTED),
+    (dict(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE), _abi.GDR_EUNSUPPORTED),
+    (dict(H=300000), _abi.GDR_EUNSUPPORTED),
+    (dict(workspace=None), _abi.GDR_EWORKSPACE),
+    (dict(workspace=FAKE + 16), _abi.GDR_EWORKSPACE),          # not 256-byte aligned
+    (dict(workspace_bytes=4 * (2 * 128 * 128 + 3 * 32 * 128) - 1), _abi.GDR_EWORKSPACE),
+])
+def test_chunk_bwd_rejects(kw, want):
+    assert bwd(**kw) == want
+
+
+def test_chunk_bwd_empty_batch_is_a_no_op():
+    assert bwd(B=0, q=None, k=None, v=None, d_o=None, dq=None, dk=None, dv=None, dbeta=None,
+               workspace=None, workspace_bytes=0) == _abi.GDR_OK
