@@ -32,7 +32,9 @@ SIGNATURES = {
     "gdr_chunk_fwd_workspace_bytes": (_sz, [_c_int] * 9),
     "gdr_chunk_bwd_workspace_bytes": (_sz, [_c_int] * 8),
     "gdr_chunk_bwd": (_c_int, [_c_int] * 8 + [_vp] * 15 + [_sz, _vp]),
+    "gdr_chunk_bwd_noalloc": (_c_int, [_c_int] * 8 + [_vp] * 15),
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 _lock = threading.Lock()
@@ -119,3 +121,12 @@ def gdr_chunk_bwd(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alp
     return load().gdr_chunk_bwd(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
                                 initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
                                 d_initial_state, workspace, workspace_bytes, stream)
+
+
+def gdr_chunk_bwd_noalloc(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
+                          initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                          d_initial_state, stream):
+    """Raw call of the C entry point with integer sizes and raw pointers."""
+    return load().gdr_chunk_bwd_noalloc(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta,
+                                        log_alpha, initial_state, d_o, d_final_state, dq, dk, dv,
+                                        dbeta, dlog_alpha, d_initial_state, stream)

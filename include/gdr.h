@@ -232,6 +232,30 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
                   hipStream_t stream);
 
 /*
+ * gdr_chunk_bwd_noalloc -- gdr_chunk_bwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc.  Same arguments and results
+ * without the workspace, which is a static device array of
+ * GDR_NOALLOC_SCRATCH_BYTES inside the library (one per GPU the library runs
+ * on, held until the process ends); the call allocates nothing.  A call whose
+ * gdr_chunk_bwd_workspace_bytes exceeds GDR_NOALLOC_SCRATCH_BYTES (64 MiB:
+ * e.g. 372 chain-chunks of 32 tokens at Dk = Dv = 128, such as B = 1, H = 4,
+ * T = 2976) returns GDR_EWORKSPACE and launches nothing.  Every call on a GPU
+ * uses that GPU's one array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  The array's
+ * contents between calls are unspecified; nothing in them is read before
+ * the call writes it.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdr_chunk_bwd_noalloc(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,
+                          int gate, const void *q, const void *k, const void *v,
+                          const float *beta, const float *log_alpha,
+                          const float *initial_state,
+                          const void *d_o, const float *d_final_state,
+                          float *dq, float *dk, float *dv, float *dbeta, float *dlog_alpha,
+                          float *d_initial_state, hipStream_t stream);
+
+/*
  * gdr_recurrent_step -- one decode step: a single new token for each of N
  * independent sequences, with the fp32 state updated IN PLACE (the
  * constant-size memory that replaces the KV cache; diosapp tutorial,

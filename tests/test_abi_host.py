@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["gdr_abi_version", "gdr_chunk_bwd", "gdr_chunk_bwd_workspace_bytes",
+    assert names == ["gdr_abi_version", "gdr_chunk_bwd", "gdr_chunk_bwd_noalloc",
+                     "gdr_chunk_bwd_workspace_bytes",
                      "gdr_chunk_fwd", "gdr_chunk_fwd_ex", "gdr_chunk_fwd_workspace_bytes",
                      "gdr_recurrent_step", "gdr_recurrent_step_ex", "gdr_status_str"], names
     assert set(names) == set(_abi.SIGNATURES)
@@ -247,3 +248,29 @@ def test_chunk_bwd_rejects(kw, want):
 def test_chunk_bwd_empty_batch_is_a_no_op():
     assert bwd(B=0, q=None, k=None, v=None, d_o=None, dq=None, dk=None, dv=None, dbeta=None,
                workspace=None, workspace_bytes=0) == _abi.GDR_OK
+
+
+
+def test_noalloc_backward_refuses_more_than_its_array():
+    """gdr_chunk_bwd_noalloc rejects, before any launch, a call whose workspace
+    would not fit its static array; empty calls succeed without one."""
+    limit = _abi.NOALLOC_SCRATCH_BYTES
+    assert limit == 64 << 20
+    # 8 x 16 chains x 128 chunks need about 2.8 GiB
+    assert bwd_ws() > limit
+    a = dict(B=8, T=4096, H=16, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+             gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, log_alpha=FAKE,
+             initial_state=None, d_o=FAKE, d_final_state=None, dq=FAKE, dk=FAKE, dv=FAKE,
+             dbeta=FAKE, dlog_alpha=FAKE, d_initial_state=None, stream=None)
+    assert _abi.gdr_chunk_bwd_noalloc(**a) == _abi.GDR_EWORKSPACE
+    # one chain-chunk more than fits is refused too
+    per = 4 * (2 * 128 * 128 + 3 * 32 * 128)
+    fit = limit // per
+    assert bwd_ws(B=1, H=1, T=32 * (fit + 1)) > limit >= bwd_ws(B=1, H=1, T=32 * fit)
+    assert _abi.gdr_chunk_bwd_noalloc(**dict(a, B=1, H=1, T=32 * (fit + 1))) == \
+        _abi.GDR_EWORKSPACE
+    # invalid and empty calls: the usual statuses, nothing launched
+    assert _abi.gdr_chunk_bwd_noalloc(**dict(a, B=-1)) == _abi.GDR_EINVAL
+    assert _abi.gdr_chunk_bwd_noalloc(**dict(a, B=0, q=None)) == _abi.GDR_OK
+    assert _abi.gdr_chunk_bwd_noalloc(**dict(a, gate=_abi.GDR_GATE_CHANNEL)) == \
+        _abi.GDR_EUNSUPPORTED
