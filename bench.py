@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "chunk_fwd_bf16_kernel": ["chunk_fwd_bf16.hip", "mfma_util.h", "common.h"],
     "chunk_fwd_kda_kernel": ["chunk_fwd_kda.hip", "mfma_util.h", "common.h"],
     "recurrent_step_kernel": ["recurrent_step.hip", "common.h"],
+    "chunk_bwd_grad_kernel": ["chunk_bwd.hip", "mfma_util.h", "common.h", "internal.h"],
 }
 # the plain copy used to calibrate the byte counters: |x| over 1 GiB of fp32
 COPY_BYTES = 1 << 30
@@ -502,6 +503,75 @@ def decode_parity(torch, W, d, seqs=(0, 97, 255)):
             "pass": bool(e_o <= 1e-5 and e_S <= 1e-5)}
 
 
+def bwd_alg_bytes(w):
+    """Single-pass minimum HBM bytes of one chunk_bwd call (zero initial state,
+    no loss on the final state, dS_0 written): q, k, v, dO in (input dtype),
+    beta and log alpha in, dq, dk, dv (fp32) out, dbeta and dlog alpha out."""
+    th = w.B * w.T * w.H
+    in_b = 2 if w.in_dtype == "bf16" else 4
+    per_th = in_b * (2 * w.Dk + 2 * w.Dv) + 4 + 4 * (2 * w.Dk + w.Dv) + 4
+    if w.gate == "scalar":
+        per_th += 8
+    return th * per_th + w.B * w.H * w.Dk * w.Dv * 4
+
+
+def bwd_line(torch, gdr, W, w, steps, warmup, settle_s=0.0, chains=((0, 0), (7, 15))):
+    """Timed gdr_chunk_bwd calls on a chunk workload (the recompute pass, the
+    reverse pass and the chunk-parallel gradients), outputs and workspace
+    preallocated; then the gradients of sampled chains against the fp64
+    oracle's reverse sweep."""
+    import numpy as np
+    from oracle import gated_delta_backward
+    inp = W.make_workload_inputs(w, seed=0, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    d_o = torch.randn(w.B, w.T, w.H, w.Dv, device="cuda", generator=g).to(inp["q"].dtype)
+    ws = torch.empty(gdr.chunk_bwd_workspace_bytes(inp["q"], inp["log_alpha"]), device="cuda",
+                     dtype=torch.uint8)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    out = {"dq": torch.empty(w.B, w.T, w.H, w.Dk, **f32), "dk": torch.empty(w.B, w.T, w.H, w.Dk, **f32),
+           "dv": torch.empty(w.B, w.T, w.H, w.Dv, **f32), "dbeta": torch.empty(w.B, w.T, w.H, **f32),
+           "dlog_alpha": None if inp["log_alpha"] is None else torch.empty(w.B, w.T, w.H, **f32),
+           "d_initial_state": torch.empty(w.B, w.H, w.Dk, w.Dv, **f32)}
+
+    def step():
+        gdr.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None, d_o,
+                      None, workspace=ws, out=out)
+    wall, per = time_launches(torch, step, steps, warmup, settle_s)
+    mean_ms = statistics.fmean(per)
+    alg_b = bwd_alg_bytes(w)
+    achieved = alg_b / (mean_ms * 1e-3) / 1e9
+    # sampled chains against the oracle
+    errs = {}
+    for b, h in chains:
+        sl = lambda x: None if x is None else W.to_f64(x[b:b + 1, :, h:h + 1])
+        ref = gated_delta_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]),
+                                   sl(inp["log_alpha"]), None, sl(d_o), None)
+        pairs = [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dbeta", "dbeta"),
+                 ("dlog_alpha", "dlog_alpha")]
+        for n, rn in pairs:
+            if out[n] is None:
+                continue
+            e = rel_err(W.to_f64(out[n][b:b + 1, :, h:h + 1]), ref[rn])
+            errs[n] = max(errs.get(n, 0.0), e)
+        e = rel_err(W.to_f64(out["d_initial_state"][b:b + 1, h:h + 1]), ref["dS0"])
+        errs["dS0"] = max(errs.get("dS0", 0.0), e)
+    return {
+        "workload": w.name, "unit": "tokens/s", "value": w.B * w.T / (mean_ms * 1e-3),
+        "kernel_ms": {"mean": mean_ms, "median": statistics.median(per), "min": min(per)},
+        "kernels": "chunk_fwd_bf16_kernel <.., mode 1> (recompute), <.., mode 2> (reverse), "
+                   "chunk_bwd_grad_kernel (token gradients): one event pair around the three",
+        "workspace_bytes": int(ws.numel()),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": alg_b,
+                     "note": "algorithmic bytes exclude the workspace the three passes "
+                             "write and read"},
+        "parity": {"max_abs_over_rms": errs, "tol": PARITY_TOL,
+                   "chains_checked": [list(c) for c in chains], "chains_total": w.B * w.H,
+                   "pass": bool(all(v <= PARITY_TOL for v in errs.values()))},
+    }
+
+
 def small_lines(torch, gdr, W, settle_s):
     """The tiny fp32 workload (launch-latency bound: microseconds per call,
     warm) and the B=4, H=8, T=2048 DeltaNet / Gated DeltaNet workloads,
@@ -552,6 +622,18 @@ def run_counter_targets(torch, gdr, W, reps=3):
     one_pass()
     torch.cuda.synchronize()
     print(f"counters: {d.name} x{d.steps}", flush=True)
+    # the backward on the headline shape (its three kernels)
+    w = W.HEADLINE
+    inp = W.make_workload_inputs(w, seed=0, device="cuda")
+    d_o = torch.randn(w.B, w.T, w.H, w.Dv, device="cuda").to(inp["q"].dtype)
+    ws = torch.empty(gdr.chunk_bwd_workspace_bytes(inp["q"], inp["log_alpha"]), device="cuda",
+                     dtype=torch.uint8)
+    for _ in range(reps):
+        gdr.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None, d_o,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    del inp, d_o, ws
+    print(f"counters: backward {w.name} x{reps}", flush=True)
     src = torch.empty(COPY_BYTES // 4, device="cuda", dtype=torch.float32)
     dst = torch.empty_like(src)
     for _ in range(reps):
@@ -726,7 +808,7 @@ def main(argv=None):
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("OPS_DIR", "UTIL_DIR"))
     ap.add_argument("--pmc-command", default="rocprofv3 --pmc {counter} --kernel-include-regex "
-                    "'chunk_fwd|recurrent_step|AbsFunctor|Cijk' --output-format csv -d {dir} "
+                    "'chunk_fwd|chunk_bwd|recurrent_step|AbsFunctor|Cijk' --output-format csv -d {dir} "
                     "-o pmc -- python3 bench.py --only counters")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
@@ -814,6 +896,7 @@ def main(argv=None):
         rec["decode"]["roofline"] = with_copy_frac(rec["decode"]["roofline"], copy)
         rec["decode"]["parity"] = decode_parity(torch, W, W.DECODE)
         rec.update(small_lines(torch, gdr, W, args.settle_s))
+        rec["backward"] = bwd_line(torch, gdr, W, w, nb, 2, args.settle_s)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -195,7 +195,7 @@ def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0):
 
 
 def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_final_state=None,
-              *, chunk=0, workspace=None, want_d_initial_state=True):
+              *, chunk=0, workspace=None, want_d_initial_state=True, out=None):
     """Gradients of chunk_fwd's o and final state.
 
     Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, no gate or the
@@ -205,7 +205,8 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     (None without a gate, else [B, T, H]) and d_initial_state
     [B, H, Dk, Dv] (None when want_d_initial_state is False).  `workspace`,
     a uint8 GPU tensor of at least chunk_bwd_workspace_bytes, is allocated
-    with torch when not given.
+    with torch when not given; `out`, a dict of the same keys and shapes,
+    receives the gradients when given (nothing is allocated then).
     """
     _check_dev("q", q)
     if q.dtype not in _DT:
@@ -233,10 +234,22 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     if tuple(d_o.shape) != (B, T, H, Dv):
         raise ValueError("d_o must be [B, T, H, Dv]")
     f32 = dict(device=q.device, dtype=torch.float32)
-    out = {"dq": torch.empty(B, T, H, Dk, **f32), "dk": torch.empty(B, T, H, Dk, **f32),
-           "dv": torch.empty(B, T, H, Dv, **f32), "dbeta": torch.empty(B, T, H, **f32),
-           "dlog_alpha": None if log_alpha is None else torch.empty(B, T, H, **f32),
-           "d_initial_state": torch.empty(B, H, Dk, Dv, **f32) if want_d_initial_state else None}
+    shapes = {"dq": (B, T, H, Dk), "dk": (B, T, H, Dk), "dv": (B, T, H, Dv),
+              "dbeta": (B, T, H), "dlog_alpha": None if log_alpha is None else (B, T, H),
+              "d_initial_state": (B, H, Dk, Dv) if want_d_initial_state else None}
+    if out is None:
+        out = {n: None if shp is None else torch.empty(*shp, **f32) for n, shp in shapes.items()}
+    else:
+        for n, shp in shapes.items():
+            t = out.get(n)
+            if shp is None:
+                if t is not None and n == "dlog_alpha":
+                    raise ValueError("dlog_alpha must be None without a gate")
+                out[n] = t if n == "d_initial_state" else None
+                continue
+            _check_dev(n, t, torch.float32)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{n} must be {shp}")
     need = int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)

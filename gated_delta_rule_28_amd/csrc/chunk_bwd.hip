@@ -46,11 +46,10 @@ template <int DK>
 struct __align__(16) BwdSmem {
   static constexpr int LDB = DK + 8;   // bf16 row stride of q, k, dO: 16-byte row reads of
                                        // 16 rows hit distinct banks
-  static constexpr int LDF = DK + 4;   // fp32 row stride of U, dY
   static constexpr int LDN = C + 1;    // fp32 [C][C]
   static constexpr int LDX = C + 8;    // bf16 [C][C] hi / lo
   bf16 Q[C][LDB], K[C][LDB], D[C][LDB];
-  float U[C][LDF], Y[C][LDF];
+  bf16 Uh[C][LDB], Ul[C][LDB], Yh[C][LDB], Yl[C][LDB];   // U and dY split once
   float G[C][LDN];                     // dM o M + dP o P
   float Hm[C][LDN];                    // dA o M
   bf16 XPh[C][LDX], XPl[C][LDX];       // dP o Gam, lower inclusive
@@ -62,29 +61,21 @@ struct __align__(16) BwdSmem {
   float tlast[NW], hdh[NW];            // per-wave sums for dg_last
 };
 
-// two fp32 float4 (8 consecutive values) -> bf16 hi / lo, times a factor
-__device__ __forceinline__ void split8(const float *p, float f, bf16x8 &hi, bf16x8 &lo) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p) * f;
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4) * f;
-  bf16x4 ah, al, bh, bl;
-  split4(a, ah, al);
-  split4(b, bh, bl);
-  hi = cat(ah, bh);
-  lo = cat(al, bl);
-}
-__device__ __forceinline__ void split8g(const float *p, bf16x8 &hi, bf16x8 &lo, float &dot,
-                                        const float *q) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-  const f32x4 c = *reinterpret_cast<const f32x4 *>(q);
-  const f32x4 d = *reinterpret_cast<const f32x4 *>(q + 4);
-  dot += (a[0] * c[0] + a[1] * c[1]) + (a[2] * c[2] + a[3] * c[3]) +
-         (b[0] * d[0] + b[1] * d[1]) + (b[2] * d[2] + b[3] * d[3]);
-  bf16x4 ah, al, bh, bl;
-  split4(a, ah, al);
-  split4(b, bh, bl);
-  hi = cat(ah, bh);
-  lo = cat(al, bl);
+// acc + sum_i a_i b_i over 8 values given as bf16 hi / lo parts, as
+// hi.hi + hi.lo + lo.hi (the split products' precision), with packed bf16
+// dot products: the fp32 values need not stay live after their split
+__device__ __forceinline__ float dot8_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl,
+                                            float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t a0 = {ah[2 * i], ah[2 * i + 1]}, a1 = {al[2 * i], al[2 * i + 1]};
+    const bf16x2_t b0 = {bh[2 * i], bh[2 * i + 1]}, b1 = {bl[2 * i], bl[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(a0, b0, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(a0, b1, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(a1, b0, acc, false);
+  }
+  return acc;
 }
 
 // sum over the 16 lanes of each row of a wave (lanes 16 j .. 16 j + 15)
@@ -131,6 +122,27 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const long wsS = ((long)chain * nchunks + c) * (DK * DV);   // h, dh of this chunk
   const long wsR = ((long)chain * nchunks + c) * (C * DV);    // R, U, dY of this chunk
 
+  // h^T and dh^T of one of this wave's 16-column dk tiles as B operands:
+  // column dk = dkt + lr, rows dv 32 kk + 8 lg .. +7.  The first tile's loads
+  // are issued here, so their latency overlaps the input loads and the n x n
+  // tiles; the second tile's before the first is used.
+  struct Fetch {
+    f32x4 h[KKV][2], g[KKV][2];
+  };
+  auto fetch = [&](int nt, Fetch &f) {
+    const int dkt = 16 * (NTW * wave + nt);
+#pragma unroll
+    for (int kk = 0; kk < KKV; ++kk) {
+      const long o = wsS + (long)(dkt + lr) * DV + 32 * kk + 8 * lg;
+      f.h[kk][0] = *reinterpret_cast<const f32x4 *>(ws_h + o);
+      f.h[kk][1] = *reinterpret_cast<const f32x4 *>(ws_h + o + 4);
+      f.g[kk][0] = *reinterpret_cast<const f32x4 *>(ws_dh + o);
+      f.g[kk][1] = *reinterpret_cast<const f32x4 *>(ws_dh + o + 4);
+    }
+  };
+  Fetch fa, fb;
+  fetch(0, fa);
+
   // ---- P0: inputs into LDS; dV = b dY; sum_v dY R; decays ----
   for (int i = tid; i < C * SM::LDX; i += 64 * NW) {     // upper-right blocks stay zero
     (&sm.XPh[0][0])[i] = (bf16)0.0f;
@@ -143,38 +155,55 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     (&sm.Hm[0][0])[i] = 0.0f;
   }
   {
+    // every load of this phase is issued before any of them is used: one
+    // memory round trip
     constexpr int BPR = DK / 8;                          // 16-byte blocks per bf16 row
-#pragma unroll
-    for (int i = tid; i < C * BPR; i += 64 * NW) {
-      const int r = i / BPR, blk = i % BPR;
-      u32x4 xq = {0u, 0u, 0u, 0u}, xk = xq, xd = xq;
-      if (r < n) {
-        const long off = trow(r) * DK + 8 * blk;
-        xq = *reinterpret_cast<const u32x4 *>(q + off);
-        xk = *reinterpret_cast<const u32x4 *>(k + off);
-        xd = *reinterpret_cast<const u32x4 *>(d_o + off);
-      }
-      *reinterpret_cast<u32x4 *>(&sm.Q[r][8 * blk]) = xq;
-      *reinterpret_cast<u32x4 *>(&sm.K[r][8 * blk]) = xk;
-      *reinterpret_cast<u32x4 *>(&sm.D[r][8 * blk]) = xd;
-    }
-  }
-  {
-    // 8 threads per row, DV / 32 float4 each
-    constexpr int F4 = DV / 32;
+    constexpr int NB = C * BPR / (64 * NW);              // blocks per thread
+    constexpr int F4 = DV / 32;                          // 8 threads per row, F4 float4 each
     const int r = tid >> 3, f0 = (tid & 7) * F4;
+    u32x4 xq[NB], xk[NB], xd[NB];
+    f32x4 u[F4], y[F4], rr[F4];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = tid + 64 * NW * j, rj = i / BPR, blk = i % BPR;
+      xq[j] = u32x4{0u, 0u, 0u, 0u};
+      xk[j] = xq[j];
+      xd[j] = xq[j];
+      if (rj < n) {
+        const long off = trow(rj) * DK + 8 * blk;
+        xq[j] = *reinterpret_cast<const u32x4 *>(q + off);
+        xk[j] = *reinterpret_cast<const u32x4 *>(k + off);
+        xd[j] = *reinterpret_cast<const u32x4 *>(d_o + off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < F4; ++j) {
+      const long o = wsR + r * DV + 4 * (f0 + j);
+      u[j] = *reinterpret_cast<const f32x4 *>(ws_u + o);
+      y[j] = *reinterpret_cast<const f32x4 *>(ws_dy + o);
+      rr[j] = *reinterpret_cast<const f32x4 *>(ws_r + o);
+    }
     const float b = r < n ? beta[trow(r)] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = tid + 64 * NW * j, rj = i / BPR, blk = i % BPR;
+      *reinterpret_cast<u32x4 *>(&sm.Q[rj][8 * blk]) = xq[j];
+      *reinterpret_cast<u32x4 *>(&sm.K[rj][8 * blk]) = xk[j];
+      *reinterpret_cast<u32x4 *>(&sm.D[rj][8 * blk]) = xd[j];
+    }
     float dot = 0.0f;
 #pragma unroll
     for (int j = 0; j < F4; ++j) {
       const int col = 4 * (f0 + j);
-      const f32x4 u = *reinterpret_cast<const f32x4 *>(ws_u + wsR + r * DV + col);
-      const f32x4 y = *reinterpret_cast<const f32x4 *>(ws_dy + wsR + r * DV + col);
-      const f32x4 rr = *reinterpret_cast<const f32x4 *>(ws_r + wsR + r * DV + col);
-      *reinterpret_cast<f32x4 *>(&sm.U[r][col]) = u;
-      *reinterpret_cast<f32x4 *>(&sm.Y[r][col]) = y;
-      dot += (y[0] * rr[0] + y[1] * rr[1]) + (y[2] * rr[2] + y[3] * rr[3]);
-      if (r < n) *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + col) = y * b;
+      bf16x4 h4, l4;
+      split4(u[j], h4, l4);
+      *reinterpret_cast<bf16x4 *>(&sm.Uh[r][col]) = h4;
+      *reinterpret_cast<bf16x4 *>(&sm.Ul[r][col]) = l4;
+      split4(y[j], h4, l4);
+      *reinterpret_cast<bf16x4 *>(&sm.Yh[r][col]) = h4;
+      *reinterpret_cast<bf16x4 *>(&sm.Yl[r][col]) = l4;
+      dot += (y[j][0] * rr[j][0] + y[j][1] * rr[j][1]) + (y[j][2] * rr[j][2] + y[j][3] * rr[j][3]);
+      if (r < n) *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + col) = y[j] * b;
     }
     dot += __shfl_xor(dot, 1);
     dot += __shfl_xor(dot, 2);
@@ -212,9 +241,8 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const bf16x8 ka = ld8(&sm.K[16 * ti + lr][kc]);
       const bf16x8 kb = ld8(&sm.K[16 * tj + lr][kc]);
       const bf16x8 da = ld8(&sm.D[16 * ti + lr][kc]);
-      bf16x8 yh, yl, uh, ul;
-      split8(&sm.Y[16 * ti + lr][kc], 1.0f, yh, yl);
-      split8(&sm.U[16 * tj + lr][kc], 1.0f, uh, ul);
+      const bf16x8 yh = ld8(&sm.Yh[16 * ti + lr][kc]), yl = ld8(&sm.Yl[16 * ti + lr][kc]);
+      const bf16x8 uh = ld8(&sm.Uh[16 * tj + lr][kc]), ul = ld8(&sm.Ul[16 * tj + lr][kc]);
       pt = mfma_bf16(qa, kb, pt);
       mt = mfma_bf16(ka, kb, mt);
       at = mfma_bf16(yh, uh, at);
@@ -259,13 +287,16 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   // ---- P2: dQ and dK, this wave's dk columns, one 16-column tile at a time ----
   {
-    const float brow[2] = {sm.beta[lr], sm.beta[16 + lr]};
     float hdh = 0.0f, tl = 0.0f;
     float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 1
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int dkt = 16 * (NTW * wave + nt);   // first dk column of this tile
-      f32x4 aq[2], ar[2], au[2];
+    struct Acc {
+      f32x4 q[2], r[2], u[2];
+    };
+    // dO h^T, dR h^T and U dh^T for one tile
+    auto tile_mm = [&](const Fetch &f, Acc &acc) {
+      f32x4(&aq)[2] = acc.q;
+      f32x4(&ar)[2] = acc.r;
+      f32x4(&au)[2] = acc.u;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         aq[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -275,17 +306,26 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
       for (int kk = 0; kk < KKV; ++kk) {
         const int kc = 32 * kk + 8 * lg;
-        // h^T and dh^T as B operands: column dk = dkt + lr, rows dv kc .. kc + 7
-        const long o = wsS + (long)(dkt + lr) * DV + kc;
         bf16x8 hh, hl, gh, gl;
-        split8g(ws_h + o, hh, hl, hdh, ws_dh + o);
-        split8(ws_dh + o, 1.0f, gh, gl);
+        {
+          const f32x4 a = f.h[kk][0], b = f.h[kk][1], c2 = f.g[kk][0], d = f.g[kk][1];
+          bf16x4 ah, al, bh, bl;
+          split4(a, ah, al);
+          split4(b, bh, bl);
+          hh = cat(ah, bh);
+          hl = cat(al, bl);
+          split4(c2, ah, al);
+          split4(d, bh, bl);
+          gh = cat(ah, bh);
+          gl = cat(al, bl);
+        }
+        if constexpr (GATE == kGateScalar) hdh = dot8_split(hh, hl, gh, gl, hdh);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const bf16x8 da = ld8(&sm.D[16 * rb + lr][kc]);
-          bf16x8 rh, rl, uh, ul;
-          split8(&sm.Y[16 * rb + lr][kc], brow[rb], rh, rl);   // dR = b dY
-          split8(&sm.U[16 * rb + lr][kc], 1.0f, uh, ul);
+          // dY h^T here; the row factor b (dR = diag(b) dY) is applied after
+          const bf16x8 rh = ld8(&sm.Yh[16 * rb + lr][kc]), rl = ld8(&sm.Yl[16 * rb + lr][kc]);
+          const bf16x8 uh = ld8(&sm.Uh[16 * rb + lr][kc]), ul = ld8(&sm.Ul[16 * rb + lr][kc]);
           aq[rb] = mfma_bf16(da, hh, aq[rb]);
           aq[rb] = mfma_bf16(da, hl, aq[rb]);
           ar[rb] = mfma_bf16(rh, hh, ar[rb]);
@@ -296,6 +336,19 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           au[rb] = mfma_bf16(uh, gl, au[rb]);
         }
       }
+    };
+    // dq and dk rows of this chunk: a buffer range that ends at the last valid
+    // row, so stores to rows past the sequence's end are dropped (the host
+    // bounds one chunk's rows below 4 GiB)
+    const unsigned rows_bytes = 4u * ((unsigned)(n - 1) * (unsigned)(H * DK) + DK);
+    const rsrc_t rdq = make_rsrc32(dq + row0 * DK, rows_bytes);
+    const rsrc_t rdk = make_rsrc32(dk + row0 * DK, rows_bytes);
+    // the n x n x dk products, then dQ, dK and the dg terms of one tile
+    auto tile_out = [&](int nt, const Acc &acc) {
+      const int dkt = 16 * (NTW * wave + nt);   // first dk column of this tile
+      const f32x4(&aq)[2] = acc.q;
+      const f32x4(&ar)[2] = acc.r;
+      const f32x4(&au)[2] = acc.u;
       // the n x n x dk products: k = tokens {4 lg + j} u {16 + 4 lg + j};
       // K and Q columns dkt + lr as B operands (transposing reads)
       const int c0 = dkt + 4 * (lr & 3);
@@ -328,16 +381,16 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const int r0 = 16 * rb + 4 * lg, col = dkt + lr;
         const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&sm.gam[r0]);
         const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&sm.ec[r0]);
+        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&sm.beta[r0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = r0 + e;
           const float gq = gm4[e] * aq[rb][e];
-          const float gr = gm4[e] * ar[rb][e];
+          const float gr = gm4[e] * b4[e] * ar[rb][e];
           const float gu = ec4[e] * au[rb][e];
-          if (r < n) {
-            dq[trow(r) * DK + col] = gq + xq[e];
-            dk[trow(r) * DK + col] = gu - gr + xk[e];
-          }
+          const unsigned off = 4u * ((unsigned)r * (unsigned)(H * DK) + (unsigned)col);
+          buf_st1(gq + xq[e], rdq, off);
+          buf_st1(gu - gr + xk[e], rdk, off);
           if constexpr (GATE == kGateScalar) {
             const float qv = (float)sm.Q[r][col], kv = (float)sm.K[r][col];
             part[rb][e] += qv * gq - kv * gr - kv * gu;
@@ -345,6 +398,18 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           }
         }
       }
+    };
+    Acc acc;
+    tile_mm(fa, acc);
+    tile_out(0, acc);
+    if constexpr (NTW == 2) {
+      // the second tile after the first: both tiles' operands live at once
+      // would not fit the registers (the other workgroup on the CU covers
+      // this fetch's latency)
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(1, fb);
+      tile_mm(fb, acc);
+      tile_out(1, acc);
     }
     if constexpr (GATE == kGateScalar) {
 #pragma unroll
