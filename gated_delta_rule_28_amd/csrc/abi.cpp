@@ -192,13 +192,12 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;
   a.d_initial_state = d_initial_state;
-  // workspace partitions: h, dh [chain][chunk][D][D]; R, U, dY [chain][chunk][C][D]
+  // workspace partitions: h, dh [chain][chunk][D][D]; U, dY [chain][chunk][C][D]
   const long nblk = (long)B * H * ((T + gdr::kBwdChunk - 1) / gdr::kBwdChunk);
   float *w = static_cast<float *>(workspace);
   a.ws_h = w;
   a.ws_dh = a.ws_h + nblk * Dk * Dk;
-  a.ws_r = a.ws_dh + nblk * Dk * Dk;
-  a.ws_u = a.ws_r + nblk * gdr::kBwdChunk * Dk;
+  a.ws_u = a.ws_dh + nblk * Dk * Dk;
   a.ws_dy = a.ws_u + nblk * gdr::kBwdChunk * Dk;
   a.stream = stream;
   hipError_t e = gdr::launch_chunk_bwd_passes(a);

@@ -12,14 +12,16 @@
 //   O = diag(gam) Q h + P U,        h' = gam_last h + K^T diag(ec) U
 //
 // is differentiated in reverse.  Two sequential passes (the forward kernel in
-// its recompute and reverse modes) leave in the workspace, per chunk, h, R and
-// U and, from the reverse pass, dh (the gradient of the state leaving the
+// its recompute and reverse modes) leave in the workspace, per chunk, h and U
+// and, from the reverse pass, dh (the gradient of the state leaving the
 // chunk) and dY = T^T dU with dU = diag(ec) K dh + P^T dO.  Given those, every
 // chunk's gradients are independent:
 //
 //   dR = diag(b) dY = dV          dA = -strict_lower(dY U^T)
 //   dP = lower_incl(dO U^T)       dM = diag(b) dA
 //   db_r  = sum_v dY_rv R_rv + sum_s dA_rs M_rs
+//         = dY_r . v_r - gam_r k_r . (dY h^T)_r + sum_s dA_rs M_rs
+//           (R = V - diag(gam) K h: the first sum needs no stored R)
 //   dQ = diag(gam) dO h^T + (dP o Gam) K
 //   dK = -diag(gam) dR h^T + diag(ec) U dh^T + (dM o Gam) K + (dM o Gam)^T K
 //        + (dP o Gam)^T Q
@@ -55,7 +57,8 @@ struct __align__(16) BwdSmem {
   bf16 XPh[C][LDX], XPl[C][LDX];       // dP o Gam, lower inclusive
   bf16 XMh[C][LDX], XMl[C][LDX];       // dM o Gam, strictly lower
   float g[C], gam[C], ec[C], beta[C];
-  float dba[C];                        // sum_v dY_rv R_rv
+  float dba[C];                        // sum_v dY_rv V_rv
+  float dbp[NW][C];                    // per-wave gam_r k_r . (dY h^T)_r
   float dg[C];
   float dgp[NW][C];                    // per-wave row terms of dg
   float tlast[NW], hdh[NW];            // per-wave sums for dg_last
@@ -96,9 +99,10 @@ __device__ __forceinline__ float sum64(float x) {
 template <int DK, int GATE>
 __global__ void __launch_bounds__(64 * NW, 2)
 chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
-                      const float *__restrict__ beta, const float *__restrict__ log_alpha,
+                      const bf16 *__restrict__ v, const float *__restrict__ beta,
+                      const float *__restrict__ log_alpha,
                       const bf16 *__restrict__ d_o, const float *__restrict__ ws_h,
-                      const float *__restrict__ ws_r, const float *__restrict__ ws_u,
+                      const float *__restrict__ ws_u,
                       const float *__restrict__ ws_dh, const float *__restrict__ ws_dy,
                       float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
                       float *__restrict__ dbeta, float *__restrict__ dlog_alpha, int B, int T,
@@ -120,7 +124,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const long row0 = ((long)bb * T + (long)c * C) * H + hh;   // token row of the chunk's row 0
   auto trow = [&](int r) { return row0 + (long)r * H; };
   const long wsS = ((long)chain * nchunks + c) * (DK * DV);   // h, dh of this chunk
-  const long wsR = ((long)chain * nchunks + c) * (C * DV);    // R, U, dY of this chunk
+  const long wsR = ((long)chain * nchunks + c) * (C * DV);    // U, dY of this chunk
 
   // h^T and dh^T of one of this wave's 16-column dk tiles as B operands:
   // column dk = dkt + lr, rows dv 32 kk + 8 lg .. +7.  The first tile's loads
@@ -143,7 +147,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   Fetch fa, fb;
   fetch(0, fa);
 
-  // ---- P0: inputs into LDS; dV = b dY; sum_v dY R; decays ----
+  // ---- P0: inputs into LDS; dV = b dY; sum_v dY V; decays ----
   for (int i = tid; i < C * SM::LDX; i += 64 * NW) {     // upper-right blocks stay zero
     (&sm.XPh[0][0])[i] = (bf16)0.0f;
     (&sm.XPl[0][0])[i] = (bf16)0.0f;
@@ -162,7 +166,8 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     constexpr int F4 = DV / 32;                          // 8 threads per row, F4 float4 each
     const int r = tid >> 3, f0 = (tid & 7) * F4;
     u32x4 xq[NB], xk[NB], xd[NB];
-    f32x4 u[F4], y[F4], rr[F4];
+    f32x4 u[F4], y[F4];
+    bf16x4 vr[F4];                                       // v_r at the same columns as y
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int i = tid + 64 * NW * j, rj = i / BPR, blk = i % BPR;
@@ -181,7 +186,8 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const long o = wsR + r * DV + 4 * (f0 + j);
       u[j] = *reinterpret_cast<const f32x4 *>(ws_u + o);
       y[j] = *reinterpret_cast<const f32x4 *>(ws_dy + o);
-      rr[j] = *reinterpret_cast<const f32x4 *>(ws_r + o);
+      vr[j] = bf16x4{(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+      if (r < n) vr[j] = *reinterpret_cast<const bf16x4 *>(v + trow(r) * DV + 4 * (f0 + j));
     }
     const float b = r < n ? beta[trow(r)] : 0.0f;
 #pragma unroll
@@ -202,7 +208,8 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       split4(y[j], h4, l4);
       *reinterpret_cast<bf16x4 *>(&sm.Yh[r][col]) = h4;
       *reinterpret_cast<bf16x4 *>(&sm.Yl[r][col]) = l4;
-      dot += (y[j][0] * rr[j][0] + y[j][1] * rr[j][1]) + (y[j][2] * rr[j][2] + y[j][3] * rr[j][3]);
+      dot += (y[j][0] * (float)vr[j][0] + y[j][1] * (float)vr[j][1]) +
+             (y[j][2] * (float)vr[j][2] + y[j][3] * (float)vr[j][3]);
       if (r < n) *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + col) = y[j] * b;
     }
     dot += __shfl_xor(dot, 1);
@@ -288,7 +295,6 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // ---- P2: dQ and dK, this wave's dk columns, one 16-column tile at a time ----
   {
     float hdh = 0.0f, tl = 0.0f;
-    float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     struct Acc {
       f32x4 q[2], r[2], u[2];
     };
@@ -335,6 +341,9 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           au[rb] = mfma_bf16(ul, gh, au[rb]);
           au[rb] = mfma_bf16(uh, gl, au[rb]);
         }
+        // keep the LDS operand reads of at most two k steps in flight: hoisting
+        // all of them ahead of the products runs the registers out
+        if (kk & 1) __builtin_amdgcn_sched_barrier(0);
       }
     };
     // dq and dk rows of this chunk: a buffer range that ends at the last valid
@@ -356,8 +365,12 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                             ld_tr4(&sm.K[16 + 4 * lg + (lr >> 2)][c0]));
       const bf16x8 qb = cat(ld_tr4(&sm.Q[4 * lg + (lr >> 2)][c0]),
                             ld_tr4(&sm.Q[16 + 4 * lg + (lr >> 2)][c0]));
+      // per-row sums of this tile, added into this wave's LDS rows at its end
+      float part[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      float partb[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
+        if (rb == 1) __builtin_amdgcn_sched_barrier(0);   // one row block's operands at a time
         const int ra = 16 * rb + lr;
         auto row8 = [&](const bf16(*X)[SM::LDX]) {
           return cat(*reinterpret_cast<const bf16x4 *>(&X[ra][4 * lg]),
@@ -391,13 +404,29 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const unsigned off = 4u * ((unsigned)r * (unsigned)(H * DK) + (unsigned)col);
           buf_st1(gq + xq[e], rdq, off);
           buf_st1(gu - gr + xk[e], rdk, off);
+          const float kv = (float)sm.K[r][col];
+          partb[rb][e] += kv * (gm4[e] * ar[rb][e]);
           if constexpr (GATE == kGateScalar) {
-            const float qv = (float)sm.Q[r][col], kv = (float)sm.K[r][col];
+            const float qv = (float)sm.Q[r][col];
             part[rb][e] += qv * gq - kv * gr - kv * gu;
             tl += kv * gu;
           }
         }
       }
+      // lane lr = 0 of each row group owns rows 16 rb + 4 lg + e of this wave's
+      // slots: the first tile writes them, the second adds (same lane, in order)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * lg + e;
+          const float pb = sum16(partb[rb][e]);
+          if (lr == 0) sm.dbp[wave][r] = (nt == 0 ? 0.0f : sm.dbp[wave][r]) + pb;
+          if constexpr (GATE == kGateScalar) {
+            const float p = sum16(part[rb][e]);
+            if (lr == 0) sm.dgp[wave][r] = (nt == 0 ? 0.0f : sm.dgp[wave][r]) + p;
+          }
+        }
     };
     Acc acc;
     tile_mm(fa, acc);
@@ -412,13 +441,6 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       tile_out(1, acc);
     }
     if constexpr (GATE == kGateScalar) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = sum16(part[rb][e]);
-          if (lr == 0) sm.dgp[wave][16 * rb + 4 * lg + e] = p;
-        }
       tl = sum64(tl);
       hdh = sum64(hdh);
       if (lane == 0) {
@@ -433,6 +455,8 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   if (wave == 0) {
     const int r = lane & 31;
     float db = sm.dba[r], gsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) db -= sm.dbp[w][r];
 #pragma unroll 8
     for (int s2 = 0; s2 < C; ++s2) {
       db += sm.Hm[r][s2];
@@ -467,8 +491,9 @@ hipError_t launch_dk(const BwdArgs &a) {
   dim3 grid((unsigned)((long)a.B * a.H * nchunks)), block(64 * NW);
 #define GDR_LAUNCH(G)                                                                           \
   hipLaunchKernelGGL((chunk_bwd_grad_kernel<DK, G>), grid, block, 0, a.stream,                  \
-                     (const bf16 *)a.q, (const bf16 *)a.k, a.beta, a.log_alpha,                \
-                     (const bf16 *)a.d_o, a.ws_h, a.ws_r, a.ws_u, a.ws_dh, a.ws_dy, a.dq, a.dk, \
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,          \
+                     a.log_alpha, (const bf16 *)a.d_o, a.ws_h, a.ws_u, a.ws_dh, a.ws_dy, a.dq,  \
+                     a.dk,                                                                     \
                      a.dv, a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
   if (a.gate == kGateNone) GDR_LAUNCH(kGateNone);
   else GDR_LAUNCH(kGateScalar);

@@ -61,7 +61,7 @@
 //
 // Backward passes (template MODE).  The same pipeline runs the two sequential
 // passes of the backward: kModeRec recomputes the forward and stores, per
-// chunk, the entering state h, R = V - diag(gam) K h and U (no outputs);
+// chunk, the entering state h and U (no outputs);
 // kModeRev walks the chunks in reverse with v = dO, carrying dS, the
 // gradient of the state (dS_T in, dS_0 out):
 //
@@ -472,14 +472,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             rr[e] = (ERASE ? (float)vv[e] - gm4[e] * KS[rb][e] : (float)vv[e]) * b4[e];
-          if constexpr (MODE == kModeRec) {
-            // R = V - diag(gam) K S of chunk s (before the factor b)
-            float *rbp = ws_b + ((long)chain * nchunks + s) * (C * DV);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              __builtin_nontemporal_store((float)vv[e] - gm4[e] * KS[rb][e],
-                                          rbp + (r0 + e) * DV + col0 + lr);
-          }
           rv[rb] = rr;
           split4(rr, rh2[rb], rl2[rb]);
         }
@@ -509,7 +501,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             u = mfma_bf16(tl, Rh, u);
             u = mfma_bf16(th, Rl, u);
             if constexpr (MODE == kModeRec) {
-              float *ubp = ws_c + ((long)chain * nchunks + s) * (C * DV);
+              float *ubp = ws_b + ((long)chain * nchunks + s) * (C * DV);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 __builtin_nontemporal_store(u[e], ubp + (16 * rb + 4 * lg + e) * DV + col0 + lr);
@@ -921,7 +913,7 @@ hipError_t launch_passes(const BwdArgs &a) {
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, true, false, kModeRec>), grid,
                      block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      a.beta, a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0,
-                     nullptr, a.ws_h, a.ws_r, a.ws_u);
+                     nullptr, a.ws_h, a.ws_u, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, true, false, kModeRev>), grid,

@@ -61,16 +61,16 @@ struct BwdArgs {
   const void *d_o;              // dL/do [B, T, H, D], dtype of q
   const float *d_final_state;   // dL/dS_T or nullptr
   float *dq, *dk, *dv, *dbeta, *dlog_alpha, *d_initial_state;
-  // workspace partitions, per (chain, chunk): the entering state h, R, U
-  // (recompute pass); dh, dY (reverse pass)
-  float *ws_h, *ws_r, *ws_u, *ws_dh, *ws_dy;
+  // workspace partitions, per (chain, chunk): the entering state h and U
+  // (recompute pass); dh and dY (reverse pass)
+  float *ws_h, *ws_u, *ws_dh, *ws_dy;
   hipStream_t stream;
 };
 
-// workspace floats per (chain, chunk): h and dh [D][D], R, U, dY [C][D]
-inline long bwd_ws_floats_per_chunk(int D) { return 2L * D * D + 3L * kBwdChunk * D; }
+// workspace floats per (chain, chunk): h and dh [D][D], U and dY [C][D]
+inline long bwd_ws_floats_per_chunk(int D) { return 2L * D * D + 2L * kBwdChunk * D; }
 bool chunk_bwd_supported(int D, bool in_bf16, int gate, bool erase, long H);
-// the two sequential passes: the forward recomputed (h, R, U per chunk), then
+// the two sequential passes: the forward recomputed (h, U per chunk), then
 // the reverse pass (dh, dY per chunk, and dS_0)
 hipError_t launch_chunk_bwd_passes(const BwdArgs &a);
 // the chunk-parallel gradients dq, dk, dv, dbeta, dlog_alpha

@@ -183,9 +183,9 @@ size_t gdr_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
 /*
  * gdr_chunk_bwd_workspace_bytes -- device workspace gdr_chunk_bwd needs for
  * these arguments: per (batch, head) chain and 32-token chunk, two Dk x Dv
- * fp32 states and three 32 x Dv fp32 tiles, 4 (2 Dk Dv + 96 Dv) bytes (about
- * 2.8 GiB for B = 8, H = 16, T = 4096, Dk = Dv = 128).  0 when the call is
- * not supported or has no tokens.
+ * fp32 states and two 32 x Dv fp32 tiles, 4 (2 Dk Dv + 64 Dv) bytes (2.5 GiB
+ * for B = 8, H = 16, T = 4096, Dk = Dv = 128).  0 when the call is not
+ * supported or has no tokens.
  */
 size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                                      int in_dtype, int gate);
@@ -239,8 +239,8 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
  * GDR_NOALLOC_SCRATCH_BYTES inside the library (one per GPU the library runs
  * on, held until the process ends); the call allocates nothing.  A call whose
  * gdr_chunk_bwd_workspace_bytes exceeds GDR_NOALLOC_SCRATCH_BYTES (64 MiB:
- * e.g. 372 chain-chunks of 32 tokens at Dk = Dv = 128, such as B = 1, H = 4,
- * T = 2976) returns GDR_EWORKSPACE and launches nothing.  Every call on a GPU
+ * 409 chain-chunks of 32 tokens at Dk = Dv = 128, such as B = 1, H = 4,
+ * T = 3264) returns GDR_EWORKSPACE and launches nothing.  Every call on a GPU
  * uses that GPU's one array: calls that overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller.  The array's
  * contents between calls are unspecified; nothing in them is read before

@@ -197,12 +197,12 @@ def bwd_ws(B=8, T=4096, H=16, D=128, chunk=0, in_dtype=_abi.GDR_BF16, gate=_abi.
 
 
 def test_backward_workspace_size():
-    # per chain and 32-token chunk: two D x D states and three 32 x D tiles, fp32
-    per = 4 * (2 * 128 * 128 + 3 * 32 * 128)
+    # per chain and 32-token chunk: two D x D states and two 32 x D tiles, fp32
+    per = 4 * (2 * 128 * 128 + 2 * 32 * 128)
     assert bwd_ws() == 8 * 16 * 128 * per
     assert bwd_ws(T=33) == 8 * 16 * 2 * per                 # a ragged tail is one more chunk
     assert bwd_ws(gate=_abi.GDR_GATE_NONE) == bwd_ws()
-    assert bwd_ws(D=64, T=64, B=1, H=1) == 2 * 4 * (2 * 64 * 64 + 3 * 32 * 64)
+    assert bwd_ws(D=64, T=64, B=1, H=1) == 2 * 4 * (2 * 64 * 64 + 2 * 32 * 64)
     # unsupported calls and empty inputs need none
     for kw in (dict(in_dtype=_abi.GDR_F32), dict(gate=_abi.GDR_GATE_CHANNEL), dict(D=32),
                dict(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE), dict(T=0), dict(B=0),
@@ -239,7 +239,7 @@ def bwd(**kw):
     (dict(H=300000), _abi.GDR_EUNSUPPORTED),
     (dict(workspace=None), _abi.GDR_EWORKSPACE),
     (dict(workspace=FAKE + 16), _abi.GDR_EWORKSPACE),          # not 256-byte aligned
-    (dict(workspace_bytes=4 * (2 * 128 * 128 + 3 * 32 * 128) - 1), _abi.GDR_EWORKSPACE),
+    (dict(workspace_bytes=4 * (2 * 128 * 128 + 2 * 32 * 128) - 1), _abi.GDR_EWORKSPACE),
 ])
 def test_chunk_bwd_rejects(kw, want):
     assert bwd(**kw) == want
@@ -264,7 +264,7 @@ def test_noalloc_backward_refuses_more_than_its_array():
              dbeta=FAKE, dlog_alpha=FAKE, d_initial_state=None, stream=None)
     assert _abi.gdr_chunk_bwd_noalloc(**a) == _abi.GDR_EWORKSPACE
     # one chain-chunk more than fits is refused too
-    per = 4 * (2 * 128 * 128 + 3 * 32 * 128)
+    per = 4 * (2 * 128 * 128 + 2 * 32 * 128)
     fit = limit // per
     assert bwd_ws(B=1, H=1, T=32 * (fit + 1)) > limit >= bwd_ws(B=1, H=1, T=32 * fit)
     assert _abi.gdr_chunk_bwd_noalloc(**dict(a, B=1, H=1, T=32 * (fit + 1))) == \
