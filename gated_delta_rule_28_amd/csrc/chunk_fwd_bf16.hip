@@ -27,12 +27,15 @@
 //
 //   state waves (DVS/16 of them) each own 16 state columns and keep them in
 //     MFMA accumulators for the whole sequence.  Every state-dependent
-//     product (K S, Q S, T'R, P U, K^T U') takes its right operand straight
-//     from accumulator registers: an accumulator tile holds rows 4g..4g+3
-//     of a column, which is what a 16x16x32 B operand needs when the k axis
-//     of S is ordered so that tile pair (2kk, 2kk+1) holds dk 32kk + 8g + j
+//     product (K S, T'R, K^T U') takes its right operand straight from
+//     accumulator registers: an accumulator tile holds rows 4g..4g+3 of a
+//     column, which is what a 16x16x32 B operand needs when the k axis of S
+//     is ordered so that tile pair (2kk, 2kk+1) holds dk 32kk + 8g + j
 //     (j < 4) and 32kk + 8g + 4 + j in its rows 4g + j.  q and k then stay
-//     in natural dk order in LDS.
+//     in natural dk order in LDS.  The output tile is formed transposed
+//     (S^T Q^T and U^T P^T, the same registers as left operands), so that a
+//     lane ends up with four adjacent values of one output row: one 16-byte
+//     store per lane and row block.
 //   prep waves 0..2 bring chunks into LDS with LDS DMA (no registers, no
 //     LDS write instructions), scan the log decays and form the decayed
 //     K K^T / Q K^T tiles (A and P); prep wave 3 solves the diagonal 16x16
@@ -245,18 +248,21 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     __syncthreads();
     __syncthreads();
 
-    // element offsets of this lane's output values from a chunk's first row,
-    // and their byte offsets in o; unsigned 32-bit, like the buffer offset
-    // they feed (the host bounds one chunk's rows of a 4-byte tensor below
-    // 4 GiB, so neither wraps)
-    unsigned oel[2][4], ooff[2][4];
+    // The output tile is formed transposed (Q S and P U as S^T Q^T and
+    // U^T P^T: the same operand registers, swapped), so lane (lr, lg) holds
+    // O[16 rb + lr][col0 + 4 lg + e], e = 0..3: four adjacent values of one
+    // row, written by one 16-byte store.  Element offsets of those values
+    // from a chunk's first row, and the byte offset of the first in o;
+    // unsigned 32-bit, like the buffer offset they feed (the host bounds one
+    // chunk's rows of a 4-byte tensor below 4 GiB, so neither wraps)
+    unsigned oel[2][4], ooff[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        oel[rb][e] = (unsigned)(16 * rb + 4 * lg + e) * (unsigned)(H * DV) + (unsigned)(col0 + lr);
-        ooff[rb][e] = (unsigned)sizeof(OutT) * oel[rb][e];
-      }
+      for (int e = 0; e < 4; ++e)
+        oel[rb][e] = (unsigned)(16 * rb + lr) * (unsigned)(H * DV) + (unsigned)(col0 + 4 * lg + e);
+      ooff[rb] = (unsigned)sizeof(OutT) * oel[rb][0];
+    }
     // v, transposing read: rows 16 rb + 4 lg + (lr >> 2), columns
     // 16 wave + 4 (lr & 3) .. +3 (an 8-byte half of a 16-byte block)
     const int v_off = v_at(4 * lg + (lr >> 2), 2 * wave + ((lr & 3) >> 1)) + 8 * (lr & 1);
@@ -280,7 +286,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         Sl[kk] = cat(l0, l1);
       }
     };
-    split_state();
 
     // the fused output gate of this lane's O values, loaded one chunk ahead
     // (the state waves are the serial path: a load used in the same chunk
@@ -309,6 +314,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const int s = it - 1;            // chunk of this iteration
      if constexpr (MODE == kModeRev) {
       if (s >= 0) {
+        // the hi/lo split of dS for this chunk's products: after the barrier,
+        // in the same block as the products, so the scheduler can overlap the
+        // split with their issue
+        split_state();
         const int c = nchunks - 1 - s;   // chunks run last to first
         const In &bs = *at_off(&sm.in[0], slot_off(s % NIN, (int)sizeof(In)));
         const typename SM::PT &ps = *at_off(&sm.p[0], slot_off(s % NPR, (int)sizeof(typename SM::PT)));
@@ -403,7 +412,6 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(aq, Bql, acc);
           Sacc[mb] = acc;
         }
-        split_state();
       }
      } else {
       f32x4 QS[2];
@@ -431,6 +439,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             for (int e = 0; e < 4; ++e)
               __builtin_nontemporal_store(Sacc[mb][e], hb + srow(mb, e) * DV + col0 + lr);
         }
+        // the hi/lo split of S for this chunk's products: after the barrier,
+        // in the same block as K S and Q S, so the scheduler can overlap the
+        // split with their issue
+        split_state();
         f32x4 KS[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -444,14 +456,15 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             } else if constexpr (ERASE) {
               const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
               const bf16x8 ak = ld8(reinterpret_cast<const bf16 *>(Kb + 16 * rb * QRB + kq_off[kk]));
+              // K S, and Q S transposed (S^T Q^T: operands swapped)
               a1 = mfma_bf16(ak, Sh[kk], a1);
-              a2 = mfma_bf16(aq, Sh[kk], a2);
+              a2 = mfma_bf16(Sh[kk], aq, a2);
               a1 = mfma_bf16(ak, Sl[kk], a1);
-              a2 = mfma_bf16(aq, Sl[kk], a2);
+              a2 = mfma_bf16(Sl[kk], aq, a2);
             } else {
               const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
-              a2 = mfma_bf16(aq, Sh[kk], a2);
-              a2 = mfma_bf16(aq, Sl[kk], a2);
+              a2 = mfma_bf16(Sh[kk], aq, a2);
+              a2 = mfma_bf16(Sl[kk], aq, a2);
             }
           }
           KS[rb] = a1;
@@ -524,29 +537,22 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const long orow = (tok0 + (long)t0 * H) * DV;   // element offset of the chunk's first row
         // the chunk's rows: smaller than 4 GiB (the host checks the shape)
         const rsrc_t ro = make_rsrc32(o + orow, (unsigned)sizeof(OutT) * ((unsigned)(n - 1) * H * DV + DV));
+        f32x4 oacc[2];
 #pragma unroll
         for (int rb = 0; rb < 2 && WANT_O; ++rb) {
-          const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&bs.fq[16 * rb + 4 * lg]);
-          f32x4 acc = gm4 * QS[rb];
+          // O^T = diag(gam) (Q S)^T + U^T P^T: this lane's values are all of
+          // token 16 rb + lr
+          f32x4 acc = bs.fq[16 * rb + lr] * QS[rb];
+          // row 16 rb + lr of P (k = tokens {4 lg + j} u {16 + 4 lg + j}),
+          // the B operand of U^T P^T
           const bf16x8 ph = cat(ld_tr4(&ps.Ph[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
                                 ld_tr4(&ps.Ph[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
           const bf16x8 pl = cat(ld_tr4(&ps.Pl[4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]),
                                 ld_tr4(&ps.Pl[16 + 4 * lg + (lr >> 2)][16 * rb + 4 * (lr & 3)]));
-          acc = mfma_bf16(ph, Uh, acc);
-          acc = mfma_bf16(pl, Uh, acc);
-          acc = mfma_bf16(ph, Ul, acc);
-          if constexpr (FUSED) acc = acc * og[rb];
-          // lane holds O rows 16 rb + 4 lg + e of column col0 + lr: stored
-          // straight from the accumulator (16 lanes write 16 adjacent values
-          // of a row); rows past the end of the sequence are not written
-          if (n == C) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[rb][e]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (16 * rb + 4 * lg + e < n) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[rb][e]);
-          }
+          acc = mfma_bf16(Uh, ph, acc);
+          acc = mfma_bf16(Uh, pl, acc);
+          acc = mfma_bf16(Ul, ph, acc);
+          oacc[rb] = acc;
         }
         const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
         const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
@@ -560,7 +566,17 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(a, Wl, acc);
           Sacc[mb] = acc;
         }
-        split_state();   // for the next chunk
+        // lane holds O[16 rb + lr][col0 + 4 lg .. +3], stored straight from
+        // the accumulator by one wide store (the 4 lanes of a row write its
+        // 16 adjacent values).  Rows past the end of the sequence lie beyond
+        // the descriptor (row r >= n starts at r H DV >= (n - 1) H DV + DV
+        // elements) and are dropped: no branch on the row count
+#pragma unroll
+        for (int rb = 0; rb < 2 && WANT_O; ++rb) {
+          f32x4 acc = oacc[rb];
+          if constexpr (FUSED) acc = acc * og[rb];
+          buf_st4(acc, ro, ooff[rb], OutT{});
+        }
       }
      }
       __syncthreads();

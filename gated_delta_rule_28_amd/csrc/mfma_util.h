@@ -129,6 +129,7 @@ __device__ __forceinline__ bf16x4 ld_tr4(const bf16 *p) {
 // bounds every access by the end of the tensor.  Offsets are in bytes; the
 // scalar offset stays 0 so the bounds check sees the whole offset.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Descriptor of a range known to be shorter than 4 GiB (no clamp: a 64-bit
 // clamp compiles to VALU compares that the scalar code then waits for).
@@ -151,6 +152,20 @@ __device__ __forceinline__ void buf_st1(float x, rsrc_t r, unsigned off) {
 }
 __device__ __forceinline__ void buf_st1(bf16 x, rsrc_t r, unsigned off) {
   __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r,
+                                        __builtin_bit_cast(int, off), 0, 0);
+}
+
+// four adjacent output values of a row in one 16-byte (fp32) or 8-byte
+// (bf16) store
+__device__ __forceinline__ void buf_st4(f32x4 x, rsrc_t r, unsigned off, float) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r,
+                                         __builtin_bit_cast(int, off), 0, 0);
+}
+__device__ __forceinline__ void buf_st4(f32x4 x, rsrc_t r, unsigned off, bf16) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  const bf16x4_t h = __builtin_convertvector(x, bf16x4_t);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, h), r,
                                         __builtin_bit_cast(int, off), 0, 0);
 }
 

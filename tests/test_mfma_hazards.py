@@ -12,8 +12,8 @@ compiles them to assembly and checks, along the shortest path in layout
 order, that every read of an MFMA result reached across a branch is at
 least 8 wait states after the MFMA.  It also checks that no inline-assembly
 instruction writes a register that an MFMA issued just before still reads as
-its accumulator input: the compiler inserts the wait states for that only
-before its own instructions.
+its accumulator input, over every path into the write: the compiler
+inserts the wait states for that only before its own instructions.
 
 A third check covers the DPP forms written as inline assembly (the
 v_fmac_f32_dpp row broadcasts of the diagonal triangular solve).  A DPP
@@ -120,13 +120,41 @@ def short_reads(lines, min_ws=MIN_WAIT_STATES):
     return found
 
 
-def asm_writes_after_mfma(lines, min_ws=MIN_WAIT_STATES):
-    """(mfma line, asm line) where an inline-assembly instruction writes a VGPR
-    that an MFMA issued fewer than min_ws wait states before reads as its
-    accumulator input (the compiler protects that read only from its own
-    instructions).  The first operand of each instruction in an inline
-    block is taken as its destination."""
+ACC_WAR_WAIT_STATES = 18   # more than the longest MFMA here (8 passes) reads its accumulator
+
+
+def _branch_sources(lines):
+    """label -> indices of the branch instructions that jump to it"""
+    out = {}
+    for i, line in enumerate(lines):
+        t = line.strip()
+        if t.startswith(("s_cbranch", "s_branch")):
+            out.setdefault(t.split()[1], []).append(i)
+    return out
+
+
+def _falls_through_into(lines, i):
+    """whether the instruction before line i (a label) can fall through to it"""
+    k = i - 1
+    while k >= 0:
+        t = lines[k].strip()
+        if t and not t.startswith((";", ".")) and not t.endswith(":"):
+            return not t.startswith(("s_branch", "s_endpgm", "s_setpc"))
+        if t.endswith(":") and not t.startswith(";"):
+            return True
+        k -= 1
+    return False
+
+
+def asm_writes_after_mfma(lines, min_ws=ACC_WAR_WAIT_STATES):
+    """(mfma line, asm line, wait states) where an inline-assembly instruction
+    writes a VGPR that an MFMA reads as its accumulator input fewer than
+    min_ws wait states earlier, on any path into the write (fall-through and
+    every branch to each label crossed, walked backwards).  The compiler
+    protects that read only from its own instructions.  The first operand of
+    each instruction in an inline block is taken as its destination."""
     found = []
+    sources = _branch_sources(lines)
     inside = False
     for j, line in enumerate(lines):
         s = line.strip()
@@ -142,19 +170,26 @@ def asm_writes_after_mfma(lines, min_ws=MIN_WAIT_STATES):
         if len(parts) < 2:
             continue
         dst = _vregs(parts[1].split(",")[0])
-        ws = 0
-        for i in range(j - 1, max(j - 1 - WINDOW, -1), -1):
-            t_ = lines[i].strip()
-            if not t_ or t_.startswith((";", ".")):
-                continue
-            if t_.startswith(("s_cbranch", "s_branch", "s_endpgm")) or t_.endswith(":"):
-                break
-            if t_.startswith("v_mfma"):
-                ops = t_.split(None, 1)[1].split(",")
-                if len(ops) >= 4 and _vregs(ops[3]) & dst and ws < min_ws:
-                    found.append((i + 1, j + 1))
-                break
-            ws += int(t_.split()[1]) + 1 if t_.startswith("s_nop") else 1
+        stack, seen, near = [(j - 1, 0)], set(), {}
+        while stack:
+            i, ws = stack.pop()
+            while i >= 0 and ws < min_ws and (i, ws) not in seen:
+                seen.add((i, ws))
+                t_ = lines[i].strip()
+                if t_.endswith(":") and not t_.startswith(";"):
+                    stack.extend((b, ws) for b in sources.get(t_[:-1], []))
+                    if not _falls_through_into(lines, i):
+                        break
+                elif t_ and not t_.startswith((";", ".")):
+                    if t_.startswith("s_endpgm"):
+                        break
+                    if t_.startswith("v_mfma"):
+                        ops = t_.split(None, 1)[1].split(",")
+                        if len(ops) >= 4 and _vregs(ops[3]) & dst:
+                            near[i + 1] = min(near.get(i + 1, ws), ws)
+                    ws += int(t_.split()[1]) + 1 if t_.startswith("s_nop") else 1
+                i -= 1
+        found.extend((m, j + 1, w) for m, w in sorted(near.items()))
     return found
 
 
@@ -232,10 +267,37 @@ def test_scanner_flags_an_asm_write_of_an_mfma_accumulator_input():
 """.splitlines()
     assert len(asm_writes_after_mfma(lines)) == 1
     # far enough after the MFMA, or writing another register, it is fine
-    late = lines[:2] + ["    s_nop 7"] + lines[2:]
+    late = lines[:2] + ["    s_nop 7", "    s_nop 7", "    s_nop 1"] + lines[2:]
     assert asm_writes_after_mfma(late) == []
     other = [l.replace("v142,", "v150,") for l in lines]
     assert asm_writes_after_mfma(other) == []
+    # a later MFMA in between does not hide the earlier one
+    two = lines[:2] + ["    v_mfma_f32_16x16x32_bf16 v[20:23], v[2:5], v[6:9], v[20:23]"] + lines[2:]
+    assert len(asm_writes_after_mfma(two)) == 1
+
+
+def test_scanner_follows_branches_into_an_asm_write():
+    # the write sits at a loop head: the path from the back edge ends in an
+    # MFMA that reads v142 as its accumulator input
+    lines = """
+    s_branch .LBB0_2
+.LBB0_1:
+    v_mfma_f32_16x16x32_bf16 v[12:15], v[162:165], v[56:59], v[142:145]
+    s_cbranch_scc1 .LBB0_3
+.LBB0_2:
+    s_mov_b32 s4, 0
+    ;;#ASMSTART
+    v_dot2_f32_bf16 v142, v154, s23, v170
+    ;;#ASMEND
+    s_branch .LBB0_1
+.LBB0_3:
+    s_endpgm
+""".splitlines()
+    assert [f[2] for f in asm_writes_after_mfma(lines)] == [2]
+    # padded on the back-edge path it is fine
+    fixed = [l.replace("s_cbranch_scc1 .LBB0_3", "s_nop 7\n    s_nop 7\n    s_nop 7\n    s_cbranch_scc1 .LBB0_3")
+             for l in lines]
+    assert asm_writes_after_mfma("\n".join(fixed).splitlines()) == []
 
 
 def test_scanner_flags_a_read_that_skips_an_if_block():
