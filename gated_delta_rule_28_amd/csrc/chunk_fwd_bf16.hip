@@ -278,13 +278,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     bf16x8 Sh[KKD], Sl[KKD];
     auto split_state = [&]() {
 #pragma unroll
-      for (int kk = 0; kk < KKD; ++kk) {
-        bf16x4 h0, l0, h1, l1;
-        split4(Sacc[2 * kk], h0, l0);
-        split4(Sacc[2 * kk + 1], h1, l1);
-        Sh[kk] = cat(h0, h1);
-        Sl[kk] = cat(l0, l1);
-      }
+      for (int kk = 0; kk < KKD; ++kk) split8_keep(Sacc[2 * kk], Sacc[2 * kk + 1], Sh[kk], Sl[kk]);
     };
 
     // the fused output gate of this lane's O values, loaded one chunk ahead
@@ -597,45 +591,50 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // =======================================================================
   const int pw = wave - NSW;           // prep wave index 0..NPW-1
 
-  // A (X = K, strict lower, times b) or P (X = Q, lower incl.) tile (ti, tj)
-  // of X K^T with the decay, as the MFMA accumulator: lane (lr, lg) holds
-  // rows 16 ti + 4 lg + e of column 16 tj + lr
-  auto tile_acc = [&](const In &bf, bool isq, int ti, int tj) {
-    const char *X = reinterpret_cast<const char *>(isq ? &bf.Q[0][0] : &bf.K[0][0]);
+  // The A tile (K K^T: strict lower, times b) and the P tile (Q K^T: lower
+  // inclusive) at one position (ti, tj), with the decay: both take the key
+  // rows of block tj as their right operand (read once, and once in all on
+  // the diagonal, where A's left operand is the same rows) and the same
+  // factors e^{g_r - g_s} (formed once).  Lane (lr, lg) ends up with rows
+  // 16 ti + 4 lg + e of column 16 tj + lr.  g and b are the calling wave's
+  // copies; with the fused normalisation A takes the row factor 1/|k_r| and
+  // P 1/|q_r|, both the column factor 1/|k_s|.
+  auto tile_pair = [&](const In &bf, const float *g, const float *bw, int ti, int tj, f32x4 &va,
+                       f32x4 &vp) {
     const char *Kc = reinterpret_cast<const char *>(&bf.K[0][0]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const char *Qc = reinterpret_cast<const char *>(&bf.Q[0][0]);
+    f32x4 aa = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KKD; ++kk)
-      acc = mfma_bf16(ld8(reinterpret_cast<const bf16 *>(X + 16 * ti * QRB + kq_off[kk])),
-                      ld8(reinterpret_cast<const bf16 *>(Kc + 16 * tj * QRB + kq_off[kk])), acc);
-    return acc;
-  };
-  // the decay, the mask and (for A) the factor b of tile (ti, tj); g and b
-  // are the calling wave's copies; with the fused normalisation the row
-  // factor 1/|q_r| (P) or 1/|k_r| (A) and the column factor 1/|k_s|
-  auto decayed = [&](const In &bf, const float *g, const float *bw, f32x4 acc, int ti, int tj,
-                     bool isq) {
+    for (int kk = 0; kk < KKD; ++kk) {
+      const bf16x8 kt = ld8(reinterpret_cast<const bf16 *>(Kc + 16 * tj * QRB + kq_off[kk]));
+      if constexpr (ERASE) {
+        const bf16x8 ki =
+            (ti == tj) ? kt : ld8(reinterpret_cast<const bf16 *>(Kc + 16 * ti * QRB + kq_off[kk]));
+        aa = mfma_bf16(ki, kt, aa);
+      }
+      if constexpr (WANT_P)
+        ap = mfma_bf16(ld8(reinterpret_cast<const bf16 *>(Qc + 16 * ti * QRB + kq_off[kk])), kt, ap);
+    }
     const int sc = 16 * tj + lr;
     const int r0 = 16 * ti + 4 * lg;
     const float gs = g[sc];
     const f32x4 gr4 = *reinterpret_cast<const f32x4 *>(&g[r0]);
     // the norms are read whether or not they were formed and picked by a
-    // select: a branch here would sit between the tile's MFMA and the read
-    // of its result, which can hide the wait states that read needs
-    const f32x4 b0 = isq ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4 *>(&bw[r0]);
-    const f32x4 bn = b0 * *reinterpret_cast<const f32x4 *>(&bf.nrm[isq ? 0 : 1][r0]) * bf.nrm[1][sc];
+    // select: a branch here would sit between the tiles' MFMAs and the reads
+    // of their results, which can hide the wait states those reads need
+    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&bw[r0]);
+    const float nks = bf.nrm[1][sc];
+    const f32x4 nkr = *reinterpret_cast<const f32x4 *>(&bf.nrm[1][r0]);
+    const f32x4 nqr = *reinterpret_cast<const f32x4 *>(&bf.nrm[0][r0]);
     const bool l2 = (fuse & kFuseL2) != 0;
-    f32x4 b4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) b4[e] = l2 ? bn[e] : b0[e];
-    f32x4 val;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float dec = (GATE == kGateNone) ? 1.0f : __expf(gr4[e] - gs);
-      val[e] = isq ? ((sc <= r0 + e) ? b4[e] * acc[e] * dec : 0.0f)
-                   : ((sc < r0 + e) ? b4[e] * acc[e] * dec : 0.0f);
+      const float fa = l2 ? b0[e] * nkr[e] * nks : b0[e];
+      const float fp = l2 ? nqr[e] * nks : 1.0f;
+      va[e] = (sc < r0 + e) ? fa * aa[e] * dec : 0.0f;
+      vp[e] = (sc <= r0 + e) ? fp * ap[e] * dec : 0.0f;
     }
-    return val;
   };
   auto store_p = [&](typename SM::PT &pt, f32x4 val, int ti, int tj) {
     bf16x4 h4, l4;
@@ -796,9 +795,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // cumulative log decay itself (an inclusive scan over lanes 0..C-1;
   // tokens past the end carry log a = 0 and b = 0) into its own copy of g,
   // so no tile waits on another wave; wave 0 also writes e^g and
-  // e^{g_last - g} for the state waves.  Shares: wave 0 A10 and the second
-  // diagonal A block, wave 1 the first diagonal A block and P11, wave 2 P10
-  // and P00.
+  // e^{g_last - g} for the state waves.  Shares, by position: wave 0 the
+  // off-diagonal block (A10 and P10), wave 1 the second diagonal block,
+  // wave 2 the first (A and P of one position share their key operands and
+  // decay factors).
   auto tiles = [&](int j) {
     In &bf = *at_off(&sm.in[0], slot_off(j % NIN, (int)sizeof(In)));
     float *g = sm.gw[pw], *bw = sm.bw[pw];
@@ -833,24 +833,23 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     typename SM::PT &pt = *at_off(&sm.p[0], slot_off(j % NPR, (int)sizeof(typename SM::PT)));
     const int a10o = slot_off(j & 1, (int)sizeof(sm.A10h[0]));
     const int ao = slot_off(j & 1, (int)sizeof(sm.ATd[0]));
+    f32x4 va, vp;
     if (pw == 0) {
-      if constexpr (!ERASE) return;                  // no A without the erase term
-      const f32x4 val = decayed(bf, g, bw, tile_acc(bf, false, 1, 0), 1, 0, false);
-      bf16x4 h4, l4;
-      split4(val, h4, l4);
-      *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10h[0][0], a10o)[lr][4 * lg]) = h4;
-      *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10l[0][0], a10o)[lr][4 * lg]) = l4;
-      *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[1][lr][4 * lg]) =
-          -decayed(bf, g, bw, tile_acc(bf, false, 1, 1), 1, 1, false);
-    } else if (pw == 1) {
-      if constexpr (ERASE)
-        *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[0][lr][4 * lg]) =
-            -decayed(bf, g, bw, tile_acc(bf, false, 0, 0), 0, 0, false);
-      if constexpr (WANT_P)
-        store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 1), 1, 1, true), 1, 1);
-    } else if constexpr (WANT_P) {
-      store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 1, 0), 1, 0, true), 1, 0);
-      store_p(pt, decayed(bf, g, bw, tile_acc(bf, true, 0, 0), 0, 0, true), 0, 0);
+      tile_pair(bf, g, bw, 1, 0, va, vp);
+      if constexpr (ERASE) {
+        bf16x4 h4, l4;
+        split4(va, h4, l4);
+        *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10h[0][0], a10o)[lr][4 * lg]) = h4;
+        *reinterpret_cast<bf16x4 *>(&at_off(&sm.A10l[0][0], a10o)[lr][4 * lg]) = l4;
+      }
+      if constexpr (WANT_P) store_p(pt, vp, 1, 0);
+    } else {
+      // wave 1: block (1,1); wave 2: block (0,0)
+      const int b = (pw == 1) ? 1 : 0;
+      if (pw == 1) tile_pair(bf, g, bw, 1, 1, va, vp);
+      else tile_pair(bf, g, bw, 0, 0, va, vp);
+      if constexpr (ERASE) *reinterpret_cast<f32x4 *>(&(*at_off(&sm.ATd[0], ao))[b][lr][4 * lg]) = -va;
+      if constexpr (WANT_P) store_p(pt, vp, b, b);
     }
   };
 

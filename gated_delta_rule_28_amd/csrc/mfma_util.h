@@ -98,6 +98,55 @@ __device__ __forceinline__ void split2(float x0, float x1, unsigned &hi, unsigne
   lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
+// split4 of two tiles whose values stay live after the split (the state):
+// the same steps as split2, with x - hi from the three-operand packed dot
+// product, whose result register is not tied to its accumulator input (the
+// two-operand form that the builtin selects needs a copy of each x first).
+// Written as one block of inline assembly, which takes on the wait states
+// the compiler keeps for its own instructions on this target:
+//  - the block starts with 4 wait states: a VALU write of a register that an
+//    MFMA issued just before still reads as its accumulator input needs 3
+//    (the compiler's own code keeps 3 after a 16x16x32 bf16 MFMA);
+//  - a dot product's result may be read by another VALU instruction only 3
+//    wait states after it is written: the eight products come first, then
+//    the four conversions (each reads its inputs at least 3 later);
+//  - an MFMA may read a VALU result 2 wait states after it is written: the
+//    block ends with them.
+// The assembly scan of the kernels checks the first and the last rule on
+// every path.
+__device__ __forceinline__ void split8_keep(const f32x4 a, const f32x4 b, bf16x8 &hi, bf16x8 &lo) {
+  unsigned h[4];
+  h[0] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a[0], a[1]}, bf16x2));
+  h[1] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a[2], a[3]}, bf16x2));
+  h[2] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{b[0], b[1]}, bf16x2));
+  h[3] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{b[2], b[3]}, bf16x2));
+  unsigned m0 = 0x0000BF80u, m1 = 0xBF800000u;
+  asm("" : "+s"(m0), "+s"(m1));
+  float r[8];
+  unsigned l[4];
+  asm("s_nop 3\n\t"
+      "v_dot2_f32_bf16 %4, %12, %16, %18\n\t"
+      "v_dot2_f32_bf16 %5, %12, %17, %19\n\t"
+      "v_dot2_f32_bf16 %6, %13, %16, %20\n\t"
+      "v_dot2_f32_bf16 %7, %13, %17, %21\n\t"
+      "v_dot2_f32_bf16 %8, %14, %16, %22\n\t"
+      "v_dot2_f32_bf16 %9, %14, %17, %23\n\t"
+      "v_dot2_f32_bf16 %10, %15, %16, %24\n\t"
+      "v_dot2_f32_bf16 %11, %15, %17, %25\n\t"
+      "v_cvt_pk_bf16_f32 %0, %4, %5\n\t"
+      "v_cvt_pk_bf16_f32 %1, %6, %7\n\t"
+      "v_cvt_pk_bf16_f32 %2, %8, %9\n\t"
+      "v_cvt_pk_bf16_f32 %3, %10, %11\n\t"
+      "s_nop 1"
+      : "=&v"(l[0]), "=&v"(l[1]), "=&v"(l[2]), "=&v"(l[3]), "=&v"(r[0]), "=&v"(r[1]),
+        "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "s"(m0), "s"(m1), "v"(a[0]), "v"(a[1]),
+        "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+  typedef unsigned u32x4_ __attribute__((ext_vector_type(4)));
+  hi = __builtin_bit_cast(bf16x8, u32x4_{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4_{l[0], l[1], l[2], l[3]});
+}
+
 template <bool DOT = true>
 __device__ __forceinline__ void split4(const f32x4 x, bf16x4 &hi, bf16x4 &lo) {
   unsigned h01, l01, h23, l23;

@@ -12,8 +12,10 @@ compiles them to assembly and checks, along the shortest path in layout
 order, that every read of an MFMA result reached across a branch is at
 least 8 wait states after the MFMA.  It also checks that no inline-assembly
 instruction writes a register that an MFMA issued just before still reads as
-its accumulator input, over every path into the write: the compiler
-inserts the wait states for that only before its own instructions.
+its accumulator input, over every path into the write, and that no MFMA
+reads a register an inline-assembly instruction wrote just before: the
+compiler inserts the wait states for both only around its own
+instructions.
 
 A third check covers the DPP forms written as inline assembly (the
 v_fmac_f32_dpp row broadcasts of the diagonal triangular solve).  A DPP
@@ -120,7 +122,14 @@ def short_reads(lines, min_ws=MIN_WAIT_STATES):
     return found
 
 
-ACC_WAR_WAIT_STATES = 18   # more than the longest MFMA here (8 passes) reads its accumulator
+# A VALU write of a register that an in-flight 16x16x32 (or 16x16x16) bf16
+# MFMA reads as its accumulator input needs 3 wait states after the MFMA on
+# gfx950: the compiler's own code for these kernels keeps exactly 3 (an
+# s_nop 2 where nothing else fills them); the scan asks for 4.
+ACC_WAR_WAIT_STATES = 4
+# an MFMA may read a VALU result 2 wait states after it is written (the
+# compiler's own code keeps 2)
+VALU_MFMA_RAW_WAIT_STATES = 2
 
 
 def _branch_sources(lines):
@@ -190,6 +199,63 @@ def asm_writes_after_mfma(lines, min_ws=ACC_WAR_WAIT_STATES):
                     ws += int(t_.split()[1]) + 1 if t_.startswith("s_nop") else 1
                 i -= 1
         found.extend((m, j + 1, w) for m, w in sorted(near.items()))
+    return found
+
+
+def _labels(lines):
+    return {l.strip()[:-1]: i for i, l in enumerate(lines)
+            if l.strip().endswith(":") and not l.strip().startswith(";")}
+
+
+def mfma_reads_after_asm_write(lines, min_ws=VALU_MFMA_RAW_WAIT_STATES):
+    """(asm line, mfma line, wait states) where an MFMA reads a VGPR that an
+    inline-assembly instruction wrote fewer than min_ws wait states before,
+    on any path out of the write (fall-through and branch targets, walked
+    forwards until the register is written again)."""
+    found = []
+    labels = _labels(lines)
+    inside = False
+    for j, line in enumerate(lines):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if not inside or not s.startswith("v_"):
+            continue
+        parts = s.split(None, 1)
+        if len(parts) < 2:
+            continue
+        dst = _vregs(parts[1].split(",")[0])
+        stack, seen = [(j + 1, 0)], set()
+        while stack:
+            i, ws = stack.pop()
+            while i < len(lines) and ws < min_ws and (i, ws) not in seen:
+                seen.add((i, ws))
+                t_ = lines[i].strip()
+                if not t_ or t_.startswith((";", ".")) or t_.endswith(":"):
+                    i += 1
+                    continue
+                if t_.startswith("s_endpgm"):
+                    break
+                if t_.startswith("v_mfma"):
+                    ops = t_.split(None, 1)[1].split(",")
+                    if any(_vregs(o) & dst for o in ops[1:]):
+                        found.append((j + 1, i + 1, ws))
+                        break
+                if t_.startswith(("s_cbranch", "s_branch")):
+                    tgt = labels.get(t_.split()[1])
+                    if tgt is not None:
+                        stack.append((tgt + 1, ws + 1))
+                    if t_.startswith("s_branch"):
+                        break
+                elif t_.startswith("v_") and len(t_.split(None, 1)) == 2 and \
+                        _vregs(t_.split(None, 1)[1].split(",")[0]) >= dst:
+                    break       # written again
+                ws += int(t_.split()[1]) + 1 if t_.startswith("s_nop") else 1
+                i += 1
     return found
 
 
@@ -267,13 +333,28 @@ def test_scanner_flags_an_asm_write_of_an_mfma_accumulator_input():
 """.splitlines()
     assert len(asm_writes_after_mfma(lines)) == 1
     # far enough after the MFMA, or writing another register, it is fine
-    late = lines[:2] + ["    s_nop 7", "    s_nop 7", "    s_nop 1"] + lines[2:]
+    late = lines[:2] + ["    s_nop 3"] + lines[2:]
     assert asm_writes_after_mfma(late) == []
     other = [l.replace("v142,", "v150,") for l in lines]
     assert asm_writes_after_mfma(other) == []
     # a later MFMA in between does not hide the earlier one
     two = lines[:2] + ["    v_mfma_f32_16x16x32_bf16 v[20:23], v[2:5], v[6:9], v[20:23]"] + lines[2:]
     assert len(asm_writes_after_mfma(two)) == 1
+
+
+def test_scanner_flags_an_mfma_read_right_after_an_asm_write():
+    lines = """
+    ;;#ASMSTART
+    v_cvt_pk_bf16_f32 v40, v41, v42
+    ;;#ASMEND
+    v_mfma_f32_16x16x32_bf16 v[12:15], v[162:165], v[40:43], v[12:15]
+""".splitlines()
+    assert [f[2] for f in mfma_reads_after_asm_write(lines)] == [0]
+    padded = lines[:4] + ["    s_nop 1"] + lines[4:]
+    assert mfma_reads_after_asm_write(padded) == []
+    # a write of another register in between is not a read of v40
+    other = [l.replace("v[40:43]", "v[44:47]") for l in lines]
+    assert mfma_reads_after_asm_write(other) == []
 
 
 def test_scanner_follows_branches_into_an_asm_write():
@@ -337,6 +418,8 @@ def test_mfma_results_are_not_read_early_across_branches():
     assert all(not p for p in problems.values()), problems
     asm_problems = {src: asm_writes_after_mfma(lines)[:5] for src, lines in asm.items()}
     assert all(not p for p in asm_problems.values()), asm_problems
+    raw_problems = {src: mfma_reads_after_asm_write(lines)[:5] for src, lines in asm.items()}
+    assert all(not p for p in raw_problems.values()), raw_problems
     dpp_problems = {src: dpp_reads_after_valu_write(lines)[:5] for src, lines in asm.items()}
     assert all(not p for p in dpp_problems.values()), dpp_problems
     # the scan saw the solve's inline DPP instructions (it is not vacuous)
