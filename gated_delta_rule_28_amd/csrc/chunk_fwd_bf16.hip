@@ -132,6 +132,8 @@ struct __align__(16) PipeSmem {
     float fq[C], fk[C], bt[C];         // factors of Q S and K S (e^g, times 1/|q|, 1/|k|
                                        // when fused), b (after the fused sigmoid)
     float nrm[2][C];                   // fused L2 normalisation: 1/|q|, 1/|k| per token
+    float zsc[4];                      // carried-scale form: [0] the state's factor before
+                                       // the update, [1] the scale after it
   };
   struct __align__(16) PT {
     bf16 Ph[C][LDC], Pl[C][LDC];       // P^T: [s][r] = P[r][s]; rows 16..31 x cols 0..15 stay zero
@@ -170,6 +172,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(MODE == kModeFwd || (ERASE && !FUSED && GATE != kGateChannel),
                 "the backward passes run the erasing, unfused scalar-gate form");
   constexpr bool WANT_O = MODE == kModeFwd;      // outputs (Q S, P U, o)
+  // Carried-scale form of the state (forward, scalar decay): the state
+  // waves hold Z with S = Z_scale * Z, so that the decay of a chunk does not
+  // multiply every state element: the scale goes into the row factors of
+  // K S and Q S (times Z_scale) and of the update (divided by the scale
+  // after it), and Z is multiplied only when the scale would drop below
+  // 2^-40 (then by the accumulated scale, which returns to 1).  The scale
+  // is kept by the prep wave that forms the factors, chunk by chunk.
+  constexpr bool LAZY = MODE == kModeFwd && GATE == kGateScalar;
   constexpr bool WANT_P = MODE != kModeRec;      // the P tiles and q
   __shared__ SM sm;
   // calls without a fused prologue or epilogue compile without their code
@@ -548,8 +558,19 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           acc = mfma_bf16(Ul, ph, acc);
           oacc[rb] = acc;
         }
-        const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
         const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
+        float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
+        if constexpr (LAZY) {
+          // the state's factor before this update: 1 unless the scale is
+          // folded back in (a wave-uniform value and branch)
+          glast = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                __builtin_bit_cast(int, bs.zsc[0])));
+          if (glast != 1.0f) {
+#pragma unroll
+            for (int mb = 0; mb < DK / 16; ++mb) Sacc[mb] = Sacc[mb] * glast;
+          }
+          glast = 1.0f;
+        }
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb) {
           const char *p = Kb + kt_off[mb >> 1] + 8 * (mb & 1);
@@ -577,11 +598,15 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
 
     if (final_state) {
+      // the carried scale after the last chunk (1 without chunks)
+      float zf = 1.0f;
+      if (LAZY && nchunks > 0)
+        zf = at_off(&sm.in[0], slot_off((nchunks - 1) % NIN, (int)sizeof(In)))->zsc[1];
       float *SF = final_state + (long)chain * DK * DV;
 #pragma unroll
       for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) SF[(long)srow(mb, e) * DV + col0 + lr] = Sacc[mb][e];
+        for (int e = 0; e < 4; ++e) SF[(long)srow(mb, e) * DV + col0 + lr] = Sacc[mb][e] * zf;
     }
     return;
   }
@@ -741,6 +766,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int N0 = NVI + 1 + (SCALAR ? 1 : 0);   // DMA instructions per chunk, wave 0
   constexpr int N12 = NQI;                         // waves 1 and 2
   unsigned voff[NI];
+  float zscale = 1.0f;                 // carried scale of the state entering the next chunk (wave 0)
   if (pw == 0) {
     constexpr int BPR = VRB / 16, RPI = 1024 / VRB;
 #pragma unroll
@@ -816,6 +842,20 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       // e^{g_last - g} (times 1/|k|) for the update, b
       const float glast = __builtin_bit_cast(
           float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), C - 1));
+      // carried scale: z = scale entering the chunk; the state factor before
+      // the update and the scale after it (uniform)
+      float z = 1.0f, zinv = 1.0f;
+      if constexpr (LAZY) {
+        const float zn = zscale * __expf(glast);
+        const bool fold = zn < 0x1p-40f;
+        z = zscale;
+        zscale = fold ? 1.0f : zn;
+        zinv = 1.0f / zscale;
+        if (lane == 0) {
+          bf.zsc[0] = fold ? zn : 1.0f;
+          bf.zsc[1] = zscale;
+        }
+      }
       if (lane < C) {
         const float gm = (GATE == kGateNone) ? 1.0f : __expf(sc);
         const float e = (GATE == kGateNone) ? 1.0f : __expf(glast - sc);
@@ -823,9 +863,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const float nq = bf.nrm[0][lane], nk = bf.nrm[1][lane];
         const float rq = l2 ? nq : 1.0f, rk = l2 ? nk : 1.0f;
         bf.gam[lane] = gm;
-        bf.fq[lane] = gm * rq;
-        bf.fk[lane] = gm * rk;
-        bf.ec[lane] = e * rk;
+        bf.fq[lane] = gm * rq * z;
+        bf.fk[lane] = gm * rk * z;
+        bf.ec[lane] = e * rk * zinv;
         bf.bt[lane] = bl;
       }
     }
