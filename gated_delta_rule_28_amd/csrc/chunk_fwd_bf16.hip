@@ -300,18 +300,16 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // The loads are unconditional: without a gate, or past the last chunk,
     // the descriptor is empty and they read zeros without touching memory.
     f32x4 og[2] = {};
-    unsigned og_next[2][4] = {};
+    u32x2 og_next[2] = {};               // four bf16 gate values per row block
     auto load_gate = [&](int c) {
       const bool valid = gated && c < nchunks;
       const int n = valid ? min(C, T - c * C) : 1;
       const long orow = valid ? (tok0 + (long)c * C * H) * DV : 0;
       const rsrc_t rg = make_rsrc32(out_gate + orow,
                                     valid ? 2u * ((unsigned)(n - 1) * H * DV + DV) : 0u);
+      // the lane's four adjacent values of a row: one 8-byte load
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          og_next[rb][e] = buf_ld_u16(rg, 2u * oel[rb][e]);
+      for (int rb = 0; rb < 2; ++rb) og_next[rb] = buf_ld_b64(rg, 2u * oel[rb][0]);
     };
 
     for (int it = 0; it < nchunks + 1; ++it) {
@@ -425,7 +423,9 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            og[rb][e] = gated ? silu_gate(1.0f, bf16_bits_to_f32(og_next[rb][e])) : 1.0f;
+            og[rb][e] = gated ? silu_gate(1.0f, bf16_bits_to_f32(
+                                    e & 1 ? og_next[rb][e >> 1] >> 16 : og_next[rb][e >> 1] & 0xffffu))
+                              : 1.0f;
         load_gate(it);
       }
       // ---- K S, Q S, R = V - diag(gam) K S, U = T' R ----

@@ -191,6 +191,11 @@ __device__ __forceinline__ rsrc_t make_rsrc32(const void *base, unsigned bytes) 
 __device__ __forceinline__ unsigned buf_ld_u16(rsrc_t r, unsigned off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, __builtin_bit_cast(int, off), 0, 0);
 }
+// four adjacent bf16 values (8 bytes) as two dwords
+__device__ __forceinline__ u32x2 buf_ld_b64(rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                       r, __builtin_bit_cast(int, off), 0, 0));
+}
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned u) {
   return __builtin_bit_cast(float, u << 16);
 }
