@@ -649,6 +649,18 @@ def run_counter_targets(torch, gdr, W, reps=3):
     print(f"counters: bf16 GEMM {GEMM_N}^3 x{reps}", flush=True)
 
 
+# The template instance each counter summary covers: the launch the bench
+# line times (the backward's passes are instances of the same scalar-gate
+# kernel template, with their own traffic, so the name alone is not enough).
+# Mangled template arguments: <Dk, Dv slice, output type, gate, erase, fused,
+# mode> and <Dk, Dv slice, output type, erase, fused>.
+COUNTED_INSTANCE = {
+    "chunk_fwd_bf16_kernel": "chunk_fwd_bf16_kernelILi128ELi64EfLi1ELb1ELb0ELi0E",
+    "chunk_fwd_kda_kernel": "chunk_fwd_kda_kernelILi128ELi32EfLb1ELb0E",
+    "recurrent_step_kernel": "recurrent_step_kernel",
+}
+
+
 def _pmc_means(d, counter):
     """Mean per dispatch of `counter` (summed over its dimensions), by kernel."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -689,8 +701,8 @@ def summarize_pmc(fetch_dir, write_dir, command, out_dir=PROFILES):
                 chunk_alg_bytes(W.by_name("kda_bf16_b2h32t8192"))),
                ("recurrent_step_kernel", W.DECODE.name, decode_alg_bytes(W.DECODE))]
     for kern, wname, alg in targets:
-        kf, nf = mean_of(fetch, kern)
-        kw, nw = mean_of(write, kern)
+        kf, nf = mean_of(fetch, COUNTED_INSTANCE[kern])
+        kw, nw = mean_of(write, COUNTED_INSTANCE[kern])
         if kf is None or kw is None:
             print(f"{kern}: no dispatches in the counter runs", file=sys.stderr)
             continue
@@ -750,10 +762,10 @@ def summarize_mfma(ops_dir, util_dir, command, out_dir=PROFILES):
                 chunk_alg_flops(W.HEADLINE, KERNEL_CHUNK["scalar"])),
                ("chunk_fwd_kda_kernel", kda.name, chunk_alg_flops(kda, KERNEL_CHUNK["channel"]))]
     for kern, wname, alg in targets:
-        m, nm = mean_of(mops, kern)
-        u, nu = mean_of(util, kern)
-        ni, _ = mean_of(insts, kern)
-        nb, _ = mean_of(busy, kern)
+        m, nm = mean_of(mops, COUNTED_INSTANCE[kern])
+        u, nu = mean_of(util, COUNTED_INSTANCE[kern])
+        ni, _ = mean_of(insts, COUNTED_INSTANCE[kern])
+        nb, _ = mean_of(busy, COUNTED_INSTANCE[kern])
         if m is None or u is None:
             print(f"{kern}: no dispatches in the counter runs", file=sys.stderr)
             continue

@@ -53,14 +53,22 @@ def _write_csv(d, counter, rows):
                              "Counter_Name": counter, "Counter_Value": val * part})
 
 
+# kernel names as rocprofv3 reports them (mangled): the timed forward launch,
+# and a pass of the backward, an instance of the same template
+FWD = ("_ZN3gdr12_GLOBAL__N_121chunk_fwd_bf16_kernelILi128ELi64EfLi1ELb1ELb0ELi0EEEvPKDF16bS3_"
+       "S3_PKfS5_S5_PT1_PfiiiiS3_S8_S8_S8_")
+BWD_PASS = FWD.replace("ELi0EEEv", "ELi1EEEv")
+
+
 def test_counter_summary_scales_by_the_copy(tmp_path):
     copy_kib = bench.COPY_BYTES / 1024.0
-    kern = "void gdr::(anonymous namespace)::chunk_fwd_bf16_kernel<128, 64, float, 1>(...)"
-    # the counters read half of the true bytes: the copy calibrates that away
+    kern = FWD
+    # the counters read half of the true bytes: the copy calibrates that away;
+    # the backward's pass (same template, other traffic) is not counted
     _write_csv(tmp_path / "f", "FETCH_SIZE",
-               [("at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>", copy_kib / 2)] * 3 + [(kern, 1000.0), (kern, 1200.0)])
+               [("at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>", copy_kib / 2)] * 3 + [(kern, 1000.0), (kern, 1200.0), (BWD_PASS, 9.0e6)])
     _write_csv(tmp_path / "w", "WRITE_SIZE",
-               [("at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>", copy_kib / 4)] * 3 + [(kern, 500.0), (kern, 500.0)])
+               [("at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>", copy_kib / 4)] * 3 + [(kern, 500.0), (kern, 500.0), (BWD_PASS, 9.0e6)])
     out = tmp_path / "prof"
     assert bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "cmd {counter} {dir}",
                                out_dir=str(out)) == 0
@@ -110,12 +118,12 @@ def test_cpu_baseline_splits_chains_and_checks_parity():
 
 
 def test_mfma_summary(tmp_path):
-    kern = "void gdr::(anonymous namespace)::chunk_fwd_bf16_kernel<128, 64, float, 1>(...)"
+    kern = FWD
     gemm = "Cijk_Alik_Bljk_BBS_BH_MT256x256x64"
     gemm_mops = 2.0 * bench.GEMM_N ** 3 / 512.0
     _write_csv(tmp_path / "o", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-               [(gemm, gemm_mops)] * 2 + [(kern, 1.0e8), (kern, 1.0e8)])
-    _write_csv(tmp_path / "u", "MfmaUtil", [(gemm, 80.0), (kern, 25.0), (kern, 27.0)])
+               [(gemm, gemm_mops)] * 2 + [(kern, 1.0e8), (kern, 1.0e8), (BWD_PASS, 5.0e9)])
+    _write_csv(tmp_path / "u", "MfmaUtil", [(gemm, 80.0), (kern, 25.0), (kern, 27.0), (BWD_PASS, 90.0)])
     out = tmp_path / "prof"
     assert bench.summarize_mfma(str(tmp_path / "o"), str(tmp_path / "u"),
                                 "cmd {counter} {dir}", out_dir=str(out)) == 0
