@@ -50,6 +50,7 @@
 //   state:  chunk i-2
 // Raw inputs live four iterations (DMA to derivation), derived operands
 // three, v three, T' and P two.
+#include <cstddef>
 #include <type_traits>
 
 #include "common.h"
@@ -64,6 +65,10 @@ constexpr int KC = 16;               // tokens per chunk
 template <int DVS>
 constexpr int kda_npw() { return DVS == 32 ? 6 : 4; }
 constexpr float kMaxSpan = 64.0f;    // per-channel in-chunk log-decay bound of the factored form
+// The in-chunk log decays are kept in base-2 units (G = log2 of the decay
+// products), so that every factor e^{...} is one hardware exp2.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaxSpan2 = kMaxSpan * kLog2e;   // the bound in those units
 constexpr int NRAW = 4;              // raw slots: chunk j from iteration j-3 to j
 constexpr int NDER = 3;              // derived slots: chunk j from iteration j to j+2
 constexpr int NVB = 3;               // v slots: chunk j from iteration j to j+2
@@ -73,7 +78,7 @@ struct __align__(16) KdaSmem {
   static constexpr int LDX = 20;          // fp32 stride of the 16x16 exact-path and solve tiles
   struct __align__(16) Raw {              // one chunk as the DMA leaves it
     bf16 Q[KC][DK], K[KC][DK];            // natural channel order
-    float G[KC][DK];                      // log a, summed in place into G
+    float G[KC][DK];                      // log a, summed in place into G (base 2)
     float beta[64];                       // b of the 64 tokens from the chunk start (16 used)
     float nrm[2][KC];                     // fused L2 normalisation: 1/|q|, 1/|k| per token
     int flag[4];                          // [0]: some channel's in-chunk log decay < -kMaxSpan
@@ -83,6 +88,8 @@ struct __align__(16) KdaSmem {
     bf16 Qh[KC][DK], Ql[KC][DK];          // Q^ = Q o e^G
     bf16 Rh[KC][DK], Rl[KC][DK];          // R^ = K o e^{-G} (exact path: K o e^{g_last - G})
     float egl[DK];                        // e^{g_last}
+    float egp[DK];                        // the factor after the update: e^{g_last}, or 1 on
+                                          // the exact path (which applies it first)
     float beta[KC];
     int flag[4];
   };
@@ -215,6 +222,29 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const bool gated = out_gate != nullptr;
     f32x4 og = {};
     unsigned og_next[4] = {};
+    // this lane's K^ and Q^ fragments (hi, lo) of the chunk the next
+    // iteration multiplies, read one iteration ahead: a chunk's derived slot
+    // is complete from the iteration after its derivation, and the reads
+    // would otherwise start every chunk's serial products with an LDS round
+    // trip.  Before the first chunk (and past the last) they read a slot
+    // that is not used, which is harmless.
+    bf16x8 fkh[KKD], fkl[KKD], fqh[KKD], fql[KKD];
+    auto load_kq = [&](int c) {
+      const typename SM::Der &d = *at_off(&sm.der[0], slot_off(c % NDER, (int)sizeof(typename SM::Der)));
+      const char *Kh = reinterpret_cast<const char *>(&d.Kh[0][0]);
+      const char *Kl = reinterpret_cast<const char *>(&d.Kl[0][0]);
+      const char *Qh = reinterpret_cast<const char *>(&d.Qh[0][0]);
+      const char *Ql = reinterpret_cast<const char *>(&d.Ql[0][0]);
+#pragma unroll
+      for (int kk = 0; kk < KKD; ++kk) {
+        fqh[kk] = ld8(reinterpret_cast<const bf16 *>(Qh + kq_off[kk]));
+        fql[kk] = ld8(reinterpret_cast<const bf16 *>(Ql + kq_off[kk]));
+        if constexpr (ERASE) {
+          fkh[kk] = ld8(reinterpret_cast<const bf16 *>(Kh + kq_off[kk]));
+          fkl[kk] = ld8(reinterpret_cast<const bf16 *>(Kl + kq_off[kk]));
+        }
+      }
+    };
     for (int it = 0; it < nchunks + 2; ++it) {
       const int s = it - 2;
       if constexpr (FUSED) {
@@ -236,17 +266,11 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
         // ---- K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
-        const char *Kh = reinterpret_cast<const char *>(&d.Kh[0][0]);
-        const char *Kl = reinterpret_cast<const char *>(&d.Kl[0][0]);
-        const char *Qh = reinterpret_cast<const char *>(&d.Qh[0][0]);
-        const char *Ql = reinterpret_cast<const char *>(&d.Ql[0][0]);
 #pragma unroll
         for (int kk = 0; kk < KKD; ++kk) {
-          const bf16x8 qh = ld8(reinterpret_cast<const bf16 *>(Qh + kq_off[kk]));
-          const bf16x8 ql = ld8(reinterpret_cast<const bf16 *>(Ql + kq_off[kk]));
+          const bf16x8 qh = fqh[kk], ql = fql[kk];
           if constexpr (ERASE) {
-            const bf16x8 kh = ld8(reinterpret_cast<const bf16 *>(Kh + kq_off[kk]));
-            const bf16x8 kl = ld8(reinterpret_cast<const bf16 *>(Kl + kq_off[kk]));
+            const bf16x8 kh = fkh[kk], kl = fkl[kk];
             a1 = mfma_bf16(kh, Sh[kk], a1);
             a2 = mfma_bf16(qh, Sh[kk], a2);
             a1 = mfma_bf16(kh, Sl[kk], a1);
@@ -304,22 +328,32 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
 
         // ---- S <- Diag(e^{g_last}) (S + R^T U) (exact path: factor first) ----
+        // The exact path's factor is a wave-uniform branch taken only by
+        // such chunks; the factor after the update is 1 on that path (egp),
+        // so the common path pays one multiply per element.  Sacc is last
+        // written by a VALU multiply on every path, so no MFMA result is read
+        // across the branch.
+        if (exact) {
+#pragma unroll
+          for (int mb = 0; mb < DK / 16; ++mb)
+            Sacc[mb] = Sacc[mb] * *reinterpret_cast<const f32x4 *>(&d.egl[srow(mb, 0)]);
+        }
         const bf16x8 b1 = cat(uh4, uh4), b2 = cat(ul4, zero4);
         const char *Rh = reinterpret_cast<const char *>(&d.Rh[0][0]);
         const char *Rl = reinterpret_cast<const char *>(&d.Rl[0][0]);
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb) {
-          const f32x4 eg4 = *reinterpret_cast<const f32x4 *>(&d.egl[srow(mb, 0)]);
+          const f32x4 ep4 = *reinterpret_cast<const f32x4 *>(&d.egp[srow(mb, 0)]);
           const int off = kt_off[mb >> 1] + 8 * (mb & 1);
           const bf16x8 a = cat(ld_tr4(reinterpret_cast<const bf16 *>(Rh + off)),
                                ld_tr4(reinterpret_cast<const bf16 *>(Rl + off)));
-          f32x4 sa = exact ? Sacc[mb] * eg4 : Sacc[mb];
-          sa = mfma_bf16(a, b1, sa);
+          f32x4 sa = mfma_bf16(a, b1, Sacc[mb]);
           sa = mfma_bf16(a, b2, sa);
-          Sacc[mb] = exact ? sa : sa * eg4;
+          Sacc[mb] = sa * ep4;
         }
         split_state();
       }
+      load_kq(s + 1 < 0 ? 0 : s + 1);
       __syncthreads();
     }
 
@@ -483,9 +517,9 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int i = 0; i < NVI; ++i) lds_dma16(rv, voff[i], lv + 1024 * i);
   };
 
-  // in-chunk cumulative log decay of chunk j, in place (wave 1): lane = a
-  // channel pair; padded tokens read log a = 0; flags a chunk whose
-  // factored operands could leave the floating-point range
+  // in-chunk cumulative log decay of chunk j in base 2, in place (wave 1):
+  // lane = a channel pair; padded tokens read log a = 0; flags a chunk
+  // whose factored operands could leave the floating-point range
   auto gsum = [&](int j) {
     typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
     constexpr int NCP = DK / 2;
@@ -493,10 +527,11 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     f32x2 acc = {0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < KC; ++r) {
-      acc += *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      const f32x2 x = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+      acc = f32x2{fmaf(x[0], kLog2e, acc[0]), fmaf(x[1], kLog2e, acc[1])};
       if (lane < NCP) *reinterpret_cast<f32x2 *>(&rw.G[r][c0]) = acc;
     }
-    const unsigned long long bad = __ballot(acc[0] < -kMaxSpan || acc[1] < -kMaxSpan);
+    const unsigned long long bad = __ballot(acc[0] < -kMaxSpan2 || acc[1] < -kMaxSpan2);
     if (lane == 0) rw.flag[0] = bad != 0ull;
   };
   // with a fused decay transform (two transcendentals per element) the
@@ -525,7 +560,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const int r = rg * RPG + i;
       const f32x2 x = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
       // padded tokens keep log a = 0
-      run += (r < n) ? f32x2{decay_transform(x[0], gla), decay_transform(x[1], gla)}
+      run += (r < n) ? f32x2{decay_transform(x[0], gla) * kLog2e, decay_transform(x[1], gla) * kLog2e}
                      : f32x2{0.f, 0.f};
       part[i] = run;
     }
@@ -553,7 +588,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     for (int i = 0; i < RPG; ++i)
       *reinterpret_cast<f32x2 *>(&rw.G[rg * RPG + i][c0]) = part[i] + excl;
     const unsigned long long bad =
-        __ballot(rg == RGN - 1 && (incl[0] < -kMaxSpan || incl[1] < -kMaxSpan));
+        __ballot(rg == RGN - 1 && (incl[0] < -kMaxSpan2 || incl[1] < -kMaxSpan2));
     if (lane == 0) rw.flag[gi] = bad != 0ull;
   };
   const bool shared_gsum = FUSED && (fuse & (kFuseSoftplus | kFuseGla)) != 0;
@@ -630,7 +665,13 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
   auto derive = [&](int j) {
     const typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
-    typename SM::Der &d = *at_off(&sm.der[0], slot_off(j % NDER, (int)sizeof(typename SM::Der)));
+    // the derived slot's LDS address, array base included, as an opaque
+    // wave-uniform value: the row loop's six stores then differ by constant
+    // offsets below 64 KiB, which the store instructions carry (with the
+    // base left constant the offsets exceed that field)
+    int dso = __builtin_amdgcn_readfirstlane((j % NDER) * (int)sizeof(typename SM::Der) + (int)offsetof(SM, der));
+    asm volatile("" : "+s"(dso));   // emits nothing; hides the constant part
+    typename SM::Der &d = *reinterpret_cast<typename SM::Der *>(reinterpret_cast<char *>(&sm) + dso);
     int fl = rw.flag[0];
     if (shared_gsum) {
 #pragma unroll
@@ -640,14 +681,17 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int cp = lane % NCP, c0 = 2 * cp;
     const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
     if (pw == 0) {
-      if (lane < NCP) *reinterpret_cast<f32x2 *>(&d.egl[c0]) = f32x2{__expf(gl[0]), __expf(gl[1])};
+      if (lane < NCP) {
+        const f32x2 eg = {__builtin_amdgcn_exp2f(gl[0]), __builtin_amdgcn_exp2f(gl[1])};
+        *reinterpret_cast<f32x2 *>(&d.egl[c0]) = eg;
+        *reinterpret_cast<f32x2 *>(&d.egp[c0]) = exact ? f32x2{1.0f, 1.0f} : eg;
+      }
       if (lane < KC) d.beta[lane] = (lane < min(KC, T - j * KC)) ? fused_beta(rw.beta[lane], fuse) : 0.0f;
       if (lane == 0) d.flag[0] = exact;
     }
     const int rb0 = row_bound(dw), rb1 = row_bound(dw + 1);
     const bool l2f = (fuse & kFuseL2) != 0;
     const int coff = 2 * (c0 & 7);                 // byte offset inside the 16-byte block
-    const f32x2 sh = exact ? gl : f32x2{0.f, 0.f};   // R^ = K o e^{sh - G}
     auto put = [&](bf16 (*hi)[DK], bf16 (*lo)[DK], int r, float x0, float x1) {
       unsigned h, l;
       split2<false>(x0, x1, h, l);
@@ -655,24 +699,31 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       *reinterpret_cast<unsigned *>(reinterpret_cast<char *>(&hi[0][0]) + off) = h;
       *reinterpret_cast<unsigned *>(reinterpret_cast<char *>(&lo[0][0]) + off) = l;
     };
-    for (int w = rb0; w < rb1; ++w) {
-      const int r = w * TPR + lane / NCP;
-      const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
-      const unsigned kb = *reinterpret_cast<const unsigned *>(&rw.K[r][c0]);
-      const unsigned qb = *reinterpret_cast<const unsigned *>(&rw.Q[r][c0]);
-      const float k0 = __builtin_bit_cast(float, kb << 16), k1 = __builtin_bit_cast(float, kb & 0xffff0000u);
-      const float q0 = __builtin_bit_cast(float, qb << 16), q1 = __builtin_bit_cast(float, qb & 0xffff0000u);
-      // the fused norms are read whether or not they were formed and picked
-      // by a select (no branch in the row loop)
-      const float nq = rw.nrm[0][r], nk = rw.nrm[1][r];
-      const float rq = l2f ? nq : 1.0f, rk = l2f ? nk : 1.0f;
-      const float eq0 = __expf(g[0]) * rq, eq1 = __expf(g[1]) * rq;
-      const float e0 = __expf(g[0]) * rk, e1 = __expf(g[1]) * rk;
-      const float f0 = __expf(sh[0] - g[0]) * rk, f1 = __expf(sh[1] - g[1]) * rk;
-      if constexpr (ERASE) put(d.Kh, d.Kl, r, k0 * e0, k1 * e1);   // K^ feeds only K^ S and A
-      put(d.Qh, d.Ql, r, q0 * eq0, q1 * eq1);
-      put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);
-    }
+    // R^ = K o e^{-G}, on the exact path K o e^{g_last - G}: one row loop
+    // per path (exact is wave-uniform), so the common one has no shift
+    auto rows = [&](auto exact_path) {
+      constexpr bool EX = decltype(exact_path)::value;
+      for (int w = rb0; w < rb1; ++w) {
+        const int r = w * TPR + lane / NCP;
+        const f32x2 g = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
+        const unsigned kb = *reinterpret_cast<const unsigned *>(&rw.K[r][c0]);
+        const unsigned qb = *reinterpret_cast<const unsigned *>(&rw.Q[r][c0]);
+        const float k0 = __builtin_bit_cast(float, kb << 16), k1 = __builtin_bit_cast(float, kb & 0xffff0000u);
+        const float q0 = __builtin_bit_cast(float, qb << 16), q1 = __builtin_bit_cast(float, qb & 0xffff0000u);
+        // the fused norms are read whether or not they were formed and
+        // picked by a select (no branch in the row loop)
+        const float nq = rw.nrm[0][r], nk = rw.nrm[1][r];
+        const float rq = l2f ? nq : 1.0f, rk = l2f ? nk : 1.0f;
+        const float x0 = __builtin_amdgcn_exp2f(g[0]), x1 = __builtin_amdgcn_exp2f(g[1]);
+        const float f0 = __builtin_amdgcn_exp2f(EX ? gl[0] - g[0] : -g[0]) * rk;
+        const float f1 = __builtin_amdgcn_exp2f(EX ? gl[1] - g[1] : -g[1]) * rk;
+        if constexpr (ERASE) put(d.Kh, d.Kl, r, k0 * (x0 * rk), k1 * (x1 * rk));   // K^ feeds only K^ S and A
+        put(d.Qh, d.Ql, r, q0 * (x0 * rq), q1 * (x1 * rq));
+        put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);
+      }
+    };
+    if (exact) rows(std::true_type{});
+    else rows(std::false_type{});
     if (exact) {
       // exact Gram and scores: every decay formed directly; entry (r, s)
       // of both tiles per item, 256 items over the deriving waves
@@ -681,7 +732,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         float sa = 0.0f, sp = 0.0f;
         if (s <= r) {
           for (int c = 0; c < DK; ++c) {
-            const float ks = (float)rw.K[s][c] * __expf(rw.G[r][c] - rw.G[s][c]);
+            const float ks = (float)rw.K[s][c] * __builtin_amdgcn_exp2f(rw.G[r][c] - rw.G[s][c]);
             sa += (float)rw.K[r][c] * ks;
             sp += (float)rw.Q[r][c] * ks;
           }
