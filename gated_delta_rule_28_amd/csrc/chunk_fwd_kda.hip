@@ -553,15 +553,19 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int c0 = 2 * (gi * PPW + p);
     const int n = min(KC, T - j * KC);
     const bool gla = (fuse & kFuseGla) != 0;   // a transform is on whenever the sums are shared
+    // every row's load first (one LDS wait), then the transform of every
+    // row, masked by a factor: padded tokens keep log a = 0 (their rows
+    // hold the DMA's zeros, whose transform is finite), and no row sits in
+    // a branch of its own around its load
+    f32x2 x[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) x[i] = *reinterpret_cast<const f32x2 *>(&rw.G[rg * RPG + i][c0]);
     f32x2 part[RPG];
     f32x2 run = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-      const int r = rg * RPG + i;
-      const f32x2 x = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
-      // padded tokens keep log a = 0
-      run += (r < n) ? f32x2{decay_transform(x[0], gla) * kLog2e, decay_transform(x[1], gla) * kLog2e}
-                     : f32x2{0.f, 0.f};
+      const float keep = (rg * RPG + i < n) ? 1.0f : 0.0f;
+      run += f32x2{decay_transform2(x[i][0], gla), decay_transform2(x[i][1], gla)} * keep;
       part[i] = run;
     }
     f32x2 incl = run;

@@ -32,23 +32,33 @@ constexpr float kL2Eps = 1e-6f;   // q, k <- x / sqrt(sum x^2 + eps)
 __device__ __forceinline__ float sigmoid_f(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
-// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}), without
-// overflow for large |x| (the log's argument lies in (1, 2])
-__device__ __forceinline__ float softplus_f(float x) {
-  return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x)));
+// softplus(x) log2(e) = max(x, 0) log2(e) + log2(1 + 2^{-|x| log2(e)}):
+// log(1 + e^x) without overflow for large |x|, in base 2, where each step
+// is one hardware instruction (exp2; log2 of an argument in (1, 2], so no
+// denormal scaling).  The natural-log library call costs about twelve
+// instructions per value, which made the per-channel decay transform the
+// slowest stage of the fused chunk kernel.
+__device__ __forceinline__ float softplus2_f(float x) {
+  const float l = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f));
+  return fmaf(fmaxf(x, 0.0f), 1.4426950408889634f, l);
 }
+__device__ __forceinline__ float softplus_f(float x) { return softplus2_f(x) * 0.6931471805599453f; }
 // b from the beta input
 __device__ __forceinline__ float fused_beta(float b, int fuse) {
   return (fuse & kFuseBetaSigmoid) ? sigmoid_f(b) : b;
 }
-// log a from the log_alpha input: -softplus(x), or GLA's sigmoid(x)^{1/16}
-// log a from x when a decay transform is on (gla: GLA's gate, else the
+// log2 a from x when a decay transform is on (gla: GLA's gate, else the
 // softplus decay); one softplus either way: log sigmoid(x)^{1/16} =
 // -softplus(-x) / 16
-__device__ __forceinline__ float decay_transform(float x, bool gla) {
-  const float sp = softplus_f(gla ? -x : x);
-  return gla ? sp * (-1.0f / 16.0f) : -sp;
+__device__ __forceinline__ float decay_transform2(float x, bool gla) {
+  const float sp2 = softplus2_f(gla ? -x : x);
+  return gla ? sp2 * (-1.0f / 16.0f) : -sp2;
 }
+// the same in natural-log units
+__device__ __forceinline__ float decay_transform(float x, bool gla) {
+  return decay_transform2(x, gla) * 0.6931471805599453f;
+}
+// log a from the log_alpha input: -softplus(x), or GLA's sigmoid(x)^{1/16}
 __device__ __forceinline__ float fused_log_alpha(float x, int fuse) {
   if (!(fuse & (kFuseSoftplus | kFuseGla))) return x;
   return decay_transform(x, (fuse & kFuseGla) != 0);
