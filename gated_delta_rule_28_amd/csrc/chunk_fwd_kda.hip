@@ -48,6 +48,9 @@
 //   waves 4, 5 (32-column slices): derive chunk i (shares)
 //   LDS DMA of v of chunk i: wave 5, or wave 2 with four prep waves
 //   state:  chunk i-2
+//   with a fused decay transform, the state waves (and with six prep waves
+//   also waves 3 and 5) transform chunk i+2's decay pre-activations, a share
+//   of its rows each
 // Raw inputs live four iterations (DMA to derivation), derived operands
 // three, v three, T' and P two.
 #include <cstddef>
@@ -158,8 +161,53 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
   for (int kk = 0; kk < KKD; ++kk) kq_off[kk] = qk_at(lr, 4 * kk + lg);
 
-  // Every role runs two prologue barriers and nchunks + 2 iterations of one
-  // barrier, so all waves execute the same sequence of workgroup barriers.
+  // With a fused decay transform (two transcendentals per element) the waves
+  // that wait at the barrier for much of an iteration in that kernel turn
+  // chunk j's decay pre-activations into log2 a in place in iteration
+  // j - 2, a share of the rows each; the raw DMA waves then wait
+  // for their loads within the iteration that issues them (a chunk's loads
+  // land well inside one iteration), so chunk j is in LDS from iteration
+  // j - 2 on, and its sums in iteration j - 1 add the transformed values.
+  const bool xf = FUSED && (fuse & (kFuseSoftplus | kFuseGla)) != 0;
+  // The transform's rows are shared by the waves that have time to spare:
+  // the state waves, and with six prep waves also the solver and the v DMA
+  // wave (prep waves 3 and 5), two row passes each, the state waves the
+  // rest.  A pass is TPRX rows of 64 lanes, a lane one channel pair; NP
+  // passes from pass pb, straight-line.  Padded tokens get log a = 0.
+  constexpr int NCPX = DK / 2, TPRX = 64 / NCPX, NPT = KC / TPRX;
+  constexpr int XSIDE = (DVS == 32) ? 2 * NPT / 16 : 0;        // passes of waves 3 and 5 each
+  constexpr int XSTATE = (NPT - 2 * XSIDE) / (DVS / 16);       // passes of each state wave
+  static_assert(XSTATE * (DVS / 16) + 2 * XSIDE == NPT, "transform shares cover the chunk");
+  auto xform = [&](int j, int pb, auto np_) {
+    constexpr int NP = decltype(np_)::value;
+    typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
+    const int n = min(KC, T - j * KC);
+    const int c0 = 2 * (lane % NCPX), r0 = TPRX * pb + lane / NCPX;
+    const bool gla = (fuse & kFuseGla) != 0;
+    f32x2 x[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) x[i] = *reinterpret_cast<const f32x2 *>(&rw.G[r0 + TPRX * i][c0]);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const float keep = (r0 + TPRX * i < n) ? 1.0f : 0.0f;
+      *reinterpret_cast<f32x2 *>(&rw.G[r0 + TPRX * i][c0]) =
+          f32x2{decay_transform2(x[i][0], gla), decay_transform2(x[i][1], gla)} * keep;
+    }
+  };
+  // this wave's share: the state waves, then waves 3 and 5 of six prep waves
+  auto xform_share = [&](int j) {
+    if (wave < DVS / 16) {
+      xform(j, XSTATE * wave, std::integral_constant<int, XSTATE>{});
+    } else if constexpr (XSIDE > 0) {
+      const int p = wave - DVS / 16;
+      if (p == 3) xform(j, NPT - 2 * XSIDE, std::integral_constant<int, XSIDE>{});
+      if (p == 5) xform(j, NPT - XSIDE, std::integral_constant<int, XSIDE>{});
+    }
+  };
+  const bool xpart = wave < DVS / 16 || (DVS == 32 && (wave - DVS / 16 == 3 || wave - DVS / 16 == 5));
+
+  // Every role runs three prologue barriers and nchunks + 2 iterations of
+  // one barrier, so all waves execute the same sequence of workgroup barriers.
   if (wave < NSW) {
     // =====================================================================
     // state waves: the serial pass, 16 state columns each
@@ -175,6 +223,11 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[mb][e] = S0[(long)srow(mb, e) * DV + col0 + lr];
+    }
+    __syncthreads();
+    if (xf) {
+      if (nchunks > 0) xform_share(0);
+      if (nchunks > 1) xform_share(1);
     }
     __syncthreads();
     __syncthreads();
@@ -353,6 +406,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         }
         split_state();
       }
+      if (xf && it + 2 < nchunks) xform_share(it + 2);
       load_kq(s + 1 < 0 ? 0 : s + 1);
       __syncthreads();
     }
@@ -392,6 +446,11 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 
   if (pw == 3) {
     // ---- Gram and solve of chunk it-1: T' = (I + A)^{-1} diag(b) ----
+    __syncthreads();
+    if (xf && xpart) {
+      if (nchunks > 0) xform_share(0);
+      if (nchunks > 1) xform_share(1);
+    }
     __syncthreads();
     __syncthreads();
     for (int it = 0; it < nchunks + 2; ++it) {
@@ -448,6 +507,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           }
         }
       }
+      if (xf && xpart && it + 2 < nchunks) xform_share(it + 2);
       __syncthreads();
     }
     return;
@@ -524,87 +584,24 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
     constexpr int NCP = DK / 2;
     const int c0 = 2 * (lane % NCP);
+    const float lscale = xf ? 1.0f : kLog2e;   // transformed values are log2 a already
     f32x2 acc = {0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < KC; ++r) {
       const f32x2 x = *reinterpret_cast<const f32x2 *>(&rw.G[r][c0]);
-      acc = f32x2{fmaf(x[0], kLog2e, acc[0]), fmaf(x[1], kLog2e, acc[1])};
+      acc = f32x2{fmaf(x[0], lscale, acc[0]), fmaf(x[1], lscale, acc[1])};
       if (lane < NCP) *reinterpret_cast<f32x2 *>(&rw.G[r][c0]) = acc;
     }
     const unsigned long long bad = __ballot(acc[0] < -kMaxSpan2 || acc[1] < -kMaxSpan2);
     if (lane == 0) rw.flag[0] = bad != 0ull;
   };
-  // with a fused decay transform (two transcendentals per element) the
-  // transform and the sums are shared by NGW waves: wave gi takes channel
-  // pairs PPW gi .. +PPW-1, a lane one pair and RPG consecutive rows, the
-  // RGN row groups of a pair in adjacent lanes, so that the scan of the
-  // group totals is a few DPP row shifts; each wave flags its own channels
-  // in flag[gi]
+  // the fused L2 norms are shared by NGW waves
   constexpr int NGW = (kda_npw<DVS>() == 6) ? 4 : 2;
-  constexpr int PPW = (DK / 2) / NGW, RGN = 64 / PPW, RPG = KC / RGN;
-  static_assert(PPW * RGN == 64 && RGN * RPG == KC && RGN <= 16, "shared decay sums");
-  auto row_shr = [](float x, auto n) {   // x of the lane n below in the 16-lane row
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), 0x110 + decltype(n)::value, 0xF, 0xF, true));
-  };
-  auto gsum_fused = [&](int j, int gi) {
-    typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
-    const int p = lane / RGN, rg = lane % RGN;
-    const int c0 = 2 * (gi * PPW + p);
-    const int n = min(KC, T - j * KC);
-    const bool gla = (fuse & kFuseGla) != 0;   // a transform is on whenever the sums are shared
-    // every row's load first (one LDS wait), then the transform of every
-    // row, masked by a factor: padded tokens keep log a = 0 (their rows
-    // hold the DMA's zeros, whose transform is finite), and no row sits in
-    // a branch of its own around its load
-    f32x2 x[RPG];
-#pragma unroll
-    for (int i = 0; i < RPG; ++i) x[i] = *reinterpret_cast<const f32x2 *>(&rw.G[rg * RPG + i][c0]);
-    f32x2 part[RPG];
-    f32x2 run = {0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      const float keep = (rg * RPG + i < n) ? 1.0f : 0.0f;
-      run += f32x2{decay_transform2(x[i][0], gla), decay_transform2(x[i][1], gla)} * keep;
-      part[i] = run;
-    }
-    f32x2 incl = run;
-    if constexpr (RGN > 1) {
-      const f32x2 y = {row_shr(incl[0], std::integral_constant<int, 1>{}),
-                       row_shr(incl[1], std::integral_constant<int, 1>{})};
-      if (rg >= 1) incl += y;
-    }
-    if constexpr (RGN > 2) {
-      const f32x2 y = {row_shr(incl[0], std::integral_constant<int, 2>{}),
-                       row_shr(incl[1], std::integral_constant<int, 2>{})};
-      if (rg >= 2) incl += y;
-    }
-    if constexpr (RGN > 4) {
-      const f32x2 y = {row_shr(incl[0], std::integral_constant<int, 4>{}),
-                       row_shr(incl[1], std::integral_constant<int, 4>{})};
-      if (rg >= 4) incl += y;
-    }
-    static_assert(RGN <= 8, "three scan steps");
-    f32x2 excl = {row_shr(incl[0], std::integral_constant<int, 1>{}),
-                  row_shr(incl[1], std::integral_constant<int, 1>{})};
-    if (rg == 0) excl = f32x2{0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < RPG; ++i)
-      *reinterpret_cast<f32x2 *>(&rw.G[rg * RPG + i][c0]) = part[i] + excl;
-    const unsigned long long bad =
-        __ballot(rg == RGN - 1 && (incl[0] < -kMaxSpan2 || incl[1] < -kMaxSpan2));
-    if (lane == 0) rw.flag[gi] = bad != 0ull;
-  };
-  const bool shared_gsum = FUSED && (fuse & (kFuseSoftplus | kFuseGla)) != 0;
-  // index of this wave among the NGW summing waves, or -1
+  // index of this wave among the NGW norm waves, or -1
   const int gsum_idx = (kda_npw<DVS>() == 6) ? (pw < 2 ? pw : (pw >= 4 ? pw - 2 : -1))
                                              : (pw < 2 ? pw : -1);
   auto sums = [&](int j) {
-    if (shared_gsum) {
-      if (gsum_idx >= 0) gsum_fused(j, gsum_idx);
-    } else if (pw == 1) {
-      gsum(j);
-    }
+    if (pw == 1) gsum(j);
   };
 
   // fused L2 normalisation of chunk j: 1/|q_r| and 1/|k_r|, shared by the
@@ -654,17 +651,13 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int NDW = NPW - 1;                 // deriving waves
   constexpr int NCP = DK / 2, TPR = 64 / NCP, NRW = KC / TPR;
   const int dw = pw < 3 ? pw : pw - 1;         // index among the deriving waves
-  // With the decay sums shared (fused decay transform) the summing waves
-  // take fewer rows and the scores wave more (measured on the KDA shape).
   auto row_bound = [&](int w) {
     if constexpr (NPW == 6) {
       constexpr int b[6] = {0, 4, 7, 9, 13, 16};
-      constexpr int bs[6] = {0, 3, 5, 10, 13, 16};
-      return (shared_gsum ? bs[w] : b[w]) * NRW / 16;
+      return b[w] * NRW / 16;
     } else {
       constexpr int b[4] = {0, 7, 12, 16};
-      constexpr int bs[4] = {0, 3, 7, 16};
-      return (shared_gsum ? bs[w] : b[w]) * NRW / 16;
+      return b[w] * NRW / 16;
     }
   };
   auto derive = [&](int j) {
@@ -676,12 +669,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     int dso = __builtin_amdgcn_readfirstlane((j % NDER) * (int)sizeof(typename SM::Der) + (int)offsetof(SM, der));
     asm volatile("" : "+s"(dso));   // emits nothing; hides the constant part
     typename SM::Der &d = *reinterpret_cast<typename SM::Der *>(reinterpret_cast<char *>(&sm) + dso);
-    int fl = rw.flag[0];
-    if (shared_gsum) {
-#pragma unroll
-      for (int i = 1; i < NGW; ++i) fl |= rw.flag[i];
-    }
-    const int exact = __builtin_amdgcn_readfirstlane(fl);
+    const int exact = __builtin_amdgcn_readfirstlane(rw.flag[0]);
     const int cp = lane % NCP, c0 = 2 * cp;
     const f32x2 gl = *reinterpret_cast<const f32x2 *>(&rw.G[KC - 1][c0]);
     if (pw == 0) {
@@ -781,14 +769,21 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
   };
 
-  // prologue: raw chunks 0..2 in flight, 0 and 1 landed, chunk 0 summed
+  // prologue: raw chunks 0..2 in flight, 0 and 1 landed (all three with a
+  // fused decay transform, whose participants then transform 0 and 1),
+  // chunk 0 summed
   if (pw < 2) {
     if (nchunks > 0) issue_raw(0);
     if (nchunks > 1) issue_raw(1);
     if (nchunks > 2) issue_raw(2);
-    wait_own(nchunks > 2);
+    wait_own(!xf && nchunks > 2);
   }
   const bool l2 = (fuse & kFuseL2) && gsum_idx >= 0;
+  __syncthreads();
+  if (xf && xpart) {   // the transform of chunks 0 and 1 (fused decay)
+    if (nchunks > 0) xform_share(0);
+    if (nchunks > 1) xform_share(1);
+  }
   __syncthreads();
   if (nchunks > 0) sums(0);
   if (l2 && nchunks > 0) norms(0, gsum_idx);
@@ -801,14 +796,14 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       if (it + 1 < nchunks) sums(it + 1);
       if (l2 && it + 1 < nchunks) norms(it + 1, gsum_idx);
       if (it < nchunks) derive(it);
-      wait_own(more);
+      wait_own(more && !xf);
     } else {
       const bool more = it < nchunks;
       if (pw == PW_V && more) issue_v(it);
       if (l2 && it + 1 < nchunks) norms(it + 1, gsum_idx);
-      if (shared_gsum && it + 1 < nchunks) sums(it + 1);
       if (pw == 2 && it >= 1 && it - 1 < nchunks) scores(it - 1);
       if (it < nchunks) derive(it);
+      if (xf && xpart && it + 2 < nchunks) xform_share(it + 2);
       if (pw == PW_V) wait_own(more);
     }
     __syncthreads();
