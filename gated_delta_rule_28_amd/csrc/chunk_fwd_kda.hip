@@ -686,7 +686,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int coff = 2 * (c0 & 7);                 // byte offset inside the 16-byte block
     auto put = [&](bf16 (*hi)[DK], bf16 (*lo)[DK], int r, float x0, float x1) {
       unsigned h, l;
-      split2<false>(x0, x1, h, l);
+      split2(x0, x1, h, l);
       const int off = qk_at(r, c0 >> 3) + coff;
       *reinterpret_cast<unsigned *>(reinterpret_cast<char *>(&hi[0][0]) + off) = h;
       *reinterpret_cast<unsigned *>(reinterpret_cast<char *>(&lo[0][0]) + off) = l;
