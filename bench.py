@@ -503,6 +503,28 @@ def decode_parity(torch, W, d, seqs=(0, 97, 255)):
             "pass": bool(e_o <= 1e-5 and e_S <= 1e-5)}
 
 
+def sampled_parity(torch, W, kept, chains, tol=PARITY_TOL):
+    """The timed run's o and S_T on sampled (batch, head) chains, over the
+    whole sequence, against the fp64 oracle recurrence on the same inputs."""
+    import numpy as np
+    from oracle import gated_delta_recurrence
+    inp = kept["inp"]
+
+    def pick(x):   # [B, T, H, ...] -> [n, T, 1, ...]: the sampled chains as a batch
+        if x is None:
+            return None
+        a = W.to_f64(x)
+        return np.stack([a[b, :, h] for b, h in chains])[:, :, None]
+    o_ref, S_ref = gated_delta_recurrence(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]),
+                                          pick(inp["beta"]), pick(inp["log_alpha"]), None)
+    e_o = rel_err(pick(kept["o"]), o_ref)
+    S = W.to_f64(kept["S"])
+    e_S = rel_err(np.stack([S[b, h] for b, h in chains]), S_ref[:, 0])
+    return {"o_max_abs_over_rms": e_o, "S_T_max_abs_over_rms": e_S, "tol": tol,
+            "chains_checked": [list(c) for c in chains], "pass": bool(e_o <= tol and e_S <= tol),
+            "against": "fp64 oracle recurrence on the timed run's inputs, whole sequences"}
+
+
 def bwd_alg_bytes(w):
     """Single-pass minimum HBM bytes of one chunk_bwd call (zero initial state,
     no loss on the final state, dS_0 written): q, k, v, dO in (input dtype),
@@ -884,11 +906,14 @@ def main(argv=None):
         rec["bf16_output"] = {"value": w.B * w.T / (b["kernel_ms"]["mean"] * 1e-3),
                               "unit": "tokens/s", "kernel_ms": b["kernel_ms"],
                               "roofline": b["roofline"]}
+        kept_kda = {}
         kda = chunk_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2, torch.float32,
-                         args.settle_s)
+                         args.settle_s, keep=kept_kda)
         rec["kda"] = {k: kda[k] for k in keys}
         rec["kda"]["roofline"] = with_copy_frac(kda["roofline"], copy)
         rec["kda"]["unit"] = "tokens/s"
+        rec["kda"]["parity"] = sampled_parity(torch, W, kept_kda, ((0, 0), (1, 31)))
+        kept_kda.clear()
         # the erase-free variant (additive write) through the same kernels:
         # the Mamba-2 / SSD decay on the headline shape, GLA's on the KDA shape
         for key, wl in (("additive_scalar", w), ("additive_channel", W.by_name("kda_bf16_b2h32t8192"))):
