@@ -244,6 +244,40 @@ def fused_inputs(torch, inp, w):
     return out
 
 
+def separate_passes_line(torch, gdr, W, w, steps, warmup, settle_s, copy_gbs, unfused_ms):
+    """The fused options done as separate passes around the unfused kernel,
+    for comparison with the fused line: log a = -softplus(x) of the decay
+    pre-activations, q and k L2-normalised, b = sigmoid of its logit, the
+    kernel, then o *= silu(gate).  One step = all of them, timed with the
+    same events (torch's elementwise kernels for the passes).  Also the bytes
+    the passes move (each reads its input and writes its output once) and
+    their time at the measured copy rate."""
+    import torch.nn.functional as F
+    inp = fused_inputs(torch, W.make_workload_inputs(w, seed=0, device="cuda"), w)
+    o = torch.empty(w.B, w.T, w.H, w.Dv, device="cuda", dtype=torch.float32)
+    S = torch.empty(w.B, w.H, w.Dk, w.Dv, device="cuda", dtype=torch.float32)
+
+    def step():
+        la = F.logsigmoid(-inp["log_alpha"]) if inp["log_alpha"] is not None else None
+        qn = F.normalize(inp["q"], dim=-1)
+        kn = F.normalize(inp["k"], dim=-1)
+        b = torch.sigmoid(inp["beta"])
+        gdr.chunk_fwd(qn, kn, inp["v"], b, la, None, chunk=w.chunk, o=o, final_state=S)
+        o.mul_(F.silu(inp["out_gate"]))
+    _, per = time_launches(torch, step, steps, warmup, settle_s)
+    th = w.B * w.T * w.H
+    in_b = 2 if w.in_dtype == "bf16" else 4
+    la_n = {"none": 0, "scalar": th, "channel": th * w.Dk}[w.gate]
+    passes_bytes = (2 * 4 * la_n + 2 * 2 * in_b * th * w.Dk + 2 * 4 * th
+                    + (4 + in_b + 4) * th * w.Dv)
+    at_copy = passes_bytes / (copy_gbs * 1e9) * 1e3 if copy_gbs else None
+    return {"ms": statistics.fmean(per), "passes_bytes": passes_bytes,
+            "passes_ms_at_copy_rate": at_copy,
+            "unfused_kernel_plus_passes_at_copy_rate_ms": (unfused_ms + at_copy) if at_copy else None,
+            "note": "torch elementwise passes (logsigmoid, normalize, sigmoid, silu and mul) "
+                    "around the unfused kernel, timed as one step"}
+
+
 def chunk_setup(torch, gdr, W, w, out_dtype, erase=True, fused=False, keep=None):
     inp = W.make_workload_inputs(w, seed=0, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.Dv, device="cuda", dtype=out_dtype)
@@ -929,6 +963,9 @@ def main(argv=None):
             rec[key]["unit"] = "tokens/s"
             rec[key]["variant"] = ("fused prologue (q, k L2 norm, sigmoid b, softplus decay) "
                                    "and SiLU output gate")
+            unfused_ms = (head if key == "fused" else kda)["kernel_ms"]["mean"]
+            rec[key]["separate_passes"] = separate_passes_line(
+                torch, gdr, W, wl, nb, 2, args.settle_s, copy["GB/s"] if copy else None, unfused_ms)
         rec["decode"] = decode_line(torch, gdr, W, W.DECODE, settle_s=args.settle_s)
         rec["decode"]["roofline"] = with_copy_frac(rec["decode"]["roofline"], copy)
         rec["decode"]["parity"] = decode_parity(torch, W, W.DECODE)
