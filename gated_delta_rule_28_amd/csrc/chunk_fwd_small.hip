@@ -101,11 +101,16 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
       }
       __syncthreads();
     }
-    // cumulative log decay down each channel (padded tokens carry 0)
+    // cumulative log decay down each channel (padded tokens carry 0), the
+    // column loaded into registers first
     for (int c = tid; c < D; c += NT) {
+      float gc[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) gc[r] = sm.G[r][c];
       float acc = 0.f;
+#pragma unroll
       for (int r = 0; r < C; ++r) {
-        acc += sm.G[r][c];
+        acc += gc[r];
         sm.G[r][c] = acc;
       }
     }
@@ -137,14 +142,24 @@ chunk_fwd_small_kernel(const void *__restrict__ q, const void *__restrict__ k,
       sm.U[r][c] = sm.V[r][c] - acc;
     }
     __syncthreads();
-    // (I + A) U = diag(b) R by forward substitution, one lane per column
+    // (I + A) U = diag(b) R by forward substitution, one lane per column,
+    // the column kept in registers (A is read by broadcast, U never goes
+    // back to LDS until the column is done)
     if (tid < 64) {
       for (int c = tid; c < D; c += 64) {
-        for (int r = 0; r < C; ++r) {
-          float acc = sm.beta[r] * sm.U[r][c];
-          for (int s = 0; s < r; ++s) acc -= sm.A[r][s] * sm.U[s][c];
-          sm.U[r][c] = acc;
+        // right-looking: once u[s] is final it updates every later row, so
+        // the dependent chain is one FMA per step and the rows' updates are
+        // independent
+        float u[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) u[r] = sm.beta[r] * sm.U[r][c];
+#pragma unroll
+        for (int s2 = 0; s2 < C - 1; ++s2) {
+#pragma unroll
+          for (int r = s2 + 1; r < C; ++r) u[r] -= sm.A[r][s2] * u[s2];
         }
+#pragma unroll
+        for (int r = 0; r < C; ++r) sm.U[r][c] = u[r];
       }
     }
     __syncthreads();
