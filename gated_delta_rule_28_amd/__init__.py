@@ -186,20 +186,20 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
     return o
 
 
-def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0):
+def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0, erase=True):
     """Bytes of device workspace chunk_bwd needs for inputs shaped like q
     ([B, T, H, Dk]) and this gate (0 when the call is not supported)."""
     B, T, H, Dk = q.shape
-    gate = _gate_of(log_alpha, (B, T, H), Dk)
+    gate = _gate_of(log_alpha, (B, T, H), Dk) | (0 if erase else _abi.GDR_NO_ERASE)
     return int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dk, int(chunk), _DT[q.dtype], gate))
 
 
 def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_final_state=None,
-              *, chunk=0, workspace=None, want_d_initial_state=True, out=None):
+              *, chunk=0, erase=True, workspace=None, want_d_initial_state=True, out=None):
     """Gradients of chunk_fwd's o and final state.
 
     Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, no gate or the
-    per-head gate); d_o [B, T, H, Dv] in the dtype of q (None for zero) and
+    per-head gate, with or without the erase term); d_o [B, T, H, Dv] in the dtype of q (None for zero) and
     d_final_state [B, H, Dk, Dv] fp32 (None for zero).  Returns a dict with
     dq, dk, dv (fp32, shaped like q, k, v), dbeta [B, T, H], dlog_alpha
     (None without a gate, else [B, T, H]) and d_initial_state
@@ -220,7 +220,7 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     Dv = v.shape[3]
     if tuple(beta.shape) != (B, T, H):
         raise ValueError("beta must be [B, T, H]")
-    gate = _gate_of(log_alpha, (B, T, H), Dk)
+    gate = _gate_of(log_alpha, (B, T, H), Dk) | (0 if erase else _abi.GDR_NO_ERASE)
     if log_alpha is not None:
         _check_dev("log_alpha", log_alpha, torch.float32)
     for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):

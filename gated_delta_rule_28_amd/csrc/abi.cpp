@@ -188,6 +188,7 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   gdr::BwdArgs a;
   a.B = B; a.T = T; a.H = H; a.D = Dk;
   a.gate = gate_kind(gate);
+  a.erase = erases(gate);
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
   a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;

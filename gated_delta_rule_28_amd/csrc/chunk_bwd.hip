@@ -30,6 +30,11 @@
 //   dg_last += sum_r ec_r k_r.(U dh^T)_r + gam_last <h, dh>
 //   dlog a_t = sum_{r >= t} dg_r           (g is a within-chunk cumsum)
 //
+// Without the erase term (S' = gam_last S + K^T diag(ec) U, U = diag(b) V)
+// T = I and R = V: dY = dU, A and M vanish, and so do every dA / dM term and
+// the dR h^T terms (R no longer depends on h): db_r = dY_r . v_r,
+// dK = diag(ec) U dh^T + (dP o Gam)^T Q, E = dP o P (template flag ERASE).
+//
 // One workgroup of four waves per (chain, chunk).  q, k and dO are exact
 // bf16 and enter MFMAs unsplit; every derived operand (h, dh, U, dR, dY,
 // the n x n gradient matrices) is split into bf16 hi + lo, as in the forward
@@ -96,7 +101,7 @@ __device__ __forceinline__ float sum64(float x) {
   return x;
 }
 
-template <int DK, int GATE>
+template <int DK, int GATE, bool ERASE>
 __global__ void __launch_bounds__(64 * NW, 2)
 chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ v, const float *__restrict__ beta,
@@ -251,10 +256,12 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const bf16x8 yh = ld8(&sm.Yh[16 * ti + lr][kc]), yl = ld8(&sm.Yl[16 * ti + lr][kc]);
       const bf16x8 uh = ld8(&sm.Uh[16 * tj + lr][kc]), ul = ld8(&sm.Ul[16 * tj + lr][kc]);
       pt = mfma_bf16(qa, kb, pt);
-      mt = mfma_bf16(ka, kb, mt);
-      at = mfma_bf16(yh, uh, at);
-      at = mfma_bf16(yl, uh, at);
-      at = mfma_bf16(yh, ul, at);
+      if constexpr (ERASE) {
+        mt = mfma_bf16(ka, kb, mt);
+        at = mfma_bf16(yh, uh, at);
+        at = mfma_bf16(yl, uh, at);
+        at = mfma_bf16(yh, ul, at);
+      }
       dt = mfma_bf16(da, uh, dt);
       dt = mfma_bf16(da, ul, dt);
     }
@@ -267,8 +274,8 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const int r = 16 * ti + 4 * lg + e;
       const float gm = (GATE == kGateNone) ? 1.0f : __expf(sm.g[r] - gs);
       const float P = (s <= r) ? pt[e] * gm : 0.0f;
-      const float M = (s < r) ? mt[e] * gm : 0.0f;
-      const float dA = (s < r) ? -at[e] : 0.0f;
+      const float M = (ERASE && s < r) ? mt[e] * gm : 0.0f;
+      const float dA = (ERASE && s < r) ? -at[e] : 0.0f;
       const float dP = (s <= r) ? dt[e] : 0.0f;
       const float dM = sm.beta[r] * dA;
       sm.Hm[r][s] = dA * M;
@@ -334,9 +341,11 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const bf16x8 uh = ld8(&sm.Uh[16 * rb + lr][kc]), ul = ld8(&sm.Ul[16 * rb + lr][kc]);
           aq[rb] = mfma_bf16(da, hh, aq[rb]);
           aq[rb] = mfma_bf16(da, hl, aq[rb]);
-          ar[rb] = mfma_bf16(rh, hh, ar[rb]);
-          ar[rb] = mfma_bf16(rl, hh, ar[rb]);
-          ar[rb] = mfma_bf16(rh, hl, ar[rb]);
+          if constexpr (ERASE) {
+            ar[rb] = mfma_bf16(rh, hh, ar[rb]);
+            ar[rb] = mfma_bf16(rl, hh, ar[rb]);
+            ar[rb] = mfma_bf16(rh, hl, ar[rb]);
+          }
           au[rb] = mfma_bf16(uh, gh, au[rb]);
           au[rb] = mfma_bf16(ul, gh, au[rb]);
           au[rb] = mfma_bf16(uh, gl, au[rb]);
@@ -384,10 +393,12 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xk = xq;
         xq = mfma_bf16(row8(sm.XPh), kb, xq);
         xq = mfma_bf16(row8(sm.XPl), kb, xq);
-        xk = mfma_bf16(row8(sm.XMh), kb, xk);
-        xk = mfma_bf16(row8(sm.XMl), kb, xk);
-        xk = mfma_bf16(col8(sm.XMh), kb, xk);
-        xk = mfma_bf16(col8(sm.XMl), kb, xk);
+        if constexpr (ERASE) {
+          xk = mfma_bf16(row8(sm.XMh), kb, xk);
+          xk = mfma_bf16(row8(sm.XMl), kb, xk);
+          xk = mfma_bf16(col8(sm.XMh), kb, xk);
+          xk = mfma_bf16(col8(sm.XMl), kb, xk);
+        }
         xk = mfma_bf16(col8(sm.XPh), qb, xk);
         xk = mfma_bf16(col8(sm.XPl), qb, xk);
         // lane holds rows r0 + e of column dkt + lr
@@ -399,13 +410,13 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int e = 0; e < 4; ++e) {
           const int r = r0 + e;
           const float gq = gm4[e] * aq[rb][e];
-          const float gr = gm4[e] * b4[e] * ar[rb][e];
+          const float gr = ERASE ? gm4[e] * b4[e] * ar[rb][e] : 0.0f;
           const float gu = ec4[e] * au[rb][e];
           const unsigned off = 4u * ((unsigned)r * (unsigned)(H * DK) + (unsigned)col);
           buf_st1(gq + xq[e], rdq, off);
           buf_st1(gu - gr + xk[e], rdk, off);
           const float kv = (float)sm.K[r][col];
-          partb[rb][e] += kv * (gm4[e] * ar[rb][e]);
+          if constexpr (ERASE) partb[rb][e] += kv * (gm4[e] * ar[rb][e]);
           if constexpr (GATE == kGateScalar) {
             const float qv = (float)sm.Q[r][col];
             part[rb][e] += qv * gq - kv * gr - kv * gu;
@@ -420,8 +431,10 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rb + 4 * lg + e;
-          const float pb = sum16(partb[rb][e]);
-          if (lr == 0) sm.dbp[wave][r] = (nt == 0 ? 0.0f : sm.dbp[wave][r]) + pb;
+          if constexpr (ERASE) {
+            const float pb = sum16(partb[rb][e]);
+            if (lr == 0) sm.dbp[wave][r] = (nt == 0 ? 0.0f : sm.dbp[wave][r]) + pb;
+          }
           if constexpr (GATE == kGateScalar) {
             const float p = sum16(part[rb][e]);
             if (lr == 0) sm.dgp[wave][r] = (nt == 0 ? 0.0f : sm.dgp[wave][r]) + p;
@@ -455,11 +468,13 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   if (wave == 0) {
     const int r = lane & 31;
     float db = sm.dba[r], gsum = 0.0f;
+    if constexpr (ERASE) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) db -= sm.dbp[w][r];
+      for (int w = 0; w < NW; ++w) db -= sm.dbp[w][r];
+    }
 #pragma unroll 8
     for (int s2 = 0; s2 < C; ++s2) {
-      db += sm.Hm[r][s2];
+      if constexpr (ERASE) db += sm.Hm[r][s2];
       gsum += sm.G[r][s2] - sm.G[s2][r];
     }
     if (lane < C && r < n) dbeta[trow(r)] = db;
@@ -489,14 +504,19 @@ template <int DK>
 hipError_t launch_dk(const BwdArgs &a) {
   const int nchunks = (a.T + C - 1) / C;
   dim3 grid((unsigned)((long)a.B * a.H * nchunks)), block(64 * NW);
-#define GDR_LAUNCH(G)                                                                           \
-  hipLaunchKernelGGL((chunk_bwd_grad_kernel<DK, G>), grid, block, 0, a.stream,                  \
+#define GDR_LAUNCH(G, E)                                                                        \
+  hipLaunchKernelGGL((chunk_bwd_grad_kernel<DK, G, E>), grid, block, 0, a.stream,               \
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,          \
                      a.log_alpha, (const bf16 *)a.d_o, a.ws_h, a.ws_u, a.ws_dh, a.ws_dy, a.dq,  \
                      a.dk,                                                                     \
                      a.dv, a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
-  if (a.gate == kGateNone) GDR_LAUNCH(kGateNone);
-  else GDR_LAUNCH(kGateScalar);
+  if (a.erase) {
+    if (a.gate == kGateNone) GDR_LAUNCH(kGateNone, true);
+    else GDR_LAUNCH(kGateScalar, true);
+  } else {
+    if (a.gate == kGateNone) GDR_LAUNCH(kGateNone, false);
+    else GDR_LAUNCH(kGateScalar, false);
+  }
 #undef GDR_LAUNCH
   return hipGetLastError();
 }

@@ -169,8 +169,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   static_assert(sizeof(SM) <= 160 * 1024, "LDS budget");
   static_assert(sizeof(In) % 16 == 0 && (C * QRB) % 1024 == 0 && (C * VRB) % 1024 == 0,
                 "DMA runs are whole 1 KiB waves");
-  static_assert(MODE == kModeFwd || (ERASE && !FUSED && GATE != kGateChannel),
-                "the backward passes run the erasing, unfused scalar-gate form");
+  static_assert(MODE == kModeFwd || (!FUSED && GATE != kGateChannel),
+                "the backward passes run the unfused forms without the per-channel gate");
   constexpr bool WANT_O = MODE == kModeFwd;      // outputs (Q S, P U, o)
   // Carried-scale form of the state (forward, scalar decay): the state
   // waves hold Z with S = Z_scale * Z, so that the decay of a chunk does not
@@ -359,6 +359,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         // dU = diag(e^{g_last - g}) K dS + P^T dO; row r of P^T is row r of
         // the stored P^T tile, k = tokens {4 lg + j} u {16 + 4 lg + j}
         bf16x4 duh[2], dul[2];
+        f32x4 du[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
@@ -369,6 +370,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                                 *reinterpret_cast<const bf16x4 *>(&ps.Pl[16 * rb + lr][16 + 4 * lg]));
           acc = mfma_bf16(ph, Dd, acc);
           acc = mfma_bf16(pl, Dd, acc);
+          du[rb] = acc;
           split4(acc, duh[rb], dul[rb]);
         }
         const bf16x8 DUh = cat(duh[0], duh[1]), DUl = cat(dul[0], dul[1]);
@@ -378,14 +380,18 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         bf16x4 bqh[2], bql[2], bkh[2], bkl[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const bf16x8 th = cat(*reinterpret_cast<const bf16x4 *>(&Th[16 * rb + lr][4 * lg]),
-                                *reinterpret_cast<const bf16x4 *>(&Th[16 * rb + lr][16 + 4 * lg]));
-          const bf16x8 tl = cat(*reinterpret_cast<const bf16x4 *>(&Tl[16 * rb + lr][4 * lg]),
-                                *reinterpret_cast<const bf16x4 *>(&Tl[16 * rb + lr][16 + 4 * lg]));
-          f32x4 y = {0.f, 0.f, 0.f, 0.f};
-          y = mfma_bf16(th, DUh, y);
-          y = mfma_bf16(tl, DUh, y);
-          y = mfma_bf16(th, DUl, y);
+          // without the erase term T = I: dY = dU
+          f32x4 y = du[rb];
+          if constexpr (ERASE) {
+            const bf16x8 th = cat(*reinterpret_cast<const bf16x4 *>(&Th[16 * rb + lr][4 * lg]),
+                                  *reinterpret_cast<const bf16x4 *>(&Th[16 * rb + lr][16 + 4 * lg]));
+            const bf16x8 tl = cat(*reinterpret_cast<const bf16x4 *>(&Tl[16 * rb + lr][4 * lg]),
+                                  *reinterpret_cast<const bf16x4 *>(&Tl[16 * rb + lr][16 + 4 * lg]));
+            y = f32x4{0.f, 0.f, 0.f, 0.f};
+            y = mfma_bf16(th, DUh, y);
+            y = mfma_bf16(tl, DUh, y);
+            y = mfma_bf16(th, DUl, y);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             __builtin_nontemporal_store(y[e], dyb + (16 * rb + 4 * lg + e) * DV + col0 + lr);
@@ -395,10 +401,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
           for (int e = 0; e < 4; ++e) gd[e] = gm4[e] * (float)dov[rb][e];
           split4(gd, bqh[rb], bql[rb]);
-          split4(-(gm4 * b4) * y, bkh[rb], bkl[rb]);
+          if constexpr (ERASE) split4(-(gm4 * b4) * y, bkh[rb], bkl[rb]);
         }
         const bf16x8 Bqh = cat(bqh[0], bqh[1]), Bql = cat(bql[0], bql[1]);
-        const bf16x8 Bkh = cat(bkh[0], bkh[1]), Bkl = cat(bkl[0], bkl[1]);
+        bf16x8 Bkh = {}, Bkl = {};
+        if constexpr (ERASE) {
+          Bkh = cat(bkh[0], bkh[1]);
+          Bkl = cat(bkl[0], bkl[1]);
+        }
         const float glast = (GATE == kGateNone) ? 1.0f : bs.gam[C - 1];
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb) {
@@ -408,8 +418,10 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const bf16x8 aq = cat(ld_tr4(reinterpret_cast<const bf16 *>(Qb + off)),
                                 ld_tr4(reinterpret_cast<const bf16 *>(Qb + off + 16 * QRB)));
           f32x4 acc = Sacc[mb] * glast;
-          acc = mfma_bf16(ak, Bkh, acc);
-          acc = mfma_bf16(ak, Bkl, acc);
+          if constexpr (ERASE) {   // dS = gam_last dS' + Q^T diag(gam) dO - K^T diag(gam b) dY
+            acc = mfma_bf16(ak, Bkh, acc);
+            acc = mfma_bf16(ak, Bkl, acc);
+          }
           acc = mfma_bf16(aq, Bqh, acc);
           acc = mfma_bf16(aq, Bql, acc);
           Sacc[mb] = acc;
@@ -465,7 +477,8 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
               a2 = mfma_bf16(Sh[kk], aq, a2);
               a1 = mfma_bf16(ak, Sl[kk], a1);
               a2 = mfma_bf16(Sl[kk], aq, a2);
-            } else {
+            } else if constexpr (WANT_O) {
+              // no erase term: Q S only (and nothing in the recompute pass)
               const bf16x8 aq = ld8(reinterpret_cast<const bf16 *>(Qb + 16 * rb * QRB + kq_off[kk]));
               a2 = mfma_bf16(Sh[kk], aq, a2);
               a2 = mfma_bf16(Sl[kk], aq, a2);
@@ -499,6 +512,12 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int rb = 0; rb < 2; ++rb) {
             uh[rb] = rh2[rb];
             ul[rb] = rl2[rb];
+            if constexpr (MODE == kModeRec) {   // U = b o V
+              float *ubp = ws_b + ((long)chain * nchunks + s) * (C * DV);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                __builtin_nontemporal_store(rv[rb][e], ubp + (16 * rb + 4 * lg + e) * DV + col0 + lr);
+            }
             const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
             split4(rv[rb] * ec4, wh[rb], wl[rb]);
           }
@@ -961,17 +980,17 @@ hipError_t launch_fused(const ChunkArgs &a) {
 }
 
 // the backward's two sequential passes at one tile configuration
-template <int DK, int DVS, int GATE>
+template <int DK, int DVS, int GATE, bool ERASE>
 hipError_t launch_passes(const BwdArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, true, false, kModeRec>), grid,
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, ERASE, false, kModeRec>), grid,
                      block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
                      a.beta, a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0,
                      nullptr, a.ws_h, a.ws_u, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, true, false, kModeRev>), grid,
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, ERASE, false, kModeRev>), grid,
                      block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.d_o,
                      a.beta, a.log_alpha, a.d_final_state, nullptr, a.d_initial_state, a.B, a.T,
                      a.H, 0, nullptr, a.ws_dh, a.ws_dy, nullptr);
@@ -980,8 +999,12 @@ hipError_t launch_passes(const BwdArgs &a) {
 
 template <int DK, int DVS>
 hipError_t passes_by_gate(const BwdArgs &a) {
-  if (a.gate == kGateNone) return launch_passes<DK, DVS, kGateNone>(a);
-  return launch_passes<DK, DVS, kGateScalar>(a);
+  if (a.erase) {
+    if (a.gate == kGateNone) return launch_passes<DK, DVS, kGateNone, true>(a);
+    return launch_passes<DK, DVS, kGateScalar, true>(a);
+  }
+  if (a.gate == kGateNone) return launch_passes<DK, DVS, kGateNone, false>(a);
+  return launch_passes<DK, DVS, kGateScalar, false>(a);
 }
 
 template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
@@ -1019,8 +1042,9 @@ bool chunk_fwd_bf16_supported(const ChunkArgs &a) {
 
 bool chunk_bwd_supported(int D, bool in_bf16, int gate, bool erase, long H) {
   const long chunk_bytes = (long)4 * ((long)(C - 1) * H * D + D);
+  (void)erase;   // both forms: with the erase term and without (additive write)
   return in_bf16 && (D == 128 || D == 64) && (gate == kGateNone || gate == kGateScalar) &&
-         erase && chunk_bytes < 0xFFFFFFFFL;
+         chunk_bytes < 0xFFFFFFFFL;
 }
 
 hipError_t launch_chunk_bwd_passes(const BwdArgs &a) {

@@ -49,12 +49,13 @@ bool chunk_fwd_small_supported(const ChunkArgs &a);
 hipError_t launch_state_passthrough(const float *src, float *dst, long count, hipStream_t stream);
 
 // ---- backward of the chunk forward (bf16 q/k/v/dO, D = 64 or 128, no gate
-//      or the scalar gate, with the erase term) ----
+//      or the scalar gate, with or without the erase term) ----
 constexpr int kBwdChunk = 32;   // tokens per chunk of the passes and of the workspace
 
 struct BwdArgs {
   int B, T, H, D;
   int gate;                     // kGateNone or kGateScalar
+  bool erase;                   // false: the additive write (no erase term)
   const void *q, *k, *v;
   const float *beta, *log_alpha;
   const float *initial_state;   // S_0 or nullptr

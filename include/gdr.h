@@ -201,8 +201,8 @@ size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
  *   B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
  *   initial_state  exactly as passed to gdr_chunk_fwd.  Supported: bf16
  *                 q/k/v, Dk == Dv in {64, 128}, GDR_GATE_NONE or
- *                 GDR_GATE_SCALAR without GDR_NO_ERASE (others return
- *                 GDR_EUNSUPPORTED)
+ *                 GDR_GATE_SCALAR, with or without GDR_NO_ERASE (others
+ *                 return GDR_EUNSUPPORTED)
  *   d_o           [B, T, H, Dv] in_dtype, dL/do
  *   d_final_state [B, H, Dk, Dv] fp32, or NULL for zero
  *   dq, dk        [B, T, H, Dk] fp32 (written)

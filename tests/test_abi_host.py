@@ -202,10 +202,13 @@ def test_backward_workspace_size():
     assert bwd_ws() == 8 * 16 * 128 * per
     assert bwd_ws(T=33) == 8 * 16 * 2 * per                 # a ragged tail is one more chunk
     assert bwd_ws(gate=_abi.GDR_GATE_NONE) == bwd_ws()
+    # the erase-free forms keep the same partitions (U holds b o V there)
+    assert bwd_ws(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE) == bwd_ws()
+    assert bwd_ws(gate=_abi.GDR_GATE_NONE | _abi.GDR_NO_ERASE) == bwd_ws()
     assert bwd_ws(D=64, T=64, B=1, H=1) == 2 * 4 * (2 * 64 * 64 + 2 * 32 * 64)
     # unsupported calls and empty inputs need none
     for kw in (dict(in_dtype=_abi.GDR_F32), dict(gate=_abi.GDR_GATE_CHANNEL), dict(D=32),
-               dict(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE), dict(T=0), dict(B=0),
+               dict(gate=_abi.GDR_GATE_CHANNEL | _abi.GDR_NO_ERASE), dict(T=0), dict(B=0),
                dict(chunk=48), dict(gate=9)):
         assert bwd_ws(**kw) == 0, kw
 
@@ -235,7 +238,7 @@ def bwd(**kw):
     (dict(Dk=32, Dv=32), _abi.GDR_EUNSUPPORTED),
     (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
     (dict(gate=_abi.GDR_GATE_CHANNEL), _abi.GDR_EUNSUPPORTED),
-    (dict(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE), _abi.GDR_EUNSUPPORTED),
+    (dict(gate=_abi.GDR_GATE_CHANNEL | _abi.GDR_NO_ERASE), _abi.GDR_EUNSUPPORTED),
     (dict(H=300000), _abi.GDR_EUNSUPPORTED),
     (dict(workspace=None), _abi.GDR_EWORKSPACE),
     (dict(workspace=FAKE + 16), _abi.GDR_EWORKSPACE),          # not 256-byte aligned

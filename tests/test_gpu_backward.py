@@ -61,20 +61,21 @@ def run_gpu(inp, **kw):
     return out
 
 
-def oracle(inp, chains=None):
+def oracle(inp, chains=None, erase=True):
     """Oracle gradients over all chains, or over a list of (b, h) chains
     (then a list of per-chain dicts)."""
     a = {k: f64(v) for k, v in inp.items()}
     if chains is None:
         return gated_delta_backward(a["q"], a["k"], a["v"], a["beta"], a["log_alpha"],
-                                    a["initial_state"], a["d_o"], a["d_final_state"])
+                                    a["initial_state"], a["d_o"], a["d_final_state"],
+                                    erase=erase)
     outs = []
     for b, h in chains:
         sl = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]
         st = lambda x: None if x is None else x[b:b + 1, h:h + 1]
         outs.append(gated_delta_backward(sl(a["q"]), sl(a["k"]), sl(a["v"]), sl(a["beta"]),
                                          sl(a["log_alpha"]), st(a["initial_state"]),
-                                         sl(a["d_o"]), st(a["d_final_state"])))
+                                         sl(a["d_o"]), st(a["d_final_state"]), erase=erase))
     return outs
 
 
@@ -162,3 +163,38 @@ def test_backward_headline_shape_sampled_chains():
                (got[n][b:b + 1, h:h + 1] if n == "dS0" else got[n][b:b + 1, :, h:h + 1])
                for n in NAMES}
         check_all(sub, ref, w.gate)
+
+
+# The erase-free forms (S_t = a_t S_{t-1} + b_t k_t v_t^T): linear attention
+# without a gate, the Mamba-2 / SSD decay with the per-head gate.
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("gate", ["none", "scalar"])
+@pytest.mark.parametrize("T", [1, 33, 100])
+def test_backward_erase_free(D, gate, T):
+    say("bwd erase-free", D, gate, T)
+    inp = make_case(2, T, 2, D, gate, seed=3 * T + D)
+    check_all(run_gpu(inp, erase=False), oracle(inp, erase=False), gate)
+
+
+def test_backward_erase_free_many_chains_and_strong_decay():
+    """The wide launch, a strong steady decay and a hard reset mid-chunk."""
+    say("bwd erase-free many chains")
+    inp = make_case(4, 70, 32, 128, "scalar", seed=41, s0=True, dst=True)
+    la = inp["log_alpha"].clone()
+    la[0] = -2.0
+    la[1, 30] = -50.0
+    inp["log_alpha"] = la
+    check_all(run_gpu(inp, erase=False), oracle(inp, erase=False), "scalar")
+
+
+def test_backward_erase_free_differs_from_the_erase_form():
+    """The erase flag reaches the kernels: the two forms give different dk."""
+    say("bwd erase flag")
+    inp = make_case(1, 40, 2, 64, "scalar", seed=7)
+    a = run_gpu(inp, erase=False)
+    b = run_gpu(inp, erase=True)
+    ref = oracle(inp, erase=True)
+    assert rel_err(f64(b["dk"]), ref["dk"]) <= TOL
+    assert rel_err(f64(a["dk"]), ref["dk"]) > 0.05
