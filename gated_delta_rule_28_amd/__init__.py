@@ -198,11 +198,12 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
               *, chunk=0, erase=True, workspace=None, want_d_initial_state=True, out=None):
     """Gradients of chunk_fwd's o and final state.
 
-    Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, no gate or the
-    per-head gate, with or without the erase term); d_o [B, T, H, Dv] in the dtype of q (None for zero) and
-    d_final_state [B, H, Dk, Dv] fp32 (None for zero).  Returns a dict with
-    dq, dk, dv (fp32, shaped like q, k, v), dbeta [B, T, H], dlog_alpha
-    (None without a gate, else [B, T, H]) and d_initial_state
+    Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, every gate,
+    with or without the erase term); d_o [B, T, H, Dv] in the dtype of q
+    (None for zero) and d_final_state [B, H, Dk, Dv] fp32 (None for zero).
+    Returns a dict with dq, dk, dv (fp32, shaped like q, k, v), dbeta
+    [B, T, H], dlog_alpha (None without a gate, else shaped like log_alpha)
+    and d_initial_state
     [B, H, Dk, Dv] (None when want_d_initial_state is False).  `workspace`,
     a uint8 GPU tensor of at least chunk_bwd_workspace_bytes, is allocated
     with torch when not given; `out`, a dict of the same keys and shapes,
@@ -235,7 +236,8 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
         raise ValueError("d_o must be [B, T, H, Dv]")
     f32 = dict(device=q.device, dtype=torch.float32)
     shapes = {"dq": (B, T, H, Dk), "dk": (B, T, H, Dk), "dv": (B, T, H, Dv),
-              "dbeta": (B, T, H), "dlog_alpha": None if log_alpha is None else (B, T, H),
+              "dbeta": (B, T, H),
+              "dlog_alpha": None if log_alpha is None else tuple(log_alpha.shape),
               "d_initial_state": (B, H, Dk, Dv) if want_d_initial_state else None}
     if out is None:
         out = {n: None if shp is None else torch.empty(*shp, **f32) for n, shp in shapes.items()}

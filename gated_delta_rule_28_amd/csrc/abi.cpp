@@ -132,9 +132,11 @@ size_t gdr_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
 namespace {
 
 // workspace bytes of a supported backward call with at least one token
-size_t bwd_workspace(long B, long T, long H, int D) {
-  const long nchunks = (T + gdr::kBwdChunk - 1) / gdr::kBwdChunk;
-  return (size_t)(B * H * nchunks) * (size_t)gdr::bwd_ws_floats_per_chunk(D) * sizeof(float);
+// (gate: the gate kind, which sets the chunk of the passes)
+size_t bwd_workspace(long B, long T, long H, int D, int gate) {
+  const int C = gdr::bwd_chunk(gate);
+  const long nchunks = (T + C - 1) / C;
+  return (size_t)(B * H * nchunks) * (size_t)gdr::bwd_ws_floats_per_chunk(D, gate) * sizeof(float);
 }
 
 bool bwd_shape_ok(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate) {
@@ -142,7 +144,8 @@ bool bwd_shape_ok(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   if (!gdr::chunk_bwd_supported(Dk, in_dtype == GDR_BF16, gate_kind(gate), erases(gate), H))
     return false;
   // one workgroup per (chain, chunk) in the gradient kernel
-  const long nchunks = ((long)T + gdr::kBwdChunk - 1) / gdr::kBwdChunk;
+  const int C = gdr::bwd_chunk(gate_kind(gate));
+  const long nchunks = ((long)T + C - 1) / C;
   return (long)B * H * nchunks < 0x7FFFFFFFL;
 }
 
@@ -152,7 +155,7 @@ size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
                                      int in_dtype, int gate) {
   if (B <= 0 || T <= 0 || H <= 0 || !valid_dtype(in_dtype) || !valid_gate(gate)) return 0;
   if (!bwd_shape_ok(B, T, H, Dk, Dv, chunk, in_dtype, gate)) return 0;
-  return bwd_workspace(B, T, H, Dk);
+  return bwd_workspace(B, T, H, Dk, gate_kind(gate));
 }
 
 int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
@@ -181,7 +184,7 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
       !aligned16(dk) || !aligned16(dv) || !aligned(beta, 4) || !aligned(dbeta, 4) ||
       (log_alpha && !aligned(log_alpha, 4)) || (dlog_alpha && !aligned(dlog_alpha, 4)))
     return GDR_EINVAL;
-  const size_t need = bwd_workspace(B, T, H, Dk);
+  const size_t need = bwd_workspace(B, T, H, Dk, gate_kind(gate));
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
     return GDR_EWORKSPACE;
 
@@ -194,15 +197,17 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;
   a.d_initial_state = d_initial_state;
   // workspace partitions: h, dh [chain][chunk][D][D]; U, dY [chain][chunk][C][D]
-  const long nblk = (long)B * H * ((T + gdr::kBwdChunk - 1) / gdr::kBwdChunk);
+  const int C = gdr::bwd_chunk(a.gate);
+  const long nblk = (long)B * H * ((T + C - 1) / C);
   float *w = static_cast<float *>(workspace);
   a.ws_h = w;
   a.ws_dh = a.ws_h + nblk * Dk * Dk;
   a.ws_u = a.ws_dh + nblk * Dk * Dk;
-  a.ws_dy = a.ws_u + nblk * gdr::kBwdChunk * Dk;
+  a.ws_dy = a.ws_u + nblk * C * Dk;
   a.stream = stream;
-  hipError_t e = gdr::launch_chunk_bwd_passes(a);
-  if (e == hipSuccess) e = gdr::launch_chunk_bwd_grads(a);
+  const bool kda = a.gate == GDR_GATE_CHANNEL;
+  hipError_t e = kda ? gdr::launch_chunk_bwd_kda_passes(a) : gdr::launch_chunk_bwd_passes(a);
+  if (e == hipSuccess) e = kda ? gdr::launch_chunk_bwd_kda_grads(a) : gdr::launch_chunk_bwd_grads(a);
   return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 SOURCES = ["abi.cpp", "passthrough.hip", "recurrent_step.hip", "chunk_fwd_bf16.hip",
-           "chunk_fwd_kda.hip", "chunk_fwd_small.hip", "chunk_bwd.hip",
+           "chunk_fwd_kda.hip", "chunk_fwd_small.hip", "chunk_bwd.hip", "chunk_bwd_kda.hip",
            "bwd_noalloc.hip"]
 ARCH = "gfx950"
 

@@ -86,21 +86,6 @@ __device__ __forceinline__ float dot8_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf1
   return acc;
 }
 
-// sum over the 16 lanes of each row of a wave (lanes 16 j .. 16 j + 15)
-__device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
-}
-__device__ __forceinline__ float sum64(float x) {
-  x = sum16(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
 template <int DK, int GATE, bool ERASE>
 __global__ void __launch_bounds__(64 * NW, 2)
 chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,

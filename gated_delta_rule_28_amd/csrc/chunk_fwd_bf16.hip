@@ -96,7 +96,6 @@ constexpr int NIN = 5;     // input slots: chunk j DMA'd from iteration j-3, las
 constexpr int NPR = 3;     // P slots: chunk j written in iteration j-1, read in j+1
 constexpr int NTS = 2;     // T slots: chunk j written in iteration j, read in j+1
 
-enum Mode { kModeFwd = 0, kModeRec = 1, kModeRev = 2 };
 
 // Inclusive prefix sum over lanes 0..31 of a wave with DPP row shifts
 // (within 16-lane rows) and a row broadcast of lane 15 into the next row.
@@ -1041,10 +1040,12 @@ bool chunk_fwd_bf16_supported(const ChunkArgs &a) {
 }
 
 bool chunk_bwd_supported(int D, bool in_bf16, int gate, bool erase, long H) {
+  // the per-chunk buffer descriptors (of the widest rows: fp32 [*, H, D]) are
+  // 32-bit; the bound of the 32-token chunk covers the 16-token one too
   const long chunk_bytes = (long)4 * ((long)(C - 1) * H * D + D);
   (void)erase;   // both forms: with the erase term and without (additive write)
-  return in_bf16 && (D == 128 || D == 64) && (gate == kGateNone || gate == kGateScalar) &&
-         chunk_bytes < 0xFFFFFFFFL;
+  return in_bf16 && (D == 128 || D == 64) && chunk_bytes < 0xFFFFFFFFL &&
+         (gate == kGateNone || gate == kGateScalar || gate == kGateChannel);
 }
 
 hipError_t launch_chunk_bwd_passes(const BwdArgs &a) {

@@ -54,6 +54,19 @@
 //   of its rows each
 // Raw inputs live four iterations (DMA to derivation), derived operands
 // three, v three, T' and P two.
+//
+// Backward passes (template MODE).  kModeRec recomputes the forward and
+// stores, per chunk, the entering state h and U (no outputs, no scores);
+// kModeRev walks the chunks in reverse with v = dO and the state gradient X
+// (the gradient of the state leaving the chunk; dS_T in, dS_0 out) in the
+// accumulators, the adjoint of the lines above:
+//
+//   Y1  = Diag(e^{g_last}) X                     (the exact path: Y1 = X)
+//   dU  = R^ Y1 + P^T dO,   dY = T^T dU          (T = (I + A)^{-1}, unscaled)
+//   X  <- Y1 + Q^ ^T dO - K^ ^T diag(b) dY      (the exact path: e^{g_last} o Y1)
+//
+// storing X and dY per chunk; the solver stores T instead of T' in that mode.
+// The chunk-parallel kernel (chunk_bwd_kda.hip) forms the token gradients.
 #include <cstddef>
 #include <type_traits>
 
@@ -107,13 +120,16 @@ struct __align__(16) KdaSmem {
   float At[KC][LDX];                      // -A^T of the chunk being solved
 };
 
-template <int DK, int DVS, typename OutT, bool ERASE, bool FUSED>
+// ws_a, ws_b: the backward passes' per-chunk stores ([chain][chunk] of
+// [DK][DV] and [KC][DV] fp32): h and U (kModeRec), X and dY (kModeRev)
+template <int DK, int DVS, typename OutT, bool ERASE, bool FUSED, int MODE>
 __global__ void __launch_bounds__(64 * (DVS / 16 + kda_npw<DVS>()), 1)
 chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ beta,
                      const float *__restrict__ log_alpha, const float *initial_state,
                      OutT *__restrict__ o, float *final_state, int B, int T, int H, int fuse,
-                     const bf16 *__restrict__ out_gate) {
+                     const bf16 *__restrict__ out_gate, float *__restrict__ ws_a,
+                     float *__restrict__ ws_b) {
   constexpr int NSW = DVS / 16;
   constexpr int DV = DK;
   constexpr int NSLICE = DV / DVS;
@@ -121,6 +137,9 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int QB = DK / 8, VB = DVS / 8;      // 16-byte blocks per q/k and v row
   constexpr int QRB = 2 * DK, VRB = 2 * DVS;    // bytes per q/k and v row
   static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
+  static_assert(MODE == kModeFwd || !FUSED, "the backward passes take no fused options");
+  constexpr bool WANT_O = MODE == kModeFwd;    // outputs (Q^ S, P U, o)
+  constexpr bool WANT_P = MODE != kModeRec;    // Q^ and the P tiles
   // calls without a fused prologue or epilogue compile without their code
   if constexpr (!FUSED) {
     fuse = 0;
@@ -154,6 +173,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   const int bb = chain / H, hh = chain % H;
   const int nchunks = (T + KC - 1) / KC;
   const long tok0 = (long)bb * T * H + hh;   // token row of token 0 of this chain
+  // the sequence chunk of pipeline position j (the reverse pass runs last to first)
+  auto chunk_of = [&](int j) { return MODE == kModeRev ? nchunks - 1 - j : j; };
 
   // byte offset inside a derived tile of row r, natural 16-byte block b
   auto qk_at = [](int r, int b) { return r * QRB + 16 * (b ^ swz_qk<QB>(r)); };
@@ -182,7 +203,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   auto xform = [&](int j, int pb, auto np_) {
     constexpr int NP = decltype(np_)::value;
     typename SM::Raw &rw = *at_off(&sm.raw[0], slot_off(j % NRAW, (int)sizeof(typename SM::Raw)));
-    const int n = min(KC, T - j * KC);
+    const int n = min(KC, T - chunk_of(j) * KC);
     const int c0 = 2 * (lane % NCPX), r0 = TPRX * pb + lane / NCPX;
     const bool gla = (fuse & kFuseGla) != 0;
     f32x2 x[NP];
@@ -282,18 +303,22 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // would otherwise start every chunk's serial products with an LDS round
     // trip.  Before the first chunk (and past the last) they read a slot
     // that is not used, which is harmless.
+    // (The reverse pass reads R^ into the K^ registers: its first product is
+    // R^ Y1.)
     bf16x8 fkh[KKD], fkl[KKD], fqh[KKD], fql[KKD];
     auto load_kq = [&](int c) {
       const typename SM::Der &d = *at_off(&sm.der[0], slot_off(c % NDER, (int)sizeof(typename SM::Der)));
-      const char *Kh = reinterpret_cast<const char *>(&d.Kh[0][0]);
-      const char *Kl = reinterpret_cast<const char *>(&d.Kl[0][0]);
+      const char *Kh = reinterpret_cast<const char *>(MODE == kModeRev ? &d.Rh[0][0] : &d.Kh[0][0]);
+      const char *Kl = reinterpret_cast<const char *>(MODE == kModeRev ? &d.Rl[0][0] : &d.Kl[0][0]);
       const char *Qh = reinterpret_cast<const char *>(&d.Qh[0][0]);
       const char *Ql = reinterpret_cast<const char *>(&d.Ql[0][0]);
 #pragma unroll
       for (int kk = 0; kk < KKD; ++kk) {
-        fqh[kk] = ld8(reinterpret_cast<const bf16 *>(Qh + kq_off[kk]));
-        fql[kk] = ld8(reinterpret_cast<const bf16 *>(Ql + kq_off[kk]));
-        if constexpr (ERASE) {
+        if constexpr (WANT_O) {
+          fqh[kk] = ld8(reinterpret_cast<const bf16 *>(Qh + kq_off[kk]));
+          fql[kk] = ld8(reinterpret_cast<const bf16 *>(Ql + kq_off[kk]));
+        }
+        if constexpr (ERASE || MODE == kModeRev) {
           fkh[kk] = ld8(reinterpret_cast<const bf16 *>(Kh + kq_off[kk]));
           fkl[kk] = ld8(reinterpret_cast<const bf16 *>(Kl + kq_off[kk]));
         }
@@ -314,16 +339,107 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) og_next[e] = buf_ld_u16(rg, 2u * oel[e]);
       }
-      if (s >= 0) {
+      if (MODE == kModeRev && s >= 0) {
+        const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));
+        const int t1 = slot_off(s & 1, (int)sizeof(sm.Th[0]));
+        const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
+        const int c = nchunks - 1 - s;   // chunks run last to first
+        // X, the gradient of the state leaving chunk c
+        float *xp = ws_a + ((long)chain * nchunks + c) * (DK * DV);
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_nontemporal_store(Sacc[mb][e], xp + (long)srow(mb, e) * DV + col0 + lr);
+        // Y1 = X times the factor the forward applied after its update
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb)
+          Sacc[mb] = Sacc[mb] * *reinterpret_cast<const f32x4 *>(&d.egp[srow(mb, 0)]);
+        split_state();
+        // ---- dU = R^ Y1 + P^T dO (R^ rows in the K^ registers) ----
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KKD; ++kk) {
+          a1 = mfma_bf16(fkh[kk], Sh[kk], a1);
+          a1 = mfma_bf16(fkh[kk], Sl[kk], a1);
+          a1 = mfma_bf16(fkl[kk], Sh[kk], a1);
+        }
+        // dO rows 4 lg + c of this lane's column (the v slot holds dO)
+        const bf16x4 dov = ld_tr4(reinterpret_cast<const bf16 *>(
+            reinterpret_cast<const char *>(&sm.V[0][0][0]) + slot_off(s % NVB, (int)sizeof(sm.V[0])) + v_off));
+        // row lr of P^T is row lr of the stored tile; dO is exact bf16
+        const bf16x8 pa = cat(*reinterpret_cast<const bf16x4 *>(&at_off(&sm.Ph[0][0], t1)[lr][4 * lg]),
+                              *reinterpret_cast<const bf16x4 *>(&at_off(&sm.Pl[0][0], t1)[lr][4 * lg]));
+        f32x4 du = mfma_bf16(pa, cat(dov, dov), a1);
+        // ---- dY = T^T dU (without the erase term T = I) ----
+        f32x4 y = du;
+        if constexpr (ERASE) {
+          bf16x4 duh, dul;
+          split4(du, duh, dul);
+          const bf16x8 ta = cat(*reinterpret_cast<const bf16x4 *>(&at_off(&sm.Th[0][0], t1)[lr][4 * lg]),
+                                *reinterpret_cast<const bf16x4 *>(&at_off(&sm.Tl[0][0], t1)[lr][4 * lg]));
+          y = f32x4{0.f, 0.f, 0.f, 0.f};
+          y = mfma_bf16(ta, cat(duh, duh), y);
+          y = mfma_bf16(ta, cat(dul, zero4), y);
+        }
+        float *yp = ws_b + ((long)chain * nchunks + c) * (KC * DV);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_nontemporal_store(y[e], yp + (4 * lg + e) * DV + col0 + lr);
+        // ---- X <- Y1 + Q^ ^T dO - K^ ^T diag(b) dY (the exact path: e^{g_last} o Y1) ----
+        if (exact) {
+#pragma unroll
+          for (int mb = 0; mb < DK / 16; ++mb)
+            Sacc[mb] = Sacc[mb] * *reinterpret_cast<const f32x4 *>(&d.egl[srow(mb, 0)]);
+        }
+        bf16x4 drh = zero4, drl = zero4;
+        if constexpr (ERASE) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&d.beta[4 * lg]);
+          split4(-(b4 * y), drh, drl);
+        }
+        const bf16x8 bq = cat(dov, dov), bk1 = cat(drh, drh), bk2 = cat(drl, zero4);
+        const char *Qh = reinterpret_cast<const char *>(&d.Qh[0][0]);
+        const char *Ql = reinterpret_cast<const char *>(&d.Ql[0][0]);
+        const char *Kh = reinterpret_cast<const char *>(&d.Kh[0][0]);
+        const char *Kl = reinterpret_cast<const char *>(&d.Kl[0][0]);
+#pragma unroll
+        for (int mb = 0; mb < DK / 16; ++mb) {
+          const int off = kt_off[mb >> 1] + 8 * (mb & 1);
+          const bf16x8 aq = cat(ld_tr4(reinterpret_cast<const bf16 *>(Qh + off)),
+                                ld_tr4(reinterpret_cast<const bf16 *>(Ql + off)));
+          f32x4 acc = mfma_bf16(aq, bq, Sacc[mb]);
+          if constexpr (ERASE) {
+            const bf16x8 ak = cat(ld_tr4(reinterpret_cast<const bf16 *>(Kh + off)),
+                                  ld_tr4(reinterpret_cast<const bf16 *>(Kl + off)));
+            acc = mfma_bf16(ak, bk1, acc);
+            acc = mfma_bf16(ak, bk2, acc);
+          }
+          Sacc[mb] = acc;
+        }
+      }
+      if (MODE != kModeRev && s >= 0) {
         const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));
         const int t1 = slot_off(s & 1, (int)sizeof(sm.Th[0]));   // T' and P slots (same size)
         const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
+        if constexpr (MODE == kModeRec) {   // the state entering chunk s
+          float *hp = ws_a + ((long)chain * nchunks + s) * (DK * DV);
+#pragma unroll
+          for (int mb = 0; mb < DK / 16; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              __builtin_nontemporal_store(Sacc[mb][e], hp + (long)srow(mb, e) * DV + col0 + lr);
+        }
         // ---- K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KKD; ++kk) {
           const bf16x8 qh = fqh[kk], ql = fql[kk];
-          if constexpr (ERASE) {
+          if constexpr (ERASE && !WANT_O) {
+            const bf16x8 kh = fkh[kk], kl = fkl[kk];
+            a1 = mfma_bf16(kh, Sh[kk], a1);
+            a1 = mfma_bf16(kh, Sl[kk], a1);
+            a1 = mfma_bf16(kl, Sh[kk], a1);
+          } else if constexpr (ERASE) {
             const bf16x8 kh = fkh[kk], kl = fkl[kk];
             a1 = mfma_bf16(kh, Sh[kk], a1);
             a2 = mfma_bf16(qh, Sh[kk], a2);
@@ -331,7 +447,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             a2 = mfma_bf16(qh, Sl[kk], a2);
             a1 = mfma_bf16(kl, Sh[kk], a1);
             a2 = mfma_bf16(ql, Sh[kk], a2);
-          } else {
+          } else if constexpr (WANT_O) {
             a2 = mfma_bf16(qh, Sh[kk], a2);
             a2 = mfma_bf16(qh, Sl[kk], a2);
             a2 = mfma_bf16(ql, Sh[kk], a2);
@@ -353,6 +469,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           u = mfma_bf16(ta, cat(rh4, rh4), u);
           u = mfma_bf16(ta, cat(rl4, zero4), u);
           split4(u, uh4, ul4);
+          rr = u;
         } else {
           // no erase term: U = diag(b) V
           const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&d.beta[4 * lg]);
@@ -360,8 +477,15 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int e = 0; e < 4; ++e) rr[e] = b4[e] * (float)vv[e];
           split4(rr, uh4, ul4);
         }
+        if constexpr (MODE == kModeRec) {   // U of chunk s (rr holds it on both paths)
+          float *up = ws_b + ((long)chain * nchunks + s) * (KC * DV);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_nontemporal_store(rr[e], up + (4 * lg + e) * DV + col0 + lr);
+        }
 
         // ---- O = Q^ S + P U ----
+       if constexpr (WANT_O) {
         const int t0 = s * KC, n = min(KC, T - t0);
         const bf16x8 pa = cat(ld_tr4(&at_off(&sm.Ph[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]),
                               ld_tr4(&at_off(&sm.Pl[0][0], t1)[4 * lg + (lr >> 2)][4 * (lr & 3)]));
@@ -380,6 +504,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int e = 0; e < 4; ++e)
             if (4 * lg + e < n) buf_st1(from_f32<OutT>(acc[e]), ro, ooff[e]);
         }
+       }
 
         // ---- S <- Diag(e^{g_last}) (S + R^T U) (exact path: factor first) ----
         // The exact path's factor is a wave-uniform branch taken only by
@@ -494,9 +619,10 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
                          : "+v"(x[r]) : "v"(na[r]), "v"(x[s2]), "i"(s2));
         }
-        // T'^T[col][r] = T[r][col] b_col, hi/lo (lanes 16..63 hold duplicates)
+        // T'^T[col][r] = T[r][col] b_col, hi/lo (lanes 16..63 hold duplicates);
+        // the reverse pass takes T^T itself (b_col = 1)
         if (lane < 16) {
-          const float bcol = d.beta[col];
+          const float bcol = MODE == kModeRev ? 1.0f : d.beta[col];
           unsigned h8[2][4], l8[2][4];
 #pragma unroll
           for (int r = 0; r < 16; r += 2)
@@ -550,8 +676,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   // q, k, log a and b of chunk j (waves 0 and 1)
   auto issue_raw = [&](int j) {
     typename SM::Raw &dst = sm.raw[j % NRAW];
-    const int n = min(KC, T - j * KC);
-    const long row0 = tok0 + (long)j * KC * H;
+    const int n = min(KC, T - chunk_of(j) * KC);
+    const long row0 = tok0 + (long)chunk_of(j) * KC * H;
     if (pw == 0) {
       const u32x4 rl = rsrc_words(log_alpha + row0 * DK, 4u * ((unsigned)(n - 1) * H * DK + DK));
       const unsigned ll = lds_addr(&dst.G[0][0]);
@@ -570,8 +696,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   };
   // v of chunk j, this slice's columns (wave 2)
   auto issue_v = [&](int j) {
-    const int n = min(KC, T - j * KC);
-    const long row0 = tok0 + (long)j * KC * H;
+    const int n = min(KC, T - chunk_of(j) * KC);
+    const long row0 = tok0 + (long)chunk_of(j) * KC * H;
     const u32x4 rv = rsrc_words(v + row0 * DV, 2u * ((unsigned)(n - 1) * H * DV + DV));
     const unsigned lv = lds_addr(&sm.V[j % NVB][0][0]);
 #pragma unroll
@@ -685,7 +811,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         *reinterpret_cast<f32x2 *>(&d.egl[c0]) = eg;
         *reinterpret_cast<f32x2 *>(&d.egp[c0]) = exact ? f32x2{1.0f, 1.0f} : eg;
       }
-      if (lane < KC) d.beta[lane] = (lane < min(KC, T - j * KC)) ? fused_beta(rw.beta[lane], fuse) : 0.0f;
+      if (lane < KC) d.beta[lane] = (lane < min(KC, T - chunk_of(j) * KC)) ? fused_beta(rw.beta[lane], fuse) : 0.0f;
       if (lane == 0) d.flag[0] = exact;
     }
     const int rb0 = row_bound(dw), rb1 = row_bound(dw + 1);
@@ -717,7 +843,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const float f0 = __builtin_amdgcn_exp2f(EX ? gl[0] - g[0] : -g[0]) * rk;
         const float f1 = __builtin_amdgcn_exp2f(EX ? gl[1] - g[1] : -g[1]) * rk;
         if constexpr (ERASE) put(d.Kh, d.Kl, r, k0 * (x0 * rk), k1 * (x1 * rk));   // K^ feeds only K^ S and A
-        put(d.Qh, d.Ql, r, q0 * (x0 * rq), q1 * (x1 * rq));
+        if constexpr (WANT_P) put(d.Qh, d.Ql, r, q0 * (x0 * rq), q1 * (x1 * rq));
         put(d.Rh, d.Rl, r, k0 * f0, k1 * f1);
       }
     };
@@ -740,7 +866,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           sa *= rw.nrm[1][r] * rw.nrm[1][s];
           sp *= rw.nrm[0][r] * rw.nrm[1][s];
         }
-        const float br = (r < min(KC, T - j * KC)) ? fused_beta(rw.beta[r], fuse) : 0.0f;
+        const float br = (r < min(KC, T - chunk_of(j) * KC)) ? fused_beta(rw.beta[r], fuse) : 0.0f;
         if constexpr (ERASE) sm.xA[j & 1][s][r] = (s < r) ? -br * sa : 0.0f;
         sm.xP[j & 1][s][r] = sp;
       }
@@ -808,7 +934,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       const bool more = it < nchunks;
       if (pw == PW_V && more) issue_v(it);
       if (l2 && it + 1 < nchunks) norms(it + 1, gsum_idx);
-      if (pw == 2 && it >= 1 && it - 1 < nchunks) scores(it - 1);
+      if (WANT_P && pw == 2 && it >= 1 && it - 1 < nchunks) scores(it - 1);
       if (it < nchunks) derive(it);
       if (xf && xpart && it + 2 < nchunks) xform_share(it + 2);
       if (pw == PW_V) wait_own(more);
@@ -821,11 +947,34 @@ template <int DK, int DVS, typename OutT, bool ERASE, bool FUSED>
 hipError_t launch_kda_fused(const ChunkArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
-  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT, ERASE, FUSED>), grid, block, 0, a.stream,
-                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,
-                     a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H, a.fuse,
-                     (const bf16 *)a.out_gate);
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT, ERASE, FUSED, kModeFwd>), grid, block, 0,
+                     a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,
+                     a.log_alpha, a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H,
+                     a.fuse, (const bf16 *)a.out_gate, nullptr, nullptr);
   return hipGetLastError();
+}
+
+// the backward's two sequential passes at one tile configuration
+template <int DK, int DVS, bool ERASE>
+hipError_t launch_kda_passes(const BwdArgs &a) {
+  const int nslice = DK / DVS;
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, float, ERASE, false, kModeRec>), grid, block, 0,
+                     a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,
+                     a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0, nullptr,
+                     a.ws_h, a.ws_u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, float, ERASE, false, kModeRev>), grid, block, 0,
+                     a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.d_o, a.beta,
+                     a.log_alpha, a.d_final_state, nullptr, a.d_initial_state, a.B, a.T, a.H, 0,
+                     nullptr, a.ws_dh, a.ws_dy);
+  return hipGetLastError();
+}
+
+template <int DK, int DVS>
+hipError_t kda_passes_by_erase(const BwdArgs &a) {
+  return a.erase ? launch_kda_passes<DK, DVS, true>(a) : launch_kda_passes<DK, DVS, false>(a);
 }
 
 template <int DK, int DVS, typename OutT, bool ERASE>
@@ -847,6 +996,18 @@ bool chunk_fwd_kda_supported(const ChunkArgs &a) {
   // are 32-bit
   return a.in_bf16 && (a.D == 128 || a.D == 64) && a.gate == kGateChannel &&
          4.0 * ((double)(KC - 1) * a.H * a.D + a.D) < 4294967295.0;
+}
+
+hipError_t launch_chunk_bwd_kda_passes(const BwdArgs &a) {
+  static_assert(KC == kBwdChunkKda, "the workspace holds this kernel's chunks");
+  // the forward's launch shapes
+  const long chains = (long)a.B * a.H;
+  if (a.D == 128) {
+    if (chains * 2 >= 256) return kda_passes_by_erase<128, 64>(a);
+    return kda_passes_by_erase<128, 32>(a);
+  }
+  if (chains >= 256) return kda_passes_by_erase<64, 64>(a);
+  return kda_passes_by_erase<64, 32>(a);
 }
 
 hipError_t launch_chunk_fwd_kda(const ChunkArgs &a) {

@@ -48,13 +48,15 @@ bool chunk_fwd_small_supported(const ChunkArgs &a);
 // zero or copy the state for T == 0
 hipError_t launch_state_passthrough(const float *src, float *dst, long count, hipStream_t stream);
 
-// ---- backward of the chunk forward (bf16 q/k/v/dO, D = 64 or 128, no gate
-//      or the scalar gate, with or without the erase term) ----
-constexpr int kBwdChunk = 32;   // tokens per chunk of the passes and of the workspace
+// ---- backward of the chunk forward (bf16 q/k/v/dO, D = 64 or 128, every
+//      gate, with or without the erase term) ----
+constexpr int kBwdChunk = 32;      // tokens per chunk of the passes and of the workspace
+constexpr int kBwdChunkKda = 16;   // the same with the per-channel gate
+inline int bwd_chunk(int gate) { return gate == 2 ? kBwdChunkKda : kBwdChunk; }
 
 struct BwdArgs {
   int B, T, H, D;
-  int gate;                     // kGateNone or kGateScalar
+  int gate;                     // kGateNone, kGateScalar or kGateChannel
   bool erase;                   // false: the additive write (no erase term)
   const void *q, *k, *v;
   const float *beta, *log_alpha;
@@ -69,12 +71,17 @@ struct BwdArgs {
 };
 
 // workspace floats per (chain, chunk): h and dh [D][D], U and dY [C][D]
-inline long bwd_ws_floats_per_chunk(int D) { return 2L * D * D + 2L * kBwdChunk * D; }
+inline long bwd_ws_floats_per_chunk(int D, int gate) {
+  return 2L * D * D + 2L * bwd_chunk(gate) * D;
+}
 bool chunk_bwd_supported(int D, bool in_bf16, int gate, bool erase, long H);
 // the two sequential passes: the forward recomputed (h, U per chunk), then
 // the reverse pass (dh, dY per chunk, and dS_0)
 hipError_t launch_chunk_bwd_passes(const BwdArgs &a);
 // the chunk-parallel gradients dq, dk, dv, dbeta, dlog_alpha
 hipError_t launch_chunk_bwd_grads(const BwdArgs &a);
+// the same two steps with the per-channel gate (16-token chunks)
+hipError_t launch_chunk_bwd_kda_passes(const BwdArgs &a);
+hipError_t launch_chunk_bwd_kda_grads(const BwdArgs &a);
 
 }  // namespace gdr

@@ -293,4 +293,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// sum over the 16 lanes of each row of a wave (lanes 16 j .. 16 j + 15)
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+__device__ __forceinline__ float sum64(float x) {
+  x = sum16(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
 }  // namespace gdr

@@ -205,10 +205,15 @@ def test_backward_workspace_size():
     # the erase-free forms keep the same partitions (U holds b o V there)
     assert bwd_ws(gate=_abi.GDR_GATE_SCALAR | _abi.GDR_NO_ERASE) == bwd_ws()
     assert bwd_ws(gate=_abi.GDR_GATE_NONE | _abi.GDR_NO_ERASE) == bwd_ws()
+    # the per-channel gate: 16-token chunks, the same partitions per chunk
+    per16 = 4 * (2 * 128 * 128 + 2 * 16 * 128)
+    assert bwd_ws(gate=_abi.GDR_GATE_CHANNEL) == 8 * 16 * 256 * per16
+    assert bwd_ws(gate=_abi.GDR_GATE_CHANNEL, T=17) == 8 * 16 * 2 * per16
+    assert bwd_ws(gate=_abi.GDR_GATE_CHANNEL | _abi.GDR_NO_ERASE) == \
+        bwd_ws(gate=_abi.GDR_GATE_CHANNEL)
     assert bwd_ws(D=64, T=64, B=1, H=1) == 2 * 4 * (2 * 64 * 64 + 2 * 32 * 64)
     # unsupported calls and empty inputs need none
-    for kw in (dict(in_dtype=_abi.GDR_F32), dict(gate=_abi.GDR_GATE_CHANNEL), dict(D=32),
-               dict(gate=_abi.GDR_GATE_CHANNEL | _abi.GDR_NO_ERASE), dict(T=0), dict(B=0),
+    for kw in (dict(in_dtype=_abi.GDR_F32), dict(D=32), dict(T=0), dict(B=0),
                dict(chunk=48), dict(gate=9)):
         assert bwd_ws(**kw) == 0, kw
 
@@ -237,8 +242,6 @@ def bwd(**kw):
     (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
     (dict(Dk=32, Dv=32), _abi.GDR_EUNSUPPORTED),
     (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
-    (dict(gate=_abi.GDR_GATE_CHANNEL), _abi.GDR_EUNSUPPORTED),
-    (dict(gate=_abi.GDR_GATE_CHANNEL | _abi.GDR_NO_ERASE), _abi.GDR_EUNSUPPORTED),
     (dict(H=300000), _abi.GDR_EUNSUPPORTED),
     (dict(workspace=None), _abi.GDR_EWORKSPACE),
     (dict(workspace=FAKE + 16), _abi.GDR_EWORKSPACE),          # not 256-byte aligned
@@ -275,5 +278,5 @@ def test_noalloc_backward_refuses_more_than_its_array():
     # invalid and empty calls: the usual statuses, nothing launched
     assert _abi.gdr_chunk_bwd_noalloc(**dict(a, B=-1)) == _abi.GDR_EINVAL
     assert _abi.gdr_chunk_bwd_noalloc(**dict(a, B=0, q=None)) == _abi.GDR_OK
-    assert _abi.gdr_chunk_bwd_noalloc(**dict(a, gate=_abi.GDR_GATE_CHANNEL)) == \
+    assert _abi.gdr_chunk_bwd_noalloc(**dict(a, in_dtype=_abi.GDR_F32)) == \
         _abi.GDR_EUNSUPPORTED

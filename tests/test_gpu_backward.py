@@ -198,3 +198,63 @@ def test_backward_erase_free_differs_from_the_erase_form():
     ref = oracle(inp, erase=True)
     assert rel_err(f64(b["dk"]), ref["dk"]) <= TOL
     assert rel_err(f64(a["dk"]), ref["dk"]) > 0.05
+
+
+# The per-channel gate (KDA; without the erase term GLA's decay): 16-token
+# chunks through the KDA kernel's recompute and reverse passes and its own
+# gradient kernel.
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 16, 17, 40, 100])
+def test_backward_kda(D, T):
+    say("bwd kda", D, T)
+    inp = make_case(2, T, 2, D, "channel", seed=5 * T + D)
+    check_all(run_gpu(inp), oracle(inp), "channel")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T", [1, 33, 100])
+def test_backward_kda_erase_free(D, T):
+    say("bwd gla decay", D, T)
+    inp = make_case(2, T, 2, D, "channel", seed=7 * T + D)
+    check_all(run_gpu(inp, erase=False), oracle(inp, erase=False), "channel")
+
+
+@pytest.mark.parametrize("erase", [True, False])
+def test_backward_kda_exact_path(erase):
+    """Chunks where some channel's in-chunk log decay falls below -64 (and a
+    hard reset of one channel), which take the directly formed decays."""
+    say("bwd kda exact path", erase)
+    inp = make_case(2, 70, 2, 128, "channel", seed=23)
+    la = inp["log_alpha"].clone()
+    la[0, 16:32, :, :8] = -6.0     # a whole chunk 96 below on eight channels
+    la[1, 40, 1, 5] = -80.0        # one channel reset mid-chunk
+    la[1, 50:60, 0, 100:] = -9.0   # part of a chunk, strong
+    inp["log_alpha"] = la
+    check_all(run_gpu(inp, erase=erase), oracle(inp, erase=erase), "channel")
+
+
+@pytest.mark.parametrize("D,B,H", [(128, 2, 32), (128, 4, 32), (64, 8, 32)])
+def test_backward_kda_many_chains(D, B, H):
+    """Both slice widths of the passes (32 columns below 128 chains at d = 128,
+    64 above), sampled chains against the oracle."""
+    say("bwd kda many chains", D, B, H)
+    inp = make_case(B, 37, H, D, "channel", seed=11)
+    got = run_gpu(inp)
+    chains = [(0, 0), (B - 1, H - 1), (B // 2, 7)]
+    refs = oracle(inp, chains=chains)
+    for (b, h), ref in zip(chains, refs):
+        sub = {n: (got[n][b:b + 1, :, h:h + 1] if n != "dS0" else got[n][b:b + 1, h:h + 1])
+               for n in NAMES}
+        check_all(sub, ref, "channel")
+
+
+def test_backward_kda_no_state_gradients_and_determinism():
+    say("bwd kda no S0 / no dS_T, determinism")
+    inp = make_case(1, 50, 3, 64, "channel", seed=3, s0=False, dst=False)
+    a = run_gpu(inp)
+    check_all(a, oracle(inp), "channel")
+    b = run_gpu(inp)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
