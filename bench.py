@@ -562,12 +562,15 @@ def sampled_parity(torch, W, kept, chains, tol=PARITY_TOL):
 def bwd_alg_bytes(w):
     """Single-pass minimum HBM bytes of one chunk_bwd call (zero initial state,
     no loss on the final state, dS_0 written): q, k, v, dO in (input dtype),
-    beta and log alpha in, dq, dk, dv (fp32) out, dbeta and dlog alpha out."""
+    beta and log alpha in, dq, dk, dv (fp32) out, dbeta and dlog alpha out
+    (log alpha and its gradient per channel with the per-channel gate)."""
     th = w.B * w.T * w.H
     in_b = 2 if w.in_dtype == "bf16" else 4
     per_th = in_b * (2 * w.Dk + 2 * w.Dv) + 4 + 4 * (2 * w.Dk + w.Dv) + 4
     if w.gate == "scalar":
         per_th += 8
+    elif w.gate == "channel":
+        per_th += 8 * w.Dk
     return th * per_th + w.B * w.H * w.Dk * w.Dv * 4
 
 
@@ -587,7 +590,8 @@ def bwd_line(torch, gdr, W, w, steps, warmup, settle_s=0.0, chains=((0, 0), (7, 
     f32 = dict(device="cuda", dtype=torch.float32)
     out = {"dq": torch.empty(w.B, w.T, w.H, w.Dk, **f32), "dk": torch.empty(w.B, w.T, w.H, w.Dk, **f32),
            "dv": torch.empty(w.B, w.T, w.H, w.Dv, **f32), "dbeta": torch.empty(w.B, w.T, w.H, **f32),
-           "dlog_alpha": None if inp["log_alpha"] is None else torch.empty(w.B, w.T, w.H, **f32),
+           "dlog_alpha": (None if inp["log_alpha"] is None
+                          else torch.empty(*inp["log_alpha"].shape, **f32)),
            "d_initial_state": torch.empty(w.B, w.H, w.Dk, w.Dv, **f32)}
 
     def step():
@@ -615,8 +619,11 @@ def bwd_line(torch, gdr, W, w, steps, warmup, settle_s=0.0, chains=((0, 0), (7, 
     return {
         "workload": w.name, "unit": "tokens/s", "value": w.B * w.T / (mean_ms * 1e-3),
         "kernel_ms": {"mean": mean_ms, "median": statistics.median(per), "min": min(per)},
-        "kernels": "chunk_fwd_bf16_kernel <.., mode 1> (recompute), <.., mode 2> (reverse), "
-                   "chunk_bwd_grad_kernel (token gradients): one event pair around the three",
+        "kernels": ("chunk_fwd_kda_kernel <.., mode 1> (recompute), <.., mode 2> (reverse), "
+                    "chunk_bwd_kda_kernel (token gradients): one event pair around the three"
+                    if w.gate == "channel" else
+                    "chunk_fwd_bf16_kernel <.., mode 1> (recompute), <.., mode 2> (reverse), "
+                    "chunk_bwd_grad_kernel (token gradients): one event pair around the three"),
         "workspace_bytes": int(ws.numel()),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "alg_bytes_per_launch": alg_b,
@@ -971,6 +978,8 @@ def main(argv=None):
         rec["decode"]["parity"] = decode_parity(torch, W, W.DECODE)
         rec.update(small_lines(torch, gdr, W, args.settle_s))
         rec["backward"] = bwd_line(torch, gdr, W, w, nb, 2, args.settle_s)
+        rec["kda_backward"] = bwd_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2,
+                                       args.settle_s, chains=((0, 0), (1, 31)))
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -184,8 +184,10 @@ size_t gdr_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
  * gdr_chunk_bwd_workspace_bytes -- device workspace gdr_chunk_bwd needs for
  * these arguments: per (batch, head) chain and 32-token chunk, two Dk x Dv
  * fp32 states and two 32 x Dv fp32 tiles, 4 (2 Dk Dv + 64 Dv) bytes (2.5 GiB
- * for B = 8, H = 16, T = 4096, Dk = Dv = 128).  0 when the call is not
- * supported or has no tokens.
+ * for B = 8, H = 16, T = 4096, Dk = Dv = 128); with GDR_GATE_CHANNEL the
+ * chunk is 16 tokens, 4 (2 Dk Dv + 32 Dv) bytes per chain and chunk (4.5 GiB
+ * for B = 2, H = 32, T = 8192).  0 when the call is not supported or has no
+ * tokens.
  */
 size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk,
                                      int in_dtype, int gate);
@@ -200,15 +202,16 @@ size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
  *
  *   B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
  *   initial_state  exactly as passed to gdr_chunk_fwd.  Supported: bf16
- *                 q/k/v, Dk == Dv in {64, 128}, GDR_GATE_NONE or
- *                 GDR_GATE_SCALAR, with or without GDR_NO_ERASE (others
- *                 return GDR_EUNSUPPORTED)
+ *                 q/k/v, Dk == Dv in {64, 128}, every gate, with or
+ *                 without GDR_NO_ERASE (others return GDR_EUNSUPPORTED)
  *   d_o           [B, T, H, Dv] in_dtype, dL/do
  *   d_final_state [B, H, Dk, Dv] fp32, or NULL for zero
  *   dq, dk        [B, T, H, Dk] fp32 (written)
  *   dv            [B, T, H, Dv] fp32 (written)
  *   dbeta         [B, T, H] fp32 (written)
- *   dlog_alpha    [B, T, H] fp32 (written); NULL iff gate == GDR_GATE_NONE
+ *   dlog_alpha    shaped like log_alpha ([B, T, H], or [B, T, H, Dk] with
+ *                 GDR_GATE_CHANNEL), fp32 (written); NULL iff gate ==
+ *                 GDR_GATE_NONE
  *   d_initial_state [B, H, Dk, Dv] fp32 (written), or NULL (not written)
  *   workspace     device memory of at least gdr_chunk_bwd_workspace_bytes,
  *                 256-byte aligned, owned by the caller; its contents on entry
@@ -240,7 +243,8 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
  * on, held until the process ends); the call allocates nothing.  A call whose
  * gdr_chunk_bwd_workspace_bytes exceeds GDR_NOALLOC_SCRATCH_BYTES (64 MiB:
  * 409 chain-chunks of 32 tokens at Dk = Dv = 128, such as B = 1, H = 4,
- * T = 3264) returns GDR_EWORKSPACE and launches nothing.  Every call on a GPU
+ * T = 3264; 455 chain-chunks of 16 tokens with GDR_GATE_CHANNEL) returns
+ * GDR_EWORKSPACE and launches nothing.  Every call on a GPU
  * uses that GPU's one array: calls that overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller.  The array's
  * contents between calls are unspecified; nothing in them is read before

@@ -48,11 +48,13 @@ def case(B, T, H, D, gate, seed):
 
 def noalloc(inp):
     B, T, H, D = inp["q"].shape
-    gate = _abi.GDR_GATE_NONE if inp["log_alpha"] is None else _abi.GDR_GATE_SCALAR
+    la = inp["log_alpha"]
+    gate = (_abi.GDR_GATE_NONE if la is None else
+            _abi.GDR_GATE_CHANNEL if la.dim() == 4 else _abi.GDR_GATE_SCALAR)
     f32 = dict(device=DEV, dtype=torch.float32)
     out = {"dq": torch.empty(B, T, H, D, **f32), "dk": torch.empty(B, T, H, D, **f32),
            "dv": torch.empty(B, T, H, D, **f32), "dbeta": torch.empty(B, T, H, **f32),
-           "dlog_alpha": None if inp["log_alpha"] is None else torch.empty(B, T, H, **f32),
+           "dlog_alpha": None if la is None else torch.empty(*la.shape, **f32),
            "d_initial_state": torch.empty(B, H, D, D, **f32)}
     ptr = lambda t: None if t is None else t.data_ptr()
     st = _abi.gdr_chunk_bwd_noalloc(
@@ -69,7 +71,9 @@ def noalloc(inp):
 
 def test_noalloc_backward_equals_the_workspace_entry_point():
     # the second call is smaller: it runs on what the first left in the array
-    for B, T, H, D, gate, seed in ((2, 100, 3, 128, "scalar", 1), (1, 40, 2, 64, "none", 2)):
+    # (the per-channel gate's passes and gradient kernel too, on a third call)
+    for B, T, H, D, gate, seed in ((2, 100, 3, 128, "scalar", 1), (1, 40, 2, 64, "none", 2),
+                                   (1, 30, 2, 64, "channel", 3)):
         say("noalloc bwd", B, T, H, D, gate)
         inp = case(B, T, H, D, gate, seed)
         need = gdr.chunk_bwd_workspace_bytes(inp["q"], inp["log_alpha"])
