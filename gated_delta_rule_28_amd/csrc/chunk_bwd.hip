@@ -127,7 +127,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     const int dkt = 16 * (NTW * wave + nt);
 #pragma unroll
     for (int kk = 0; kk < KKV; ++kk) {
-      const long o = wsS + (long)(dkt + lr) * DV + 32 * kk + 8 * lg;
+      const long o = wsS + ws_state_off(DK, dkt + lr, 32 * kk + 8 * lg);   // 8 contiguous
       f.h[kk][0] = *reinterpret_cast<const f32x4 *>(ws_h + o);
       f.h[kk][1] = *reinterpret_cast<const f32x4 *>(ws_h + o + 4);
       f.g[kk][0] = *reinterpret_cast<const f32x4 *>(ws_dh + o);
@@ -173,7 +173,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     }
 #pragma unroll
     for (int j = 0; j < F4; ++j) {
-      const long o = wsR + r * DV + 4 * (f0 + j);
+      const long o = wsR + ws_tile_off(C, r, 4 * (f0 + j));
       u[j] = *reinterpret_cast<const f32x4 *>(ws_u + o);
       y[j] = *reinterpret_cast<const f32x4 *>(ws_dy + o);
       vr[j] = bf16x4{(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};

@@ -126,7 +126,7 @@ chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         la0 = *reinterpret_cast<const f32x4 *>(log_alpha + off);
         la1 = *reinterpret_cast<const f32x4 *>(log_alpha + off + 4);
       }
-      const long o = wsR + r * DV + c8;
+      const long o = wsR + ws_tile_off(C, r, c8);   // 8 contiguous
       const f32x4 u0 = *reinterpret_cast<const f32x4 *>(ws_u + o);
       const f32x4 u1 = *reinterpret_cast<const f32x4 *>(ws_u + o + 4);
       const f32x4 y0 = *reinterpret_cast<const f32x4 *>(ws_dy + o);
@@ -319,7 +319,7 @@ chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       f32x4 hf[KKV][2], gf[KKV][2];
 #pragma unroll
       for (int kk = 0; kk < KKV; ++kk) {
-        const long o = wsS + (long)ch * DV + 32 * kk + 8 * lg;
+        const long o = wsS + ws_state_off(DK, ch, 32 * kk + 8 * lg);   // 8 contiguous
         hf[kk][0] = *reinterpret_cast<const f32x4 *>(ws_h + o);
         hf[kk][1] = *reinterpret_cast<const f32x4 *>(ws_h + o + 4);
         gf[kk][0] = *reinterpret_cast<const f32x4 *>(ws_dh + o);

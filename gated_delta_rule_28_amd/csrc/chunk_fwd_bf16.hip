@@ -334,7 +334,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(Sacc[mb][e], dh + srow(mb, e) * DV + col0 + lr);
+            __builtin_nontemporal_store(Sacc[mb][e], dh + ws_frag(DK / 16, col0 >> 4, mb, e, lg, lr));
         // K dS
         f32x4 KS[2];
 #pragma unroll
@@ -393,7 +393,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(y[e], dyb + (16 * rb + 4 * lg + e) * DV + col0 + lr);
+            __builtin_nontemporal_store(y[e], dyb + ws_frag(C / 16, col0 >> 4, rb, e, lg, lr));
           const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&bs.gam[16 * rb + 4 * lg]);
           const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&bs.bt[16 * rb + 4 * lg]);
           f32x4 gd;
@@ -452,7 +452,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              __builtin_nontemporal_store(Sacc[mb][e], hb + srow(mb, e) * DV + col0 + lr);
+              __builtin_nontemporal_store(Sacc[mb][e], hb + ws_frag(DK / 16, col0 >> 4, mb, e, lg, lr));
         }
         // the hi/lo split of S for this chunk's products: after the barrier,
         // in the same block as K S and Q S, so the scheduler can overlap the
@@ -515,7 +515,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
               float *ubp = ws_b + ((long)chain * nchunks + s) * (C * DV);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                __builtin_nontemporal_store(rv[rb][e], ubp + (16 * rb + 4 * lg + e) * DV + col0 + lr);
+                __builtin_nontemporal_store(rv[rb][e], ubp + ws_frag(C / 16, col0 >> 4, rb, e, lg, lr));
             }
             const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);
             split4(rv[rb] * ec4, wh[rb], wl[rb]);
@@ -539,7 +539,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
               float *ubp = ws_b + ((long)chain * nchunks + s) * (C * DV);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                __builtin_nontemporal_store(u[e], ubp + (16 * rb + 4 * lg + e) * DV + col0 + lr);
+                __builtin_nontemporal_store(u[e], ubp + ws_frag(C / 16, col0 >> 4, rb, e, lg, lr));
             }
             split4(u, uh[rb], ul[rb]);
             const f32x4 ec4 = *reinterpret_cast<const f32x4 *>(&bs.ec[16 * rb + 4 * lg]);

@@ -350,7 +350,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(Sacc[mb][e], xp + (long)srow(mb, e) * DV + col0 + lr);
+            __builtin_nontemporal_store(Sacc[mb][e], xp + ws_frag(DK / 16, col0 >> 4, mb, e, lg, lr));
         // Y1 = X times the factor the forward applied after its update
 #pragma unroll
         for (int mb = 0; mb < DK / 16; ++mb)
@@ -385,7 +385,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         float *yp = ws_b + ((long)chain * nchunks + c) * (KC * DV);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          __builtin_nontemporal_store(y[e], yp + (4 * lg + e) * DV + col0 + lr);
+          __builtin_nontemporal_store(y[e], yp + ws_frag(KC / 16, col0 >> 4, 0, e, lg, lr));
         // ---- X <- Y1 + Q^ ^T dO - K^ ^T diag(b) dY (the exact path: e^{g_last} o Y1) ----
         if (exact) {
 #pragma unroll
@@ -427,7 +427,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int mb = 0; mb < DK / 16; ++mb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              __builtin_nontemporal_store(Sacc[mb][e], hp + (long)srow(mb, e) * DV + col0 + lr);
+              __builtin_nontemporal_store(Sacc[mb][e], hp + ws_frag(DK / 16, col0 >> 4, mb, e, lg, lr));
         }
         // ---- K^ S, Q^ S (three products each), R = V - K^ S, U = T' R ----
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -481,7 +481,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           float *up = ws_b + ((long)chain * nchunks + s) * (KC * DV);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            __builtin_nontemporal_store(rr[e], up + (4 * lg + e) * DV + col0 + lr);
+            __builtin_nontemporal_store(rr[e], up + ws_frag(KC / 16, col0 >> 4, 0, e, lg, lr));
         }
 
         // ---- O = Q^ S + P U ----

@@ -65,7 +65,8 @@ struct BwdArgs {
   const float *d_final_state;   // dL/dS_T or nullptr
   float *dq, *dk, *dv, *dbeta, *dlog_alpha, *d_initial_state;
   // workspace partitions, per (chain, chunk): the entering state h and U
-  // (recompute pass); dh and dY (reverse pass)
+  // (recompute pass); dh and dY (reverse pass); each chunk's block in the
+  // state waves' fragment order (ws_frag, mfma_util.h)
   float *ws_h, *ws_u, *ws_dh, *ws_dy;
   hipStream_t stream;
 };

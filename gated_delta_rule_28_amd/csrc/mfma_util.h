@@ -308,4 +308,25 @@ __device__ __forceinline__ float sum64(float x) {
   return x;
 }
 
+// The backward's workspace in fragment order.  A chunk's D x D state (h or
+// dh; k channel c, value column v) and its C x D tiles (U or dY; row r,
+// column v) are stored in the order the chunk kernels' state waves hold
+// them, so that each of their store instructions writes 256 contiguous
+// bytes (row-major, a wave's 16 columns would be four 64-byte pieces of
+// different lines).  With c = 32 (mb >> 1) + 8 g + 4 (mb & 1) + e (the
+// state waves' row order) and r = 16 rb + 4 g + e, the elements sit at
+//   state (c, v): (((v >> 4) D/16 + mb) 4 + e) 4 + g) 16 + (v & 15)
+//   tile  (r, v): (((v >> 4) C/16 + rb) 4 + e) 4 + g) 16 + (v & 15)
+// Eight consecutive v of one c (or r) inside a 16-column block stay
+// contiguous: the gradient kernels' operand reads.
+__device__ __forceinline__ int ws_frag(int nblk, int vb, int mb, int e, int g, int l) {
+  return (((vb * nblk + mb) * 4 + e) * 4 + g) * 16 + l;
+}
+__device__ __forceinline__ int ws_state_off(int D, int c, int v) {
+  return ws_frag(D >> 4, v >> 4, 2 * (c >> 5) + ((c >> 2) & 1), c & 3, (c >> 3) & 3, v & 15);
+}
+__device__ __forceinline__ int ws_tile_off(int C, int r, int v) {
+  return ws_frag(C >> 4, v >> 4, r >> 4, r & 3, (r >> 2) & 3, v & 15);
+}
+
 }  // namespace gdr
