@@ -8,6 +8,14 @@ All arithmetic runs in the HIP kernels.
     o      = recurrent_step(q, k, v, beta, log_alpha, state)   # state in place
     grads  = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final_state)
 
+For training, chunk_fwd_train returns the forward's outputs together with
+the backward's workspace, which chunk_bwd(..., workspace=ws, saved=True)
+reads instead of recomputing the forward:
+
+    o, S_T, ws = chunk_fwd_train(q, k, v, beta, log_alpha, initial_state)
+    grads = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final_state,
+                      workspace=ws, saved=True)
+
 Gate kind follows log_alpha: None -> DeltaNet (alpha = 1); [B, T, H] ->
 Gated DeltaNet (one decay per head); [B, T, H, Dk] -> KDA (one per channel).
 erase=False drops the erase term (S = alpha S + beta k v^T): linear
@@ -25,8 +33,9 @@ import torch
 from . import _abi
 from ._abi import GdrError, abi_version, status_str, LIB_PATH
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_bwd", "chunk_bwd_workspace_bytes", "GdrError",
-           "abi_version", "status_str", "LIB_PATH", "library_loaded"]
+__all__ = ["chunk_fwd", "chunk_fwd_train", "recurrent_step", "chunk_bwd",
+           "chunk_bwd_workspace_bytes", "GdrError", "abi_version", "status_str", "LIB_PATH",
+           "library_loaded"]
 
 _DT = {torch.float32: _abi.GDR_F32, torch.bfloat16: _abi.GDR_BF16}
 
@@ -83,24 +92,10 @@ def _check_gate_tensor(out_gate, shape, dtype):
         raise ValueError(f"out_gate must be {tuple(shape)}")
 
 
-def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
-              out_dtype=torch.float32, output_final_state=True, o=None, final_state=None,
-              erase=True, qk_l2norm=False, beta_sigmoid=False, decay=None, out_gate=None):
-    """Chunkwise forward over whole sequences.
-
-    q, k [B, T, H, Dk] and v [B, T, H, Dv] (bf16 or fp32, same dtype);
-    beta [B, T, H] fp32; log_alpha None | [B, T, H] | [B, T, H, Dk] fp32;
-    initial_state None | [B, H, Dk, Dv] fp32.  Returns (o [B, T, H, Dv] in
-    out_dtype, final state [B, H, Dk, Dv] fp32 or None).  `o` and
-    `final_state` may be passed preallocated; final_state may be the
-    initial_state tensor itself (in-place carry).
-
-    erase=False drops the erase term (additive write).  Fused options
-    (applied inside the kernels, see the module docstring): qk_l2norm,
-    beta_sigmoid (beta holds logits), decay="softplus" | "gla" (log_alpha
-    holds the pre-activation; needs a gate), out_gate [B, T, H, Dv] in the
-    dtype of q (o <- o * g * sigmoid(g)).
-    """
+def _fwd_args(q, k, v, beta, log_alpha, initial_state, out_dtype, output_final_state, o,
+              final_state, erase):
+    """Checks of a forward call's tensors; allocates o and the final state
+    when not given.  Returns B, T, H, Dk, Dv, the gate flags, o, final_state."""
     _check_dev("q", q)
     if q.dtype not in _DT:
         raise TypeError("q/k/v must be bf16 or fp32")
@@ -134,6 +129,30 @@ def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
         _check_dev("final_state", final_state, torch.float32)
         if tuple(final_state.shape) != (B, H, Dk, Dv):
             raise ValueError("final_state must be [B, H, Dk, Dv]")
+    return B, T, H, Dk, Dv, gate, o, final_state
+
+
+def chunk_fwd(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
+              out_dtype=torch.float32, output_final_state=True, o=None, final_state=None,
+              erase=True, qk_l2norm=False, beta_sigmoid=False, decay=None, out_gate=None):
+    """Chunkwise forward over whole sequences.
+
+    q, k [B, T, H, Dk] and v [B, T, H, Dv] (bf16 or fp32, same dtype);
+    beta [B, T, H] fp32; log_alpha None | [B, T, H] | [B, T, H, Dk] fp32;
+    initial_state None | [B, H, Dk, Dv] fp32.  Returns (o [B, T, H, Dv] in
+    out_dtype, final state [B, H, Dk, Dv] fp32 or None).  `o` and
+    `final_state` may be passed preallocated; final_state may be the
+    initial_state tensor itself (in-place carry).
+
+    erase=False drops the erase term (additive write).  Fused options
+    (applied inside the kernels, see the module docstring): qk_l2norm,
+    beta_sigmoid (beta holds logits), decay="softplus" | "gla" (log_alpha
+    holds the pre-activation; needs a gate), out_gate [B, T, H, Dv] in the
+    dtype of q (o <- o * g * sigmoid(g)).
+    """
+    B, T, H, Dk, Dv, gate, o, final_state = _fwd_args(
+        q, k, v, beta, log_alpha, initial_state, out_dtype, output_final_state, o, final_state,
+        erase)
     fuse = _fuse_flags(qk_l2norm, beta_sigmoid, decay)
     _check_gate_tensor(out_gate, (B, T, H, Dv), q.dtype)
     st = _abi.gdr_chunk_fwd_ex(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], _DT[out_dtype], gate,
@@ -186,6 +205,37 @@ def recurrent_step(q, k, v, beta, log_alpha, state, *, out_dtype=torch.float32, 
     return o
 
 
+def chunk_fwd_train(q, k, v, beta, log_alpha=None, initial_state=None, *, chunk=0,
+                    out_dtype=torch.float32, output_final_state=True, o=None, final_state=None,
+                    erase=True, workspace=None):
+    """chunk_fwd for training: the same (o, final state), and besides the
+    backward's workspace holding what chunk_bwd(..., saved=True) reads in
+    place of its recompute pass.  Returns (o, final_state, workspace).
+
+    Inputs within chunk_bwd's supported set (bf16 q/k/v, Dk = Dv in {64,
+    128}, every gate, with or without the erase term), no fused options.
+    `workspace`, a uint8 GPU tensor of at least chunk_bwd_workspace_bytes,
+    is allocated with torch when not given.  Pass the same inputs and this
+    workspace, unchanged, to chunk_bwd(..., saved=True).
+    """
+    B, T, H, Dk, Dv, gate, o, final_state = _fwd_args(
+        q, k, v, beta, log_alpha, initial_state, out_dtype, output_final_state, o, final_state,
+        erase)
+    need = int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    else:
+        _check_dev("workspace", workspace, torch.uint8)
+    st = _abi.gdr_chunk_fwd_train(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], _DT[out_dtype], gate,
+                                  q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                  _ptr(log_alpha), _ptr(initial_state), o.data_ptr(),
+                                  _ptr(final_state), workspace.data_ptr(), workspace.numel(),
+                                  _stream(q.device))
+    if st != _abi.GDR_OK:
+        raise GdrError(st, "gdr_chunk_fwd_train")
+    return o, final_state, workspace
+
+
 def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0, erase=True):
     """Bytes of device workspace chunk_bwd needs for inputs shaped like q
     ([B, T, H, Dk]) and this gate (0 when the call is not supported)."""
@@ -195,7 +245,8 @@ def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0, erase=True):
 
 
 def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_final_state=None,
-              *, chunk=0, erase=True, workspace=None, want_d_initial_state=True, out=None):
+              *, chunk=0, erase=True, workspace=None, want_d_initial_state=True, out=None,
+              saved=False):
     """Gradients of chunk_fwd's o and final state.
 
     Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, every gate,
@@ -208,6 +259,8 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     a uint8 GPU tensor of at least chunk_bwd_workspace_bytes, is allocated
     with torch when not given; `out`, a dict of the same keys and shapes,
     receives the gradients when given (nothing is allocated then).
+    saved=True: `workspace` is the one chunk_fwd_train filled for these same
+    inputs; the recompute pass is skipped.
     """
     _check_dev("q", q)
     if q.dtype not in _DT:
@@ -254,10 +307,13 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
                 raise ValueError(f"{n} must be {shp}")
     need = int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate))
     if workspace is None:
+        if saved:
+            raise ValueError("saved=True needs the workspace chunk_fwd_train filled")
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     else:
         _check_dev("workspace", workspace, torch.uint8)
-    st = _abi.gdr_chunk_bwd(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate, q.data_ptr(),
+    fn = _abi.gdr_chunk_bwd_saved if saved else _abi.gdr_chunk_bwd
+    st = fn(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate, q.data_ptr(),
                             k.data_ptr(), v.data_ptr(), beta.data_ptr(), _ptr(log_alpha),
                             _ptr(initial_state), d_o.data_ptr(), _ptr(d_final_state),
                             out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(),
@@ -265,5 +321,5 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
                             _ptr(out["d_initial_state"]), workspace.data_ptr(),
                             workspace.numel(), _stream(q.device))
     if st != _abi.GDR_OK:
-        raise GdrError(st, "gdr_chunk_bwd")
+        raise GdrError(st, "gdr_chunk_bwd_saved" if saved else "gdr_chunk_bwd")
     return out

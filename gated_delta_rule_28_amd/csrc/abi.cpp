@@ -158,12 +158,28 @@ size_t gdr_chunk_bwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int ch
   return bwd_workspace(B, T, H, Dk, gate_kind(gate));
 }
 
-int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
-                  const void *q, const void *k, const void *v, const float *beta,
-                  const float *log_alpha, const float *initial_state, const void *d_o,
-                  const float *d_final_state, float *dq, float *dk, float *dv, float *dbeta,
-                  float *dlog_alpha, float *d_initial_state, void *workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// the workspace partitions of a backward call: h, dh [chain][chunk][D][D];
+// U, dY [chain][chunk][C][D] (each chunk's block in fragment order)
+void bwd_partitions(gdr::BwdArgs &a, void *workspace) {
+  const int C = gdr::bwd_chunk(a.gate);
+  const long nblk = (long)a.B * a.H * ((a.T + C - 1) / C);
+  float *w = static_cast<float *>(workspace);
+  a.ws_h = w;
+  a.ws_dh = a.ws_h + nblk * a.D * a.D;
+  a.ws_u = a.ws_dh + nblk * a.D * a.D;
+  a.ws_dy = a.ws_u + nblk * C * a.D;
+}
+
+// gdr_chunk_bwd, and with saved = true gdr_chunk_bwd_saved (the workspace
+// holds h and U from gdr_chunk_fwd_train: no recompute pass)
+int chunk_bwd_impl(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
+                   const void *q, const void *k, const void *v, const float *beta,
+                   const float *log_alpha, const float *initial_state, const void *d_o,
+                   const float *d_final_state, float *dq, float *dk, float *dv, float *dbeta,
+                   float *dlog_alpha, float *d_initial_state, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream, bool saved) {
   if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
   if (!valid_dtype(in_dtype) || !valid_gate(gate)) return GDR_EINVAL;
   if ((gate_kind(gate) == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
@@ -196,18 +212,81 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
   a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;
   a.d_initial_state = d_initial_state;
-  // workspace partitions: h, dh [chain][chunk][D][D]; U, dY [chain][chunk][C][D]
-  const int C = gdr::bwd_chunk(a.gate);
-  const long nblk = (long)B * H * ((T + C - 1) / C);
-  float *w = static_cast<float *>(workspace);
-  a.ws_h = w;
-  a.ws_dh = a.ws_h + nblk * Dk * Dk;
-  a.ws_u = a.ws_dh + nblk * Dk * Dk;
-  a.ws_dy = a.ws_u + nblk * C * Dk;
+  a.saved = saved;
+  bwd_partitions(a, workspace);
   a.stream = stream;
   const bool kda = a.gate == GDR_GATE_CHANNEL;
   hipError_t e = kda ? gdr::launch_chunk_bwd_kda_passes(a) : gdr::launch_chunk_bwd_passes(a);
   if (e == hipSuccess) e = kda ? gdr::launch_chunk_bwd_kda_grads(a) : gdr::launch_chunk_bwd_grads(a);
+  return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+}  // namespace
+
+int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
+                  const void *q, const void *k, const void *v, const float *beta,
+                  const float *log_alpha, const float *initial_state, const void *d_o,
+                  const float *d_final_state, float *dq, float *dk, float *dv, float *dbeta,
+                  float *dlog_alpha, float *d_initial_state, void *workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
+                        initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                        d_initial_state, workspace, workspace_bytes, stream, false);
+}
+
+int gdr_chunk_bwd_saved(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
+                        const void *q, const void *k, const void *v, const float *beta,
+                        const float *log_alpha, const float *initial_state, const void *d_o,
+                        const float *d_final_state, float *dq, float *dk, float *dv,
+                        float *dbeta, float *dlog_alpha, float *d_initial_state,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
+                        initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                        d_initial_state, workspace, workspace_bytes, stream, true);
+}
+
+int gdr_chunk_fwd_train(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,
+                        int out_dtype, int gate, const void *q, const void *k, const void *v,
+                        const float *beta, const float *log_alpha, const float *initial_state,
+                        void *o, float *final_state, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate)) return GDR_EINVAL;
+  if ((gate_kind(gate) == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
+  if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+    return GDR_EINVAL;
+  // the supported set of the backward, whose workspace this call fills
+  if (!bwd_shape_ok(B, T, H, Dk, Dv, chunk, in_dtype, gate)) return GDR_EUNSUPPORTED;
+  if ((long)B * H == 0) return GDR_OK;                   // nothing to compute
+  if (T == 0) {                                          // no tokens: S_T = S_0, nothing saved
+    if (!final_state || final_state == initial_state) return GDR_OK;
+    hipError_t e = gdr::launch_state_passthrough(initial_state, final_state,
+                                                 (long)B * H * Dk * Dv, stream);
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+  }
+  int st = check_common(Dk, Dv, in_dtype, out_dtype, gate, q, k, v, beta, log_alpha, o);
+  if (st != GDR_OK) return st;
+  if (gate_kind(gate) == GDR_GATE_CHANNEL && !aligned16(log_alpha)) return GDR_EINVAL;
+  const size_t need = bwd_workspace(B, T, H, Dk, gate_kind(gate));
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
+    return GDR_EWORKSPACE;
+
+  gdr::ChunkArgs a;
+  a.B = B; a.T = T; a.H = H; a.D = Dk; a.chunk = chunk;
+  a.in_bf16 = true; a.out_bf16 = out_dtype == GDR_BF16;
+  a.gate = gate_kind(gate);
+  a.erase = erases(gate);
+  a.fuse = 0;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.out_gate = nullptr;
+  a.initial_state = initial_state; a.o = o; a.final_state = final_state;
+  a.stream = stream;
+  gdr::BwdArgs w;
+  w.B = B; w.T = T; w.H = H; w.D = Dk; w.gate = gate_kind(gate);
+  bwd_partitions(w, workspace);
+  const hipError_t e = a.gate == GDR_GATE_CHANNEL
+                           ? gdr::launch_chunk_fwd_kda_save(a, w.ws_h, w.ws_u)
+                           : gdr::launch_chunk_fwd_bf16_save(a, w.ws_h, w.ws_u);
   return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 

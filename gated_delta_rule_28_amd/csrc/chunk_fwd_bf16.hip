@@ -170,14 +170,16 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                 "DMA runs are whole 1 KiB waves");
   static_assert(MODE == kModeFwd || (!FUSED && GATE != kGateChannel),
                 "the backward passes run the unfused forms without the per-channel gate");
-  constexpr bool WANT_O = MODE == kModeFwd;      // outputs (Q S, P U, o)
+  constexpr bool WANT_O = MODE == kModeFwd || MODE == kModeFwdSave;   // outputs (Q S, P U, o)
+  constexpr bool SAVE = MODE == kModeRec || MODE == kModeFwdSave;     // h and U per chunk
   // Carried-scale form of the state (forward, scalar decay): the state
   // waves hold Z with S = Z_scale * Z, so that the decay of a chunk does not
   // multiply every state element: the scale goes into the row factors of
   // K S and Q S (times Z_scale) and of the update (divided by the scale
   // after it), and Z is multiplied only when the scale would drop below
   // 2^-40 (then by the accumulated scale, which returns to 1).  The scale
-  // is kept by the prep wave that forms the factors, chunk by chunk.
+  // is kept by the prep wave that forms the factors, chunk by chunk.  (The
+  // modes that store the state keep it unscaled.)
   constexpr bool LAZY = MODE == kModeFwd && GATE == kGateScalar;
   constexpr bool WANT_P = MODE != kModeRec;      // the P tiles and q
   __shared__ SM sm;
@@ -445,7 +447,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const char *Kb = reinterpret_cast<const char *>(&bs.K[0][0]);
         const char *Qb = reinterpret_cast<const char *>(&bs.Q[0][0]);
         const char *Vb = reinterpret_cast<const char *>(&bs.V[0][0]);
-        if constexpr (MODE == kModeRec) {
+        if constexpr (SAVE) {
           // the state entering chunk s
           float *hb = ws_a + ((long)chain * nchunks + s) * (DK * DV);
 #pragma unroll
@@ -511,7 +513,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int rb = 0; rb < 2; ++rb) {
             uh[rb] = rh2[rb];
             ul[rb] = rl2[rb];
-            if constexpr (MODE == kModeRec) {   // U = b o V
+            if constexpr (SAVE) {   // U = b o V
               float *ubp = ws_b + ((long)chain * nchunks + s) * (C * DV);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -535,7 +537,7 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
             u = mfma_bf16(th, Rh, u);
             u = mfma_bf16(tl, Rh, u);
             u = mfma_bf16(th, Rl, u);
-            if constexpr (MODE == kModeRec) {
+            if constexpr (SAVE) {
               float *ubp = ws_b + ((long)chain * nchunks + s) * (C * DV);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -978,17 +980,49 @@ hipError_t launch_fused(const ChunkArgs &a) {
   return hipGetLastError();
 }
 
-// the backward's two sequential passes at one tile configuration
+// the forward that also stores h and U per chunk (the recompute pass's
+// stores) at one tile configuration
+template <int DK, int DVS, typename OutT, int GATE, bool ERASE>
+hipError_t launch_save(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  const int nslice = DK / DVS;
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
+  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, OutT, GATE, ERASE, false, kModeFwdSave>),
+                     grid, block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                     (const bf16 *)a.v, a.beta, a.log_alpha, a.initial_state, (OutT *)a.o,
+                     a.final_state, a.B, a.T, a.H, 0, nullptr, ws_h, ws_u, nullptr);
+  return hipGetLastError();
+}
+
+template <int DK, int DVS, typename OutT>
+hipError_t save_by_gate(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  if (a.erase) {
+    if (a.gate == kGateNone) return launch_save<DK, DVS, OutT, kGateNone, true>(a, ws_h, ws_u);
+    return launch_save<DK, DVS, OutT, kGateScalar, true>(a, ws_h, ws_u);
+  }
+  if (a.gate == kGateNone) return launch_save<DK, DVS, OutT, kGateNone, false>(a, ws_h, ws_u);
+  return launch_save<DK, DVS, OutT, kGateScalar, false>(a, ws_h, ws_u);
+}
+
+template <int DK, int DVS>
+hipError_t save_by_out(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  return a.out_bf16 ? save_by_gate<DK, DVS, bf16>(a, ws_h, ws_u)
+                    : save_by_gate<DK, DVS, float>(a, ws_h, ws_u);
+}
+
+// the backward's two sequential passes at one tile configuration (the first
+// skipped when a training forward has stored its results)
 template <int DK, int DVS, int GATE, bool ERASE>
 hipError_t launch_passes(const BwdArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + NPW));
-  hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, ERASE, false, kModeRec>), grid,
-                     block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
-                     a.beta, a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0,
-                     nullptr, a.ws_h, a.ws_u, nullptr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.saved) {
+    hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, ERASE, false, kModeRec>),
+                       grid, block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k,
+                       (const bf16 *)a.v, a.beta, a.log_alpha, a.initial_state, nullptr, nullptr,
+                       a.B, a.T, a.H, 0, nullptr, a.ws_h, a.ws_u, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((chunk_fwd_bf16_kernel<DK, DVS, float, GATE, ERASE, false, kModeRev>), grid,
                      block, 0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.d_o,
                      a.beta, a.log_alpha, a.d_final_state, nullptr, a.d_initial_state, a.B, a.T,
@@ -1059,6 +1093,17 @@ hipError_t launch_chunk_bwd_passes(const BwdArgs &a) {
   }
   if (chains >= 256) return passes_by_gate<64, 64>(a);
   return passes_by_gate<64, 32>(a);
+}
+
+hipError_t launch_chunk_fwd_bf16_save(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  static_assert(C == kBwdChunk, "the workspace holds this kernel's chunks");
+  const long chains = (long)a.B * a.H;   // the forward's launch shapes
+  if (a.D == 128) {
+    if (chains * 2 >= 256) return save_by_out<128, 64>(a, ws_h, ws_u);
+    return save_by_out<128, 32>(a, ws_h, ws_u);
+  }
+  if (chains >= 256) return save_by_out<64, 64>(a, ws_h, ws_u);
+  return save_by_out<64, 32>(a, ws_h, ws_u);
 }
 
 hipError_t launch_chunk_fwd_bf16(const ChunkArgs &a) {

@@ -138,7 +138,8 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   constexpr int QRB = 2 * DK, VRB = 2 * DVS;    // bytes per q/k and v row
   static_assert((DK == 64 || DK == 128) && (DVS == 32 || DVS == 64) && DVS <= DK, "tile config");
   static_assert(MODE == kModeFwd || !FUSED, "the backward passes take no fused options");
-  constexpr bool WANT_O = MODE == kModeFwd;    // outputs (Q^ S, P U, o)
+  constexpr bool WANT_O = MODE == kModeFwd || MODE == kModeFwdSave;   // outputs (Q^ S, P U, o)
+  constexpr bool SAVE = MODE == kModeRec || MODE == kModeFwdSave;     // h and U per chunk
   constexpr bool WANT_P = MODE != kModeRec;    // Q^ and the P tiles
   // calls without a fused prologue or epilogue compile without their code
   if constexpr (!FUSED) {
@@ -421,7 +422,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const typename SM::Der &d = *at_off(&sm.der[0], slot_off(s % NDER, (int)sizeof(typename SM::Der)));
         const int t1 = slot_off(s & 1, (int)sizeof(sm.Th[0]));   // T' and P slots (same size)
         const int exact = __builtin_amdgcn_readfirstlane(d.flag[0]);
-        if constexpr (MODE == kModeRec) {   // the state entering chunk s
+        if constexpr (SAVE) {   // the state entering chunk s
           float *hp = ws_a + ((long)chain * nchunks + s) * (DK * DV);
 #pragma unroll
           for (int mb = 0; mb < DK / 16; ++mb)
@@ -477,7 +478,7 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           for (int e = 0; e < 4; ++e) rr[e] = b4[e] * (float)vv[e];
           split4(rr, uh4, ul4);
         }
-        if constexpr (MODE == kModeRec) {   // U of chunk s (rr holds it on both paths)
+        if constexpr (SAVE) {   // U of chunk s (rr holds it on both paths)
           float *up = ws_b + ((long)chain * nchunks + s) * (KC * DV);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -954,17 +955,42 @@ hipError_t launch_kda_fused(const ChunkArgs &a) {
   return hipGetLastError();
 }
 
-// the backward's two sequential passes at one tile configuration
+// the forward that also stores h and U per chunk (the recompute pass's
+// stores) at one tile configuration
+template <int DK, int DVS, typename OutT, bool ERASE>
+hipError_t launch_kda_save(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  const int nslice = DK / DVS;
+  dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
+  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, OutT, ERASE, false, kModeFwdSave>), grid, block,
+                     0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,
+                     a.log_alpha, a.initial_state, (OutT *)a.o, a.final_state, a.B, a.T, a.H, 0,
+                     nullptr, ws_h, ws_u);
+  return hipGetLastError();
+}
+
+template <int DK, int DVS>
+hipError_t kda_save_by_out(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  if (a.erase)
+    return a.out_bf16 ? launch_kda_save<DK, DVS, bf16, true>(a, ws_h, ws_u)
+                      : launch_kda_save<DK, DVS, float, true>(a, ws_h, ws_u);
+  return a.out_bf16 ? launch_kda_save<DK, DVS, bf16, false>(a, ws_h, ws_u)
+                    : launch_kda_save<DK, DVS, float, false>(a, ws_h, ws_u);
+}
+
+// the backward's two sequential passes at one tile configuration (the first
+// skipped when a training forward has stored its results)
 template <int DK, int DVS, bool ERASE>
 hipError_t launch_kda_passes(const BwdArgs &a) {
   const int nslice = DK / DVS;
   dim3 grid((unsigned)(a.B * a.H * nslice)), block(64 * (DVS / 16 + kda_npw<DVS>()));
-  hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, float, ERASE, false, kModeRec>), grid, block, 0,
-                     a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,
-                     a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0, nullptr,
-                     a.ws_h, a.ws_u);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.saved) {
+    hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, float, ERASE, false, kModeRec>), grid, block,
+                       0, a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v,
+                       a.beta, a.log_alpha, a.initial_state, nullptr, nullptr, a.B, a.T, a.H, 0,
+                       nullptr, a.ws_h, a.ws_u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((chunk_fwd_kda_kernel<DK, DVS, float, ERASE, false, kModeRev>), grid, block, 0,
                      a.stream, (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.d_o, a.beta,
                      a.log_alpha, a.d_final_state, nullptr, a.d_initial_state, a.B, a.T, a.H, 0,
@@ -1008,6 +1034,16 @@ hipError_t launch_chunk_bwd_kda_passes(const BwdArgs &a) {
   }
   if (chains >= 256) return kda_passes_by_erase<64, 64>(a);
   return kda_passes_by_erase<64, 32>(a);
+}
+
+hipError_t launch_chunk_fwd_kda_save(const ChunkArgs &a, float *ws_h, float *ws_u) {
+  const long chains = (long)a.B * a.H;   // the forward's launch shapes
+  if (a.D == 128) {
+    if (chains * 2 >= 256) return kda_save_by_out<128, 64>(a, ws_h, ws_u);
+    return kda_save_by_out<128, 32>(a, ws_h, ws_u);
+  }
+  if (chains >= 256) return kda_save_by_out<64, 64>(a, ws_h, ws_u);
+  return kda_save_by_out<64, 32>(a, ws_h, ws_u);
 }
 
 hipError_t launch_chunk_fwd_kda(const ChunkArgs &a) {

@@ -16,8 +16,9 @@ enum Gate { kGateNone = 0, kGateScalar = 1, kGateChannel = 2 };
 
 // What a chunk kernel computes: the forward, or one of the backward's two
 // sequential passes (the forward recomputed, storing per chunk the entering
-// state and U; the reverse walk storing the state gradient and dY).
-enum Mode { kModeFwd = 0, kModeRec = 1, kModeRev = 2 };
+// state and U; the reverse walk storing the state gradient and dY), or the
+// forward that also stores what the first pass would (for training).
+enum Mode { kModeFwd = 0, kModeRec = 1, kModeRev = 2, kModeFwdSave = 3 };
 
 template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }

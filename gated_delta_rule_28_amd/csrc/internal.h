@@ -58,6 +58,8 @@ struct BwdArgs {
   int B, T, H, D;
   int gate;                     // kGateNone, kGateScalar or kGateChannel
   bool erase;                   // false: the additive write (no erase term)
+  bool saved;                   // h and U are in the workspace already (a training
+                                // forward stored them): no recompute pass
   const void *q, *k, *v;
   const float *beta, *log_alpha;
   const float *initial_state;   // S_0 or nullptr
@@ -84,5 +86,9 @@ hipError_t launch_chunk_bwd_grads(const BwdArgs &a);
 // the same two steps with the per-channel gate (16-token chunks)
 hipError_t launch_chunk_bwd_kda_passes(const BwdArgs &a);
 hipError_t launch_chunk_bwd_kda_grads(const BwdArgs &a);
+// the forward that also stores, per chunk, h and U into the backward's
+// workspace partitions (the training forward; bf16, D = 64 or 128)
+hipError_t launch_chunk_fwd_bf16_save(const ChunkArgs &a, float *ws_h, float *ws_u);
+hipError_t launch_chunk_fwd_kda_save(const ChunkArgs &a, float *ws_h, float *ws_u);
 
 }  // namespace gdr

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -233,6 +233,50 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
                   float *d_initial_state,
                   void *workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * gdr_chunk_fwd_train -- gdr_chunk_fwd for training: the same o and
+ * final_state, and besides, into `workspace`, the per-chunk states and write
+ * residuals that gdr_chunk_bwd's first pass would recompute, so that
+ * gdr_chunk_bwd_saved can skip that pass (the forward pass of training, which
+ * the backward follows: diosapp tutorial, section 五).
+ *
+ *   B .. final_state  as gdr_chunk_fwd, within gdr_chunk_bwd's supported set
+ *                 (bf16 q/k/v, Dk == Dv in {64, 128}, every gate, with or
+ *                 without GDR_NO_ERASE; others return GDR_EUNSUPPORTED);
+ *                 no fused options
+ *   workspace     device memory of at least gdr_chunk_bwd_workspace_bytes for
+ *                 the same shape, chunk, dtype and gate, 256-byte aligned,
+ *                 owned by the caller (GDR_EWORKSPACE otherwise).  Written:
+ *                 the part gdr_chunk_bwd_saved reads; the rest is untouched.
+ *
+ * o is the forward's output to the forward's accuracy (for the scalar gate
+ * the state is kept unscaled here, so the last bits of o may differ from
+ * gdr_chunk_fwd's).  One kernel launch on `stream`.
+ */
+int gdr_chunk_fwd_train(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,
+                        int out_dtype, int gate, const void *q, const void *k, const void *v,
+                        const float *beta, const float *log_alpha, const float *initial_state,
+                        void *o, float *final_state, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * gdr_chunk_bwd_saved -- gdr_chunk_bwd after gdr_chunk_fwd_train: the same
+ * arguments and results, with `workspace` holding what gdr_chunk_fwd_train
+ * stored for the same inputs (q, k, v, beta, log_alpha, initial_state, gate
+ * and shape) and unchanged since.  It skips the recompute pass (two kernel
+ * launches).  Other workspace contents give meaningless gradients; nothing
+ * is read outside the workspace and the inputs.
+ */
+int gdr_chunk_bwd_saved(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
+                        const void *q, const void *k, const void *v,
+                        const float *beta, const float *log_alpha,
+                        const float *initial_state,
+                        const void *d_o, const float *d_final_state,
+                        float *dq, float *dk, float *dv, float *dbeta, float *dlog_alpha,
+                        float *d_initial_state,
+                        void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /*
  * gdr_chunk_bwd_noalloc -- gdr_chunk_bwd for callers that cannot allocate

@@ -26,8 +26,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == ["gdr_abi_version", "gdr_chunk_bwd", "gdr_chunk_bwd_noalloc",
-                     "gdr_chunk_bwd_workspace_bytes",
-                     "gdr_chunk_fwd", "gdr_chunk_fwd_ex", "gdr_chunk_fwd_workspace_bytes",
+                     "gdr_chunk_bwd_saved", "gdr_chunk_bwd_workspace_bytes",
+                     "gdr_chunk_fwd", "gdr_chunk_fwd_ex", "gdr_chunk_fwd_train",
+                     "gdr_chunk_fwd_workspace_bytes",
                      "gdr_recurrent_step", "gdr_recurrent_step_ex", "gdr_status_str"], names
     assert set(names) == set(_abi.SIGNATURES)
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert _abi.abi_version() == _abi.ABI_VERSION == 2
+    assert _abi.abi_version() == _abi.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -249,6 +250,60 @@ def bwd(**kw):
 ])
 def test_chunk_bwd_rejects(kw, want):
     assert bwd(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), _abi.GDR_EINVAL),
+    (dict(dq=None), _abi.GDR_EINVAL),
+    (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
+    (dict(workspace=None), _abi.GDR_EWORKSPACE),
+])
+def test_chunk_bwd_saved_validates_like_chunk_bwd(kw, want):
+    a = dict(B=1, T=8, H=1, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+             gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, log_alpha=FAKE,
+             initial_state=None, d_o=FAKE, d_final_state=None, dq=FAKE, dk=FAKE, dv=FAKE,
+             dbeta=FAKE, dlog_alpha=FAKE, d_initial_state=None, workspace=FAKE,
+             workspace_bytes=1 << 40, stream=None)
+    a.update(kw)
+    assert _abi.gdr_chunk_bwd_saved(**a) == want
+    assert _abi.gdr_chunk_bwd(**a) == want
+
+
+def fwd_train(**kw):
+    a = dict(B=1, T=8, H=1, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+             out_dtype=_abi.GDR_F32, gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE,
+             beta=FAKE, log_alpha=FAKE, initial_state=None, o=FAKE, final_state=None,
+             workspace=FAKE, workspace_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return _abi.gdr_chunk_fwd_train(**a)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), _abi.GDR_EINVAL),
+    (dict(q=None), _abi.GDR_EINVAL),
+    (dict(o=None), _abi.GDR_EINVAL),
+    (dict(log_alpha=None), _abi.GDR_EINVAL),
+    (dict(gate=_abi.GDR_GATE_NONE), _abi.GDR_EINVAL),          # log_alpha without a gate
+    (dict(final_state=FAKE + 4), _abi.GDR_EINVAL),
+    (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),      # the backward's supported set
+    (dict(Dk=32, Dv=32), _abi.GDR_EUNSUPPORTED),
+    (dict(Dk=128, Dv=64), _abi.GDR_EUNSUPPORTED),
+    (dict(chunk=48), _abi.GDR_EUNSUPPORTED),
+    (dict(workspace=None), _abi.GDR_EWORKSPACE),
+    (dict(workspace=FAKE + 16), _abi.GDR_EWORKSPACE),
+    (dict(workspace_bytes=4 * (2 * 128 * 128 + 2 * 32 * 128) - 1), _abi.GDR_EWORKSPACE),
+    (dict(gate=_abi.GDR_GATE_CHANNEL, workspace_bytes=4 * (2 * 128 * 128 + 2 * 16 * 128) - 1),
+     _abi.GDR_EWORKSPACE),
+])
+def test_chunk_fwd_train_rejects(kw, want):
+    assert fwd_train(**kw) == want
+
+
+def test_chunk_fwd_train_empty_calls_need_nothing():
+    assert fwd_train(B=0, q=None, k=None, v=None, o=None, workspace=None,
+                     workspace_bytes=0) == _abi.GDR_OK
+    assert fwd_train(T=0, q=None, k=None, v=None, o=None, workspace=None,
+                     workspace_bytes=0) == _abi.GDR_OK
 
 
 def test_chunk_bwd_empty_batch_is_a_no_op():

@@ -250,6 +250,25 @@ def test_backward_kda_many_chains(D, B, H):
         check_all(sub, ref, "channel")
 
 
+def test_backward_kda_full_shape_sampled_chains():
+    """The KDA layer shape B=2, H=32, T=8192, d=128 with the workload's own
+    decay distribution, in the launch the benchmark times (32-column slices);
+    the oracle checks two chains in full, every token's gradients and dS_0."""
+    w = W.by_name("kda_bf16_b2h32t8192")
+    say("bwd", w.name, "sampled")
+    inp = W.make_workload_inputs(w, seed=0, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    inp["d_o"] = torch.randn(w.B, w.T, w.H, w.Dv, device=DEV, generator=g).to(torch.bfloat16)
+    inp["d_final_state"] = 0.5 * torch.randn(w.B, w.H, w.Dk, w.Dv, device=DEV, generator=g)
+    got = run_gpu(inp)
+    chains = [(0, 0), (1, 31)]
+    for (b, h), ref in zip(chains, oracle(inp, chains)):
+        sub = {n: (got[n][b:b + 1, h:h + 1] if n == "dS0" else got[n][b:b + 1, :, h:h + 1])
+               for n in NAMES}
+        check_all(sub, ref, "channel")
+
+
 def test_backward_kda_no_state_gradients_and_determinism():
     say("bwd kda no S0 / no dS_T, determinism")
     inp = make_case(1, 50, 3, 64, "channel", seed=3, s0=False, dst=False)

@@ -1,0 +1,162 @@
+"""GPU parity of the training pair: gdr_chunk_fwd_train (the forward that also
+fills the backward's workspace) and gdr_chunk_bwd_saved (the backward that
+reads it instead of recomputing the forward).
+
+The forward's o and S_T are compared with the fp64 oracle recurrence at the
+2e-3 bar of the bf16 path, and with chunk_fwd; the saved backward's gradients
+with the fp64 oracle's reverse sweep at 2e-3 and with the backward that
+recomputes the forward itself, which computes the same stored values.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_28_amd as gdr
+import workloads as W
+from oracle import gated_delta_backward, gated_delta_recurrence
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+DEV = "cuda"
+NAMES = ("dq", "dk", "dv", "dbeta", "dlog_alpha", "d_initial_state")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, ref):
+    got = W.to_f64(got) if torch.is_tensor(got) else np.asarray(got, np.float64)
+    ref = W.to_f64(ref) if torch.is_tensor(ref) else np.asarray(ref, np.float64)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref))) / max(rms, 1e-300)
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place of x (8 significant bits)."""
+    ax = np.maximum(np.abs(x), 1e-38)
+    return np.exp2(np.floor(np.log2(ax)) - 8.0)
+
+
+def make_case(B, T, H, D, gate, seed):
+    inp = W.make_chunk_inputs(B, T, H, D, D, gate, "bf16", seed=seed, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(500 + seed)
+    inp["initial_state"] = 0.3 * torch.randn(B, H, D, D, device=DEV, generator=g)
+    inp["d_o"] = torch.randn(B, T, H, D, device=DEV, generator=g).to(torch.bfloat16)
+    inp["d_final_state"] = 0.5 * torch.randn(B, H, D, D, device=DEV, generator=g)
+    return inp
+
+
+def args(inp):
+    return (inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["initial_state"])
+
+
+def oracle_fwd(inp, erase):
+    f = lambda x: None if x is None else W.to_f64(x)
+    return gated_delta_recurrence(*(f(x) for x in args(inp)), erase=erase)
+
+
+def oracle_bwd(inp, erase):
+    f = lambda x: None if x is None else W.to_f64(x)
+    return gated_delta_backward(*(f(x) for x in args(inp)), f(inp["d_o"]),
+                                f(inp["d_final_state"]), erase=erase)
+
+
+@pytest.mark.parametrize("erase", [True, False])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("D,T", [(64, 1), (128, 40), (64, 100), (128, 100)])
+def test_train_pair_matches_the_oracle(D, T, gate, erase):
+    say("train pair", D, T, gate, erase)
+    inp = make_case(2, T, 2, D, gate, seed=T + D + len(gate))
+    o, S, ws = gdr.chunk_fwd_train(*args(inp), erase=erase)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_fwd(inp, erase)
+    e_o, e_s = rel_err(o, o_ref), rel_err(S, S_ref)
+    o2, S2 = gdr.chunk_fwd(*args(inp), erase=erase)
+    torch.cuda.synchronize()
+    e_o2 = rel_err(o, o2)
+    say(f"o {e_o:.2e}  S {e_s:.2e}  o vs chunk_fwd {e_o2:.2e}")
+    assert e_o <= TOL and e_s <= TOL
+    assert e_o2 <= 1e-4
+
+    got = gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"], erase=erase,
+                        workspace=ws, saved=True)
+    plain = gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"], erase=erase)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(inp, erase)
+    ref["d_initial_state"] = ref.pop("dS0")
+    errs, diffs = {}, {}
+    for n in NAMES:
+        if gate == "none" and n == "dlog_alpha":
+            assert got[n] is None
+            continue
+        errs[n] = rel_err(got[n], ref[n])
+        diffs[n] = rel_err(got[n], plain[n])
+    say("vs oracle", {k: f"{v:.2e}" for k, v in errs.items()},
+        "vs recomputing backward", {k: f"{v:.1e}" for k, v in diffs.items()})
+    assert all(v <= TOL for v in errs.values()), errs
+    assert all(v <= 1e-5 for v in diffs.values()), diffs
+
+
+def test_train_pair_bf16_output_and_in_place_state():
+    """bf16 o, and the final state written over the initial one (the saved
+    backward reads the entering states from its workspace, not S_0)."""
+    say("train pair bf16 o, in-place carry")
+    inp = make_case(2, 77, 3, 128, "scalar", seed=3)
+    s0 = inp["initial_state"].clone()
+    ref_in = dict(inp, initial_state=s0)
+    o, S, ws = gdr.chunk_fwd_train(*args(inp), out_dtype=torch.bfloat16,
+                                   final_state=inp["initial_state"])
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16 and S.data_ptr() == inp["initial_state"].data_ptr()
+    o_ref, S_ref = oracle_fwd(ref_in, True)
+    # the 2e-3 bar plus the rounding of each value to bf16
+    rms = math.sqrt(float(np.mean(o_ref ** 2)))
+    assert np.all(np.abs(W.to_f64(o) - o_ref) <= TOL * rms + bf16_half_ulp(o_ref))
+    assert rel_err(S, S_ref) <= TOL
+    got = gdr.chunk_bwd(*args(ref_in), inp["d_o"], inp["d_final_state"], workspace=ws,
+                        saved=True)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(ref_in, True)
+    for n, rn in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dbeta", "dbeta"),
+                  ("dlog_alpha", "dlog_alpha"), ("d_initial_state", "dS0")):
+        assert rel_err(got[n], ref[rn]) <= TOL, n
+
+
+def test_train_pair_many_chains_sampled():
+    """Both slice widths of the launches (64-column slices at 256 chains)."""
+    for gate, B, H in (("scalar", 8, 32), ("channel", 4, 32)):
+        say("train pair many chains", gate, B, H)
+        inp = make_case(B, 50, H, 128, gate, seed=9)
+        o, S, ws = gdr.chunk_fwd_train(*args(inp))
+        got = gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"], workspace=ws,
+                            saved=True)
+        plain = gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"])
+        torch.cuda.synchronize()
+        for n in NAMES:
+            assert rel_err(got[n], plain[n]) <= 1e-5, n
+        for b, h in ((0, 0), (B - 1, H - 1)):
+            sl = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]
+            st = lambda x: None if x is None else x[b:b + 1, h:h + 1]
+            sub = {"q": sl(inp["q"]), "k": sl(inp["k"]), "v": sl(inp["v"]),
+                   "beta": sl(inp["beta"]), "log_alpha": sl(inp["log_alpha"]),
+                   "initial_state": st(inp["initial_state"]), "d_o": sl(inp["d_o"]),
+                   "d_final_state": st(inp["d_final_state"])}
+            o_ref, _ = oracle_fwd(sub, True)
+            assert rel_err(o[b:b + 1, :, h:h + 1], o_ref) <= TOL
+            ref = oracle_bwd(sub, True)
+            assert rel_err(got["dk"][b:b + 1, :, h:h + 1], ref["dk"]) <= TOL
+            assert rel_err(got["dlog_alpha"][b:b + 1, :, h:h + 1], ref["dlog_alpha"]) <= TOL
+
+
+def test_saved_backward_needs_the_workspace():
+    inp = make_case(1, 8, 1, 64, "scalar", seed=1)
+    with pytest.raises(ValueError):
+        gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"], saved=True)
