@@ -574,6 +574,46 @@ def bwd_alg_bytes(w):
     return th * per_th + w.B * w.H * w.Dk * w.Dv * 4
 
 
+def train_line(torch, gdr, W, w, steps, warmup, settle_s=0.0):
+    """One training step's chunk work on a workload: the forward and the
+    backward, timed as gdr_chunk_fwd + gdr_chunk_bwd (the backward
+    recomputes the forward) and as gdr_chunk_fwd_train + gdr_chunk_bwd_saved
+    (the forward stores what the backward would recompute), with every
+    output and the workspace preallocated."""
+    inp = W.make_workload_inputs(w, seed=0, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    d_o = torch.randn(w.B, w.T, w.H, w.Dv, device="cuda", generator=g).to(inp["q"].dtype)
+    ws = torch.empty(gdr.chunk_bwd_workspace_bytes(inp["q"], inp["log_alpha"]), device="cuda",
+                     dtype=torch.uint8)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    o = torch.empty(w.B, w.T, w.H, w.Dv, **f32)
+    S = torch.empty(w.B, w.H, w.Dk, w.Dv, **f32)
+    out = {"dq": torch.empty(w.B, w.T, w.H, w.Dk, **f32), "dk": torch.empty(w.B, w.T, w.H, w.Dk, **f32),
+           "dv": torch.empty(w.B, w.T, w.H, w.Dv, **f32), "dbeta": torch.empty(w.B, w.T, w.H, **f32),
+           "dlog_alpha": (None if inp["log_alpha"] is None
+                          else torch.empty(*inp["log_alpha"].shape, **f32)),
+           "d_initial_state": torch.empty(w.B, w.H, w.Dk, w.Dv, **f32)}
+    a = (inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None)
+
+    def plain():
+        gdr.chunk_fwd(*a, o=o, final_state=S)
+        gdr.chunk_bwd(*a, d_o, None, workspace=ws, out=out)
+
+    def saved():
+        gdr.chunk_fwd_train(*a, o=o, final_state=S, workspace=ws)
+        gdr.chunk_bwd(*a, d_o, None, workspace=ws, out=out, saved=True)
+    res = {"workload": w.name, "unit": "tokens/s"}
+    for key, fn in (("recompute", plain), ("saved", saved)):
+        _, per = time_launches(torch, fn, steps, warmup, settle_s)
+        ms = statistics.fmean(per)
+        res[key] = {"ms": ms, "value": w.B * w.T / (ms * 1e-3)}
+    res["value"] = res["saved"]["value"]
+    res["note"] = ("forward + backward of the chunk layer per step: chunk_fwd + chunk_bwd "
+                   "(recompute), chunk_fwd_train + chunk_bwd(saved=True) (saved)")
+    return res
+
+
 def bwd_line(torch, gdr, W, w, steps, warmup, settle_s=0.0, chains=((0, 0), (7, 15))):
     """Timed gdr_chunk_bwd calls on a chunk workload (the recompute pass, the
     reverse pass and the chunk-parallel gradients), outputs and workspace
@@ -713,13 +753,13 @@ def run_counter_targets(torch, gdr, W, reps=3):
 
 
 # The template instance each counter summary covers: the launch the bench
-# line times (the backward's passes are instances of the same scalar-gate
-# kernel template, with their own traffic, so the name alone is not enough).
-# Mangled template arguments: <Dk, Dv slice, output type, gate, erase, fused,
-# mode> and <Dk, Dv slice, output type, erase, fused>.
+# line times (the backward's passes and the training forward are instances
+# of the same kernel templates, with their own traffic, so the name alone is
+# not enough).  Mangled template arguments: <Dk, Dv slice, output type, gate,
+# erase, fused, mode> and <Dk, Dv slice, output type, erase, fused, mode>.
 COUNTED_INSTANCE = {
     "chunk_fwd_bf16_kernel": "chunk_fwd_bf16_kernelILi128ELi64EfLi1ELb1ELb0ELi0E",
-    "chunk_fwd_kda_kernel": "chunk_fwd_kda_kernelILi128ELi32EfLb1ELb0E",
+    "chunk_fwd_kda_kernel": "chunk_fwd_kda_kernelILi128ELi32EfLb1ELb0ELi0E",
     "recurrent_step_kernel": "recurrent_step_kernel",
 }
 
@@ -980,6 +1020,9 @@ def main(argv=None):
         rec["backward"] = bwd_line(torch, gdr, W, w, nb, 2, args.settle_s)
         rec["kda_backward"] = bwd_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb, 2,
                                        args.settle_s, chains=((0, 0), (1, 31)))
+        rec["train_step"] = train_line(torch, gdr, W, w, nb, 2, args.settle_s)
+        rec["kda_train_step"] = train_line(torch, gdr, W, W.by_name("kda_bf16_b2h32t8192"), nb,
+                                           2, args.settle_s)
     print(json.dumps(rec), flush=True)
     return 0
 
