@@ -74,7 +74,9 @@
 // storing dS (the gradient of the state leaving the chunk) and dY per chunk.
 // Both take the prep waves' A, P and T tiles unchanged (T^T and P^T are the
 // tiles as stored); the chunk-parallel kernel (chunk_bwd.hip) forms the
-// token gradients from what they store.
+// token gradients from what they store.  kModeFwdSave, the training forward,
+// is the forward with kModeRec's stores (the state kept unscaled), so that
+// the backward can skip its recompute pass.
 //
 // Precision.  q, k, v are exact bf16 and enter MFMAs unsplit; every derived
 // operand (S, R, U, T, P) is split into bf16

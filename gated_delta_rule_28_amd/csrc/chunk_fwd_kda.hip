@@ -67,6 +67,7 @@
 //
 // storing X and dY per chunk; the solver stores T instead of T' in that mode.
 // The chunk-parallel kernel (chunk_bwd_kda.hip) forms the token gradients.
+// kModeFwdSave, the training forward, is the forward with kModeRec's stores.
 #include <cstddef>
 #include <type_traits>
 
