@@ -16,6 +16,10 @@ reads instead of recomputing the forward:
     grads = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final_state,
                       workspace=ws, saved=True)
 
+chunk_gated_delta_rule wraps that pair as a torch.autograd.Function, so that
+o, S_T = chunk_gated_delta_rule(q, k, v, beta, log_alpha, initial_state)
+takes part in loss.backward() (every gradient from the kernels above).
+
 Gate kind follows log_alpha: None -> DeltaNet (alpha = 1); [B, T, H] ->
 Gated DeltaNet (one decay per head); [B, T, H, Dk] -> KDA (one per channel).
 erase=False drops the erase term (S = alpha S + beta k v^T): linear
@@ -33,7 +37,7 @@ import torch
 from . import _abi
 from ._abi import GdrError, abi_version, status_str, LIB_PATH
 
-__all__ = ["chunk_fwd", "chunk_fwd_train", "recurrent_step", "chunk_bwd",
+__all__ = ["chunk_fwd", "chunk_fwd_train", "chunk_gated_delta_rule", "recurrent_step", "chunk_bwd",
            "chunk_bwd_workspace_bytes", "GdrError", "abi_version", "status_str", "LIB_PATH",
            "library_loaded"]
 
@@ -323,3 +327,45 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     if st != _abi.GDR_OK:
         raise GdrError(st, "gdr_chunk_bwd_saved" if saved else "gdr_chunk_bwd")
     return out
+
+
+class _ChunkRule(torch.autograd.Function):
+    """chunk_fwd_train in the forward, chunk_bwd(saved=True) in the backward;
+    the workspace lives on the autograd graph between the two."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, log_alpha, initial_state, erase, chunk):
+        o, S, ws = chunk_fwd_train(q, k, v, beta, log_alpha, initial_state, chunk=chunk,
+                                   erase=erase)
+        ctx.save_for_backward(q, k, v, beta, log_alpha, initial_state)
+        ctx.ws, ctx.erase, ctx.chunk = ws, erase, chunk
+        return o, S
+
+    @staticmethod
+    def backward(ctx, d_o, d_final):
+        q, k, v, beta, log_alpha, initial_state = ctx.saved_tensors
+        # the kernels take dL/do in the dtype of q (exact MFMA operands)
+        d_o = torch.zeros_like(v) if d_o is None else d_o.to(q.dtype).contiguous()
+        d_final = None if d_final is None else d_final.float().contiguous()
+        g = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final, chunk=ctx.chunk,
+                      erase=ctx.erase, workspace=ctx.ws, saved=True,
+                      want_d_initial_state=initial_state is not None)
+        ctx.ws = None
+
+        def like(x, t):
+            return None if x is None or t is None else x.to(t.dtype)
+        return (like(g["dq"], q), like(g["dk"], k), like(g["dv"], v), g["dbeta"],
+                g["dlog_alpha"], g["d_initial_state"], None, None)
+
+
+def chunk_gated_delta_rule(q, k, v, beta, log_alpha=None, initial_state=None, *, erase=True,
+                           chunk=0):
+    """Differentiable chunkwise forward: (o [B, T, H, Dv] fp32, final state
+    [B, H, Dk, Dv] fp32), with gradients for q, k, v, beta, log_alpha and
+    initial_state from chunk_bwd.  Inputs as for chunk_fwd_train (bf16
+    q/k/v, Dk = Dv in {64, 128}, every gate, erase or not).  The upstream
+    gradient of o is rounded to the dtype of q before the backward kernels
+    read it; the backward's workspace (chunk_bwd_workspace_bytes) is held
+    from the forward until the backward has run.
+    """
+    return _ChunkRule.apply(q, k, v, beta, log_alpha, initial_state, erase, int(chunk))

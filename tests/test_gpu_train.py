@@ -160,3 +160,35 @@ def test_saved_backward_needs_the_workspace():
     inp = make_case(1, 8, 1, 64, "scalar", seed=1)
     with pytest.raises(ValueError):
         gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"], saved=True)
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_autograd_function_gives_the_kernels_gradients(gate):
+    """loss.backward() through chunk_gated_delta_rule: every input gradient is
+    chunk_bwd's for the same upstream gradients (bitwise, cast to the input
+    dtypes), and within the 2e-3 bar of the oracle."""
+    say("autograd", gate)
+    inp = make_case(2, 70, 2, 64, gate, seed=13)
+    leaves = {n: inp[n].detach().clone().requires_grad_(True)
+              for n in ("q", "k", "v", "beta", "log_alpha", "initial_state")
+              if inp[n] is not None}
+    get = lambda n: leaves.get(n)
+    o, S = gdr.chunk_gated_delta_rule(get("q"), get("k"), get("v"), get("beta"),
+                                      get("log_alpha"), get("initial_state"))
+    w_o = inp["d_o"].float()
+    w_s = inp["d_final_state"]
+    ((o * w_o).sum() + (S * w_s).sum()).backward()
+    torch.cuda.synchronize()
+    ref = gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"])
+    torch.cuda.synchronize()
+    pairs = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta"),
+             ("initial_state", "d_initial_state")]
+    if gate != "none":
+        pairs.append(("log_alpha", "dlog_alpha"))
+    orc = oracle_bwd(inp, True)
+    orc["d_initial_state"] = orc.pop("dS0")
+    for n, g in pairs:
+        got = leaves[n].grad
+        assert got is not None and got.dtype == leaves[n].dtype, n
+        assert torch.equal(got, ref[g].to(got.dtype)), n
+        assert rel_err(ref[g], orc[g]) <= TOL, n
