@@ -331,7 +331,8 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
 
 class _ChunkRule(torch.autograd.Function):
     """chunk_fwd_train in the forward, chunk_bwd(saved=True) in the backward;
-    the workspace lives on the autograd graph between the two."""
+    the workspace lives on the autograd graph between the two (released with
+    the graph, so a retained graph can be differentiated again)."""
 
     @staticmethod
     def forward(ctx, q, k, v, beta, log_alpha, initial_state, erase, chunk):
@@ -350,7 +351,6 @@ class _ChunkRule(torch.autograd.Function):
         g = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final, chunk=ctx.chunk,
                       erase=ctx.erase, workspace=ctx.ws, saved=True,
                       want_d_initial_state=initial_state is not None)
-        ctx.ws = None
 
         def like(x, t):
             return None if x is None or t is None else x.to(t.dtype)
