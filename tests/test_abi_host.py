@@ -40,6 +40,12 @@ def test_library_exports_every_declared_symbol():
     assert _abi.abi_version() == _abi.ABI_VERSION == 3
 
 
+def test_build_entry_accepts_the_built_library():
+    """The check build() runs after compiling passes on the built library."""
+    import __graft_entry__
+    __graft_entry__.check_loaded()
+
+
 def test_status_strings():
     for st in (0, -1, -2, -3, -4):
         assert _abi.status_str(st).startswith("GDR_")
