@@ -302,9 +302,11 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
         for n, shp in shapes.items():
             t = out.get(n)
             if shp is None:
-                if t is not None and n == "dlog_alpha":
-                    raise ValueError("dlog_alpha must be None without a gate")
-                out[n] = t if n == "d_initial_state" else None
+                if t is not None:
+                    raise ValueError("dlog_alpha must be None without a gate" if n == "dlog_alpha"
+                                     else "d_initial_state must be None when "
+                                          "want_d_initial_state is False")
+                out[n] = None
                 continue
             _check_dev(n, t, torch.float32)
             if tuple(t.shape) != shp:

@@ -147,6 +147,13 @@ def test_backward_without_initial_state_gradient():
     assert out["d_initial_state"] is None
     ref = oracle(inp)
     assert rel_err(f64(out["dq"]), ref["dq"]) <= TOL
+    # a d_initial_state buffer in `out` is refused rather than written unchecked
+    buf = {n: torch.empty_like(t) for n, t in out.items() if t is not None}
+    buf["d_initial_state"] = torch.empty(1, device=DEV)
+    with pytest.raises(ValueError):
+        gdr.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                      inp["initial_state"], inp["d_o"], inp["d_final_state"],
+                      want_d_initial_state=False, out=buf)
 
 
 def test_backward_headline_shape_sampled_chains():
