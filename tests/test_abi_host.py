@@ -164,6 +164,31 @@ def test_chunk_fwd_size_bound_with_fused_gate(gate, H):
         _abi.GDR_EUNSUPPORTED
 
 
+def test_chunk_bwd_refuses_an_unrequested_initial_state_buffer(monkeypatch):
+    """With want_d_initial_state=False a d_initial_state buffer in `out` raises
+    before any launch instead of being handed to the kernel unchecked (it
+    would be written with B*H*Dk*Dv floats whatever its size)."""
+    import torch
+    import gated_delta_rule_28_amd as gdr
+
+    def host_check(name, t, dtype=None):
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(name)
+
+    called = []
+    monkeypatch.setattr(gdr, "_check_dev", host_check)
+    monkeypatch.setattr(_abi, "gdr_chunk_bwd", lambda *a: called.append(a) or 0)
+    B, T, H, D = 1, 8, 2, 64
+    q = torch.zeros(B, T, H, D, dtype=torch.bfloat16)
+    beta = torch.zeros(B, T, H)
+    out = {"dq": torch.zeros(B, T, H, D), "dk": torch.zeros(B, T, H, D),
+           "dv": torch.zeros(B, T, H, D), "dbeta": torch.zeros(B, T, H),
+           "dlog_alpha": None, "d_initial_state": torch.zeros(1)}
+    with pytest.raises(ValueError, match="d_initial_state"):
+        gdr.chunk_bwd(q, q, q, beta, None, None, q, None, want_d_initial_state=False, out=out)
+    assert not called
+
+
 def test_recurrent_step_checks_output_shape_before_launch(monkeypatch):
     """A preallocated o of the wrong shape raises in Python and the C entry
     point is never called (a smaller o would be written past its end)."""
