@@ -794,14 +794,14 @@ chunk_fwd_bf16_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = i * RPI + lane / BPR, sb = lane % BPR;
-      voff[i] = (unsigned)(row * H * DV * 2 + 2 * slice * DVS + 16 * (sb ^ swz_v<VB>(row)));
+      voff[i] = (unsigned)row * (2u * H * DV) + (unsigned)(2 * slice * DVS + 16 * (sb ^ swz_v<VB>(row)));
     }
   } else {
     constexpr int BPR = QRB / 16, RPI = 1024 / QRB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = i * RPI + lane / BPR, sb = lane % BPR;
-      voff[i] = (unsigned)(row * H * DK * 2 + 16 * (sb ^ swz_qk<QB>(row)));
+      voff[i] = (unsigned)row * (2u * H * DK) + (unsigned)(16 * (sb ^ swz_qk<QB>(row)));
     }
   }
   const unsigned soff = (unsigned)(lane * H * 4);   // log a / b of token `lane`

@@ -656,21 +656,21 @@ chunk_fwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = i * RPI + lane / BPR;
-      voff[i] = (unsigned)(row * H * DK * 4 + 16 * (lane % BPR));
+      voff[i] = (unsigned)row * (4u * H * DK) + 16u * (lane % BPR);
     }
   } else if (pw == 1) {
     constexpr int BPR = QRB / 16, RPI = 1024 / QRB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = i * RPI + lane / BPR;
-      voff[i] = (unsigned)(row * H * DK * 2 + 16 * (lane % BPR));
+      voff[i] = (unsigned)row * (2u * H * DK) + 16u * (lane % BPR);
     }
   } else {
     constexpr int BPR = VRB / 16, RPI = 1024 / VRB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = i * RPI + lane / BPR, sb = lane % BPR;
-      voff[i] = (unsigned)(row * H * DV * 2 + 2 * slice * DVS + 16 * (sb ^ swz_v<VB>(row)));
+      voff[i] = (unsigned)row * (2u * H * DV) + (unsigned)(2 * slice * DVS + 16 * (sb ^ swz_v<VB>(row)));
     }
   }
   const unsigned soff = (unsigned)(lane * H * 4);   // b of token `lane`
