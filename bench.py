@@ -559,14 +559,15 @@ def sampled_parity(torch, W, kept, chains, tol=PARITY_TOL):
             "against": "fp64 oracle recurrence on the timed run's inputs, whole sequences"}
 
 
-def bwd_alg_bytes(w):
+def bwd_alg_bytes(w, grad_b=4):
     """Single-pass minimum HBM bytes of one chunk_bwd call (zero initial state,
     no loss on the final state, dS_0 written): q, k, v, dO in (input dtype),
-    beta and log alpha in, dq, dk, dv (fp32) out, dbeta and dlog alpha out
-    (log alpha and its gradient per channel with the per-channel gate)."""
+    beta and log alpha in, dq, dk, dv out (grad_b bytes each: fp32 or bf16),
+    dbeta and dlog alpha out (log alpha and its gradient per channel with the
+    per-channel gate)."""
     th = w.B * w.T * w.H
     in_b = 2 if w.in_dtype == "bf16" else 4
-    per_th = in_b * (2 * w.Dk + 2 * w.Dv) + 4 + 4 * (2 * w.Dk + w.Dv) + 4
+    per_th = in_b * (2 * w.Dk + 2 * w.Dv) + 4 + grad_b * (2 * w.Dk + w.Dv) + 4
     if w.gate == "scalar":
         per_th += 8
     elif w.gate == "channel":
@@ -603,14 +604,30 @@ def train_line(torch, gdr, W, w, steps, warmup, settle_s=0.0):
     def saved():
         gdr.chunk_fwd_train(*a, o=o, final_state=S, workspace=ws)
         gdr.chunk_bwd(*a, d_o, None, workspace=ws, out=out, saved=True)
+    bf = dict(device="cuda", dtype=torch.bfloat16)
+    out_b = dict(out, dq=torch.empty(w.B, w.T, w.H, w.Dk, **bf),
+                 dk=torch.empty(w.B, w.T, w.H, w.Dk, **bf), dv=torch.empty(w.B, w.T, w.H, w.Dv, **bf))
+
+    def saved_bf16():
+        gdr.chunk_fwd_train(*a, o=o, final_state=S, workspace=ws)
+        gdr.chunk_bwd(*a, d_o, None, workspace=ws, out=out_b, saved=True,
+                      grad_dtype=torch.bfloat16)
+    def saved_cast():   # fp32 gradients cast to the bf16 of the inputs afterwards
+        saved()
+        for n in ("dq", "dk", "dv"):
+            out[n].to(torch.bfloat16)
     res = {"workload": w.name, "unit": "tokens/s"}
-    for key, fn in (("recompute", plain), ("saved", saved)):
+    for key, fn in (("recompute", plain), ("saved", saved), ("saved_fp32_grads_cast", saved_cast),
+                    ("saved_bf16_grads", saved_bf16)):
         _, per = time_launches(torch, fn, steps, warmup, settle_s)
         ms = statistics.fmean(per)
         res[key] = {"ms": ms, "value": w.B * w.T / (ms * 1e-3)}
-    res["value"] = res["saved"]["value"]
+    res["value"] = res["saved_bf16_grads"]["value"]
     res["note"] = ("forward + backward of the chunk layer per step: chunk_fwd + chunk_bwd "
-                   "(recompute), chunk_fwd_train + chunk_bwd(saved=True) (saved)")
+                   "(recompute), chunk_fwd_train + chunk_bwd(saved=True) (saved), the same "
+                   "with dq, dk, dv cast to bf16 afterwards (saved_fp32_grads_cast) and written "
+                   "as bf16 by the kernels (saved_bf16_grads, the value: what the autograd "
+                   "wrapper runs)")
     return res
 
 
@@ -634,13 +651,27 @@ def bwd_line(torch, gdr, W, w, steps, warmup, settle_s=0.0, chains=((0, 0), (7, 
                           else torch.empty(*inp["log_alpha"].shape, **f32)),
            "d_initial_state": torch.empty(w.B, w.H, w.Dk, w.Dv, **f32)}
 
+    bf = dict(device="cuda", dtype=torch.bfloat16)
+    out_b = dict(out, dq=torch.empty(w.B, w.T, w.H, w.Dk, **bf),
+                 dk=torch.empty(w.B, w.T, w.H, w.Dk, **bf), dv=torch.empty(w.B, w.T, w.H, w.Dv, **bf))
+
+    def step_b():   # dq, dk, dv written as bf16 (what a bf16 training step keeps)
+        gdr.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None, d_o,
+                      None, workspace=ws, out=out_b, grad_dtype=torch.bfloat16)
+    _, per_b = time_launches(torch, step_b, steps, warmup, settle_s)
+
     def step():
         gdr.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], None, d_o,
                       None, workspace=ws, out=out)
     wall, per = time_launches(torch, step, steps, warmup, settle_s)
+    torch.cuda.synchronize()
+    rounded = all(torch.equal(out_b[n], out[n].to(torch.bfloat16)) for n in ("dq", "dk", "dv"))
     mean_ms = statistics.fmean(per)
     alg_b = bwd_alg_bytes(w)
     achieved = alg_b / (mean_ms * 1e-3) / 1e9
+    mean_b = statistics.fmean(per_b)
+    alg_bb = bwd_alg_bytes(w, grad_b=2)
+    achieved_b = alg_bb / (mean_b * 1e-3) / 1e9
     # sampled chains against the oracle
     errs = {}
     for b, h in chains:
@@ -672,6 +703,15 @@ def bwd_line(torch, gdr, W, w, steps, warmup, settle_s=0.0, chains=((0, 0), (7, 
         "parity": {"max_abs_over_rms": errs, "tol": PARITY_TOL,
                    "chains_checked": [list(c) for c in chains], "chains_total": w.B * w.H,
                    "pass": bool(all(v <= PARITY_TOL for v in errs.values()))},
+        "bf16_grads": {
+            "value": w.B * w.T / (mean_b * 1e-3),
+            "kernel_ms": {"mean": mean_b, "median": statistics.median(per_b), "min": min(per_b)},
+            "roofline": {"bound": "hbm", "achieved": achieved_b, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved_b / HBM_PEAK_GBS,
+                         "alg_bytes_per_launch": alg_bb},
+            "equals_fp32_rounded": bool(rounded),
+            "note": "grad_dtype=bf16: dq, dk, dv written as bf16 (the fp32 values rounded to "
+                    "nearest even; every element compared with the fp32 call's)"},
     }
 
 

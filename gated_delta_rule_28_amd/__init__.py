@@ -250,13 +250,14 @@ def chunk_bwd_workspace_bytes(q, log_alpha=None, chunk=0, erase=True):
 
 def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_final_state=None,
               *, chunk=0, erase=True, workspace=None, want_d_initial_state=True, out=None,
-              saved=False):
+              saved=False, grad_dtype=torch.float32):
     """Gradients of chunk_fwd's o and final state.
 
     Inputs as for chunk_fwd (bf16 q/k/v, Dk = Dv in {64, 128}, every gate,
     with or without the erase term); d_o [B, T, H, Dv] in the dtype of q
     (None for zero) and d_final_state [B, H, Dk, Dv] fp32 (None for zero).
-    Returns a dict with dq, dk, dv (fp32, shaped like q, k, v), dbeta
+    Returns a dict with dq, dk, dv (grad_dtype: fp32 or bf16, each the fp32
+    gradient rounded to nearest even; shaped like q, k, v), dbeta
     [B, T, H], dlog_alpha (None without a gate, else shaped like log_alpha)
     and d_initial_state
     [B, H, Dk, Dv] (None when want_d_initial_state is False).  `workspace`,
@@ -266,6 +267,8 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     saved=True: `workspace` is the one chunk_fwd_train filled for these same
     inputs; the recompute pass is skipped.
     """
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("grad_dtype must be torch.float32 or torch.bfloat16")
     _check_dev("q", q)
     if q.dtype not in _DT:
         raise TypeError("q/k/v must be bf16 or fp32")
@@ -291,13 +294,14 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
     _check_dev("d_o", d_o, q.dtype)
     if tuple(d_o.shape) != (B, T, H, Dv):
         raise ValueError("d_o must be [B, T, H, Dv]")
-    f32 = dict(device=q.device, dtype=torch.float32)
     shapes = {"dq": (B, T, H, Dk), "dk": (B, T, H, Dk), "dv": (B, T, H, Dv),
               "dbeta": (B, T, H),
               "dlog_alpha": None if log_alpha is None else tuple(log_alpha.shape),
               "d_initial_state": (B, H, Dk, Dv) if want_d_initial_state else None}
+    dtypes = {n: grad_dtype if n in ("dq", "dk", "dv") else torch.float32 for n in shapes}
     if out is None:
-        out = {n: None if shp is None else torch.empty(*shp, **f32) for n, shp in shapes.items()}
+        out = {n: None if shp is None else torch.empty(*shp, device=q.device, dtype=dtypes[n])
+               for n, shp in shapes.items()}
     else:
         for n, shp in shapes.items():
             t = out.get(n)
@@ -308,7 +312,7 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
                                           "want_d_initial_state is False")
                 out[n] = None
                 continue
-            _check_dev(n, t, torch.float32)
+            _check_dev(n, t, dtypes[n])
             if tuple(t.shape) != shp:
                 raise ValueError(f"{n} must be {shp}")
     need = int(_abi.gdr_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate))
@@ -318,16 +322,21 @@ def chunk_bwd(q, k, v, beta, log_alpha=None, initial_state=None, d_o=None, d_fin
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     else:
         _check_dev("workspace", workspace, torch.uint8)
-    fn = _abi.gdr_chunk_bwd_saved if saved else _abi.gdr_chunk_bwd
-    st = fn(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate, q.data_ptr(),
-                            k.data_ptr(), v.data_ptr(), beta.data_ptr(), _ptr(log_alpha),
-                            _ptr(initial_state), d_o.data_ptr(), _ptr(d_final_state),
-                            out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(),
-                            out["dbeta"].data_ptr(), _ptr(out["dlog_alpha"]),
-                            _ptr(out["d_initial_state"]), workspace.data_ptr(),
-                            workspace.numel(), _stream(q.device))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(), _ptr(log_alpha),
+            _ptr(initial_state), d_o.data_ptr(), _ptr(d_final_state), out["dq"].data_ptr(),
+            out["dk"].data_ptr(), out["dv"].data_ptr(), out["dbeta"].data_ptr(),
+            _ptr(out["dlog_alpha"]), _ptr(out["d_initial_state"]), workspace.data_ptr(),
+            workspace.numel())
+    if grad_dtype == torch.float32:   # the fp32 entry points
+        name = "gdr_chunk_bwd_saved" if saved else "gdr_chunk_bwd"
+        st = getattr(_abi, name)(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], gate, *ptrs,
+                                 _stream(q.device))
+    else:
+        name = "gdr_chunk_bwd_ex"
+        st = _abi.gdr_chunk_bwd_ex(B, T, H, Dk, Dv, int(chunk), _DT[q.dtype], _DT[grad_dtype],
+                                   gate, *ptrs, saved, _stream(q.device))
     if st != _abi.GDR_OK:
-        raise GdrError(st, "gdr_chunk_bwd_saved" if saved else "gdr_chunk_bwd")
+        raise GdrError(st, name)
     return out
 
 
@@ -350,9 +359,10 @@ class _ChunkRule(torch.autograd.Function):
         # the kernels take dL/do in the dtype of q (exact MFMA operands)
         d_o = torch.zeros_like(v) if d_o is None else d_o.to(q.dtype).contiguous()
         d_final = None if d_final is None else d_final.float().contiguous()
+        # dq, dk, dv come out of the kernels in the dtype of q, k, v
         g = chunk_bwd(q, k, v, beta, log_alpha, initial_state, d_o, d_final, chunk=ctx.chunk,
                       erase=ctx.erase, workspace=ctx.ws, saved=True,
-                      want_d_initial_state=initial_state is not None)
+                      want_d_initial_state=initial_state is not None, grad_dtype=q.dtype)
 
         def like(x, t):
             return None if x is None or t is None else x.to(t.dtype)

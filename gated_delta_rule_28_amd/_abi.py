@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EHIP, GDR_EWORKSPACE = 0, -1, -2, -3, -4
-ABI_VERSION = 3
+ABI_VERSION = 4
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_NONE, GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1, 2
 GDR_NO_ERASE = 0x100   # OR'd into a gate: additive write, no erase term
@@ -35,6 +35,7 @@ SIGNATURES = {
     "gdr_chunk_bwd_noalloc": (_c_int, [_c_int] * 8 + [_vp] * 15),
     "gdr_chunk_fwd_train": (_c_int, [_c_int] * 9 + [_vp] * 9 + [_sz, _vp]),
     "gdr_chunk_bwd_saved": (_c_int, [_c_int] * 8 + [_vp] * 15 + [_sz, _vp]),
+    "gdr_chunk_bwd_ex": (_c_int, [_c_int] * 9 + [_vp] * 15 + [_sz, _c_int, _vp]),
 }
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -142,6 +143,16 @@ def gdr_chunk_bwd_saved(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, l
                                       log_alpha, initial_state, d_o, d_final_state, dq, dk, dv,
                                       dbeta, dlog_alpha, d_initial_state, workspace,
                                       workspace_bytes, stream)
+
+
+def gdr_chunk_bwd_ex(B, T, H, Dk, Dv, chunk, in_dtype, grad_dtype, gate, q, k, v, beta,
+                     log_alpha, initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                     d_initial_state, workspace, workspace_bytes, saved, stream):
+    """Raw call of the C entry point with integer sizes and raw pointers."""
+    return load().gdr_chunk_bwd_ex(B, T, H, Dk, Dv, chunk, in_dtype, grad_dtype, gate, q, k, v,
+                                   beta, log_alpha, initial_state, d_o, d_final_state, dq, dk,
+                                   dv, dbeta, dlog_alpha, d_initial_state, workspace,
+                                   workspace_bytes, int(saved), stream)
 
 
 def gdr_chunk_bwd_noalloc(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,

@@ -172,16 +172,17 @@ void bwd_partitions(gdr::BwdArgs &a, void *workspace) {
   a.ws_dy = a.ws_u + nblk * C * a.D;
 }
 
-// gdr_chunk_bwd, and with saved = true gdr_chunk_bwd_saved (the workspace
-// holds h and U from gdr_chunk_fwd_train: no recompute pass)
-int chunk_bwd_impl(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
-                   const void *q, const void *k, const void *v, const float *beta,
+// gdr_chunk_bwd_ex: gdr_chunk_bwd with dq, dk, dv in grad_dtype, and with
+// saved = true gdr_chunk_bwd_saved (the workspace holds h and U from
+// gdr_chunk_fwd_train: no recompute pass)
+int chunk_bwd_impl(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int grad_dtype,
+                   int gate, const void *q, const void *k, const void *v, const float *beta,
                    const float *log_alpha, const float *initial_state, const void *d_o,
-                   const float *d_final_state, float *dq, float *dk, float *dv, float *dbeta,
+                   const float *d_final_state, void *dq, void *dk, void *dv, float *dbeta,
                    float *dlog_alpha, float *d_initial_state, void *workspace,
                    size_t workspace_bytes, hipStream_t stream, bool saved) {
   if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDR_EINVAL;
-  if (!valid_dtype(in_dtype) || !valid_gate(gate)) return GDR_EINVAL;
+  if (!valid_dtype(in_dtype) || !valid_dtype(grad_dtype) || !valid_gate(gate)) return GDR_EINVAL;
   if ((gate_kind(gate) == GDR_GATE_NONE) != (log_alpha == nullptr)) return GDR_EINVAL;
   if ((gate_kind(gate) == GDR_GATE_NONE) != (dlog_alpha == nullptr)) return GDR_EINVAL;
   if ((initial_state && !aligned16(initial_state)) || (d_final_state && !aligned16(d_final_state)) ||
@@ -210,7 +211,8 @@ int chunk_bwd_impl(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,
   a.erase = erases(gate);
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
   a.initial_state = initial_state; a.d_o = d_o; a.d_final_state = d_final_state;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.grad_bf16 = grad_dtype == GDR_BF16;
+  a.dbeta = dbeta; a.dlog_alpha = dlog_alpha;
   a.d_initial_state = d_initial_state;
   a.saved = saved;
   bwd_partitions(a, workspace);
@@ -229,9 +231,21 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
                   const float *d_final_state, float *dq, float *dk, float *dv, float *dbeta,
                   float *dlog_alpha, float *d_initial_state, void *workspace,
                   size_t workspace_bytes, hipStream_t stream) {
-  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
-                        initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
-                        d_initial_state, workspace, workspace_bytes, stream, false);
+  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, GDR_F32, gate, q, k, v, beta,
+                        log_alpha, initial_state, d_o, d_final_state, dq, dk, dv, dbeta,
+                        dlog_alpha, d_initial_state, workspace, workspace_bytes, stream, false);
+}
+
+int gdr_chunk_bwd_ex(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,
+                     int grad_dtype, int gate, const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_alpha, const float *initial_state,
+                     const void *d_o, const float *d_final_state, void *dq, void *dk, void *dv,
+                     float *dbeta, float *dlog_alpha, float *d_initial_state, void *workspace,
+                     size_t workspace_bytes, int saved, hipStream_t stream) {
+  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, grad_dtype, gate, q, k, v, beta,
+                        log_alpha, initial_state, d_o, d_final_state, dq, dk, dv, dbeta,
+                        dlog_alpha, d_initial_state, workspace, workspace_bytes, stream,
+                        saved != 0);
 }
 
 int gdr_chunk_bwd_saved(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, int gate,
@@ -240,9 +254,9 @@ int gdr_chunk_bwd_saved(int B, int T, int H, int Dk, int Dv, int chunk, int in_d
                         const float *d_final_state, float *dq, float *dk, float *dv,
                         float *dbeta, float *dlog_alpha, float *d_initial_state,
                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, gate, q, k, v, beta, log_alpha,
-                        initial_state, d_o, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
-                        d_initial_state, workspace, workspace_bytes, stream, true);
+  return chunk_bwd_impl(B, T, H, Dk, Dv, chunk, in_dtype, GDR_F32, gate, q, k, v, beta,
+                        log_alpha, initial_state, d_o, d_final_state, dq, dk, dv, dbeta,
+                        dlog_alpha, d_initial_state, workspace, workspace_bytes, stream, true);
 }
 
 int gdr_chunk_fwd_train(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,

@@ -86,7 +86,7 @@ __device__ __forceinline__ float dot8_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf1
   return acc;
 }
 
-template <int DK, int GATE, bool ERASE>
+template <int DK, int GATE, bool ERASE, typename GT>
 __global__ void __launch_bounds__(64 * NW, 2)
 chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ v, const float *__restrict__ beta,
@@ -94,7 +94,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                       const bf16 *__restrict__ d_o, const float *__restrict__ ws_h,
                       const float *__restrict__ ws_u,
                       const float *__restrict__ ws_dh, const float *__restrict__ ws_dy,
-                      float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+                      GT *__restrict__ dq, GT *__restrict__ dk, GT *__restrict__ dv,
                       float *__restrict__ dbeta, float *__restrict__ dlog_alpha, int B, int T,
                       int H) {
   constexpr int DV = DK;
@@ -200,7 +200,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
       *reinterpret_cast<bf16x4 *>(&sm.Yl[r][col]) = l4;
       dot += (y[j][0] * (float)vr[j][0] + y[j][1] * (float)vr[j][1]) +
              (y[j][2] * (float)vr[j][2] + y[j][3] * (float)vr[j][3]);
-      if (r < n) *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + col) = y[j] * b;
+      if (r < n) st4(dv + trow(r) * DV + col, y[j] * b);
     }
     dot += __shfl_xor(dot, 1);
     dot += __shfl_xor(dot, 2);
@@ -343,7 +343,7 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // dq and dk rows of this chunk: a buffer range that ends at the last valid
     // row, so stores to rows past the sequence's end are dropped (the host
     // bounds one chunk's rows below 4 GiB)
-    const unsigned rows_bytes = 4u * ((unsigned)(n - 1) * (unsigned)(H * DK) + DK);
+    const unsigned rows_bytes = (unsigned)sizeof(GT) * ((unsigned)(n - 1) * (unsigned)(H * DK) + DK);
     const rsrc_t rdq = make_rsrc32(dq + row0 * DK, rows_bytes);
     const rsrc_t rdk = make_rsrc32(dk + row0 * DK, rows_bytes);
     // the n x n x dk products, then dQ, dK and the dg terms of one tile
@@ -397,9 +397,9 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
           const float gq = gm4[e] * aq[rb][e];
           const float gr = ERASE ? gm4[e] * b4[e] * ar[rb][e] : 0.0f;
           const float gu = ec4[e] * au[rb][e];
-          const unsigned off = 4u * ((unsigned)r * (unsigned)(H * DK) + (unsigned)col);
-          buf_st1(gq + xq[e], rdq, off);
-          buf_st1(gu - gr + xk[e], rdk, off);
+          const unsigned off = (unsigned)sizeof(GT) * ((unsigned)r * (unsigned)(H * DK) + (unsigned)col);
+          buf_st1(GT(gq + xq[e]), rdq, off);
+          buf_st1(GT(gu - gr + xk[e]), rdk, off);
           const float kv = (float)sm.K[r][col];
           if constexpr (ERASE) partb[rb][e] += kv * (gm4[e] * ar[rb][e]);
           if constexpr (GATE == kGateScalar) {
@@ -485,16 +485,15 @@ chunk_bwd_grad_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 }
 
-template <int DK>
+template <int DK, typename GT>
 hipError_t launch_dk(const BwdArgs &a) {
   const int nchunks = (a.T + C - 1) / C;
   dim3 grid((unsigned)((long)a.B * a.H * nchunks)), block(64 * NW);
 #define GDR_LAUNCH(G, E)                                                                        \
-  hipLaunchKernelGGL((chunk_bwd_grad_kernel<DK, G, E>), grid, block, 0, a.stream,               \
+  hipLaunchKernelGGL((chunk_bwd_grad_kernel<DK, G, E, GT>), grid, block, 0, a.stream,           \
                      (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,          \
-                     a.log_alpha, (const bf16 *)a.d_o, a.ws_h, a.ws_u, a.ws_dh, a.ws_dy, a.dq,  \
-                     a.dk,                                                                     \
-                     a.dv, a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
+                     a.log_alpha, (const bf16 *)a.d_o, a.ws_h, a.ws_u, a.ws_dh, a.ws_dy,        \
+                     (GT *)a.dq, (GT *)a.dk, (GT *)a.dv, a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
   if (a.erase) {
     if (a.gate == kGateNone) GDR_LAUNCH(kGateNone, true);
     else GDR_LAUNCH(kGateScalar, true);
@@ -506,10 +505,15 @@ hipError_t launch_dk(const BwdArgs &a) {
   return hipGetLastError();
 }
 
+template <int DK>
+hipError_t launch_dk_by_grad(const BwdArgs &a) {
+  return a.grad_bf16 ? launch_dk<DK, bf16>(a) : launch_dk<DK, float>(a);
+}
+
 }  // namespace
 
 hipError_t launch_chunk_bwd_grads(const BwdArgs &a) {
-  return a.D == 128 ? launch_dk<128>(a) : launch_dk<64>(a);
+  return a.D == 128 ? launch_dk_by_grad<128>(a) : launch_dk_by_grad<64>(a);
 }
 
 }  // namespace gdr

@@ -78,14 +78,14 @@ __device__ __forceinline__ void split1(float x, bf16 &h, bf16 &l) {
   l = (bf16)(x - (float)h);
 }
 
-template <int DK, bool ERASE>
+template <int DK, bool ERASE, typename GT>
 __global__ void __launch_bounds__(64 * NW, 2)
 chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
                      const bf16 *__restrict__ v, const float *__restrict__ beta,
                      const float *__restrict__ log_alpha, const bf16 *__restrict__ d_o,
                      const float *__restrict__ ws_h, const float *__restrict__ ws_u,
                      const float *__restrict__ ws_dh, const float *__restrict__ ws_dy,
-                     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+                     GT *__restrict__ dq, GT *__restrict__ dk, GT *__restrict__ dv,
                      float *__restrict__ dbeta, float *__restrict__ dlog_alpha, int B, int T,
                      int H) {
   constexpr int DV = DK;
@@ -157,8 +157,8 @@ chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         sm.beta[r] = b;
       }
       if (ok) {
-        *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + c8) = y0 * b;
-        *reinterpret_cast<f32x4 *>(dv + trow(r) * DV + c8 + 4) = y1 * b;
+        st4(dv + trow(r) * DV + c8, y0 * b);
+        st4(dv + trow(r) * DV + c8 + 4, y1 * b);
       }
     }
   }
@@ -303,7 +303,7 @@ chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
     // dq and dk rows of this chunk: a buffer range that ends at the last valid
     // row, so stores to rows past the sequence's end are dropped (the host
     // bounds one chunk's rows below 4 GiB)
-    const unsigned rows_bytes = 4u * ((unsigned)(n - 1) * (unsigned)(H * DK) + DK);
+    const unsigned rows_bytes = (unsigned)sizeof(GT) * ((unsigned)(n - 1) * (unsigned)(H * DK) + DK);
     const rsrc_t rdq = make_rsrc32(dq + row0 * DK, rows_bytes);
     const rsrc_t rdk = make_rsrc32(dk + row0 * DK, rows_bytes);
     float dbpart[4] = {0.f, 0.f, 0.f, 0.f};
@@ -431,9 +431,9 @@ chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
         const float dqv = eg * aq[e] + xp[e];
         const float kpart = eg * dkh + xm[e];
         const float ku = ekb * au[e];
-        const unsigned off = 4u * ((unsigned)r * (unsigned)(H * DK) + (unsigned)ch);
-        buf_st1(dqv, rdq, off);
-        buf_st1(kpart + yf[e] + ku, rdk, off);
+        const unsigned off = (unsigned)sizeof(GT) * ((unsigned)r * (unsigned)(H * DK) + (unsigned)ch);
+        buf_st1(GT(dqv), rdq, off);
+        buf_st1(GT(kpart + yf[e] + ku), rdk, off);
         sm.G[r][ch] = qv * dqv + kv * (kpart - yf[e] - ku);
         if constexpr (ERASE) dbpart[e] += kv * eg * ar[e];
         tl += kv * ku;
@@ -473,15 +473,15 @@ chunk_bwd_kda_kernel(const bf16 *__restrict__ q, const bf16 *__restrict__ k,
   }
 }
 
-template <int DK>
+template <int DK, typename GT>
 hipError_t launch_kda_grads(const BwdArgs &a) {
   const int nchunks = (a.T + C - 1) / C;
   dim3 grid((unsigned)((long)a.B * a.H * nchunks)), block(64 * NW);
 #define GDR_LAUNCH(E)                                                                           \
-  hipLaunchKernelGGL((chunk_bwd_kda_kernel<DK, E>), grid, block, 0, a.stream, (const bf16 *)a.q, \
-                     (const bf16 *)a.k, (const bf16 *)a.v, a.beta, a.log_alpha,                   \
-                     (const bf16 *)a.d_o, a.ws_h, a.ws_u, a.ws_dh, a.ws_dy, a.dq, a.dk, a.dv,     \
-                     a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
+  hipLaunchKernelGGL((chunk_bwd_kda_kernel<DK, E, GT>), grid, block, 0, a.stream,               \
+                     (const bf16 *)a.q, (const bf16 *)a.k, (const bf16 *)a.v, a.beta,           \
+                     a.log_alpha, (const bf16 *)a.d_o, a.ws_h, a.ws_u, a.ws_dh, a.ws_dy,         \
+                     (GT *)a.dq, (GT *)a.dk, (GT *)a.dv, a.dbeta, a.dlog_alpha, a.B, a.T, a.H)
   if (a.erase) GDR_LAUNCH(true);
   else GDR_LAUNCH(false);
 #undef GDR_LAUNCH
@@ -491,7 +491,8 @@ hipError_t launch_kda_grads(const BwdArgs &a) {
 }  // namespace
 
 hipError_t launch_chunk_bwd_kda_grads(const BwdArgs &a) {
-  return a.D == 128 ? launch_kda_grads<128>(a) : launch_kda_grads<64>(a);
+  if (a.grad_bf16) return a.D == 128 ? launch_kda_grads<128, bf16>(a) : launch_kda_grads<64, bf16>(a);
+  return a.D == 128 ? launch_kda_grads<128, float>(a) : launch_kda_grads<64, float>(a);
 }
 
 }  // namespace gdr

@@ -65,7 +65,9 @@ struct BwdArgs {
   const float *initial_state;   // S_0 or nullptr
   const void *d_o;              // dL/do [B, T, H, D], dtype of q
   const float *d_final_state;   // dL/dS_T or nullptr
-  float *dq, *dk, *dv, *dbeta, *dlog_alpha, *d_initial_state;
+  void *dq, *dk, *dv;            // fp32, or bf16 when grad_bf16
+  bool grad_bf16;
+  float *dbeta, *dlog_alpha, *d_initial_state;
   // workspace partitions, per (chain, chunk): the entering state h and U
   // (recompute pass); dh and dY (reverse pass); each chunk's block in the
   // state waves' fragment order (ws_frag, mfma_util.h)

@@ -209,6 +209,14 @@ __device__ __forceinline__ void buf_st1(bf16 x, rsrc_t r, unsigned off) {
                                         __builtin_bit_cast(int, off), 0, 0);
 }
 
+// four adjacent values of a row at a global address, fp32 or bf16 (rounded
+// to nearest even): one 16-byte or 8-byte store
+__device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+__device__ __forceinline__ void st4(bf16 *p, f32x4 x) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<bf16x4_t *>(p) = __builtin_convertvector(x, bf16x4_t);
+}
+
 // four adjacent output values of a row in one 16-byte (fp32) or 8-byte
 // (bf16) store
 __device__ __forceinline__ void buf_st4(f32x4 x, rsrc_t r, unsigned off, float) {

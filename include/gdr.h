@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 typedef enum gdr_status {
   GDR_OK = 0,
@@ -233,6 +233,37 @@ int gdr_chunk_bwd(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype, 
                   float *d_initial_state,
                   void *workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * gdr_chunk_bwd_ex -- gdr_chunk_bwd with the dtype of dq, dk and dv chosen,
+ * and gdr_chunk_bwd_saved by a switch (the backward pass of training:
+ * diosapp tutorial, section 五).  Training keeps each gradient in its
+ * parameter's dtype; with grad_dtype = GDR_BF16 the kernels write bf16
+ * gradients directly (half the bytes, and no cast afterwards).
+ *
+ *   B .. d_final_state  as gdr_chunk_bwd
+ *   grad_dtype    GDR_F32 or GDR_BF16 (anything else: GDR_EINVAL): the dtype
+ *                 of dq, dk [B, T, H, Dk] and dv [B, T, H, Dv], each the fp32
+ *                 gradient rounded to nearest even.  dbeta, dlog_alpha and
+ *                 d_initial_state stay fp32, the dtypes of beta, log_alpha
+ *                 and the state
+ *   dq .. workspace_bytes  as gdr_chunk_bwd (dq, dk, dv 16-byte aligned)
+ *   saved         0: as gdr_chunk_bwd; nonzero: as gdr_chunk_bwd_saved (the
+ *                 workspace holds what gdr_chunk_fwd_train stored)
+ *
+ * With grad_dtype = GDR_F32 it is gdr_chunk_bwd (saved = 0) or
+ * gdr_chunk_bwd_saved, bit for bit.
+ */
+int gdr_chunk_bwd_ex(int B, int T, int H, int Dk, int Dv, int chunk, int in_dtype,
+                     int grad_dtype, int gate,
+                     const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_alpha,
+                     const float *initial_state,
+                     const void *d_o, const float *d_final_state,
+                     void *dq, void *dk, void *dv, float *dbeta, float *dlog_alpha,
+                     float *d_initial_state,
+                     void *workspace, size_t workspace_bytes, int saved,
+                     hipStream_t stream);
 
 /*
  * gdr_chunk_fwd_train -- gdr_chunk_fwd for training: the same o and

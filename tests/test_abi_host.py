@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == ["gdr_abi_version", "gdr_chunk_bwd", "gdr_chunk_bwd_noalloc",
+    assert names == ["gdr_abi_version", "gdr_chunk_bwd", "gdr_chunk_bwd_ex", "gdr_chunk_bwd_noalloc",
                      "gdr_chunk_bwd_saved", "gdr_chunk_bwd_workspace_bytes",
                      "gdr_chunk_fwd", "gdr_chunk_fwd_ex", "gdr_chunk_fwd_train",
                      "gdr_chunk_fwd_workspace_bytes",
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert _abi.abi_version() == _abi.ABI_VERSION == 3
+    assert _abi.abi_version() == _abi.ABI_VERSION == 4
 
 
 def test_build_entry_accepts_the_built_library():
@@ -298,6 +298,33 @@ def test_chunk_bwd_saved_validates_like_chunk_bwd(kw, want):
     a.update(kw)
     assert _abi.gdr_chunk_bwd_saved(**a) == want
     assert _abi.gdr_chunk_bwd(**a) == want
+
+
+@pytest.mark.parametrize("saved", [0, 1])
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=-1), _abi.GDR_EINVAL),
+    (dict(grad_dtype=2), _abi.GDR_EINVAL),                     # neither fp32 nor bf16
+    (dict(grad_dtype=-1), _abi.GDR_EINVAL),
+    (dict(dv=None), _abi.GDR_EINVAL),
+    (dict(dq=FAKE + 8), _abi.GDR_EINVAL),
+    (dict(in_dtype=_abi.GDR_F32), _abi.GDR_EUNSUPPORTED),
+    (dict(Dk=32, Dv=32), _abi.GDR_EUNSUPPORTED),
+    (dict(workspace=None), _abi.GDR_EWORKSPACE),
+    (dict(B=0, q=None, k=None, v=None, d_o=None, dq=None, dk=None, dv=None, dbeta=None,
+          workspace=None, workspace_bytes=0), _abi.GDR_OK),
+])
+def test_chunk_bwd_ex_validates_like_chunk_bwd(kw, want, saved):
+    """gdr_chunk_bwd_ex checks its arguments as gdr_chunk_bwd does, with either
+    gradient dtype and either value of `saved`, and refuses an unknown
+    gradient dtype."""
+    for grad in (_abi.GDR_F32, _abi.GDR_BF16):
+        a = dict(B=1, T=8, H=1, Dk=128, Dv=128, chunk=0, in_dtype=_abi.GDR_BF16,
+                 grad_dtype=grad, gate=_abi.GDR_GATE_SCALAR, q=FAKE, k=FAKE, v=FAKE,
+                 beta=FAKE, log_alpha=FAKE, initial_state=None, d_o=FAKE, d_final_state=None,
+                 dq=FAKE, dk=FAKE, dv=FAKE, dbeta=FAKE, dlog_alpha=FAKE, d_initial_state=None,
+                 workspace=FAKE, workspace_bytes=1 << 40, saved=saved, stream=None)
+        a.update(kw)
+        assert _abi.gdr_chunk_bwd_ex(**a) == want, grad
 
 
 def fwd_train(**kw):

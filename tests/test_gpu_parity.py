@@ -81,7 +81,7 @@ def with_state(inp, std=0.3, seed=99):
 
 
 def test_library_is_the_hip_build():
-    assert gdr.abi_version() == gdr._abi.ABI_VERSION == 3
+    assert gdr.abi_version() == gdr._abi.ABI_VERSION == 4
     assert gdr.library_loaded()
 
 

@@ -160,6 +160,57 @@ def test_train_pair_many_chains_sampled():
                 assert rel_err(got["dlog_alpha"][b:b + 1, :, h:h + 1], ref["dlog_alpha"]) <= TOL
 
 
+@pytest.mark.parametrize("erase", [True, False])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("D,T", [(64, 33), (128, 100)])
+def test_bf16_gradients_are_the_fp32_ones_rounded(D, T, gate, erase):
+    """grad_dtype=bf16 (gdr_chunk_bwd_ex): dq, dk, dv are the fp32 gradients
+    rounded to nearest even, bit for bit, and the other outputs those of the
+    fp32 call; so within the 2e-3 bar plus half a bf16 ulp of the oracle.
+    Likewise after the training forward (saved), and gdr_chunk_bwd_ex with
+    fp32 gradients is gdr_chunk_bwd bit for bit."""
+    say("bf16 gradients", D, T, gate, erase)
+    inp = make_case(2, T, 2, D, gate, seed=7 * T + D + len(gate))
+    bw = lambda **kw: gdr.chunk_bwd(*args(inp), inp["d_o"], inp["d_final_state"], erase=erase,
+                                    **kw)
+    f32 = bw()
+    b16 = bw(grad_dtype=torch.bfloat16)
+    _, _, ws = gdr.chunk_fwd_train(*args(inp), erase=erase)
+    f32s = bw(workspace=ws, saved=True)
+    b16s = bw(workspace=ws, saved=True, grad_dtype=torch.bfloat16)
+    # the fp32 form of the extended entry point, called directly
+    ex = {n: torch.full_like(t, float("nan")) for n, t in f32.items() if t is not None}
+    B, T_, H, Dk = inp["q"].shape
+    gate_flags = gdr._gate_of(inp["log_alpha"], (B, T_, H), Dk) | (0 if erase else gdr._abi.GDR_NO_ERASE)
+    need = gdr.chunk_bwd_workspace_bytes(inp["q"], inp["log_alpha"], erase=erase)
+    ws2 = torch.empty(need, device=DEV, dtype=torch.uint8)
+    p = lambda t: None if t is None else t.data_ptr()
+    st = gdr._abi.gdr_chunk_bwd_ex(
+        B, T_, H, Dk, Dk, 0, gdr._abi.GDR_BF16, gdr._abi.GDR_F32, gate_flags,
+        *(p(t) for t in args(inp)), p(inp["d_o"]), p(inp["d_final_state"]), p(ex["dq"]),
+        p(ex["dk"]), p(ex["dv"]), p(ex["dbeta"]), p(ex.get("dlog_alpha")),
+        p(ex["d_initial_state"]), ws2.data_ptr(), need, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == gdr._abi.GDR_OK
+    for n in NAMES:
+        if f32[n] is None:
+            assert b16[n] is None and b16s[n] is None
+            continue
+        assert torch.equal(ex[n], f32[n]), n
+        if n in ("dq", "dk", "dv"):
+            assert b16[n].dtype == torch.bfloat16 and b16s[n].dtype == torch.bfloat16
+            assert torch.equal(b16[n], f32[n].to(torch.bfloat16)), n
+            assert torch.equal(b16s[n], f32s[n].to(torch.bfloat16)), n
+        else:
+            assert b16[n].dtype == torch.float32
+            assert torch.equal(b16[n], f32[n]) and torch.equal(b16s[n], f32s[n]), n
+    ref = oracle_bwd(inp, erase)
+    for n in ("dq", "dk", "dv"):
+        r = ref[n]
+        rms = math.sqrt(float(np.mean(r * r)))
+        assert np.all(np.abs(W.to_f64(b16[n]) - r) <= TOL * rms + bf16_half_ulp(r)), n
+
+
 def test_saved_backward_needs_the_workspace():
     inp = make_case(1, 8, 1, 64, "scalar", seed=1)
     with pytest.raises(ValueError):
@@ -170,7 +221,8 @@ def test_saved_backward_needs_the_workspace():
 def test_autograd_function_gives_the_kernels_gradients(gate):
     """loss.backward() through chunk_gated_delta_rule: every input gradient is
     chunk_bwd's for the same upstream gradients (bitwise, cast to the input
-    dtypes), and within the 2e-3 bar of the oracle."""
+    dtypes: the kernels write dq, dk, dv as bf16 directly, the fp32 values
+    rounded to nearest even), and within the 2e-3 bar of the oracle."""
     say("autograd", gate)
     inp = make_case(2, 70, 2, 64, gate, seed=13)
     leaves = {n: inp[n].detach().clone().requires_grad_(True)
