@@ -1,5 +1,6 @@
 // Chunk-parallel gradients of the chunkwise gated delta-rule forward
-// (bf16 q/k/v/dO, fp32 state, MFMA, gfx950).
+// (bf16 q/k/v/dO, fp32 state, MFMA, gfx950; dq, dk, dv written as fp32 or as
+// bf16 rounded to nearest even, template argument GT).
 //
 // The forward evaluated per chunk (xhh.club digest "Transformer 入坑笔记（五）",
 // chunked computation; page "NLP——线性注意力相关总结", sections "Gated DeltaNet

@@ -1,5 +1,6 @@
 // Chunk-parallel gradients of the chunkwise KDA forward (per-channel decay;
-// bf16 q/k/v/dO, fp32 state, MFMA, gfx950).
+// bf16 q/k/v/dO, fp32 state, MFMA, gfx950; dq, dk, dv written as fp32 or as
+// bf16 rounded to nearest even, template argument GT).
 //
 // The forward per chunk of C = 16 tokens (page "NLP——线性注意力相关总结",
 // section "Kimi Delta Attention (KDA)"; xhh.club digest "Transformer 入坑笔记
