@@ -248,3 +248,23 @@ def test_autograd_function_gives_the_kernels_gradients(gate):
         assert got is not None and got.dtype == leaves[n].dtype, n
         assert torch.equal(got, ref[g].to(got.dtype)), n
         assert rel_err(ref[g], orc[g]) <= TOL, n
+
+
+def test_autograd_retained_graph_differentiates_twice():
+    """The workspace lives on the autograd graph: with retain_graph=True a
+    second backward reads it again and accumulates the same gradients (every
+    leaf's gradient is exactly twice the first one's)."""
+    say("autograd retain_graph")
+    inp = make_case(1, 45, 2, 64, "channel", seed=17)
+    leaves = {n: inp[n].detach().clone().requires_grad_(True)
+              for n in ("q", "k", "v", "beta", "log_alpha", "initial_state")}
+    o, S = gdr.chunk_gated_delta_rule(*(leaves[n] for n in ("q", "k", "v", "beta", "log_alpha",
+                                                            "initial_state")))
+    loss = (o * inp["d_o"].float()).sum() + (S * inp["d_final_state"]).sum()
+    loss.backward(retain_graph=True)
+    torch.cuda.synchronize()
+    first = {n: t.grad.clone() for n, t in leaves.items()}
+    loss.backward()
+    torch.cuda.synchronize()
+    for n, t in leaves.items():
+        assert torch.equal(t.grad, 2 * first[n]), n
