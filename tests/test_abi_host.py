@@ -46,6 +46,24 @@ def test_build_entry_accepts_the_built_library():
     __graft_entry__.check_loaded()
 
 
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
+def test_header_compiles_as_c_and_cpp(tmp_path, lang, std):
+    """include/gdr.h is a plain C interface: a C99 (and a C++) translation unit
+    that includes it and calls an entry point compiles."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("no host compiler or ROCm headers")
+    src = tmp_path / "use_gdr.c"
+    src.write_text('#include "gdr.h"\n'
+                   "int main(void) { return gdr_abi_version() == GDR_ABI_VERSION ? 0 : 1; }\n")
+    r = subprocess.run([cc, std, "-Wall", "-Werror", "-fsyntax-only", "-x", lang,
+                        "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+
+
 def test_status_strings():
     for st in (0, -1, -2, -3, -4):
         assert _abi.status_str(st).startswith("GDR_")
