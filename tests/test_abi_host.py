@@ -64,6 +64,18 @@ def test_header_compiles_as_c_and_cpp(tmp_path, lang, std):
     assert r.returncode == 0, r.stderr[-2000:]
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises at once: the path
+    has no other implementation to fall back on."""
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "libgdr.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.abi_version()
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.gdr_chunk_bwd_workspace_bytes(1, 1, 1, 64, 64, 0, _abi.GDR_BF16,
+                                           _abi.GDR_GATE_SCALAR)
+
+
 def test_status_strings():
     for st in (0, -1, -2, -3, -4):
         assert _abi.status_str(st).startswith("GDR_")
